@@ -1,0 +1,252 @@
+"""Pins of the oracle's calibration steps against closed forms, brute force and
+textbook values (no GPU)."""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- statistics
+def test_covariance_matches_pure_python():
+    rng = np.random.default_rng(1)
+    K = rng.standard_normal((7, 3)) + 2.0
+    V = rng.standard_normal((7, 3))
+    Q = rng.standard_normal((2, 3))
+    st = oracle.head_stats(K, V, Q)
+    n = 7
+    mu = [sum(K[i][j] for i in range(n)) / n for j in range(3)]
+    for a in range(3):
+        for b in range(3):
+            ref = sum((K[i][a] - mu[a]) * (K[i][b] - mu[b]) for i in range(n)) / n
+            assert abs(st["SigK"][a, b] - ref) < 1e-12
+    assert np.allclose(st["muK"], mu, atol=1e-14)
+
+
+def test_attention_statistics_brute_force():
+    """M_Q and gamma_V with plain loops (no expansion of ||v_i - o||^2)."""
+    rng = np.random.default_rng(2)
+    N, d, nq = 5, 3, 4
+    K = rng.standard_normal((N, d))
+    V = rng.standard_normal((N, d))
+    Q = 2.0 * rng.standard_normal((nq, d))
+    st = oracle.head_stats(K, V, Q)
+    MQ = [[0.0] * d for _ in range(d)]
+    gam = 0.0
+    for q in Q:
+        s = [sum(q[j] * K[i][j] for j in range(d)) / math.sqrt(d) for i in range(N)]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        A = [x / sum(e) for x in e]
+        o = [sum(A[i] * V[i][j] for i in range(N)) for j in range(d)]
+        g = sum(A[i] ** 2 * sum((V[i][j] - o[j]) ** 2 for j in range(d)) for i in range(N))
+        gam += sum(a * a for a in A)
+        for a in range(d):
+            for b in range(d):
+                MQ[a][b] += g * q[a] * q[b]
+    assert np.allclose(st["MQ"], np.array(MQ) / nq, rtol=1e-12, atol=1e-14)
+    assert abs(st["gammaV"] - gam / nq) < 1e-14
+
+
+def test_identical_keys_give_uniform_attention():
+    rng = np.random.default_rng(3)
+    N, d = 9, 4
+    K = np.tile(rng.standard_normal(d), (N, 1))
+    V = rng.standard_normal((N, d))
+    Q = rng.standard_normal((3, d))
+    st = oracle.head_stats(K, V, Q)
+    assert abs(st["gammaV"] - 1.0 / N) < 1e-15
+    g = ((V - V.mean(0)) ** 2).sum() / N ** 2
+    assert np.allclose(st["MQ"], g * Q.T @ Q / 3, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- KLT
+def test_klt_recovers_constructed_spectrum():
+    rng = np.random.default_rng(4)
+    d = 16
+    U0 = synth.haar_orthogonal(d, rng)
+    lam0 = np.sort(rng.uniform(0.1, 5.0, d))[::-1]
+    S = (U0 * lam0) @ U0.T
+    lam, U = oracle.klt(S)
+    assert np.allclose(lam, lam0, rtol=1e-12)
+    assert np.abs(U.T @ U - np.eye(d)).max() < 1e-12
+    D = U.T @ S @ U
+    assert np.abs(D - np.diag(np.diag(D))).max() < 1e-12 * lam0.max()
+    # columns equal the constructed ones up to sign, and follow the sign rule
+    for j in range(d):
+        assert abs(abs(U[:, j] @ U0[:, j]) - 1.0) < 1e-10
+        i = int(np.argmax(np.abs(U[:, j])))
+        assert U[i, j] > 0
+
+
+def test_klt_2x2_closed_form():
+    a, b, c = 3.0, 1.25, 1.0
+    lam, U = oracle.klt(np.array([[a, b], [b, c]]))
+    r = math.sqrt(((a - c) / 2) ** 2 + b * b)
+    assert abs(lam[0] - ((a + c) / 2 + r)) < 1e-14
+    assert abs(lam[1] - ((a + c) / 2 - r)) < 1e-14
+    # eigenvector of the larger eigenvalue is (b, lam0 - a) normalised
+    v = np.array([b, lam[0] - a])
+    v /= np.linalg.norm(v)
+    assert np.allclose(U[:, 0], v, atol=1e-14)
+
+
+# ---------------------------------------------------------------- weights
+def test_channel_weights_transform_domain():
+    """x^K_j = lambda_j (U^T M_Q U)_jj / d and x^V_j = lambda_j gamma_V, written with loops."""
+    rng = np.random.default_rng(5)
+    d = 4
+    st = {"MQ": np.cov(rng.standard_normal((d, 10))), "gammaV": 0.37}
+    UK = synth.haar_orthogonal(d, rng)
+    UV = synth.haar_orthogonal(d, rng)
+    lamK = np.array([4.0, 2.0, 1.0, 0.5])
+    lamV = np.array([3.0, 1.5, 0.2, 0.1])
+    xK, xV = oracle.channel_weights(st, UK, lamK, UV, lamV)
+    for j in range(d):
+        w = sum(UK[a, j] * st["MQ"][a, b] * UK[b, j] for a in range(d) for b in range(d)) / d
+        assert abs(xK[j] - lamK[j] * w) < 1e-14
+        assert abs(xV[j] - lamV[j] * 0.37) < 1e-15
+
+
+# ---------------------------------------------------------------- water-filling
+def test_waterfill_closed_form_no_cap():
+    rng = np.random.default_rng(6)
+    x = np.exp(rng.uniform(-3, 3, 24))
+    B = 40.0
+    theta, R = oracle.waterfill_theta(x, B)
+    assert abs(R.sum() - B) < 1e-9
+    # closed form over the active set: log2(theta) = (sum_A log2 x - 2B)/|A|
+    xs = np.sort(x)[::-1]
+    for n_act in range(len(xs), 0, -1):
+        lt = (np.log2(xs[:n_act]).sum() - 2 * B) / n_act
+        if xs[n_act - 1] > 2 ** lt:
+            break
+    assert abs(math.log2(theta) - lt) < 1e-9
+    assert R.max() < 8
+    # per-channel distortion of the continuous solution is min(theta, x_j)
+    D = x * 4.0 ** (-R)
+    assert np.allclose(D, np.minimum(theta, x), rtol=1e-9)
+
+
+def test_waterfill_cap_binds():
+    x = np.array([1e12, 1.0, 0.5, 0.25])
+    theta, R = oracle.waterfill_theta(x, 12.0, max_bits=8)
+    assert abs(R.sum() - 12.0) < 1e-9
+    assert R[0] == 8.0
+
+
+def _brute_force_alloc(xK, xV, B, max_bits):
+    x = list(xK) + list(xV)
+    best = None
+    for b in itertools.product(range(max_bits + 1), repeat=len(x)):
+        if sum(b) != B:
+            continue
+        cost = sum(xi * 4.0 ** (-bi) for xi, bi in zip(x, b))
+        if best is None or cost < best[0] - 1e-15:
+            best = (cost, b)
+    return best
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_integer_allocation_is_optimal_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    xK = np.exp(rng.uniform(-4, 4, 2))
+    xV = np.exp(rng.uniform(-4, 4, 2))
+    max_bits = 5
+    B = int(rng.integers(0, 4 * max_bits + 1))
+    bK, bV = oracle.allocate_bits(xK, xV, B, max_bits=max_bits)
+    assert bK.sum() + bV.sum() == B
+    cost = sum(x * 4.0 ** (-b) for x, b in zip(list(xK) + list(xV), list(bK) + list(bV)))
+    best = _brute_force_alloc(xK, xV, B, max_bits)
+    assert cost <= best[0] * (1 + 1e-12) + 1e-300
+
+
+def test_integer_allocation_properties():
+    w = synth.WORKLOADS["llama_32k"]
+    hm = synth.head_model(w, 0, 3)
+    K, V, Q = synth.calibration_samples(w, hm, 0, 3)
+    st = oracle.head_stats(K, V, Q)
+    cb = oracle.build_head_codebook(st, 2.75)
+    assert cb.bK.sum() + cb.bV.sum() == 704
+    assert cb.bK.min() >= 0 and cb.bK.max() <= 8 and cb.bV.max() <= 8
+    # monotone in x within keys and within values
+    for x, b in ((cb.xK, cb.bK), (cb.xV, cb.bV)):
+        o = np.argsort(-x, kind="stable")
+        assert np.all(np.diff(b[o]) <= 0)
+    # within one bit of the continuous solution for active, uncapped channels
+    x = np.concatenate([cb.xK, cb.xV])
+    b = np.concatenate([cb.bK, cb.bV])
+    theta, R = oracle.waterfill_theta(x, 704)
+    act = (R > 0) & (R < 8)
+    assert np.all(np.abs(b[act] - R[act]) <= 1.0 + 1e-9)
+
+
+def test_uniform_weights_give_uniform_bits():
+    d = 8
+    x = np.ones(d)
+    bK, bV = oracle.allocate_bits(x, x, 2 * d * 3)
+    assert np.all(bK == 3) and np.all(bV == 3)
+    bK, bV = oracle.allocate_bits(x, 2 * x, 2 * d * 3, joint=False)
+    assert np.all(bK == 3) and np.all(bV == 3)
+
+
+# ---------------------------------------------------------------- quantizer design
+def test_one_bit_step_closed_form():
+    # 2-level optimum reconstructs at +-E|X| = +-sqrt(2/pi)
+    assert abs(oracle.optimal_step(1) - 2 * math.sqrt(2 / math.pi)) < 1e-9
+
+
+def test_max_1960_table():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "max1960_uniform_gaussian.txt"))
+            if l.strip() and not l.startswith("#")]
+    for levels, step, mse in rows:
+        b = int(round(math.log2(int(levels))))
+        s = oracle.optimal_step(b)
+        assert abs(s - float(step)) < 6e-4 * float(step) + 1e-4, (levels, s, step)
+        m = oracle.uniform_quantizer_mse(s, int(levels))
+        assert abs(m - float(mse)) < 2e-3 * float(mse), (levels, m, mse)
+
+
+def test_quantizer_mse_against_quadrature():
+    from scipy import integrate
+    step, levels = 0.7, 8
+    half = levels // 2
+
+    def err(x):
+        k = min(max(math.floor(x / step), -half), half - 1)
+        r = (k + 0.5) * step
+        return (x - r) ** 2 * math.exp(-x * x / 2) / math.sqrt(2 * math.pi)
+
+    pts = [k * step for k in range(-half + 1, half)]
+    total = 0.0
+    edges = [-12.0] + pts + [12.0]
+    for a, b in zip(edges[:-1], edges[1:]):
+        total += integrate.quad(err, a, b, epsabs=1e-14, epsrel=1e-12)[0]
+    assert abs(oracle.uniform_quantizer_mse(step, levels) - total) < 1e-10
+
+
+def test_high_resolution_limit():
+    """With a loading of +-6 sigma the overload term vanishes and the MSE is step^2/12
+    up to O(step^4) (granular noise of a smooth density)."""
+    step = 12.0 / 256
+    m = oracle.uniform_quantizer_mse(step, 256)
+    assert abs(m / (step * step / 12) - 1) < 1e-3
+    # the optimal 256-level step also has the granular term dominant
+    s = oracle.optimal_step(8)
+    assert 1.0 < oracle.uniform_quantizer_mse(s, 256) / (s * s / 12) < 1.2
+
+
+def test_compression_ratio_matches_pages():
+    for line in open(os.path.join(GOLDEN, "pages_compression.txt")):
+        if line.strip() and not line.startswith("#"):
+            rbar, ratio = map(float, line.split())
+            d = 128
+            B = int(2 * d * rbar)
+            bits_bf16 = 2 * d * 16
+            assert round(bits_bf16 / B, 1) == ratio
