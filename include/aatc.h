@@ -1,0 +1,222 @@
+/*
+ * aatc.h - C ABI of the MI355X transform-coded KV cache (Attention-Aware Transform
+ * Coding, AATC).
+ *
+ * The method (pages: "KV Cache Compression Through the Lens of Transform Coding",
+ * abstract and Methodology; "Attention-Aware Transform Coding Guide", sections
+ * "Decorrelation via the Karhunen-Loeve Transform", "Optimal Bit Allocation via
+ * Reverse Water-Filling" and "Theorem: Additive Error Decomposition"; "Spend Bits
+ * Where Queries Look" abstract for the fixed per-token bit count):
+ *   calibrate: per (layer, kv-head) statistics -> KLT bases U_K, U_V, attention-aware
+ *              channel weights, integer bits per channel by reverse water-filling under
+ *              an average bits/element budget, scalar quantizer steps;
+ *   encode:    bf16 K, V -> KLT coefficients -> per-channel codes -> packed tiles with a
+ *              fixed number of bits per token;
+ *   decode_attention: queries scored in the key transform domain (q' = U_K^T q) straight
+ *              from the packed cache, online softmax, value coefficients accumulated and
+ *              inverse-transformed once per query head.
+ *
+ * Conventions
+ *   - Every function returns an int status: AATC_OK (0) or a negative AATC_ERR_* code;
+ *     aatc_last_error() gives a thread-local message for the last failure.
+ *   - Argument errors are detected before anything is enqueued; on error nothing is
+ *     launched.  Device faults surface at the caller's next synchronisation.
+ *   - The caller owns all device memory and streams ("stream" is a hipStream_t passed
+ *     as void*; NULL is the null stream).  The library allocates host memory only (the
+ *     codebook) and never synchronises a stream.  Device pointers must be 16-byte
+ *     aligned.  A codebook is immutable once created and may be shared across threads.
+ *   - head_dim d is 64 or 128; the query group size G = H_q / H_kv is 1..16; the budget
+ *     B = 2 * d * avg_bits bits per token and kv-head must be an even integer.
+ *   - Matrices are row-major.  A basis U is d x d with U[i*d + j] = component i of basis
+ *     vector j (coefficients are c = (x - mu) U).
+ */
+#ifndef AATC_H
+#define AATC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AATC_VERSION 1
+#define AATC_LAYOUT_VERSION 1
+
+#define AATC_OK 0
+#define AATC_ERR_INVALID_ARG (-1)
+#define AATC_ERR_UNSUPPORTED (-2)
+#define AATC_ERR_BUDGET (-3)
+#define AATC_ERR_STATS (-4)
+#define AATC_ERR_NO_CONVERGENCE (-5)
+#define AATC_ERR_CAPACITY (-6)
+#define AATC_ERR_WORKSPACE (-7)
+#define AATC_ERR_HIP (-8)
+#define AATC_ERR_IO (-9)
+#define AATC_ERR_VERSION (-10)
+
+/* Opaque host-side codebook: bases, bits and steps of n_layers * n_kv heads. */
+typedef struct aatc_codebook aatc_codebook;
+
+/* Calibration statistics of one (layer, kv-head); caller-owned arrays.
+ * mu_k, mu_v: [d] channel means; sigma_k, sigma_v: [d*d] centred covariances (1/N);
+ * m_q: [d*d] attention-weighted query moment mean_q g(q) q q^T with
+ *      g(q) = sum_i A_i^2 ||v_i - o(q)||^2 over the calibration tokens;
+ * gamma_v: mean_q sum_i A_i^2.  (Pages: the KLT section's channel covariances; the
+ * theorem's key and value weights, read as expectations over calibration queries.) */
+typedef struct {
+    const double* mu_k;
+    const double* mu_v;
+    const double* sigma_k;
+    const double* sigma_v;
+    const double* m_q;
+    double gamma_v;
+} aatc_head_stats;
+
+/* Calibration parameters.  avg_bits: average bits per cached element (the budget of the
+ * reverse water-filling section, sum_j R_j = d * avg_bits per tensor); max_bits: per
+ * channel cap (1..8); joint: 1 = keys and values share one budget of 2*d*avg_bits bits
+ * per token (one water level for the sum D_K + D_V of the theorem), 0 = d*avg_bits each;
+ * max_sweeps: Jacobi sweep limit of the eigensolver (0 = default 60). */
+typedef struct {
+    double avg_bits;
+    int32_t max_bits;
+    int32_t joint;
+    int32_t max_sweeps;
+    int32_t reserved;
+} aatc_calib_params;
+
+/* Device-side cache descriptor.  data: caller-allocated device memory of
+ * aatc_cache_bytes() bytes, zero-filled before first use.  The cache of
+ * (layer, seq, kv-head) is a run of ceil(max_tokens/64) tiles of 64 token slots;
+ * tile t lives at byte (((layer*n_seqs + seq)*n_kv + head)*n_tiles + t) * tile_bytes. */
+typedef struct {
+    void* data;
+    int32_t n_layers;
+    int32_t n_seqs;
+    int64_t max_tokens;
+} aatc_cache;
+
+/* ---- version and errors ------------------------------------------------------------ */
+int aatc_version(void);                     /* AATC_VERSION */
+int aatc_layout_version(void);              /* AATC_LAYOUT_VERSION */
+const char* aatc_status_string(int status); /* static string for a status code */
+const char* aatc_last_error(void);          /* thread-local detail of the last failure */
+
+/* ---- host calibration ---------------------------------------------------------------- */
+
+/* Statistics of one (layer, kv-head) from host samples (float32, row-major):
+ * K, V [n x d] calibration keys/values, Q [nq x d] calibration queries of the G query
+ * heads of the group, pooled.  Attention of every query over the n tokens is exact and
+ * non-causal.  Outputs are caller-allocated: mu_k, mu_v [d]; sigma_k, sigma_v, m_q [d*d];
+ * gamma_v [1].  Errors: INVALID_ARG (null pointer, n < 2, nq < 1, bad d), STATS
+ * (non-finite input).  Runs on host threads. */
+int aatc_stats_from_samples(int32_t d, const float* K, const float* V, int64_t n,
+                            const float* Q, int64_t nq, double* mu_k, double* mu_v,
+                            double* sigma_k, double* sigma_v, double* m_q, double* gamma_v);
+
+/* Calibrate n_layers * n_kv heads (stats indexed layer*n_kv + head): eigendecomposition of
+ * both covariances (eigenvalues descending; each eigenvector's largest-magnitude entry
+ * positive), channel weights x_K = lambda_K (U_K^T M_Q U_K)_jj / d and
+ * x_V = lambda_V gamma_V, integer bits in [0, max_bits] with an exact total per token
+ * (greedy on marginal gains x_j 4^-k; ties: keys, then lower channel, then lower k), and
+ * steps step_b * sqrt(lambda_j) of the Gaussian-MSE-optimal 2^b-level uniform quantizer.
+ * *out is allocated by the library (free with aatc_codebook_free).
+ * Errors: INVALID_ARG, BUDGET (2*d*avg_bits not an even integer, or out of range),
+ * STATS (non-finite or non-PSD input), NO_CONVERGENCE (eigensolver). */
+int aatc_calibrate(int32_t d, int32_t n_layers, int32_t n_kv, int32_t group,
+                   const aatc_head_stats* stats, const aatc_calib_params* params,
+                   aatc_codebook** out);
+
+/* Build a codebook from explicit per-head arrays (e.g. produced by another calibration
+ * tool): U_k, U_v [n_heads][d][d] float64; mu_k, mu_v [n_heads][d] float64; bits_k,
+ * bits_v [n_heads][d] int32 in [0,8]; step_k, step_v [n_heads][d] float32 (> 0 where
+ * bits > 0).  Every head must have the same total bits per token (an even number).
+ * Errors: INVALID_ARG, BUDGET. */
+int aatc_codebook_create(int32_t d, int32_t n_layers, int32_t n_kv, int32_t group,
+                         const double* U_k, const double* U_v, const double* mu_k,
+                         const double* mu_v, const int32_t* bits_k, const int32_t* bits_v,
+                         const float* step_k, const float* step_v, aatc_codebook** out);
+
+/* Geometry of a codebook; any output pointer may be NULL.  total_bits = bits per token
+ * and kv-head (keys and values); tile_bytes = 8 * total_bits. */
+int aatc_codebook_info(const aatc_codebook* cb, int32_t* d, int32_t* n_layers,
+                       int32_t* n_kv, int32_t* group, int32_t* total_bits,
+                       int32_t* tile_bytes);
+
+/* Copy out one head's calibration results (any pointer may be NULL): U_k, U_v [d*d],
+ * lam_k, lam_v, mu_k, mu_v, x_k, x_v [d] float64; bits_k, bits_v [d] int32;
+ * step_k, step_v [d] float32; theta [1] (continuous water level, 0 if not calibrated). */
+int aatc_codebook_head(const aatc_codebook* cb, int32_t head, double* U_k, double* U_v,
+                       double* lam_k, double* lam_v, double* mu_k, double* mu_v,
+                       double* x_k, double* x_v, int32_t* bits_k, int32_t* bits_v,
+                       float* step_k, float* step_v, double* theta);
+
+/* Persist / restore a codebook (versioned binary file with checksum).
+ * Errors: IO, VERSION (layout or format mismatch, checksum failure). */
+int aatc_codebook_save(const aatc_codebook* cb, const char* path);
+int aatc_codebook_load(const char* path, aatc_codebook** out);
+void aatc_codebook_free(aatc_codebook* cb);
+
+/* ---- device side ------------------------------------------------------------------- */
+
+/* Bytes of the device blob (bases, steps, bias vectors and kernel tables of all heads). */
+int aatc_codebook_device_bytes(const aatc_codebook* cb, size_t* bytes);
+
+/* Copy the blob to caller-allocated device memory d_blob (bytes >= device_bytes) with an
+ * asynchronous copy on `stream`; the codebook must stay alive until the copy completes.
+ * Errors: INVALID_ARG, WORKSPACE (too small), HIP. */
+int aatc_codebook_upload(const aatc_codebook* cb, void* d_blob, size_t bytes, void* stream);
+
+/* Bytes of a cache for n_layers x n_seqs sequences of up to max_tokens tokens. */
+int aatc_cache_bytes(const aatc_codebook* cb, int32_t n_layers, int32_t n_seqs,
+                     int64_t max_tokens, size_t* bytes);
+
+/* Append n_tokens tokens to each of n_seqs sequences of one layer.
+ * seq_ids [n_seqs], start_pos [n_seqs]: host arrays; sequence s writes token slots
+ * start_pos[s] .. start_pos[s]+n_tokens-1.  K, V: device bf16 [n_seqs][n_tokens][n_kv][d]
+ * (contiguous).  Tokens of a sequence must be appended in order: the slots being written
+ * must still be zero (a partially filled tile is read, OR-ed and written back).
+ * Coefficients: c = x (U_hi + U_lo) - mu (U_hi + U_lo) with U_hi/U_lo the bf16 split of
+ * U (bf16 MFMA, fp32 accumulation); codes as the quantizer of aatc_encode_coeffs.
+ * Errors: INVALID_ARG, CAPACITY (start_pos + n_tokens > max_tokens), HIP. */
+int aatc_encode(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
+                int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                const int64_t* start_pos, int64_t n_tokens, const uint16_t* K,
+                const uint16_t* V, void* stream);
+
+/* Encode given KLT coefficients (skips the projection): coeffs device float32
+ * [n_tokens][n_kv][2][d] (keys then values, KLT channel order) for one (layer, seq)
+ * starting at slot start_pos.  Code of channel j with b > 0 bits:
+ * t = fp32(c * fp32(1/step_j)) (one rounding), code = clamp(floor(t) + 2^(b-1), 0, 2^b-1).
+ * Non-finite coefficients give unspecified codes.  Errors as aatc_encode. */
+int aatc_encode_coeffs(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
+                       int32_t layer, int32_t seq, int64_t start_pos, int64_t n_tokens,
+                       const float* coeffs, void* stream);
+
+/* Workspace bytes for aatc_decode_attention with n_seqs sequences of length <= max_len. */
+int aatc_decode_workspace_bytes(const aatc_codebook* cb, int32_t n_seqs, int64_t max_len,
+                                size_t* bytes);
+
+/* One decode step of one layer: out[s][h] = softmax(q_h K_hat^T / sqrt(d)) V_hat over the
+ * first seq_lens[s] cached tokens of sequence seq_ids[s] (no mask), query head h reading
+ * kv-head floor(h / G).  seq_ids [n_seqs] int32 and seq_lens [n_seqs] int64 are DEVICE
+ * arrays (1 <= seq_lens[s] <= max_len <= max_tokens); max_len (host) sizes the grid.
+ * q: device bf16 [n_seqs][H_q][d]; out: device float32 [n_seqs][H_q][d]; workspace:
+ * device scratch of aatc_decode_workspace_bytes() bytes (no initialisation needed).
+ * Errors: INVALID_ARG, CAPACITY, WORKSPACE, HIP. */
+int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
+                          int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                          const int64_t* seq_lens, int64_t max_len, const uint16_t* q,
+                          float* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* ---- measurement helpers ----------------------------------------------------------- */
+
+/* Overwrite `bytes` of caller-allocated device memory with a streaming write (used to
+ * evict the device's last-level cache between timed repetitions).  Errors: HIP. */
+int aatc_flush_write(void* d_buf, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AATC_H */

@@ -1,0 +1,80 @@
+// Internal definitions shared by the host calibration code and the HIP kernels:
+// the codebook object, the per-head device blob and error reporting.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/aatc.h"
+
+namespace aatc {
+
+constexpr int kTile = 64;        // token slots per tile
+constexpr int kMaxD = 128;       // largest head_dim
+constexpr int kMaxPieces = 512;  // >= 3 pieces per channel * 128 channels
+
+// One power-of-two piece of a channel's code: bits [shift, shift + width) of the code.
+// Pieces are ordered by width (8, 4, 2, 1) then by KLT channel; `offset` is the sum of the
+// widths before it (bit offset inside a token's key record, or slab index for values).
+struct Piece {
+    int chan;
+    int width;
+    int shift;
+    int offset;
+};
+
+struct HeadCB {
+    std::vector<double> UK, UV;      // d*d, U[i*d + j] = component i of basis vector j
+    std::vector<double> lamK, lamV;  // eigenvalues (descending) or empty
+    std::vector<double> muK, muV;
+    std::vector<double> xK, xV;      // channel weights (empty if not calibrated)
+    std::vector<int32_t> bK, bV;
+    std::vector<float> stepK, stepV;
+    double theta = 0.0;
+    // derived
+    std::vector<Piece> pK, pV;
+    int BK = 0, BV = 0;
+};
+
+// Device blob of one head.  Arrays are sized for d = 128 and indexed densely for the
+// actual d (e.g. UK[i*d + j]).  Packed piece words: chan | width<<8 | shift<<12 | offset<<16.
+struct alignas(256) DevHead {
+    int32_t d, BK, BV, nKp, nVp;
+    int32_t pad0[59];
+    float UK[kMaxD * kMaxD];      // fp32 basis (query transform)
+    float UV[kMaxD * kMaxD];      // fp32 basis (inverse transform of values)
+    uint16_t UKhi[kMaxD * kMaxD]; // bf16 split of U_K: U = hi + lo (+ rounding)
+    uint16_t UKlo[kMaxD * kMaxD];
+    uint16_t UVhi[kMaxD * kMaxD];
+    uint16_t UVlo[kMaxD * kMaxD];
+    float muV[kMaxD];
+    float biasK[kMaxD];           // mu_K (U_hi + U_lo), fp64 sum rounded once
+    float biasV[kMaxD];
+    float stepK[kMaxD], stepV[kMaxD];
+    float invK[kMaxD], invV[kMaxD];
+    int32_t bitsK[kMaxD], bitsV[kMaxD];
+    int32_t pieceK[kMaxPieces];
+    int32_t pieceV[kMaxPieces];
+};
+
+}  // namespace aatc
+
+struct aatc_codebook {
+    int d = 0, n_layers = 0, n_kv = 0, group = 0;
+    int total_bits = 0;
+    double avg_bits = 0.0;
+    int max_bits = 8;
+    int joint = 1;
+    std::vector<aatc::HeadCB> heads;
+    std::vector<aatc::DevHead> blob;  // built by aatc::finalize
+};
+
+namespace aatc {
+
+int set_error(int code, const char* fmt, ...);
+int finalize(aatc_codebook* cb);  // pieces, B, device blob; validates budget
+uint16_t f32_to_bf16(float f);
+float bf16_to_f32(uint16_t h);
+
+}  // namespace aatc

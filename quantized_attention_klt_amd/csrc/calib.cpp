@@ -1,0 +1,815 @@
+// Host calibration of the transform-coded KV cache: statistics, Jacobi KLT, attention-aware
+// channel weights, reverse water-filling and exact-budget integer bits, Gaussian-optimal
+// uniform quantizer steps, codebook construction, persistence and the per-head device blob.
+//
+// Method references (pages): "Attention-Aware Transform Coding Guide", sections
+// "Decorrelation via the Karhunen-Loeve Transform (KLT)" (covariances, eigenbasis),
+// "Theorem: Additive Error Decomposition" (key/value weights) and "Optimal Bit Allocation
+// via Reverse Water-Filling" (R_j = max(0, 1/2 log2(w_j lambda_j / theta)), sum R_j fixed);
+// "KV Cache Compression Through the Lens of Transform Coding", Methodology (whitening).
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <thread>
+
+#include "aatc_internal.h"
+
+namespace aatc {
+
+static thread_local std::string g_last_error;
+
+int set_error(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+uint16_t f32_to_bf16(float f) {
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+float bf16_to_f32(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+// Run fn(i) for i in [0, n) on up to hardware_concurrency threads.
+template <class F>
+static void parallel_for(int64_t n, F fn) {
+    unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+    if (n < 2 || nt == 1) {
+        for (int64_t i = 0; i < n; ++i) fn(i, 0u);
+        return;
+    }
+    nt = (unsigned)std::min<int64_t>(nt, n);
+    std::atomic<int64_t> next(0);
+    std::vector<std::thread> th;
+    for (unsigned t = 0; t < nt; ++t)
+        th.emplace_back([&, t] {
+            for (int64_t i; (i = next.fetch_add(1)) < n;) fn(i, t);
+        });
+    for (auto& x : th) x.join();
+}
+
+static unsigned n_workers() {
+    return std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+}
+
+// ------------------------------------------------------------------------------------
+// Symmetric eigensolver: cyclic Jacobi rotations (fp64), eigenvalues descending, each
+// eigenvector's largest-magnitude entry positive (lowest row index on ties).
+// ------------------------------------------------------------------------------------
+static int jacobi_eigen(int d, const double* S, int max_sweeps, std::vector<double>& lam,
+                        std::vector<double>& U) {
+    std::vector<double> A(S, S + (size_t)d * d), Vm((size_t)d * d, 0.0);
+    for (int i = 0; i < d; ++i) Vm[(size_t)i * d + i] = 1.0;
+    double fro = 0.0;
+    for (size_t i = 0; i < A.size(); ++i) fro += A[i] * A[i];
+    fro = std::sqrt(fro);
+    bool converged = fro == 0.0;
+    for (int sweep = 0; sweep < max_sweeps && !converged; ++sweep) {
+        double off = 0.0;
+        for (int p = 0; p < d; ++p)
+            for (int q = p + 1; q < d; ++q) off += A[(size_t)p * d + q] * A[(size_t)p * d + q];
+        if (std::sqrt(2.0 * off) <= 1e-15 * fro) {
+            converged = true;
+            break;
+        }
+        for (int p = 0; p < d - 1; ++p) {
+            for (int q = p + 1; q < d; ++q) {
+                double apq = A[(size_t)p * d + q];
+                if (apq == 0.0) continue;
+                double app = A[(size_t)p * d + p], aqq = A[(size_t)q * d + q];
+                double th = (aqq - app) / (2.0 * apq);
+                double t = (th >= 0 ? 1.0 : -1.0) / (std::fabs(th) + std::sqrt(th * th + 1.0));
+                double c = 1.0 / std::sqrt(t * t + 1.0), s = t * c;
+                for (int k = 0; k < d; ++k) {  // columns p, q
+                    double akp = A[(size_t)k * d + p], akq = A[(size_t)k * d + q];
+                    A[(size_t)k * d + p] = c * akp - s * akq;
+                    A[(size_t)k * d + q] = s * akp + c * akq;
+                }
+                for (int k = 0; k < d; ++k) {  // rows p, q
+                    double apk = A[(size_t)p * d + k], aqk = A[(size_t)q * d + k];
+                    A[(size_t)p * d + k] = c * apk - s * aqk;
+                    A[(size_t)q * d + k] = s * apk + c * aqk;
+                }
+                A[(size_t)p * d + q] = A[(size_t)q * d + p] = 0.0;
+                for (int k = 0; k < d; ++k) {
+                    double vkp = Vm[(size_t)k * d + p], vkq = Vm[(size_t)k * d + q];
+                    Vm[(size_t)k * d + p] = c * vkp - s * vkq;
+                    Vm[(size_t)k * d + q] = s * vkp + c * vkq;
+                }
+            }
+        }
+    }
+    if (!converged) {
+        double off = 0.0;
+        for (int p = 0; p < d; ++p)
+            for (int q = p + 1; q < d; ++q) off += A[(size_t)p * d + q] * A[(size_t)p * d + q];
+        if (!(std::sqrt(2.0 * off) <= 1e-15 * fro))
+            return set_error(AATC_ERR_NO_CONVERGENCE, "Jacobi eigensolver did not converge in %d sweeps",
+                             max_sweeps);
+    }
+    std::vector<int> order(d);
+    for (int i = 0; i < d; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+        return A[(size_t)a * d + a] > A[(size_t)b * d + b];
+    });
+    lam.assign(d, 0.0);
+    U.assign((size_t)d * d, 0.0);
+    for (int j = 0; j < d; ++j) {
+        int o = order[j];
+        lam[j] = std::max(0.0, A[(size_t)o * d + o]);
+        int imax = 0;
+        double vmax = -1.0;
+        for (int i = 0; i < d; ++i) {
+            double v = std::fabs(Vm[(size_t)i * d + o]);
+            if (v > vmax) {
+                vmax = v;
+                imax = i;
+            }
+        }
+        double sgn = Vm[(size_t)imax * d + o] < 0 ? -1.0 : 1.0;
+        for (int i = 0; i < d; ++i) U[(size_t)i * d + j] = sgn * Vm[(size_t)i * d + o];
+    }
+    return AATC_OK;
+}
+
+// ------------------------------------------------------------------------------------
+// Reverse water-filling (continuous), for reporting the water level theta.
+// ------------------------------------------------------------------------------------
+static double waterfill_theta(const std::vector<double>& x, double total, int max_bits) {
+    double xmin = INFINITY, xmax = 0.0;
+    int npos = 0;
+    for (double v : x)
+        if (v > 0) {
+            xmin = std::min(xmin, v);
+            xmax = std::max(xmax, v);
+            ++npos;
+        }
+    if (total <= 0 || npos == 0) return INFINITY;
+    if (total >= (double)max_bits * npos) return 0.0;
+    auto rate = [&](double lt) {
+        double s = 0.0;
+        for (double v : x)
+            if (v > 0) {
+                double r = 0.5 * (std::log2(v) - lt / std::log(2.0));
+                s += std::min<double>(std::max(r, 0.0), max_bits);
+            }
+        return s;
+    };
+    double lo = std::log(xmin) - 2.0 * max_bits * std::log(2.0) - 1.0, hi = std::log(xmax);
+    for (int it = 0; it < 400; ++it) {
+        double mid = 0.5 * (lo + hi);
+        if (rate(mid) > total)
+            lo = mid;
+        else
+            hi = mid;
+        if (hi - lo < 1e-15 * std::max(1.0, std::fabs(mid))) break;
+    }
+    return std::exp(0.5 * (lo + hi));
+}
+
+// Exact-budget integer allocation: the `budget` largest marginal gains x_j 4^-k (k < max_bits),
+// ties broken by (keys first, lower channel, lower k).
+struct Gain {
+    double g;
+    int kv, j, k;
+};
+
+static void allocate_bits(const std::vector<double>* groups[2], int ngroups, const int* gid,
+                          int budget, int max_bits, std::vector<int32_t>* out[2]) {
+    std::vector<Gain> c;
+    for (int gi = 0; gi < ngroups; ++gi) {
+        const std::vector<double>& x = *groups[gi];
+        for (int j = 0; j < (int)x.size(); ++j)
+            for (int k = 0; k < max_bits; ++k) c.push_back({std::ldexp(x[j], -2 * k), gid[gi], j, k});
+    }
+    std::sort(c.begin(), c.end(), [](const Gain& a, const Gain& b) {
+        if (a.g != b.g) return a.g > b.g;
+        if (a.kv != b.kv) return a.kv < b.kv;
+        if (a.j != b.j) return a.j < b.j;
+        return a.k < b.k;
+    });
+    for (int i = 0; i < budget && i < (int)c.size(); ++i) {
+        for (int gi = 0; gi < ngroups; ++gi)
+            if (gid[gi] == c[i].kv) (*out[gi])[c[i].j] += 1;
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Gaussian-optimal midrise uniform quantizer (unit variance, 2^b levels): root of the
+// MSE's derivative with respect to the step (reconstruction points move, cell boundaries
+// contribute nothing to first order).
+// ------------------------------------------------------------------------------------
+static double phi(double x) { return std::isfinite(x) ? std::exp(-0.5 * x * x) / std::sqrt(2.0 * M_PI) : 0.0; }
+static double Phi(double x) {
+    if (x == INFINITY) return 1.0;
+    if (x == -INFINITY) return 0.0;
+    return 0.5 * std::erfc(-x / std::sqrt(2.0));
+}
+
+static double mse_slope(double step, int levels) {
+    int half = levels / 2;
+    double total = 0.0;
+    for (int k = -half; k < half; ++k) {
+        double a = k == -half ? -INFINITY : k * step;
+        double b = k == half - 1 ? INFINITY : (k + 1) * step;
+        double c = k + 0.5;
+        total += c * (c * step * (Phi(b) - Phi(a)) - (phi(a) - phi(b)));
+    }
+    return total;
+}
+
+static double optimal_step(int bits) {
+    int levels = 1 << bits;
+    double lo = 1e-4, hi = 4.0;
+    for (int it = 0; it < 200; ++it) {
+        double mid = 0.5 * (lo + hi);
+        if (mse_slope(mid, levels) < 0.0)
+            lo = mid;
+        else
+            hi = mid;
+        if (hi - lo <= 4e-16 * hi) break;
+    }
+    return 0.5 * (lo + hi);
+}
+
+static const double* step_table() {
+    static double tab[9];
+    static bool init = false;
+    if (!init) {
+        tab[0] = 0.0;
+        for (int b = 1; b <= 8; ++b) tab[b] = optimal_step(b);
+        init = true;
+    }
+    return tab;
+}
+
+// ------------------------------------------------------------------------------------
+// derived tables and device blob
+// ------------------------------------------------------------------------------------
+static void make_pieces(const std::vector<int32_t>& bits, std::vector<Piece>& out, int& total) {
+    out.clear();
+    int off = 0;
+    for (int w = 8; w >= 1; w >>= 1)
+        for (int j = 0; j < (int)bits.size(); ++j)
+            if (bits[j] & w) {
+                out.push_back({j, w, bits[j] & (w - 1), off});
+                off += w;
+            }
+    total = off;
+}
+
+int finalize(aatc_codebook* cb) {
+    const int d = cb->d;
+    int total = -1;
+    for (size_t h = 0; h < cb->heads.size(); ++h) {
+        HeadCB& H = cb->heads[h];
+        for (int j = 0; j < d; ++j) {
+            if (H.bK[j] < 0 || H.bK[j] > 8 || H.bV[j] < 0 || H.bV[j] > 8)
+                return set_error(AATC_ERR_BUDGET, "head %zu: bits out of [0,8]", h);
+            if ((H.bK[j] > 0 && !(H.stepK[j] > 0 && std::isfinite(H.stepK[j]))) ||
+                (H.bV[j] > 0 && !(H.stepV[j] > 0 && std::isfinite(H.stepV[j]))))
+                return set_error(AATC_ERR_STATS, "head %zu channel %d: coded channel needs a positive step", h, j);
+        }
+        make_pieces(H.bK, H.pK, H.BK);
+        make_pieces(H.bV, H.pV, H.BV);
+        int B = H.BK + H.BV;
+        if (total < 0) total = B;
+        if (B != total) return set_error(AATC_ERR_BUDGET, "head %zu has %d bits per token, head 0 has %d", h, B, total);
+    }
+    if (total <= 0 || total % 2) return set_error(AATC_ERR_BUDGET, "bits per token (%d) must be a positive even number", total);
+    cb->total_bits = total;
+
+    cb->blob.assign(cb->heads.size(), DevHead());
+    for (size_t h = 0; h < cb->heads.size(); ++h) {
+        const HeadCB& H = cb->heads[h];
+        DevHead& D = cb->blob[h];
+        std::memset(&D, 0, sizeof(DevHead));
+        D.d = d;
+        D.BK = H.BK;
+        D.BV = H.BV;
+        D.nKp = (int)H.pK.size();
+        D.nVp = (int)H.pV.size();
+        for (int which = 0; which < 2; ++which) {
+            const std::vector<double>& U = which ? H.UV : H.UK;
+            const std::vector<double>& mu = which ? H.muV : H.muK;
+            float* U32 = which ? D.UV : D.UK;
+            uint16_t* hi = which ? D.UVhi : D.UKhi;
+            uint16_t* lo = which ? D.UVlo : D.UKlo;
+            float* bias = which ? D.biasV : D.biasK;
+            for (int i = 0; i < d * d; ++i) {
+                float u = (float)U[i];
+                U32[i] = u;
+                hi[i] = f32_to_bf16(u);
+                lo[i] = f32_to_bf16(u - bf16_to_f32(hi[i]));
+            }
+            for (int j = 0; j < d; ++j) {
+                double s = 0.0;
+                for (int i = 0; i < d; ++i)
+                    s += mu[i] * ((double)bf16_to_f32(hi[i * d + j]) + (double)bf16_to_f32(lo[i * d + j]));
+                bias[j] = (float)s;
+            }
+        }
+        for (int j = 0; j < d; ++j) {
+            D.muV[j] = (float)H.muV[j];
+            D.bitsK[j] = H.bK[j];
+            D.bitsV[j] = H.bV[j];
+            D.stepK[j] = H.bK[j] ? H.stepK[j] : 0.0f;
+            D.stepV[j] = H.bV[j] ? H.stepV[j] : 0.0f;
+            D.invK[j] = H.bK[j] ? (float)(1.0 / (double)H.stepK[j]) : 0.0f;
+            D.invV[j] = H.bV[j] ? (float)(1.0 / (double)H.stepV[j]) : 0.0f;
+        }
+        for (size_t p = 0; p < H.pK.size(); ++p)
+            D.pieceK[p] = H.pK[p].chan | (H.pK[p].width << 8) | (H.pK[p].shift << 12) | (H.pK[p].offset << 16);
+        for (size_t p = 0; p < H.pV.size(); ++p)
+            D.pieceV[p] = H.pV[p].chan | (H.pV[p].width << 8) | (H.pV[p].shift << 12) | (H.pV[p].offset << 16);
+    }
+    return AATC_OK;
+}
+
+static bool finite_all(const double* p, size_t n) {
+    for (size_t i = 0; i < n; ++i)
+        if (!std::isfinite(p[i])) return false;
+    return true;
+}
+
+}  // namespace aatc
+
+using namespace aatc;
+
+// ======================================================================================
+// C ABI: version / errors
+// ======================================================================================
+extern "C" int aatc_version(void) { return AATC_VERSION; }
+extern "C" int aatc_layout_version(void) { return AATC_LAYOUT_VERSION; }
+
+extern "C" const char* aatc_status_string(int s) {
+    switch (s) {
+        case AATC_OK: return "ok";
+        case AATC_ERR_INVALID_ARG: return "invalid argument";
+        case AATC_ERR_UNSUPPORTED: return "unsupported";
+        case AATC_ERR_BUDGET: return "bit budget";
+        case AATC_ERR_STATS: return "bad statistics";
+        case AATC_ERR_NO_CONVERGENCE: return "no convergence";
+        case AATC_ERR_CAPACITY: return "capacity";
+        case AATC_ERR_WORKSPACE: return "workspace too small";
+        case AATC_ERR_HIP: return "HIP error";
+        case AATC_ERR_IO: return "I/O error";
+        case AATC_ERR_VERSION: return "version mismatch";
+        default: return "unknown status";
+    }
+}
+
+extern "C" const char* aatc_last_error(void) { return g_last_error.c_str(); }
+
+// ======================================================================================
+// C ABI: statistics
+// ======================================================================================
+extern "C" int aatc_stats_from_samples(int32_t d, const float* K, const float* V, int64_t n,
+                                       const float* Q, int64_t nq, double* mu_k, double* mu_v,
+                                       double* sigma_k, double* sigma_v, double* m_q,
+                                       double* gamma_v) {
+    if (d != 64 && d != 128) return set_error(AATC_ERR_INVALID_ARG, "d must be 64 or 128 (got %d)", d);
+    if (!K || !V || !Q || !mu_k || !mu_v || !sigma_k || !sigma_v || !m_q || !gamma_v)
+        return set_error(AATC_ERR_INVALID_ARG, "null pointer");
+    if (n < 2 || nq < 1) return set_error(AATC_ERR_INVALID_ARG, "need n >= 2 samples and nq >= 1 queries");
+    for (int64_t i = 0; i < n * d; ++i)
+        if (!std::isfinite(K[i]) || !std::isfinite(V[i])) return set_error(AATC_ERR_STATS, "non-finite K/V sample");
+    for (int64_t i = 0; i < nq * d; ++i)
+        if (!std::isfinite(Q[i])) return set_error(AATC_ERR_STATS, "non-finite query sample");
+
+    // means and centred covariances (1/n)
+    for (int which = 0; which < 2; ++which) {
+        const float* X = which ? V : K;
+        double* mu = which ? mu_v : mu_k;
+        double* S = which ? sigma_v : sigma_k;
+        std::vector<double> m(d, 0.0);
+        for (int64_t i = 0; i < n; ++i)
+            for (int j = 0; j < d; ++j) m[j] += X[i * d + j];
+        for (int j = 0; j < d; ++j) m[j] /= (double)n, mu[j] = m[j];
+        std::vector<double> XT((size_t)d * n);  // centred, channel-major
+        for (int64_t i = 0; i < n; ++i)
+            for (int j = 0; j < d; ++j) XT[(size_t)j * n + i] = (double)X[i * d + j] - m[j];
+        parallel_for(d, [&](int64_t a, unsigned) {
+            const double* xa = &XT[(size_t)a * n];
+            for (int b = (int)a; b < d; ++b) {
+                const double* xb = &XT[(size_t)b * n];
+                double s = 0.0;
+                for (int64_t i = 0; i < n; ++i) s += xa[i] * xb[i];
+                S[a * d + b] = S[b * d + a] = s / (double)n;
+            }
+        });
+    }
+
+    // attention-weighted query moment and value weight (exact calibration attention)
+    unsigned nw = n_workers();
+    std::vector<std::vector<double>> MQp(nw, std::vector<double>((size_t)d * d, 0.0));
+    std::vector<double> gp(nw, 0.0);
+    std::vector<double> Kd((size_t)n * d), Vd((size_t)n * d);
+    for (int64_t i = 0; i < n * d; ++i) Kd[i] = K[i], Vd[i] = V[i];
+    const double rs = 1.0 / std::sqrt((double)d);
+    parallel_for(nq, [&](int64_t qi, unsigned t) {
+        std::vector<double> s(n), o(d, 0.0);
+        const float* q = Q + qi * d;
+        double qd[kMaxD];
+        for (int j = 0; j < d; ++j) qd[j] = q[j];
+        double mx = -INFINITY;
+        for (int64_t i = 0; i < n; ++i) {
+            double acc = 0.0;
+            const double* k = &Kd[(size_t)i * d];
+            for (int j = 0; j < d; ++j) acc += qd[j] * k[j];
+            s[i] = acc * rs;
+            mx = std::max(mx, s[i]);
+        }
+        double z = 0.0;
+        for (int64_t i = 0; i < n; ++i) z += (s[i] = std::exp(s[i] - mx));
+        for (int64_t i = 0; i < n; ++i) s[i] /= z;
+        for (int64_t i = 0; i < n; ++i) {
+            const double* v = &Vd[(size_t)i * d];
+            for (int j = 0; j < d; ++j) o[j] += s[i] * v[j];
+        }
+        double g = 0.0, a2 = 0.0;
+        for (int64_t i = 0; i < n; ++i) {
+            const double* v = &Vd[(size_t)i * d];
+            double r = 0.0;
+            for (int j = 0; j < d; ++j) r += (v[j] - o[j]) * (v[j] - o[j]);
+            g += s[i] * s[i] * r;
+            a2 += s[i] * s[i];
+        }
+        std::vector<double>& M = MQp[t];
+        for (int a = 0; a < d; ++a)
+            for (int b = 0; b < d; ++b) M[(size_t)a * d + b] += g * qd[a] * qd[b];
+        gp[t] += a2;
+    });
+    for (int i = 0; i < d * d; ++i) {
+        double s = 0.0;
+        for (unsigned t = 0; t < nw; ++t) s += MQp[t][i];
+        m_q[i] = s / (double)nq;
+    }
+    double g = 0.0;
+    for (unsigned t = 0; t < nw; ++t) g += gp[t];
+    *gamma_v = g / (double)nq;
+    return AATC_OK;
+}
+
+// ======================================================================================
+// C ABI: calibration
+// ======================================================================================
+extern "C" int aatc_calibrate(int32_t d, int32_t n_layers, int32_t n_kv, int32_t group,
+                              const aatc_head_stats* stats, const aatc_calib_params* p,
+                              aatc_codebook** out) {
+    if (!out || !stats || !p) return set_error(AATC_ERR_INVALID_ARG, "null pointer");
+    *out = nullptr;
+    if (d != 64 && d != 128) return set_error(AATC_ERR_INVALID_ARG, "d must be 64 or 128 (got %d)", d);
+    if (n_layers < 1 || n_kv < 1 || group < 1 || group > 16)
+        return set_error(AATC_ERR_INVALID_ARG, "need n_layers >= 1, n_kv >= 1, 1 <= group <= 16");
+    int max_bits = p->max_bits ? p->max_bits : 8;
+    if (max_bits < 1 || max_bits > 8) return set_error(AATC_ERR_INVALID_ARG, "max_bits must be in [1,8]");
+    double totf = 2.0 * d * p->avg_bits;
+    int total = (int)std::llround(totf);
+    if (!(p->avg_bits > 0) || std::fabs(totf - total) > 1e-9 || total % 2 || total > 2 * d * max_bits)
+        return set_error(AATC_ERR_BUDGET, "2*d*avg_bits = %g must be an even integer in (0, %d]", totf, 2 * d * max_bits);
+    const int sweeps = p->max_sweeps > 0 ? p->max_sweeps : 60;
+    const int n_heads = n_layers * n_kv;
+
+    auto* cb = new aatc_codebook();
+    cb->d = d;
+    cb->n_layers = n_layers;
+    cb->n_kv = n_kv;
+    cb->group = group;
+    cb->avg_bits = p->avg_bits;
+    cb->max_bits = max_bits;
+    cb->joint = p->joint ? 1 : 0;
+    cb->heads.resize(n_heads);
+    std::vector<int> status(n_heads, AATC_OK);
+    std::vector<std::string> msg(n_heads);
+    const double* steps = step_table();
+
+    parallel_for(n_heads, [&](int64_t h, unsigned) {
+        const aatc_head_stats& S = stats[h];
+        HeadCB& H = cb->heads[h];
+        if (!S.mu_k || !S.mu_v || !S.sigma_k || !S.sigma_v || !S.m_q) {
+            status[h] = AATC_ERR_INVALID_ARG;
+            msg[h] = "null statistics pointer";
+            return;
+        }
+        if (!finite_all(S.mu_k, d) || !finite_all(S.mu_v, d) || !finite_all(S.sigma_k, (size_t)d * d) ||
+            !finite_all(S.sigma_v, (size_t)d * d) || !finite_all(S.m_q, (size_t)d * d) ||
+            !std::isfinite(S.gamma_v) || S.gamma_v < 0) {
+            status[h] = AATC_ERR_STATS;
+            msg[h] = "non-finite statistics";
+            return;
+        }
+        int rc = jacobi_eigen(d, S.sigma_k, sweeps, H.lamK, H.UK);
+        if (rc == AATC_OK) rc = jacobi_eigen(d, S.sigma_v, sweeps, H.lamV, H.UV);
+        if (rc != AATC_OK) {
+            status[h] = rc;
+            msg[h] = aatc_last_error();
+            return;
+        }
+        // a PSD covariance has no significantly negative eigenvalue (clamped to 0 above)
+        H.muK.assign(S.mu_k, S.mu_k + d);
+        H.muV.assign(S.mu_v, S.mu_v + d);
+        H.xK.assign(d, 0.0);
+        H.xV.assign(d, 0.0);
+        for (int j = 0; j < d; ++j) {
+            double w = 0.0;
+            for (int a = 0; a < d; ++a) {
+                double ua = H.UK[(size_t)a * d + j];
+                if (ua == 0.0) continue;
+                double r = 0.0;
+                for (int b = 0; b < d; ++b) r += S.m_q[(size_t)a * d + b] * H.UK[(size_t)b * d + j];
+                w += ua * r;
+            }
+            H.xK[j] = std::max(0.0, H.lamK[j] * w / d);
+            H.xV[j] = std::max(0.0, H.lamV[j] * S.gamma_v);
+        }
+        std::vector<double> xall(H.xK);
+        xall.insert(xall.end(), H.xV.begin(), H.xV.end());
+        H.theta = waterfill_theta(xall, total, max_bits);
+        H.bK.assign(d, 0);
+        H.bV.assign(d, 0);
+        if (cb->joint) {
+            const std::vector<double>* groups[2] = {&H.xK, &H.xV};
+            int gid[2] = {0, 1};
+            std::vector<int32_t>* outs[2] = {&H.bK, &H.bV};
+            allocate_bits(groups, 2, gid, total, max_bits, outs);
+        } else {
+            const std::vector<double>* gk[2] = {&H.xK, nullptr};
+            const std::vector<double>* gv[2] = {&H.xV, nullptr};
+            int idk[2] = {0, 0}, idv[2] = {1, 1};
+            std::vector<int32_t>* ok[2] = {&H.bK, nullptr};
+            std::vector<int32_t>* ov[2] = {&H.bV, nullptr};
+            allocate_bits(gk, 1, idk, total / 2, max_bits, ok);
+            allocate_bits(gv, 1, idv, total / 2, max_bits, ov);
+        }
+        H.stepK.assign(d, 0.0f);
+        H.stepV.assign(d, 0.0f);
+        for (int j = 0; j < d; ++j) {
+            if (H.bK[j]) H.stepK[j] = (float)(steps[H.bK[j]] * std::sqrt(H.lamK[j]));
+            if (H.bV[j]) H.stepV[j] = (float)(steps[H.bV[j]] * std::sqrt(H.lamV[j]));
+        }
+    });
+    for (int h = 0; h < n_heads; ++h)
+        if (status[h] != AATC_OK) {
+            delete cb;
+            return set_error(status[h], "head %d: %s", h, msg[h].c_str());
+        }
+    int rc = finalize(cb);
+    if (rc != AATC_OK) {
+        delete cb;
+        return rc;
+    }
+    *out = cb;
+    return AATC_OK;
+}
+
+extern "C" int aatc_codebook_create(int32_t d, int32_t n_layers, int32_t n_kv, int32_t group,
+                                    const double* U_k, const double* U_v, const double* mu_k,
+                                    const double* mu_v, const int32_t* bits_k, const int32_t* bits_v,
+                                    const float* step_k, const float* step_v, aatc_codebook** out) {
+    if (!out) return set_error(AATC_ERR_INVALID_ARG, "null pointer");
+    *out = nullptr;
+    if (d != 64 && d != 128) return set_error(AATC_ERR_INVALID_ARG, "d must be 64 or 128 (got %d)", d);
+    if (n_layers < 1 || n_kv < 1 || group < 1 || group > 16)
+        return set_error(AATC_ERR_INVALID_ARG, "need n_layers >= 1, n_kv >= 1, 1 <= group <= 16");
+    if (!U_k || !U_v || !mu_k || !mu_v || !bits_k || !bits_v || !step_k || !step_v)
+        return set_error(AATC_ERR_INVALID_ARG, "null pointer");
+    const int n_heads = n_layers * n_kv;
+    auto* cb = new aatc_codebook();
+    cb->d = d;
+    cb->n_layers = n_layers;
+    cb->n_kv = n_kv;
+    cb->group = group;
+    cb->heads.resize(n_heads);
+    const size_t dd = (size_t)d * d;
+    for (int h = 0; h < n_heads; ++h) {
+        HeadCB& H = cb->heads[h];
+        H.UK.assign(U_k + h * dd, U_k + (h + 1) * dd);
+        H.UV.assign(U_v + h * dd, U_v + (h + 1) * dd);
+        H.muK.assign(mu_k + (size_t)h * d, mu_k + (size_t)(h + 1) * d);
+        H.muV.assign(mu_v + (size_t)h * d, mu_v + (size_t)(h + 1) * d);
+        H.bK.assign(bits_k + (size_t)h * d, bits_k + (size_t)(h + 1) * d);
+        H.bV.assign(bits_v + (size_t)h * d, bits_v + (size_t)(h + 1) * d);
+        H.stepK.assign(step_k + (size_t)h * d, step_k + (size_t)(h + 1) * d);
+        H.stepV.assign(step_v + (size_t)h * d, step_v + (size_t)(h + 1) * d);
+        if (!finite_all(H.UK.data(), dd) || !finite_all(H.UV.data(), dd) || !finite_all(H.muK.data(), d) ||
+            !finite_all(H.muV.data(), d)) {
+            delete cb;
+            return set_error(AATC_ERR_INVALID_ARG, "head %d: non-finite basis or mean", h);
+        }
+    }
+    int rc = finalize(cb);
+    if (rc != AATC_OK) {
+        delete cb;
+        return rc;
+    }
+    cb->avg_bits = cb->total_bits / (2.0 * d);
+    *out = cb;
+    return AATC_OK;
+}
+
+extern "C" int aatc_codebook_info(const aatc_codebook* cb, int32_t* d, int32_t* n_layers, int32_t* n_kv,
+                                  int32_t* group, int32_t* total_bits, int32_t* tile_bytes) {
+    if (!cb) return set_error(AATC_ERR_INVALID_ARG, "null codebook");
+    if (d) *d = cb->d;
+    if (n_layers) *n_layers = cb->n_layers;
+    if (n_kv) *n_kv = cb->n_kv;
+    if (group) *group = cb->group;
+    if (total_bits) *total_bits = cb->total_bits;
+    if (tile_bytes) *tile_bytes = 8 * cb->total_bits;
+    return AATC_OK;
+}
+
+template <class T, class S>
+static void copy_out(T* dst, const std::vector<S>& src) {
+    if (dst)
+        for (size_t i = 0; i < src.size(); ++i) dst[i] = (T)src[i];
+}
+
+extern "C" int aatc_codebook_head(const aatc_codebook* cb, int32_t head, double* U_k, double* U_v,
+                                  double* lam_k, double* lam_v, double* mu_k, double* mu_v, double* x_k,
+                                  double* x_v, int32_t* bits_k, int32_t* bits_v, float* step_k,
+                                  float* step_v, double* theta) {
+    if (!cb) return set_error(AATC_ERR_INVALID_ARG, "null codebook");
+    if (head < 0 || head >= (int)cb->heads.size()) return set_error(AATC_ERR_INVALID_ARG, "head %d out of range", head);
+    const HeadCB& H = cb->heads[head];
+    const int d = cb->d;
+    copy_out(U_k, H.UK);
+    copy_out(U_v, H.UV);
+    if (lam_k) std::fill(lam_k, lam_k + d, 0.0), copy_out(lam_k, H.lamK);
+    if (lam_v) std::fill(lam_v, lam_v + d, 0.0), copy_out(lam_v, H.lamV);
+    copy_out(mu_k, H.muK);
+    copy_out(mu_v, H.muV);
+    if (x_k) std::fill(x_k, x_k + d, 0.0), copy_out(x_k, H.xK);
+    if (x_v) std::fill(x_v, x_v + d, 0.0), copy_out(x_v, H.xV);
+    copy_out(bits_k, H.bK);
+    copy_out(bits_v, H.bV);
+    copy_out(step_k, H.stepK);
+    copy_out(step_v, H.stepV);
+    if (theta) *theta = H.theta;
+    return AATC_OK;
+}
+
+extern "C" void aatc_codebook_free(aatc_codebook* cb) { delete cb; }
+
+// ======================================================================================
+// persistence: "AATCCB\0\1" magic, format/layout versions, geometry, per-head arrays,
+// FNV-1a 64 checksum of everything before it
+// ======================================================================================
+namespace {
+struct Writer {
+    std::vector<uint8_t> buf;
+    template <class T>
+    void put(const T& v) {
+        const uint8_t* p = (const uint8_t*)&v;
+        buf.insert(buf.end(), p, p + sizeof(T));
+    }
+    template <class T>
+    void vec(const std::vector<T>& v, size_t n) {
+        for (size_t i = 0; i < n; ++i) put<T>(i < v.size() ? v[i] : T(0));
+    }
+};
+struct Reader {
+    const uint8_t* p;
+    size_t n, at = 0;
+    bool ok = true;
+    template <class T>
+    T get() {
+        T v{};
+        if (at + sizeof(T) > n) {
+            ok = false;
+            return v;
+        }
+        std::memcpy(&v, p + at, sizeof(T));
+        at += sizeof(T);
+        return v;
+    }
+    template <class T>
+    void vec(std::vector<T>& v, size_t cnt) {
+        v.resize(cnt);
+        for (size_t i = 0; i < cnt; ++i) v[i] = get<T>();
+    }
+};
+uint64_t fnv1a(const uint8_t* p, size_t n) {
+    uint64_t h = 1469598103934665603ull;
+    for (size_t i = 0; i < n; ++i) h = (h ^ p[i]) * 1099511628211ull;
+    return h;
+}
+const char kMagic[8] = {'A', 'A', 'T', 'C', 'C', 'B', 0, 1};
+}  // namespace
+
+extern "C" int aatc_codebook_save(const aatc_codebook* cb, const char* path) {
+    if (!cb || !path) return set_error(AATC_ERR_INVALID_ARG, "null pointer");
+    Writer w;
+    for (char c : kMagic) w.put(c);
+    w.put<int32_t>(AATC_VERSION);
+    w.put<int32_t>(AATC_LAYOUT_VERSION);
+    w.put<int32_t>(cb->d);
+    w.put<int32_t>(cb->n_layers);
+    w.put<int32_t>(cb->n_kv);
+    w.put<int32_t>(cb->group);
+    w.put<int32_t>(cb->max_bits);
+    w.put<int32_t>(cb->joint);
+    w.put<double>(cb->avg_bits);
+    const size_t d = cb->d, dd = d * d;
+    for (const HeadCB& H : cb->heads) {
+        w.vec(H.UK, dd);
+        w.vec(H.UV, dd);
+        w.vec(H.lamK, d);
+        w.vec(H.lamV, d);
+        w.vec(H.muK, d);
+        w.vec(H.muV, d);
+        w.vec(H.xK, d);
+        w.vec(H.xV, d);
+        w.vec(H.bK, d);
+        w.vec(H.bV, d);
+        w.vec(H.stepK, d);
+        w.vec(H.stepV, d);
+        w.put<double>(H.theta);
+    }
+    w.put<uint64_t>(fnv1a(w.buf.data(), w.buf.size()));
+    FILE* f = std::fopen(path, "wb");
+    if (!f) return set_error(AATC_ERR_IO, "cannot open %s for writing", path);
+    size_t wr = std::fwrite(w.buf.data(), 1, w.buf.size(), f);
+    int cl = std::fclose(f);
+    if (wr != w.buf.size() || cl != 0) return set_error(AATC_ERR_IO, "short write to %s", path);
+    return AATC_OK;
+}
+
+extern "C" int aatc_codebook_load(const char* path, aatc_codebook** out) {
+    if (!path || !out) return set_error(AATC_ERR_INVALID_ARG, "null pointer");
+    *out = nullptr;
+    FILE* f = std::fopen(path, "rb");
+    if (!f) return set_error(AATC_ERR_IO, "cannot open %s", path);
+    std::vector<uint8_t> buf;
+    uint8_t tmp[65536];
+    size_t r;
+    while ((r = std::fread(tmp, 1, sizeof tmp, f)) > 0) buf.insert(buf.end(), tmp, tmp + r);
+    std::fclose(f);
+    if (buf.size() < 8 + 8 * 4 + 8 + 8 || std::memcmp(buf.data(), kMagic, 8) != 0)
+        return set_error(AATC_ERR_VERSION, "%s is not a codebook file", path);
+    uint64_t stored;
+    std::memcpy(&stored, buf.data() + buf.size() - 8, 8);
+    if (fnv1a(buf.data(), buf.size() - 8) != stored) return set_error(AATC_ERR_VERSION, "%s: checksum mismatch", path);
+    Reader rd{buf.data(), buf.size() - 8};
+    rd.at = 8;
+    int ver = rd.get<int32_t>(), lay = rd.get<int32_t>();
+    if (ver != AATC_VERSION || lay != AATC_LAYOUT_VERSION)
+        return set_error(AATC_ERR_VERSION, "%s: format %d/layout %d, library %d/%d", path, ver, lay, AATC_VERSION,
+                         AATC_LAYOUT_VERSION);
+    auto* cb = new aatc_codebook();
+    cb->d = rd.get<int32_t>();
+    cb->n_layers = rd.get<int32_t>();
+    cb->n_kv = rd.get<int32_t>();
+    cb->group = rd.get<int32_t>();
+    cb->max_bits = rd.get<int32_t>();
+    cb->joint = rd.get<int32_t>();
+    cb->avg_bits = rd.get<double>();
+    if (!rd.ok || (cb->d != 64 && cb->d != 128) || cb->n_layers < 1 || cb->n_kv < 1 || cb->n_layers * (int64_t)cb->n_kv > (1 << 20)) {
+        delete cb;
+        return set_error(AATC_ERR_VERSION, "%s: bad header", path);
+    }
+    const size_t d = cb->d, dd = d * d;
+    cb->heads.resize((size_t)cb->n_layers * cb->n_kv);
+    for (HeadCB& H : cb->heads) {
+        rd.vec(H.UK, dd);
+        rd.vec(H.UV, dd);
+        rd.vec(H.lamK, d);
+        rd.vec(H.lamV, d);
+        rd.vec(H.muK, d);
+        rd.vec(H.muV, d);
+        rd.vec(H.xK, d);
+        rd.vec(H.xV, d);
+        rd.vec(H.bK, d);
+        rd.vec(H.bV, d);
+        rd.vec(H.stepK, d);
+        rd.vec(H.stepV, d);
+        H.theta = rd.get<double>();
+    }
+    if (!rd.ok || rd.at != rd.n) {
+        delete cb;
+        return set_error(AATC_ERR_VERSION, "%s: truncated or oversized file", path);
+    }
+    int rc = finalize(cb);
+    if (rc != AATC_OK) {
+        delete cb;
+        return rc;
+    }
+    *out = cb;
+    return AATC_OK;
+}

@@ -1,0 +1,197 @@
+"""GPU parity of the HIP path (through the C ABI) against the oracle.
+
+Bars: packed bytes bit-exact when the encoder is fed the oracle's fp32 coefficients;
+end-to-end codes differ on at most 1e-4 of coded (token, channel) pairs and by one level;
+decode attention within 2e-3 normwise relative error (max over sequences and query heads
+of max_j |o - o_ref| / max_j |o_ref|) of the oracle run on the same packed bytes.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from util import Case, normwise_rel_err
+
+pytestmark = pytest.mark.gpu
+
+FLIP_BAR = 1e-4
+ATTN_BAR = 2e-3
+# GPU encode + GPU decode against oracle encode + oracle decode: the two caches differ by
+# the code flips the encode bar allows (one level at rounding boundaries), so the decode
+# bar does not apply; each flip moves one coefficient by one step, a small relative change
+# of the (small) attention output.  Bound used for the composition: 1e-2.
+END_TO_END_BAR = 1e-2
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    return t
+
+
+def _device_codebook(q, torch, case):
+    a = case.codebook_arrays()
+    cb = q.codebook_create(case.d, 1, case.n_kv, case.group, a["UK"], a["UV"], a["muK"], a["muV"], a["bK"],
+                           a["bV"], a["stepK"], a["stepV"])
+    blob = torch.empty(cb.device_bytes(), dtype=torch.uint8, device="cuda")
+    cb.upload(blob)
+    return cb, blob
+
+
+def _new_cache(q, torch, cb, n_seqs, max_tokens):
+    t = torch.zeros(cb.cache_bytes(1, n_seqs, max_tokens), dtype=torch.uint8, device="cuda")
+    return t, q.make_cache(t, 1, n_seqs, max_tokens)
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.parametrize("wname,ctx,chunks", [
+    ("tiny", 512, [512]),
+    ("tiny", 130, [37, 1, 60, 32]),
+    ("llama_32k", 200, [200]),
+    ("llama_32k", 300, [64, 100, 136]),
+])
+def test_encode_coeffs_bit_exact(lib, torch, wname, ctx, chunks):
+    _log(f"encode_coeffs {wname} ctx={ctx} chunks={chunks}")
+    case = Case(wname, ctx, n_calib_q=64)
+    cb, blob = _device_codebook(lib, torch, case)
+    ct, cache = _new_cache(lib, torch, cb, 1, ctx)
+    coeffs = torch.from_numpy(case.coeffs(0)).cuda()
+    pos = 0
+    for n in chunks:
+        lib.encode_coeffs(cb, blob, cache, 0, 0, pos, n, coeffs[pos:pos + n])
+        pos += n
+    torch.cuda.synchronize()
+    got = ct.cpu().numpy().reshape(case.n_kv, -1)
+    ref, _ = case.oracle_cache()
+    assert np.array_equal(got, ref[0])
+
+
+@pytest.mark.parametrize("wname,ctx,chunks", [
+    ("tiny", 512, [512]),
+    ("llama_32k", 1000, [1000]),
+    ("llama_32k", 333, [1, 127, 205]),
+])
+def test_encode_end_to_end_flips(lib, torch, wname, ctx, chunks):
+    _log(f"encode {wname} ctx={ctx} chunks={chunks}")
+    case = Case(wname, ctx, n_calib_q=64)
+    cb, blob = _device_codebook(lib, torch, case)
+    ct, cache = _new_cache(lib, torch, cb, 1, ctx)
+    K = torch.from_numpy(case.k_bits.view(np.int16)).cuda()
+    V = torch.from_numpy(case.v_bits.view(np.int16)).cuda()
+    pos = 0
+    for n in chunks:
+        lib.encode(cb, blob, cache, 0, [0], [pos], n, K[:, pos:pos + n].contiguous(), V[:, pos:pos + n].contiguous())
+        pos += n
+    torch.cuda.synchronize()
+    got = ct.cpu().numpy().reshape(case.n_kv, -1)
+    ref, codes = case.oracle_cache()
+    flips, total, worst = 0, 0, 0
+    for h, c in enumerate(case.cbs):
+        gK, gV = oracle.unpack_cache(got[h], c.bK, c.bV, ctx)
+        rK, rV = codes[(0, h)]
+        for g, r, b in ((gK, rK, c.bK), (gV, rV, c.bV)):
+            m = np.broadcast_to(b > 0, g.shape)
+            dlt = np.abs(g - r)[m]
+            flips += int((dlt > 0).sum())
+            total += int(m.sum())
+            worst = max(worst, int(dlt.max()))
+    _log(f"  flips {flips}/{total}")
+    assert worst <= 1
+    assert flips <= FLIP_BAR * total
+
+
+def test_encode_is_deterministic(lib, torch):
+    case = Case("llama_32k", 256, n_calib_q=32)
+    cb, blob = _device_codebook(lib, torch, case)
+    K = torch.from_numpy(case.k_bits.view(np.int16)).cuda()
+    V = torch.from_numpy(case.v_bits.view(np.int16)).cuda()
+    outs = []
+    for _ in range(2):
+        ct, cache = _new_cache(lib, torch, cb, 1, 256)
+        lib.encode(cb, blob, cache, 0, [0], [0], 256, K, V)
+        torch.cuda.synchronize()
+        outs.append(ct.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+
+
+def _decode(lib, torch, case, cache_host, lens, max_tokens):
+    cb, blob = _device_codebook(lib, torch, case)
+    ct, cache = _new_cache(lib, torch, cb, case.n_seqs, max_tokens)
+    ct.copy_(torch.from_numpy(cache_host.reshape(-1)))
+    ids = torch.arange(case.n_seqs, dtype=torch.int32, device="cuda")
+    ln = torch.tensor(lens, dtype=torch.int64, device="cuda")
+    qd = torch.from_numpy(case.q_bits.view(np.int16)).cuda()
+    out = torch.full((case.n_seqs, case.n_q, case.d), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((cb.decode_workspace_bytes(case.n_seqs, max(lens)) // 4,), float("nan"), dtype=torch.float32,
+                    device="cuda")
+    lib.decode_attention(cb, blob, cache, 0, ids, ln, max(lens), qd, out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("wname,ctx,n_seqs,lens", [
+    ("tiny", 512, 1, [512]),
+    ("tiny", 512, 1, [1]),
+    ("tiny", 512, 1, [65]),
+    ("tiny", 512, 3, [512, 1, 300]),
+    ("llama_32k", 1000, 1, [1000]),
+    ("llama_32k", 32768, 1, [32768]),
+])
+def test_decode_parity(lib, torch, wname, ctx, n_seqs, lens):
+    _log(f"decode {wname} ctx={ctx} lens={lens}")
+    case = Case(wname, ctx, n_seqs=n_seqs, n_calib_q=64, lens=lens)
+    cache_host, _ = case.oracle_cache()
+    got = _decode(lib, torch, case, cache_host, lens, ctx)
+    ref = case.oracle_decode(cache_host, lens)
+    err = normwise_rel_err(got, ref)
+    _log(f"  rel err {err:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= ATTN_BAR
+
+
+def test_encode_then_decode_end_to_end(lib, torch):
+    """GPU encode followed by GPU decode, against the oracle's own encode and decode."""
+    case = Case("llama_32k", 4096, n_calib_q=64)
+    cb, blob = _device_codebook(lib, torch, case)
+    ct, cache = _new_cache(lib, torch, cb, 1, 4096)
+    K = torch.from_numpy(case.k_bits.view(np.int16)).cuda()
+    V = torch.from_numpy(case.v_bits.view(np.int16)).cuda()
+    lib.encode(cb, blob, cache, 0, [0], [0], 4096, K, V)
+    ids = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ln = torch.full((1,), 4096, dtype=torch.int64, device="cuda")
+    qd = torch.from_numpy(case.q_bits.view(np.int16)).cuda()
+    out = torch.empty((1, case.n_q, case.d), dtype=torch.float32, device="cuda")
+    ws = torch.empty((cb.decode_workspace_bytes(1, 4096),), dtype=torch.uint8, device="cuda")
+    lib.decode_attention(cb, blob, cache, 0, ids, ln, 4096, qd, out, ws)
+    torch.cuda.synchronize()
+    ref_cache, _ = case.oracle_cache()
+    ref = case.oracle_decode(ref_cache)
+    err = normwise_rel_err(out.cpu().numpy(), ref)
+    _log(f"  end-to-end rel err {err:.3e}")
+    assert err <= END_TO_END_BAR
+
+
+def test_decode_argument_errors(lib, torch):
+    case = Case("tiny", 128, n_calib_q=16)
+    cb, blob = _device_codebook(lib, torch, case)
+    ct, cache = _new_cache(lib, torch, cb, 1, 128)
+    ids = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ln = torch.full((1,), 128, dtype=torch.int64, device="cuda")
+    qd = torch.zeros((1, case.n_q, case.d), dtype=torch.int16, device="cuda")
+    out = torch.empty((1, case.n_q, case.d), dtype=torch.float32, device="cuda")
+    ws = torch.empty((cb.decode_workspace_bytes(1, 128),), dtype=torch.uint8, device="cuda")
+    with pytest.raises(lib.AatcError) as e:
+        lib.decode_attention(cb, blob, cache, 0, ids, ln, 129, qd, out, ws)
+    assert e.value.status == -6
+    small = torch.empty((16,), dtype=torch.uint8, device="cuda")
+    with pytest.raises(lib.AatcError) as e:
+        lib.decode_attention(cb, blob, cache, 0, ids, ln, 128, qd, out, small)
+    assert e.value.status == -7
+    K = torch.zeros((1, 10, 1, 64), dtype=torch.int16, device="cuda")
+    with pytest.raises(lib.AatcError) as e:
+        lib.encode(cb, blob, cache, 0, [0], [120], 10, K, K)
+    assert e.value.status == -6

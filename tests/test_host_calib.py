@@ -1,0 +1,129 @@
+"""Host calibration of the library against the oracle (no GPU)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import quantized_attention_klt_amd as q
+import synth
+
+
+def _samples(wname, head=0, layer=0):
+    w = synth.WORKLOADS[wname]
+    hm = synth.head_model(w, layer, head)
+    K, V, Q = synth.calibration_samples(w, hm, layer, head)
+    return w, K.astype(np.float32), V.astype(np.float32), Q.astype(np.float32)
+
+
+@pytest.mark.parametrize("wname", ["tiny", "llama_32k"])
+def test_stats_match_oracle(wname):
+    w, K, V, Q = _samples(wname)
+    if wname != "tiny":
+        K, V, Q = K[:2048], V[:2048], Q[:256]
+    lib = q.stats_from_samples(K, V, Q)
+    ref = oracle.head_stats(K.astype(np.float64), V.astype(np.float64), Q.astype(np.float64))
+    for k in ("muK", "muV", "SigK", "SigV", "MQ"):
+        scale = np.abs(ref[k]).max()
+        assert np.abs(lib[k] - ref[k]).max() <= 1e-11 * scale, k
+    assert abs(lib["gammaV"] - ref["gammaV"]) <= 1e-12 * ref["gammaV"]
+
+
+@pytest.mark.parametrize("wname,joint", [("tiny", True), ("llama_32k", True), ("llama_32k", False)])
+def test_calibrate_matches_oracle(wname, joint):
+    w, K, V, Q = _samples(wname, head=1 if w_name_has_heads(wname) else 0)
+    st = oracle.head_stats(K.astype(np.float64), V.astype(np.float64), Q.astype(np.float64))
+    cb = q.calibrate([st], w.d, 1, 1, w.group, w.avg_bits, joint=joint)
+    ref = oracle.build_head_codebook(st, w.avg_bits, joint=joint)
+    h = cb.head(0)
+    lm = ref.lamK.max()
+    assert np.abs(h["lamK"] - ref.lamK).max() <= 1e-10 * lm
+    assert np.abs(h["lamV"] - ref.lamV).max() <= 1e-10 * ref.lamV.max()
+    # U agrees where eigenvalues are well separated (the sign rule fixes the sign)
+    for U, Ur, lam in ((h["UK"], ref.UK, ref.lamK), (h["UV"], ref.UV, ref.lamV)):
+        gap = np.minimum(np.r_[np.inf, -np.diff(lam)], np.r_[-np.diff(lam), np.inf])
+        sep = gap > 1e-6 * lam.max()
+        assert np.abs(U[:, sep] - Ur[:, sep]).max() < 1e-7
+        assert np.abs(U.T @ U - np.eye(w.d)).max() < 1e-12
+    assert np.array_equal(h["bK"], ref.bK) and np.array_equal(h["bV"], ref.bV)
+    assert h["bK"].sum() + h["bV"].sum() == int(2 * w.d * w.avg_bits)
+    assert np.allclose(h["stepK"], ref.stepK, rtol=1e-6) and np.allclose(h["stepV"], ref.stepV, rtol=1e-6)
+    assert abs(h["theta"] / ref.theta - 1) < 1e-9
+    assert np.allclose(h["xK"], ref.xK, rtol=1e-9) and np.allclose(h["xV"], ref.xV, rtol=1e-9)
+    assert cb.total_bits == int(2 * w.d * w.avg_bits) and cb.tile_bytes == 8 * cb.total_bits
+
+
+def w_name_has_heads(wname):
+    return synth.WORKLOADS[wname].n_kv > 1
+
+
+def _oracle_codebook(wname="tiny"):
+    w, K, V, Q = _samples(wname)
+    st = oracle.head_stats(K.astype(np.float64), V.astype(np.float64), Q.astype(np.float64))
+    return w, oracle.build_head_codebook(st, w.avg_bits)
+
+
+def test_codebook_create_and_persist(tmp_path):
+    w, ref = _oracle_codebook()
+    cb = q.codebook_create(w.d, 1, 1, w.group, ref.UK[None], ref.UV[None], ref.muK[None], ref.muV[None],
+                           ref.bK[None], ref.bV[None], ref.stepK[None], ref.stepV[None])
+    assert cb.total_bits == 384
+    path = str(tmp_path / "cb.bin")
+    cb.save(path)
+    cb2 = q.codebook_load(path)
+    a, b = cb.head(0), cb2.head(0)
+    for k in a:
+        assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), k
+    # a flipped byte is caught by the checksum
+    raw = bytearray(open(path, "rb").read())
+    raw[100] ^= 1
+    open(path, "wb").write(bytes(raw))
+    with pytest.raises(q.AatcError) as e:
+        q.codebook_load(path)
+    assert e.value.status == -10
+    with pytest.raises(q.AatcError) as e:
+        q.codebook_load(str(tmp_path / "missing.bin"))
+    assert e.value.status == -9
+
+
+def test_error_paths():
+    w, ref = _oracle_codebook()
+    st = oracle.head_stats(*[x.astype(np.float64) for x in _samples("tiny")[1:]])
+    with pytest.raises(q.AatcError) as e:  # 2*d*avg_bits not an even integer
+        q.calibrate([st], 64, 1, 1, 4, 2.7)
+    assert e.value.status == -3
+    with pytest.raises(q.AatcError) as e:
+        q.calibrate([st], 96, 1, 1, 4, 3.0)
+    assert e.value.status == -1
+    with pytest.raises(q.AatcError) as e:  # eigensolver sweep limit
+        q.calibrate([st], 64, 1, 1, 4, 3.0, max_sweeps=1)
+    assert e.value.status == -5
+    bad = dict(st)
+    bad["SigK"] = st["SigK"].copy()
+    bad["SigK"][0, 0] = np.nan
+    with pytest.raises(q.AatcError) as e:
+        q.calibrate([bad], 64, 1, 1, 4, 3.0)
+    assert e.value.status == -4
+    bK = ref.bK.copy()
+    bK[0] += 1  # total bits now odd and different
+    with pytest.raises(q.AatcError) as e:
+        q.codebook_create(64, 1, 1, 4, ref.UK[None], ref.UV[None], ref.muK[None], ref.muV[None], bK[None],
+                          ref.bV[None], ref.stepK[None], ref.stepV[None])
+    assert e.value.status == -3
+    with pytest.raises(q.AatcError) as e:
+        q.stats_from_samples(np.zeros((1, 64)), np.zeros((1, 64)), np.zeros((1, 64)))
+    assert e.value.status == -1
+
+
+def test_multi_head_codebook_geometry():
+    w = synth.WORKLOADS["tiny"]
+    stats = []
+    for layer in range(2):
+        for h in range(2):
+            hm = synth.head_model(w, layer, h)
+            K, V, Q = synth.calibration_samples(w, hm, layer, h)
+            stats.append(oracle.head_stats(K, V, Q[:64]))
+    cb = q.calibrate(stats, 64, 2, 2, 4, 3.0)
+    assert cb.n_layers == 2 and cb.n_kv == 2 and cb.n_heads == 4
+    assert cb.cache_bytes(2, 3, 100) == 2 * 3 * 2 * 2 * 3072
+    assert cb.device_bytes() > 0
