@@ -5,10 +5,12 @@ Packed layout (ours; the pages fix only a fixed per-token bit count, p3 abstract
 
 * The cache of one (layer, sequence, kv-head) is a run of tiles of 64 token slots.
   A tile is 8*B bytes, B = B_K + B_V = sum of all channel widths of the head.
-* Each channel of width b > 0 is split into "pieces" of power-of-two widths, one per
-  set bit of b; the piece of width w holds code bits [e, e+w) with e = b mod w.
-  Pieces are ordered by width (8, 4, 2, 1), then by KLT channel index.  O_p is the
-  sum of the widths of the pieces before p (so O_p is a multiple of w_p).
+* Each channel of width b > 0 is split into "pieces" of width 4, 2 or 1: as many 4-bit
+  pieces as fit (from the most significant bit), then a 2-bit and/or a 1-bit piece
+  (b = 8 -> 4+4, 7 -> 4+2+1, 6 -> 4+2, 5 -> 4+1, 3 -> 2+1).  The piece of width w with
+  shift e holds code bits [e, e+w).  Pieces are ordered by width (4, 2, 1), then by KLT
+  channel index, then by shift (high first).  O_p is the sum of the widths of the pieces
+  before p (so O_p is a multiple of w_p).
 * Bit n of a block is bit n%8 of byte n//8 (little endian).
 * K block (first 8*B_K bytes): token slot s holds a record of B_K bits starting at
   bit s*B_K; piece p of that token sits at record bits [O_p, O_p + w_p).
@@ -24,13 +26,27 @@ import numpy as np
 TILE = 64
 
 
+def _split(b: int):
+    """Power-of-two pieces of a b-bit code, most significant first: as many 4-bit pieces as
+    fit, then a 2-bit and/or a 1-bit piece.  Returns [(width, shift)]."""
+    out, rem = [], b
+    for w in (4, 4, 2, 1):
+        if rem >= w:
+            rem -= w
+            out.append((w, rem))
+    return out
+
+
 def pieces(bits: np.ndarray):
-    """Pieces of a head's K or V channels: list of (channel, width, shift), ordered."""
+    """Pieces of a head's K or V channels: list of (channel, width, shift), ordered by width
+    (4, 2, 1), then channel, then shift (high first)."""
     out = []
-    for w in (8, 4, 2, 1):
-        for j, b in enumerate(np.asarray(bits).tolist()):
-            if b & w:
-                out.append((j, w, b & (w - 1)))
+    blist = np.asarray(bits).tolist()
+    for w in (4, 2, 1):
+        for j, b in enumerate(blist):
+            for (pw, e) in _split(b):
+                if pw == w:
+                    out.append((j, w, e))
     return out
 
 

@@ -13,9 +13,11 @@ namespace aatc {
 constexpr int kTile = 64;        // token slots per tile
 constexpr int kMaxD = 128;       // largest head_dim
 constexpr int kMaxPieces = 512;  // >= 3 pieces per channel * 128 channels
+constexpr int kMaxQB = 32;       // score MFMA operand blocks per head (key record <= 32 words)
+constexpr int kMaxVB = 32;       // value column blocks of 16 pieces per head
 
 // One power-of-two piece of a channel's code: bits [shift, shift + width) of the code.
-// Pieces are ordered by width (8, 4, 2, 1) then by KLT channel; `offset` is the sum of the
+// Pieces are ordered by width (4, 2, 1) then by KLT channel; `offset` is the sum of the
 // widths before it (bit offset inside a token's key record, or slab index for values).
 struct Piece {
     int chan;
@@ -56,6 +58,24 @@ struct alignas(256) DevHead {
     int32_t bitsK[kMaxD], bitsV[kMaxD];
     int32_t pieceK[kMaxPieces];
     int32_t pieceV[kMaxPieces];
+    // ---- decode schedule -------------------------------------------------------------
+    // Score operand blocks ("qblocks"), nqb[0] of 4-bit mode, then nqb[1] 2-bit, nqb[2]
+    // 1-bit.  For qblock q and lane group g (lanes 16g..16g+15 of a wave), kq_dw[q][g][i]
+    // is the key-record word extracted (mode 4 uses two words, the others one; a 1-bit
+    // qblock takes half a word: bits 4*(g&1) .. of each byte lane).  kq_map[q][g][16] gives
+    // the channel and shift (chan | e << 8) of each int8 operand slot, -1 for slots that
+    // multiply zero.
+    int32_t nqb[3];
+    int32_t nvb[3];  // value column blocks of widths 4, 2, 1 (16 pieces each)
+    int32_t pad1[2];
+    int16_t kq_dw[kMaxQB][4][2];
+    int16_t kq_map[kMaxQB][4][16];
+    // value column blocks: first word of each column's slab inside the value block
+    // (padding columns repeat a real slab), and chan | e << 8 (-1 for padding)
+    int16_t vb_slab[kMaxVB][16];
+    int16_t vb_map[kMaxVB][16];
+    // value channel j -> up to 3 (column | shift << 12) entries, -1 terminated
+    int16_t chan_cols[kMaxD][4];
 };
 
 }  // namespace aatc

@@ -261,16 +261,120 @@ static const double* step_table() {
 // ------------------------------------------------------------------------------------
 // derived tables and device blob
 // ------------------------------------------------------------------------------------
+// Pieces of width 4, 2 or 1 (as many 4-bit pieces as fit from the top bit, then 2, then 1),
+// ordered by width, channel, then shift (high first).
 static void make_pieces(const std::vector<int32_t>& bits, std::vector<Piece>& out, int& total) {
     out.clear();
     int off = 0;
-    for (int w = 8; w >= 1; w >>= 1)
-        for (int j = 0; j < (int)bits.size(); ++j)
-            if (bits[j] & w) {
-                out.push_back({j, w, bits[j] & (w - 1), off});
-                off += w;
+    for (int w = 4; w >= 1; w >>= 1)
+        for (int j = 0; j < (int)bits.size(); ++j) {
+            int rem = bits[j];
+            for (int pw : {4, 4, 2, 1}) {
+                if (rem < pw) continue;
+                rem -= pw;
+                if (pw == w) {
+                    out.push_back({j, w, rem, off});
+                    off += w;
+                }
             }
+        }
     total = off;
+}
+
+// Decode schedule of one head (see DevHead): which key-record words each lane group
+// unpacks for each score MFMA, which channel/shift each int8 slot carries, and the value
+// pieces grouped into MFMA column blocks of one width.
+static int build_decode_schedule(const HeadCB& H, DevHead& D) {
+    for (int q = 0; q < kMaxQB; ++q)
+        for (int g = 0; g < 4; ++g) {
+            D.kq_dw[q][g][0] = D.kq_dw[q][g][1] = 0;
+            for (int i = 0; i < 16; ++i) D.kq_map[q][g][i] = -1;
+        }
+    // key record: bit position -> (width, chan | e << 8) of the piece starting there
+    std::vector<int> at_w(H.BK + 1, 0), at_id(H.BK + 1, -1);
+    int n_w[3] = {0, 0, 0}, o_w[3] = {-1, -1, -1};
+    for (const Piece& p : H.pK) {
+        at_w[p.offset] = p.width;
+        at_id[p.offset] = p.chan | (p.shift << 8);
+        int m = p.width == 4 ? 0 : p.width == 2 ? 1 : 2;
+        if (n_w[m] == 0) o_w[m] = p.offset;
+        n_w[m]++;
+    }
+    auto field = [&](int bit, int w) -> int16_t {
+        if (bit < 0 || bit >= H.BK || at_w[bit] != w) return -1;
+        return (int16_t)at_id[bit];
+    };
+    int q = 0;
+    const int width_of[3] = {4, 2, 1};
+    const int words_per_qb[3] = {8, 4, 2};
+    for (int m = 0; m < 3; ++m) {
+        std::vector<int> dws;
+        if (n_w[m]) {
+            int w = width_of[m];
+            int first = o_w[m] / 32, last = (o_w[m] + n_w[m] * w - 1) / 32;
+            for (int r = first; r <= last; ++r) dws.push_back(r);
+        }
+        int nq = ((int)dws.size() + words_per_qb[m] - 1) / words_per_qb[m];
+        D.nqb[m] = nq;
+        for (int k = 0; k < nq; ++k, ++q) {
+            if (q >= kMaxQB) return AATC_ERR_UNSUPPORTED;
+            for (int g = 0; g < 4; ++g) {
+                for (int od = 0; od < 4; ++od)
+                    for (int i = 0; i < 4; ++i) {
+                        int idx, bit;
+                        if (m == 0) {  // 4-bit: two words per group, nibble 2i + (od & 1)
+                            idx = 8 * k + 2 * g + (od >> 1);
+                            if (idx >= (int)dws.size()) continue;
+                            bit = 32 * dws[idx] + 4 * (2 * i + (od & 1));
+                        } else if (m == 1) {  // 2-bit: one word per group, crumb 4i + od
+                            idx = 4 * k + g;
+                            if (idx >= (int)dws.size()) continue;
+                            bit = 32 * dws[idx] + 2 * (4 * i + od);
+                        } else {  // 1-bit: half a word per group, bit 8i + 4(g&1) + od
+                            idx = 2 * k + (g >> 1);
+                            if (idx >= (int)dws.size()) continue;
+                            bit = 32 * dws[idx] + 8 * i + 4 * (g & 1) + od;
+                        }
+                        D.kq_map[q][g][od * 4 + i] = field(bit, width_of[m]);
+                    }
+                for (int t = 0; t < (m == 0 ? 2 : 1); ++t) {
+                    int idx = m == 0 ? 8 * k + 2 * g + t : m == 1 ? 4 * k + g : 2 * k + (g >> 1);
+                    D.kq_dw[q][g][t] = (int16_t)(idx < (int)dws.size() ? dws[idx] : 0);
+                }
+            }
+        }
+    }
+    // value column blocks
+    for (int cb = 0; cb < kMaxVB; ++cb)
+        for (int c = 0; c < 16; ++c) D.vb_slab[cb][c] = 0, D.vb_map[cb][c] = -1;
+    for (int j = 0; j < kMaxD; ++j)
+        for (int t = 0; t < 4; ++t) D.chan_cols[j][t] = -1;
+    int cb = 0;
+    for (int m = 0; m < 3; ++m) {
+        std::vector<const Piece*> ps;
+        for (const Piece& p : H.pV)
+            if (p.width == width_of[m]) ps.push_back(&p);
+        int nb = ((int)ps.size() + 15) / 16;
+        D.nvb[m] = nb;
+        for (int b = 0; b < nb; ++b, ++cb) {
+            if (cb >= kMaxVB) return AATC_ERR_UNSUPPORTED;
+            for (int c = 0; c < 16; ++c) {
+                int i = 16 * b + c;
+                const Piece* p = i < (int)ps.size() ? ps[i] : ps[16 * b];
+                D.vb_slab[cb][c] = (int16_t)(2 * p->offset);
+                if (i < (int)ps.size()) {
+                    D.vb_map[cb][c] = (int16_t)(p->chan | (p->shift << 8));
+                    int col = 16 * cb + c;
+                    for (int t = 0; t < 3; ++t)
+                        if (D.chan_cols[p->chan][t] < 0) {
+                            D.chan_cols[p->chan][t] = (int16_t)(col | (p->shift << 12));
+                            break;
+                        }
+                }
+            }
+        }
+    }
+    return AATC_OK;
 }
 
 int finalize(aatc_codebook* cb) {
@@ -337,6 +441,8 @@ int finalize(aatc_codebook* cb) {
             D.pieceK[p] = H.pK[p].chan | (H.pK[p].width << 8) | (H.pK[p].shift << 12) | (H.pK[p].offset << 16);
         for (size_t p = 0; p < H.pV.size(); ++p)
             D.pieceV[p] = H.pV[p].chan | (H.pV[p].width << 8) | (H.pV[p].shift << 12) | (H.pV[p].offset << 16);
+        int rc = build_decode_schedule(H, D);
+        if (rc != AATC_OK) return set_error(rc, "head %zu: %s", h, "decode schedule exceeds kernel limits");
     }
     return AATC_OK;
 }

@@ -139,7 +139,10 @@ def _decode(lib, torch, case, cache_host, lens, max_tokens):
     ("tiny", 512, 1, [65]),
     ("tiny", 512, 3, [512, 1, 300]),
     ("llama_32k", 1000, 1, [1000]),
+    ("llama_32k", 16400, 1, [16400]),
     ("llama_32k", 32768, 1, [32768]),
+    ("llama_batch", 700, 3, [700, 64, 129]),
+    ("qwen_128k", 2000, 1, [2000]),
 ])
 def test_decode_parity(lib, torch, wname, ctx, n_seqs, lens):
     _log(f"decode {wname} ctx={ctx} lens={lens}")

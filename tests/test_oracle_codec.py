@@ -50,11 +50,25 @@ def _pack_bit_by_bit(codesK, codesV, bK, bV):
             buf[bit_index // 8] |= 1 << (bit_index % 8)
 
     def plist(bits):
+        # widths 4, 2, 1; a channel's pieces taken greedily from its top bit
+        per = {}
+        for j in range(len(bits)):
+            rem, lst = bits[j], []
+            while rem >= 4:
+                rem -= 4
+                lst.append((4, rem))
+            if rem >= 2:
+                rem -= 2
+                lst.append((2, rem))
+            if rem == 1:
+                lst.append((1, 0))
+            per[j] = lst
         out = []
-        for w in (8, 4, 2, 1):
+        for w in (4, 2, 1):
             for j in range(len(bits)):
-                if bits[j] & w:
-                    out.append((j, w, bits[j] % w))
+                for (pw, e) in per[j]:
+                    if pw == w:
+                        out.append((j, w, e))
         return out
 
     for t in range(n):
@@ -105,6 +119,15 @@ def test_tile_size_and_zero_padding():
     # V block starts at byte 40: pieces (ch1 w2)=3 slot0 at bit 0..1; (ch0 w1)=1 at slab 64*2
     assert t[40] == 0b11 and t[40 + 16] == 1
     assert t.sum() == 0b11111 + 0b11 + 1
+
+
+def test_eight_bit_code_is_two_nibbles():
+    bK = np.array([8, 1])
+    bV = np.array([2, 1])
+    assert oracle.pieces(bK) == [(0, 4, 4), (0, 4, 0), (1, 1, 0)]
+    t = oracle.pack_cache(np.array([[0xA5, 1]]), np.array([[2, 1]]), bK, bV)
+    # record: high nibble 0xA at bits 0..3, low nibble 0x5 at bits 4..7, then the 1-bit piece
+    assert t[0] == 0x5A and t[1] == 1
 
 
 # ---------------------------------------------------------------- attention
