@@ -183,7 +183,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "i8+f32",
         "data": "synthetic",
         "config": {"workload": "llama3.1-8b-attention-layer", "kv_heads": w.n_kv, "q_heads": w.n_q,
                    "head_dim": w.d, "ctx": ctx, "batch": 1, "bits_per_element": w.avg_bits,

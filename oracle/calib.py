@@ -136,41 +136,66 @@ def waterfill_theta(x: np.ndarray, total_bits: float, max_bits: int = 8):
     return math.exp(lt), rate(lt)
 
 
+def _greedy(groups, budget: int, max_bits: int):
+    """The `budget` largest marginal gains x_j 4^(-k), k < max_bits, over the channels of
+    `groups` [(group id, x)]; ties: lower group id, then lower channel, then lower k.
+    Returns {group id: bits}."""
+    cand = []
+    for gi, x in groups:
+        for j in range(x.size):
+            for k in range(max_bits):
+                cand.append((-(x[j] * 4.0 ** (-k)), gi, j, k))
+    cand.sort()
+    bits = {gi: np.zeros(x.size, np.int64) for gi, x in groups}
+    for c in cand[:budget]:
+        bits[c[1]][c[2]] += 1
+    return bits
+
+
+def _cost(x, b):
+    return float(sum(xi * 4.0 ** (-int(bi)) for xi, bi in zip(x.tolist(), b.tolist())))
+
+
 def allocate_bits(xK: np.ndarray, xV: np.ndarray, total_bits: int, max_bits: int = 8,
-                  joint: bool = True):
+                  joint: bool = True, key_align: int = 1):
     """Integer bits per channel under an exact budget (reading of p2's water-filling
     "rounded to integers under the budget").
 
     Distortion model: channel j at b bits costs x_j 4^(-b).  The marginal gain of the
-    (k+1)-th bit is proportional to x_j 4^(-k); taking the total_bits largest gains
-    (k < max_bits) gives the exact-budget optimum of the separable convex problem.
-    Ties: keys before values, then lower channel index, then lower k.
-    joint=False splits the budget evenly between keys and values.
+    (k+1)-th bit is proportional to x_j 4^(-k); taking the largest gains (k < max_bits)
+    gives the exact-budget optimum of the separable convex problem (ties: keys before
+    values, then lower channel index, then lower k).
+
+    key_align: the keys' total bits must be a multiple of key_align (the packed layout
+    keeps each token's key record in whole 32-bit words, key_align = 32).  The result is
+    the optimum over such splits: for every admissible key budget B_K the key and value
+    sub-problems are solved exactly, and the split of least total cost is taken (ties:
+    the smaller B_K).  joint=False gives keys and values total_bits/2 each.
     """
     xK = np.asarray(xK, np.float64)
     xV = np.asarray(xV, np.float64)
     d = xK.size
-
-    def greedy(groups, budget):
-        cand = []
-        for gi, x in groups:
-            for j in range(x.size):
-                for k in range(max_bits):
-                    cand.append((-(x[j] * 4.0 ** (-k)), gi, j, k))
-        cand.sort()
-        bits = {gi: np.zeros(x.size, np.int64) for gi, x in groups}
-        for c in cand[:budget]:
-            bits[c[1]][c[2]] += 1
-        return bits
-
-    if joint:
-        assert 0 <= total_bits <= 2 * d * max_bits
-        b = greedy([(0, xK), (1, xV)], int(total_bits))
+    if not joint:
+        assert total_bits % 2 == 0 and (total_bits // 2) % key_align == 0
+        return (_greedy([(0, xK)], total_bits // 2, max_bits)[0],
+                _greedy([(1, xV)], total_bits // 2, max_bits)[1])
+    assert 0 <= total_bits <= 2 * d * max_bits
+    if key_align == 1:
+        b = _greedy([(0, xK), (1, xV)], int(total_bits), max_bits)
         return b[0], b[1]
-    assert total_bits % 2 == 0
-    bk = greedy([(0, xK)], total_bits // 2)[0]
-    bv = greedy([(1, xV)], total_bits // 2)[1]
-    return bk, bv
+    best = None
+    for bk_total in range(0, min(total_bits, d * max_bits) + 1, key_align):
+        bv_total = total_bits - bk_total
+        if bv_total > d * max_bits:
+            continue
+        bK = _greedy([(0, xK)], bk_total, max_bits)[0]
+        bV = _greedy([(1, xV)], bv_total, max_bits)[1]
+        cost = _cost(xK, bK) + _cost(xV, bV)
+        if best is None or cost < best[0]:
+            best = (cost, bK, bV)
+    if best is None:
+        raise ValueError("no admissible key/value split of the budget")
+    return best[1], best[2]
 
 
 # ----------------------------------------------------------------------------------------
@@ -291,10 +316,14 @@ def step_table(max_bits: int = 8) -> np.ndarray:
     return _STEP_CACHE[max_bits]
 
 
+KEY_ALIGN = 32  # key bits per token are kept a multiple of one 32-bit word
+
+
 def build_head_codebook(stats: dict, avg_bits: float, max_bits: int = 8,
                         joint: bool = True) -> HeadCodebook:
     """Calibrate one head: KLT of both covariances, weights, exact-budget integer bits
-    with total 2 d avg_bits, and fp32 steps step_b * sqrt(lambda_j)."""
+    with total 2 d avg_bits (key bits a multiple of 32), and fp32 steps
+    step_b * sqrt(lambda_j)."""
     d = stats["d"]
     total = 2.0 * d * avg_bits
     B = int(round(total))
@@ -304,7 +333,7 @@ def build_head_codebook(stats: dict, avg_bits: float, max_bits: int = 8,
     lamV, UV = klt(stats["SigV"])
     xK, xV = channel_weights(stats, UK, lamK, UV, lamV)
     theta, _ = waterfill_theta(np.concatenate([xK, xV]), B, max_bits)
-    bK, bV = allocate_bits(xK, xV, B, max_bits, joint)
+    bK, bV = allocate_bits(xK, xV, B, max_bits, joint, key_align=KEY_ALIGN)
     st = step_table(max_bits)
     stepK = np.where(bK > 0, st[bK] * np.sqrt(lamK), 0.0).astype(np.float32)
     stepV = np.where(bV > 0, st[bV] * np.sqrt(lamV), 0.0).astype(np.float32)

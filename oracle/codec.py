@@ -12,8 +12,9 @@ Packed layout (ours; the pages fix only a fixed per-token bit count, p3 abstract
   channel index, then by shift (high first).  O_p is the sum of the widths of the pieces
   before p (so O_p is a multiple of w_p).
 * Bit n of a block is bit n%8 of byte n//8 (little endian).
-* K block (first 8*B_K bytes): token slot s holds a record of B_K bits starting at
-  bit s*B_K; piece p of that token sits at record bits [O_p, O_p + w_p).
+* K block (first 8*B_K bytes; B_K is a multiple of 32): each token slot s has a record
+  of B_K bits, piece p at record bits [O_p, O_p + w_p).  Record word r (bits
+  [32r, 32r+32)) of slot s is word 64*r + s of the K block.
 * V block (next 8*B_V bytes): piece p owns a slab of 64*w_p bits starting at bit
   64*O_p.  Slab word r (32 bits) holds token slots r*(32/w) + k, k < 32/w, with slot
   k's field at word bits [8*(k%4) + w*(k//4), +w).
@@ -103,6 +104,8 @@ def pack_cache(codesK: np.ndarray, codesV: np.ndarray, bK: np.ndarray, bV: np.nd
     """Pack codes of tokens 0..n-1 (KLT channel order) into tiles; returns uint8 bytes."""
     n = codesK.shape[0]
     BK, BV = record_bits(bK), record_bits(bV)
+    if BK % 32:
+        raise ValueError("key bits per token must be a multiple of 32")
     if n_tiles is None:
         n_tiles = (n + TILE - 1) // TILE
     kbits = 64 * BK
@@ -114,7 +117,8 @@ def pack_cache(codesK: np.ndarray, codesV: np.ndarray, bK: np.ndarray, bV: np.nd
     off = 0
     for (j, w, e) in pieces(bK):
         vals = (codesK[:, j] >> e) & ((1 << w) - 1)
-        pos = tile[:, None] * tbits + slot[:, None] * BK + off + np.arange(w)[None, :]
+        rbit = off + np.arange(w)[None, :]
+        pos = tile[:, None] * tbits + 32 * ((rbit // 32) * 64 + slot[:, None]) + rbit % 32
         bitarr[pos] = _field_bits(vals, w)
         off += w
     off = 0
@@ -143,10 +147,11 @@ def unpack_cache(cache: np.ndarray, bK: np.ndarray, bV: np.ndarray, n: int):
     tile = tok // TILE
     slot = tok % TILE
     cK = np.zeros((n, d), np.int64)
-    cV = np.zeros((n, d), np.int64)
+    cV = np.zeros((n, len(bV)), np.int64)
     off = 0
     for (j, w, e) in pieces(bK):
-        pos = tile[:, None] * tbits + slot[:, None] * BK + off + np.arange(w)[None, :]
+        rbit = off + np.arange(w)[None, :]
+        pos = tile[:, None] * tbits + 32 * ((rbit // 32) * 64 + slot[:, None]) + rbit % 32
         weights = (1 << np.arange(w))[None, :]
         cK[:, j] += ((bitarr[pos].astype(np.int64) * weights).sum(axis=1)) << e
         off += w

@@ -15,6 +15,7 @@ constexpr int kMaxD = 128;       // largest head_dim
 constexpr int kMaxPieces = 512;  // >= 3 pieces per channel * 128 channels
 constexpr int kMaxQB = 32;       // score MFMA operand blocks per head (key record <= 32 words)
 constexpr int kMaxVB = 32;       // value column blocks of 16 pieces per head
+constexpr int kKeyAlign = 32;    // key bits per token are a multiple of one 32-bit word
 
 // One power-of-two piece of a channel's code: bits [shift, shift + width) of the code.
 // Pieces are ordered by width (4, 2, 1) then by KLT channel; `offset` is the sum of the
@@ -46,6 +47,7 @@ struct alignas(256) DevHead {
     int32_t pad0[59];
     float UK[kMaxD * kMaxD];      // fp32 basis (query transform)
     float UV[kMaxD * kMaxD];      // fp32 basis (inverse transform of values)
+    float UVt[kMaxD * kMaxD];     // its transpose, UVt[j*d + i] = UV[i*d + j]
     uint16_t UKhi[kMaxD * kMaxD]; // bf16 split of U_K: U = hi + lo (+ rounding)
     uint16_t UKlo[kMaxD * kMaxD];
     uint16_t UVhi[kMaxD * kMaxD];

@@ -182,30 +182,49 @@ static double waterfill_theta(const std::vector<double>& x, double total, int ma
     return std::exp(0.5 * (lo + hi));
 }
 
-// Exact-budget integer allocation: the `budget` largest marginal gains x_j 4^-k (k < max_bits),
-// ties broken by (keys first, lower channel, lower k).
-struct Gain {
-    double g;
-    int kv, j, k;
-};
-
-static void allocate_bits(const std::vector<double>* groups[2], int ngroups, const int* gid,
-                          int budget, int max_bits, std::vector<int32_t>* out[2]) {
+// Exact-budget integer allocation of one group of channels: the `budget` largest marginal
+// gains x_j 4^-k (k < max_bits), ties broken by lower channel then lower k.
+static std::vector<int32_t> greedy_bits(const std::vector<double>& x, int budget, int max_bits) {
+    struct Gain {
+        double g;
+        int j, k;
+    };
     std::vector<Gain> c;
-    for (int gi = 0; gi < ngroups; ++gi) {
-        const std::vector<double>& x = *groups[gi];
-        for (int j = 0; j < (int)x.size(); ++j)
-            for (int k = 0; k < max_bits; ++k) c.push_back({std::ldexp(x[j], -2 * k), gid[gi], j, k});
-    }
+    for (int j = 0; j < (int)x.size(); ++j)
+        for (int k = 0; k < max_bits; ++k) c.push_back({std::ldexp(x[j], -2 * k), j, k});
     std::sort(c.begin(), c.end(), [](const Gain& a, const Gain& b) {
         if (a.g != b.g) return a.g > b.g;
-        if (a.kv != b.kv) return a.kv < b.kv;
         if (a.j != b.j) return a.j < b.j;
         return a.k < b.k;
     });
-    for (int i = 0; i < budget && i < (int)c.size(); ++i) {
-        for (int gi = 0; gi < ngroups; ++gi)
-            if (gid[gi] == c[i].kv) (*out[gi])[c[i].j] += 1;
+    std::vector<int32_t> bits(x.size(), 0);
+    for (int i = 0; i < budget && i < (int)c.size(); ++i) bits[c[i].j] += 1;
+    return bits;
+}
+
+static double alloc_cost(const std::vector<double>& x, const std::vector<int32_t>& b) {
+    double s = 0.0;
+    for (size_t j = 0; j < x.size(); ++j) s += std::ldexp(x[j], -2 * b[j]);
+    return s;
+}
+
+// Joint allocation with the keys' total a multiple of key_align bits (whole record words):
+// every admissible key budget is solved exactly for keys and values, the cheapest split
+// wins (ties: smaller key budget).
+static void allocate_joint(const std::vector<double>& xK, const std::vector<double>& xV, int total, int max_bits,
+                           int key_align, std::vector<int32_t>& bK, std::vector<int32_t>& bV) {
+    const int d = (int)xK.size();
+    double best = INFINITY;
+    for (int bk = 0; bk <= std::min(total, d * max_bits); bk += key_align) {
+        const int bv = total - bk;
+        if (bv > d * max_bits) continue;
+        std::vector<int32_t> k = greedy_bits(xK, bk, max_bits), v = greedy_bits(xV, bv, max_bits);
+        const double cost = alloc_cost(xK, k) + alloc_cost(xV, v);
+        if (cost < best) {
+            best = cost;
+            bK = k;
+            bV = v;
+        }
     }
 }
 
@@ -391,6 +410,9 @@ int finalize(aatc_codebook* cb) {
         }
         make_pieces(H.bK, H.pK, H.BK);
         make_pieces(H.bV, H.pV, H.BV);
+        if (H.BK % kKeyAlign)
+            return set_error(AATC_ERR_BUDGET, "head %zu: key bits per token (%d) must be a multiple of %d", h, H.BK,
+                             kKeyAlign);
         int B = H.BK + H.BV;
         if (total < 0) total = B;
         if (B != total) return set_error(AATC_ERR_BUDGET, "head %zu has %d bits per token, head 0 has %d", h, B, total);
@@ -428,6 +450,8 @@ int finalize(aatc_codebook* cb) {
                 bias[j] = (float)s;
             }
         }
+        for (int i = 0; i < d; ++i)
+            for (int j = 0; j < d; ++j) D.UVt[j * d + i] = D.UV[i * d + j];
         for (int j = 0; j < d; ++j) {
             D.muV[j] = (float)H.muV[j];
             D.bitsK[j] = H.bK[j];
@@ -589,6 +613,9 @@ extern "C" int aatc_calibrate(int32_t d, int32_t n_layers, int32_t n_kv, int32_t
     int total = (int)std::llround(totf);
     if (!(p->avg_bits > 0) || std::fabs(totf - total) > 1e-9 || total % 2 || total > 2 * d * max_bits)
         return set_error(AATC_ERR_BUDGET, "2*d*avg_bits = %g must be an even integer in (0, %d]", totf, 2 * d * max_bits);
+    if (!p->joint && (total / 2) % kKeyAlign)
+        return set_error(AATC_ERR_BUDGET, "separate key/value budgets need d*avg_bits (%d) to be a multiple of %d",
+                         total / 2, kKeyAlign);
     const int sweeps = p->max_sweeps > 0 ? p->max_sweeps : 60;
     const int n_heads = n_layers * n_kv;
 
@@ -647,21 +674,11 @@ extern "C" int aatc_calibrate(int32_t d, int32_t n_layers, int32_t n_kv, int32_t
         std::vector<double> xall(H.xK);
         xall.insert(xall.end(), H.xV.begin(), H.xV.end());
         H.theta = waterfill_theta(xall, total, max_bits);
-        H.bK.assign(d, 0);
-        H.bV.assign(d, 0);
         if (cb->joint) {
-            const std::vector<double>* groups[2] = {&H.xK, &H.xV};
-            int gid[2] = {0, 1};
-            std::vector<int32_t>* outs[2] = {&H.bK, &H.bV};
-            allocate_bits(groups, 2, gid, total, max_bits, outs);
+            allocate_joint(H.xK, H.xV, total, max_bits, kKeyAlign, H.bK, H.bV);
         } else {
-            const std::vector<double>* gk[2] = {&H.xK, nullptr};
-            const std::vector<double>* gv[2] = {&H.xV, nullptr};
-            int idk[2] = {0, 0}, idv[2] = {1, 1};
-            std::vector<int32_t>* ok[2] = {&H.bK, nullptr};
-            std::vector<int32_t>* ov[2] = {&H.bV, nullptr};
-            allocate_bits(gk, 1, idk, total / 2, max_bits, ok);
-            allocate_bits(gv, 1, idv, total / 2, max_bits, ov);
+            H.bK = greedy_bits(H.xK, total / 2, max_bits);
+            H.bV = greedy_bits(H.xV, total / 2, max_bits);
         }
         H.stepK.assign(d, 0.0f);
         H.stepV.assign(d, 0.0f);

@@ -114,8 +114,8 @@ __global__ __launch_bounds__(256) void encode_kernel(const DevHead* __restrict__
         uint32_t code = codes[(s * 2 + (isK ? 0 : 1)) * d + chan];
         uint32_t val = (code >> e) & ((1u << w) - 1u);
         uint32_t pos;
-        if (isK) {
-            pos = (uint32_t)s * BK + off;
+        if (isK) {  // record word r of slot s is block word 64 r + s
+            pos = 32u * (64u * (uint32_t)(off >> 5) + (uint32_t)s) + (uint32_t)(off & 31);
         } else {
             int per = 32 / w, r = s / per, k = s % per;
             pos = 64u * BK + 64u * off + 32u * r + 8u * (k & 3) + (uint32_t)w * (k >> 2);

@@ -167,6 +167,27 @@ def test_integer_allocation_is_optimal_brute_force(seed):
     assert cost <= best[0] * (1 + 1e-12) + 1e-300
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_key_aligned_allocation_brute_force(seed):
+    """With key_align the key total is a multiple of it, and the result is the best such
+    allocation (brute force over all allocations with that property)."""
+    rng = np.random.default_rng(300 + seed)
+    xK = np.exp(rng.uniform(-4, 4, 2))
+    xV = np.exp(rng.uniform(-4, 4, 2))
+    max_bits, align = 5, 4
+    B = int(rng.integers(0, 4 * max_bits + 1))
+    bK, bV = oracle.allocate_bits(xK, xV, B, max_bits=max_bits, key_align=align)
+    assert bK.sum() % align == 0 and bK.sum() + bV.sum() == B
+    cost = sum(x * 4.0 ** (-b) for x, b in zip(list(xK) + list(xV), list(bK) + list(bV)))
+    best = None
+    for b in itertools.product(range(max_bits + 1), repeat=4):
+        if sum(b) != B or (b[0] + b[1]) % align:
+            continue
+        c = sum(xi * 4.0 ** (-bi) for xi, bi in zip(list(xK) + list(xV), b))
+        best = c if best is None else min(best, c)
+    assert cost <= best * (1 + 1e-12)
+
+
 def test_integer_allocation_properties():
     w = synth.WORKLOADS["llama_32k"]
     hm = synth.head_model(w, 0, 3)
@@ -174,17 +195,19 @@ def test_integer_allocation_properties():
     st = oracle.head_stats(K, V, Q)
     cb = oracle.build_head_codebook(st, 2.75)
     assert cb.bK.sum() + cb.bV.sum() == 704
+    assert cb.bK.sum() % 32 == 0
     assert cb.bK.min() >= 0 and cb.bK.max() <= 8 and cb.bV.max() <= 8
     # monotone in x within keys and within values
     for x, b in ((cb.xK, cb.bK), (cb.xV, cb.bV)):
         o = np.argsort(-x, kind="stable")
         assert np.all(np.diff(b[o]) <= 0)
-    # within one bit of the continuous solution for active, uncapped channels
-    x = np.concatenate([cb.xK, cb.xV])
-    b = np.concatenate([cb.bK, cb.bV])
-    theta, R = oracle.waterfill_theta(x, 704)
-    act = (R > 0) & (R < 8)
-    assert np.all(np.abs(b[act] - R[act]) <= 1.0 + 1e-9)
+        # within one bit of the continuous water-filling of the same sub-budget
+        theta, R = oracle.waterfill_theta(x, int(b.sum()))
+        act = (R > 0) & (R < 8)
+        assert np.all(np.abs(b[act] - R[act]) <= 1.0 + 1e-9)
+    # the key/value split moves at most 16 bits against the unaligned optimum
+    bK0, bV0 = oracle.allocate_bits(cb.xK, cb.xV, 704)
+    assert abs(int(cb.bK.sum()) - int(bK0.sum())) <= 16
 
 
 def test_uniform_weights_give_uniform_bits():

@@ -78,7 +78,8 @@ def _pack_bit_by_bit(codesK, codesV, bK, bV):
         for (j, w, e) in plist(bK):
             val = (codesK[t][j] >> e) & ((1 << w) - 1)
             for i in range(w):
-                put(base + s * BK + off + i, (val >> i) & 1)
+                rb = off + i  # record bit; record word r of slot s is block word 64 r + s
+                put(base + 32 * (64 * (rb // 32) + s) + rb % 32, (val >> i) & 1)
             off += w
         off = 0
         for (j, w, e) in plist(bV):
@@ -95,7 +96,7 @@ def _pack_bit_by_bit(codesK, codesV, bK, bV):
 @pytest.mark.parametrize("n", [1, 63, 64, 70, 130])
 def test_pack_matches_bit_by_bit_writer(n):
     rng = np.random.default_rng(n)
-    bK = np.array([8, 0, 7, 3, 1, 2, 5, 6, 4])
+    bK = np.array([8, 0, 7, 3, 1, 2, 5, 6, 4, 8, 7, 5, 8])  # 64 bits: two record words
     bV = np.array([1, 2, 0, 4, 8, 3, 7, 5, 6])
     cK = np.stack([rng.integers(0, 1 << b, n) if b else np.zeros(n, int) for b in bK], 1)
     cV = np.stack([rng.integers(0, 1 << b, n) if b else np.zeros(n, int) for b in bV], 1)
@@ -108,26 +109,44 @@ def test_pack_matches_bit_by_bit_writer(n):
 
 
 def test_tile_size_and_zero_padding():
-    bK = np.array([3, 2])
+    bK = np.array([8, 8, 8, 8])  # 32 bits: one record word of eight nibbles
     bV = np.array([1, 2])
-    assert oracle.tile_bytes(bK, bV) == 8 * 8
-    cK = np.array([[7, 3]])
-    cV = np.array([[1, 3]])
+    assert oracle.tile_bytes(bK, bV) == 8 * 35
+    cK = np.array([[0x12, 0x34, 0x56, 0x78], [0x9A, 0, 0, 0]])
+    cV = np.array([[1, 3], [0, 2]])
     t = oracle.pack_cache(cK, cV, bK, bV)
-    # K record of slot 0: pieces (ch0 w2 e1)=3, (ch1 w2)=3, (ch0 w1)=1 -> bits 0..4 = 11111
-    assert t[0] == 0b11111 and t[1:40].sum() == 0
-    # V block starts at byte 40: pieces (ch1 w2)=3 slot0 at bit 0..1; (ch0 w1)=1 at slab 64*2
-    assert t[40] == 0b11 and t[40 + 16] == 1
-    assert t.sum() == 0b11111 + 0b11 + 1
+    # slot 0's record word = block word 0: nibbles hi/lo of each code in channel order
+    assert t[0:4].tolist() == [0x21, 0x43, 0x65, 0x87]
+    # slot 1's record word = block word 1
+    assert t[4:8].tolist() == [0xA9, 0, 0, 0]
+    assert t[8:256].sum() == 0
+    # V block at byte 256: (ch1 w2) slab first: slot0 = 3 at bits 0..1, slot1 = 2 at bits 8..9;
+    # (ch0 w1) slab at bit 64*2: slot0 = 1 at bit 0
+    assert t[256] == 0b11 and t[257] == 0b10 and t[256 + 16] == 1
+    assert int(t.astype(np.int64).sum()) == 0x21 + 0x43 + 0x65 + 0x87 + 0xA9 + 3 + 2 + 1
+
+
+def test_two_word_records_are_word_major():
+    bK = np.array([8] * 8)  # 64 bits: record words 0 and 1
+    cK = np.zeros((3, 8), np.int64)
+    cK[2, 4] = 0xFF  # slot 2, channel 4 -> record word 1, low byte
+    t = oracle.pack_cache(cK, np.zeros((3, 1), np.int64), bK, np.array([2]))
+    w = t[:64 * 2 * 4].view(np.uint32)
+    assert w[64 * 1 + 2] == 0xFF and int(w.sum()) == 0xFF
 
 
 def test_eight_bit_code_is_two_nibbles():
-    bK = np.array([8, 1])
+    bK = np.array([8, 8, 8, 8])
     bV = np.array([2, 1])
-    assert oracle.pieces(bK) == [(0, 4, 4), (0, 4, 0), (1, 1, 0)]
-    t = oracle.pack_cache(np.array([[0xA5, 1]]), np.array([[2, 1]]), bK, bV)
-    # record: high nibble 0xA at bits 0..3, low nibble 0x5 at bits 4..7, then the 1-bit piece
-    assert t[0] == 0x5A and t[1] == 1
+    assert oracle.pieces(bK)[:2] == [(0, 4, 4), (0, 4, 0)]
+    t = oracle.pack_cache(np.array([[0xA5, 0, 0, 0]]), np.array([[2, 1]]), bK, bV)
+    # record: high nibble 0xA at bits 0..3, low nibble 0x5 at bits 4..7
+    assert t[0] == 0x5A
+
+
+def test_key_bits_must_fill_words():
+    with pytest.raises(ValueError):
+        oracle.pack_cache(np.zeros((1, 2), np.int64), np.zeros((1, 1), np.int64), np.array([3, 2]), np.array([1]))
 
 
 # ---------------------------------------------------------------- attention
