@@ -127,7 +127,7 @@ def main():
     V = torch.from_numpy(vb.view(np.int16)).to(dev)
     Qd = torch.from_numpy(qb.view(np.int16)).to(dev)
     out = torch.empty((1, w.n_q, w.d), dtype=torch.float32, device=dev)
-    ws = torch.empty(cb.decode_workspace_bytes(1, ctx), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(cb.decode_workspace_bytes(1, ctx), dtype=torch.uint8, device=dev)
     ids = torch.zeros(1, dtype=torch.int32, device=dev)
     lens = torch.full((1,), ctx, dtype=torch.int64, device=dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)

@@ -6,27 +6,34 @@
 // inverse-transformed once per query head); "Spend Bits Where Queries Look" abstract
 // (decoding reads the whole cache every step and is bandwidth-bound).
 //
-// Two kernels, both on the caller's stream:
-//   qprep   : q' = U_K^T q per query head, scaled by the key steps (and log2 e / sqrt d),
-//             split into three int8 digits and laid out as the A operands of the score
-//             MFMAs of each kv-head (slot order = the key unpack schedule); clears the
-//             completion counters used by the decode kernel.
-//   decode  : a workgroup of 4 waves streams a run of 64-token tiles of one (sequence,
-//             kv-head) through LDS (direct global->LDS loads, double-buffered) and works on
-//             each tile cooperatively:
-//               scores  - wave w takes tokens 16w..16w+15: key pieces are unpacked with
-//                         SWAR shift/mask into int8 operands of v_mfma_i32_16x16x64_i8;
-//                         MFMA rows are 4*head + digit, so a lane holds the three digit
-//                         rows of one head and combines them in registers;
-//               softmax - per-head tile maxima meet in LDS; every wave keeps the same
-//                         online reference maximum (base 2, raised lazily with headroom);
-//                         probabilities become three int8 digits in LDS;
-//               values  - wave w takes value column blocks w, w+4, ... over all 64 tokens
-//                         and accumulates P x pieces in int32 with the same MFMA.
-//             Each wave holds a quarter of the value accumulators, which keeps registers
-//             low enough for four waves per SIMD.  The workgroup writes one partial
-//             (max, sum, accumulator); the last workgroup of each (sequence, kv-head)
-//             merges them, dequantises the value coefficients and applies U_V and mu_V.
+// Two kernels on the caller's stream:
+//   qprep  - one workgroup per (sequence, kv-head) forms q' = U_K^T q for its query
+//            heads, scales it by the key steps (and log2 e / sqrt d) and splits it into
+//            three int8 digits laid out as the A operands of the score MFMAs (slot order =
+//            the key unpack schedule).
+//   decode - a workgroup of 4 waves owns a run of 64-token tiles of one (sequence,
+//            kv-head):
+//   prologue - the query operands, the channel map and the first tiles stream into LDS
+//              (direct global->LDS loads); the operands then stay in registers.
+//   tiles    - the four waves work on each tile together:
+//                scores  - wave w takes tokens 16w..16w+15: key pieces are unpacked with
+//                          SWAR shift/mask into int8 operands of v_mfma_i32_16x16x64_i8;
+//                          MFMA rows are 4*head + digit, so a lane holds the three digit
+//                          rows of one head and combines them in registers;
+//                softmax - per-head tile maxima meet in LDS; every wave keeps the same
+//                          online reference maximum (base 2, raised lazily with headroom);
+//                          probabilities become three int8 digits in LDS;
+//                values  - wave w takes value column blocks w, w+4, ... over all 64
+//                          tokens and accumulates P x pieces in int32 with the same MFMA.
+//              Barriers only order LDS; the ring keeps up to nb-1 tiles in flight and each
+//              wave waits on its own load count.
+//   merge    - each workgroup writes one partial (max, sum, coefficient accumulator per
+//              query head) with device-coherent stores; the last workgroup of each group
+//              of partials merges them, and the last group merger of each (sequence,
+//              kv-head) merges the group results, dequantises the value coefficients and
+//              applies U_V and mu_V.  Arrival counters wrap to zero on the last arrival
+//              (atomic increment modulo the member count), so a zeroed workspace stays
+//              ready for the next call.
 // Inner loops are branch-free straight-line code (compile-time bounds NQB score operand
 // blocks and NVB value column blocks; the unpack mode of a block is a uniform select).
 #include <hip/hip_runtime.h>
@@ -50,7 +57,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kWaves = 4;            // waves per workgroup
-constexpr int kTargetGroups = 1024;  // workgroups per launch (4 per CU on 256 CUs)
+constexpr int kMergeGroup = 16;      // partials per first-level merge
+// Arrival counters occupy a fixed table at the start of the workspace, whatever the call's
+// shape, so counters a call leaves at zero are never overwritten by another call's partials.
+constexpr int kCounterSlots = 32768;
+constexpr size_t kCounterBytes = kCounterSlots * sizeof(uint32_t);
 constexpr float kHeadroom = 2.0f;    // log2 headroom added to the reference max at a rescale
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kM4 = 0x0F0F0F0Fu, kM2 = 0x03030303u, kM1 = 0x01010101u;
@@ -60,16 +71,36 @@ struct DecodeArgs {
     int layer, n_kv, G, n_seqs_cache;
     int64_t n_tiles_cap;
     int64_t max_len;
-    int tile_bytes, tpg, wg_per_head, nqb_max;
-    // LDS carve-up (bytes)
-    int off_qsc, off_ccol, off_buf, buf_bytes, off_P, off_tm;
+    int tile_bytes, tpg, wg_per_head, n_grp;
+    // LDS carve-up (bytes): per wave two tile buffers + the probability operand
+    int buf_bytes, wave_bytes, off_flag;
 };
 
-// order this wave's earlier LDS writes before its later LDS reads
-__device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// LDS-only workgroup barrier: this wave's LDS operations are complete, then s_barrier.
+// (Global->LDS tile loads in flight are not waited for; their waits are explicit.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// all of this wave's memory operations (incl. global->LDS tile loads) have completed
-__device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
+// wait until at most n of this wave's vector memory operations are outstanding (n is
+// clamped to 15, which only waits longer)
+__device__ __forceinline__ void wait_vm(int n) {
+    switch (n) {
+#define AATC_W(k) \
+    case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+        AATC_W(0) AATC_W(1) AATC_W(2) AATC_W(3) AATC_W(4) AATC_W(5) AATC_W(6) AATC_W(7)
+        AATC_W(8) AATC_W(9) AATC_W(10) AATC_W(11) AATC_W(12) AATC_W(13) AATC_W(14)
+#undef AATC_W
+        default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+    }
+}
+
+// data exchanged between workgroups: device-scope loads and stores (coherent across the
+// per-XCD L2 caches without a cache writeback)
+__device__ __forceinline__ float ld_dev(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -89,15 +120,17 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x + dpp<0x140>(x);
 }
 
-// Stream one tile (bytes, a multiple of 16) from global memory into LDS with the whole
-// workgroup: wave w moves the 1 KiB chunks w, w+4, ... (16 bytes per lane per instruction;
-// LDS address = chunk base + 16 * lane).
-__device__ __forceinline__ void load_tile(const uint8_t* src, LDS_AS uint8_t* lds, int bytes, int wave, int lane) {
-    for (int off = 1024 * wave; off < bytes; off += 1024 * kWaves) {
+// Stream one tile (bytes, a multiple of 16) from global memory into LDS with one wave:
+// 1 KiB per instruction, 16 bytes per lane (LDS address = chunk base + 16 * lane).
+__device__ __forceinline__ void load_tile(const uint8_t* src, LDS_AS uint8_t* lds, int bytes, int lane) {
+    for (int off = 0; off < bytes; off += 1024) {
         const int o = off + 16 * lane;
         if (o < bytes) __builtin_amdgcn_global_load_lds((const void*)(src + o), (LDS_AS void*)(lds + off), 16, 0, 0);
     }
 }
+
+// all of this wave's memory operations (incl. global->LDS tile loads) have completed
+__device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
 
 // Four int8 operand words from packed pieces.  m4 / m2 select the 4-bit / 2-bit modes
 // (uniform), otherwise 1-bit: 4-bit takes the nibbles of x0 then x1, 2-bit the crumbs of
@@ -110,121 +143,207 @@ __device__ __forceinline__ v4i unpack(uint32_t x0, uint32_t x1, bool m4, bool m2
     return v4i{(int)(base & M), (int)((base >> s1) & M), (int)((hi >> s2) & M), (int)((hi >> s3) & M)};
 }
 
+// The same, one width at a time (compile-time mode, no selects).
+template <int W>
+__device__ __forceinline__ v4i unpack_w(uint32_t x0, uint32_t x1, uint32_t pre) {
+    if constexpr (W == 4) {
+        return v4i{(int)(x0 & kM4), (int)((x0 >> 4) & kM4), (int)(x1 & kM4), (int)((x1 >> 4) & kM4)};
+    } else if constexpr (W == 2) {
+        return v4i{(int)(x0 & kM2), (int)((x0 >> 2) & kM2), (int)((x0 >> 4) & kM2), (int)((x0 >> 6) & kM2)};
+    } else {
+        const uint32_t b = x0 >> pre;
+        return v4i{(int)(b & kM1), (int)((b >> 1) & kM1), (int)((b >> 2) & kM1), (int)((b >> 3) & kM1)};
+    }
+}
 
-// ---------------------------------------------------------------------------------------
-// query preparation: int8 digits of q'' in the A-operand layout of the score MFMAs
-// (row 16 rb + 4 h' + k holds digit k of query head 4 rb + h' of the group)
-// ---------------------------------------------------------------------------------------
-template <int RB, int D>
-__global__ __launch_bounds__(256) void qprep_kernel(const DevHead* __restrict__ blob, int layer, int n_kv, int G,
-                                                    int nqb_max, const uint16_t* __restrict__ q,
-                                                    int8_t* __restrict__ qa_out, float* __restrict__ qsc_out,
-                                                    uint32_t* __restrict__ counters) {
-    constexpr int PARTS = 256 / D;     // row slices of U_K per column
-    constexpr int ROWS = D / PARTS;    // rows per slice
-    __shared__ float qf[16][D];
-    __shared__ float part_s[PARTS][16][D];
-    __shared__ int smax[16];
-    __shared__ int16_t kmap[aatc::kMaxQB * 64];
-    const int h = blockIdx.x, z = blockIdx.y, tid = threadIdx.x;
-    const DevHead& H = blob[layer * n_kv + h];
-    const int nq = n_kv * G;
-    const int nqb = H.nqb[0] + H.nqb[1] + H.nqb[2];
-    // every global read is issued up front so that a cold codebook costs one latency
-    const int j = tid % D, part = tid / D;
-    float u[ROWS];
+// three base-254 digits of x: x = d0 + d1 / 254 + d2 / 254^2 (+ rounding); each fits int8
+// when |x| <= 127
+__device__ __forceinline__ void digits(float x, float& d0, float& d1, float& d2) {
+    d0 = rintf(x);
+    const float r1 = (x - d0) * 254.0f;
+    d1 = rintf(r1);
+    d2 = rintf((r1 - d1) * 254.0f);
+}
+
+// Merge n partials (reference max m, sum l, coefficient accumulator x[d] per query head,
+// stored at src[(s * G + hh) * (D + 2) + {0, 1, 2 + jj}]) into the running (M, L, A) of
+// this thread's columns i = tid + 256 k (head i / D, coefficient i % D), CH partials per
+// round with every load of a round in flight at once.
+template <int D, int CPT, int CH>
+__device__ __forceinline__ void merge_cols(const float* src, int n, int G, int tid, float (&M)[CPT], float (&L)[CPT],
+                                           float (&A)[CPT]) {
+    constexpr int ld = D + 2;
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) u[r] = H.UK[(part * ROWS + r) * D + j];
-    const int b = H.bitsK[j];
-    const float st = H.stepK[j];
-    for (int i = tid; i < nqb * 64; i += 256) kmap[i] = (&H.kq_map[0][0][0])[i];
-    if (tid == 0) counters[z * n_kv + h] = 0u;
-    const uint16_t* qg = q + ((int64_t)z * nq + h * G) * D;
-    for (int i = tid; i < G * D; i += 256) qf[i / D][i % D] = aatc::bf16f(qg[i]);
-    if (tid < 16) smax[tid] = 0;
-    __syncthreads();
-    // q' = U_K^T q: thread (j, part) sums its slice of rows, slices meet in LDS
-    for (int g = 0; g < G; ++g) {
-        float a = 0.0f;
+    for (int k = 0; k < CPT; ++k) M[k] = -INFINITY, L[k] = 0.0f, A[k] = 0.0f;
+    for (int s0 = 0; s0 < n; s0 += CH) {
+        float m[CPT][CH], l[CPT][CH], x[CPT][CH];
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r) a = fmaf(u[r], qf[g][part * ROWS + r], a);
-        part_s[part][g][j] = a;
-    }
-    __syncthreads();
-    const float qs = kLog2e / sqrtf((float)D);
-    const int top = b >= 4 ? b - 4 : (b >= 2 ? b - 2 : 0);  // shift of the channel's top piece
-    for (int g = part; g < G; g += PARTS) {
-        float a = 0.0f;
+        for (int k = 0; k < CPT; ++k) {
+            const int i = tid + 256 * k, hh = min(i / D, G - 1), jj = i % D;
 #pragma unroll
-        for (int pp = 0; pp < PARTS; ++pp) a += part_s[pp][g][j];
-        const float v = b ? a * st * qs : 0.0f;
-        qf[g][j] = v;  // q'' (qf is free again)
-        atomicMax(&smax[g], __float_as_int(fabsf(v) * (float)(1 << top)));
-    }
-    __syncthreads();
-    int8_t* qa = qa_out + ((int64_t)z * n_kv + h) * nqb_max * RB * 1024;
-    for (int i = tid; i < nqb_max * RB * 1024; i += 256) {
-        const int bb = i & 15, lane = (i >> 4) & 63, rb = (i >> 10) % RB, qb = (i >> 10) / RB;
-        const int row = lane & 15, g = lane >> 4;
-        const int hh = 4 * rb + (row >> 2), k = row & 3;
-        int val = 0;
-        if (qb < nqb && hh < G && k < 3) {
-            const int m = kmap[(qb * 4 + g) * 16 + bb];
-            if (m >= 0) {
-                const float mx = __int_as_float(smax[hh]);
-                const float x = mx > 0.0f ? qf[hh][m & 255] * (float)(1 << (m >> 8)) * (127.0f / mx) : 0.0f;
-                const float d0 = rintf(x);
-                const float r1 = (x - d0) * 254.0f;
-                const float d1 = rintf(r1);
-                const float d2 = rintf((r1 - d1) * 254.0f);
-                val = (int)(k == 0 ? d0 : (k == 1 ? d1 : d2));
+            for (int e = 0; e < CH; ++e) {
+                const float* p = src + (min(s0 + e, n - 1) * G + hh) * ld;
+                m[k][e] = ld_dev(p);
+                l[k][e] = ld_dev(p + 1);
+                x[k][e] = ld_dev(p + 2 + jj);
             }
         }
-        qa[i] = (int8_t)val;
-    }
-    float* qsc = qsc_out + ((int64_t)z * n_kv + h) * RB * 16;
-    for (int r = tid; r < RB * 16; r += 256) {
-        const int hh = r >> 2, k = r & 3;
-        float v = 0.0f;
-        if (hh < G && k < 3) {
-            const float mx = __int_as_float(smax[hh]);
-            v = (mx / 127.0f) * (k == 0 ? 1.0f : (k == 1 ? kDig1 : kDig2));
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            float mx = M[k];
+#pragma unroll
+            for (int e = 0; e < CH; ++e)
+                if (s0 + e < n) mx = fmaxf(mx, m[k][e]);
+            const float f = M[k] == -INFINITY ? 0.0f : exp2f(M[k] - mx);
+            L[k] *= f;
+            A[k] *= f;
+#pragma unroll
+            for (int e = 0; e < CH; ++e) {
+                const float wgt = (s0 + e < n && m[k][e] != -INFINITY) ? exp2f(m[k][e] - mx) : 0.0f;
+                L[k] = fmaf(wgt, l[k][e], L[k]);
+                A[k] = fmaf(wgt, x[k][e], A[k]);
+            }
+            M[k] = mx;
         }
-        qsc[r] = v;
     }
 }
 
 // ---------------------------------------------------------------------------------------
-// split decode (+ the final merge by the last workgroup of each (sequence, kv-head))
+// query preparation, one workgroup per (sequence, kv-head): q'' = (U_K^T q) * step_K *
+// log2(e) / sqrt(d) for the G query heads, split into three int8 digits and written as the
+// A operands of the score MFMAs ([qb][rb][lane][16] bytes; lane row = 4 head + digit, slot
+// order = the key unpack schedule), plus the per-head digit scale (max |q'' 2^top| / 127).
+// Every global read is issued in one batch so that a cold codebook costs one latency.
 // ---------------------------------------------------------------------------------------
-// waves per SIMD the register budget is sized for: four for the common shapes (one row
-// block, up to 16 value column blocks), fewer where more accumulators are live
-constexpr int waves_for(int rb, int nqb, int nvb) { return rb * nvb <= 16 && nqb <= 8 ? 4 : (rb * nvb <= 24 ? 3 : 2); }
+template <int RB, int NQB, int D>
+__global__ __launch_bounds__(256) void qprep_kernel(const DevHead* __restrict__ blob, int layer, int n_kv, int G,
+                                                    const uint16_t* __restrict__ q, uint32_t* __restrict__ qa_out,
+                                                    float* __restrict__ qscale_out) {
+    constexpr int PARTS = 256 / D;           // row slices of U_K per column
+    constexpr int ROWS = D / PARTS;          // rows per slice
+    constexpr int QPT = 16 * D / 256;        // query elements per thread (<= 16 heads)
+    constexpr int KPT = (NQB * 64 + 255) / 256;
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) float qf[16 * D];
+    __shared__ float ps[PARTS * 16 * D];
+    __shared__ int smax[16];
+    __shared__ int16_t kmap[KPT * 256];
+    const int h = blockIdx.x, z = blockIdx.y, tid = threadIdx.x;
+    const DevHead& H = blob[layer * n_kv + h];
+    const int64_t zh = (int64_t)z * n_kv + h;
+    const int j = tid % D, pt = __builtin_amdgcn_readfirstlane(tid / D);
+    const float* ub = H.UK + pt * ROWS * D + j;
+    float u[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) u[r] = ub[r * D];
+    const int bj = H.bitsK[j];
+    const float stj = H.stepK[j];
+    const int nqb = H.nqb[0] + H.nqb[1] + H.nqb[2];
+    const uint16_t* qg = q + zh * G * D;
+    uint16_t qv[QPT];
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) qv[k] = qg[min(tid + 256 * k, G * D - 1)];
+    int16_t km[KPT];
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) km[k] = (&H.kq_map[0][0][0])[tid + 256 * k];
+#pragma unroll
+    for (int k = 0; k < QPT; ++k)
+        if (tid + 256 * k < G * D) qf[tid + 256 * k] = aatc::bf16f(qv[k]);
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) kmap[tid + 256 * k] = km[k];
+    if (tid < 16) smax[tid] = 0;
+    __syncthreads();
+    // q' = U_K^T q: thread (j, pt) sums its slice of rows, slices meet in LDS
+    for (int hh = 0; hh < G; ++hh) {
+        const f4* q4 = (const f4*)(qf + hh * D + pt * ROWS);
+        float acc = 0.0f;
+#pragma unroll
+        for (int r4 = 0; r4 < ROWS / 4; ++r4) {
+            const f4 x = q4[r4];
+            acc = fmaf(u[4 * r4], x[0], acc);
+            acc = fmaf(u[4 * r4 + 1], x[1], acc);
+            acc = fmaf(u[4 * r4 + 2], x[2], acc);
+            acc = fmaf(u[4 * r4 + 3], x[3], acc);
+        }
+        ps[(pt * 16 + hh) * D + j] = acc;
+    }
+    __syncthreads();
+    const float qscale = kLog2e / sqrtf((float)D);
+    const int top = bj >= 4 ? bj - 4 : (bj >= 2 ? bj - 2 : 0);  // shift of the channel's top piece
+    for (int hh = pt; hh < G; hh += PARTS) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int p2 = 0; p2 < PARTS; ++p2) acc += ps[(p2 * 16 + hh) * D + j];
+        const float v = bj ? acc * stj * qscale : 0.0f;
+        qf[hh * D + j] = v;
+        // per-head max of |v| 2^top: wave maximum, then one LDS max per wave
+        float mag = fabsf(v) * (float)(1 << top);
+        mag = row16_max(mag);
+        mag = fmaxf(mag, __shfl_xor(mag, 16));
+        mag = fmaxf(mag, __shfl_xor(mag, 32));
+        if ((tid & 63) == 0) atomicMax(&smax[hh], __float_as_int(mag));
+    }
+    __syncthreads();
+    // operand word i: bytes 4i..4i+3 of [qb][rb][lane][16]
+    uint32_t* qa = qa_out + zh * NQB * RB * 256;
+    for (int i = tid; i < NQB * RB * 256; i += 256) {
+        const int bb = (i & 3) * 4, ln = (i >> 2) & 63, rb = (i >> 8) % RB, qb = (i >> 8) / RB;
+        const int row = ln & 15, gg = ln >> 4;
+        const int hh = 4 * rb + (row >> 2), k = row & 3;
+        uint32_t word = 0u;
+        if (qb < nqb && hh < G && k < 3) {
+            const float mx = __int_as_float(smax[hh]);
+            const float sc = mx > 0.0f ? 127.0f / mx : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = kmap[(qb * 4 + gg) * 16 + bb + e];
+                if (m >= 0) {
+                    float d0, d1, d2;
+                    digits(qf[hh * D + (m & 255)] * (float)(1 << (m >> 8)) * sc, d0, d1, d2);
+                    const int dv = (int)(k == 0 ? d0 : (k == 1 ? d1 : d2));
+                    word |= ((uint32_t)dv & 0xFFu) << (8 * e);
+                }
+            }
+        }
+        qa[i] = word;
+    }
+    if (tid < 16) qscale_out[zh * 16 + tid] = tid < G ? __int_as_float(smax[tid]) * (1.0f / 127.0f) : 0.0f;
+}
 
-template <int RB, int NQB, int NVB>
+// Registers per lane grow with the row blocks and value column blocks; the waves per SIMD
+// the allocation is sized for (the LDS plan matches it).
+constexpr int vgpr_estimate(int rb, int nqb, int nvb) { return rb * nvb * 4 + nqb * rb * 4 + rb * 16 + nvb / 2 + nqb + 50; }
+constexpr int waves_for(int rb, int nqb, int nvb) {
+    return vgpr_estimate(rb, nqb, nvb) <= 128 ? 4 : (vgpr_estimate(rb, nqb, nvb) <= 168 ? 3 : 2);
+}
+
+template <int RB, int NQB, int NVB, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQB, NVB)))) void decode_kernel(
     const DevHead* __restrict__ blob, const uint8_t* __restrict__ cache, DecodeArgs a,
-    const int32_t* __restrict__ seq_ids, const int64_t* __restrict__ seq_lens, const int8_t* __restrict__ qa_all,
-    const float* __restrict__ qsc_all, float* __restrict__ part, uint32_t* __restrict__ counters,
-    float* __restrict__ out) {
-    constexpr int NVW = NVB / kWaves;  // value column blocks per wave
+    const int32_t* __restrict__ seq_ids, const int64_t* __restrict__ seq_lens, const uint8_t* __restrict__ qa_all,
+    const float* __restrict__ qscale, float* __restrict__ part1, float* __restrict__ part2,
+    uint32_t* __restrict__ cnt1, uint32_t* __restrict__ cnt2, float* __restrict__ out) {
+    constexpr int PARTS = 256 / D;  // row slices of a d x d matrix per column
+    constexpr int ROWS = D / PARTS;  // rows per slice
+    constexpr int PST = 80;          // bytes per row of the probability operand (64 tokens + pad)
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     LDS_AS uint8_t* sm = (LDS_AS uint8_t*)smem_generic;
     const int wgi = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, c = lane & 15;
     const DevHead& H = blob[a.layer * a.n_kv + h];
-    const int G = a.G, d = H.d, TB = a.tile_bytes;
+    const int G = a.G, TB = a.tile_bytes, BB = a.buf_bytes;
     const int WK = H.BK >> 5;  // key record words per token
-    const int nqb4 = H.nqb[0], nqb2 = H.nqb[1], nqb = H.nqb[0] + H.nqb[1] + H.nqb[2];
-    const int nvb4 = H.nvb[0], nvb2 = H.nvb[1], nvb = H.nvb[0] + H.nvb[1] + H.nvb[2];
+    int nqb4 = H.nqb[0], nqb2 = H.nqb[1];
+    const int nqb = H.nqb[0] + H.nqb[1] + H.nqb[2];
+    int nvb4 = H.nvb[0], nvb2 = H.nvb[1];
+    const int nvb = H.nvb[0] + H.nvb[1] + H.nvb[2];
+    const int64_t zh = (int64_t)z * a.n_kv + h;
 
-    LDS_AS int8_t* qa_lds = (LDS_AS int8_t*)sm;                  // [NQB][RB][64 lanes][16]
-    LDS_AS float* qsc_lds = (LDS_AS float*)(sm + a.off_qsc);     // [RB*4 heads][4 digits]
-    LDS_AS int16_t* ccol_lds = (LDS_AS int16_t*)(sm + a.off_ccol);
-    LDS_AS uint8_t* buf0 = sm + a.off_buf;                       // two tile buffers
-    LDS_AS uint8_t* P = sm + a.off_P;                            // [RB*16 rows][64 tokens] digits
-    LDS_AS float* tm = (LDS_AS float*)(sm + a.off_tm);           // [4 waves][RB*4 heads] maxima
+    // this wave's LDS: two tile buffers and the probability operand [RB*16 rows][PST]
+    LDS_AS uint8_t* ring = sm + w * a.wave_bytes;
+    LDS_AS uint8_t* P = ring + 2 * BB;
+    LDS_AS int* flag = (LDS_AS int*)(sm + a.off_flag);
 
     // ---- sequence geometry (device arguments clamped: no read outside the cache)
     const int seq = seq_ids[z];
@@ -234,249 +353,332 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
     const int64_t t_begin = (int64_t)wgi * a.tpg;
     const int64_t t_end = min(t_begin + a.tpg, n_tiles);
     const uint8_t* tiles = cache + (((int64_t)a.layer * a.n_seqs_cache + seq) * a.n_kv + h) * a.n_tiles_cap * TB;
-    if (t_begin < t_end) load_tile(tiles + t_begin * TB, buf0, TB, w, lane);
 
-    // ---- per-lane schedule constants (registers) and staged operands (LDS)
+    // ---- prologue: one batch of reads, waited for before the first tile load
+    v4i Aq[NQB][RB];  // score A operands (query digits), resident for the whole loop
+    {
+        const v4i* src = (const v4i*)(qa_all + zh * NQB * RB * 1024);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) Aq[qb][rb] = src[(qb * RB + rb) * 64 + lane];
+    }
     uint32_t kofs[NQB];  // key record words (o0 | o1 << 16) of this lane group for each score block
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
         kofs[qb] = qb < nqb ? (uint32_t)H.kq_dw[qb][g][0] | ((uint32_t)H.kq_dw[qb][g][1] << 16) : 0u;
-    uint32_t vofs[NVW];  // first word of this lane's value slab in this wave's column blocks
+    constexpr int NVP = (NVB + 1) / 2;
+    uint32_t vofs[NVP];  // first words of this lane's value slabs, two column blocks per register
 #pragma unroll
-    for (int j = 0; j < NVW; ++j) {
-        const int cb = w + kWaves * j;
-        vofs[j] = cb < nvb ? (uint32_t)H.vb_slab[cb][c] : 0u;
+    for (int k = 0; k < NVP; ++k) {
+        const uint32_t lo = 2 * k < nvb ? (uint32_t)H.vb_slab[2 * k][c] : 0u;
+        const uint32_t hi = 2 * k + 1 < nvb ? (uint32_t)H.vb_slab[2 * k + 1][c] : 0u;
+        vofs[k] = lo | (hi << 16);
     }
-    {
-        const u32x4* src = (const u32x4*)(qa_all + ((int64_t)z * a.n_kv + h) * a.nqb_max * RB * 1024);
-        LDS_AS u32x4* dst = (LDS_AS u32x4*)qa_lds;
-        for (int i = tid; i < NQB * RB * 64; i += 256)
-            dst[i] = i < nqb * RB * 64 ? src[i] : u32x4{0u, 0u, 0u, 0u};
-        const float* qs = qsc_all + ((int64_t)z * a.n_kv + h) * RB * 16;
-        for (int i = tid; i < RB * 16; i += 256) qsc_lds[i] = qs[i];
-        for (int i = tid; i < d * 4; i += 256) ccol_lds[i] = (&H.chan_cols[0][0])[i];
-        LDS_AS uint32_t* Pw = (LDS_AS uint32_t*)P;
-        for (int i = tid; i < RB * 16 * 16; i += 256) Pw[i] = 0u;
-    }
-    __syncthreads();
-
-    const int tok = 16 * w + c;  // this lane's token inside the tile (scores, softmax)
-    float qs[RB][3];
+    float qs[RB][3];  // digit scales of this lane's query head
     bool hv[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         hv[rb] = 4 * rb + g < G;
+        const float mx = qscale[zh * 16 + 4 * rb + g];
+        qs[rb][0] = mx;
+        qs[rb][1] = mx * kDig1;
+        qs[rb][2] = mx * kDig2;
+    }
+    // the operands have arrived before any tile load: inside the loop the only vector
+    // memory operations are this wave's tile loads
 #pragma unroll
-        for (int k = 0; k < 3; ++k) qs[rb][k] = qsc_lds[(4 * rb + g) * 4 + k];
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(Aq[qb][rb]));
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) asm volatile("" ::"v"(kofs[qb]));
+#pragma unroll
+    for (int k = 0; k < NVP; ++k) asm volatile("" ::"v"(vofs[k]));
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(qs[rb][0]));
+
+    {
+        LDS_AS uint32_t* Pw = (LDS_AS uint32_t*)P;  // digit row 3 of each head stays zero
+        for (int i = lane; i < RB * 16 * PST / 4; i += 64) Pw[i] = 0u;
     }
     const uint32_t vwi4 = 2 * g, vwi2 = g, vwi1 = g >> 1, pre1 = 4 * (g & 1);
 
-    v4i acc_i[RB][NVW];
-    float acc_f[RB][NVW][3];
+    // int32 sums of P digits x value pieces, relative to the reference max mref (a rescale
+    // combines the three digit sums, scales by 2^(old - new) and splits the result into
+    // digits again: the error is a float rounding of the running sum)
+    v4i acc_i[RB][NVB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int j = 0; j < NVW; ++j) {
-            acc_i[rb][j] = v4i{0, 0, 0, 0};
-#pragma unroll
-            for (int k = 0; k < 3; ++k) acc_f[rb][j][k] = 0.0f;
-        }
+        for (int cb = 0; cb < NVB; ++cb) acc_i[rb][cb] = v4i{0, 0, 0, 0};
     float mref[RB], lsum[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) mref[rb] = -INFINITY, lsum[rb] = 0.0f;
 
-    for (int64_t t = t_begin; t < t_end; ++t) {
-        LDS_AS uint8_t* cur = buf0 + (((t - t_begin) & 1) ? a.buf_bytes : 0);
-        LDS_AS uint8_t* nxt = buf0 + (((t - t_begin) & 1) ? 0 : a.buf_bytes);
-        wait_all();
-        __syncthreads();  // tile t resident; every wave is done with tile t-1 (buffers, P, tm)
-        if (t + 1 < t_end) load_tile(tiles + (t + 1) * TB, nxt, TB, w, lane);
-        const LDS_AS uint32_t* kw = (const LDS_AS uint32_t*)cur + tok;  // record word r at kw[64 r]
-        const LDS_AS uint32_t* vw = (const LDS_AS uint32_t*)cur + 64 * WK;
+    // ---- tiles t_begin + w, t_begin + w + 4, ...: double-buffered per wave
+    int64_t t = t_begin + w;
+    if (t < t_end) load_tile(tiles + t * TB, ring, TB, lane);
+    int buf = 0;
+    for (; t < t_end; t += kWaves) {
+        // the per-block unpack modes derive from these counts inside the loop (a few scalar
+        // ops per block) instead of being hoisted into dozens of live scalar registers
+        asm volatile("" : "+s"(nqb4), "+s"(nqb2), "+s"(nvb4), "+s"(nvb2));
+        wait_all();  // tile t has landed; this wave's reads of the other buffer are done
+        if (t + kWaves < t_end) load_tile(tiles + (t + kWaves) * TB, ring + (buf ^ 1) * BB, TB, lane);
+        const LDS_AS uint32_t* cur = (const LDS_AS uint32_t*)(ring + buf * BB);
+        buf ^= 1;
         const int valid = (int)min((int64_t)kTile, len - t * kTile);
 
-        // ---------------- scores of this wave's 16 tokens: S[4 head + digit][token]
-        v4i S[RB];
+        // ---------------- scores: token group tg, lane (g, c) -> token 4c + tg
+        v4i S[4][RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) S[rb] = v4i{0, 0, 0, 0};
+        for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) S[tg][rb] = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
-            const bool m4 = qb < nqb4, m2 = !m4 && qb < nqb4 + nqb2;
-            const v4i B = unpack(kw[64 * (kofs[qb] & 0xFFFFu)], kw[64 * (kofs[qb] >> 16)], m4, m2, pre1);
+            const LDS_AS uint32_t* k0 = cur + 64 * (kofs[qb] & 0xFFFFu) + 4 * c;
+            const LDS_AS uint32_t* k1 = cur + 64 * (kofs[qb] >> 16) + 4 * c;
+            // the block's width is uniform: one scalar branch, then straight-line unpacks
+            if (qb >= nqb) {
+                // padding block: nothing to add
+            } else if (qb < nqb4) {
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const v4i A = *(const LDS_AS v4i*)(qa_lds + ((qb * RB + rb) * 64 + lane) * 16);
-                S[rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, S[rb], 0, 0, 0);
+                for (int tg = 0; tg < 4; ++tg) {
+                    const v4i B = unpack_w<4>(k0[tg], k1[tg], pre1);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        S[tg][rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[qb][rb], B, S[tg][rb], 0, 0, 0);
+                }
+            } else if (qb < nqb4 + nqb2) {
+#pragma unroll
+                for (int tg = 0; tg < 4; ++tg) {
+                    const v4i B = unpack_w<2>(k0[tg], 0u, pre1);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        S[tg][rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[qb][rb], B, S[tg][rb], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int tg = 0; tg < 4; ++tg) {
+                    const v4i B = unpack_w<1>(k0[tg], 0u, pre1);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        S[tg][rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[qb][rb], B, S[tg][rb], 0, 0, 0);
+                }
             }
+            __builtin_amdgcn_sched_barrier(0);  // bound the operand words in flight (registers)
         }
-        // lane (g, c): head 4rb+g, token 16w+c; per-wave head maxima to LDS
-        float s[RB];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const float v = (float)S[rb][0] * qs[rb][0] + (float)S[rb][1] * qs[rb][1] + (float)S[rb][2] * qs[rb][2];
-            s[rb] = (hv[rb] && tok < valid) ? v : -INFINITY;
-            const float mx = row16_max(s[rb]);
-            if (c == 0) tm[w * RB * 4 + 4 * rb + g] = mx;
-        }
-        __syncthreads();  // per-wave maxima visible
-
-        // ---------------- online softmax (all waves keep the same reference maxima)
-        float tmax[RB];
+        // lane (g, c) holds head 4rb+g, tokens 4c..4c+3, digit rows 0..2
+        __builtin_amdgcn_sched_barrier(0);
+        float s[RB][4], tmx[RB];
         bool need = false;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            float mx = tm[4 * rb + g];
+            float mx = -INFINITY;
 #pragma unroll
-            for (int ww = 1; ww < kWaves; ++ww) mx = fmaxf(mx, tm[ww * RB * 4 + 4 * rb + g]);
-            tmax[rb] = mx;
-            need |= mx > mref[rb];
+            for (int tg = 0; tg < 4; ++tg) {
+                const float v = (float)S[tg][rb][0] * qs[rb][0] + (float)S[tg][rb][1] * qs[rb][1] +
+                                (float)S[tg][rb][2] * qs[rb][2];
+                s[rb][tg] = (hv[rb] && 4 * c + tg < valid) ? v : -INFINITY;
+                mx = fmaxf(mx, s[rb][tg]);
+            }
+            tmx[rb] = row16_max(mx);
+            if (tmx[rb] > mref[rb]) need = true;
         }
         if (__any(need)) {
-            // raise the reference of heads whose tile max passed it; fold the int
-            // accumulators (relative to the old reference) into the float ones and rescale
+            // raise the reference of heads whose tile max passed it and rescale their sums
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
-                const float nref = tmax[rb] > mref[rb] ? tmax[rb] + kHeadroom : mref[rb];
+                const float nref = tmx[rb] > mref[rb] ? tmx[rb] + kHeadroom : mref[rb];
                 const float al = hv[rb] ? exp2f(mref[rb] - nref) : 0.0f;
                 lsum[rb] *= al;
                 mref[rb] = nref;
 #pragma unroll
-                for (int j = 0; j < NVW; ++j) {
-                    acc_f[rb][j][0] = (acc_f[rb][j][0] + (float)acc_i[rb][j][0] * (1.0f / 127.0f)) * al;
-                    acc_f[rb][j][1] = (acc_f[rb][j][1] + (float)acc_i[rb][j][1] * (kDig1 / 127.0f)) * al;
-                    acc_f[rb][j][2] = (acc_f[rb][j][2] + (float)acc_i[rb][j][2] * (kDig2 / 127.0f)) * al;
-                    acc_i[rb][j] = v4i{0, 0, 0, 0};
+                for (int cb = 0; cb < NVB; ++cb) {
+                    const float v = ((float)acc_i[rb][cb][0] + (float)acc_i[rb][cb][1] * kDig1 +
+                                     (float)acc_i[rb][cb][2] * kDig2) *
+                                    al;
+                    float d0, d1, d2;
+                    digits(v, d0, d1, d2);
+                    acc_i[rb][cb] = v4i{(int)d0, (int)d1, (int)d2, 0};
                 }
             }
         }
         // probabilities as three int8 digits (p*127 = d0 + d1/254 + d2/254^2) into
-        // P[4 head + digit][token], the value MFMA's A operand
+        // P[16 rb + 4 head + digit][token], the value MFMA's A operand (wave-private)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            const float p = hv[rb] ? exp2f(s[rb] - mref[rb]) : 0.0f;
-            lsum[rb] += p;
-            const float x = p * 127.0f;
-            const float d0 = rintf(x);
-            const float r1 = (x - d0) * 254.0f;
-            const float d1 = rintf(r1);
-            const float d2 = rintf((r1 - d1) * 254.0f);
-            LDS_AS int8_t* pp = (LDS_AS int8_t*)(P + (16 * rb + 4 * g) * 64 + tok);
-            pp[0] = (int8_t)(int)d0;
-            pp[64] = (int8_t)(int)d1;
-            pp[128] = (int8_t)(int)d2;
+            uint32_t pk0 = 0u, pk1 = 0u, pk2 = 0u;
+#pragma unroll
+            for (int tg = 0; tg < 4; ++tg) {
+                const float p = hv[rb] ? exp2f(s[rb][tg] - mref[rb]) : 0.0f;
+                lsum[rb] += p;
+                float d0, d1, d2;
+                digits(p * 127.0f, d0, d1, d2);
+                pk0 |= ((uint32_t)(int)d0 & 0xFFu) << (8 * tg);
+                pk1 |= ((uint32_t)(int)d1 & 0xFFu) << (8 * tg);
+                pk2 |= ((uint32_t)(int)d2 & 0xFFu) << (8 * tg);
+            }
+            LDS_AS uint32_t* pw = (LDS_AS uint32_t*)(P + (16 * rb + 4 * g) * PST + 4 * c);
+            pw[0] = pk0;
+            pw[PST / 4] = pk1;
+            pw[2 * PST / 4] = pk2;
         }
-        __syncthreads();  // all 64 tokens' digits in P
-
-        // ---------------- values: this wave's column blocks over all 64 tokens
+        asm volatile("" ::: "memory");  // the operand reads below follow this wave's writes
+        __builtin_amdgcn_sched_barrier(0);
         v4i Ap[RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) Ap[rb] = *(const LDS_AS v4i*)(P + (16 * rb + c) * 64 + 16 * g);
+        for (int rb = 0; rb < RB; ++rb) Ap[rb] = *(const LDS_AS v4i*)(P + (16 * rb + c) * PST + 16 * g);
+
+        // ---------------- values: every column block over the 64 tokens
+        const LDS_AS uint32_t* vw = cur + 64 * WK;
 #pragma unroll
-        for (int j = 0; j < NVW; ++j) {
-            const int cb = w + kWaves * j;
-            const bool m4 = cb < nvb4, m2 = !m4 && cb < nvb4 + nvb2;
-            const uint32_t wi = vofs[j] + (m4 ? vwi4 : (m2 ? vwi2 : vwi1));
-            const v4i B = unpack(vw[wi], vw[wi + 1], m4, m2, pre1);
+        for (int cb = 0; cb < NVB; ++cb) {
+            const uint32_t slab = (vofs[cb >> 1] >> (16 * (cb & 1))) & 0xFFFFu;
+            v4i B;
+            if (cb >= nvb)
+                continue;  // padding block
+            else if (cb < nvb4)
+                B = unpack_w<4>(vw[slab + vwi4], vw[slab + vwi4 + 1], pre1);
+            else if (cb < nvb4 + nvb2)
+                B = unpack_w<2>(vw[slab + vwi2], 0u, pre1);
+            else
+                B = unpack_w<1>(vw[slab + vwi1], 0u, pre1);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-                acc_i[rb][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ap[rb], B, acc_i[rb][j], 0, 0, 0);
+                acc_i[rb][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ap[rb], B, acc_i[rb][cb], 0, 0, 0);
+            if (cb % 4 == 3) __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // ---------------- epilogue: fold, reduce digits and pieces, one partial per workgroup
+    // ---------------- epilogue: the four waves' results meet in LDS (ring reused)
     wait_all();
-    __syncthreads();  // tile buffers free
+    lds_barrier();
+    const int ld = D + 2;
     const int ncol = 16 * nvb;
-    LDS_AS float* accg = (LDS_AS float*)buf0;          // [RB*4 heads][ncol]
-    LDS_AS float* lsw = accg + RB * 4 * ncol;          // [4 waves][RB*4 heads]
-    LDS_AS float* wp = lsw + kWaves * RB * 4;          // [G][d+2]
+    LDS_AS float* wm = (LDS_AS float*)sm;                 // [4 waves][RB*4 heads] reference maxima
+    LDS_AS float* wl = wm + kWaves * RB * 4;              // [4 waves][RB*4 heads] sums
+    LDS_AS float* wa = wl + kWaves * RB * 4;              // [4 waves][RB*4 heads][16 NVB] accumulators
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const float ls = row16_sum(lsum[rb]);
-        if (c == 0) lsw[w * RB * 4 + 4 * rb + g] = ls;
-#pragma unroll
-        for (int j = 0; j < NVW; ++j) {
-            const int cb = w + kWaves * j;
-            if (cb < nvb)
-                accg[(4 * rb + g) * ncol + 16 * cb + c] =
-                    acc_f[rb][j][0] + (float)acc_i[rb][j][0] * (1.0f / 127.0f) + acc_f[rb][j][1] +
-                    (float)acc_i[rb][j][1] * (kDig1 / 127.0f) + acc_f[rb][j][2] +
-                    (float)acc_i[rb][j][2] * (kDig2 / 127.0f);
+        if (c == 0) {
+            wm[w * RB * 4 + 4 * rb + g] = mref[rb];
+            wl[w * RB * 4 + 4 * rb + g] = ls;
         }
-        if (w == 0 && c == 0 && hv[rb]) wp[(4 * rb + g) * (d + 2)] = mref[rb];
+#pragma unroll
+        for (int cb = 0; cb < NVB; ++cb)
+            if (cb < nvb)
+                wa[(w * RB * 4 + 4 * rb + g) * 16 * NVB + 16 * cb + c] =
+                    ((float)acc_i[rb][cb][0] + (float)acc_i[rb][cb][1] * kDig1 + (float)acc_i[rb][cb][2] * kDig2) *
+                    (1.0f / 127.0f);
     }
-    __syncthreads();
-    float* pout = part + (((int64_t)z * a.n_kv + h) * a.wg_per_head + wgi) * G * (d + 2);
-    for (int i = tid; i < G * (d + 2); i += 256) {
-        const int hh = i / (d + 2), col = i % (d + 2);
+    lds_barrier();
+    const int W = a.wg_per_head, NG = a.n_grp;
+    const int grp_size = (W + NG - 1) / NG;
+    const int grp = wgi / grp_size;
+    float* pout = part1 + (zh * W + wgi) * G * ld;
+    for (int i = tid; i < G * ld; i += 256) {
+        const int hh = i / ld, col = i - hh * ld;
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, wm[ww * RB * 4 + hh]);
+        float e[kWaves];
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            const float m = wm[ww * RB * 4 + hh];
+            e[ww] = m == -INFINITY ? 0.0f : exp2f(m - M);
+        }
         float v;
         if (col == 0) {
-            v = wp[hh * (d + 2)];
+            v = M;
         } else if (col == 1) {
             v = 0.0f;
 #pragma unroll
-            for (int ww = 0; ww < kWaves; ++ww) v += lsw[ww * RB * 4 + hh];
+            for (int ww = 0; ww < kWaves; ++ww) v += e[ww] * wl[ww * RB * 4 + hh];
         } else {
             const int jj = col - 2;
             v = 0.0f;
 #pragma unroll
             for (int tt = 0; tt < 3; ++tt) {
-                const int e = ccol_lds[jj * 4 + tt];
-                if (e >= 0) v += (float)(1 << (e >> 12)) * accg[hh * ncol + (e & 0xfff)];
+                const int en = H.chan_cols[jj][tt];
+                if (en >= 0) {
+                    float x = 0.0f;
+#pragma unroll
+                    for (int ww = 0; ww < kWaves; ++ww) x += e[ww] * wa[(ww * RB * 4 + hh) * 16 * NVB + (en & 0xfff)];
+                    v += (float)(1 << (en >> 12)) * x;
+                }
             }
         }
-        pout[i] = v;
+        st_dev(pout + i, v);
     }
+    (void)ncol;
+    wait_vm(0);     // this wave's partial stores have completed
+    lds_barrier();  // ... and every wave's
+    const int members1 = min(grp_size, W - grp * grp_size);
+    if (tid == 0) *flag = atomicInc(cnt1 + zh * NG + grp, (uint32_t)members1 - 1u) == (uint32_t)members1 - 1u;
+    lds_barrier();
+    if (!*flag) return;
 
-    // ---------------- the last workgroup of this (sequence, kv-head) merges all partials,
-    // dequantises the value coefficients and applies the inverse transform
-    __threadfence();
-    __syncthreads();
-    __shared__ int is_last;
-    if (tid == 0) is_last = atomicAdd(&counters[z * a.n_kv + h], 1u) == (uint32_t)(a.wg_per_head - 1);
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    const int W = a.wg_per_head;
-    const float* ph = part + ((int64_t)z * a.n_kv + h) * W * G * (d + 2);
-    LDS_AS float* wgt = (LDS_AS float*)sm;  // [G][W] maxima, then merge weights
-    LDS_AS float* lw = wgt + G * W;         // [G][W] sums
-    LDS_AS float* Ls = lw + G * W;          // [G]
-    LDS_AS float* cbar = Ls + G;            // [G][d]
-    for (int i = tid; i < G * W; i += 256) {
-        const float* src = ph + ((i % W) * G + i / W) * (d + 2);
-        wgt[i] = src[0];
-        lw[i] = src[1];
-    }
-    __syncthreads();
-    if (tid < G) {
-        float M = -INFINITY;
-        for (int s2 = 0; s2 < W; ++s2) M = fmaxf(M, wgt[tid * W + s2]);
-        float L = 0.0f;
-        for (int s2 = 0; s2 < W; ++s2) {
-            const float m = wgt[tid * W + s2];
-            const float wt = m == -INFINITY ? 0.0f : exp2f(m - M);
-            wgt[tid * W + s2] = wt;
-            L += wt * lw[tid * W + s2];
+    // ---------------- merges (coefficient domain), then dequantise + inverse transform
+    // thread columns: i = tid + 256 k -> query head i / D, coefficient i % D
+    constexpr int CPT = RB * 4 * D / 256;
+    constexpr int CH = 16 / RB;  // partials per merge round
+    float M[CPT], L[CPT], A[CPT];
+    merge_cols<D, CPT, CH>(part1 + (zh * W + grp * grp_size) * G * ld, members1, G, tid, M, L, A);
+    if (NG > 1) {
+        float* gout = part2 + (zh * NG + grp) * G * ld;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const int i = tid + 256 * k, hh = i / D, jj = i - hh * D;
+            if (hh < G) {
+                st_dev(gout + hh * ld + 2 + jj, A[k]);
+                if (jj == 0) {
+                    st_dev(gout + hh * ld, M[k]);
+                    st_dev(gout + hh * ld + 1, L[k]);
+                }
+            }
         }
-        Ls[tid] = L;
+        wait_vm(0);
+        lds_barrier();
+        if (tid == 0) *flag = atomicInc(cnt2 + zh, (uint32_t)NG - 1u) == (uint32_t)NG - 1u;
+        lds_barrier();
+        if (!*flag) return;
+        merge_cols<D, CPT, CH>(part2 + zh * NG * G * ld, NG, G, tid, M, L, A);
     }
-    __syncthreads();
-    for (int i = tid; i < G * d; i += 256) {
-        const int hh = i / d, jj = i % d;
-        float A = 0.0f;
-#pragma unroll 8
-        for (int s2 = 0; s2 < W; ++s2) A += wgt[hh * W + s2] * ph[(s2 * G + hh) * (d + 2) + 2 + jj];
-        const int bv = H.bitsV[jj];
-        cbar[i] = bv ? H.stepV[jj] * (A / Ls[hh] - (float)(1 << (bv - 1)) + 0.5f) : 0.0f;
+    // basis slice for the inverse transform: thread (column ii, slice pt)
+    const int ii = tid % D, pt = __builtin_amdgcn_readfirstlane(tid / D);
+    const float* vb = H.UVt + pt * ROWS * D + ii;
+    float uv[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) uv[r] = vb[r * D];
+    LDS_AS float* cbar = (LDS_AS float*)sm;  // [G][D]
+    LDS_AS float* red = cbar + G * D;          // [PARTS][G][D]
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int i = tid + 256 * k, hh = i / D, jj = i - hh * D;
+        if (hh < G) {
+            const int bv = H.bitsV[jj];
+            cbar[i] = (bv && L[k] > 0.0f) ? H.stepV[jj] * (A[k] / L[k] - (float)(1 << (bv - 1)) + 0.5f) : 0.0f;
+        }
     }
-    __syncthreads();
-    for (int i = tid; i < G * d; i += 256) {
-        const int hh = i / d, ii = i % d;
-        float o = H.muV[ii];
-#pragma unroll 8
-        for (int jj = 0; jj < d; ++jj) o = fmaf(H.UVt[jj * d + ii], cbar[hh * d + jj], o);
-        out[((int64_t)z * a.n_kv * G + h * G + hh) * d + ii] = o;
+    lds_barrier();
+    // out = mu_V + U_V cbar: UVt[j * d + i] = U_V[i][j]; thread (ii, pt) sums rows j of its slice
+    for (int hh = 0; hh < G; ++hh) {
+        float o = 0.0f;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) o = fmaf(uv[r], cbar[hh * D + pt * ROWS + r], o);
+        red[(pt * G + hh) * D + ii] = o;
+    }
+    lds_barrier();
+    for (int i = tid; i < G * D; i += 256) {
+        const int hh = i / D, i2 = i - hh * D;
+        float o = H.muV[i2];
+#pragma unroll
+        for (int p2 = 0; p2 < PARTS; ++p2) o += red[(p2 * G + hh) * D + i2];
+        out[(zh * G + hh) * D + i2] = o;
     }
 }
 
@@ -487,25 +689,27 @@ struct Variant {
     int rb, nqb, nvb;
 };
 // compile-time (row blocks, score operand blocks, value column blocks) bounds available;
-// value column blocks are a multiple of 4 (a quarter per wave)
-constexpr Variant kVariants[] = {{1, 4, 8},  {1, 6, 12},  {1, 8, 16},  {1, 12, 24}, {1, 12, 32},
-                                 {2, 6, 12}, {2, 8, 16},  {2, 12, 24}, {2, 12, 32}, {3, 6, 12},
-                                 {3, 8, 16}, {3, 12, 24}, {3, 12, 32}, {4, 6, 12}, {4, 8, 16},
-                                 {4, 12, 24}, {4, 12, 32}};
+// (the operand blocks of a head must fit the bounds; unused blocks multiply zero)
+constexpr Variant kVariants[] = {{1, 4, 8},  {1, 6, 12}, {1, 8, 16}, {1, 12, 24}, {1, 12, 32}, {2, 6, 12},
+                                 {2, 8, 16}, {2, 12, 24}, {2, 12, 32}, {3, 6, 12}, {3, 8, 16}, {3, 12, 24},
+                                 {3, 12, 32}, {4, 6, 12}, {4, 8, 16}, {4, 12, 24}, {4, 12, 32}};
 
 struct Plan {
     Variant v;
-    int nqb_max, nvb_max, tpg, wg_per_head;
-    size_t qa_bytes, qsc_bytes, part_bytes, cnt_bytes;
+    int nqb_max, nvb_max, tpg, wg_per_head, n_grp, wgs_per_cu;
+    size_t qa_bytes, qsc_bytes, part1_bytes, part2_bytes;
+    int64_t n_counters;
     DecodeArgs args;
     size_t lds;
 };
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, Plan& p) {
     const int G = cb->group, d = cb->d;
     const int RB = (G + 3) / 4;
+    const int PARTS = 256 / d;
     p.nqb_max = 0;
     p.nvb_max = 0;
     for (int h = 0; h < cb->n_kv; ++h) {
@@ -525,60 +729,54 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
                          p.nqb_max, p.nvb_max);
     const int64_t tiles = n_tiles_of(max_len);
     const int64_t total = tiles * cb->n_kv * (int64_t)n_seqs;
-    p.tpg = (int)std::max<int64_t>(1, (total + kTargetGroups - 1) / kTargetGroups);
+    // one wave per tile at a time: aim for every wave slot of the chip busy
+    const int64_t target = 256 * (int64_t)waves_for(p.v.rb, p.v.nqb, p.v.nvb) * kWaves;
+    p.tpg = (int)std::max<int64_t>(kWaves, (total + target - 1) / target * kWaves);
     p.wg_per_head = (int)((tiles + p.tpg - 1) / p.tpg);
-    p.qa_bytes = (size_t)n_seqs * cb->n_kv * p.nqb_max * RB * 1024;
-    p.qsc_bytes = (size_t)n_seqs * cb->n_kv * RB * 16 * sizeof(float);
-    p.part_bytes = (size_t)n_seqs * cb->n_kv * p.wg_per_head * G * (d + 2) * sizeof(float);
-    p.cnt_bytes = (size_t)n_seqs * cb->n_kv * sizeof(uint32_t);
+    p.n_grp = (p.wg_per_head + kMergeGroup - 1) / kMergeGroup;
+    const size_t ld = (size_t)d + 2;
+    p.qa_bytes = (size_t)n_seqs * cb->n_kv * p.v.nqb * RB * 1024;
+    p.qsc_bytes = (size_t)n_seqs * cb->n_kv * 16 * sizeof(float);
+    p.part1_bytes = (size_t)n_seqs * cb->n_kv * p.wg_per_head * G * ld * sizeof(float);
+    p.part2_bytes = (size_t)n_seqs * cb->n_kv * p.n_grp * G * ld * sizeof(float);
+    p.n_counters = (int64_t)n_seqs * cb->n_kv * (p.n_grp + 1);
+    if (p.n_counters > kCounterSlots)
+        return set_error(AATC_ERR_CAPACITY, "%d sequences x %d kv-heads need %lld arrival counters (at most %d); split the batch",
+                         n_seqs, cb->n_kv, (long long)p.n_counters, kCounterSlots);
     DecodeArgs& a = p.args;
     a.G = G;
     a.tile_bytes = 8 * cb->total_bits;
     a.tpg = p.tpg;
     a.wg_per_head = p.wg_per_head;
-    a.nqb_max = p.nqb_max;
-    auto al16 = [](size_t x) { return (int)((x + 15) & ~(size_t)15); };
-    a.off_qsc = al16((size_t)p.v.nqb * RB * 1024);
-    a.off_ccol = al16(a.off_qsc + RB * 16 * sizeof(float));
-    a.off_buf = al16(a.off_ccol + (size_t)d * 4 * sizeof(int16_t));
-    a.buf_bytes = al16(a.tile_bytes + 16);
-    // the epilogue reuses the tile buffers
-    const size_t epi = ((size_t)RB * 4 * 16 * p.nvb_max + kWaves * RB * 4 + (size_t)G * (d + 2)) * sizeof(float);
-    const size_t bufs = std::max(2 * (size_t)a.buf_bytes, epi);
-    a.off_P = al16(a.off_buf + bufs);
-    a.off_tm = al16(a.off_P + (size_t)RB * 16 * 64);
-    const size_t merge = ((size_t)2 * G * p.wg_per_head + G + (size_t)G * d) * sizeof(float);
-    p.lds = std::max((size_t)a.off_tm + kWaves * RB * 4 * sizeof(float), merge);
+    a.n_grp = p.n_grp;
+    a.buf_bytes = (int)al16(a.tile_bytes + 16);  // (+16: the value unpack may read one word past the tile)
+    a.wave_bytes = (int)al16(2 * (size_t)a.buf_bytes + (size_t)RB * 16 * 80);
+    // the epilogue and the merges reuse the buffers
+    const size_t epi = ((size_t)2 * kWaves * RB * 4 + (size_t)kWaves * RB * 4 * 16 * p.v.nvb) * sizeof(float);
+    const size_t mrg = ((size_t)G * d + (size_t)PARTS * G * d) * sizeof(float);
+    a.off_flag = (int)al16(std::max({(size_t)kWaves * a.wave_bytes, epi, mrg}));
+    p.lds = a.off_flag + 16;
+    p.wgs_per_cu = std::min<int>(waves_for(p.v.rb, p.v.nqb, p.v.nvb), (int)((160 * 1024) / p.lds));
     if (p.lds > 160 * 1024 - 256)
         return set_error(AATC_ERR_UNSUPPORTED, "decode needs %zu bytes of LDS per workgroup", p.lds);
     return AATC_OK;
 }
 
-template <int RB, int NQB, int NVB>
-int launch_decode(const Plan& p, dim3 grid, hipStream_t st, const DevHead* blob, const uint8_t* cache,
-                  const int32_t* ids, const int64_t* lens, const int8_t* qa, const float* qsc, float* part,
-                  uint32_t* counters, float* out) {
-    static size_t attr_lds = 0;  // dynamic LDS limit already granted to this instantiation
-    if (p.lds > attr_lds) {
-        HIP_TRY(hipFuncSetAttribute((const void*)decode_kernel<RB, NQB, NVB>,
+template <int RB, int NQB, int NVB, int D>
+int launch_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* blob, const uint8_t* cache,
+                  const int32_t* ids, const int64_t* lens, const uint16_t* q, uint8_t* qa, float* qsc, float* part1,
+                  float* part2, uint32_t* cnt1, uint32_t* cnt2, float* out) {
+    const DecodeArgs& a = p.args;
+    hipLaunchKernelGGL((qprep_kernel<RB, NQB, D>), dim3(a.n_kv, n_seqs), dim3(256), 0, st, blob, a.layer, a.n_kv, a.G,
+                       q, (uint32_t*)qa, qsc);
+    HIP_TRY(hipGetLastError());
+    if (p.lds > 64 * 1024)
+        HIP_TRY(hipFuncSetAttribute((const void*)decode_kernel<RB, NQB, NVB, D>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds));
-        attr_lds = p.lds;
-    }
-    hipLaunchKernelGGL((decode_kernel<RB, NQB, NVB>), grid, dim3(256), p.lds, st, blob, cache, p.args, ids, lens, qa,
-                       qsc, part, counters, out);
+    hipLaunchKernelGGL((decode_kernel<RB, NQB, NVB, D>), dim3(p.wg_per_head, a.n_kv, n_seqs), dim3(256), p.lds, st,
+                       blob, cache, a, ids, lens, qa, qsc, part1, part2, cnt1, cnt2, out);
     HIP_TRY(hipGetLastError());
     return AATC_OK;
-}
-
-template <int RB>
-void launch_qprep(const Plan& p, int d, int layer, int n_kv, int G, int n_seqs, hipStream_t st, const DevHead* blob,
-                  const uint16_t* q, int8_t* qa, float* qsc, uint32_t* counters) {
-    if (d == 64)
-        hipLaunchKernelGGL((qprep_kernel<RB, 64>), dim3(n_kv, n_seqs), dim3(256), 0, st, blob, layer, n_kv, G,
-                           p.nqb_max, q, qa, qsc, counters);
-    else
-        hipLaunchKernelGGL((qprep_kernel<RB, 128>), dim3(n_kv, n_seqs), dim3(256), 0, st, blob, layer, n_kv, G,
-                           p.nqb_max, q, qa, qsc, counters);
 }
 
 }  // namespace
@@ -591,7 +789,8 @@ extern "C" int aatc_decode_workspace_bytes(const aatc_codebook* cb, int32_t n_se
         Plan p;
         int rc = make_plan(cb, layer, n_seqs, max_len, p);
         if (rc) return rc;
-        worst = std::max(worst, al256(p.qa_bytes) + al256(p.qsc_bytes) + al256(p.part_bytes) + p.cnt_bytes);
+        worst = std::max(worst, kCounterBytes + al256(p.qa_bytes) + al256(p.qsc_bytes) + al256(p.part1_bytes) +
+                                    p.part2_bytes);
     }
     *bytes = worst;
     return AATC_OK;
@@ -613,13 +812,16 @@ extern "C" int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob
     Plan p;
     rc = make_plan(cb, layer, n_seqs, max_len, p);
     if (rc) return rc;
-    const size_t need = al256(p.qa_bytes) + al256(p.qsc_bytes) + al256(p.part_bytes) + p.cnt_bytes;
+    const size_t need =
+        kCounterBytes + al256(p.qa_bytes) + al256(p.qsc_bytes) + al256(p.part1_bytes) + p.part2_bytes;
     if (ws_bytes < need) return set_error(AATC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
     uint8_t* wsp = (uint8_t*)workspace;
-    int8_t* qa = (int8_t*)wsp;
-    float* qsc = (float*)(wsp + al256(p.qa_bytes));
-    float* part = (float*)(wsp + al256(p.qa_bytes) + al256(p.qsc_bytes));
-    uint32_t* counters = (uint32_t*)(wsp + al256(p.qa_bytes) + al256(p.qsc_bytes) + al256(p.part_bytes));
+    uint32_t* cnt1 = (uint32_t*)wsp;  // [n_seqs][n_kv][n_grp] group arrivals
+    uint32_t* cnt2 = cnt1 + (size_t)n_seqs * cb->n_kv * p.n_grp;  // [n_seqs][n_kv] group-merger arrivals
+    uint8_t* qa = wsp + kCounterBytes;  // [n_seqs][n_kv][NQB][RB][64][16] score operands
+    float* qsc = (float*)(qa + al256(p.qa_bytes));  // [n_seqs][n_kv][16] digit scales
+    float* part1 = (float*)((uint8_t*)qsc + al256(p.qsc_bytes));
+    float* part2 = (float*)((uint8_t*)part1 + al256(p.part1_bytes));
     DecodeArgs& a = p.args;
     a.layer = layer;
     a.n_kv = cb->n_kv;
@@ -628,19 +830,13 @@ extern "C" int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob
     a.max_len = max_len;
     const DevHead* blob = (const DevHead*)d_blob;
     hipStream_t st = (hipStream_t)stream;
-    const int G = cb->group;
-    switch (p.v.rb) {
-        case 1: launch_qprep<1>(p, cb->d, layer, cb->n_kv, G, n_seqs, st, blob, q, qa, qsc, counters); break;
-        case 2: launch_qprep<2>(p, cb->d, layer, cb->n_kv, G, n_seqs, st, blob, q, qa, qsc, counters); break;
-        case 3: launch_qprep<3>(p, cb->d, layer, cb->n_kv, G, n_seqs, st, blob, q, qa, qsc, counters); break;
-        default: launch_qprep<4>(p, cb->d, layer, cb->n_kv, G, n_seqs, st, blob, q, qa, qsc, counters); break;
-    }
-    HIP_TRY(hipGetLastError());
-    dim3 grid(p.wg_per_head, cb->n_kv, n_seqs);
     const uint8_t* c = (const uint8_t*)cache->data;
-#define AATC_DECODE_CASE(rb_, nqb_, nvb_)                                                                     \
-    if (p.v.rb == rb_ && p.v.nqb == nqb_ && p.v.nvb == nvb_)                                                  \
-        return launch_decode<rb_, nqb_, nvb_>(p, grid, st, blob, c, seq_ids, seq_lens, qa, qsc, part, counters, out);
+#define AATC_DECODE_CASE(rb_, nqb_, nvb_)                                                                         \
+    if (p.v.rb == rb_ && p.v.nqb == nqb_ && p.v.nvb == nvb_)                                                      \
+        return cb->d == 64 ? launch_decode<rb_, nqb_, nvb_, 64>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, qa,  \
+                                                                qsc, part1, part2, cnt1, cnt2, out)                \
+                           : launch_decode<rb_, nqb_, nvb_, 128>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, qa, \
+                                                                 qsc, part1, part2, cnt1, cnt2, out);
     AATC_DECODE_CASE(1, 4, 8)
     AATC_DECODE_CASE(1, 6, 12)
     AATC_DECODE_CASE(1, 8, 16)
