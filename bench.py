@@ -15,6 +15,7 @@ streaming write, untimed) before every timed encode and decode.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +27,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_kernel_llama128k_pmc.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "quantized_attention_klt_amd", "csrc", "decode.hip")
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "decode-attn effective HBM GB/s (% of peak) + encode tokens/s, 128k ctx, 2.75 b/elem"
 
@@ -59,6 +62,28 @@ def build_inputs(wname: str, ctx: int):
     qb = synth.to_bf16_bits(synth.decode_queries(w, hms, 0, 0))[None]
     log(f"inputs generated ({time.perf_counter() - t2:.1f}s)")
     return w, cb, kb, vb, qb, t2 - t0
+
+
+def source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the split-decode kernel from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or None when the
+    summary is missing or was taken from another revision of the kernel source."""
+    try:
+        fields = dict(l.split(":", 1) for l in open(PMC_SUMMARY) if ":" in l and not l.startswith("#"))
+    except OSError:
+        return None
+    fields = {k.strip(): v.strip() for k, v in fields.items()}
+    if fields.get("source_sha256_16") != source_hash():
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(wname: str, n_tokens: int = 16384):
@@ -102,6 +127,8 @@ def main():
     ap.add_argument("--workload", default="llama_128k")
     ap.add_argument("--ctx", type=int, default=0, help="override context length")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path has no multi-GPU "
@@ -146,6 +173,7 @@ def main():
         q.flush_write(flush)
         decode()
     torch.cuda.synchronize()
+    q.profile_begin(args.steps)  # device events around the split-decode kernel of each step
     t0 = time.perf_counter()
     for i in range(args.steps):
         q.flush_write(flush)
@@ -158,14 +186,25 @@ def main():
         ev[i][3].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    kern_ms = q.profile_end(args.steps)
     enc_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     dec_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    if args.copy_probe_mb:
+        a = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_probe_mb} MiB read + written")
 
     tb = cb.tile_bytes
     n_tiles = (ctx + 63) // 64
     cache_bytes = w.n_kv * n_tiles * tb
     side = 2 * w.n_kv * w.d * w.d * 4 + w.n_q * w.d * 2 + w.n_q * w.d * 4
     dec_bytes = cache_bytes + side
+    # the split-decode kernel alone: the packed cache, U_V and mu_V, and the output
+    kern_bytes = cache_bytes + w.n_kv * (w.d * w.d + w.d) * 4 + w.n_q * w.d * 4
+    kern_s = float(kern_ms.mean()) / 1e3
+    kern_gbs = kern_bytes / kern_s / 1e9
     enc_bytes = 2 * ctx * w.n_kv * w.d * 2 + cache_bytes
     dec_s = dec_ms.mean() / 1e3
     enc_s = enc_ms.mean() / 1e3
@@ -189,6 +228,7 @@ def main():
                    "head_dim": w.d, "ctx": ctx, "batch": 1, "bits_per_element": w.avg_bits,
                    "step": "prefill-encode of ctx tokens + one decode-attention step"},
         "decode_ms": round(float(dec_ms.mean()), 4),
+        "decode_bytes": dec_bytes,
         "decode_ms_min": round(float(dec_ms.min()), 4),
         "decode_frac_of_peak": round(dec_gbs / HBM_PEAK_GBS, 4),
         "encode_ms": round(float(enc_ms.mean()), 4),
@@ -197,10 +237,11 @@ def main():
         "compression_ratio": round(16.0 / w.avg_bits, 4),
         "calibration_s": round(calib_s, 3),
         "wall_s_timed_region": round(wall, 3),
-        "roofline": {"kernel": "decode_attention (qtransform + split + combine)", "bound": "hbm",
-                     "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "algorithmic_bytes": dec_bytes},
+        "roofline": {"kernel": "decode_kernel (split decode + merge + inverse transform)", "bound": "hbm",
+                     "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "algorithmic_bytes": kern_bytes, "kernel_ms": round(kern_s * 1e3, 4),
+                     "source_sha256_16": source_hash()},
         "roofline_encode": {"kernel": "encode", "bound": "hbm", "achieved": round(enc_gbs, 2),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(enc_gbs / HBM_PEAK_GBS, 4),
                             "mfma_tflops": round(enc_flops / enc_s / 1e12, 2),

@@ -222,6 +222,16 @@ int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob, const aat
  * evict the device's last-level cache between timed repetitions).  Errors: HIP. */
 int aatc_flush_write(void* d_buf, size_t bytes, void* stream);
 
+/* Kernel timing for measurement: after aatc_profile_begin(n) the next n calls of
+ * aatc_decode_attention (any thread, current device) record a pair of device events
+ * around their split-decode kernel on the call's stream (the query-preparation kernel
+ * before it is not included).  aatc_profile_end waits for those events and writes the
+ * kernel durations in milliseconds to ms[0 .. *n_out) (ms holds the n given to begin),
+ * then releases the events.  Meant for benchmarks, not for concurrent production use.
+ * Errors: INVALID_ARG (n < 1, profiling already active / not active), HIP. */
+int aatc_profile_begin(int32_t n);
+int aatc_profile_end(float* ms, int32_t* n_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,7 +51,7 @@ EXPORTS = [
     "aatc_codebook_head", "aatc_codebook_save", "aatc_codebook_load", "aatc_codebook_free",
     "aatc_codebook_device_bytes", "aatc_codebook_upload", "aatc_cache_bytes", "aatc_encode",
     "aatc_encode_coeffs", "aatc_decode_workspace_bytes", "aatc_decode_attention",
-    "aatc_flush_write",
+    "aatc_flush_write", "aatc_profile_begin", "aatc_profile_end",
 ]
 
 _lib = None
@@ -95,6 +95,8 @@ def load() -> C.CDLL:
         "aatc_decode_attention": ([P, P, C.POINTER(Cache), i32, i32, P, P, i64, P, P, P, C.c_size_t, P],
                                   C.c_int),
         "aatc_flush_write": ([P, C.c_size_t, P], C.c_int),
+        "aatc_profile_begin": ([i32], C.c_int),
+        "aatc_profile_end": ([C.POINTER(C.c_float), C.POINTER(i32)], C.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -289,3 +291,16 @@ def decode_attention(cb: Codebook, d_blob, cache: Cache, layer: int, seq_ids, se
 
 def flush_write(buf, stream=None):
     _check(load().aatc_flush_write(_dev(buf), buf.numel() * buf.element_size(), _stream(stream)))
+
+
+def profile_begin(n: int):
+    """aatc_profile_begin: time the split-decode kernel of the next n decode calls."""
+    _check(load().aatc_profile_begin(n))
+
+
+def profile_end(n: int) -> np.ndarray:
+    """aatc_profile_end: the recorded kernel durations (ms) of the calls since profile_begin(n)."""
+    ms = np.zeros(n, np.float32)
+    got = C.c_int32(0)
+    _check(load().aatc_profile_end(ms.ctypes.data_as(C.POINTER(C.c_float)), C.byref(got)))
+    return ms[:got.value].copy()

@@ -40,6 +40,8 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
+#include <vector>
 
 #include "hip_common.h"
 
@@ -762,6 +764,30 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     return AATC_OK;
 }
 
+// Measurement hook (aatc_profile_begin / aatc_profile_end): event pairs recorded around
+// the split-decode kernel of the next calls.
+struct Profile {
+    std::mutex mu;
+    bool active = false;
+    std::vector<hipEvent_t> ev;  // 2 per call slot
+    int used = 0;
+};
+Profile& profile() {
+    static Profile p;
+    return p;
+}
+
+// the event pair for this call, or nulls when not profiling (or out of slots)
+void profile_slot(hipEvent_t& a, hipEvent_t& b) {
+    Profile& P = profile();
+    std::lock_guard<std::mutex> lk(P.mu);
+    a = b = nullptr;
+    if (!P.active || 2 * (P.used + 1) > (int)P.ev.size()) return;
+    a = P.ev[2 * P.used];
+    b = P.ev[2 * P.used + 1];
+    ++P.used;
+}
+
 template <int RB, int NQB, int NVB, int D>
 int launch_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* blob, const uint8_t* cache,
                   const int32_t* ids, const int64_t* lens, const uint16_t* q, uint8_t* qa, float* qsc, float* part1,
@@ -773,13 +799,56 @@ int launch_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* blob
     if (p.lds > 64 * 1024)
         HIP_TRY(hipFuncSetAttribute((const void*)decode_kernel<RB, NQB, NVB, D>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds));
+    hipEvent_t e0, e1;
+    profile_slot(e0, e1);
+    if (e0) HIP_TRY(hipEventRecord(e0, st));
     hipLaunchKernelGGL((decode_kernel<RB, NQB, NVB, D>), dim3(p.wg_per_head, a.n_kv, n_seqs), dim3(256), p.lds, st,
                        blob, cache, a, ids, lens, qa, qsc, part1, part2, cnt1, cnt2, out);
     HIP_TRY(hipGetLastError());
+    if (e1) HIP_TRY(hipEventRecord(e1, st));
     return AATC_OK;
 }
 
 }  // namespace
+
+extern "C" int aatc_profile_begin(int32_t n) {
+    if (n < 1) return set_error(AATC_ERR_INVALID_ARG, "need n >= 1");
+    Profile& P = profile();
+    std::lock_guard<std::mutex> lk(P.mu);
+    if (P.active) return set_error(AATC_ERR_INVALID_ARG, "profiling already active");
+    P.ev.assign(2 * (size_t)n, nullptr);
+    for (auto& e : P.ev) {
+        hipError_t rc = hipEventCreate(&e);
+        if (rc != hipSuccess) {
+            for (auto& f : P.ev)
+                if (f) (void)hipEventDestroy(f);
+            P.ev.clear();
+            return set_error(AATC_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(rc));
+        }
+    }
+    P.used = 0;
+    P.active = true;
+    return AATC_OK;
+}
+
+extern "C" int aatc_profile_end(float* ms, int32_t* n_out) {
+    if (!ms || !n_out) return set_error(AATC_ERR_INVALID_ARG, "null pointer");
+    Profile& P = profile();
+    std::lock_guard<std::mutex> lk(P.mu);
+    if (!P.active) return set_error(AATC_ERR_INVALID_ARG, "profiling not active");
+    int rc = AATC_OK;
+    for (int i = 0; i < P.used && rc == AATC_OK; ++i) {
+        hipError_t e = hipEventSynchronize(P.ev[2 * i + 1]);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms[i], P.ev[2 * i], P.ev[2 * i + 1]);
+        if (e != hipSuccess) rc = set_error(AATC_ERR_HIP, "profile events: %s", hipGetErrorString(e));
+    }
+    *n_out = P.used;
+    for (auto& e : P.ev) (void)hipEventDestroy(e);
+    P.ev.clear();
+    P.used = 0;
+    P.active = false;
+    return rc;
+}
 
 extern "C" int aatc_decode_workspace_bytes(const aatc_codebook* cb, int32_t n_seqs, int64_t max_len, size_t* bytes) {
     if (!cb || !bytes) return set_error(AATC_ERR_INVALID_ARG, "null pointer");
