@@ -132,7 +132,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path has no multi-GPU "
-              "component; see DESIGN.md for how it would shard.", file=sys.stderr)
+              "component (it would shard by kv-head, by sequence, or by context with an all-gather of "
+              "the split partials).", file=sys.stderr)
         sys.exit(2)
 
     import torch

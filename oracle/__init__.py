@@ -20,7 +20,7 @@ function cites the passage of the AATC pages it follows:
   bit count, bandwidth-bound decoding.
 
 Readings taken where the pages are silent, garbled or contradict each other
-are listed in DESIGN.md (section "Readings").  Parity status of each function:
+are stated in the docstring of the function that takes them.  Parity status:
 every public function is pinned by a CPU test against closed forms, brute
 force or textbook values (tests/test_oracle_*.py); the packed layout is ours
 and is pinned by an independent bit-by-bit implementation in the tests.
