@@ -18,7 +18,12 @@ Packed layout (ours; the pages fix only a fixed per-token bit count, p3 abstract
 * V block (next 8*B_V bytes): piece p owns a slab of 64*w_p bits starting at bit
   64*O_p.  Slab word r (32 bits) holds token slots r*(32/w) + k, k < 32/w, with slot
   k's field at word bits [8*(k%4) + w*(k//4), +w).
-* Slots not yet written are zero.
+* Every byte of a written slot's key record is stored with its most significant bit
+  inverted (XOR 0x80): an extraction that masks one field per byte then reads, as a
+  two's-complement int8, field * 2^(bit position) when the field stays below bit 7 and
+  that value minus 128 when it ends at bit 7 -- a constant per byte position that a
+  reader can correct for.
+* Slots not yet written are zero (all of their bytes, key records included).
 """
 from __future__ import annotations
 
@@ -132,7 +137,19 @@ def pack_cache(codesK: np.ndarray, codesV: np.ndarray, bK: np.ndarray, bV: np.nd
         pos = base[:, None] + np.arange(w)[None, :]
         bitarr[pos] = _field_bits(vals, w)
         off += w
-    return np.packbits(bitarr, bitorder="little")
+    out = np.packbits(bitarr, bitorder="little")
+    _flip_key_bytes(out, n, BK, 8 * (BK + BV))
+    return out
+
+
+def _flip_key_bytes(buf: np.ndarray, n: int, BK: int, tbytes: int) -> None:
+    """Invert bit 7 of every byte of the key records of token slots 0..n-1, in place."""
+    tok = np.arange(n)
+    tile, slot = tok // TILE, tok % TILE
+    for r in range(BK // 32):
+        byte0 = tile * tbytes + 4 * (64 * r + slot)
+        for k in range(4):
+            buf[byte0 + k] ^= np.uint8(0x80)
 
 
 def unpack_cache(cache: np.ndarray, bK: np.ndarray, bV: np.ndarray, n: int):
@@ -142,7 +159,9 @@ def unpack_cache(cache: np.ndarray, bK: np.ndarray, bV: np.ndarray, n: int):
     kbits = 64 * BK
     tbits = 64 * (BK + BV)
     n_tiles = (n + TILE - 1) // TILE
-    bitarr = np.unpackbits(np.asarray(cache, np.uint8)[: n_tiles * tbits // 8], bitorder="little")
+    raw = np.array(np.asarray(cache, np.uint8)[: n_tiles * tbits // 8])
+    _flip_key_bytes(raw, n, BK, tbits // 8)
+    bitarr = np.unpackbits(raw, bitorder="little")
     tok = np.arange(n)
     tile = tok // TILE
     slot = tok % TILE

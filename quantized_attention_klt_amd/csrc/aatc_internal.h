@@ -13,7 +13,7 @@ namespace aatc {
 constexpr int kTile = 64;        // token slots per tile
 constexpr int kMaxD = 128;       // largest head_dim
 constexpr int kMaxPieces = 512;  // >= 3 pieces per channel * 128 channels
-constexpr int kMaxQB = 32;       // score MFMA operand blocks per head (key record <= 32 words)
+constexpr int kMaxQM = 16;       // score MFMAs per token group (<= 32 words x 8 fields / 16)
 constexpr int kMaxVB = 32;       // value column blocks of 16 pieces per head
 constexpr int kKeyAlign = 32;    // key bits per token are a multiple of one 32-bit word
 
@@ -53,6 +53,7 @@ struct alignas(256) DevHead {
     uint16_t UVhi[kMaxD * kMaxD];
     uint16_t UVlo[kMaxD * kMaxD];
     float muV[kMaxD];
+    float obias[kMaxD];           // mu_V - U_V (step_V * (2^(b-1) - 1/2)): output of all-zero codes
     float biasK[kMaxD];           // mu_K (U_hi + U_lo), fp64 sum rounded once
     float biasV[kMaxD];
     float stepK[kMaxD], stepV[kMaxD];
@@ -61,17 +62,19 @@ struct alignas(256) DevHead {
     int32_t pieceK[kMaxPieces];
     int32_t pieceV[kMaxPieces];
     // ---- decode schedule -------------------------------------------------------------
-    // Score operand blocks ("qblocks"), nqb[0] of 4-bit mode, then nqb[1] 2-bit, nqb[2]
-    // 1-bit.  For qblock q and lane group g (lanes 16g..16g+15 of a wave), kq_dw[q][g][i]
-    // is the key-record word extracted (mode 4 uses two words, the others one; a 1-bit
-    // qblock takes half a word: bits 4*(g&1) .. of each byte lane).  kq_map[q][g][16] gives
-    // the channel and shift (chan | e << 8) of each int8 operand slot, -1 for slots that
-    // multiply zero.
-    int32_t nqb[3];
+    // Score MFMAs: nqm per token group.  The B operand of lane group g (lanes 16g..16g+15,
+    // K-slots 16g..16g+15) in MFMA m is four dwords; dword i is key-record word
+    // kq_word[m][g][i] of the lane's token ANDed with kq_mask[m][g][i], which keeps one
+    // field per byte.  kq_slot[m][g][4i+b] describes the field kept in byte b:
+    // chan | shift << 8 | pos << 11 | flip << 14 (pos = bit position in the byte; flip =
+    // the field ends at bit 7, so the stored inverted bit 7 makes the byte read 128 low),
+    // 0xFFFF for an empty byte.
+    int32_t nqm;
     int32_t nvb[3];  // value column blocks of widths 4, 2, 1 (16 pieces each)
-    int32_t pad1[2];
-    int16_t kq_dw[kMaxQB][4][2];
-    int16_t kq_map[kMaxQB][4][16];
+    int32_t pad1[4];
+    int16_t kq_word[kMaxQM][4][4];
+    uint32_t kq_mask[kMaxQM][4][4];
+    uint16_t kq_slot[kMaxQM][4][16];
     // value column blocks: first word of each column's slab inside the value block
     // (padding columns repeat a real slab), and chan | e << 8 (-1 for padding)
     int16_t vb_slab[kMaxVB][16];

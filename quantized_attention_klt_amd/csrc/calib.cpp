@@ -300,74 +300,64 @@ static void make_pieces(const std::vector<int32_t>& bits, std::vector<Piece>& ou
     total = off;
 }
 
-// Decode schedule of one head (see DevHead): which key-record words each lane group
-// unpacks for each score MFMA, which channel/shift each int8 slot carries, and the value
+// Decode schedule of one head (see DevHead).  Scores: every key-record word is split
+// into "dwords", one per field position (a byte holds 2 nibbles, 4 crumbs or 8 bits, or a
+// mix at a width boundary); each dword keeps one field per byte under a mask.  Dwords
+// fill the score MFMAs in record order, 16 per MFMA (four per lane group).  Values: the
 // pieces grouped into MFMA column blocks of one width.
 static int build_decode_schedule(const HeadCB& H, DevHead& D) {
-    for (int q = 0; q < kMaxQB; ++q)
+    for (int m = 0; m < kMaxQM; ++m)
         for (int g = 0; g < 4; ++g) {
-            D.kq_dw[q][g][0] = D.kq_dw[q][g][1] = 0;
-            for (int i = 0; i < 16; ++i) D.kq_map[q][g][i] = -1;
+            for (int i = 0; i < 4; ++i) D.kq_word[m][g][i] = 0, D.kq_mask[m][g][i] = 0u;
+            for (int i = 0; i < 16; ++i) D.kq_slot[m][g][i] = 0xFFFF;
         }
-    // key record: bit position -> (width, chan | e << 8) of the piece starting there
-    std::vector<int> at_w(H.BK + 1, 0), at_id(H.BK + 1, -1);
-    int n_w[3] = {0, 0, 0}, o_w[3] = {-1, -1, -1};
-    for (const Piece& p : H.pK) {
-        at_w[p.offset] = p.width;
-        at_id[p.offset] = p.chan | (p.shift << 8);
-        int m = p.width == 4 ? 0 : p.width == 2 ? 1 : 2;
-        if (n_w[m] == 0) o_w[m] = p.offset;
-        n_w[m]++;
-    }
-    auto field = [&](int bit, int w) -> int16_t {
-        if (bit < 0 || bit >= H.BK || at_w[bit] != w) return -1;
-        return (int16_t)at_id[bit];
+    struct Field {
+        int chan, w, shift, pos;
     };
-    int q = 0;
-    const int width_of[3] = {4, 2, 1};
-    const int words_per_qb[3] = {8, 4, 2};
-    for (int m = 0; m < 3; ++m) {
-        std::vector<int> dws;
-        if (n_w[m]) {
-            int w = width_of[m];
-            int first = o_w[m] / 32, last = (o_w[m] + n_w[m] * w - 1) / 32;
-            for (int r = first; r <= last; ++r) dws.push_back(r);
-        }
-        int nq = ((int)dws.size() + words_per_qb[m] - 1) / words_per_qb[m];
-        D.nqb[m] = nq;
-        for (int k = 0; k < nq; ++k, ++q) {
-            if (q >= kMaxQB) return AATC_ERR_UNSUPPORTED;
-            for (int g = 0; g < 4; ++g) {
-                for (int od = 0; od < 4; ++od)
-                    for (int i = 0; i < 4; ++i) {
-                        int idx, bit;
-                        if (m == 0) {  // 4-bit: two words per group, nibble 2i + (od & 1)
-                            idx = 8 * k + 2 * g + (od >> 1);
-                            if (idx >= (int)dws.size()) continue;
-                            bit = 32 * dws[idx] + 4 * (2 * i + (od & 1));
-                        } else if (m == 1) {  // 2-bit: one word per group, crumb 4i + od
-                            idx = 4 * k + g;
-                            if (idx >= (int)dws.size()) continue;
-                            bit = 32 * dws[idx] + 2 * (4 * i + od);
-                        } else {  // 1-bit: half a word per group, bit 8i + 4(g&1) + od
-                            idx = 2 * k + (g >> 1);
-                            if (idx >= (int)dws.size()) continue;
-                            bit = 32 * dws[idx] + 8 * i + 4 * (g & 1) + od;
-                        }
-                        D.kq_map[q][g][od * 4 + i] = field(bit, width_of[m]);
-                    }
-                for (int t = 0; t < (m == 0 ? 2 : 1); ++t) {
-                    int idx = m == 0 ? 8 * k + 2 * g + t : m == 1 ? 4 * k + g : 2 * k + (g >> 1);
-                    D.kq_dw[q][g][t] = (int16_t)(idx < (int)dws.size() ? dws[idx] : 0);
-                }
+    struct Dword {
+        int word;
+        uint32_t mask;
+        uint16_t slot[4];
+    };
+    std::vector<Dword> dws;
+    const int WK = H.BK / 32;
+    for (int r = 0; r < WK; ++r) {
+        std::vector<Field> fb[4];
+        for (const Piece& p : H.pK)
+            if (p.offset >= 32 * r && p.offset < 32 * r + 32) {
+                const int bit = p.offset - 32 * r;
+                if (bit / 8 != (bit + p.width - 1) / 8) return AATC_ERR_UNSUPPORTED;  // fields never straddle bytes
+                fb[bit / 8].push_back({p.chan, p.width, p.shift, bit % 8});
             }
+        size_t nd = 0;
+        for (int b = 0; b < 4; ++b) nd = std::max(nd, fb[b].size());
+        for (size_t j = 0; j < nd; ++j) {
+            Dword dw{r, 0u, {0xFFFF, 0xFFFF, 0xFFFF, 0xFFFF}};
+            for (int b = 0; b < 4; ++b) {
+                if (j >= fb[b].size()) continue;
+                const Field& f = fb[b][j];
+                dw.mask |= ((1u << f.w) - 1u) << (8 * b + f.pos);
+                const int flip = f.pos + f.w == 8 ? 1 : 0;
+                dw.slot[b] = (uint16_t)(f.chan | (f.shift << 8) | (f.pos << 11) | (flip << 14));
+            }
+            dws.push_back(dw);
         }
+    }
+    const int nqm = ((int)dws.size() + 15) / 16;
+    if (nqm > kMaxQM) return AATC_ERR_UNSUPPORTED;
+    D.nqm = std::max(nqm, 1);
+    for (size_t k = 0; k < dws.size(); ++k) {
+        const int m = (int)k / 16, g = ((int)k / 4) % 4, i = (int)k % 4;
+        D.kq_word[m][g][i] = (int16_t)dws[k].word;
+        D.kq_mask[m][g][i] = dws[k].mask;
+        for (int b = 0; b < 4; ++b) D.kq_slot[m][g][4 * i + b] = dws[k].slot[b];
     }
     // value column blocks
     for (int cb = 0; cb < kMaxVB; ++cb)
         for (int c = 0; c < 16; ++c) D.vb_slab[cb][c] = 0, D.vb_map[cb][c] = -1;
     for (int j = 0; j < kMaxD; ++j)
         for (int t = 0; t < 4; ++t) D.chan_cols[j][t] = -1;
+    const int width_of[3] = {4, 2, 1};
     int cb = 0;
     for (int m = 0; m < 3; ++m) {
         std::vector<const Piece*> ps;
@@ -460,6 +450,14 @@ int finalize(aatc_codebook* cb) {
             D.stepV[j] = H.bV[j] ? H.stepV[j] : 0.0f;
             D.invK[j] = H.bK[j] ? (float)(1.0 / (double)H.stepK[j]) : 0.0f;
             D.invV[j] = H.bV[j] ? (float)(1.0 / (double)H.stepV[j]) : 0.0f;
+        }
+        // output offset: the dequantized value coefficient is step (code - 2^(b-1) + 1/2), so
+        // o = mu_V + U_V (step * code_mean) - U_V (step * (2^(b-1) - 1/2))
+        for (int i = 0; i < d; ++i) {
+            double o = H.muV[i];
+            for (int j = 0; j < d; ++j)
+                if (H.bV[j] > 0) o -= H.UV[(size_t)i * d + j] * (double)H.stepV[j] * ((double)(1 << (H.bV[j] - 1)) - 0.5);
+            D.obias[i] = (float)o;
         }
         for (size_t p = 0; p < H.pK.size(); ++p)
             D.pieceK[p] = H.pK[p].chan | (H.pK[p].width << 8) | (H.pK[p].shift << 12) | (H.pK[p].offset << 16);

@@ -34,7 +34,7 @@
 //              applies U_V and mu_V.  Arrival counters wrap to zero on the last arrival
 //              (atomic increment modulo the member count), so a zeroed workspace stays
 //              ready for the next call.
-// Inner loops are branch-free straight-line code (compile-time bounds NQB score operand
+// Inner loops are branch-free straight-line code (compile-time bounds NQM score MFMAs per
 // blocks and NVB value column blocks; the unpack mode of a block is a uniform select).
 #include <hip/hip_runtime.h>
 
@@ -68,14 +68,15 @@ constexpr float kHeadroom = 2.0f;    // log2 headroom added to the reference max
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kM4 = 0x0F0F0F0Fu, kM2 = 0x03030303u, kM1 = 0x01010101u;
 constexpr float kDig1 = 1.0f / 254.0f, kDig2 = 1.0f / 64516.0f;
+constexpr int kQscStride = 80;  // floats per (sequence, kv-head) in the query-scale buffer
 
 struct DecodeArgs {
     int layer, n_kv, G, n_seqs_cache;
     int64_t n_tiles_cap;
     int64_t max_len;
     int tile_bytes, tpg, wg_per_head, n_grp;
-    // LDS carve-up (bytes): per wave two tile buffers + the probability operand
-    int buf_bytes, wave_bytes, off_flag;
+    // LDS carve-up (bytes): per wave a ring of nbw tile buffers
+    int nbw, buf_bytes, wave_bytes, off_ksched, off_flag;
 };
 
 // LDS-only workgroup barrier: this wave's LDS operations are complete, then s_barrier.
@@ -123,11 +124,15 @@ __device__ __forceinline__ float row16_sum(float x) {
 }
 
 // Stream one tile (bytes, a multiple of 16) from global memory into LDS with one wave:
-// 1 KiB per instruction, 16 bytes per lane (LDS address = chunk base + 16 * lane).
+// 1 KiB per instruction, 16 bytes per lane (LDS address = chunk base + 16 * lane).  The
+// loads carry the non-temporal hint (cache policy bit 1): the cache is read once per step,
+// and with the default policy these direct-to-LDS loads stream at about half the rate.
+constexpr int kStreamPolicy = 2;
 __device__ __forceinline__ void load_tile(const uint8_t* src, LDS_AS uint8_t* lds, int bytes, int lane) {
     for (int off = 0; off < bytes; off += 1024) {
         const int o = off + 16 * lane;
-        if (o < bytes) __builtin_amdgcn_global_load_lds((const void*)(src + o), (LDS_AS void*)(lds + off), 16, 0, 0);
+        if (o < bytes)
+            __builtin_amdgcn_global_load_lds((const void*)(src + o), (LDS_AS void*)(lds + off), 16, 0, kStreamPolicy);
     }
 }
 
@@ -217,19 +222,20 @@ __device__ __forceinline__ void merge_cols(const float* src, int n, int G, int t
 // order = the key unpack schedule), plus the per-head digit scale (max |q'' 2^top| / 127).
 // Every global read is issued in one batch so that a cold codebook costs one latency.
 // ---------------------------------------------------------------------------------------
-template <int RB, int NQB, int D>
+template <int RB, int NQM, int D>
 __global__ __launch_bounds__(256) void qprep_kernel(const DevHead* __restrict__ blob, int layer, int n_kv, int G,
                                                     const uint16_t* __restrict__ q, uint32_t* __restrict__ qa_out,
                                                     float* __restrict__ qscale_out) {
     constexpr int PARTS = 256 / D;           // row slices of U_K per column
     constexpr int ROWS = D / PARTS;          // rows per slice
     constexpr int QPT = 16 * D / 256;        // query elements per thread (<= 16 heads)
-    constexpr int KPT = (NQB * 64 + 255) / 256;
+    constexpr int KPT = (NQM * 64 + 255) / 256;
     typedef float f4 __attribute__((ext_vector_type(4)));
     __shared__ __attribute__((aligned(16))) float qf[16 * D];
     __shared__ float ps[PARTS * 16 * D];
     __shared__ int smax[16];
-    __shared__ int16_t kmap[KPT * 256];
+    __shared__ uint16_t kmap[KPT * 256];
+    __shared__ int corr[64];  // per operand row: sum of the digits in inverted-bit-7 slots
     const int h = blockIdx.x, z = blockIdx.y, tid = threadIdx.x;
     const DevHead& H = blob[layer * n_kv + h];
     const int64_t zh = (int64_t)z * n_kv + h;
@@ -240,20 +246,21 @@ __global__ __launch_bounds__(256) void qprep_kernel(const DevHead* __restrict__ 
     for (int r = 0; r < ROWS; ++r) u[r] = ub[r * D];
     const int bj = H.bitsK[j];
     const float stj = H.stepK[j];
-    const int nqb = H.nqb[0] + H.nqb[1] + H.nqb[2];
+    const int nqm = H.nqm;
     const uint16_t* qg = q + zh * G * D;
     uint16_t qv[QPT];
 #pragma unroll
     for (int k = 0; k < QPT; ++k) qv[k] = qg[min(tid + 256 * k, G * D - 1)];
-    int16_t km[KPT];
+    uint16_t km[KPT];
 #pragma unroll
-    for (int k = 0; k < KPT; ++k) km[k] = (&H.kq_map[0][0][0])[tid + 256 * k];
+    for (int k = 0; k < KPT; ++k) km[k] = (&H.kq_slot[0][0][0])[tid + 256 * k];
 #pragma unroll
     for (int k = 0; k < QPT; ++k)
         if (tid + 256 * k < G * D) qf[tid + 256 * k] = aatc::bf16f(qv[k]);
 #pragma unroll
     for (int k = 0; k < KPT; ++k) kmap[tid + 256 * k] = km[k];
     if (tid < 16) smax[tid] = 0;
+    if (tid < 64) corr[tid] = 0;
     __syncthreads();
     // q' = U_K^T q: thread (j, pt) sums its slice of rows, slices meet in LDS
     for (int hh = 0; hh < G; ++hh) {
@@ -286,48 +293,58 @@ __global__ __launch_bounds__(256) void qprep_kernel(const DevHead* __restrict__ 
         if ((tid & 63) == 0) atomicMax(&smax[hh], __float_as_int(mag));
     }
     __syncthreads();
-    // operand word i: bytes 4i..4i+3 of [qb][rb][lane][16]
-    uint32_t* qa = qa_out + zh * NQB * RB * 256;
-    for (int i = tid; i < NQB * RB * 256; i += 256) {
-        const int bb = (i & 3) * 4, ln = (i >> 2) & 63, rb = (i >> 8) % RB, qb = (i >> 8) / RB;
+    // operand word i: bytes 4i..4i+3 of [m][rb][lane][16]; byte 4i'+b of lane group g holds
+    // the slot kq_slot[m][g][4i'+b]: q''[chan] 2^shift / 2^pos (the field is read at bit pos)
+    uint32_t* qa = qa_out + zh * NQM * RB * 256;
+    for (int i = tid; i < NQM * RB * 256; i += 256) {
+        const int bb = (i & 3) * 4, ln = (i >> 2) & 63, rb = (i >> 8) % RB, m = (i >> 8) / RB;
         const int row = ln & 15, gg = ln >> 4;
         const int hh = 4 * rb + (row >> 2), k = row & 3;
         uint32_t word = 0u;
-        if (qb < nqb && hh < G && k < 3) {
+        int flipped = 0;
+        if (m < nqm && hh < G && k < 3) {
             const float mx = __int_as_float(smax[hh]);
             const float sc = mx > 0.0f ? 127.0f / mx : 0.0f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int m = kmap[(qb * 4 + gg) * 16 + bb + e];
-                if (m >= 0) {
+                const uint32_t sl = kmap[(m * 4 + gg) * 16 + bb + e];
+                if (sl != 0xFFFFu) {
+                    const int chan = sl & 255, sh = (sl >> 8) & 7, pos = (sl >> 11) & 7;
                     float d0, d1, d2;
-                    digits(qf[hh * D + (m & 255)] * (float)(1 << (m >> 8)) * sc, d0, d1, d2);
+                    digits(qf[hh * D + chan] * (float)(1 << sh) * (1.0f / (float)(1 << pos)) * sc, d0, d1, d2);
                     const int dv = (int)(k == 0 ? d0 : (k == 1 ? d1 : d2));
                     word |= ((uint32_t)dv & 0xFFu) << (8 * e);
+                    if (sl & 0x4000u) flipped += dv;
                 }
             }
         }
+        if (flipped) atomicAdd(&corr[rb * 16 + row], flipped);
         qa[i] = word;
     }
-    if (tid < 16) qscale_out[zh * 16 + tid] = tid < G ? __int_as_float(smax[tid]) * (1.0f / 127.0f) : 0.0f;
+    __syncthreads();
+    // [0, 16): per-head digit scale; [16, 16 + 64): per operand row the accumulator's start
+    // value, 128 x the digits that multiply inverted-bit-7 bytes
+    float* qsc = qscale_out + zh * kQscStride;
+    if (tid < 16) qsc[tid] = tid < G ? __int_as_float(smax[tid]) * (1.0f / 127.0f) : 0.0f;
+    if (tid < 64) ((int*)qsc)[16 + tid] = 128 * corr[tid];
 }
 
 // Registers per lane grow with the row blocks and value column blocks; the waves per SIMD
 // the allocation is sized for (the LDS plan matches it).
-constexpr int vgpr_estimate(int rb, int nqb, int nvb) { return rb * nvb * 4 + nqb * rb * 4 + rb * 16 + nvb / 2 + nqb + 50; }
-constexpr int waves_for(int rb, int nqb, int nvb) {
-    return vgpr_estimate(rb, nqb, nvb) <= 128 ? 4 : (vgpr_estimate(rb, nqb, nvb) <= 168 ? 3 : 2);
+constexpr int vgpr_estimate(int rb, int nqm, int nvb) { return rb * nvb * 4 + nqm * (rb * 4 + 8) + rb * 16 + nvb / 2 + 50; }
+constexpr int waves_for(int rb, int nqm, int nvb) {
+    return vgpr_estimate(rb, nqm, nvb) <= 128 ? 4 : (vgpr_estimate(rb, nqm, nvb) <= 168 ? 3 : 2);
 }
 
-template <int RB, int NQB, int NVB, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQB, NVB)))) void decode_kernel(
+template <int RB, int NQM, int NVB, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel(
     const DevHead* __restrict__ blob, const uint8_t* __restrict__ cache, DecodeArgs a,
     const int32_t* __restrict__ seq_ids, const int64_t* __restrict__ seq_lens, const uint8_t* __restrict__ qa_all,
     const float* __restrict__ qscale, float* __restrict__ part1, float* __restrict__ part2,
     uint32_t* __restrict__ cnt1, uint32_t* __restrict__ cnt2, float* __restrict__ out) {
     constexpr int PARTS = 256 / D;  // row slices of a d x d matrix per column
     constexpr int ROWS = D / PARTS;  // rows per slice
-    constexpr int PST = 80;          // bytes per row of the probability operand (64 tokens + pad)
+    constexpr int PST = 64;          // bytes per row of the probability operand (64 tokens)
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     LDS_AS uint8_t* sm = (LDS_AS uint8_t*)smem_generic;
     const int wgi = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
@@ -336,15 +353,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
     const DevHead& H = blob[a.layer * a.n_kv + h];
     const int G = a.G, TB = a.tile_bytes, BB = a.buf_bytes;
     const int WK = H.BK >> 5;  // key record words per token
-    int nqb4 = H.nqb[0], nqb2 = H.nqb[1];
-    const int nqb = H.nqb[0] + H.nqb[1] + H.nqb[2];
     int nvb4 = H.nvb[0], nvb2 = H.nvb[1];
     const int nvb = H.nvb[0] + H.nvb[1] + H.nvb[2];
     const int64_t zh = (int64_t)z * a.n_kv + h;
 
-    // this wave's LDS: two tile buffers and the probability operand [RB*16 rows][PST]
+    // this wave's LDS: two tile buffers; the probability operand [RB*16 rows][64 tokens]
+    // overwrites the key block of the current tile once its scores are done
     LDS_AS uint8_t* ring = sm + w * a.wave_bytes;
-    LDS_AS uint8_t* P = ring + 2 * BB;
     LDS_AS int* flag = (LDS_AS int*)(sm + a.off_flag);
 
     // ---- sequence geometry (device arguments clamped: no read outside the cache)
@@ -357,54 +372,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
     const uint8_t* tiles = cache + (((int64_t)a.layer * a.n_seqs_cache + seq) * a.n_kv + h) * a.n_tiles_cap * TB;
 
     // ---- prologue: one batch of reads, waited for before the first tile load
-    v4i Aq[NQB][RB];  // score A operands (query digits), resident for the whole loop
+    v4i Aq[NQM][RB];  // score A operands (query digits), resident for the whole loop
     {
-        const v4i* src = (const v4i*)(qa_all + zh * NQB * RB * 1024);
+        const v4i* src = (const v4i*)(qa_all + zh * NQM * RB * 1024);
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
+        for (int m = 0; m < NQM; ++m)
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) Aq[qb][rb] = src[(qb * RB + rb) * 64 + lane];
+            for (int rb = 0; rb < RB; ++rb) Aq[m][rb] = src[(m * RB + rb) * 64 + lane];
     }
-    uint32_t kofs[NQB];  // key record words (o0 | o1 << 16) of this lane group for each score block
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-        kofs[qb] = qb < nqb ? (uint32_t)H.kq_dw[qb][g][0] | ((uint32_t)H.kq_dw[qb][g][1] << 16) : 0u;
+    // key dwords per (MFMA, lane group): LDS byte offset of the record word in the tile and
+    // the field mask, staged once in LDS ([m][g] -> 4 offsets then 4 masks) and read per tile
+    LDS_AS u32x4* ksched = (LDS_AS u32x4*)(sm + a.off_ksched);
+    for (int i = tid; i < NQM * 4 * 8; i += 256) {
+        const int m = i >> 5, gg = (i >> 3) & 3, e = i & 7;
+        ((LDS_AS uint32_t*)ksched)[i] =
+            e < 4 ? 256u * (uint32_t)H.kq_word[m][gg][e] : H.kq_mask[m][gg][e - 4];
+    }
     constexpr int NVP = (NVB + 1) / 2;
-    uint32_t vofs[NVP];  // first words of this lane's value slabs, two column blocks per register
+    uint32_t vofs[NVP];  // word of this lane's value slab (+ its 16-token offset), two blocks per register
 #pragma unroll
     for (int k = 0; k < NVP; ++k) {
-        const uint32_t lo = 2 * k < nvb ? (uint32_t)H.vb_slab[2 * k][c] : 0u;
-        const uint32_t hi = 2 * k + 1 < nvb ? (uint32_t)H.vb_slab[2 * k + 1][c] : 0u;
-        vofs[k] = lo | (hi << 16);
+        uint32_t v2 = 0u;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int cb = 2 * k + e;
+            const int mode = cb < nvb4 ? 0 : (cb < nvb4 + nvb2 ? 1 : 2);
+            const uint32_t wi = cb < nvb ? (uint32_t)H.vb_slab[cb][c] + (uint32_t)((2 * g) >> mode) : 0u;
+            v2 |= wi << (16 * e);
+        }
+        vofs[k] = v2;
     }
     float qs[RB][3];  // digit scales of this lane's query head
     bool hv[RB];
+    v4i sinit[RB];    // score accumulator start: the inverted-bit-7 correction of each row
+    {
+        const float* qsc = qscale + zh * kQscStride;
+        const int* qci = (const int*)qsc + 16;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        hv[rb] = 4 * rb + g < G;
-        const float mx = qscale[zh * 16 + 4 * rb + g];
-        qs[rb][0] = mx;
-        qs[rb][1] = mx * kDig1;
-        qs[rb][2] = mx * kDig2;
+        for (int rb = 0; rb < RB; ++rb) {
+            hv[rb] = 4 * rb + g < G;
+            const float mx = qsc[4 * rb + g];
+            qs[rb][0] = mx;
+            qs[rb][1] = mx * kDig1;
+            qs[rb][2] = mx * kDig2;
+            sinit[rb] = v4i{qci[16 * rb + 4 * g], qci[16 * rb + 4 * g + 1], qci[16 * rb + 4 * g + 2], 0};
+        }
     }
     // the operands have arrived before any tile load: inside the loop the only vector
     // memory operations are this wave's tile loads
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
+    for (int m = 0; m < NQM; ++m)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(Aq[qb][rb]));
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) asm volatile("" ::"v"(kofs[qb]));
+        for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(Aq[m][rb]));
+    lds_barrier();  // the key schedule table is staged
 #pragma unroll
     for (int k = 0; k < NVP; ++k) asm volatile("" ::"v"(vofs[k]));
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(qs[rb][0]));
-
-    {
-        LDS_AS uint32_t* Pw = (LDS_AS uint32_t*)P;  // digit row 3 of each head stays zero
-        for (int i = lane; i < RB * 16 * PST / 4; i += 64) Pw[i] = 0u;
-    }
-    const uint32_t vwi4 = 2 * g, vwi2 = g, vwi1 = g >> 1, pre1 = 4 * (g & 1);
+    for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(qs[rb][0]), "v"(sinit[rb]));
+    const uint32_t pre1 = 4 * (g & 1);
 
     // int32 sums of P digits x value pieces, relative to the reference max mref (a rescale
     // combines the three digit sums, scales by 2^(old - new) and splits the result into
@@ -418,62 +443,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) mref[rb] = -INFINITY, lsum[rb] = 0.0f;
 
-    // ---- tiles t_begin + w, t_begin + w + 4, ...: double-buffered per wave
+    // ---- tiles t_begin + w, t_begin + w + 4, ...: a ring of NBW buffers per wave keeps up
+    // to NBW - 1 of them in flight; the wave waits on its own load count
+    const int NBW = a.nbw;
+    const int nl = (TB + 1023) >> 10;  // load instructions per tile
     int64_t t = t_begin + w;
-    if (t < t_end) load_tile(tiles + t * TB, ring, TB, lane);
-    int buf = 0;
+    for (int k = 0; k < NBW - 1 && t + kWaves * k < t_end; ++k)
+        load_tile(tiles + (t + kWaves * k) * TB, ring + k * BB, TB, lane);
+    int slot = 0;
     for (; t < t_end; t += kWaves) {
-        // the per-block unpack modes derive from these counts inside the loop (a few scalar
-        // ops per block) instead of being hoisted into dozens of live scalar registers
-        asm volatile("" : "+s"(nqb4), "+s"(nqb2), "+s"(nvb4), "+s"(nvb2));
-        wait_all();  // tile t has landed; this wave's reads of the other buffer are done
-        if (t + kWaves < t_end) load_tile(tiles + (t + kWaves) * TB, ring + (buf ^ 1) * BB, TB, lane);
-        const LDS_AS uint32_t* cur = (const LDS_AS uint32_t*)(ring + buf * BB);
-        buf ^= 1;
+        // the unpack modes of the value blocks derive from these counts inside the loop (a
+        // few scalar ops per block) instead of being hoisted into live scalar registers
+        asm volatile("" : "+s"(nvb4), "+s"(nvb2));
+        // tile t has landed once only the later tiles' loads may be outstanding; this wave's
+        // LDS reads of the slot refilled next are done
+        wait_vm(nl * (int)min((int64_t)NBW - 2, (t_end - 1 - t) / kWaves));
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int64_t tn = t + (int64_t)kWaves * (NBW - 1);
+        if (tn < t_end) load_tile(tiles + tn * TB, ring + (slot == 0 ? NBW - 1 : slot - 1) * BB, TB, lane);
+        LDS_AS uint8_t* curb = ring + slot * BB;
+        const LDS_AS uint32_t* cur = (const LDS_AS uint32_t*)curb;
+        slot = slot + 1 == NBW ? 0 : slot + 1;
         const int valid = (int)min((int64_t)kTile, len - t * kTile);
 
-        // ---------------- scores: token group tg, lane (g, c) -> token 4c + tg
+        // ---------------- scores: token group tg, lane (g, c) -> token 4c + tg.  One 16-byte
+        // read gives a record word of the lane's four tokens; each operand dword keeps one
+        // field per byte (a mask), so no shifts.
         v4i S[4][RB];
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg)
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) S[tg][rb] = v4i{0, 0, 0, 0};
+            for (int rb = 0; rb < RB; ++rb) S[tg][rb] = sinit[rb];
+        const LDS_AS uint8_t* kbase = curb + 16 * c;  // record word 0 of tokens 4c..4c+3
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-            const LDS_AS uint32_t* k0 = cur + 64 * (kofs[qb] & 0xFFFFu) + 4 * c;
-            const LDS_AS uint32_t* k1 = cur + 64 * (kofs[qb] >> 16) + 4 * c;
-            // the block's width is uniform: one scalar branch, then straight-line unpacks
-            if (qb >= nqb) {
-                // padding block: nothing to add
-            } else if (qb < nqb4) {
+        for (int m = 0; m < NQM; ++m) {
+            const u32x4 koff = ksched[(m * 4 + g) * 2], kmask = ksched[(m * 4 + g) * 2 + 1];
+            u32x4 x[4];
 #pragma unroll
-                for (int tg = 0; tg < 4; ++tg) {
-                    const v4i B = unpack_w<4>(k0[tg], k1[tg], pre1);
+            for (int i = 0; i < 4; ++i) x[i] = *(const LDS_AS u32x4*)(kbase + koff[i]);
 #pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-                        S[tg][rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[qb][rb], B, S[tg][rb], 0, 0, 0);
-                }
-            } else if (qb < nqb4 + nqb2) {
+            for (int tg = 0; tg < 4; ++tg) {
+                const v4i B = v4i{(int)(x[0][tg] & kmask[0]), (int)(x[1][tg] & kmask[1]), (int)(x[2][tg] & kmask[2]),
+                                  (int)(x[3][tg] & kmask[3])};
 #pragma unroll
-                for (int tg = 0; tg < 4; ++tg) {
-                    const v4i B = unpack_w<2>(k0[tg], 0u, pre1);
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-                        S[tg][rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[qb][rb], B, S[tg][rb], 0, 0, 0);
-                }
-            } else {
-#pragma unroll
-                for (int tg = 0; tg < 4; ++tg) {
-                    const v4i B = unpack_w<1>(k0[tg], 0u, pre1);
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-                        S[tg][rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[qb][rb], B, S[tg][rb], 0, 0, 0);
-                }
+                for (int rb = 0; rb < RB; ++rb)
+                    S[tg][rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[m][rb], B, S[tg][rb], 0, 0, 0);
             }
-            __builtin_amdgcn_sched_barrier(0);  // bound the operand words in flight (registers)
         }
         // lane (g, c) holds head 4rb+g, tokens 4c..4c+3, digit rows 0..2
-        __builtin_amdgcn_sched_barrier(0);
         float s[RB][4], tmx[RB];
         bool need = false;
 #pragma unroll
@@ -509,7 +526,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
             }
         }
         // probabilities as three int8 digits (p*127 = d0 + d1/254 + d2/254^2) into
-        // P[16 rb + 4 head + digit][token], the value MFMA's A operand (wave-private)
+        // P[16 rb + 4 head + digit][token] over the tile's key block (wave-private; the key
+        // words of this tile were all read above)
+        LDS_AS uint8_t* P = curb;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             uint32_t pk0 = 0u, pk1 = 0u, pk2 = 0u;
@@ -527,31 +546,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
             pw[0] = pk0;
             pw[PST / 4] = pk1;
             pw[2 * PST / 4] = pk2;
+            pw[3 * PST / 4] = 0u;  // digit row 3 multiplies nothing
         }
         asm volatile("" ::: "memory");  // the operand reads below follow this wave's writes
-        __builtin_amdgcn_sched_barrier(0);
         v4i Ap[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) Ap[rb] = *(const LDS_AS v4i*)(P + (16 * rb + c) * PST + 16 * g);
 
-        // ---------------- values: every column block over the 64 tokens
+        // ---------------- values: every column block over the 64 tokens.  The block's width
+        // is uniform: shift counts and mask follow from it with scalar ops.
         const LDS_AS uint32_t* vw = cur + 64 * WK;
 #pragma unroll
         for (int cb = 0; cb < NVB; ++cb) {
-            const uint32_t slab = (vofs[cb >> 1] >> (16 * (cb & 1))) & 0xFFFFu;
-            v4i B;
-            if (cb >= nvb)
-                continue;  // padding block
-            else if (cb < nvb4)
-                B = unpack_w<4>(vw[slab + vwi4], vw[slab + vwi4 + 1], pre1);
-            else if (cb < nvb4 + nvb2)
-                B = unpack_w<2>(vw[slab + vwi2], 0u, pre1);
-            else
-                B = unpack_w<1>(vw[slab + vwi1], 0u, pre1);
+            int mode = cb < nvb4 ? 0 : (cb < nvb4 + nvb2 ? 1 : 2);  // 4-, 2-, 1-bit pieces
+            asm volatile("" : "+s"(mode));
+            const uint32_t wbits = 4u >> mode;
+            const uint32_t M = 0x01010101u * ((1u << wbits) - 1u);
+            const uint32_t s2 = mode == 0 ? 0u : 2u * wbits, s3 = mode == 0 ? 4u : 3u * wbits;
+            const uint32_t wi = (vofs[cb >> 1] >> (16 * (cb & 1))) & 0xFFFFu;
+            const uint32_t x0 = vw[wi], x1 = vw[wi + 1];
+            const uint32_t base = x0 >> (mode == 2 ? pre1 : 0u);
+            const uint32_t hi = mode == 0 ? x1 : base;
+            const v4i B = v4i{(int)(base & M), (int)((base >> wbits) & M), (int)((hi >> s2) & M), (int)((hi >> s3) & M)};
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
                 acc_i[rb][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ap[rb], B, acc_i[rb][cb], 0, 0, 0);
-            if (cb % 4 == 3) __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -624,12 +643,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
     lds_barrier();
     if (!*flag) return;
 
-    // ---------------- merges (coefficient domain), then dequantise + inverse transform
+    // ---------------- merges.  Each group merger combines its group in the coefficient
+    // domain and applies the inverse transform to its own (unnormalised) result,
+    // y = U_V (step * A); the last of them combines the y's: o = obias + Y / L.
+    const int ii = tid % D, pt = __builtin_amdgcn_readfirstlane(tid / D);  // (column, row slice)
+    const float* vb = H.UVt + pt * ROWS * D + ii;  // UVt[j * d + i] = U_V[i][j]
+    float uv[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) uv[r] = vb[r * D];
     // thread columns: i = tid + 256 k -> query head i / D, coefficient i % D
     constexpr int CPT = RB * 4 * D / 256;
-    constexpr int CH = 16 / RB;  // partials per merge round
+    constexpr int CH = RB == 1 ? 8 : 4;  // partials per merge round
     float M[CPT], L[CPT], A[CPT];
     merge_cols<D, CPT, CH>(part1 + (zh * W + grp * grp_size) * G * ld, members1, G, tid, M, L, A);
+    LDS_AS float* cbar = (LDS_AS float*)sm;  // [G][D] step * A
+    LDS_AS float* red = cbar + G * D;        // [PARTS][G][D]
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int i = tid + 256 * k, hh = i / D, jj = i - hh * D;
+        if (hh < G) cbar[i] = H.bitsV[jj] ? H.stepV[jj] * A[k] : 0.0f;
+    }
+    lds_barrier();
+    for (int hh = 0; hh < G; ++hh) {
+        float o = 0.0f;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) o = fmaf(uv[r], cbar[hh * D + pt * ROWS + r], o);
+        red[(pt * G + hh) * D + ii] = o;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int i = tid + 256 * k, hh = i / D, i2 = i - hh * D;
+        float y = 0.0f;
+        if (hh < G) {
+#pragma unroll
+            for (int p2 = 0; p2 < PARTS; ++p2) y += red[(p2 * G + hh) * D + i2];
+        }
+        A[k] = y;
+    }
     if (NG > 1) {
         float* gout = part2 + (zh * NG + grp) * G * ld;
 #pragma unroll
@@ -650,37 +701,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
         if (!*flag) return;
         merge_cols<D, CPT, CH>(part2 + zh * NG * G * ld, NG, G, tid, M, L, A);
     }
-    // basis slice for the inverse transform: thread (column ii, slice pt)
-    const int ii = tid % D, pt = __builtin_amdgcn_readfirstlane(tid / D);
-    const float* vb = H.UVt + pt * ROWS * D + ii;
-    float uv[ROWS];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) uv[r] = vb[r * D];
-    LDS_AS float* cbar = (LDS_AS float*)sm;  // [G][D]
-    LDS_AS float* red = cbar + G * D;          // [PARTS][G][D]
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-        const int i = tid + 256 * k, hh = i / D, jj = i - hh * D;
-        if (hh < G) {
-            const int bv = H.bitsV[jj];
-            cbar[i] = (bv && L[k] > 0.0f) ? H.stepV[jj] * (A[k] / L[k] - (float)(1 << (bv - 1)) + 0.5f) : 0.0f;
-        }
-    }
-    lds_barrier();
-    // out = mu_V + U_V cbar: UVt[j * d + i] = U_V[i][j]; thread (ii, pt) sums rows j of its slice
-    for (int hh = 0; hh < G; ++hh) {
-        float o = 0.0f;
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) o = fmaf(uv[r], cbar[hh * D + pt * ROWS + r], o);
-        red[(pt * G + hh) * D + ii] = o;
-    }
-    lds_barrier();
-    for (int i = tid; i < G * D; i += 256) {
-        const int hh = i / D, i2 = i - hh * D;
-        float o = H.muV[i2];
-#pragma unroll
-        for (int p2 = 0; p2 < PARTS; ++p2) o += red[(p2 * G + hh) * D + i2];
-        out[(zh * G + hh) * D + i2] = o;
+        const int i = tid + 256 * k, hh = i / D, i2 = i - hh * D;
+        if (hh < G) out[(zh * G + hh) * D + i2] = L[k] > 0.0f ? H.obias[i2] + A[k] / L[k] : H.muV[i2];
     }
 }
 
@@ -688,17 +712,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
 // host side
 // ---------------------------------------------------------------------------------------
 struct Variant {
-    int rb, nqb, nvb;
+    int rb, nqm, nvb;
 };
 // compile-time (row blocks, score operand blocks, value column blocks) bounds available;
 // (the operand blocks of a head must fit the bounds; unused blocks multiply zero)
-constexpr Variant kVariants[] = {{1, 4, 8},  {1, 6, 12}, {1, 8, 16}, {1, 12, 24}, {1, 12, 32}, {2, 6, 12},
-                                 {2, 8, 16}, {2, 12, 24}, {2, 12, 32}, {3, 6, 12}, {3, 8, 16}, {3, 12, 24},
-                                 {3, 12, 32}, {4, 6, 12}, {4, 8, 16}, {4, 12, 24}, {4, 12, 32}};
+constexpr Variant kVariants[] = {{1, 3, 8}, {1, 3, 12}, {1, 4, 12}, {1, 4, 16}, {1, 5, 12}, {1, 5, 16}, {1, 6, 16}, {1, 6, 24}, {1, 8, 24}, {1, 8, 32}, {1, 16, 32}, {2, 3, 12}, {2, 4, 12}, {2, 4, 16}, {2, 6, 24}, {2, 8, 32}, {2, 16, 32}, {3, 4, 16}, {3, 8, 32}, {3, 16, 32}, {4, 4, 16}, {4, 8, 32}, {4, 16, 32}};
 
 struct Plan {
     Variant v;
-    int nqb_max, nvb_max, tpg, wg_per_head, n_grp, wgs_per_cu;
+    int nqm_max, nvb_max, tpg, wg_per_head, n_grp, wgs_per_cu;
     size_t qa_bytes, qsc_bytes, part1_bytes, part2_bytes;
     int64_t n_counters;
     DecodeArgs args;
@@ -712,33 +734,33 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     const int G = cb->group, d = cb->d;
     const int RB = (G + 3) / 4;
     const int PARTS = 256 / d;
-    p.nqb_max = 0;
+    p.nqm_max = 0;
     p.nvb_max = 0;
     for (int h = 0; h < cb->n_kv; ++h) {
         const DevHead& D = cb->blob[(size_t)layer * cb->n_kv + h];
-        p.nqb_max = std::max(p.nqb_max, D.nqb[0] + D.nqb[1] + D.nqb[2]);
+        p.nqm_max = std::max(p.nqm_max, D.nqm);
         p.nvb_max = std::max(p.nvb_max, D.nvb[0] + D.nvb[1] + D.nvb[2]);
     }
     bool found = false;
     for (const Variant& v : kVariants)
-        if (v.rb == RB && v.nqb >= p.nqb_max && v.nvb >= p.nvb_max) {
+        if (v.rb == RB && v.nqm >= p.nqm_max && v.nvb >= p.nvb_max) {
             p.v = v;
             found = true;
             break;
         }
     if (!found)
-        return set_error(AATC_ERR_UNSUPPORTED, "no decode variant for %d query heads, %d score and %d value blocks", G,
-                         p.nqb_max, p.nvb_max);
+        return set_error(AATC_ERR_UNSUPPORTED, "no decode variant for %d query heads, %d score MFMAs and %d value blocks", G,
+                         p.nqm_max, p.nvb_max);
     const int64_t tiles = n_tiles_of(max_len);
     const int64_t total = tiles * cb->n_kv * (int64_t)n_seqs;
     // one wave per tile at a time: aim for every wave slot of the chip busy
-    const int64_t target = 256 * (int64_t)waves_for(p.v.rb, p.v.nqb, p.v.nvb) * kWaves;
+    const int64_t target = 256 * (int64_t)waves_for(p.v.rb, p.v.nqm, p.v.nvb) * kWaves;
     p.tpg = (int)std::max<int64_t>(kWaves, (total + target - 1) / target * kWaves);
     p.wg_per_head = (int)((tiles + p.tpg - 1) / p.tpg);
     p.n_grp = (p.wg_per_head + kMergeGroup - 1) / kMergeGroup;
     const size_t ld = (size_t)d + 2;
-    p.qa_bytes = (size_t)n_seqs * cb->n_kv * p.v.nqb * RB * 1024;
-    p.qsc_bytes = (size_t)n_seqs * cb->n_kv * 16 * sizeof(float);
+    p.qa_bytes = (size_t)n_seqs * cb->n_kv * p.v.nqm * RB * 1024;
+    p.qsc_bytes = (size_t)n_seqs * cb->n_kv * kQscStride * sizeof(float);
     p.part1_bytes = (size_t)n_seqs * cb->n_kv * p.wg_per_head * G * ld * sizeof(float);
     p.part2_bytes = (size_t)n_seqs * cb->n_kv * p.n_grp * G * ld * sizeof(float);
     p.n_counters = (int64_t)n_seqs * cb->n_kv * (p.n_grp + 1);
@@ -752,13 +774,25 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     a.wg_per_head = p.wg_per_head;
     a.n_grp = p.n_grp;
     a.buf_bytes = (int)al16(a.tile_bytes + 16);  // (+16: the value unpack may read one word past the tile)
-    a.wave_bytes = (int)al16(2 * (size_t)a.buf_bytes + (size_t)RB * 16 * 80);
+    // the probability operand (RB KiB) overwrites the tile's key block (8 B_K bytes)
+    int bk_min = 1 << 30;
+    for (int h = 0; h < cb->n_kv; ++h) bk_min = std::min(bk_min, cb->blob[(size_t)layer * cb->n_kv + h].BK);
+    if (RB * 1024 > 8 * bk_min)
+        return set_error(AATC_ERR_UNSUPPORTED, "%d key bits per token are too few for %d query heads", bk_min, G);
     // the epilogue and the merges reuse the buffers
     const size_t epi = ((size_t)2 * kWaves * RB * 4 + (size_t)kWaves * RB * 4 * 16 * p.v.nvb) * sizeof(float);
     const size_t mrg = ((size_t)G * d + (size_t)PARTS * G * d) * sizeof(float);
-    a.off_flag = (int)al16(std::max({(size_t)kWaves * a.wave_bytes, epi, mrg}));
+    // ring depth: the deepest that the workgroups resident per CU (set by registers) leave
+    // room for, between 2 and 4 buffers per wave
+    const int wgs = waves_for(p.v.rb, p.v.nqm, p.v.nvb);
+    const size_t budget = (size_t)(160 * 1024) / wgs - 64 - (size_t)p.v.nqm * 128;
+    a.nbw = 2;
+    while (a.nbw < 4 && (size_t)kWaves * (a.nbw + 1) * a.buf_bytes <= budget) ++a.nbw;
+    a.wave_bytes = a.nbw * a.buf_bytes;
+    a.off_ksched = (int)al16(std::max({(size_t)kWaves * a.wave_bytes, epi, mrg}));
+    a.off_flag = a.off_ksched + p.v.nqm * 4 * 8 * 4;
     p.lds = a.off_flag + 16;
-    p.wgs_per_cu = std::min<int>(waves_for(p.v.rb, p.v.nqb, p.v.nvb), (int)((160 * 1024) / p.lds));
+    p.wgs_per_cu = std::min<int>(wgs, (int)((160 * 1024) / p.lds));
     if (p.lds > 160 * 1024 - 256)
         return set_error(AATC_ERR_UNSUPPORTED, "decode needs %zu bytes of LDS per workgroup", p.lds);
     return AATC_OK;
@@ -788,21 +822,21 @@ void profile_slot(hipEvent_t& a, hipEvent_t& b) {
     ++P.used;
 }
 
-template <int RB, int NQB, int NVB, int D>
+template <int RB, int NQM, int NVB, int D>
 int launch_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* blob, const uint8_t* cache,
                   const int32_t* ids, const int64_t* lens, const uint16_t* q, uint8_t* qa, float* qsc, float* part1,
                   float* part2, uint32_t* cnt1, uint32_t* cnt2, float* out) {
     const DecodeArgs& a = p.args;
-    hipLaunchKernelGGL((qprep_kernel<RB, NQB, D>), dim3(a.n_kv, n_seqs), dim3(256), 0, st, blob, a.layer, a.n_kv, a.G,
+    hipLaunchKernelGGL((qprep_kernel<RB, NQM, D>), dim3(a.n_kv, n_seqs), dim3(256), 0, st, blob, a.layer, a.n_kv, a.G,
                        q, (uint32_t*)qa, qsc);
     HIP_TRY(hipGetLastError());
     if (p.lds > 64 * 1024)
-        HIP_TRY(hipFuncSetAttribute((const void*)decode_kernel<RB, NQB, NVB, D>,
+        HIP_TRY(hipFuncSetAttribute((const void*)decode_kernel<RB, NQM, NVB, D>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds));
     hipEvent_t e0, e1;
     profile_slot(e0, e1);
     if (e0) HIP_TRY(hipEventRecord(e0, st));
-    hipLaunchKernelGGL((decode_kernel<RB, NQB, NVB, D>), dim3(p.wg_per_head, a.n_kv, n_seqs), dim3(256), p.lds, st,
+    hipLaunchKernelGGL((decode_kernel<RB, NQM, NVB, D>), dim3(p.wg_per_head, a.n_kv, n_seqs), dim3(256), p.lds, st,
                        blob, cache, a, ids, lens, qa, qsc, part1, part2, cnt1, cnt2, out);
     HIP_TRY(hipGetLastError());
     if (e1) HIP_TRY(hipEventRecord(e1, st));
@@ -887,8 +921,8 @@ extern "C" int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob
     uint8_t* wsp = (uint8_t*)workspace;
     uint32_t* cnt1 = (uint32_t*)wsp;  // [n_seqs][n_kv][n_grp] group arrivals
     uint32_t* cnt2 = cnt1 + (size_t)n_seqs * cb->n_kv * p.n_grp;  // [n_seqs][n_kv] group-merger arrivals
-    uint8_t* qa = wsp + kCounterBytes;  // [n_seqs][n_kv][NQB][RB][64][16] score operands
-    float* qsc = (float*)(qa + al256(p.qa_bytes));  // [n_seqs][n_kv][16] digit scales
+    uint8_t* qa = wsp + kCounterBytes;  // [n_seqs][n_kv][NQM][RB][64][16] score operands
+    float* qsc = (float*)(qa + al256(p.qa_bytes));  // [n_seqs][n_kv][80] digit scales, accumulator starts
     float* part1 = (float*)((uint8_t*)qsc + al256(p.qsc_bytes));
     float* part2 = (float*)((uint8_t*)part1 + al256(p.part1_bytes));
     DecodeArgs& a = p.args;
@@ -900,29 +934,35 @@ extern "C" int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob
     const DevHead* blob = (const DevHead*)d_blob;
     hipStream_t st = (hipStream_t)stream;
     const uint8_t* c = (const uint8_t*)cache->data;
-#define AATC_DECODE_CASE(rb_, nqb_, nvb_)                                                                         \
-    if (p.v.rb == rb_ && p.v.nqb == nqb_ && p.v.nvb == nvb_)                                                      \
-        return cb->d == 64 ? launch_decode<rb_, nqb_, nvb_, 64>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, qa,  \
+#define AATC_DECODE_CASE(rb_, nqm_, nvb_)                                                                         \
+    if (p.v.rb == rb_ && p.v.nqm == nqm_ && p.v.nvb == nvb_)                                                      \
+        return cb->d == 64 ? launch_decode<rb_, nqm_, nvb_, 64>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, qa,  \
                                                                 qsc, part1, part2, cnt1, cnt2, out)                \
-                           : launch_decode<rb_, nqb_, nvb_, 128>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, qa, \
+                           : launch_decode<rb_, nqm_, nvb_, 128>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, qa, \
                                                                  qsc, part1, part2, cnt1, cnt2, out);
-    AATC_DECODE_CASE(1, 4, 8)
-    AATC_DECODE_CASE(1, 6, 12)
-    AATC_DECODE_CASE(1, 8, 16)
-    AATC_DECODE_CASE(1, 12, 24)
-    AATC_DECODE_CASE(1, 12, 32)
-    AATC_DECODE_CASE(2, 6, 12)
-    AATC_DECODE_CASE(2, 8, 16)
-    AATC_DECODE_CASE(2, 12, 24)
-    AATC_DECODE_CASE(2, 12, 32)
-    AATC_DECODE_CASE(3, 6, 12)
-    AATC_DECODE_CASE(3, 8, 16)
-    AATC_DECODE_CASE(3, 12, 24)
-    AATC_DECODE_CASE(3, 12, 32)
-    AATC_DECODE_CASE(4, 6, 12)
-    AATC_DECODE_CASE(4, 8, 16)
-    AATC_DECODE_CASE(4, 12, 24)
-    AATC_DECODE_CASE(4, 12, 32)
+    AATC_DECODE_CASE(1, 3, 8)
+    AATC_DECODE_CASE(1, 3, 12)
+    AATC_DECODE_CASE(1, 4, 12)
+    AATC_DECODE_CASE(1, 4, 16)
+    AATC_DECODE_CASE(1, 5, 12)
+    AATC_DECODE_CASE(1, 5, 16)
+    AATC_DECODE_CASE(1, 6, 16)
+    AATC_DECODE_CASE(1, 6, 24)
+    AATC_DECODE_CASE(1, 8, 24)
+    AATC_DECODE_CASE(1, 8, 32)
+    AATC_DECODE_CASE(1, 16, 32)
+    AATC_DECODE_CASE(2, 3, 12)
+    AATC_DECODE_CASE(2, 4, 12)
+    AATC_DECODE_CASE(2, 4, 16)
+    AATC_DECODE_CASE(2, 6, 24)
+    AATC_DECODE_CASE(2, 8, 32)
+    AATC_DECODE_CASE(2, 16, 32)
+    AATC_DECODE_CASE(3, 4, 16)
+    AATC_DECODE_CASE(3, 8, 32)
+    AATC_DECODE_CASE(3, 16, 32)
+    AATC_DECODE_CASE(4, 4, 16)
+    AATC_DECODE_CASE(4, 8, 32)
+    AATC_DECODE_CASE(4, 16, 32)
 #undef AATC_DECODE_CASE
     return set_error(AATC_ERR_UNSUPPORTED, "decode variant missing");
 }

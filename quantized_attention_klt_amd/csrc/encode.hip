@@ -80,7 +80,13 @@ __global__ __launch_bounds__(256) void encode_kernel(const DevHead* __restrict__
     const int seq = sa.seq[zi];
     uint8_t* tp = cache + ((((int64_t)layer * n_seqs_cache + seq) * n_kv + h) * n_tiles_cap + tile) * (int64_t)tile_bytes;
     uint32_t* tw = (uint32_t*)tp;
-    for (int i = threadIdx.x; i < nw; i += blockDim.x) words[i] = tw[i];
+    // key-block word i belongs to slot i % 64; the records of the slots written here are
+    // rebuilt from zero (the stored key bytes carry bit 7 inverted)
+    const int nkw = 2 * BK;  // 64 slots * BK / 32 words
+    for (int i = threadIdx.x; i < nw; i += blockDim.x) {
+        const int s = i & 63;
+        words[i] = (i < nkw && s >= s0 && s < s1) ? 0u : tw[i];
+    }
     // codes of the slots being written
     for (int i = threadIdx.x; i < (s1 - s0) * 2 * d; i += blockDim.x) {
         int s = s0 + i / (2 * d);
@@ -123,7 +129,10 @@ __global__ __launch_bounds__(256) void encode_kernel(const DevHead* __restrict__
         lds_put(words, pos, val, w);
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < nw; i += blockDim.x) tw[i] = words[i];
+    for (int i = threadIdx.x; i < nw; i += blockDim.x) {
+        const int s = i & 63;
+        tw[i] = (i < nkw && s >= s0 && s < s1) ? words[i] ^ 0x80808080u : words[i];
+    }
 }
 
 __global__ void flush_kernel(uint4* p, size_t n) {

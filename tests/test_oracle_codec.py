@@ -90,6 +90,12 @@ def _pack_bit_by_bit(codesK, codesV, bK, bV):
             for i in range(w):
                 put(base + pos + i, (val >> i) & 1)
             off += w
+    # the key-record bytes of written slots are stored with bit 7 inverted
+    for t in range(n):
+        tile, s = divmod(t, 64)
+        for r in range(BK // 32):
+            for k in range(4):
+                buf[tile * tile_bits // 8 + 4 * (64 * r + s) + k] ^= 0x80
     return np.array(buf, np.uint8)
 
 
@@ -115,15 +121,18 @@ def test_tile_size_and_zero_padding():
     cK = np.array([[0x12, 0x34, 0x56, 0x78], [0x9A, 0, 0, 0]])
     cV = np.array([[1, 3], [0, 2]])
     t = oracle.pack_cache(cK, cV, bK, bV)
+    k = t[:256].copy()
+    k[:8] ^= 0x80  # the two written slots' key records are stored with bit 7 inverted
     # slot 0's record word = block word 0: nibbles hi/lo of each code in channel order
-    assert t[0:4].tolist() == [0x21, 0x43, 0x65, 0x87]
+    assert k[0:4].tolist() == [0x21, 0x43, 0x65, 0x87]
     # slot 1's record word = block word 1
-    assert t[4:8].tolist() == [0xA9, 0, 0, 0]
-    assert t[8:256].sum() == 0
-    # V block at byte 256: (ch1 w2) slab first: slot0 = 3 at bits 0..1, slot1 = 2 at bits 8..9;
-    # (ch0 w1) slab at bit 64*2: slot0 = 1 at bit 0
+    assert k[4:8].tolist() == [0xA9, 0, 0, 0]
+    assert k[8:256].sum() == 0
+    # V block at byte 256 (not inverted): (ch1 w2) slab first: slot0 = 3 at bits 0..1,
+    # slot1 = 2 at bits 8..9; (ch0 w1) slab at bit 64*2: slot0 = 1 at bit 0
     assert t[256] == 0b11 and t[257] == 0b10 and t[256 + 16] == 1
-    assert int(t.astype(np.int64).sum()) == 0x21 + 0x43 + 0x65 + 0x87 + 0xA9 + 3 + 2 + 1
+    assert int(t[256:].astype(np.int64).sum()) == 3 + 2 + 1
+    assert int(k.astype(np.int64).sum()) == 0x21 + 0x43 + 0x65 + 0x87 + 0xA9
 
 
 def test_two_word_records_are_word_major():
@@ -131,7 +140,9 @@ def test_two_word_records_are_word_major():
     cK = np.zeros((3, 8), np.int64)
     cK[2, 4] = 0xFF  # slot 2, channel 4 -> record word 1, low byte
     t = oracle.pack_cache(cK, np.zeros((3, 1), np.int64), bK, np.array([2]))
-    w = t[:64 * 2 * 4].view(np.uint32)
+    w = t[:64 * 2 * 4].view(np.uint32).copy()
+    for r in range(2):
+        w[64 * r:64 * r + 3] ^= np.uint32(0x80808080)  # written slots 0..2: bit 7 inverted
     assert w[64 * 1 + 2] == 0xFF and int(w.sum()) == 0xFF
 
 
@@ -140,8 +151,31 @@ def test_eight_bit_code_is_two_nibbles():
     bV = np.array([2, 1])
     assert oracle.pieces(bK)[:2] == [(0, 4, 4), (0, 4, 0)]
     t = oracle.pack_cache(np.array([[0xA5, 0, 0, 0]]), np.array([[2, 1]]), bK, bV)
-    # record: high nibble 0xA at bits 0..3, low nibble 0x5 at bits 4..7
-    assert t[0] == 0x5A
+    # record: high nibble 0xA at bits 0..3, low nibble 0x5 at bits 4..7 (stored with bit 7
+    # inverted)
+    assert t[0] == 0x5A ^ 0x80
+
+
+def test_masked_key_fields_read_as_signed_bytes():
+    """With bit 7 of key bytes inverted, masking one field of a byte and reading the byte as
+    int8 gives field * 2^p, minus 128 exactly when the field ends at bit 7."""
+    rng = np.random.default_rng(7)
+    bK = np.array([8, 7, 6, 5, 3, 2, 1, 4, 4, 8, 1, 2, 1, 3, 5, 4])  # 64 bits
+    n = 64
+    cK = np.stack([rng.integers(0, 1 << b, n) for b in bK], 1)
+    t = oracle.pack_cache(cK, np.zeros((n, 1), np.int64), bK, np.array([2]))
+    words = t[:64 * 2 * 4].view(np.uint32).reshape(2, 64)  # [record word][slot]
+    off = 0
+    for (j, w, e) in oracle.pieces(bK):
+        r, bit = divmod(off, 32)
+        byte, p = divmod(bit, 8)
+        field = (cK[:, j] >> e) & ((1 << w) - 1)
+        mask = ((1 << w) - 1) << p
+        raw = (words[r] >> np.uint32(8 * byte)) & np.uint32(0xFF)
+        got = (raw & np.uint32(mask)).astype(np.uint8).view(np.int8).astype(np.int64)
+        want = field * (1 << p) - (128 if p + w == 8 else 0)
+        assert np.array_equal(got, want), (j, w, e, p)
+        off += w
 
 
 def test_key_bits_must_fill_words():
