@@ -26,7 +26,7 @@
  *     codebook) and never synchronises a stream.  Device pointers must be 16-byte
  *     aligned.  A codebook is immutable once created and may be shared across threads.
  *   - head_dim d is 64 or 128; the query group size G = H_q / H_kv is 1..16; the budget
- *     B = 2 * d * avg_bits bits per token and kv-head must be an even integer.
+ *     B = 2 * d * avg_bits bits per token and kv-head must be a multiple of 8.
  *   - Matrices are row-major.  A basis U is d x d with U[i*d + j] = component i of basis
  *     vector j (coefficients are c = (x - mu) U).
  */
@@ -41,7 +41,7 @@ extern "C" {
 #endif
 
 #define AATC_VERSION 1
-#define AATC_LAYOUT_VERSION 1
+#define AATC_LAYOUT_VERSION 2
 
 #define AATC_OK 0
 #define AATC_ERR_INVALID_ARG (-1)
@@ -89,7 +89,15 @@ typedef struct {
 /* Device-side cache descriptor.  data: caller-allocated device memory of
  * aatc_cache_bytes() bytes, zero-filled before first use.  The cache of
  * (layer, seq, kv-head) is a run of ceil(max_tokens/64) tiles of 64 token slots;
- * tile t lives at byte (((layer*n_seqs + seq)*n_kv + head)*n_tiles + t) * tile_bytes. */
+ * tile t lives at byte (((layer*n_seqs + seq)*n_kv + head)*n_tiles + t) * tile_bytes.
+ * Inside a tile (layout version 2): a token's key record (B_K bits, a multiple of 32)
+ * and value record (B_V bits, a multiple of 8) hold the channel codes as byte-aligned
+ * fields (placement: widest channel first into the first byte with room; channels that
+ * fit nowhere are cut to fill the remaining bits; bytes renumbered by decreasing field
+ * count).  The key block (8*B_K bytes) is word-major: record word r of slot s is block
+ * word 64r + s.  The value block (next 8*B_V bytes) is byte-major: record byte q of
+ * slot s is block byte 64q + s.  Written bytes carry bit 7 inverted; unwritten slots
+ * are zero. */
 typedef struct {
     void* data;
     int32_t n_layers;
@@ -122,7 +130,7 @@ int aatc_stats_from_samples(int32_t d, const float* K, const float* V, int64_t n
  * (greedy on marginal gains x_j 4^-k; ties: keys, then lower channel, then lower k), and
  * steps step_b * sqrt(lambda_j) of the Gaussian-MSE-optimal 2^b-level uniform quantizer.
  * *out is allocated by the library (free with aatc_codebook_free).
- * Errors: INVALID_ARG, BUDGET (2*d*avg_bits not an even integer, or out of range),
+ * Errors: INVALID_ARG, BUDGET (2*d*avg_bits not a multiple of 8, or out of range),
  * STATS (non-finite or non-PSD input), NO_CONVERGENCE (eigensolver). */
 int aatc_calibrate(int32_t d, int32_t n_layers, int32_t n_kv, int32_t group,
                    const aatc_head_stats* stats, const aatc_calib_params* params,
@@ -131,7 +139,8 @@ int aatc_calibrate(int32_t d, int32_t n_layers, int32_t n_kv, int32_t group,
 /* Build a codebook from explicit per-head arrays (e.g. produced by another calibration
  * tool): U_k, U_v [n_heads][d][d] float64; mu_k, mu_v [n_heads][d] float64; bits_k,
  * bits_v [n_heads][d] int32 in [0,8]; step_k, step_v [n_heads][d] float32 (> 0 where
- * bits > 0).  Every head must have the same total bits per token (an even number).
+ * bits > 0).  Every head must have the same total bits per token (a multiple of 8), with
+ * key bits a multiple of 32.
  * Errors: INVALID_ARG, BUDGET. */
 int aatc_codebook_create(int32_t d, int32_t n_layers, int32_t n_kv, int32_t group,
                          const double* U_k, const double* U_v, const double* mu_k,
@@ -151,6 +160,15 @@ int aatc_codebook_head(const aatc_codebook* cb, int32_t head, double* U_k, doubl
                        double* lam_k, double* lam_v, double* mu_k, double* mu_v,
                        double* x_k, double* x_v, int32_t* bits_k, int32_t* bits_v,
                        float* step_k, float* step_v, double* theta);
+
+/* Layout of one head's records: the byte-aligned fields of the key (which = 0) or value
+ * (which = 1) record sorted by (byte, bit position), each packed as
+ * chan | width << 8 | shift << 12 | pos << 16 | byte << 20 (the field holds code bits
+ * [shift, shift + width) of channel chan at bits [pos, pos + width) of record byte
+ * `byte`).  *n = number of fields; out may be NULL, else it holds at least 384 entries.
+ * Errors: INVALID_ARG. */
+int aatc_codebook_fields(const aatc_codebook* cb, int32_t head, int32_t which, uint32_t* out,
+                         int32_t* n);
 
 /* Persist / restore a codebook (versioned binary file with checksum).
  * Errors: IO, VERSION (layout or format mismatch, checksum failure). */
@@ -175,8 +193,8 @@ int aatc_cache_bytes(const aatc_codebook* cb, int32_t n_layers, int32_t n_seqs,
 /* Append n_tokens tokens to each of n_seqs sequences of one layer.
  * seq_ids [n_seqs], start_pos [n_seqs]: host arrays; sequence s writes token slots
  * start_pos[s] .. start_pos[s]+n_tokens-1.  K, V: device bf16 [n_seqs][n_tokens][n_kv][d]
- * (contiguous).  Tokens of a sequence must be appended in order: the slots being written
- * must still be zero (a partially filled tile is read, OR-ed and written back).
+ * (contiguous).  The slots being written are rebuilt; the other slots of a partially
+ * filled tile are kept (the tile is read, merged and written back).
  * Coefficients: c = x (U_hi + U_lo) - mu (U_hi + U_lo) with U_hi/U_lo the bf16 split of
  * U (bf16 MFMA, fp32 accumulation); codes as the quantizer of aatc_encode_coeffs.
  * Errors: INVALID_ARG, CAPACITY (start_pos + n_tokens > max_tokens), HIP. */

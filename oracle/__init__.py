@@ -30,7 +30,7 @@ from .calib import (  # noqa: F401
     uniform_quantizer_mse, optimal_step, build_head_codebook, HeadCodebook,
 )
 from .codec import (  # noqa: F401
-    pieces, quantize, transform_coeffs, pack_cache, unpack_cache, dequantize,
+    fields, quantize, transform_coeffs, pack_cache, unpack_cache, dequantize,
     reconstruct, tile_bytes, record_bits, encode_cache,
 )
 from .attention import (  # noqa: F401

@@ -322,13 +322,14 @@ KEY_ALIGN = 32  # key bits per token are kept a multiple of one 32-bit word
 def build_head_codebook(stats: dict, avg_bits: float, max_bits: int = 8,
                         joint: bool = True) -> HeadCodebook:
     """Calibrate one head: KLT of both covariances, weights, exact-budget integer bits
-    with total 2 d avg_bits (key bits a multiple of 32), and fp32 steps
+    with total 2 d avg_bits (a multiple of 8; key bits a multiple of 32), and fp32 steps
     step_b * sqrt(lambda_j)."""
     d = stats["d"]
     total = 2.0 * d * avg_bits
     B = int(round(total))
-    if abs(total - B) > 1e-9:
-        raise ValueError("2*d*avg_bits must be an integer")
+    if abs(total - B) > 1e-9 or B % 8:
+        raise ValueError("2*d*avg_bits must be a whole number of bytes (the packed records "
+                         "are byte strings)")
     lamK, UK = klt(stats["SigK"])
     lamV, UV = klt(stats["SigV"])
     xK, xV = channel_weights(stats, UK, lamK, UV, lamV)

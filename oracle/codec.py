@@ -4,26 +4,28 @@ dequantization.  Test infrastructure only.
 Packed layout (ours; the pages fix only a fixed per-token bit count, p3 abstract):
 
 * The cache of one (layer, sequence, kv-head) is a run of tiles of 64 token slots.
-  A tile is 8*B bytes, B = B_K + B_V = sum of all channel widths of the head.
-* Each channel of width b > 0 is split into "pieces" of width 4, 2 or 1: as many 4-bit
-  pieces as fit (from the most significant bit), then a 2-bit and/or a 1-bit piece
-  (b = 8 -> 4+4, 7 -> 4+2+1, 6 -> 4+2, 5 -> 4+1, 3 -> 2+1).  The piece of width w with
-  shift e holds code bits [e, e+w).  Pieces are ordered by width (4, 2, 1), then by KLT
-  channel index, then by shift (high first).  O_p is the sum of the widths of the pieces
-  before p (so O_p is a multiple of w_p).
-* Bit n of a block is bit n%8 of byte n//8 (little endian).
-* K block (first 8*B_K bytes; B_K is a multiple of 32): each token slot s has a record
-  of B_K bits, piece p at record bits [O_p, O_p + w_p).  Record word r (bits
-  [32r, 32r+32)) of slot s is word 64*r + s of the K block.
-* V block (next 8*B_V bytes): piece p owns a slab of 64*w_p bits starting at bit
-  64*O_p.  Slab word r (32 bits) holds token slots r*(32/w) + k, k < 32/w, with slot
-  k's field at word bits [8*(k%4) + w*(k//4), +w).
-* Every byte of a written slot's key record is stored with its most significant bit
-  inverted (XOR 0x80): an extraction that masks one field per byte then reads, as a
-  two's-complement int8, field * 2^(bit position) when the field stays below bit 7 and
-  that value minus 128 when it ends at bit 7 -- a constant per byte position that a
-  reader can correct for.
-* Slots not yet written are zero (all of their bytes, key records included).
+  A tile is 8*B bytes, B = B_K + B_V = sum of all channel widths of the head; B_K is a
+  multiple of 32 and B_V a multiple of 8.
+* A token's key record (B_K bits) and value record (B_V bits) are byte strings.  The
+  coded channels of a record are placed as byte-aligned fields, a field never crossing a
+  byte boundary (``fields``):
+    1. channels with b > 0, widest first (ties: lower channel index first), each go whole
+       into the lowest-index byte with at least b free bits, at that byte's lowest free
+       bit;
+    2. channels that found no such byte are then cut, in the same order, into pieces that
+       fill free bits byte by byte from the lowest byte: each piece takes min(free bits,
+       bits left) of the code, lowest code bits first;
+    3. the bytes are renumbered by decreasing field count (ties: lower byte first).
+  A field (channel j, width w, shift e, byte q, position p) holds code bits [e, e+w) of
+  channel j at bits [p, p+w) of record byte q.
+* K block (first 8*B_K bytes): record byte q of slot s is byte 4*(64*(q//4) + s) + q%4
+  (record word r = bytes 4r..4r+3 of slot s is block word 64r + s).
+* V block (next 8*B_V bytes): record byte q of slot s is byte 64*q + s.
+* Every record byte of a written slot (keys and values) is stored with its most
+  significant bit inverted (XOR 0x80): masking one field of a stored byte and reading it
+  as a two's-complement int8 then gives field * 2^p when the field stays below bit 7,
+  and that value minus 128 when it ends at bit 7.
+* Slots not yet written are zero.
 """
 from __future__ import annotations
 
@@ -32,28 +34,38 @@ import numpy as np
 TILE = 64
 
 
-def _split(b: int):
-    """Power-of-two pieces of a b-bit code, most significant first: as many 4-bit pieces as
-    fit, then a 2-bit and/or a 1-bit piece.  Returns [(width, shift)]."""
-    out, rem = [], b
-    for w in (4, 4, 2, 1):
-        if rem >= w:
-            rem -= w
-            out.append((w, rem))
-    return out
-
-
-def pieces(bits: np.ndarray):
-    """Pieces of a head's K or V channels: list of (channel, width, shift), ordered by width
-    (4, 2, 1), then channel, then shift (high first)."""
-    out = []
-    blist = np.asarray(bits).tolist()
-    for w in (4, 2, 1):
-        for j, b in enumerate(blist):
-            for (pw, e) in _split(b):
-                if pw == w:
-                    out.append((j, w, e))
-    return out
+def fields(bits: np.ndarray):
+    """Byte-aligned fields of one record: [(chan, width, shift, byte, pos)] sorted by
+    (byte, pos); the placement rule is the one in the module docstring."""
+    b = [int(x) for x in np.asarray(bits).tolist()]
+    R = sum(b)
+    if R % 8:
+        raise ValueError("record bits must be a whole number of bytes")
+    nbytes = R // 8
+    free = [8] * nbytes
+    out, left = [], []
+    for j in sorted((j for j in range(len(b)) if b[j] > 0), key=lambda j: (-b[j], j)):
+        q = next((q for q in range(nbytes) if free[q] >= b[j]), None)
+        if q is None:
+            left.append(j)
+            continue
+        out.append((j, b[j], 0, q, 8 - free[q]))
+        free[q] -= b[j]
+    for j in left:
+        e = 0
+        for q in range(nbytes):
+            if e == b[j]:
+                break
+            w = min(free[q], b[j] - e)
+            if w:
+                out.append((j, w, e, q, 8 - free[q]))
+                free[q] -= w
+                e += w
+    count = [0] * nbytes
+    for f in out:
+        count[f[3]] += 1
+    rank = {q: i for i, q in enumerate(sorted(range(nbytes), key=lambda q: (-count[q], q)))}
+    return sorted(((j, w, e, rank[q], p) for (j, w, e, q, p) in out), key=lambda f: (f[3], f[4]))
 
 
 def record_bits(bits: np.ndarray) -> int:
@@ -99,93 +111,62 @@ def reconstruct(chat: np.ndarray, mu: np.ndarray, U: np.ndarray) -> np.ndarray:
     return mu[None, :] + chat @ np.asarray(U, np.float64).T
 
 
-def _field_bits(values: np.ndarray, w: int) -> np.ndarray:
-    """[n] ints -> [n, w] bits, least significant first."""
-    return ((values[:, None] >> np.arange(w)[None, :]) & 1).astype(np.uint8)
+def _check_bits(bK, bV):
+    BK, BV = record_bits(bK), record_bits(bV)
+    if BK % 32:
+        raise ValueError("key bits per token must be a multiple of 32")
+    if BV % 8:
+        raise ValueError("value bits per token must be a multiple of 8")
+    return BK, BV
+
+
+def _records(codes: np.ndarray, bits: np.ndarray) -> np.ndarray:
+    """[n, R/8] record bytes (before the bit-7 inversion) of codes [n, d]."""
+    rec = np.zeros((codes.shape[0], record_bits(bits) // 8), np.int64)
+    for (j, w, e, q, p) in fields(bits):
+        rec[:, q] |= ((codes[:, j] >> e) & ((1 << w) - 1)) << p
+    return rec
+
+
+def _byte_offsets(n: int, BK: int, BV: int):
+    """Cache byte offsets of record byte q of tokens 0..n-1: ([n, BK/8], [n, BV/8])."""
+    tok = np.arange(n)
+    tile, slot = tok // TILE, tok % TILE
+    tbytes = 8 * (BK + BV)
+    qk = np.arange(BK // 8)[None, :]
+    qv = np.arange(BV // 8)[None, :]
+    offK = tile[:, None] * tbytes + 4 * (64 * (qk // 4) + slot[:, None]) + qk % 4
+    offV = tile[:, None] * tbytes + 8 * BK + 64 * qv + slot[:, None]
+    return offK, offV
 
 
 def pack_cache(codesK: np.ndarray, codesV: np.ndarray, bK: np.ndarray, bV: np.ndarray,
                n_tiles: int | None = None) -> np.ndarray:
     """Pack codes of tokens 0..n-1 (KLT channel order) into tiles; returns uint8 bytes."""
     n = codesK.shape[0]
-    BK, BV = record_bits(bK), record_bits(bV)
-    if BK % 32:
-        raise ValueError("key bits per token must be a multiple of 32")
+    BK, BV = _check_bits(bK, bV)
     if n_tiles is None:
         n_tiles = (n + TILE - 1) // TILE
-    kbits = 64 * BK
-    tbits = 64 * (BK + BV)
-    bitarr = np.zeros(n_tiles * tbits, np.uint8)
-    tok = np.arange(n)
-    tile = tok // TILE
-    slot = tok % TILE
-    off = 0
-    for (j, w, e) in pieces(bK):
-        vals = (codesK[:, j] >> e) & ((1 << w) - 1)
-        rbit = off + np.arange(w)[None, :]
-        pos = tile[:, None] * tbits + 32 * ((rbit // 32) * 64 + slot[:, None]) + rbit % 32
-        bitarr[pos] = _field_bits(vals, w)
-        off += w
-    off = 0
-    for (j, w, e) in pieces(bV):
-        vals = (codesV[:, j] >> e) & ((1 << w) - 1)
-        per_word = 32 // w
-        r = slot // per_word
-        k = slot % per_word
-        inword = 8 * (k % 4) + w * (k // 4)
-        base = tile * tbits + kbits + 64 * off + 32 * r + inword
-        pos = base[:, None] + np.arange(w)[None, :]
-        bitarr[pos] = _field_bits(vals, w)
-        off += w
-    out = np.packbits(bitarr, bitorder="little")
-    _flip_key_bytes(out, n, BK, 8 * (BK + BV))
+    out = np.zeros(n_tiles * 8 * (BK + BV), np.uint8)
+    offK, offV = _byte_offsets(n, BK, BV)
+    out[offK] = (_records(np.asarray(codesK, np.int64), bK) ^ 0x80).astype(np.uint8)
+    out[offV] = (_records(np.asarray(codesV, np.int64), bV) ^ 0x80).astype(np.uint8)
     return out
-
-
-def _flip_key_bytes(buf: np.ndarray, n: int, BK: int, tbytes: int) -> None:
-    """Invert bit 7 of every byte of the key records of token slots 0..n-1, in place."""
-    tok = np.arange(n)
-    tile, slot = tok // TILE, tok % TILE
-    for r in range(BK // 32):
-        byte0 = tile * tbytes + 4 * (64 * r + slot)
-        for k in range(4):
-            buf[byte0 + k] ^= np.uint8(0x80)
 
 
 def unpack_cache(cache: np.ndarray, bK: np.ndarray, bV: np.ndarray, n: int):
     """Inverse of pack_cache for the first n token slots: (codesK, codesV) [n, d]."""
-    d = len(bK)
-    BK, BV = record_bits(bK), record_bits(bV)
-    kbits = 64 * BK
-    tbits = 64 * (BK + BV)
-    n_tiles = (n + TILE - 1) // TILE
-    raw = np.array(np.asarray(cache, np.uint8)[: n_tiles * tbits // 8])
-    _flip_key_bytes(raw, n, BK, tbits // 8)
-    bitarr = np.unpackbits(raw, bitorder="little")
-    tok = np.arange(n)
-    tile = tok // TILE
-    slot = tok % TILE
-    cK = np.zeros((n, d), np.int64)
-    cV = np.zeros((n, len(bV)), np.int64)
-    off = 0
-    for (j, w, e) in pieces(bK):
-        rbit = off + np.arange(w)[None, :]
-        pos = tile[:, None] * tbits + 32 * ((rbit // 32) * 64 + slot[:, None]) + rbit % 32
-        weights = (1 << np.arange(w))[None, :]
-        cK[:, j] += ((bitarr[pos].astype(np.int64) * weights).sum(axis=1)) << e
-        off += w
-    off = 0
-    for (j, w, e) in pieces(bV):
-        per_word = 32 // w
-        r = slot // per_word
-        k = slot % per_word
-        inword = 8 * (k % 4) + w * (k // 4)
-        base = tile * tbits + kbits + 64 * off + 32 * r + inword
-        pos = base[:, None] + np.arange(w)[None, :]
-        weights = (1 << np.arange(w))[None, :]
-        cV[:, j] += ((bitarr[pos].astype(np.int64) * weights).sum(axis=1)) << e
-        off += w
-    return cK, cV
+    BK, BV = _check_bits(bK, bV)
+    raw = np.asarray(cache, np.uint8)
+    offK, offV = _byte_offsets(n, BK, BV)
+    out = []
+    for bits, off in ((bK, offK), (bV, offV)):
+        rec = raw[off].astype(np.int64) ^ 0x80
+        c = np.zeros((n, len(bits)), np.int64)
+        for (j, w, e, q, p) in fields(bits):
+            c[:, j] |= ((rec[:, q] >> p) & ((1 << w) - 1)) << e
+        out.append(c)
+    return out[0], out[1]
 
 
 def encode_cache(K: np.ndarray, V: np.ndarray, cb, n_tiles: int | None = None):

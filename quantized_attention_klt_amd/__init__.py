@@ -48,7 +48,7 @@ class Cache(C.Structure):
 EXPORTS = [
     "aatc_version", "aatc_layout_version", "aatc_status_string", "aatc_last_error",
     "aatc_stats_from_samples", "aatc_calibrate", "aatc_codebook_create", "aatc_codebook_info",
-    "aatc_codebook_head", "aatc_codebook_save", "aatc_codebook_load", "aatc_codebook_free",
+    "aatc_codebook_head", "aatc_codebook_fields", "aatc_codebook_save", "aatc_codebook_load", "aatc_codebook_free",
     "aatc_codebook_device_bytes", "aatc_codebook_upload", "aatc_cache_bytes", "aatc_encode",
     "aatc_encode_coeffs", "aatc_decode_workspace_bytes", "aatc_decode_attention",
     "aatc_flush_write", "aatc_profile_begin", "aatc_profile_end",
@@ -83,6 +83,7 @@ def load() -> C.CDLL:
         "aatc_codebook_create": ([i32, i32, i32, i32, P, P, P, P, P, P, P, P, C.POINTER(P)], C.c_int),
         "aatc_codebook_info": ([P, P, P, P, P, P, P], C.c_int),
         "aatc_codebook_head": ([P, i32] + [P] * 13, C.c_int),
+        "aatc_codebook_fields": ([P, i32, i32, P, P], C.c_int),
         "aatc_codebook_save": ([P, C.c_char_p], C.c_int),
         "aatc_codebook_load": ([C.c_char_p, C.POINTER(P)], C.c_int),
         "aatc_codebook_free": ([P], None),
@@ -200,6 +201,14 @@ class Codebook:
                                          _ptr(r["stepV"]), _ptr(th)))
         r["theta"] = float(th[0])
         return r
+
+    def fields(self, h: int, which: int) -> list:
+        """Record fields of head h (which: 0 keys, 1 values) as (chan, width, shift, byte, pos)."""
+        n = C.c_int32(0)
+        buf = np.zeros(384, np.uint32)
+        _check(load().aatc_codebook_fields(self.handle, h, which, _ptr(buf), C.byref(n)))
+        return [(int(x) & 0xFF, (int(x) >> 8) & 0xF, (int(x) >> 12) & 0xF, int(x) >> 20, (int(x) >> 16) & 0xF)
+                for x in buf[:n.value]]
 
     def save(self, path: str):
         _check(load().aatc_codebook_save(self.handle, path.encode()))

@@ -12,19 +12,19 @@ namespace aatc {
 
 constexpr int kTile = 64;        // token slots per tile
 constexpr int kMaxD = 128;       // largest head_dim
-constexpr int kMaxPieces = 512;  // >= 3 pieces per channel * 128 channels
+constexpr int kMaxFields = 384;  // fields of one record: <= d channels + 2 per record byte
 constexpr int kMaxQM = 16;       // score MFMAs per token group (<= 32 words x 8 fields / 16)
-constexpr int kMaxVB = 32;       // value column blocks of 16 pieces per head
+constexpr int kMaxVB = 24;       // value column blocks of 16 fields per head
 constexpr int kKeyAlign = 32;    // key bits per token are a multiple of one 32-bit word
 
-// One power-of-two piece of a channel's code: bits [shift, shift + width) of the code.
-// Pieces are ordered by width (4, 2, 1) then by KLT channel; `offset` is the sum of the
-// widths before it (bit offset inside a token's key record, or slab index for values).
-struct Piece {
+// One byte-aligned field of a token record: code bits [shift, shift + width) of channel
+// chan at bits [pos, pos + width) of record byte `byte` (never crossing a byte).
+struct Field {
     int chan;
     int width;
     int shift;
-    int offset;
+    int byte;
+    int pos;
 };
 
 struct HeadCB {
@@ -35,15 +35,15 @@ struct HeadCB {
     std::vector<int32_t> bK, bV;
     std::vector<float> stepK, stepV;
     double theta = 0.0;
-    // derived
-    std::vector<Piece> pK, pV;
+    // derived: record fields sorted by (byte, pos)
+    std::vector<Field> fK, fV;
     int BK = 0, BV = 0;
 };
 
 // Device blob of one head.  Arrays are sized for d = 128 and indexed densely for the
-// actual d (e.g. UK[i*d + j]).  Packed piece words: chan | width<<8 | shift<<12 | offset<<16.
+// actual d (e.g. UK[i*d + j]).
 struct alignas(256) DevHead {
-    int32_t d, BK, BV, nKp, nVp;
+    int32_t d, BK, BV, nfK, nfV;
     int32_t pad0[59];
     float UK[kMaxD * kMaxD];      // fp32 basis (query transform)
     float UV[kMaxD * kMaxD];      // fp32 basis (inverse transform of values)
@@ -59,8 +59,9 @@ struct alignas(256) DevHead {
     float stepK[kMaxD], stepV[kMaxD];
     float invK[kMaxD], invV[kMaxD];
     int32_t bitsK[kMaxD], bitsV[kMaxD];
-    int32_t pieceK[kMaxPieces];
-    int32_t pieceV[kMaxPieces];
+    // record fields sorted by (byte, pos): chan | width << 8 | shift << 12 | pos << 16 | byte << 20
+    uint32_t fieldK[kMaxFields];
+    uint32_t fieldV[kMaxFields];
     // ---- decode schedule -------------------------------------------------------------
     // Score MFMAs: nqm per token group.  The B operand of lane group g (lanes 16g..16g+15,
     // K-slots 16g..16g+15) in MFMA m is four dwords; dword i is key-record word
@@ -70,17 +71,21 @@ struct alignas(256) DevHead {
     // the field ends at bit 7, so the stored inverted bit 7 makes the byte read 128 low),
     // 0xFFFF for an empty byte.
     int32_t nqm;
-    int32_t nvb[3];  // value column blocks of widths 4, 2, 1 (16 pieces each)
-    int32_t pad1[4];
+    int32_t nvb;  // value column blocks of 16 fields
+    int32_t pad1[6];
     int16_t kq_word[kMaxQM][4][4];
     uint32_t kq_mask[kMaxQM][4][4];
     uint16_t kq_slot[kMaxQM][4][16];
-    // value column blocks: first word of each column's slab inside the value block
-    // (padding columns repeat a real slab), and chan | e << 8 (-1 for padding)
-    int16_t vb_slab[kMaxVB][16];
-    int16_t vb_map[kMaxVB][16];
-    // value channel j -> up to 3 (column | shift << 12) entries, -1 terminated
-    int16_t chan_cols[kMaxD][4];
+    // Value MFMAs: column c of block cb is value field 16 cb + c (fieldV order): the byte
+    // plane of its record byte (value-block offset 64 * byte) and its mask within the
+    // byte; padding columns have plane 0 and mask 0.
+    uint16_t vb_plane[kMaxVB][16];
+    uint8_t vb_mask[kMaxVB][16];
+    // Value channel j: columns vch_col[vch_first[j] .. vch_first[j + 1]), each
+    // col | (shift - pos + 8) << 9 | flip << 13.
+    int16_t vch_first[kMaxD + 1];
+    int16_t pad2[7];
+    uint16_t vch_col[kMaxFields];
 };
 
 }  // namespace aatc
@@ -98,7 +103,7 @@ struct aatc_codebook {
 namespace aatc {
 
 int set_error(int code, const char* fmt, ...);
-int finalize(aatc_codebook* cb);  // pieces, B, device blob; validates budget
+int finalize(aatc_codebook* cb);  // fields, B, device blob; validates budget
 uint16_t f32_to_bf16(float f);
 float bf16_to_f32(uint16_t h);
 

@@ -280,40 +280,62 @@ static const double* step_table() {
 // ------------------------------------------------------------------------------------
 // derived tables and device blob
 // ------------------------------------------------------------------------------------
-// Pieces of width 4, 2 or 1 (as many 4-bit pieces as fit from the top bit, then 2, then 1),
-// ordered by width, channel, then shift (high first).
-static void make_pieces(const std::vector<int32_t>& bits, std::vector<Piece>& out, int& total) {
+// Byte-aligned fields of one record (the packed layout): channels with b > 0, widest
+// first (ties: lower channel), each whole in the lowest-index byte with room, at that
+// byte's lowest free bit; channels left over are cut into pieces that fill free bits byte
+// by byte (lowest code bits first); finally bytes are renumbered by decreasing field
+// count (ties: lower byte).  Returns false if the bits do not fill whole bytes.
+static bool make_fields(const std::vector<int32_t>& bits, std::vector<Field>& out, int& total) {
     out.clear();
-    int off = 0;
-    for (int w = 4; w >= 1; w >>= 1)
-        for (int j = 0; j < (int)bits.size(); ++j) {
-            int rem = bits[j];
-            for (int pw : {4, 4, 2, 1}) {
-                if (rem < pw) continue;
-                rem -= pw;
-                if (pw == w) {
-                    out.push_back({j, w, rem, off});
-                    off += w;
-                }
-            }
+    total = 0;
+    for (int b : bits) total += b;
+    if (total % 8) return false;
+    const int nbytes = total / 8;
+    std::vector<int> free(nbytes, 8), order, left;
+    for (int j = 0; j < (int)bits.size(); ++j)
+        if (bits[j] > 0) order.push_back(j);
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return bits[a] > bits[b]; });
+    for (int j : order) {
+        int q = 0;
+        while (q < nbytes && free[q] < bits[j]) ++q;
+        if (q == nbytes) {
+            left.push_back(j);
+            continue;
         }
-    total = off;
+        out.push_back({j, bits[j], 0, q, 8 - free[q]});
+        free[q] -= bits[j];
+    }
+    for (int j : left) {
+        int e = 0;
+        for (int q = 0; q < nbytes && e < bits[j]; ++q) {
+            const int w = std::min(free[q], bits[j] - e);
+            if (w <= 0) continue;
+            out.push_back({j, w, e, q, 8 - free[q]});
+            free[q] -= w;
+            e += w;
+        }
+    }
+    std::vector<int> count(nbytes, 0), byrank(nbytes), rank(nbytes);
+    for (const Field& f : out) ++count[f.byte];
+    for (int q = 0; q < nbytes; ++q) byrank[q] = q;
+    std::stable_sort(byrank.begin(), byrank.end(), [&](int a, int b) { return count[a] > count[b]; });
+    for (int i = 0; i < nbytes; ++i) rank[byrank[i]] = i;
+    for (Field& f : out) f.byte = rank[f.byte];
+    std::sort(out.begin(), out.end(),
+              [](const Field& a, const Field& b) { return a.byte != b.byte ? a.byte < b.byte : a.pos < b.pos; });
+    return true;
 }
 
 // Decode schedule of one head (see DevHead).  Scores: every key-record word is split
-// into "dwords", one per field position (a byte holds 2 nibbles, 4 crumbs or 8 bits, or a
-// mix at a width boundary); each dword keeps one field per byte under a mask.  Dwords
-// fill the score MFMAs in record order, 16 per MFMA (four per lane group).  Values: the
-// pieces grouped into MFMA column blocks of one width.
+// into "dwords", one per field index within a byte; each dword keeps one field per byte
+// under a mask.  Dwords fill the score MFMAs in record order, 16 per MFMA (four per lane
+// group).  Values: one MFMA column per value field, 16 per column block.
 static int build_decode_schedule(const HeadCB& H, DevHead& D) {
     for (int m = 0; m < kMaxQM; ++m)
         for (int g = 0; g < 4; ++g) {
             for (int i = 0; i < 4; ++i) D.kq_word[m][g][i] = 0, D.kq_mask[m][g][i] = 0u;
             for (int i = 0; i < 16; ++i) D.kq_slot[m][g][i] = 0xFFFF;
         }
-    struct Field {
-        int chan, w, shift, pos;
-    };
     struct Dword {
         int word;
         uint32_t mask;
@@ -322,22 +344,18 @@ static int build_decode_schedule(const HeadCB& H, DevHead& D) {
     std::vector<Dword> dws;
     const int WK = H.BK / 32;
     for (int r = 0; r < WK; ++r) {
-        std::vector<Field> fb[4];
-        for (const Piece& p : H.pK)
-            if (p.offset >= 32 * r && p.offset < 32 * r + 32) {
-                const int bit = p.offset - 32 * r;
-                if (bit / 8 != (bit + p.width - 1) / 8) return AATC_ERR_UNSUPPORTED;  // fields never straddle bytes
-                fb[bit / 8].push_back({p.chan, p.width, p.shift, bit % 8});
-            }
+        std::vector<const Field*> fb[4];
+        for (const Field& f : H.fK)
+            if (f.byte / 4 == r) fb[f.byte % 4].push_back(&f);  // in bit order (fields are sorted)
         size_t nd = 0;
         for (int b = 0; b < 4; ++b) nd = std::max(nd, fb[b].size());
         for (size_t j = 0; j < nd; ++j) {
             Dword dw{r, 0u, {0xFFFF, 0xFFFF, 0xFFFF, 0xFFFF}};
             for (int b = 0; b < 4; ++b) {
                 if (j >= fb[b].size()) continue;
-                const Field& f = fb[b][j];
-                dw.mask |= ((1u << f.w) - 1u) << (8 * b + f.pos);
-                const int flip = f.pos + f.w == 8 ? 1 : 0;
+                const Field& f = *fb[b][j];
+                dw.mask |= ((1u << f.width) - 1u) << (8 * b + f.pos);
+                const int flip = f.pos + f.width == 8 ? 1 : 0;
                 dw.slot[b] = (uint16_t)(f.chan | (f.shift << 8) | (f.pos << 11) | (flip << 14));
             }
             dws.push_back(dw);
@@ -352,35 +370,26 @@ static int build_decode_schedule(const HeadCB& H, DevHead& D) {
         D.kq_mask[m][g][i] = dws[k].mask;
         for (int b = 0; b < 4; ++b) D.kq_slot[m][g][4 * i + b] = dws[k].slot[b];
     }
-    // value column blocks
+    // value columns
+    const int nf = (int)H.fV.size();
+    D.nvb = std::max((nf + 15) / 16, 1);
+    if (D.nvb > kMaxVB || nf > kMaxFields) return AATC_ERR_UNSUPPORTED;
     for (int cb = 0; cb < kMaxVB; ++cb)
-        for (int c = 0; c < 16; ++c) D.vb_slab[cb][c] = 0, D.vb_map[cb][c] = -1;
-    for (int j = 0; j < kMaxD; ++j)
-        for (int t = 0; t < 4; ++t) D.chan_cols[j][t] = -1;
-    const int width_of[3] = {4, 2, 1};
-    int cb = 0;
-    for (int m = 0; m < 3; ++m) {
-        std::vector<const Piece*> ps;
-        for (const Piece& p : H.pV)
-            if (p.width == width_of[m]) ps.push_back(&p);
-        int nb = ((int)ps.size() + 15) / 16;
-        D.nvb[m] = nb;
-        for (int b = 0; b < nb; ++b, ++cb) {
-            if (cb >= kMaxVB) return AATC_ERR_UNSUPPORTED;
-            for (int c = 0; c < 16; ++c) {
-                int i = 16 * b + c;
-                const Piece* p = i < (int)ps.size() ? ps[i] : ps[16 * b];
-                D.vb_slab[cb][c] = (int16_t)(2 * p->offset);
-                if (i < (int)ps.size()) {
-                    D.vb_map[cb][c] = (int16_t)(p->chan | (p->shift << 8));
-                    int col = 16 * cb + c;
-                    for (int t = 0; t < 3; ++t)
-                        if (D.chan_cols[p->chan][t] < 0) {
-                            D.chan_cols[p->chan][t] = (int16_t)(col | (p->shift << 12));
-                            break;
-                        }
-                }
-            }
+        for (int c = 0; c < 16; ++c) D.vb_plane[cb][c] = 0, D.vb_mask[cb][c] = 0;
+    for (int i = 0; i < nf; ++i) {
+        const Field& f = H.fV[i];
+        D.vb_plane[i / 16][i % 16] = (uint16_t)(64 * f.byte);
+        D.vb_mask[i / 16][i % 16] = (uint8_t)(((1u << f.width) - 1u) << f.pos);
+    }
+    int n = 0;
+    for (int j = 0; j <= kMaxD; ++j) {
+        D.vch_first[j] = (int16_t)n;
+        if (j == kMaxD || j >= (int)H.bV.size()) continue;
+        for (int i = 0; i < nf; ++i) {
+            const Field& f = H.fV[i];
+            if (f.chan != j) continue;
+            const int flip = f.pos + f.width == 8 ? 1 : 0;
+            D.vch_col[n++] = (uint16_t)(i | ((f.shift - f.pos + 8) << 9) | (flip << 13));
         }
     }
     return AATC_OK;
@@ -398,8 +407,10 @@ int finalize(aatc_codebook* cb) {
                 (H.bV[j] > 0 && !(H.stepV[j] > 0 && std::isfinite(H.stepV[j]))))
                 return set_error(AATC_ERR_STATS, "head %zu channel %d: coded channel needs a positive step", h, j);
         }
-        make_pieces(H.bK, H.pK, H.BK);
-        make_pieces(H.bV, H.pV, H.BV);
+        if (!make_fields(H.bK, H.fK, H.BK) || !make_fields(H.bV, H.fV, H.BV))
+            return set_error(AATC_ERR_BUDGET, "head %zu: key and value bits per token must be whole bytes", h);
+        if ((int)H.fK.size() > kMaxFields || (int)H.fV.size() > kMaxFields)
+            return set_error(AATC_ERR_UNSUPPORTED, "head %zu: more than %d fields in a record", h, kMaxFields);
         if (H.BK % kKeyAlign)
             return set_error(AATC_ERR_BUDGET, "head %zu: key bits per token (%d) must be a multiple of %d", h, H.BK,
                              kKeyAlign);
@@ -407,7 +418,7 @@ int finalize(aatc_codebook* cb) {
         if (total < 0) total = B;
         if (B != total) return set_error(AATC_ERR_BUDGET, "head %zu has %d bits per token, head 0 has %d", h, B, total);
     }
-    if (total <= 0 || total % 2) return set_error(AATC_ERR_BUDGET, "bits per token (%d) must be a positive even number", total);
+    if (total <= 0 || total % 8) return set_error(AATC_ERR_BUDGET, "bits per token (%d) must be a positive multiple of 8", total);
     cb->total_bits = total;
 
     cb->blob.assign(cb->heads.size(), DevHead());
@@ -418,8 +429,8 @@ int finalize(aatc_codebook* cb) {
         D.d = d;
         D.BK = H.BK;
         D.BV = H.BV;
-        D.nKp = (int)H.pK.size();
-        D.nVp = (int)H.pV.size();
+        D.nfK = (int)H.fK.size();
+        D.nfV = (int)H.fV.size();
         for (int which = 0; which < 2; ++which) {
             const std::vector<double>& U = which ? H.UV : H.UK;
             const std::vector<double>& mu = which ? H.muV : H.muK;
@@ -459,10 +470,13 @@ int finalize(aatc_codebook* cb) {
                 if (H.bV[j] > 0) o -= H.UV[(size_t)i * d + j] * (double)H.stepV[j] * ((double)(1 << (H.bV[j] - 1)) - 0.5);
             D.obias[i] = (float)o;
         }
-        for (size_t p = 0; p < H.pK.size(); ++p)
-            D.pieceK[p] = H.pK[p].chan | (H.pK[p].width << 8) | (H.pK[p].shift << 12) | (H.pK[p].offset << 16);
-        for (size_t p = 0; p < H.pV.size(); ++p)
-            D.pieceV[p] = H.pV[p].chan | (H.pV[p].width << 8) | (H.pV[p].shift << 12) | (H.pV[p].offset << 16);
+        for (int which = 0; which < 2; ++which) {
+            const std::vector<Field>& fs = which ? H.fV : H.fK;
+            uint32_t* dst = which ? D.fieldV : D.fieldK;
+            for (size_t i = 0; i < fs.size(); ++i)
+                dst[i] = (uint32_t)(fs[i].chan | (fs[i].width << 8) | (fs[i].shift << 12) | (fs[i].pos << 16) |
+                                    (fs[i].byte << 20));
+        }
         int rc = build_decode_schedule(H, D);
         if (rc != AATC_OK) return set_error(rc, "head %zu: %s", h, "decode schedule exceeds kernel limits");
     }
@@ -609,8 +623,8 @@ extern "C" int aatc_calibrate(int32_t d, int32_t n_layers, int32_t n_kv, int32_t
     if (max_bits < 1 || max_bits > 8) return set_error(AATC_ERR_INVALID_ARG, "max_bits must be in [1,8]");
     double totf = 2.0 * d * p->avg_bits;
     int total = (int)std::llround(totf);
-    if (!(p->avg_bits > 0) || std::fabs(totf - total) > 1e-9 || total % 2 || total > 2 * d * max_bits)
-        return set_error(AATC_ERR_BUDGET, "2*d*avg_bits = %g must be an even integer in (0, %d]", totf, 2 * d * max_bits);
+    if (!(p->avg_bits > 0) || std::fabs(totf - total) > 1e-9 || total % 8 || total > 2 * d * max_bits)
+        return set_error(AATC_ERR_BUDGET, "2*d*avg_bits = %g must be a multiple of 8 in (0, %d]", totf, 2 * d * max_bits);
     if (!p->joint && (total / 2) % kKeyAlign)
         return set_error(AATC_ERR_BUDGET, "separate key/value budgets need d*avg_bits (%d) to be a multiple of %d",
                          total / 2, kKeyAlign);
@@ -783,6 +797,20 @@ extern "C" int aatc_codebook_head(const aatc_codebook* cb, int32_t head, double*
     copy_out(step_k, H.stepK);
     copy_out(step_v, H.stepV);
     if (theta) *theta = H.theta;
+    return AATC_OK;
+}
+
+extern "C" int aatc_codebook_fields(const aatc_codebook* cb, int32_t head, int32_t which, uint32_t* out,
+                                    int32_t* n) {
+    if (!cb || !n) return set_error(AATC_ERR_INVALID_ARG, "null pointer");
+    if (head < 0 || head >= (int)cb->heads.size()) return set_error(AATC_ERR_INVALID_ARG, "head %d out of range", head);
+    if (which != 0 && which != 1) return set_error(AATC_ERR_INVALID_ARG, "which must be 0 (keys) or 1 (values)");
+    const std::vector<Field>& fs = which ? cb->heads[head].fV : cb->heads[head].fK;
+    *n = (int32_t)fs.size();
+    if (out)
+        for (size_t i = 0; i < fs.size(); ++i)
+            out[i] = (uint32_t)(fs[i].chan | (fs[i].width << 8) | (fs[i].shift << 12) | (fs[i].pos << 16) |
+                                (fs[i].byte << 20));
     return AATC_OK;
 }
 

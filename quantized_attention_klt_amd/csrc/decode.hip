@@ -9,33 +9,31 @@
 // Two kernels on the caller's stream:
 //   qprep  - one workgroup per (sequence, kv-head) forms q' = U_K^T q for its query
 //            heads, scales it by the key steps (and log2 e / sqrt d) and splits it into
-//            three int8 digits laid out as the A operands of the score MFMAs (slot order =
-//            the key unpack schedule).
+//            three int8 digits laid out as the A operands of the score MFMAs (one byte per
+//            key field, weighted by the field's code shift over its bit position).
 //   decode - a workgroup of 4 waves owns a run of 64-token tiles of one (sequence,
-//            kv-head):
-//   prologue - the query operands, the channel map and the first tiles stream into LDS
-//              (direct global->LDS loads); the operands then stay in registers.
-//   tiles    - the four waves work on each tile together:
-//                scores  - wave w takes tokens 16w..16w+15: key pieces are unpacked with
-//                          SWAR shift/mask into int8 operands of v_mfma_i32_16x16x64_i8;
-//                          MFMA rows are 4*head + digit, so a lane holds the three digit
-//                          rows of one head and combines them in registers;
-//                softmax - per-head tile maxima meet in LDS; every wave keeps the same
-//                          online reference maximum (base 2, raised lazily with headroom);
-//                          probabilities become three int8 digits in LDS;
-//                values  - wave w takes value column blocks w, w+4, ... over all 64
-//                          tokens and accumulates P x pieces in int32 with the same MFMA.
-//              Barriers only order LDS; the ring keeps up to nb-1 tiles in flight and each
-//              wave waits on its own load count.
-//   merge    - each workgroup writes one partial (max, sum, coefficient accumulator per
-//              query head) with device-coherent stores; the last workgroup of each group
-//              of partials merges them, and the last group merger of each (sequence,
-//              kv-head) merges the group results, dequantises the value coefficients and
-//              applies U_V and mu_V.  Arrival counters wrap to zero on the last arrival
-//              (atomic increment modulo the member count), so a zeroed workspace stays
-//              ready for the next call.
-// Inner loops are branch-free straight-line code (compile-time bounds NQM score MFMAs per
-// blocks and NVB value column blocks; the unpack mode of a block is a uniform select).
+//            kv-head); wave w takes tiles w, w+4, ... of the run and streams them through
+//            a private ring of LDS buffers (direct global->LDS loads, counted waits, no
+//            workgroup barriers in the loop).  Per tile:
+//     scores  - v_mfma_i32_16x16x64_i8 with rows 4*head + digit and one column per token:
+//               a B dword is a key-record word ANDed with a mask that keeps one field per
+//               byte; with bit 7 of stored bytes inverted such a byte reads as
+//               field * 2^pos (- 128 when the field ends at bit 7), the 2^pos is divided
+//               out of the query digits and the -128 is the accumulator's start value;
+//     softmax - online, base 2, reference max raised lazily with headroom; probabilities
+//               p * 127 * 2^16 are rounded to integers whose bytes are three int8 digits
+//               (base 256), written over the tile's key block as the next A operand;
+//     values  - the same MFMA with one column per value field: the B operand of a column
+//               is 16 bytes of its record byte's plane (16 tokens) ANDed with the field
+//               mask.  Column weights 2^(shift - pos) and the -128 of top fields (fixed
+//               by the exact integer row sums of the probability digits) are applied once
+//               at the end.
+//   merge   - each workgroup writes one partial (max, sum, value-coefficient accumulator per
+//             query head) with device-coherent stores; the last workgroup of each group of
+//             partials merges them and applies U_V to its result, and the last group merger
+//             of each (sequence, kv-head) combines the group results into the output.
+//             Arrival counters wrap to zero on the last arrival (atomic increment modulo
+//             the member count), so a zeroed workspace stays ready for the next call.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -66,8 +64,9 @@ constexpr int kCounterSlots = 32768;
 constexpr size_t kCounterBytes = kCounterSlots * sizeof(uint32_t);
 constexpr float kHeadroom = 2.0f;    // log2 headroom added to the reference max at a rescale
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr uint32_t kM4 = 0x0F0F0F0Fu, kM2 = 0x03030303u, kM1 = 0x01010101u;
-constexpr float kDig1 = 1.0f / 254.0f, kDig2 = 1.0f / 64516.0f;
+constexpr float kQ1 = 1.0f / 254.0f, kQ2 = 1.0f / 64516.0f;  // query digit weights (base 254)
+constexpr float kP1 = 1.0f / 256.0f, kP2 = 1.0f / 65536.0f;  // probability digit weights (base 256)
+constexpr float kPScale = 127.0f * 65536.0f;                  // p -> integer of three digits
 constexpr int kQscStride = 80;  // floats per (sequence, kv-head) in the query-scale buffer
 
 struct DecodeArgs {
@@ -139,37 +138,27 @@ __device__ __forceinline__ void load_tile(const uint8_t* src, LDS_AS uint8_t* ld
 // all of this wave's memory operations (incl. global->LDS tile loads) have completed
 __device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
 
-// Four int8 operand words from packed pieces.  m4 / m2 select the 4-bit / 2-bit modes
-// (uniform), otherwise 1-bit: 4-bit takes the nibbles of x0 then x1, 2-bit the crumbs of
-// x0, 1-bit bits 0..3 of each byte of x0 >> pre.
-__device__ __forceinline__ v4i unpack(uint32_t x0, uint32_t x1, bool m4, bool m2, uint32_t pre) {
-    const uint32_t base = (m4 || m2) ? x0 : (x0 >> pre);
-    const uint32_t hi = m4 ? x1 : base;
-    const uint32_t M = m4 ? kM4 : (m2 ? kM2 : kM1);
-    const uint32_t s1 = m4 ? 4u : (m2 ? 2u : 1u), s2 = m4 ? 0u : (m2 ? 4u : 2u), s3 = m4 ? 4u : (m2 ? 6u : 3u);
-    return v4i{(int)(base & M), (int)((base >> s1) & M), (int)((hi >> s2) & M), (int)((hi >> s3) & M)};
-}
-
-// The same, one width at a time (compile-time mode, no selects).
-template <int W>
-__device__ __forceinline__ v4i unpack_w(uint32_t x0, uint32_t x1, uint32_t pre) {
-    if constexpr (W == 4) {
-        return v4i{(int)(x0 & kM4), (int)((x0 >> 4) & kM4), (int)(x1 & kM4), (int)((x1 >> 4) & kM4)};
-    } else if constexpr (W == 2) {
-        return v4i{(int)(x0 & kM2), (int)((x0 >> 2) & kM2), (int)((x0 >> 4) & kM2), (int)((x0 >> 6) & kM2)};
-    } else {
-        const uint32_t b = x0 >> pre;
-        return v4i{(int)(b & kM1), (int)((b >> 1) & kM1), (int)((b >> 2) & kM1), (int)((b >> 3) & kM1)};
-    }
-}
-
 // three base-254 digits of x: x = d0 + d1 / 254 + d2 / 254^2 (+ rounding); each fits int8
 // when |x| <= 127
-__device__ __forceinline__ void digits(float x, float& d0, float& d1, float& d2) {
+__device__ __forceinline__ void digits254(float x, float& d0, float& d1, float& d2) {
     d0 = rintf(x);
     const float r1 = (x - d0) * 254.0f;
     d1 = rintf(r1);
     d2 = rintf((r1 - d1) * 254.0f);
+}
+
+// an int32 accumulator triple (digit rows of weight 1, 1/256, 1/65536) as one float
+__device__ __forceinline__ float combine256(int a0, int a1, int a2) {
+    return (float)a0 + (float)a1 * kP1 + (float)a2 * kP2;
+}
+// ... and back: x = d0 + d1 / 256 + d2 / 65536 (+ rounding of the last digit)
+__device__ __forceinline__ void split256(float x, int& a0, int& a1, int& a2) {
+    const float d0 = rintf(x);
+    const float r1 = (x - d0) * 256.0f;
+    const float d1 = rintf(r1);
+    a0 = (int)d0;
+    a1 = (int)d1;
+    a2 = (int)rintf((r1 - d1) * 256.0f);
 }
 
 // Merge n partials (reference max m, sum l, coefficient accumulator x[d] per query head,
@@ -217,10 +206,12 @@ __device__ __forceinline__ void merge_cols(const float* src, int n, int G, int t
 
 // ---------------------------------------------------------------------------------------
 // query preparation, one workgroup per (sequence, kv-head): q'' = (U_K^T q) * step_K *
-// log2(e) / sqrt(d) for the G query heads, split into three int8 digits and written as the
-// A operands of the score MFMAs ([qb][rb][lane][16] bytes; lane row = 4 head + digit, slot
-// order = the key unpack schedule), plus the per-head digit scale (max |q'' 2^top| / 127).
-// Every global read is issued in one batch so that a cold codebook costs one latency.
+// log2(e) / sqrt(d) for the G query heads; key field (chan, shift, pos) of score slot k
+// gets q''[chan] * 2^shift / 2^pos, scaled per head so that the largest slot is 127 and
+// split into three int8 digits; written as the A operands of the score MFMAs
+// ([m][rb][lane][16] bytes; lane row = 4 head + digit).  Also per head the digit scale
+// and per operand row 128 x the digits of slots whose field ends at bit 7.  Every global
+// read is issued in one batch so that a cold codebook costs one latency.
 // ---------------------------------------------------------------------------------------
 template <int RB, int NQM, int D>
 __global__ __launch_bounds__(256) void qprep_kernel(const DevHead* __restrict__ blob, int layer, int n_kv, int G,
@@ -278,15 +269,25 @@ __global__ __launch_bounds__(256) void qprep_kernel(const DevHead* __restrict__ 
     }
     __syncthreads();
     const float qscale = kLog2e / sqrtf((float)D);
-    const int top = bj >= 4 ? bj - 4 : (bj >= 2 ? bj - 2 : 0);  // shift of the channel's top piece
     for (int hh = pt; hh < G; hh += PARTS) {
         float acc = 0.0f;
 #pragma unroll
         for (int p2 = 0; p2 < PARTS; ++p2) acc += ps[(p2 * 16 + hh) * D + j];
-        const float v = bj ? acc * stj * qscale : 0.0f;
-        qf[hh * D + j] = v;
-        // per-head max of |v| 2^top: wave maximum, then one LDS max per wave
-        float mag = fabsf(v) * (float)(1 << top);
+        qf[hh * D + j] = bj ? acc * stj * qscale : 0.0f;
+    }
+    __syncthreads();
+    // per head: the largest slot value |q''[chan]| 2^shift / 2^pos (wave maxima, then one
+    // LDS max per wave)
+    for (int hh = 0; hh < G; ++hh) {
+        float mag = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            const int i = tid + 256 * k;
+            const uint32_t sl = kmap[i];
+            if (i < NQM * 64 && sl != 0xFFFFu)
+                mag = fmaxf(mag, fabsf(qf[hh * D + (sl & 255)]) * (float)(1 << ((sl >> 8) & 7)) *
+                                     (1.0f / (float)(1 << ((sl >> 11) & 7))));
+        }
         mag = row16_max(mag);
         mag = fmaxf(mag, __shfl_xor(mag, 16));
         mag = fmaxf(mag, __shfl_xor(mag, 32));
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(256) void qprep_kernel(const DevHead* __restrict__ 
                 if (sl != 0xFFFFu) {
                     const int chan = sl & 255, sh = (sl >> 8) & 7, pos = (sl >> 11) & 7;
                     float d0, d1, d2;
-                    digits(qf[hh * D + chan] * (float)(1 << sh) * (1.0f / (float)(1 << pos)) * sc, d0, d1, d2);
+                    digits254(qf[hh * D + chan] * (float)(1 << sh) * (1.0f / (float)(1 << pos)) * sc, d0, d1, d2);
                     const int dv = (int)(k == 0 ? d0 : (k == 1 ? d1 : d2));
                     word |= ((uint32_t)dv & 0xFFu) << (8 * e);
                     if (sl & 0x4000u) flipped += dv;
@@ -331,7 +332,7 @@ __global__ __launch_bounds__(256) void qprep_kernel(const DevHead* __restrict__ 
 
 // Registers per lane grow with the row blocks and value column blocks; the waves per SIMD
 // the allocation is sized for (the LDS plan matches it).
-constexpr int vgpr_estimate(int rb, int nqm, int nvb) { return rb * nvb * 4 + nqm * (rb * 4 + 8) + rb * 16 + nvb / 2 + 50; }
+constexpr int vgpr_estimate(int rb, int nqm, int nvb) { return rb * nvb * 4 + nqm * rb * 4 + 2 * nvb + rb * 20 + 56; }
 constexpr int waves_for(int rb, int nqm, int nvb) {
     return vgpr_estimate(rb, nqm, nvb) <= 128 ? 4 : (vgpr_estimate(rb, nqm, nvb) <= 168 ? 3 : 2);
 }
@@ -352,13 +353,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
     const int g = lane >> 4, c = lane & 15;
     const DevHead& H = blob[a.layer * a.n_kv + h];
     const int G = a.G, TB = a.tile_bytes, BB = a.buf_bytes;
-    const int WK = H.BK >> 5;  // key record words per token
-    int nvb4 = H.nvb[0], nvb2 = H.nvb[1];
-    const int nvb = H.nvb[0] + H.nvb[1] + H.nvb[2];
+    const int nvb = H.nvb;
     const int64_t zh = (int64_t)z * a.n_kv + h;
 
-    // this wave's LDS: two tile buffers; the probability operand [RB*16 rows][64 tokens]
-    // overwrites the key block of the current tile once its scores are done
+    // this wave's LDS: a ring of tile buffers; the probability operand [RB*16 rows][64
+    // tokens] overwrites the key block of the current tile once its scores are done
     LDS_AS uint8_t* ring = sm + w * a.wave_bytes;
     LDS_AS int* flag = (LDS_AS int*)(sm + a.off_flag);
 
@@ -388,33 +387,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
         ((LDS_AS uint32_t*)ksched)[i] =
             e < 4 ? 256u * (uint32_t)H.kq_word[m][gg][e] : H.kq_mask[m][gg][e - 4];
     }
-    constexpr int NVP = (NVB + 1) / 2;
-    uint32_t vofs[NVP];  // word of this lane's value slab (+ its 16-token offset), two blocks per register
+    // value columns of this lane (column c of each block): tile byte offset of the lane's
+    // 16 tokens in its record byte's plane, and the field mask repeated in every byte
+    uint32_t voff[NVB], vmask[NVB];
 #pragma unroll
-    for (int k = 0; k < NVP; ++k) {
-        uint32_t v2 = 0u;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int cb = 2 * k + e;
-            const int mode = cb < nvb4 ? 0 : (cb < nvb4 + nvb2 ? 1 : 2);
-            const uint32_t wi = cb < nvb ? (uint32_t)H.vb_slab[cb][c] + (uint32_t)((2 * g) >> mode) : 0u;
-            v2 |= wi << (16 * e);
-        }
-        vofs[k] = v2;
+    for (int cb = 0; cb < NVB; ++cb) {
+        voff[cb] = 8u * (uint32_t)H.BK + (uint32_t)H.vb_plane[cb][c] + 16u * (uint32_t)g;
+        vmask[cb] = 0x01010101u * (uint32_t)H.vb_mask[cb][c];
     }
     float qs[RB][3];  // digit scales of this lane's query head
-    bool hv[RB];
     v4i sinit[RB];    // score accumulator start: the inverted-bit-7 correction of each row
     {
         const float* qsc = qscale + zh * kQscStride;
         const int* qci = (const int*)qsc + 16;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            hv[rb] = 4 * rb + g < G;
             const float mx = qsc[4 * rb + g];
             qs[rb][0] = mx;
-            qs[rb][1] = mx * kDig1;
-            qs[rb][2] = mx * kDig2;
+            qs[rb][1] = mx * kQ1;
+            qs[rb][2] = mx * kQ2;
             sinit[rb] = v4i{qci[16 * rb + 4 * g], qci[16 * rb + 4 * g + 1], qci[16 * rb + 4 * g + 2], 0};
         }
     }
@@ -426,19 +417,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
         for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(Aq[m][rb]));
     lds_barrier();  // the key schedule table is staged
 #pragma unroll
-    for (int k = 0; k < NVP; ++k) asm volatile("" ::"v"(vofs[k]));
+    for (int cb = 0; cb < NVB; ++cb) asm volatile("" ::"v"(voff[cb]), "v"(vmask[cb]));
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(qs[rb][0]), "v"(sinit[rb]));
-    const uint32_t pre1 = 4 * (g & 1);
 
-    // int32 sums of P digits x value pieces, relative to the reference max mref (a rescale
-    // combines the three digit sums, scales by 2^(old - new) and splits the result into
-    // digits again: the error is a float rounding of the running sum)
+    // int32 sums of P digits x value bytes, relative to the reference max mref, and the
+    // digit sums of this lane's probabilities (the row sums that undo the -128 of top
+    // fields).  A rescale combines the three digit sums, scales by 2^(old - new) and
+    // splits the result into digits again: the error is a float rounding of the sum.
     v4i acc_i[RB][NVB];
+    int ones[RB][3];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int cb = 0; cb < NVB; ++cb) acc_i[rb][cb] = v4i{0, 0, 0, 0};
+        ones[rb][0] = ones[rb][1] = ones[rb][2] = 0;
+    }
     float mref[RB], lsum[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) mref[rb] = -INFINITY, lsum[rb] = 0.0f;
@@ -452,9 +446,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
         load_tile(tiles + (t + kWaves * k) * TB, ring + k * BB, TB, lane);
     int slot = 0;
     for (; t < t_end; t += kWaves) {
-        // the unpack modes of the value blocks derive from these counts inside the loop (a
-        // few scalar ops per block) instead of being hoisted into live scalar registers
-        asm volatile("" : "+s"(nvb4), "+s"(nvb2));
         // tile t has landed once only the later tiles' loads may be outstanding; this wave's
         // LDS reads of the slot refilled next are done
         wait_vm(nl * (int)min((int64_t)NBW - 2, (t_end - 1 - t) / kWaves));
@@ -462,7 +453,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
         const int64_t tn = t + (int64_t)kWaves * (NBW - 1);
         if (tn < t_end) load_tile(tiles + tn * TB, ring + (slot == 0 ? NBW - 1 : slot - 1) * BB, TB, lane);
         LDS_AS uint8_t* curb = ring + slot * BB;
-        const LDS_AS uint32_t* cur = (const LDS_AS uint32_t*)curb;
         slot = slot + 1 == NBW ? 0 : slot + 1;
         const int valid = (int)min((int64_t)kTile, len - t * kTile);
 
@@ -490,7 +480,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
                     S[tg][rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[m][rb], B, S[tg][rb], 0, 0, 0);
             }
         }
-        // lane (g, c) holds head 4rb+g, tokens 4c..4c+3, digit rows 0..2
+        // lane (g, c) holds head 4rb+g, tokens 4c..4c+3, digit rows 0..2 (rows of heads
+        // >= G have zero operands and stay harmless)
         float s[RB][4], tmx[RB];
         bool need = false;
 #pragma unroll
@@ -498,9 +489,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
             float mx = -INFINITY;
 #pragma unroll
             for (int tg = 0; tg < 4; ++tg) {
-                const float v = (float)S[tg][rb][0] * qs[rb][0] + (float)S[tg][rb][1] * qs[rb][1] +
-                                (float)S[tg][rb][2] * qs[rb][2];
-                s[rb][tg] = (hv[rb] && 4 * c + tg < valid) ? v : -INFINITY;
+                s[rb][tg] = (float)S[tg][rb][0] * qs[rb][0] + (float)S[tg][rb][1] * qs[rb][1] +
+                            (float)S[tg][rb][2] * qs[rb][2];
+                if (valid < kTile) s[rb][tg] = 4 * c + tg < valid ? s[rb][tg] : -INFINITY;
                 mx = fmaxf(mx, s[rb][tg]);
             }
             tmx[rb] = row16_max(mx);
@@ -511,41 +502,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
                 const float nref = tmx[rb] > mref[rb] ? tmx[rb] + kHeadroom : mref[rb];
-                const float al = hv[rb] ? exp2f(mref[rb] - nref) : 0.0f;
+                const float al = exp2f(mref[rb] - nref);
                 lsum[rb] *= al;
                 mref[rb] = nref;
 #pragma unroll
                 for (int cb = 0; cb < NVB; ++cb) {
-                    const float v = ((float)acc_i[rb][cb][0] + (float)acc_i[rb][cb][1] * kDig1 +
-                                     (float)acc_i[rb][cb][2] * kDig2) *
-                                    al;
-                    float d0, d1, d2;
-                    digits(v, d0, d1, d2);
-                    acc_i[rb][cb] = v4i{(int)d0, (int)d1, (int)d2, 0};
+                    int d0, d1, d2;
+                    split256(combine256(acc_i[rb][cb][0], acc_i[rb][cb][1], acc_i[rb][cb][2]) * al, d0, d1, d2);
+                    acc_i[rb][cb] = v4i{d0, d1, d2, 0};
                 }
+                split256(combine256(ones[rb][0], ones[rb][1], ones[rb][2]) * al, ones[rb][0], ones[rb][1], ones[rb][2]);
             }
         }
-        // probabilities as three int8 digits (p*127 = d0 + d1/254 + d2/254^2) into
-        // P[16 rb + 4 head + digit][token] over the tile's key block (wave-private; the key
-        // words of this tile were all read above)
+        // probabilities: N = round(p * 127 * 2^16) < 2^23; the bytes of N + 0x8080 with
+        // bit 7 of the two low bytes inverted are its base-256 digits (top digit 0..127, the
+        // others -128..127).  P[16 rb + 4 head + digit][token] over the tile's key block
+        // (wave-private; the key words of this tile were all read above).
         LDS_AS uint8_t* P = curb;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            uint32_t pk0 = 0u, pk1 = 0u, pk2 = 0u;
+            uint32_t Mv[4];
 #pragma unroll
             for (int tg = 0; tg < 4; ++tg) {
-                const float p = hv[rb] ? exp2f(s[rb][tg] - mref[rb]) : 0.0f;
+                const float p = __builtin_amdgcn_exp2f(s[rb][tg] - mref[rb]);
                 lsum[rb] += p;
-                float d0, d1, d2;
-                digits(p * 127.0f, d0, d1, d2);
-                pk0 |= ((uint32_t)(int)d0 & 0xFFu) << (8 * tg);
-                pk1 |= ((uint32_t)(int)d1 & 0xFFu) << (8 * tg);
-                pk2 |= ((uint32_t)(int)d2 & 0xFFu) << (8 * tg);
+                Mv[tg] = (uint32_t)fmaf(p, kPScale, 32896.5f);  // truncation: round(p 127 2^16) + 0x8080
             }
+            const uint32_t t01 = __builtin_amdgcn_perm(Mv[1], Mv[0], 0x05010400u);  // b0 b0' b1 b1'
+            const uint32_t t23 = __builtin_amdgcn_perm(Mv[3], Mv[2], 0x05010400u);
+            const uint32_t u01 = __builtin_amdgcn_perm(Mv[1], Mv[0], 0x0C0C0602u);  // b2 b2'
+            const uint32_t u23 = __builtin_amdgcn_perm(Mv[3], Mv[2], 0x0C0C0602u);
+            const uint32_t w2 = __builtin_amdgcn_perm(u23, u01, 0x05040100u);                // top digits
+            const uint32_t w1 = __builtin_amdgcn_perm(t23, t01, 0x07060302u) ^ 0x80808080u;  // middle
+            const uint32_t w0 = __builtin_amdgcn_perm(t23, t01, 0x05040100u) ^ 0x80808080u;  // low
+            ones[rb][0] = __builtin_amdgcn_sdot4((int)w2, 0x01010101, ones[rb][0], false);
+            ones[rb][1] = __builtin_amdgcn_sdot4((int)w1, 0x01010101, ones[rb][1], false);
+            ones[rb][2] = __builtin_amdgcn_sdot4((int)w0, 0x01010101, ones[rb][2], false);
             LDS_AS uint32_t* pw = (LDS_AS uint32_t*)(P + (16 * rb + 4 * g) * PST + 4 * c);
-            pw[0] = pk0;
-            pw[PST / 4] = pk1;
-            pw[2 * PST / 4] = pk2;
+            pw[0] = w2;
+            pw[PST / 4] = w1;
+            pw[2 * PST / 4] = w0;
             pw[3 * PST / 4] = 0u;  // digit row 3 multiplies nothing
         }
         asm volatile("" ::: "memory");  // the operand reads below follow this wave's writes
@@ -553,48 +549,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) Ap[rb] = *(const LDS_AS v4i*)(P + (16 * rb + c) * PST + 16 * g);
 
-        // ---------------- values: every column block over the 64 tokens.  The block's width
-        // is uniform: shift counts and mask follow from it with scalar ops.
-        const LDS_AS uint32_t* vw = cur + 64 * WK;
+        // ---------------- values: column c of block cb = one field; its B operand is the
+        // lane's 16 tokens of the field's byte plane under the field mask
 #pragma unroll
         for (int cb = 0; cb < NVB; ++cb) {
-            int mode = cb < nvb4 ? 0 : (cb < nvb4 + nvb2 ? 1 : 2);  // 4-, 2-, 1-bit pieces
-            asm volatile("" : "+s"(mode));
-            const uint32_t wbits = 4u >> mode;
-            const uint32_t M = 0x01010101u * ((1u << wbits) - 1u);
-            const uint32_t s2 = mode == 0 ? 0u : 2u * wbits, s3 = mode == 0 ? 4u : 3u * wbits;
-            const uint32_t wi = (vofs[cb >> 1] >> (16 * (cb & 1))) & 0xFFFFu;
-            const uint32_t x0 = vw[wi], x1 = vw[wi + 1];
-            const uint32_t base = x0 >> (mode == 2 ? pre1 : 0u);
-            const uint32_t hi = mode == 0 ? x1 : base;
-            const v4i B = v4i{(int)(base & M), (int)((base >> wbits) & M), (int)((hi >> s2) & M), (int)((hi >> s3) & M)};
+            const u32x4 x = *(const LDS_AS u32x4*)(curb + voff[cb]);
+            const v4i B = v4i{(int)(x[0] & vmask[cb]), (int)(x[1] & vmask[cb]), (int)(x[2] & vmask[cb]),
+                              (int)(x[3] & vmask[cb])};
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
                 acc_i[rb][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ap[rb], B, acc_i[rb][cb], 0, 0, 0);
         }
     }
 
-    // ---------------- epilogue: the four waves' results meet in LDS (ring reused)
+    // ---------------- epilogue: the four waves' results meet in LDS (ring reused).  Per
+    // wave and head: reference max, sum, the probability digit sum (x 2^16 / 127 = 2^16 sum
+    // of p), and per value column the accumulator / 127 (= sum of p x stored byte).
     wait_all();
     lds_barrier();
     const int ld = D + 2;
-    const int ncol = 16 * nvb;
+    const int ncol = 16 * NVB;
     LDS_AS float* wm = (LDS_AS float*)sm;                 // [4 waves][RB*4 heads] reference maxima
     LDS_AS float* wl = wm + kWaves * RB * 4;              // [4 waves][RB*4 heads] sums
-    LDS_AS float* wa = wl + kWaves * RB * 4;              // [4 waves][RB*4 heads][16 NVB] accumulators
+    LDS_AS float* wo = wl + kWaves * RB * 4;              // [4 waves][RB*4 heads] 128 x digit sums / 127
+    LDS_AS float* wa = wo + kWaves * RB * 4;              // [4 waves][RB*4 heads][ncol] columns
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const float ls = row16_sum(lsum[rb]);
+        const float os = row16_sum(combine256(ones[rb][0], ones[rb][1], ones[rb][2]));
         if (c == 0) {
             wm[w * RB * 4 + 4 * rb + g] = mref[rb];
             wl[w * RB * 4 + 4 * rb + g] = ls;
+            wo[w * RB * 4 + 4 * rb + g] = os * (128.0f / 127.0f);
         }
 #pragma unroll
         for (int cb = 0; cb < NVB; ++cb)
             if (cb < nvb)
-                wa[(w * RB * 4 + 4 * rb + g) * 16 * NVB + 16 * cb + c] =
-                    ((float)acc_i[rb][cb][0] + (float)acc_i[rb][cb][1] * kDig1 + (float)acc_i[rb][cb][2] * kDig2) *
-                    (1.0f / 127.0f);
+                wa[(w * RB * 4 + 4 * rb + g) * ncol + 16 * cb + c] =
+                    combine256(acc_i[rb][cb][0], acc_i[rb][cb][1], acc_i[rb][cb][2]) * (1.0f / 127.0f);
     }
     lds_barrier();
     const int W = a.wg_per_head, NG = a.n_grp;
@@ -620,22 +612,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
 #pragma unroll
             for (int ww = 0; ww < kWaves; ++ww) v += e[ww] * wl[ww * RB * 4 + hh];
         } else {
+            // channel jj: its fields' columns, each (column + 128 flip sum p) 2^(shift - pos)
             const int jj = col - 2;
             v = 0.0f;
+            for (int f = H.vch_first[jj]; f < H.vch_first[jj + 1]; ++f) {
+                const uint32_t en = H.vch_col[f];
+                const int cc = en & 511;
+                const float sc = __builtin_amdgcn_ldexpf(1.0f, (int)((en >> 9) & 15) - 8);
+                const bool top = (en >> 13) & 1;
+                float x = 0.0f;
 #pragma unroll
-            for (int tt = 0; tt < 3; ++tt) {
-                const int en = H.chan_cols[jj][tt];
-                if (en >= 0) {
-                    float x = 0.0f;
-#pragma unroll
-                    for (int ww = 0; ww < kWaves; ++ww) x += e[ww] * wa[(ww * RB * 4 + hh) * 16 * NVB + (en & 0xfff)];
-                    v += (float)(1 << (en >> 12)) * x;
-                }
+                for (int ww = 0; ww < kWaves; ++ww)
+                    x += e[ww] * (wa[(ww * RB * 4 + hh) * ncol + cc] + (top ? wo[ww * RB * 4 + hh] : 0.0f));
+                v = fmaf(sc, x, v);
             }
         }
         st_dev(pout + i, v);
     }
-    (void)ncol;
     wait_vm(0);     // this wave's partial stores have completed
     lds_barrier();  // ... and every wave's
     const int members1 = min(grp_size, W - grp * grp_size);
@@ -716,7 +709,9 @@ struct Variant {
 };
 // compile-time (row blocks, score operand blocks, value column blocks) bounds available;
 // (the operand blocks of a head must fit the bounds; unused blocks multiply zero)
-constexpr Variant kVariants[] = {{1, 3, 8}, {1, 3, 12}, {1, 4, 12}, {1, 4, 16}, {1, 5, 12}, {1, 5, 16}, {1, 6, 16}, {1, 6, 24}, {1, 8, 24}, {1, 8, 32}, {1, 16, 32}, {2, 3, 12}, {2, 4, 12}, {2, 4, 16}, {2, 6, 24}, {2, 8, 32}, {2, 16, 32}, {3, 4, 16}, {3, 8, 32}, {3, 16, 32}, {4, 4, 16}, {4, 8, 32}, {4, 16, 32}};
+constexpr Variant kVariants[] = {{1, 2, 4},  {1, 2, 8},  {1, 3, 8},  {1, 3, 10}, {1, 4, 12}, {1, 6, 16},
+                                 {1, 8, 24}, {1, 16, 24}, {2, 2, 8},  {2, 3, 10}, {2, 4, 12}, {2, 8, 24},
+                                 {2, 16, 24}, {3, 4, 12}, {3, 16, 24}, {4, 4, 12}, {4, 16, 24}};
 
 struct Plan {
     Variant v;
@@ -739,7 +734,7 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     for (int h = 0; h < cb->n_kv; ++h) {
         const DevHead& D = cb->blob[(size_t)layer * cb->n_kv + h];
         p.nqm_max = std::max(p.nqm_max, D.nqm);
-        p.nvb_max = std::max(p.nvb_max, D.nvb[0] + D.nvb[1] + D.nvb[2]);
+        p.nvb_max = std::max(p.nvb_max, D.nvb);
     }
     bool found = false;
     for (const Variant& v : kVariants)
@@ -773,14 +768,14 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     a.tpg = p.tpg;
     a.wg_per_head = p.wg_per_head;
     a.n_grp = p.n_grp;
-    a.buf_bytes = (int)al16(a.tile_bytes + 16);  // (+16: the value unpack may read one word past the tile)
+    a.buf_bytes = (int)al16(a.tile_bytes);
     // the probability operand (RB KiB) overwrites the tile's key block (8 B_K bytes)
     int bk_min = 1 << 30;
     for (int h = 0; h < cb->n_kv; ++h) bk_min = std::min(bk_min, cb->blob[(size_t)layer * cb->n_kv + h].BK);
     if (RB * 1024 > 8 * bk_min)
         return set_error(AATC_ERR_UNSUPPORTED, "%d key bits per token are too few for %d query heads", bk_min, G);
     // the epilogue and the merges reuse the buffers
-    const size_t epi = ((size_t)2 * kWaves * RB * 4 + (size_t)kWaves * RB * 4 * 16 * p.v.nvb) * sizeof(float);
+    const size_t epi = ((size_t)3 * kWaves * RB * 4 + (size_t)kWaves * RB * 4 * 16 * p.v.nvb) * sizeof(float);
     const size_t mrg = ((size_t)G * d + (size_t)PARTS * G * d) * sizeof(float);
     // ring depth: the deepest that the workgroups resident per CU (set by registers) leave
     // room for, between 2 and 4 buffers per wave
@@ -940,29 +935,23 @@ extern "C" int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob
                                                                 qsc, part1, part2, cnt1, cnt2, out)                \
                            : launch_decode<rb_, nqm_, nvb_, 128>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, qa, \
                                                                  qsc, part1, part2, cnt1, cnt2, out);
+    AATC_DECODE_CASE(1, 2, 4)
+    AATC_DECODE_CASE(1, 2, 8)
     AATC_DECODE_CASE(1, 3, 8)
-    AATC_DECODE_CASE(1, 3, 12)
+    AATC_DECODE_CASE(1, 3, 10)
     AATC_DECODE_CASE(1, 4, 12)
-    AATC_DECODE_CASE(1, 4, 16)
-    AATC_DECODE_CASE(1, 5, 12)
-    AATC_DECODE_CASE(1, 5, 16)
     AATC_DECODE_CASE(1, 6, 16)
-    AATC_DECODE_CASE(1, 6, 24)
     AATC_DECODE_CASE(1, 8, 24)
-    AATC_DECODE_CASE(1, 8, 32)
-    AATC_DECODE_CASE(1, 16, 32)
-    AATC_DECODE_CASE(2, 3, 12)
+    AATC_DECODE_CASE(1, 16, 24)
+    AATC_DECODE_CASE(2, 2, 8)
+    AATC_DECODE_CASE(2, 3, 10)
     AATC_DECODE_CASE(2, 4, 12)
-    AATC_DECODE_CASE(2, 4, 16)
-    AATC_DECODE_CASE(2, 6, 24)
-    AATC_DECODE_CASE(2, 8, 32)
-    AATC_DECODE_CASE(2, 16, 32)
-    AATC_DECODE_CASE(3, 4, 16)
-    AATC_DECODE_CASE(3, 8, 32)
-    AATC_DECODE_CASE(3, 16, 32)
-    AATC_DECODE_CASE(4, 4, 16)
-    AATC_DECODE_CASE(4, 8, 32)
-    AATC_DECODE_CASE(4, 16, 32)
+    AATC_DECODE_CASE(2, 8, 24)
+    AATC_DECODE_CASE(2, 16, 24)
+    AATC_DECODE_CASE(3, 4, 12)
+    AATC_DECODE_CASE(3, 16, 24)
+    AATC_DECODE_CASE(4, 4, 12)
+    AATC_DECODE_CASE(4, 16, 24)
 #undef AATC_DECODE_CASE
     return set_error(AATC_ERR_UNSUPPORTED, "decode variant missing");
 }

@@ -39,17 +39,18 @@ __device__ __forceinline__ uint32_t quantize(float c, float inv, int b) {
     return (uint32_t)v;
 }
 
-// OR a field of `w` bits (w <= 8) at bit position `pos` of an LDS word array.
-__device__ __forceinline__ void lds_put(uint32_t* words, uint32_t pos, uint32_t val, int w) {
-    uint32_t wi = pos >> 5, sh = pos & 31;
-    atomicOr(&words[wi], val << sh);
-    if (sh + w > 32) atomicOr(&words[wi + 1], val >> (32 - sh));
-}
-
-__device__ __forceinline__ uint32_t lds_get(const uint32_t* words, uint32_t pos, int w) {
-    uint32_t wi = pos >> 5, sh = pos & 31;
-    uint64_t two = (uint64_t)words[wi] | ((sh + w > 32) ? ((uint64_t)words[wi + 1] << 32) : 0ull);
-    return (uint32_t)(two >> sh) & ((1u << w) - 1u);
+// Bytes of tile word i that belong to slots in [s0, s1): a key-block word (i < nkw) is
+// one slot's (slot i % 64); a value-block word holds slots 4 (i % 16) + b in byte b.
+__device__ __forceinline__ uint32_t written_mask(int i, int nkw, int s0, int s1) {
+    if (i < nkw) {
+        const int s = i & 63;
+        return s >= s0 && s < s1 ? 0xFFFFFFFFu : 0u;
+    }
+    const int sb = 4 * ((i - nkw) & 15);
+    uint32_t m = 0u;
+    for (int b = 0; b < 4; ++b)
+        if (sb + b >= s0 && sb + b < s1) m |= 0xFFu << (8 * b);
+    return m;
 }
 
 // ------------------------------------------------------------------------------------
@@ -80,13 +81,11 @@ __global__ __launch_bounds__(256) void encode_kernel(const DevHead* __restrict__
     const int seq = sa.seq[zi];
     uint8_t* tp = cache + ((((int64_t)layer * n_seqs_cache + seq) * n_kv + h) * n_tiles_cap + tile) * (int64_t)tile_bytes;
     uint32_t* tw = (uint32_t*)tp;
-    // key-block word i belongs to slot i % 64; the records of the slots written here are
-    // rebuilt from zero (the stored key bytes carry bit 7 inverted)
+    // The records of the slots written here are rebuilt from zero (their stored bytes carry
+    // bit 7 inverted): key-block word i belongs to slot i % 64; value-block word i holds
+    // byte plane (i / 16), slots 4 (i % 16) .. 4 (i % 16) + 3.
     const int nkw = 2 * BK;  // 64 slots * BK / 32 words
-    for (int i = threadIdx.x; i < nw; i += blockDim.x) {
-        const int s = i & 63;
-        words[i] = (i < nkw && s >= s0 && s < s1) ? 0u : tw[i];
-    }
+    for (int i = threadIdx.x; i < nw; i += blockDim.x) words[i] = tw[i] & ~written_mask(i, nkw, s0, s1);
     // codes of the slots being written
     for (int i = threadIdx.x; i < (s1 - s0) * 2 * d; i += blockDim.x) {
         int s = s0 + i / (2 * d);
@@ -108,31 +107,25 @@ __global__ __launch_bounds__(256) void encode_kernel(const DevHead* __restrict__
         codes[(s * 2 + kv) * d + j] = b ? (uint8_t)quantize(c, kv ? H.invV[j] : H.invK[j], b) : 0;
     }
     __syncthreads();
-    // quantize + pack: one (slot, piece) per thread iteration
-    const int nKp = H.nKp, nVp = H.nVp;
-    const int np = nKp + nVp;
-    for (int i = threadIdx.x; i < (s1 - s0) * np; i += blockDim.x) {
-        int s = s0 + i / np;
-        int p = i % np;
-        bool isK = p < nKp;
-        int pw = isK ? H.pieceK[p] : H.pieceV[p - nKp];
-        int chan = pw & 0xff, w = (pw >> 8) & 0xf, e = (pw >> 12) & 0xf, off = pw >> 16;
-        uint32_t code = codes[(s * 2 + (isK ? 0 : 1)) * d + chan];
-        uint32_t val = (code >> e) & ((1u << w) - 1u);
-        uint32_t pos;
-        if (isK) {  // record word r of slot s is block word 64 r + s
-            pos = 32u * (64u * (uint32_t)(off >> 5) + (uint32_t)s) + (uint32_t)(off & 31);
-        } else {
-            int per = 32 / w, r = s / per, k = s % per;
-            pos = 64u * BK + 64u * off + 32u * r + 8u * (k & 3) + (uint32_t)w * (k >> 2);
-        }
-        lds_put(words, pos, val, w);
+    // pack: one (slot, field) per thread iteration; fields never cross a byte
+    const int nfK = H.nfK, nfV = H.nfV;
+    const int nf = nfK + nfV;
+    for (int i = threadIdx.x; i < (s1 - s0) * nf; i += blockDim.x) {
+        const int s = s0 + i / nf;
+        const int f = i % nf;
+        const bool isK = f < nfK;
+        const uint32_t fw = isK ? H.fieldK[f] : H.fieldV[f - nfK];
+        const int chan = fw & 0xff, w = (fw >> 8) & 0xf, e = (fw >> 12) & 0xf, pos = (fw >> 16) & 0xf;
+        const uint32_t q = fw >> 20;
+        const uint32_t code = codes[(s * 2 + (isK ? 0 : 1)) * d + chan];
+        const uint32_t val = (code >> e) & ((1u << w) - 1u);
+        // key record word q/4 of slot s is block word 64 (q/4) + s; value record byte q of
+        // slot s is value-block byte 64 q + s
+        const uint32_t byte = isK ? 4u * (64u * (q >> 2) + (uint32_t)s) + (q & 3u) : 8u * BK + 64u * q + (uint32_t)s;
+        atomicOr(&words[byte >> 2], val << (8u * (byte & 3u) + (uint32_t)pos));
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < nw; i += blockDim.x) {
-        const int s = i & 63;
-        tw[i] = (i < nkw && s >= s0 && s < s1) ? words[i] ^ 0x80808080u : words[i];
-    }
+    for (int i = threadIdx.x; i < nw; i += blockDim.x) tw[i] = words[i] ^ (written_mask(i, nkw, s0, s1) & 0x80808080u);
 }
 
 __global__ void flush_kernel(uint4* p, size_t n) {

@@ -25,6 +25,6 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_versions_and_status_strings():
-    assert q.version() == 1 and q.layout_version() == 1
+    assert q.version() == 1 and q.layout_version() == 2
     assert q.status_string(0) == "ok"
     assert q.status_string(-6) == "capacity"

@@ -89,9 +89,10 @@ def test_codebook_create_and_persist(tmp_path):
 def test_error_paths():
     w, ref = _oracle_codebook()
     st = oracle.head_stats(*[x.astype(np.float64) for x in _samples("tiny")[1:]])
-    with pytest.raises(q.AatcError) as e:  # 2*d*avg_bits not an even integer
-        q.calibrate([st], 64, 1, 1, 4, 2.7)
-    assert e.value.status == -3
+    for avg in (2.7, 324 / 128):  # 2*d*avg_bits not an integer; an integer, not a multiple of 8
+        with pytest.raises(q.AatcError) as e:
+            q.calibrate([st], 64, 1, 1, 4, avg)
+        assert e.value.status == -3
     with pytest.raises(q.AatcError) as e:
         q.calibrate([st], 96, 1, 1, 4, 3.0)
     assert e.value.status == -1
@@ -127,3 +128,29 @@ def test_multi_head_codebook_geometry():
     assert cb.n_layers == 2 and cb.n_kv == 2 and cb.n_heads == 4
     assert cb.cache_bytes(2, 3, 100) == 2 * 3 * 2 * 2 * 3072
     assert cb.device_bytes() > 0
+
+
+def test_record_fields_match_the_oracle_placement():
+    """The library's field placement (what the encoder and decoder use) equals the
+    oracle's, for calibrated heads and for random bit vectors."""
+    w, ref = _oracle_codebook()
+    for seed in range(30):
+        rng = np.random.default_rng(100 + seed)
+        d = 64 if seed % 2 else 128
+        bK = rng.integers(0, 9, d)
+        bV = rng.integers(0, 9, d)
+        while bK.sum() % 32:
+            bK[rng.choice(np.flatnonzero(bK))] -= 1
+        while (bK.sum() + bV.sum()) % 8:
+            bV[rng.choice(np.flatnonzero(bV))] -= 1
+        U = np.eye(d)[None]
+        mu = np.zeros((1, d))
+        step = lambda b: np.where(b > 0, 0.1, 0.0).astype(np.float32)[None]
+        cb = q.codebook_create(d, 1, 1, 1, U, U, mu, mu, bK[None].astype(np.int32), bV[None].astype(np.int32),
+                               step(bK), step(bV))
+        assert cb.fields(0, 0) == oracle.fields(bK)
+        assert cb.fields(0, 1) == oracle.fields(bV)
+    cbl = q.codebook_create(ref.d, 1, 1, 4, ref.UK[None], ref.UV[None], ref.muK[None], ref.muV[None],
+                            ref.bK[None].astype(np.int32), ref.bV[None].astype(np.int32), ref.stepK[None],
+                            ref.stepV[None])
+    assert cbl.fields(0, 0) == oracle.fields(ref.bK) and cbl.fields(0, 1) == oracle.fields(ref.bV)
