@@ -76,6 +76,8 @@ struct alignas(256) DevHead {
     int16_t kq_word[kMaxQM][4][4];
     uint32_t kq_mask[kMaxQM][4][4];
     uint16_t kq_slot[kMaxQM][4][16];
+    // per key channel: the largest slot weight 2^(shift - pos) of its fields (0 if uncoded)
+    float kq_fmax[kMaxD];
     // Value MFMAs: column c of block cb is value field 16 cb + c (fieldV order): the byte
     // plane of its record byte (value-block offset 64 * byte) and its mask within the
     // byte; padding columns have plane 0 and mask 0.

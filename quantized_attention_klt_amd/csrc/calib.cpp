@@ -370,6 +370,8 @@ static int build_decode_schedule(const HeadCB& H, DevHead& D) {
         D.kq_mask[m][g][i] = dws[k].mask;
         for (int b = 0; b < 4; ++b) D.kq_slot[m][g][4 * i + b] = dws[k].slot[b];
     }
+    for (int j = 0; j < kMaxD; ++j) D.kq_fmax[j] = 0.0f;
+    for (const Field& f : H.fK) D.kq_fmax[f.chan] = std::max(D.kq_fmax[f.chan], std::ldexp(1.0f, f.shift - f.pos));
     // value columns
     const int nf = (int)H.fV.size();
     D.nvb = std::max((nf + 15) / 16, 1);
