@@ -568,88 +568,87 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
 // relative to the partial's reference max), then per channel j
 //   A_j = sum over its fields of 2^(shift - pos) (column + [field ends at bit 7] top sum)
 // (the stored byte of a field at bit pos is field 2^pos, minus 128 at the top of a byte)
-// and o = obias + U_V (step * A / L).
+// and o = obias + U_V (step * A / L).  Every global read is issued in one round.
 // ---------------------------------------------------------------------------------------
+constexpr int kMergeCols = 3;     // value columns per thread (16 kMaxVB <= 3 D for D >= 128)
+constexpr int kMergeRound = 16;   // partials per thread and column
+
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DevHead* __restrict__ blob, int layer, int n_kv,
                                                               int G, int W, int PL, const float* __restrict__ part,
                                                               float* __restrict__ out) {
     constexpr int SL = kMergeThreads / D;  // slices (of partials, then of U_V rows) per column
     constexpr int ROWS = D / SL;
-    constexpr int CH = 16;                 // partials per slice and load round
-    __shared__ float ew[1024];             // per partial: weight 2^(m - M) (W <= 1024)
+    constexpr int NW = kMergeThreads / 64;
+    __shared__ float ew[kMergeThreads];    // per partial: reference max, then weight 2^(m - M)
+    __shared__ float wred[3][NW];          // per wave: max, sum, top sum
     __shared__ float red[SL][D];           // slice sums
     __shared__ float colv[16 * aatc::kMaxVB];  // merged columns
     __shared__ float cbar[D];              // step * A / L
-    __shared__ float ml[4];                // M, L, top sum
     const int h = blockIdx.x, z = blockIdx.y, hh = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t zh = (int64_t)z * n_kv + h;
     const DevHead& H = blob[layer * n_kv + h];
-    const float* P = part + (zh * W * G + hh) * PL;  // partial w at P + w * G * PL
-    const int64_t PS = (int64_t)G * PL;
-    // U_V slice of this thread (in flight with the partial loads)
+    const int64_t PS = (int64_t)G * PL;              // floats between partials
+    const float* P = part + (zh * W * G + hh) * PL;  // partial w at P + w * PS
     const int ii = tid % D, sl = tid / D;
+    const int ncol = 16 * H.nvb;
+    // U_V slice, this thread's columns ii + D k of partials sl + SL r, and partial tid's
+    // (max, sum, top sum)
     float uv[ROWS];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) uv[r] = H.UVt[(sl * ROWS + r) * D + ii];  // UVt[j * d + i] = U_V[i][j]
-    // reference maxima, weights, sum and top-field sum (wave 0)
-    if (wv == 0) {
-        float M = -INFINITY;
-        for (int wgi = lane; wgi < W; wgi += 64) M = fmaxf(M, P[wgi * PS]);
-        M = wave_max(M);
-        float L = 0.0f, O = 0.0f;
-        for (int wgi = lane; wgi < W; wgi += 64) {
-            const float m = P[wgi * PS];
-            const float e = m == -INFINITY ? 0.0f : exp2f(m - M);
-            ew[wgi] = e;
-            L = fmaf(e, P[wgi * PS + 1], L);
-            O = fmaf(e, P[wgi * PS + 2], O);
+    float x[kMergeCols][kMergeRound];
+#pragma unroll
+    for (int k = 0; k < kMergeCols; ++k)
+#pragma unroll
+        for (int r = 0; r < kMergeRound; ++r) {
+            const int cc = ii + D * k, wgi = sl + SL * r;
+            x[k][r] = cc < ncol && wgi < W ? P[wgi * PS + kPartHead + cc] : 0.0f;
         }
-        L = wave_sum(L);
-        O = wave_sum(O);
-        if (lane == 0) ml[0] = M, ml[1] = L, ml[2] = O;
-    }
+    const bool mine = tid < W;
+    const float m_t = mine ? P[tid * PS] : -INFINITY;
+    const float l_t = mine ? P[tid * PS + 1] : 0.0f;
+    const float o_t = mine ? P[tid * PS + 2] : 0.0f;
+    float mx = wave_max(m_t);
+    if (lane == 0) wred[0][wv] = mx;
     __syncthreads();
-    // columns: thread (column c0 + ii, slice sl) sums partials sl, sl + SL, ...
-    const int ncol = 16 * H.nvb;
-    for (int c0 = 0; c0 < ncol; c0 += D) {
-        const int cc = c0 + ii;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) M = fmaxf(M, wred[0][k]);
+    const float e_t = m_t == -INFINITY ? 0.0f : exp2f(m_t - M);
+    const float ls = wave_sum(e_t * l_t), os = wave_sum(e_t * o_t);
+    ew[tid] = e_t;
+    if (lane == 0) wred[1][wv] = ls, wred[2][wv] = os;
+    __syncthreads();
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) L += wred[1][k], O += wred[2][k];
+    // columns: slice sums of the weighted partials, slices meet in LDS
+#pragma unroll
+    for (int k = 0; k < kMergeCols; ++k) {
+        if (D * k >= ncol) break;
         float acc = 0.0f;
-        if (cc < ncol) {
-            for (int w0 = sl; w0 < W; w0 += SL * CH) {
-                float x[CH];
 #pragma unroll
-                for (int k = 0; k < CH; ++k) {
-                    const int wgi = w0 + SL * k;
-                    x[k] = wgi < W ? P[wgi * PS + kPartHead + cc] : 0.0f;
-                }
-#pragma unroll
-                for (int k = 0; k < CH; ++k) {
-                    const int wgi = w0 + SL * k;
-                    if (wgi < W) acc = fmaf(ew[wgi], x[k], acc);
-                }
-            }
-        }
+        for (int r = 0; r < kMergeRound; ++r) acc = fmaf(ew[min(sl + SL * r, kMergeThreads - 1)], x[k][r], acc);
         red[sl][ii] = acc;
         __syncthreads();
-        if (sl == 0 && cc < ncol) {
+        if (sl == 0 && ii + D * k < ncol) {
             float v = 0.0f;
 #pragma unroll
             for (int s2 = 0; s2 < SL; ++s2) v += red[s2][ii];
-            colv[cc] = v;
+            colv[ii + D * k] = v;
         }
         __syncthreads();
     }
     // value coefficients, dequantisation step and 1 / L
     if (tid < D) {
         const int j = tid;
-        const float L = ml[1], O = ml[2];
         float A = 0.0f;
         for (int f = H.vch_first[j]; f < H.vch_first[j + 1]; ++f) {
             const uint32_t en = H.vch_col[f];
-            const float x = colv[en & 511] + (((en >> 13) & 1) ? O : 0.0f);
-            A = fmaf(__builtin_amdgcn_ldexpf(1.0f, (int)((en >> 9) & 15) - 8), x, A);
+            const float v = colv[en & 511] + (((en >> 13) & 1) ? O : 0.0f);
+            A = fmaf(__builtin_amdgcn_ldexpf(1.0f, (int)((en >> 9) & 15) - 8), v, A);
         }
         cbar[j] = H.bitsV[j] && L > 0.0f ? H.stepV[j] * A / L : 0.0f;
     }
@@ -664,7 +663,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DevHead* __r
         float o = 0.0f;
 #pragma unroll
         for (int s2 = 0; s2 < SL; ++s2) o += red[s2][tid];
-        out[(zh * G + hh) * D + tid] = ml[1] > 0.0f ? H.obias[tid] + o : H.muV[tid];
+        out[(zh * G + hh) * D + tid] = L > 0.0f ? H.obias[tid] + o : H.muV[tid];
     }
 }
 
@@ -710,6 +709,9 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     if (!found)
         return set_error(AATC_ERR_UNSUPPORTED, "no decode variant for %d query heads, %d score MFMAs and %d value blocks", G,
                          p.nqm_max, p.nvb_max);
+    if (16 * p.nvb_max > kMergeCols * d)
+        return set_error(AATC_ERR_UNSUPPORTED, "%d value fields per token exceed the merge's %d columns", 16 * p.nvb_max,
+                         kMergeCols * d);
     const int64_t tiles = n_tiles_of(max_len);
     DecodeArgs& a = p.args;
     a.G = G;
@@ -741,11 +743,11 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     if (p.lds > 160 * 1024 - 256)
         return set_error(AATC_ERR_UNSUPPORTED, "decode needs %zu bytes of LDS per workgroup", p.lds);
     // workgroups per (sequence, kv-head): every resident workgroup slot of the chip busy,
-    // at least one tile per wave, at most 1024 partials per head
+    // at least one tile per wave, at most what one merge round reads
     const int64_t pairs = (int64_t)cb->n_kv * n_seqs;
     const int64_t slots = 256 * (int64_t)p.wgs_per_cu;
     p.wg_per_head = (int)std::max<int64_t>(
-        1, std::min<int64_t>({slots / pairs, (tiles + kWaves - 1) / kWaves, (int64_t)1024}));
+        1, std::min<int64_t>({slots / pairs, (tiles + kWaves - 1) / kWaves, (int64_t)(kMergeThreads / d) * kMergeRound}));
     a.wg_per_head = p.wg_per_head;
     a.part_ld = kPartHead + 16 * p.v.nvb;
     p.part_bytes = (size_t)n_seqs * cb->n_kv * p.wg_per_head * G * a.part_ld * sizeof(float);
