@@ -48,10 +48,12 @@ struct alignas(256) DevHead {
     float UK[kMaxD * kMaxD];      // fp32 basis (query transform)
     float UV[kMaxD * kMaxD];      // fp32 basis (inverse transform of values)
     float UVt[kMaxD * kMaxD];     // its transpose, UVt[j*d + i] = UV[i*d + j]
-    uint16_t UKhi[kMaxD * kMaxD]; // bf16 split of U_K: U = hi + lo (+ rounding)
-    uint16_t UKlo[kMaxD * kMaxD];
-    uint16_t UVhi[kMaxD * kMaxD];
-    uint16_t UVlo[kMaxD * kMaxD];
+    // bf16 split of the bases, channel-major: UKt_hi[j*d + i] + UKt_lo[j*d + i] = U_K[i][j]
+    // (+ rounding), the MFMA operand order (16 consecutive bytes along i)
+    uint16_t UKt_hi[kMaxD * kMaxD];
+    uint16_t UKt_lo[kMaxD * kMaxD];
+    uint16_t UVt_hi[kMaxD * kMaxD];
+    uint16_t UVt_lo[kMaxD * kMaxD];
     float muV[kMaxD];
     float obias[kMaxD];           // mu_V - U_V (step_V * (2^(b-1) - 1/2)): output of all-zero codes
     float biasK[kMaxD];           // mu_K (U_hi + U_lo), fp64 sum rounded once
@@ -83,11 +85,9 @@ struct alignas(256) DevHead {
     // byte; padding columns have plane 0 and mask 0.
     uint16_t vb_plane[kMaxVB][16];
     uint8_t vb_mask[kMaxVB][16];
-    // Value channel j: columns vch_col[vch_first[j] .. vch_first[j + 1]), each
-    // col | (shift - pos + 8) << 9 | flip << 13.
-    int16_t vch_first[kMaxD + 1];
-    int16_t pad2[7];
-    uint16_t vch_col[kMaxFields];
+    // Value channel j: the columns of its fields (at most 8: a field has at least one bit),
+    // each col | (shift - pos + 8) << 9 | flip << 13, unused entries 0xFFFF.
+    uint16_t vch[kMaxD][8];
 };
 
 }  // namespace aatc

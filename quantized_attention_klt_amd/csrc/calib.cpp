@@ -383,16 +383,15 @@ static int build_decode_schedule(const HeadCB& H, DevHead& D) {
         D.vb_plane[i / 16][i % 16] = (uint16_t)(64 * f.byte);
         D.vb_mask[i / 16][i % 16] = (uint8_t)(((1u << f.width) - 1u) << f.pos);
     }
-    int n = 0;
-    for (int j = 0; j <= kMaxD; ++j) {
-        D.vch_first[j] = (int16_t)n;
-        if (j == kMaxD || j >= (int)H.bV.size()) continue;
-        for (int i = 0; i < nf; ++i) {
-            const Field& f = H.fV[i];
-            if (f.chan != j) continue;
-            const int flip = f.pos + f.width == 8 ? 1 : 0;
-            D.vch_col[n++] = (uint16_t)(i | ((f.shift - f.pos + 8) << 9) | (flip << 13));
-        }
+    for (int j = 0; j < kMaxD; ++j)
+        for (int k = 0; k < 8; ++k) D.vch[j][k] = 0xFFFF;
+    for (int i = 0; i < nf; ++i) {
+        const Field& f = H.fV[i];
+        int k = 0;
+        while (k < 8 && D.vch[f.chan][k] != 0xFFFF) ++k;
+        if (k == 8) return AATC_ERR_UNSUPPORTED;
+        const int flip = f.pos + f.width == 8 ? 1 : 0;
+        D.vch[f.chan][k] = (uint16_t)(i | ((f.shift - f.pos + 8) << 9) | (flip << 13));
     }
     return AATC_OK;
 }
@@ -437,19 +436,20 @@ int finalize(aatc_codebook* cb) {
             const std::vector<double>& U = which ? H.UV : H.UK;
             const std::vector<double>& mu = which ? H.muV : H.muK;
             float* U32 = which ? D.UV : D.UK;
-            uint16_t* hi = which ? D.UVhi : D.UKhi;
-            uint16_t* lo = which ? D.UVlo : D.UKlo;
+            uint16_t* hi = which ? D.UVt_hi : D.UKt_hi;  // [j * d + i]
+            uint16_t* lo = which ? D.UVt_lo : D.UKt_lo;
             float* bias = which ? D.biasV : D.biasK;
-            for (int i = 0; i < d * d; ++i) {
-                float u = (float)U[i];
-                U32[i] = u;
-                hi[i] = f32_to_bf16(u);
-                lo[i] = f32_to_bf16(u - bf16_to_f32(hi[i]));
-            }
+            for (int i = 0; i < d; ++i)
+                for (int j = 0; j < d; ++j) {
+                    const float u = (float)U[(size_t)i * d + j];
+                    U32[i * d + j] = u;
+                    hi[j * d + i] = f32_to_bf16(u);
+                    lo[j * d + i] = f32_to_bf16(u - bf16_to_f32(hi[j * d + i]));
+                }
             for (int j = 0; j < d; ++j) {
                 double s = 0.0;
                 for (int i = 0; i < d; ++i)
-                    s += mu[i] * ((double)bf16_to_f32(hi[i * d + j]) + (double)bf16_to_f32(lo[i * d + j]));
+                    s += mu[i] * ((double)bf16_to_f32(hi[j * d + i]) + (double)bf16_to_f32(lo[j * d + i]));
                 bias[j] = (float)s;
             }
         }

@@ -37,6 +37,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstddef>
 #include <mutex>
 #include <vector>
 
@@ -166,15 +167,10 @@ constexpr int waves_for(int rb, int nqm, int nvb) {
     return vgpr_estimate(rb, nqm, nvb) <= 128 ? 4 : (vgpr_estimate(rb, nqm, nvb) <= 168 ? 3 : 2);
 }
 
-// bytes of the prologue's LDS scratch: query / q'' [4 RB][D]; the other row slices'
-// partial sums [PARTS - 1][4 RB][D], later the staged operands [NQM][RB][64 lanes][16 B];
-// slots [NQM * 64]; per-head maxima [16]; per-row corrections [RB * 16]
-constexpr size_t scratch_ps_bytes(int rb, int nqm, int d) {
-    return (size_t)(256 / d - 1) * 4 * rb * d * 4 > (size_t)nqm * rb * 1024 ? (size_t)(256 / d - 1) * 4 * rb * d * 4
-                                                                              : (size_t)nqm * rb * 1024;
-}
+// bytes of the prologue's LDS scratch: q'' [4 RB][D]; staged operands [NQM][RB][64 lanes]
+// [16 B]; slots [NQM * 64]; per-wave head maxima [4][16]; per-row corrections [RB * 16]
 constexpr size_t scratch_bytes(int rb, int nqm, int d) {
-    return (size_t)4 * rb * d * 4 + scratch_ps_bytes(rb, nqm, d) + (size_t)nqm * 128 + 64 + (size_t)rb * 64;
+    return (size_t)4 * rb * d * 4 + (size_t)nqm * rb * 1024 + (size_t)nqm * 128 + 256 + (size_t)rb * 64;
 }
 
 template <int RB, int NQM, int NVB, int D>
@@ -210,105 +206,101 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
     LDS_AS uint8_t* ring = sm + w * BB;
     const int RS = kWaves * BB;  // bytes between a wave's ring slots
     int64_t t = (int64_t)wgi * kWaves + w;
-    if (a.early)  // the first tiles stream during the prologue (its scratch is in the last slot)
-        for (int k = 0; k < NBW - 1 && t + stride * k < n_tiles; ++k)
-            load_tile(tiles + (t + stride * k) * TB, ring + k * RS, TB, lane);
 
     // ---- prologue: the score operands of this (sequence, kv-head), built by every
-    // workgroup from the query and U_K, every global read issued in one batch.
-    // q'' = (U_K^T q) * step_K * log2(e) / sqrt(d) per query head; key field (chan, shift,
-    // pos) of score slot k gets q''[chan] * 2^shift / 2^pos, scaled per head so that the
-    // largest slot is 127 and split into three int8 digits (rows 4 head + digit).
-    constexpr int PSB = (int)scratch_ps_bytes(RB, NQM, D);
-    LDS_AS float* qf = (LDS_AS float*)(sm + a.off_scratch);  // [GM][D] query, then q''
-    LDS_AS float* ps = qf + GM * D;                          // [PARTS - 1][GM][D] partial sums
-    LDS_AS v4i* astage = (LDS_AS v4i*)ps;                    // [NQM][RB][64] operands (after ps)
-    LDS_AS uint16_t* kmap = (LDS_AS uint16_t*)((LDS_AS uint8_t*)ps + PSB);  // [NQM * 64] slots
-    LDS_AS float* smax = (LDS_AS float*)(kmap + NQM * 64);  // [16] per-head largest slot
-    LDS_AS int* corr = (LDS_AS int*)(smax + 16);            // [RB * 16] rows: digits of bit-7 slots
+    // workgroup.  Every global read is issued in one batch; once they have landed the first
+    // tiles start streaming and the rest of the prologue overlaps their latency (its LDS
+    // scratch is the ring's last slot, or the ring's start when the tiles wait for it).
+    // q' = U_K^T q per query head on bf16 MFMAs (q is bf16; U_K = hi + lo, channel-major),
+    // q'' = q' * step_K * log2(e) / sqrt(d); key field (chan, shift, pos) of score slot k
+    // gets q''[chan] * 2^shift / 2^pos, scaled per head so that the largest slot is 127 and
+    // split into three int8 digits (rows 4 head + digit).
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int RBW = D / 64;  // 16-channel row blocks of q' per wave
+    constexpr int KS = D / 32;   // MFMA k-steps over the input dimension
+    LDS_AS float* qf = (LDS_AS float*)(sm + a.off_scratch);  // [GM][D] q''
+    LDS_AS v4i* astage = (LDS_AS v4i*)(qf + GM * D);           // [NQM][RB][64] operands
+    LDS_AS uint16_t* kmap = (LDS_AS uint16_t*)(astage + NQM * RB * 64);  // [NQM * 64] slots
+    LDS_AS float* wmax = (LDS_AS float*)(kmap + NQM * 64);    // [4 waves][16] per-head largest slot
+    LDS_AS int* corr = (LDS_AS int*)(wmax + kWaves * 16);     // [RB * 16] rows: digits of bit-7 slots
     LDS_AS u32x4* ksched = (LDS_AS u32x4*)(sm + a.off_ksched);
     uint32_t voff[NVB], vmask[NVB];  // value columns of this lane: tile offset of its plane slice, mask
     {
-        constexpr int QPT = (GM * D + 255) / 256;
         constexpr int KPT = (NQM * 64 + 255) / 256;
-        const int j = tid % D, pt = __builtin_amdgcn_readfirstlane(tid / D);
-        const float* ub = H.UK + pt * ROWS * D + j;
-        float u[ROWS];
+        bf16x8 ah[RBW][KS], al[RBW][KS], bq[KS];
+        f4 stv[RBW], fmv[RBW];
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r) u[r] = ub[r * D];
-        const int bj = H.bitsK[j];
-        const float stj = H.stepK[j], fj = H.kq_fmax[j];
-        const uint16_t* qg = q + zh * G * D;
-        uint16_t qv[QPT];
+        for (int rbw = 0; rbw < RBW; ++rbw) {
+            const int j = 16 * (w * RBW + rbw) + c;  // A row: channel
 #pragma unroll
-        for (int k = 0; k < QPT; ++k) qv[k] = qg[min(tid + 256 * k, G * D - 1)];
+            for (int ks = 0; ks < KS; ++ks) {
+                ah[rbw][ks] = *(const bf16x8*)(H.UKt_hi + j * D + 32 * ks + 8 * g);
+                al[rbw][ks] = *(const bf16x8*)(H.UKt_lo + j * D + 32 * ks + 8 * g);
+            }
+            const int j0 = 16 * (w * RBW + rbw) + 4 * g;  // output rows of this lane
+            stv[rbw] = *(const f4*)(H.stepK + j0);
+            fmv[rbw] = *(const f4*)(H.kq_fmax + j0);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)  // B column: query head c
+            bq[ks] = c < G ? *(const bf16x8*)(q + (zh * G + c) * D + 32 * ks + 8 * g) : bf16x8{};
         uint16_t km[KPT];
 #pragma unroll
         for (int k = 0; k < KPT; ++k) km[k] = (&H.kq_slot[0][0][0])[min(tid + 256 * k, NQM * 64 - 1)];
-        uint32_t ks = 0u;  // key schedule table entry: [m][g] -> 4 word offsets then 4 masks
+        uint32_t ks_e = 0u;  // key schedule table entry: [m][g] -> 4 word offsets then 4 masks
         if (tid < NQM * 32) {
             const int m = tid >> 5, gg = (tid >> 3) & 3, e = tid & 7;
-            ks = e < 4 ? 256u * (uint32_t)H.kq_word[m][gg][e] : H.kq_mask[m][gg][e - 4];
+            ks_e = e < 4 ? 256u * (uint32_t)H.kq_word[m][gg][e] : H.kq_mask[m][gg][e - 4];
         }
+        const uint32_t vbase = 8u * (uint32_t)H.BK + 16u * (uint32_t)g;
 #pragma unroll
         for (int cb = 0; cb < NVB; ++cb) {
-            voff[cb] = H.vb_plane[cb][c];
-            vmask[cb] = H.vb_mask[cb][c];
+            voff[cb] = vbase + H.vb_plane[cb][c];
+            vmask[cb] = 0x01010101u * H.vb_mask[cb][c];
         }
+        // q' rows 16 (4 w + rbw) + 4 g + e of head c
+        const float qscale = kLog2e / sqrtf((float)D);
+        float mag = 0.0f;
 #pragma unroll
-        for (int k = 0; k < QPT; ++k)
-            if (tid + 256 * k < GM * D) qf[tid + 256 * k] = tid + 256 * k < G * D ? aatc::bf16f(qv[k]) : 0.0f;
+        for (int rbw = 0; rbw < RBW; ++rbw) {
+            f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[rbw][ks], bq[ks], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[rbw][ks], bq[ks], acc, 0, 0, 0);
+            }
+            f4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = acc[e] * stv[rbw][e] * qscale;  // step_K is 0 for uncoded channels
+                mag = fmaxf(mag, fabsf(v[e]) * fmv[rbw][e]);
+            }
+            if (c < GM) *(LDS_AS f4*)(qf + c * D + 16 * (w * RBW + rbw) + 4 * g) = v;
+        }
+        mag = fmaxf(mag, __shfl_xor(mag, 16));
+        mag = fmaxf(mag, __shfl_xor(mag, 32));
+        if (g == 0) wmax[w * 16 + c] = mag;
 #pragma unroll
         for (int k = 0; k < KPT; ++k)
             if (tid + 256 * k < NQM * 64) kmap[tid + 256 * k] = km[k];
-        if (tid < NQM * 32) ((LDS_AS uint32_t*)ksched)[tid] = ks;
-        if (tid < 16) smax[tid] = 0.0f;
+        if (tid < NQM * 32) ((LDS_AS uint32_t*)ksched)[tid] = ks_e;
         if (tid < RB * 16) corr[tid] = 0;
-        lds_barrier();
-        // q' = U_K^T q: thread (j, pt) sums its slice of rows; slices pt > 0 go through LDS
-        float part_acc[GM];
+        // every prologue read has been used: the tile loads issued next are the only vector
+        // memory operations in flight from here on
 #pragma unroll
-        for (int hh = 0; hh < GM; ++hh) {
-            const LDS_AS float* qh = qf + hh * D + pt * ROWS;
-            float acc = 0.0f;
-            if (hh < G) {
-#pragma unroll
-                for (int r4 = 0; r4 < ROWS / 4; ++r4) {
-                    const f4 x = *(const LDS_AS f4*)(qh + 4 * r4);
-                    acc = fmaf(u[4 * r4], x[0], acc);
-                    acc = fmaf(u[4 * r4 + 1], x[1], acc);
-                    acc = fmaf(u[4 * r4 + 2], x[2], acc);
-                    acc = fmaf(u[4 * r4 + 3], x[3], acc);
-                }
-            }
-            part_acc[hh] = acc;
-        }
-        if (pt > 0) {
-#pragma unroll
-            for (int hh = 0; hh < GM; ++hh) ps[((pt - 1) * GM + hh) * D + j] = part_acc[hh];
-        }
-        lds_barrier();
-        // slice 0 completes q'' and the per-head largest slot |q''[j]| max 2^(shift - pos)
-        const float qscale = kLog2e / sqrtf((float)D);
-        if (pt == 0) {
-#pragma unroll
-            for (int hh = 0; hh < GM; ++hh) {
-                float acc = part_acc[hh];
-#pragma unroll
-                for (int p2 = 1; p2 < PARTS; ++p2) acc += ps[((p2 - 1) * GM + hh) * D + j];
-                const float v = bj ? acc * stj * qscale : 0.0f;
-                qf[hh * D + j] = v;
-                const float mag = wave_max(fabsf(v) * fj);
-                if (lane == 0 && hh < G) atomicMax((int*)&smax[hh], __float_as_int(mag));
-            }
-        }
+        for (int cb = 0; cb < NVB; ++cb) asm volatile("" ::"v"(voff[cb]), "v"(vmask[cb]));
+        wait_all();
+        if (a.early)
+            for (int k = 0; k < NBW - 1 && t + stride * k < n_tiles; ++k)
+                load_tile(tiles + (t + stride * k) * TB, ring + k * RS, TB, lane);
         lds_barrier();
         // operands: thread (m, rb, lane group gg, dword iw, head hh4) forms the three digit
         // words of its four slots (rows 4 hh4 + 0..2; row 3 stays zero)
         for (int i = tid; i < NQM * RB * 64; i += 256) {
             const int hh4 = i & 3, iw = (i >> 2) & 3, gg = (i >> 4) & 3, rb = (i >> 6) % RB, m = (i >> 6) / RB;
             const int hh = 4 * rb + hh4;
-            const float mx = smax[hh];
+            const float mx = fmaxf(fmaxf(wmax[hh], wmax[16 + hh]), fmaxf(wmax[32 + hh], wmax[48 + hh]));
             const float sc = hh < G && mx > 0.0f ? 127.0f / mx : 0.0f;
             uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
             int f0 = 0, f1 = 0, f2 = 0;
@@ -348,16 +340,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
     v4i sinit[RB];    // score accumulator start: 128 x the digits multiplying bit-7 fields
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        const float mx = smax[4 * rb + g] * (1.0f / 127.0f);
+        const int hh = 4 * rb + g;
+        const float mx = fmaxf(fmaxf(wmax[hh], wmax[16 + hh]), fmaxf(wmax[32 + hh], wmax[48 + hh])) * (1.0f / 127.0f);
         qs[rb][0] = mx;
         qs[rb][1] = mx * kQ1;
         qs[rb][2] = mx * kQ2;
         sinit[rb] = v4i{128 * corr[16 * rb + 4 * g], 128 * corr[16 * rb + 4 * g + 1], 128 * corr[16 * rb + 4 * g + 2], 0};
-    }
-#pragma unroll
-    for (int cb = 0; cb < NVB; ++cb) {
-        voff[cb] = 8u * (uint32_t)H.BK + voff[cb] + 16u * (uint32_t)g;
-        vmask[cb] *= 0x01010101u;
     }
     // the operands are in registers and every prologue read has completed: inside the loop
     // the only vector memory operations are this wave's tile loads
@@ -369,7 +357,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
     for (int cb = 0; cb < NVB; ++cb) asm volatile("" ::"v"(voff[cb]), "v"(vmask[cb]));
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(qs[rb][0]), "v"(sinit[rb]));
-    wait_all();
     lds_barrier();  // the scratch is free for the ring
     if (!a.early)
         for (int k = 0; k < NBW - 1 && t + stride * k < n_tiles; ++k)
@@ -570,6 +557,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
 // (the stored byte of a field at bit pos is field 2^pos, minus 128 at the top of a byte)
 // and o = obias + U_V (step * A / L).  Every global read is issued in one round.
 // ---------------------------------------------------------------------------------------
+static_assert(offsetof(DevHead, vch) % 16 == 0, "the merge loads a channel's field table as 16 bytes");
 constexpr int kMergeCols = 3;     // value columns per thread (16 kMaxVB <= 3 D for D >= 128)
 constexpr int kMergeRound = 16;   // partials per thread and column
 
@@ -598,6 +586,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DevHead* __r
     float uv[ROWS];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) uv[r] = H.UVt[(sl * ROWS + r) * D + ii];  // UVt[j * d + i] = U_V[i][j]
+    // channel tid (tid < D): its field columns and output constants
+    typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+    const int jc = tid % D;
+    const u16x8 fl = *(const u16x8*)&H.vch[jc][0];
+    const float stv = H.bitsV[jc] ? H.stepV[jc] : 0.0f, obv = H.obias[jc], muv = H.muV[jc];
     float x[kMergeCols][kMergeRound];
 #pragma unroll
     for (int k = 0; k < kMergeCols; ++k)
@@ -643,14 +636,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DevHead* __r
     }
     // value coefficients, dequantisation step and 1 / L
     if (tid < D) {
-        const int j = tid;
         float A = 0.0f;
-        for (int f = H.vch_first[j]; f < H.vch_first[j + 1]; ++f) {
-            const uint32_t en = H.vch_col[f];
-            const float v = colv[en & 511] + (((en >> 13) & 1) ? O : 0.0f);
-            A = fmaf(__builtin_amdgcn_ldexpf(1.0f, (int)((en >> 9) & 15) - 8), v, A);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t en = fl[k];
+            if (en != 0xFFFFu) {
+                const float v = colv[en & 511] + (((en >> 13) & 1) ? O : 0.0f);
+                A = fmaf(__builtin_amdgcn_ldexpf(1.0f, (int)((en >> 9) & 15) - 8), v, A);
+            }
         }
-        cbar[j] = H.bitsV[j] && L > 0.0f ? H.stepV[j] * A / L : 0.0f;
+        cbar[tid] = L > 0.0f ? stv * A / L : 0.0f;
     }
     __syncthreads();
     // o = obias + U_V cbar: thread (i, slice) sums its rows, slices meet in LDS
@@ -663,7 +658,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DevHead* __r
         float o = 0.0f;
 #pragma unroll
         for (int s2 = 0; s2 < SL; ++s2) o += red[s2][tid];
-        out[(zh * G + hh) * D + tid] = L > 0.0f ? H.obias[tid] + o : H.muV[tid];
+        out[(zh * G + hh) * D + tid] = L > 0.0f ? obv + o : muv;
     }
 }
 

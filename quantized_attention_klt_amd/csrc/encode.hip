@@ -97,10 +97,10 @@ __global__ __launch_bounds__(256) void encode_kernel(const DevHead* __restrict__
             c = coeffs[((t * n_kv + h) * 2 + kv) * d + j];
         } else {
             const uint16_t* x = (kv ? V : K) + ((int64_t)zi * n_tokens + t) * n_kv * d + (int64_t)h * d;
-            const uint16_t* hi = kv ? H.UVhi : H.UKhi;
-            const uint16_t* lo = kv ? H.UVlo : H.UKlo;
+            const uint16_t* hi = (kv ? H.UVt_hi : H.UKt_hi) + j * d;
+            const uint16_t* lo = (kv ? H.UVt_lo : H.UKt_lo) + j * d;
             float acc = 0.0f;
-            for (int ii = 0; ii < d; ++ii) acc = fmaf(bf16f(x[ii]), bf16f(hi[ii * d + j]) + bf16f(lo[ii * d + j]), acc);
+            for (int ii = 0; ii < d; ++ii) acc = fmaf(bf16f(x[ii]), bf16f(hi[ii]) + bf16f(lo[ii]), acc);
             c = acc - (kv ? H.biasV[j] : H.biasK[j]);
         }
         int b = kv ? H.bitsV[j] : H.bitsK[j];
