@@ -16,6 +16,7 @@ constexpr int kMaxFields = 384;  // fields of one record: <= d channels + 2 per 
 constexpr int kMaxQM = 16;       // score MFMAs per token group (<= 32 words x 8 fields / 16)
 constexpr int kMaxVB = 24;       // value column blocks of 16 fields per head
 constexpr int kKeyAlign = 32;    // key bits per token are a multiple of one 32-bit word
+constexpr int kMaxRecordBytes = kMaxD;  // bytes of one record (at most 8 bits per channel)
 
 // One byte-aligned field of a token record: code bits [shift, shift + width) of channel
 // chan at bits [pos, pos + width) of record byte `byte` (never crossing a byte).
@@ -61,9 +62,12 @@ struct alignas(256) DevHead {
     float stepK[kMaxD], stepV[kMaxD];
     float invK[kMaxD], invV[kMaxD];
     int32_t bitsK[kMaxD], bitsV[kMaxD];
-    // record fields sorted by (byte, pos): chan | width << 8 | shift << 12 | pos << 16 | byte << 20
+    // record fields sorted by (byte, pos): chan | width << 8 | shift << 12 | pos << 16 | byte << 20;
+    // record byte q holds fields [fbyteK[q], fbyteK[q + 1]) (likewise for values)
     uint32_t fieldK[kMaxFields];
     uint32_t fieldV[kMaxFields];
+    int16_t fbyteK[kMaxRecordBytes + 8];
+    int16_t fbyteV[kMaxRecordBytes + 8];
     // ---- decode schedule -------------------------------------------------------------
     // Score MFMAs: nqm per token group.  The B operand of lane group g (lanes 16g..16g+15,
     // K-slots 16g..16g+15) in MFMA m is four dwords; dword i is key-record word

@@ -475,9 +475,16 @@ int finalize(aatc_codebook* cb) {
         for (int which = 0; which < 2; ++which) {
             const std::vector<Field>& fs = which ? H.fV : H.fK;
             uint32_t* dst = which ? D.fieldV : D.fieldK;
+            int16_t* first = which ? D.fbyteV : D.fbyteK;
+            const int nbytes = (which ? H.BV : H.BK) / 8;
             for (size_t i = 0; i < fs.size(); ++i)
                 dst[i] = (uint32_t)(fs[i].chan | (fs[i].width << 8) | (fs[i].shift << 12) | (fs[i].pos << 16) |
                                     (fs[i].byte << 20));
+            size_t f = 0;
+            for (int q = 0; q <= nbytes; ++q) {
+                while (f < fs.size() && fs[f].byte < q) ++f;
+                first[q] = (int16_t)f;
+            }
         }
         int rc = build_decode_schedule(H, D);
         if (rc != AATC_OK) return set_error(rc, "head %zu: %s", h, "decode schedule exceeds kernel limits");
