@@ -70,25 +70,24 @@ struct alignas(256) DevHead {
     int16_t fbyteV[kMaxRecordBytes + 8];
     // ---- decode schedule -------------------------------------------------------------
     // Score MFMAs: nqm per token group.  The B operand of lane group g (lanes 16g..16g+15,
-    // K-slots 16g..16g+15) in MFMA m is four dwords; dword i is key-record word
-    // kq_word[m][g][i] of the lane's token ANDed with kq_mask[m][g][i], which keeps one
-    // field per byte.  kq_slot[m][g][4i+b] describes the field kept in byte b:
-    // chan | shift << 8 | pos << 11 | flip << 14 (pos = bit position in the byte; flip =
-    // the field ends at bit 7, so the stored inverted bit 7 makes the byte read 128 low),
-    // 0xFFFF for an empty byte.
+    // K-slots 16g..16g+15) in MFMA m is four dwords; dword i is key-record word w_i of the
+    // lane's token ANDed with a mask that keeps one field per byte.  kq_sched[m][g] holds
+    // the four tile byte offsets 256 w_i (the record word of slots 4c..4c+3 for a lane's
+    // token column c sits at 256 w_i + 16 c) and then the four masks.  kq_slot[m][g][4i+b]
+    // describes the field kept in byte b: chan | shift << 8 | pos << 11 | flip << 14 (pos =
+    // bit position in the byte; flip = the field ends at bit 7, so the stored inverted bit 7
+    // makes the byte read 128 low), 0xFFFF for an empty byte.
     int32_t nqm;
     int32_t nvb;  // value column blocks of 16 fields
     int32_t pad1[6];
-    int16_t kq_word[kMaxQM][4][4];
-    uint32_t kq_mask[kMaxQM][4][4];
+    uint32_t kq_sched[kMaxQM][4][8];
     uint16_t kq_slot[kMaxQM][4][16];
     // per key channel: the largest slot weight 2^(shift - pos) of its fields (0 if uncoded)
     float kq_fmax[kMaxD];
-    // Value MFMAs: column c of block cb is value field 16 cb + c (fieldV order): the byte
-    // plane of its record byte (value-block offset 64 * byte) and its mask within the
-    // byte; padding columns have plane 0 and mask 0.
-    uint16_t vb_plane[kMaxVB][16];
-    uint8_t vb_mask[kMaxVB][16];
+    // Value MFMAs: column c of block cb is value field 16 cb + c (fieldV order):
+    // vb_col = (value-block offset 64 * byte of its record byte's plane) | mask << 16, the
+    // field mask within the byte; padding columns are 0.
+    uint32_t vb_col[kMaxVB][16];
     // Value channel j: the columns of its fields (at most 8: a field has at least one bit),
     // each col | (shift - pos + 8) << 9 | flip << 13, unused entries 0xFFFF.
     uint16_t vch[kMaxD][8];

@@ -333,7 +333,7 @@ static bool make_fields(const std::vector<int32_t>& bits, std::vector<Field>& ou
 static int build_decode_schedule(const HeadCB& H, DevHead& D) {
     for (int m = 0; m < kMaxQM; ++m)
         for (int g = 0; g < 4; ++g) {
-            for (int i = 0; i < 4; ++i) D.kq_word[m][g][i] = 0, D.kq_mask[m][g][i] = 0u;
+            for (int i = 0; i < 8; ++i) D.kq_sched[m][g][i] = 0u;
             for (int i = 0; i < 16; ++i) D.kq_slot[m][g][i] = 0xFFFF;
         }
     struct Dword {
@@ -366,8 +366,8 @@ static int build_decode_schedule(const HeadCB& H, DevHead& D) {
     D.nqm = std::max(nqm, 1);
     for (size_t k = 0; k < dws.size(); ++k) {
         const int m = (int)k / 16, g = ((int)k / 4) % 4, i = (int)k % 4;
-        D.kq_word[m][g][i] = (int16_t)dws[k].word;
-        D.kq_mask[m][g][i] = dws[k].mask;
+        D.kq_sched[m][g][i] = 256u * (uint32_t)dws[k].word;
+        D.kq_sched[m][g][4 + i] = dws[k].mask;
         for (int b = 0; b < 4; ++b) D.kq_slot[m][g][4 * i + b] = dws[k].slot[b];
     }
     for (int j = 0; j < kMaxD; ++j) D.kq_fmax[j] = 0.0f;
@@ -377,11 +377,10 @@ static int build_decode_schedule(const HeadCB& H, DevHead& D) {
     D.nvb = std::max((nf + 15) / 16, 1);
     if (D.nvb > kMaxVB || nf > kMaxFields) return AATC_ERR_UNSUPPORTED;
     for (int cb = 0; cb < kMaxVB; ++cb)
-        for (int c = 0; c < 16; ++c) D.vb_plane[cb][c] = 0, D.vb_mask[cb][c] = 0;
+        for (int c = 0; c < 16; ++c) D.vb_col[cb][c] = 0u;
     for (int i = 0; i < nf; ++i) {
         const Field& f = H.fV[i];
-        D.vb_plane[i / 16][i % 16] = (uint16_t)(64 * f.byte);
-        D.vb_mask[i / 16][i % 16] = (uint8_t)(((1u << f.width) - 1u) << f.pos);
+        D.vb_col[i / 16][i % 16] = (uint32_t)(64 * f.byte) | ((((1u << f.width) - 1u) << f.pos) << 16);
     }
     for (int j = 0; j < kMaxD; ++j)
         for (int k = 0; k < 8; ++k) D.vch[j][k] = 0xFFFF;

@@ -6,13 +6,14 @@
 // inverse-transformed once per query head); "Spend Bits Where Queries Look" abstract
 // (decoding reads the whole cache every step and is bandwidth-bound).
 //
-// Two kernels on the caller's stream.
+// Three kernels on the caller's stream.
+//   qprep  - one wave per (16-channel block, sequence, kv-head) forms q' = U_K^T q for the
+//            query heads on bf16 MFMAs, scales it by the key steps (and log2 e / sqrt d) and
+//            finds per head the block's largest score slot value;
 //   decode - W workgroups of 4 waves share the 64-token tiles of one (sequence, kv-head).
-//     prologue - the first tiles start streaming; meanwhile the workgroup forms
-//                q' = U_K^T q for the kv-head's query heads, scales it by the key steps
-//                (and log2 e / sqrt d) and splits it into three int8 digits laid out as
-//                the A operands of the score MFMAs (one byte per key field, weighted by the
-//                field's code shift over its bit position);
+//     prologue - the first tiles start streaming; meanwhile the workgroup splits q'' into
+//                three int8 digits laid out as the A operands of the score MFMAs (one byte
+//                per key field, weighted by the field's code shift over its bit position);
 //     tiles    - wave w of workgroup i takes tiles 4i + w + 4Wk and streams them through a
 //                private ring of LDS buffers (direct global->LDS loads, counted waits, no
 //                workgroup barriers in the loop).  Per tile:
@@ -167,19 +168,87 @@ constexpr int waves_for(int rb, int nqm, int nvb) {
     return vgpr_estimate(rb, nqm, nvb) <= 128 ? 4 : (vgpr_estimate(rb, nqm, nvb) <= 168 ? 3 : 2);
 }
 
-// bytes of the prologue's LDS scratch: q'' [4 RB][D]; staged operands [NQM][RB][64 lanes]
-// [16 B]; slots [NQM * 64]; per-wave head maxima [4][16]; per-row corrections [RB * 16]
-constexpr size_t scratch_bytes(int rb, int nqm, int d) {
-    return (size_t)4 * rb * d * 4 + (size_t)nqm * rb * 1024 + (size_t)nqm * 128 + 256 + (size_t)rb * 64;
+// bytes of the prologue's LDS scratch: q'' [4 RB][D] and block maxima [D / 16][16]; slots
+// [NQM * 64]; value columns [NVB][16]; staged operands [NQM][RB][64 lanes][16 B]; per-row
+// corrections [RB * 16]
+constexpr size_t scratch_bytes(int rb, int nqm, int nvb, int d) {
+    return ((size_t)4 * rb * d + d) * 4 + (size_t)nqm * 128 + (size_t)nvb * 64 + (size_t)nqm * rb * 1024 +
+           (size_t)rb * 64;
+}
+
+// ---------------------------------------------------------------------------------------
+// query preparation, one single-wave workgroup per (16-channel block, kv-head, sequence):
+// q' = U_K^T q for the block's channels and the kv-head's query heads on bf16 MFMAs (q is
+// bf16; U_K = hi + lo, channel-major; rows = channels, columns = heads),
+// q'' = q' * step_K * log2(e) / sqrt(d), and per head the block's largest slot value
+// |q''[j]| max over the fields of j of 2^(shift - pos).  Out: qbuf[(z, h)] = [4 RB heads][D]
+// q'' then [D / 16 blocks][16 heads] maxima.  The workgroup also streams its block's rows of
+// U_V^T (and the first one the decode prologue's tables) through LDS, so that the merge and
+// the decode prologue find them in the device cache.
+// ---------------------------------------------------------------------------------------
+template <int RB, int D>
+__global__ __launch_bounds__(64) void qprep_kernel(const DevHead* __restrict__ blob, int layer, int n_kv, int G,
+                                                   const uint16_t* __restrict__ q, float* __restrict__ qbuf) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int GM = 4 * RB;
+    constexpr int KS = D / 32;  // k-steps over the input dimension
+    __shared__ __attribute__((aligned(16))) uint8_t warm[16 * D * 4];
+    const int cb = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
+    const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
+    const DevHead& H = blob[layer * n_kv + h];
+    const int64_t zh = (int64_t)z * n_kv + h;
+    float* out = qbuf + zh * (GM * D + D);
+    // U_V^T rows 16 cb .. 16 cb + 15 into LDS (never read: they only pass through the cache)
+    for (int off = 0; off < 16 * D * 4; off += 1024)
+        __builtin_amdgcn_global_load_lds((const void*)((const uint8_t*)(H.UVt + 16 * cb * D) + off + 16 * lane),
+                                         (__attribute__((address_space(3))) void*)(warm + off), 16, 0, 0);
+    if (cb == 0 && z == 0) {  // the decode prologue's tables likewise
+        const uint8_t* tabs[3] = {(const uint8_t*)&H.kq_slot[0][0][0], (const uint8_t*)&H.kq_sched[0][0][0],
+                                  (const uint8_t*)&H.vb_col[0][0]};
+        const int sizes[3] = {(int)sizeof(H.kq_slot), (int)sizeof(H.kq_sched), (int)sizeof(H.vb_col)};
+        for (int k = 0; k < 3; ++k)
+            for (int off = 0; off < sizes[k] && off < 16 * D * 4; off += 1024)
+                if (off + 16 * lane < sizes[k])
+                    __builtin_amdgcn_global_load_lds((const void*)(tabs[k] + off + 16 * lane),
+                                                     (__attribute__((address_space(3))) void*)(warm + off), 16, 0, 0);
+    }
+    bf16x8 ah[KS], al[KS], bq[KS];
+    const int j = 16 * cb + c;  // A row: channel
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        ah[ks] = *(const bf16x8*)(H.UKt_hi + j * D + 32 * ks + 8 * g);
+        al[ks] = *(const bf16x8*)(H.UKt_lo + j * D + 32 * ks + 8 * g);
+        bq[ks] = c < G ? *(const bf16x8*)(q + (zh * G + c) * D + 32 * ks + 8 * g) : bf16x8{};  // B column: head c
+    }
+    const int j0 = 16 * cb + 4 * g;  // output rows of this lane
+    const f4 stv = *(const f4*)(H.stepK + j0), fmv = *(const f4*)(H.kq_fmax + j0);
+    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bq[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], bq[ks], acc, 0, 0, 0);
+    }
+    const float qscale = kLog2e / sqrtf((float)D);
+    f4 v;
+    float mag = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[e] = acc[e] * stv[e] * qscale;  // step_K is 0 for uncoded channels
+        mag = fmaxf(mag, fabsf(v[e]) * fmv[e]);
+    }
+    if (c < GM) *(f4*)(out + c * D + j0) = v;
+    mag = fmaxf(mag, __shfl_xor(mag, 16));
+    mag = fmaxf(mag, __shfl_xor(mag, 32));
+    if (g == 0) out[GM * D + 16 * cb + c] = mag;
+    wait_all();
 }
 
 template <int RB, int NQM, int NVB, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel(
     const DevHead* __restrict__ blob, const uint8_t* __restrict__ cache, DecodeArgs a,
-    const int32_t* __restrict__ seq_ids, const int64_t* __restrict__ seq_lens, const uint16_t* __restrict__ q,
+    const int32_t* __restrict__ seq_ids, const int64_t* __restrict__ seq_lens, const float* __restrict__ qbuf,
     float* __restrict__ part) {
-    constexpr int PARTS = 256 / D;  // row slices of U_K per column
-    constexpr int ROWS = D / PARTS;  // rows per slice
     constexpr int PST = 64;          // bytes per row of the probability operand (64 tokens)
     constexpr int GM = 4 * RB;       // query heads the operands have room for
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
@@ -206,130 +275,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
     LDS_AS uint8_t* ring = sm + w * BB;
     const int RS = kWaves * BB;  // bytes between a wave's ring slots
     int64_t t = (int64_t)wgi * kWaves + w;
-
-    // ---- prologue: the score operands of this (sequence, kv-head), built by every
-    // workgroup.  Every global read is issued in one batch; once they have landed the first
-    // tiles start streaming and the rest of the prologue overlaps their latency (its LDS
-    // scratch is the ring's last slot, or the ring's start when the tiles wait for it).
-    // q' = U_K^T q per query head on bf16 MFMAs (q is bf16; U_K = hi + lo, channel-major),
-    // q'' = q' * step_K * log2(e) / sqrt(d); key field (chan, shift, pos) of score slot k
-    // gets q''[chan] * 2^shift / 2^pos, scaled per head so that the largest slot is 127 and
-    // split into three int8 digits (rows 4 head + digit).
-    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    constexpr int RBW = D / 64;  // 16-channel row blocks of q' per wave
-    constexpr int KS = D / 32;   // MFMA k-steps over the input dimension
-    LDS_AS float* qf = (LDS_AS float*)(sm + a.off_scratch);  // [GM][D] q''
-    LDS_AS v4i* astage = (LDS_AS v4i*)(qf + GM * D);           // [NQM][RB][64] operands
-    LDS_AS uint16_t* kmap = (LDS_AS uint16_t*)(astage + NQM * RB * 64);  // [NQM * 64] slots
-    LDS_AS float* wmax = (LDS_AS float*)(kmap + NQM * 64);    // [4 waves][16] per-head largest slot
-    LDS_AS int* corr = (LDS_AS int*)(wmax + kWaves * 16);     // [RB * 16] rows: digits of bit-7 slots
-    LDS_AS u32x4* ksched = (LDS_AS u32x4*)(sm + a.off_ksched);
-    uint32_t voff[NVB], vmask[NVB];  // value columns of this lane: tile offset of its plane slice, mask
+    // ---- prologue: the score operands of this (sequence, kv-head).  Key field (chan,
+    // shift, pos) of score slot k gets q''[chan] * 2^shift / 2^pos, scaled per head so that
+    // the largest slot is 127, split into three int8 digits (rows 4 head + digit).  The
+    // tables arrive by direct global->LDS copies issued before the first tiles' copies, so
+    // waiting for them leaves the tiles in flight (the scratch is the ring's last slot, or
+    // the ring's start with the tiles issued after the prologue when it does not fit).
+    constexpr int QN = GM * D + D;  // floats of q'' and the per-block maxima
+    LDS_AS float* qf = (LDS_AS float*)(sm + a.off_scratch);        // [GM][D] q'', [D / 16][16] maxima
+    LDS_AS uint16_t* kmap = (LDS_AS uint16_t*)(qf + QN);             // [NQM * 64] slots
+    LDS_AS uint32_t* vcol = (LDS_AS uint32_t*)(kmap + NQM * 64);     // [NVB][16] value columns
+    LDS_AS v4i* astage = (LDS_AS v4i*)(vcol + NVB * 16);             // [NQM][RB][64] operands
+    LDS_AS int* corr = (LDS_AS int*)(astage + NQM * RB * 64);        // [RB * 16] rows: digits of bit-7 slots
+    LDS_AS u32x4* ksched = (LDS_AS u32x4*)(sm + a.off_ksched);      // [NQM][4][2]: offsets, masks
+    if (tid < RB * 16) corr[tid] = 0;
     {
-        constexpr int KPT = (NQM * 64 + 255) / 256;
-        bf16x8 ah[RBW][KS], al[RBW][KS], bq[KS];
-        f4 stv[RBW], fmv[RBW];
+        // wave 0: q'' and maxima; wave 1: slots; wave 2: value columns; wave 3: key schedule
+        const uint8_t* src = w == 0   ? (const uint8_t*)(qbuf + zh * QN)
+                             : w == 1 ? (const uint8_t*)&H.kq_slot[0][0][0]
+                             : w == 2 ? (const uint8_t*)&H.vb_col[0][0]
+                                      : (const uint8_t*)&H.kq_sched[0][0][0];
+        LDS_AS uint8_t* dst = w == 0 ? (LDS_AS uint8_t*)qf
+                              : w == 1 ? (LDS_AS uint8_t*)kmap
+                              : w == 2 ? (LDS_AS uint8_t*)vcol
+                                       : (LDS_AS uint8_t*)ksched;
+        const int bytes = w == 0 ? QN * 4 : w == 1 ? NQM * 128 : w == 2 ? NVB * 64 : NQM * 128;
+        load_tile(src, dst, bytes, lane);
+    }
+    int n_early = 0;  // tiles this wave has in flight
+    if (a.early)
+        for (; n_early < NBW - 1 && t + stride * n_early < n_tiles; ++n_early)
+            load_tile(tiles + (t + stride * n_early) * TB, ring + n_early * RS, TB, lane);
+    wait_vm(nl * n_early);  // this wave's table copy has landed
+    lds_barrier();
+    // operands: thread (m, rb, lane group gg, dword iw, head hh4) forms the three digit words
+    // of its four slots (rows 4 hh4 + 0..2; row 3 stays zero)
+    for (int i = tid; i < NQM * RB * 64; i += 256) {
+        const int hh4 = i & 3, iw = (i >> 2) & 3, gg = (i >> 4) & 3, rb = (i >> 6) % RB, m = (i >> 6) / RB;
+        const int hh = 4 * rb + hh4;
+        float mx = 0.0f;
 #pragma unroll
-        for (int rbw = 0; rbw < RBW; ++rbw) {
-            const int j = 16 * (w * RBW + rbw) + c;  // A row: channel
+        for (int bk = 0; bk < D / 16; ++bk) mx = fmaxf(mx, qf[GM * D + 16 * bk + hh]);
+        const float sc = hh < G && mx > 0.0f ? 127.0f / mx : 0.0f;
+        uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
+        int f0 = 0, f1 = 0, f2 = 0;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                ah[rbw][ks] = *(const bf16x8*)(H.UKt_hi + j * D + 32 * ks + 8 * g);
-                al[rbw][ks] = *(const bf16x8*)(H.UKt_lo + j * D + 32 * ks + 8 * g);
-            }
-            const int j0 = 16 * (w * RBW + rbw) + 4 * g;  // output rows of this lane
-            stv[rbw] = *(const f4*)(H.stepK + j0);
-            fmv[rbw] = *(const f4*)(H.kq_fmax + j0);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)  // B column: query head c
-            bq[ks] = c < G ? *(const bf16x8*)(q + (zh * G + c) * D + 32 * ks + 8 * g) : bf16x8{};
-        uint16_t km[KPT];
-#pragma unroll
-        for (int k = 0; k < KPT; ++k) km[k] = (&H.kq_slot[0][0][0])[min(tid + 256 * k, NQM * 64 - 1)];
-        uint32_t ks_e = 0u;  // key schedule table entry: [m][g] -> 4 word offsets then 4 masks
-        if (tid < NQM * 32) {
-            const int m = tid >> 5, gg = (tid >> 3) & 3, e = tid & 7;
-            ks_e = e < 4 ? 256u * (uint32_t)H.kq_word[m][gg][e] : H.kq_mask[m][gg][e - 4];
-        }
-        const uint32_t vbase = 8u * (uint32_t)H.BK + 16u * (uint32_t)g;
-#pragma unroll
-        for (int cb = 0; cb < NVB; ++cb) {
-            voff[cb] = vbase + H.vb_plane[cb][c];
-            vmask[cb] = 0x01010101u * H.vb_mask[cb][c];
-        }
-        // q' rows 16 (4 w + rbw) + 4 g + e of head c
-        const float qscale = kLog2e / sqrtf((float)D);
-        float mag = 0.0f;
-#pragma unroll
-        for (int rbw = 0; rbw < RBW; ++rbw) {
-            f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[rbw][ks], bq[ks], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[rbw][ks], bq[ks], acc, 0, 0, 0);
-            }
-            f4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[e] = acc[e] * stv[rbw][e] * qscale;  // step_K is 0 for uncoded channels
-                mag = fmaxf(mag, fabsf(v[e]) * fmv[rbw][e]);
-            }
-            if (c < GM) *(LDS_AS f4*)(qf + c * D + 16 * (w * RBW + rbw) + 4 * g) = v;
-        }
-        mag = fmaxf(mag, __shfl_xor(mag, 16));
-        mag = fmaxf(mag, __shfl_xor(mag, 32));
-        if (g == 0) wmax[w * 16 + c] = mag;
-#pragma unroll
-        for (int k = 0; k < KPT; ++k)
-            if (tid + 256 * k < NQM * 64) kmap[tid + 256 * k] = km[k];
-        if (tid < NQM * 32) ((LDS_AS uint32_t*)ksched)[tid] = ks_e;
-        if (tid < RB * 16) corr[tid] = 0;
-        // every prologue read has been used: the tile loads issued next are the only vector
-        // memory operations in flight from here on
-#pragma unroll
-        for (int cb = 0; cb < NVB; ++cb) asm volatile("" ::"v"(voff[cb]), "v"(vmask[cb]));
-        wait_all();
-        if (a.early)
-            for (int k = 0; k < NBW - 1 && t + stride * k < n_tiles; ++k)
-                load_tile(tiles + (t + stride * k) * TB, ring + k * RS, TB, lane);
-        lds_barrier();
-        // operands: thread (m, rb, lane group gg, dword iw, head hh4) forms the three digit
-        // words of its four slots (rows 4 hh4 + 0..2; row 3 stays zero)
-        for (int i = tid; i < NQM * RB * 64; i += 256) {
-            const int hh4 = i & 3, iw = (i >> 2) & 3, gg = (i >> 4) & 3, rb = (i >> 6) % RB, m = (i >> 6) / RB;
-            const int hh = 4 * rb + hh4;
-            const float mx = fmaxf(fmaxf(wmax[hh], wmax[16 + hh]), fmaxf(wmax[32 + hh], wmax[48 + hh]));
-            const float sc = hh < G && mx > 0.0f ? 127.0f / mx : 0.0f;
-            uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
-            int f0 = 0, f1 = 0, f2 = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t sl = kmap[(m * 4 + gg) * 16 + 4 * iw + e];
-                if (sl != 0xFFFFu) {
-                    const int sh = (int)((sl >> 8) & 7) - (int)((sl >> 11) & 7);
-                    float d0, d1, d2;
-                    digits254(qf[hh * D + (sl & 255)] * __builtin_amdgcn_ldexpf(sc, sh), d0, d1, d2);
-                    w0 |= ((uint32_t)(int)d0 & 0xFFu) << (8 * e);
-                    w1 |= ((uint32_t)(int)d1 & 0xFFu) << (8 * e);
-                    w2 |= ((uint32_t)(int)d2 & 0xFFu) << (8 * e);
-                    if (sl & 0x4000u) f0 += (int)d0, f1 += (int)d1, f2 += (int)d2;
-                }
-            }
-            // dword iw of lane (gg, row) in operand [m][rb], rows 4 hh4 + digit
-            LDS_AS uint32_t* dst = (LDS_AS uint32_t*)(astage + (m * RB + rb) * 64 + 16 * gg + 4 * hh4) + iw;
-            dst[0] = w0;
-            dst[4] = w1;
-            dst[8] = w2;
-            dst[12] = 0u;
-            if (f0 | f1 | f2) {
-                atomicAdd((int*)&corr[rb * 16 + 4 * hh4], f0);
-                atomicAdd((int*)&corr[rb * 16 + 4 * hh4 + 1], f1);
-                atomicAdd((int*)&corr[rb * 16 + 4 * hh4 + 2], f2);
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t sl = kmap[(m * 4 + gg) * 16 + 4 * iw + e];
+            if (sl != 0xFFFFu) {
+                const int sh = (int)((sl >> 8) & 7) - (int)((sl >> 11) & 7);
+                float d0, d1, d2;
+                digits254(qf[hh * D + (sl & 255)] * __builtin_amdgcn_ldexpf(sc, sh), d0, d1, d2);
+                w0 |= ((uint32_t)(int)d0 & 0xFFu) << (8 * e);
+                w1 |= ((uint32_t)(int)d1 & 0xFFu) << (8 * e);
+                w2 |= ((uint32_t)(int)d2 & 0xFFu) << (8 * e);
+                if (sl & 0x4000u) f0 += (int)d0, f1 += (int)d1, f2 += (int)d2;
             }
         }
-        lds_barrier();
+        // dword iw of lane (gg, row) in operand [m][rb], rows 4 hh4 + digit
+        LDS_AS uint32_t* dst = (LDS_AS uint32_t*)(astage + (m * RB + rb) * 64 + 16 * gg + 4 * hh4) + iw;
+        dst[0] = w0;
+        dst[4] = w1;
+        dst[8] = w2;
+        dst[12] = 0u;
+        if (f0 | f1 | f2) {
+            atomicAdd((int*)&corr[rb * 16 + 4 * hh4], f0);
+            atomicAdd((int*)&corr[rb * 16 + 4 * hh4 + 1], f1);
+            atomicAdd((int*)&corr[rb * 16 + 4 * hh4 + 2], f2);
+        }
+    }
+    lds_barrier();
+    uint32_t voff[NVB], vmask[NVB];  // value columns of this lane: tile offset of its plane slice, mask
+#pragma unroll
+    for (int cb = 0; cb < NVB; ++cb) {
+        const uint32_t v = vcol[cb * 16 + c];
+        voff[cb] = 8u * (uint32_t)H.BK + (v & 0xFFFFu) + 16u * (uint32_t)g;
+        vmask[cb] = 0x01010101u * (v >> 16);
     }
     v4i Aq[NQM][RB];  // score A operands (query digits), resident for the whole loop
 #pragma unroll
@@ -340,8 +361,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
     v4i sinit[RB];    // score accumulator start: 128 x the digits multiplying bit-7 fields
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        const int hh = 4 * rb + g;
-        const float mx = fmaxf(fmaxf(wmax[hh], wmax[16 + hh]), fmaxf(wmax[32 + hh], wmax[48 + hh])) * (1.0f / 127.0f);
+        float mx = 0.0f;
+#pragma unroll
+        for (int bk = 0; bk < D / 16; ++bk) mx = fmaxf(mx, qf[GM * D + 16 * bk + 4 * rb + g]);
+        mx *= 1.0f / 127.0f;
         qs[rb][0] = mx;
         qs[rb][1] = mx * kQ1;
         qs[rb][2] = mx * kQ2;
@@ -558,6 +581,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
 // and o = obias + U_V (step * A / L).  Every global read is issued in one round.
 // ---------------------------------------------------------------------------------------
 static_assert(offsetof(DevHead, vch) % 16 == 0, "the merge loads a channel's field table as 16 bytes");
+static_assert(offsetof(DevHead, kq_slot) % 16 == 0 && offsetof(DevHead, kq_sched) % 16 == 0 &&
+                  offsetof(DevHead, vb_col) % 16 == 0,
+              "the decode prologue copies these tables 16 bytes per lane");
 constexpr int kMergeCols = 3;     // value columns per thread (16 kMaxVB <= 3 D for D >= 128)
 constexpr int kMergeRound = 16;   // partials per thread and column
 
@@ -677,12 +703,13 @@ constexpr Variant kVariants[] = {{1, 2, 4},  {1, 2, 8},  {1, 3, 8},  {1, 3, 10},
 struct Plan {
     Variant v;
     int nqm_max, nvb_max, wg_per_head, wgs_per_cu;
-    size_t part_bytes;
+    size_t qbuf_bytes, part_bytes;
     DecodeArgs args;
     size_t lds;
 };
 
 size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, Plan& p) {
     const int G = cb->group, d = cb->d;
@@ -719,7 +746,7 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
         return set_error(AATC_ERR_UNSUPPORTED, "%d key bits per token are too few for %d query heads", bk_min, G);
     // the epilogue reuses the ring
     const size_t epi = ((size_t)3 * kWaves * 4 * RB + (size_t)kWaves * 4 * RB * 16 * p.v.nvb) * sizeof(float);
-    const size_t scr = scratch_bytes(RB, p.v.nqm, d);
+    const size_t scr = scratch_bytes(RB, p.v.nqm, p.v.nvb, d);
     const size_t ksch = (size_t)p.v.nqm * 4 * 8 * 4;
     // ring depth: the deepest that the workgroups resident per CU (set by registers) leave
     // room for, between 2 and 4 buffers per wave
@@ -745,6 +772,7 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
         1, std::min<int64_t>({slots / pairs, (tiles + kWaves - 1) / kWaves, (int64_t)(kMergeThreads / d) * kMergeRound}));
     a.wg_per_head = p.wg_per_head;
     a.part_ld = kPartHead + 16 * p.v.nvb;
+    p.qbuf_bytes = al256((size_t)n_seqs * cb->n_kv * (4 * RB * d + d) * sizeof(float));
     p.part_bytes = (size_t)n_seqs * cb->n_kv * p.wg_per_head * G * a.part_ld * sizeof(float);
     return AATC_OK;
 }
@@ -775,8 +803,11 @@ void profile_slot(hipEvent_t& a, hipEvent_t& b) {
 
 template <int RB, int NQM, int NVB, int D>
 int launch_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* blob, const uint8_t* cache,
-                  const int32_t* ids, const int64_t* lens, const uint16_t* q, float* part, float* out) {
+                  const int32_t* ids, const int64_t* lens, const uint16_t* q, float* qbuf, float* part, float* out) {
     const DecodeArgs& a = p.args;
+    hipLaunchKernelGGL((qprep_kernel<RB, D>), dim3(D / 16, a.n_kv, n_seqs), dim3(64), 0, st, blob, a.layer, a.n_kv, a.G,
+                       q, qbuf);
+    HIP_TRY(hipGetLastError());
     if (p.lds > 64 * 1024)
         HIP_TRY(hipFuncSetAttribute((const void*)decode_kernel<RB, NQM, NVB, D>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds));
@@ -784,7 +815,7 @@ int launch_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* blob
     profile_slot(e0, e1);
     if (e0) HIP_TRY(hipEventRecord(e0, st));
     hipLaunchKernelGGL((decode_kernel<RB, NQM, NVB, D>), dim3(p.wg_per_head, a.n_kv, n_seqs), dim3(256), p.lds, st,
-                       blob, cache, a, ids, lens, q, part);
+                       blob, cache, a, ids, lens, (const float*)qbuf, part);
     HIP_TRY(hipGetLastError());
     if (e1) HIP_TRY(hipEventRecord(e1, st));
     hipLaunchKernelGGL((merge_kernel<D>), dim3(a.n_kv, n_seqs, a.G), dim3(kMergeThreads), 0, st, blob, a.layer, a.n_kv,
@@ -842,7 +873,7 @@ extern "C" int aatc_decode_workspace_bytes(const aatc_codebook* cb, int32_t n_se
         Plan p;
         int rc = make_plan(cb, layer, n_seqs, max_len, p);
         if (rc) return rc;
-        worst = std::max(worst, p.part_bytes);
+        worst = std::max(worst, p.qbuf_bytes + p.part_bytes);
     }
     *bytes = worst;
     return AATC_OK;
@@ -865,9 +896,11 @@ extern "C" int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob
     Plan p;
     rc = make_plan(cb, layer, n_seqs, max_len, p);
     if (rc) return rc;
-    if (ws_bytes < p.part_bytes)
-        return set_error(AATC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, p.part_bytes);
-    float* part = (float*)workspace;  // [n_seqs][n_kv][wg][G][part_ld] partials
+    if (ws_bytes < p.qbuf_bytes + p.part_bytes)
+        return set_error(AATC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes,
+                         p.qbuf_bytes + p.part_bytes);
+    float* qbuf = (float*)workspace;                              // [n_seqs][n_kv][4 RB * d + d] q'' and maxima
+    float* part = (float*)((uint8_t*)workspace + p.qbuf_bytes);  // [n_seqs][n_kv][wg][G][part_ld] partials
     DecodeArgs& a = p.args;
     a.layer = layer;
     a.n_kv = cb->n_kv;
@@ -880,8 +913,8 @@ extern "C" int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob
 #define AATC_DECODE_CASE(rb_, nqm_, nvb_)                                                                    \
     if (p.v.rb == rb_ && p.v.nqm == nqm_ && p.v.nvb == nvb_)                                                 \
         return cb->d == 64                                                                                   \
-                   ? launch_decode<rb_, nqm_, nvb_, 64>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, part, out) \
-                   : launch_decode<rb_, nqm_, nvb_, 128>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, part, out);
+                   ? launch_decode<rb_, nqm_, nvb_, 64>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, qbuf, part, out) \
+                   : launch_decode<rb_, nqm_, nvb_, 128>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, qbuf, part, out);
     AATC_DECODE_CASE(1, 2, 4)
     AATC_DECODE_CASE(1, 2, 8)
     AATC_DECODE_CASE(1, 3, 8)
