@@ -221,13 +221,13 @@ int aatc_decode_workspace_bytes(const aatc_codebook* cb, int32_t n_seqs, int64_t
  * kv-head floor(h / G).  seq_ids [n_seqs] int32 and seq_lens [n_seqs] int64 are DEVICE
  * arrays (1 <= seq_lens[s] <= max_len <= max_tokens); max_len (host) sizes the grid.
  * q: device bf16 [n_seqs][H_q][d]; out: device float32 [n_seqs][H_q][d]; workspace:
- * device scratch of aatc_decode_workspace_bytes() bytes (256-byte aligned), zero-filled
- * once before its first use: it starts with a table of workgroup arrival counters that
- * every completed call leaves at zero, so one workspace serves any later sequence of
- * calls and shapes it is large enough for.  Calls that share a workspace must not
- * overlap in time (same stream, or ordered).  A call aborted by a device fault can leave
- * counters set: zero the workspace again before reusing it.  The counter table bounds
- * one call to about 16k (sequence, kv-head) pairs (CAPACITY beyond).
+ * device scratch of aatc_decode_workspace_bytes() bytes (256-byte aligned, no
+ * initialisation needed) for the transformed queries and the split partials.  Calls that
+ * share a workspace must not overlap in time (same stream, or ordered).  Three kernels run
+ * on `stream`: query transform, split decode over the packed tiles, merge + inverse
+ * transform ("KV Cache Compression Through the Lens of Transform Coding", Methodology;
+ * "Attention-Aware Transform Coding Guide", KLT section: q.k = (U_K^T q).(U_K^T k)).
+ * At most 65535 sequences per call (CAPACITY beyond).
  * Errors: INVALID_ARG, CAPACITY, WORKSPACE, HIP. */
 int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
                           int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
