@@ -67,13 +67,20 @@ constexpr float kP1 = 1.0f / 256.0f, kP2 = 1.0f / 65536.0f;  // probability digi
 constexpr float kPScale = 127.0f * 65536.0f;                  // p -> integer of three digits
 constexpr int kPartHead = 4;  // partial entries before the columns: max, sum, top-field sum, pad
 
+// the load instructions of one cache tile (stream_tile)
+struct TileLoads {
+    int n16, r4, r2, r1;
+};
+
 struct DecodeArgs {
     int layer, n_kv, G, n_seqs_cache;
     int64_t n_tiles_cap;
     int64_t max_len;
     int tile_bytes, wg_per_head, part_ld;
+    TileLoads tl;  // the load instructions of one tile
     // LDS carve-up (bytes): slot k of wave w's ring at (k * 4 + w) * buf_bytes; the
-    // prologue's scratch at off_scratch (in the last ring slot when early = 1)
+    // prologue's scratch at off_scratch, beside the ring (early = nbw: every slot streams
+    // from the start) or in its last nbw - early slots
     int nbw, buf_bytes, early, off_scratch, off_ksched;
 };
 
@@ -130,12 +137,37 @@ __device__ __forceinline__ float wave_sum(float x) {
 // loads carry the non-temporal hint (cache policy bit 1): the cache is read once per step,
 // and with the default policy these direct-to-LDS loads stream at about half the rate.
 constexpr int kStreamPolicy = 2;
-__device__ __forceinline__ void load_tile(const uint8_t* src, LDS_AS uint8_t* lds, int bytes, int lane) {
+template <int POLICY>
+__device__ __forceinline__ void load_tile_p(const uint8_t* src, LDS_AS uint8_t* lds, int bytes, int lane) {
     for (int off = 0; off < bytes; off += 1024) {
         const int o = off + 16 * lane;
-        if (o < bytes)
-            __builtin_amdgcn_global_load_lds((const void*)(src + o), (LDS_AS void*)(lds + off), 16, 0, kStreamPolicy);
+        if (o < bytes) __builtin_amdgcn_global_load_lds((const void*)(src + o), (LDS_AS void*)(lds + off), 16, 0, POLICY);
     }
+}
+__device__ __forceinline__ void load_tile(const uint8_t* src, LDS_AS uint8_t* lds, int bytes, int lane, int policy) {
+    if (policy == kStreamPolicy)
+        load_tile_p<kStreamPolicy>(src, lds, bytes, lane);
+    else
+        load_tile_p<0>(src, lds, bytes, lane);
+}
+
+// Stream one cache tile (64 token slots of B bits: 64 x B / 8 bytes, so every lane's share is
+// whole bytes) with all lanes active: n16 loads of 16 bytes per lane (1 KiB each), then the
+// lane share's remainder in 4-, 2- and 1-byte loads (r4, r2, r1 of them).  No per-lane
+// conditions: the issue path is a few scalar instructions per load.
+__device__ __forceinline__ void stream_tile(const uint8_t* src, LDS_AS uint8_t* lds, const TileLoads& tl, int lane) {
+    for (int k = 0; k < tl.n16; ++k)
+        __builtin_amdgcn_global_load_lds((const void*)(src + 1024 * k + 16 * lane), (LDS_AS void*)(lds + 1024 * k), 16, 0,
+                                         kStreamPolicy);
+    int off = 1024 * tl.n16;
+    for (int k = 0; k < tl.r4; ++k, off += 256)
+        __builtin_amdgcn_global_load_lds((const void*)(src + off + 4 * lane), (LDS_AS void*)(lds + off), 4, 0, kStreamPolicy);
+    if (tl.r2) {
+        __builtin_amdgcn_global_load_lds((const void*)(src + off + 2 * lane), (LDS_AS void*)(lds + off), 2, 0, kStreamPolicy);
+        off += 128;
+    }
+    if (tl.r1)
+        __builtin_amdgcn_global_load_lds((const void*)(src + off + lane), (LDS_AS void*)(lds + off), 1, 0, kStreamPolicy);
 }
 
 // three base-254 digits of x: x = d0 + d1 / 254 + d2 / 254^2 (+ rounding); each fits int8
@@ -163,55 +195,57 @@ __device__ __forceinline__ void split256(float x, int& a0, int& a1, int& a2) {
 
 // Registers per lane grow with the row blocks and value column blocks; the waves per SIMD
 // the allocation is sized for (the LDS plan matches it).
-constexpr int vgpr_estimate(int rb, int nqm, int nvb) { return rb * nvb * 4 + nqm * rb * 4 + 2 * nvb + rb * 20 + 56; }
-constexpr int waves_for(int rb, int nqm, int nvb) {
-    return vgpr_estimate(rb, nqm, nvb) <= 128 ? 4 : (vgpr_estimate(rb, nqm, nvb) <= 168 ? 3 : 2);
+// The key schedule (per score MFMA: four record-word offsets and four masks of this lane's
+// group) stays in registers when it is small.
+constexpr bool ksched_in_regs(int nqm) { return nqm <= 3; }
+constexpr int vgpr_estimate(int rb, int nqm, int nvb) {
+    return rb * nvb * 4 + nqm * rb * 4 + 2 * nvb + rb * 20 + 56 + (ksched_in_regs(nqm) ? 8 * nqm : 0);
 }
+constexpr int waves_for(int rb, int nqm, int nvb) { return vgpr_estimate(rb, nqm, nvb) <= 168 ? 3 : 2; }
 
-// bytes of the prologue's LDS scratch: q'' [4 RB][D] and block maxima [D / 16][16]; slots
-// [NQM * 64]; value columns [NVB][16]; staged operands [NQM][RB][64 lanes][16 B]; per-row
-// corrections [RB * 16]
-constexpr size_t scratch_bytes(int rb, int nqm, int nvb, int d) {
-    return ((size_t)4 * rb * d + d) * 4 + (size_t)nqm * 128 + (size_t)nvb * 64 + (size_t)nqm * rb * 1024 +
-           (size_t)rb * 64;
-}
+// bytes of the query preparation's output per (sequence, kv-head): the score A operands
+// [NQM][RB][64 lanes] (16 bytes each), then per (row block, head) a 32-byte lane record
+// (three float digit scales, three int score start values, two zero words)
+constexpr int qprep_bytes(int rb, int nqm) { return nqm * rb * 1024 + rb * 4 * 32; }
+// bytes of the decode prologue's LDS scratch: that output, then the value columns [NVB][16]
+constexpr int scratch_bytes(int rb, int nqm, int nvb) { return qprep_bytes(rb, nqm) + nvb * 64; }
 
 // ---------------------------------------------------------------------------------------
-// query preparation, one single-wave workgroup per (16-channel block, kv-head, sequence):
-// q' = U_K^T q for the block's channels and the kv-head's query heads on bf16 MFMAs (q is
-// bf16; U_K = hi + lo, channel-major; rows = channels, columns = heads),
+// query preparation, one workgroup of D / 16 waves per (kv-head, sequence).  Wave b forms
+// q' = U_K^T q for channels 16 b .. 16 b + 15 and the kv-head's query heads on bf16 MFMAs
+// (q is bf16; U_K = hi + lo, channel-major; rows = channels, columns = heads),
 // q'' = q' * step_K * log2(e) / sqrt(d), and per head the block's largest slot value
-// |q''[j]| max over the fields of j of 2^(shift - pos).  Out: qbuf[(z, h)] = [4 RB heads][D]
-// q'' then [D / 16 blocks][16 heads] maxima.  The workgroup also streams its block's rows of
-// U_V^T (and the first one the decode prologue's tables) through LDS, so that the merge and
-// the decode prologue find them in the device cache.
+// |q''[j]| max over the fields of j of 2^(shift - pos).  Then the workgroup writes the
+// decode kernel's score operands: key field (chan, shift, pos) of score slot k gets
+// q''[chan] * 2^shift / 2^pos, scaled per head so that the largest slot is 127, split into
+// three int8 digits (rows 4 head + digit of the A operand); and per (row block, head) the
+// digit scales and 128 x the digit sums of slots whose field ends at bit 7 (the score
+// accumulator's start value, which undoes the -128 those fields read as).  It also streams
+// U_V^T (the merge's) and the decode tables through the device cache.
 // ---------------------------------------------------------------------------------------
-template <int RB, int D>
-__global__ __launch_bounds__(64) void qprep_kernel(const DevHead* __restrict__ blob, int layer, int n_kv, int G,
-                                                   const uint16_t* __restrict__ q, float* __restrict__ qbuf) {
+template <int RB, int NQM, int D>
+__global__ __launch_bounds__(D * 4) void qprep_kernel(const DevHead* __restrict__ blob, int layer, int n_kv, int G,
+                                                      const uint16_t* __restrict__ q, uint8_t* __restrict__ qbuf) {
     typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     constexpr int GM = 4 * RB;
     constexpr int KS = D / 32;  // k-steps over the input dimension
-    __shared__ __attribute__((aligned(16))) uint8_t warm[16 * D * 4];
-    const int cb = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
-    const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
+    constexpr int NB = D / 16;  // 16-channel blocks, one per wave
+    constexpr int NT = NB * 64;
+    __shared__ __attribute__((aligned(16))) float qf[GM][D];  // q''
+    __shared__ float bmax[NB][16];                            // per block and head: largest slot value
+    __shared__ int corr[RB * 16];                             // per row: digit sums of bit-7 slots
+    const int h = blockIdx.x, z = blockIdx.y;
+    const int tid = threadIdx.x, cb = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
     const DevHead& H = blob[layer * n_kv + h];
     const int64_t zh = (int64_t)z * n_kv + h;
-    float* out = qbuf + zh * (GM * D + D);
-    // U_V^T rows 16 cb .. 16 cb + 15 into LDS (never read: they only pass through the cache)
-    for (int off = 0; off < 16 * D * 4; off += 1024)
-        __builtin_amdgcn_global_load_lds((const void*)((const uint8_t*)(H.UVt + 16 * cb * D) + off + 16 * lane),
-                                         (__attribute__((address_space(3))) void*)(warm + off), 16, 0, 0);
-    if (cb == 0 && z == 0) {  // the decode prologue's tables likewise
-        const uint8_t* tabs[3] = {(const uint8_t*)&H.kq_slot[0][0][0], (const uint8_t*)&H.kq_sched[0][0][0],
-                                  (const uint8_t*)&H.vb_col[0][0]};
-        const int sizes[3] = {(int)sizeof(H.kq_slot), (int)sizeof(H.kq_sched), (int)sizeof(H.vb_col)};
-        for (int k = 0; k < 3; ++k)
-            for (int off = 0; off < sizes[k] && off < 16 * D * 4; off += 1024)
-                if (off + 16 * lane < sizes[k])
-                    __builtin_amdgcn_global_load_lds((const void*)(tabs[k] + off + 16 * lane),
-                                                     (__attribute__((address_space(3))) void*)(warm + off), 16, 0, 0);
+    uint8_t* out = qbuf + zh * qprep_bytes(RB, NQM);
+    // the slot descriptors of this thread's first operand item (see below)
+    typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+    u16x4 slots0 = u16x4{0xFFFF, 0xFFFF, 0xFFFF, 0xFFFF};
+    if (tid < NQM * RB * 64) {
+        const int iw = (tid >> 2) & 3, gg = (tid >> 4) & 3, m = (tid >> 6) / RB;
+        slots0 = *(const u16x4*)&H.kq_slot[m][gg][4 * iw];
     }
     bf16x8 ah[KS], al[KS], bq[KS];
     const int j = 16 * cb + c;  // A row: channel
@@ -219,15 +253,34 @@ __global__ __launch_bounds__(64) void qprep_kernel(const DevHead* __restrict__ b
     for (int ks = 0; ks < KS; ++ks) {
         ah[ks] = *(const bf16x8*)(H.UKt_hi + j * D + 32 * ks + 8 * g);
         al[ks] = *(const bf16x8*)(H.UKt_lo + j * D + 32 * ks + 8 * g);
-        bq[ks] = c < G ? *(const bf16x8*)(q + (zh * G + c) * D + 32 * ks + 8 * g) : bf16x8{};  // B column: head c
+        bq[ks] = *(const bf16x8*)(q + (zh * G + min(c, G - 1)) * D + 32 * ks + 8 * g);  // B column: head c
     }
     const int j0 = 16 * cb + 4 * g;  // output rows of this lane
     const f4 stv = *(const f4*)(H.stepK + j0), fmv = *(const f4*)(H.kq_fmax + j0);
     f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bq[ks], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], bq[ks], acc, 0, 0, 0);
+        const bf16x8 b = c < G ? bq[ks] : bf16x8{};  // heads past G: zero columns
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], b, acc, 0, 0, 0);
+    }
+    // U_V^T (the merge's) and the decode tables pass through the device cache: loads into
+    // registers that are only waited for at the end (issued once this thread's operand
+    // loads are used, so that they delay nothing)
+    constexpr int NWV = 16 * D * 4 / 1024, KSB = NQM * 128, VCB = (int)sizeof(H.vb_col);
+    constexpr int NWT = (KSB + 1023) / 1024 + (VCB + 1023) / 1024;
+    u32x4 wv[NWV + NWT];
+    {
+        const uint8_t* uv = (const uint8_t*)(H.UVt + 16 * cb * D);
+#pragma unroll
+        for (int k = 0; k < NWV; ++k) wv[k] = *(const u32x4*)(uv + 1024 * k + 16 * lane);
+        const uint8_t* ks = (const uint8_t*)&H.kq_sched[0][0][0];
+        const uint8_t* vc = (const uint8_t*)&H.vb_col[0][0];
+        int k = NWV;
+#pragma unroll
+        for (int off = 0; off < KSB; off += 1024, ++k) wv[k] = *(const u32x4*)(ks + min(off + 16 * lane, KSB - 16));
+#pragma unroll
+        for (int off = 0; off < VCB; off += 1024, ++k) wv[k] = *(const u32x4*)(vc + min(off + 16 * lane, VCB - 16));
     }
     const float qscale = kLog2e / sqrtf((float)D);
     f4 v;
@@ -237,17 +290,70 @@ __global__ __launch_bounds__(64) void qprep_kernel(const DevHead* __restrict__ b
         v[e] = acc[e] * stv[e] * qscale;  // step_K is 0 for uncoded channels
         mag = fmaxf(mag, fabsf(v[e]) * fmv[e]);
     }
-    if (c < GM) *(f4*)(out + c * D + j0) = v;
+    if (c < GM) *(f4*)&qf[c][j0] = v;
     mag = fmaxf(mag, __shfl_xor(mag, 16));
     mag = fmaxf(mag, __shfl_xor(mag, 32));
-    if (g == 0) out[GM * D + 16 * cb + c] = mag;
-    wait_all();
+    if (g == 0) bmax[cb][c] = mag;
+    if (tid < RB * 16) corr[tid] = 0;
+    lds_barrier();  // (LDS only: the cache-warming loads stay in flight)
+    // operands: thread (m, rb, lane group gg, dword iw, head hh4) forms the three digit words
+    // of its four slots (rows 4 hh4 + 0..2; row 3 stays zero)
+    for (int i = tid; i < NQM * RB * 64; i += NT) {
+        const int hh4 = i & 3, iw = (i >> 2) & 3, gg = (i >> 4) & 3, rb = (i >> 6) % RB, m = (i >> 6) / RB;
+        const int hh = 4 * rb + hh4;
+        float mx = 0.0f;
+#pragma unroll
+        for (int bk = 0; bk < NB; ++bk) mx = fmaxf(mx, bmax[bk][hh]);
+        const float sc = hh < G && mx > 0.0f ? 127.0f / mx : 0.0f;
+        uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
+        int f0 = 0, f1 = 0, f2 = 0;
+        const u16x4 sls = i == tid ? slots0 : *(const u16x4*)&H.kq_slot[m][gg][4 * iw];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t sl = sls[e];
+            if (sl != 0xFFFFu) {
+                const int sh = (int)((sl >> 8) & 7) - (int)((sl >> 11) & 7);
+                float d0, d1, d2;
+                digits254(qf[hh][sl & 255] * __builtin_amdgcn_ldexpf(sc, sh), d0, d1, d2);
+                w0 |= ((uint32_t)(int)d0 & 0xFFu) << (8 * e);
+                w1 |= ((uint32_t)(int)d1 & 0xFFu) << (8 * e);
+                w2 |= ((uint32_t)(int)d2 & 0xFFu) << (8 * e);
+                if (sl & 0x4000u) f0 += (int)d0, f1 += (int)d1, f2 += (int)d2;
+            }
+        }
+        // dword iw of lane (gg, row) in operand [m][rb], rows 4 hh4 + digit
+        uint32_t* dst = (uint32_t*)(out + ((m * RB + rb) * 64 + 16 * gg + 4 * hh4) * 16) + iw;
+        dst[0] = w0;
+        dst[4] = w1;
+        dst[8] = w2;
+        dst[12] = 0u;
+        if (f0 | f1 | f2) {
+            atomicAdd(&corr[rb * 16 + 4 * hh4], f0);
+            atomicAdd(&corr[rb * 16 + 4 * hh4 + 1], f1);
+            atomicAdd(&corr[rb * 16 + 4 * hh4 + 2], f2);
+        }
+    }
+    lds_barrier();
+    if (tid < RB * 4) {  // lane record of (row block, head)
+        const int rb = tid >> 2, g4 = tid & 3, hh = 4 * rb + g4;
+        float mx = 0.0f;
+#pragma unroll
+        for (int bk = 0; bk < NB; ++bk) mx = fmaxf(mx, bmax[bk][hh]);
+        mx *= 1.0f / 127.0f;
+        const int* cr = &corr[16 * rb + 4 * g4];
+        u32x4* rec = (u32x4*)(out + NQM * RB * 1024 + 32 * tid);
+        rec[0] = u32x4{__builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, mx * kQ1),
+                       __builtin_bit_cast(uint32_t, mx * kQ2), (uint32_t)(128 * cr[0])};
+        rec[1] = u32x4{(uint32_t)(128 * cr[1]), (uint32_t)(128 * cr[2]), 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < NWV + NWT; ++k) asm volatile("" ::"v"(wv[k]));
 }
 
 template <int RB, int NQM, int NVB, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel(
     const DevHead* __restrict__ blob, const uint8_t* __restrict__ cache, DecodeArgs a,
-    const int32_t* __restrict__ seq_ids, const int64_t* __restrict__ seq_lens, const float* __restrict__ qbuf,
+    const int32_t* __restrict__ seq_ids, const int64_t* __restrict__ seq_lens, const uint8_t* __restrict__ qbuf,
     float* __restrict__ part) {
     constexpr int PST = 64;          // bytes per row of the probability operand (64 tokens)
     constexpr int GM = 4 * RB;       // query heads the operands have room for
@@ -260,6 +366,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
     const int G = a.G, TB = a.tile_bytes, BB = a.buf_bytes;
     const int64_t zh = (int64_t)z * a.n_kv + h;
 
+    // the value block's offset in a tile, read (as a scalar load) before any copy is issued:
+    // a vector load after them would make the compiler wait for every copy in flight
+    const uint32_t vblock = 8u * (uint32_t)H.BK;
+    asm volatile("" ::"s"(vblock));
     // ---- sequence geometry (device arguments clamped: no read outside the cache)
     const int seq = seq_ids[z];
     int64_t len = min(min(seq_lens[z], a.max_len), a.n_tiles_cap * kTile);
@@ -271,104 +381,70 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
     // neighbouring tiles.  Ring slot k of this wave: ring + k * RS.
     const int64_t stride = (int64_t)kWaves * a.wg_per_head;
     const int NBW = a.nbw;
-    const int nl = (TB + 1023) >> 10;  // load instructions per tile
+    const TileLoads tl = a.tl;
+    const int nl = tl.n16 + tl.r4 + tl.r2 + tl.r1;  // load instructions per tile
     LDS_AS uint8_t* ring = sm + w * BB;
     const int RS = kWaves * BB;  // bytes between a wave's ring slots
     int64_t t = (int64_t)wgi * kWaves + w;
-    // ---- prologue: the score operands of this (sequence, kv-head).  Key field (chan,
-    // shift, pos) of score slot k gets q''[chan] * 2^shift / 2^pos, scaled per head so that
-    // the largest slot is 127, split into three int8 digits (rows 4 head + digit).  The
-    // tables arrive by direct global->LDS copies issued before the first tiles' copies, so
-    // waiting for them leaves the tiles in flight (the scratch is the ring's last slot, or
-    // the ring's start with the tiles issued after the prologue when it does not fit).
-    constexpr int QN = GM * D + D;  // floats of q'' and the per-block maxima
-    LDS_AS float* qf = (LDS_AS float*)(sm + a.off_scratch);        // [GM][D] q'', [D / 16][16] maxima
-    LDS_AS uint16_t* kmap = (LDS_AS uint16_t*)(qf + QN);             // [NQM * 64] slots
-    LDS_AS uint32_t* vcol = (LDS_AS uint32_t*)(kmap + NQM * 64);     // [NVB][16] value columns
-    LDS_AS v4i* astage = (LDS_AS v4i*)(vcol + NVB * 16);             // [NQM][RB][64] operands
-    LDS_AS int* corr = (LDS_AS int*)(astage + NQM * RB * 64);        // [RB * 16] rows: digits of bit-7 slots
-    LDS_AS u32x4* ksched = (LDS_AS u32x4*)(sm + a.off_ksched);      // [NQM][4][2]: offsets, masks
-    if (tid < RB * 16) corr[tid] = 0;
+    // ---- prologue: the loop's register operands - the score A operands and lane records of
+    // the query preparation, this lane group's key schedule, this lane's value columns -
+    // arrive by direct global->LDS copies issued before the first tiles' copies, so waiting
+    // for them leaves the tiles in flight.  The scratch has room of its own beside the ring
+    // when it fits (every ring slot streams from the start), else it takes the ring's last
+    // slots, whose tiles are issued once the operands are in registers.
+    constexpr int QB = qprep_bytes(RB, NQM);
+    LDS_AS uint8_t* scr = sm + a.off_scratch;                   // [QB] operands and records
+    LDS_AS uint32_t* vcol = (LDS_AS uint32_t*)(scr + QB);       // [NVB][16] value columns
+    LDS_AS u32x4* ksched = (LDS_AS u32x4*)(sm + a.off_ksched);  // [NQM][4][2]: offsets, masks
     {
-        // wave 0: q'' and maxima; wave 1: slots; wave 2: value columns; wave 3: key schedule
-        const uint8_t* src = w == 0   ? (const uint8_t*)(qbuf + zh * QN)
-                             : w == 1 ? (const uint8_t*)&H.kq_slot[0][0][0]
-                             : w == 2 ? (const uint8_t*)&H.vb_col[0][0]
-                                      : (const uint8_t*)&H.kq_sched[0][0][0];
-        LDS_AS uint8_t* dst = w == 0 ? (LDS_AS uint8_t*)qf
-                              : w == 1 ? (LDS_AS uint8_t*)kmap
-                              : w == 2 ? (LDS_AS uint8_t*)vcol
-                                       : (LDS_AS uint8_t*)ksched;
-        const int bytes = w == 0 ? QN * 4 : w == 1 ? NQM * 128 : w == 2 ? NVB * 64 : NQM * 128;
-        load_tile(src, dst, bytes, lane);
+        const uint8_t* qz = qbuf + zh * QB;
+        for (int off = 1024 * w; off < QB; off += 1024 * kWaves)
+            if (off + 16 * lane < QB)
+                __builtin_amdgcn_global_load_lds((const void*)(qz + off + 16 * lane), (LDS_AS void*)(scr + off), 16, 0, 0);
+        if (w == kWaves - 1) load_tile((const uint8_t*)&H.vb_col[0][0], (LDS_AS uint8_t*)vcol, NVB * 64, lane, 0);
+        if (w == kWaves - 2) load_tile((const uint8_t*)&H.kq_sched[0][0][0], (LDS_AS uint8_t*)ksched, NQM * 128, lane, 0);
     }
-    int n_early = 0;  // tiles this wave has in flight
-    if (a.early)
-        for (; n_early < NBW - 1 && t + stride * n_early < n_tiles; ++n_early)
-            load_tile(tiles + (t + stride * n_early) * TB, ring + n_early * RS, TB, lane);
-    wait_vm(nl * n_early);  // this wave's table copy has landed
-    lds_barrier();
-    // operands: thread (m, rb, lane group gg, dword iw, head hh4) forms the three digit words
-    // of its four slots (rows 4 hh4 + 0..2; row 3 stays zero)
-    for (int i = tid; i < NQM * RB * 64; i += 256) {
-        const int hh4 = i & 3, iw = (i >> 2) & 3, gg = (i >> 4) & 3, rb = (i >> 6) % RB, m = (i >> 6) / RB;
-        const int hh = 4 * rb + hh4;
-        float mx = 0.0f;
-#pragma unroll
-        for (int bk = 0; bk < D / 16; ++bk) mx = fmaxf(mx, qf[GM * D + 16 * bk + hh]);
-        const float sc = hh < G && mx > 0.0f ? 127.0f / mx : 0.0f;
-        uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
-        int f0 = 0, f1 = 0, f2 = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t sl = kmap[(m * 4 + gg) * 16 + 4 * iw + e];
-            if (sl != 0xFFFFu) {
-                const int sh = (int)((sl >> 8) & 7) - (int)((sl >> 11) & 7);
-                float d0, d1, d2;
-                digits254(qf[hh * D + (sl & 255)] * __builtin_amdgcn_ldexpf(sc, sh), d0, d1, d2);
-                w0 |= ((uint32_t)(int)d0 & 0xFFu) << (8 * e);
-                w1 |= ((uint32_t)(int)d1 & 0xFFu) << (8 * e);
-                w2 |= ((uint32_t)(int)d2 & 0xFFu) << (8 * e);
-                if (sl & 0x4000u) f0 += (int)d0, f1 += (int)d1, f2 += (int)d2;
-            }
-        }
-        // dword iw of lane (gg, row) in operand [m][rb], rows 4 hh4 + digit
-        LDS_AS uint32_t* dst = (LDS_AS uint32_t*)(astage + (m * RB + rb) * 64 + 16 * gg + 4 * hh4) + iw;
-        dst[0] = w0;
-        dst[4] = w1;
-        dst[8] = w2;
-        dst[12] = 0u;
-        if (f0 | f1 | f2) {
-            atomicAdd((int*)&corr[rb * 16 + 4 * hh4], f0);
-            atomicAdd((int*)&corr[rb * 16 + 4 * hh4 + 1], f1);
-            atomicAdd((int*)&corr[rb * 16 + 4 * hh4 + 2], f2);
-        }
-    }
-    lds_barrier();
+    int issued = 0;  // tiles of this wave whose loads have been issued; tile number k uses ring slot k % NBW
+    for (; issued < a.early && t + stride * issued < n_tiles; ++issued)
+        stream_tile(tiles + (t + stride * issued) * TB, ring + issued * RS, tl, lane);
+    wait_vm(nl * issued);  // this wave's copies have landed
+    lds_barrier();         // ... and every wave's
     uint32_t voff[NVB], vmask[NVB];  // value columns of this lane: tile offset of its plane slice, mask
 #pragma unroll
     for (int cb = 0; cb < NVB; ++cb) {
         const uint32_t v = vcol[cb * 16 + c];
-        voff[cb] = 8u * (uint32_t)H.BK + (v & 0xFFFFu) + 16u * (uint32_t)g;
+        voff[cb] = vblock + (v & 0xFFFFu) + 16u * (uint32_t)g;
         vmask[cb] = 0x01010101u * (v >> 16);
     }
     v4i Aq[NQM][RB];  // score A operands (query digits), resident for the whole loop
 #pragma unroll
     for (int m = 0; m < NQM; ++m)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) Aq[m][rb] = astage[(m * RB + rb) * 64 + lane];
+        for (int rb = 0; rb < RB; ++rb) Aq[m][rb] = ((const LDS_AS v4i*)scr)[(m * RB + rb) * 64 + lane];
+    // key schedule of this lane group: tile offsets of the four record words of tokens
+    // 4c..4c+3 (registers), or read per tile from LDS
+    constexpr bool KREG = ksched_in_regs(NQM);
+    constexpr int KR = KREG ? NQM : 1;
+    u32x4 koffr[KR], kmaskr[KR];
+    if constexpr (KREG) {
+#pragma unroll
+        for (int m = 0; m < NQM; ++m) {
+            koffr[m] = ksched[(m * 4 + g) * 2] + (uint32_t)(16 * c);
+            kmaskr[m] = ksched[(m * 4 + g) * 2 + 1];
+        }
+    }
     float qs[RB][3];  // digit scales of this lane's query head
     v4i sinit[RB];    // score accumulator start: 128 x the digits multiplying bit-7 fields
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        float mx = 0.0f;
-#pragma unroll
-        for (int bk = 0; bk < D / 16; ++bk) mx = fmaxf(mx, qf[GM * D + 16 * bk + 4 * rb + g]);
-        mx *= 1.0f / 127.0f;
-        qs[rb][0] = mx;
-        qs[rb][1] = mx * kQ1;
-        qs[rb][2] = mx * kQ2;
-        sinit[rb] = v4i{128 * corr[16 * rb + 4 * g], 128 * corr[16 * rb + 4 * g + 1], 128 * corr[16 * rb + 4 * g + 2], 0};
+        const LDS_AS u32x4* rec = (const LDS_AS u32x4*)(scr + NQM * RB * 1024 + 32 * (4 * rb + g));
+        const u32x4 r0 = rec[0], r1 = rec[1];
+        // (through scalars: a bit cast of a vector element reads element 0 with this compiler)
+        const uint32_t q0 = r0[0], q1 = r0[1], q2 = r0[2];
+        qs[rb][0] = __uint_as_float(q0);
+        qs[rb][1] = __uint_as_float(q1);
+        qs[rb][2] = __uint_as_float(q2);
+        sinit[rb] = v4i{(int)r0[3], (int)r1[0], (int)r1[1], 0};
     }
     // the operands are in registers and every prologue read has completed: inside the loop
     // the only vector memory operations are this wave's tile loads
@@ -379,11 +455,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
 #pragma unroll
     for (int cb = 0; cb < NVB; ++cb) asm volatile("" ::"v"(voff[cb]), "v"(vmask[cb]));
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(qs[rb][0]), "v"(sinit[rb]));
-    lds_barrier();  // the scratch is free for the ring
-    if (!a.early)
-        for (int k = 0; k < NBW - 1 && t + stride * k < n_tiles; ++k)
-            load_tile(tiles + (t + stride * k) * TB, ring + k * RS, TB, lane);
+    for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(qs[rb][0]), "v"(qs[rb][1]), "v"(qs[rb][2]), "v"(sinit[rb]));
+    if constexpr (KREG) {
+#pragma unroll
+        for (int m = 0; m < NQM; ++m) asm volatile("" ::"v"(koffr[m]), "v"(kmaskr[m]));
+    }
+    if (a.early < NBW) {  // the scratch was in the ring's last slots: stream them now
+        lds_barrier();
+        for (; issued < NBW && t + stride * issued < n_tiles; ++issued)
+            stream_tile(tiles + (t + stride * issued) * TB, ring + issued * RS, tl, lane);
+    }
 
     // int32 sums of P digits x value bytes, relative to the reference max mref, and the
     // digit sums of this lane's probabilities (the row sums that undo the -128 of top
@@ -404,15 +485,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
     // ---- this wave's tiles: the ring keeps up to NBW - 1 of them in flight; the wave
     // waits on its own load count
     int slot = 0;
-    for (; t < n_tiles; t += stride) {
-        // tile t has landed once only the later tiles' loads may be outstanding; this wave's
-        // LDS reads of the slot refilled next are done
-        wait_vm(nl * (int)min((int64_t)NBW - 2, (n_tiles - 1 - t) / stride));
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        const int64_t tn = t + stride * (NBW - 1);
-        if (tn < n_tiles) load_tile(tiles + tn * TB, ring + (slot == 0 ? NBW - 1 : slot - 1) * RS, TB, lane);
+    for (int done = 0; t < n_tiles; t += stride, ++done) {
+        // tile t (this wave's tile number done) has landed once only the later tiles' loads
+        // are outstanding
+        wait_vm(nl * (issued - done - 1));
         LDS_AS uint8_t* curb = ring + slot * RS;
-        slot = slot + 1 == NBW ? 0 : slot + 1;
         const int valid = (int)min((int64_t)kTile, len - t * kTile);
 
         // ---------------- scores: token group tg, lane (g, c) -> token 4c + tg.  One 16-byte
@@ -423,10 +500,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
         for (int tg = 0; tg < 4; ++tg)
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) S[tg][rb] = sinit[rb];
-        const LDS_AS uint8_t* kbase = curb + 16 * c;  // record word 0 of tokens 4c..4c+3
 #pragma unroll
         for (int m = 0; m < NQM; ++m) {
-            const u32x4 koff = ksched[(m * 4 + g) * 2], kmask = ksched[(m * 4 + g) * 2 + 1];
+            const LDS_AS uint8_t* kbase = KREG ? curb : curb + 16 * c;  // record word 0 of tokens 4c..4c+3
+            u32x4 koff, kmask;
+            if constexpr (KREG) {
+                koff = koffr[m];
+                kmask = kmaskr[m];
+            } else {
+                koff = ksched[(m * 4 + g) * 2];
+                kmask = ksched[(m * 4 + g) * 2 + 1];
+            }
             u32x4 x[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) x[i] = *(const LDS_AS u32x4*)(kbase + koff[i]);
@@ -441,27 +525,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
         }
         // lane (g, c) holds head 4rb+g, tokens 4c..4c+3, digit rows 0..2 (rows of heads
         // >= G have zero operands and stay harmless)
-        float s[RB][4], tmx[RB];
-        bool need = false;
+        float s[RB][4], lmx[RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            float mx = -INFINITY;
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int tg = 0; tg < 4; ++tg) {
+            for (int tg = 0; tg < 4; ++tg)
                 s[rb][tg] = (float)S[tg][rb][0] * qs[rb][0] + (float)S[tg][rb][1] * qs[rb][1] +
                             (float)S[tg][rb][2] * qs[rb][2];
-                if (valid < kTile) s[rb][tg] = 4 * c + tg < valid ? s[rb][tg] : -INFINITY;
-                mx = fmaxf(mx, s[rb][tg]);
-            }
-            tmx[rb] = row16_max(mx);
-            if (tmx[rb] > mref[rb]) need = true;
+        if (valid < kTile) {  // the sequence's last tile: slots past its end score -inf
+            asm volatile("");  // (a real branch: only one tile per sequence takes it)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int tg = 0; tg < 4; ++tg) s[rb][tg] = 4 * c + tg < valid ? s[rb][tg] : -INFINITY;
         }
-        if (__any(need)) {
+        bool need = false;  // some score of this lane passed its head's reference max
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            lmx[rb] = fmaxf(fmaxf(s[rb][0], s[rb][1]), fmaxf(s[rb][2], s[rb][3]));
+            need = need || lmx[rb] > mref[rb];
+        }
+        if (done == 0) {
+            // the wave's first tile (it has a valid slot): the references start at its maxima,
+            // the sums are still zero
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) mref[rb] = row16_max(lmx[rb]) + kHeadroom;
+        } else if (__any(need)) {
+            asm volatile("");  // (a real branch: rescales are rare)
             // raise the reference of heads whose tile max passed it and rescale their sums
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
-                const float nref = tmx[rb] > mref[rb] ? tmx[rb] + kHeadroom : mref[rb];
-                const float al = exp2f(mref[rb] - nref);
+                const float tmx = row16_max(lmx[rb]);
+                const float nref = tmx > mref[rb] ? tmx + kHeadroom : mref[rb];
+                const float al = __builtin_amdgcn_exp2f(mref[rb] - nref);
                 lsum[rb] *= al;
                 mref[rb] = nref;
 #pragma unroll
@@ -510,63 +606,73 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
 
         // ---------------- values: column c of block cb = one field; its B operand is the
         // lane's 16 tokens of the field's byte plane under the field mask
+        u32x4 xv[NVB];
+#pragma unroll
+        for (int cb = 0; cb < NVB; ++cb) xv[cb] = *(const LDS_AS u32x4*)(curb + voff[cb]);
 #pragma unroll
         for (int cb = 0; cb < NVB; ++cb) {
-            const u32x4 x = *(const LDS_AS u32x4*)(curb + voff[cb]);
+            const u32x4 x = xv[cb];
             const v4i B = v4i{(int)(x[0] & vmask[cb]), (int)(x[1] & vmask[cb]), (int)(x[2] & vmask[cb]),
                               (int)(x[3] & vmask[cb])};
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
                 acc_i[rb][cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ap[rb], B, acc_i[rb][cb], 0, 0, 0);
         }
+        // the slot streams the tile NBW ahead once this wave's reads of it are done
+        const int64_t tn = t + stride * NBW;
+        if (tn < n_tiles) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            stream_tile(tiles + tn * TB, curb, tl, lane);
+            ++issued;
+        }
+        slot = slot + 1 == NBW ? 0 : slot + 1;
     }
 
-    // ---------------- epilogue: the four waves' results meet in LDS (ring reused).  Per
-    // wave and head: reference max, sum, 128 x the probability digit sum / 127, and per
-    // value column the accumulator / 127 (= sum of p x stored byte).
+    // ---------------- epilogue: the four waves' results meet in LDS (ring reused), laid out
+    // like the partial: per wave and head [reference max, sum, 128 x probability digit sum
+    // / 127, 0, columns: accumulator / 127 = sum of p x stored byte].  Per head the
+    // workgroup's reference is the largest of the waves', each wave weighted by 2^(m - M).
+    constexpr int PL = kPartHead + 16 * NVB;  // floats per partial and head
     wait_all();
     lds_barrier();
-    const int ncol = 16 * H.nvb;
-    LDS_AS float* wm = (LDS_AS float*)sm;     // [4 waves][GM] reference maxima
-    LDS_AS float* wl = wm + kWaves * GM;      // [4 waves][GM] sums
-    LDS_AS float* wo = wl + kWaves * GM;      // [4 waves][GM] top-field corrections
-    LDS_AS float* wa = wo + kWaves * GM;      // [4 waves][GM][16 NVB] columns
+    LDS_AS float* wx = (LDS_AS float*)sm;   // [4 waves][GM][PL]
+    LDS_AS float* ew = wx + kWaves * GM * PL;  // [4 waves][GM] weights, then [GM] maxima
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
+        LDS_AS float* o = wx + (w * GM + 4 * rb + g) * PL;
         const float ls = row16_sum(lsum[rb]);
         const float os = row16_sum(combine256(ones[rb][0], ones[rb][1], ones[rb][2]));
         if (c == 0) {
-            wm[w * GM + 4 * rb + g] = mref[rb];
-            wl[w * GM + 4 * rb + g] = ls;
-            wo[w * GM + 4 * rb + g] = os * (128.0f / 127.0f);
+            o[0] = mref[rb];
+            o[1] = ls;
+            o[2] = os * (128.0f / 127.0f);
+            o[3] = 0.0f;
         }
 #pragma unroll
         for (int cb = 0; cb < NVB; ++cb)
-            wa[(w * GM + 4 * rb + g) * 16 * NVB + 16 * cb + c] =
-                combine256(acc_i[rb][cb][0], acc_i[rb][cb][1], acc_i[rb][cb][2]) * (1.0f / 127.0f);
+            o[kPartHead + 16 * cb + c] = combine256(acc_i[rb][cb][0], acc_i[rb][cb][1], acc_i[rb][cb][2]) * (1.0f / 127.0f);
     }
     lds_barrier();
-    const int PL = a.part_ld;
+    if (tid < GM) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, wx[(ww * GM + tid) * PL]);
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            const float m = wx[(ww * GM + tid) * PL];
+            ew[ww * GM + tid] = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+        }
+        ew[kWaves * GM + tid] = M;
+    }
+    lds_barrier();
     float* pout = part + (zh * a.wg_per_head + wgi) * G * PL;
     for (int i = tid; i < G * PL; i += 256) {
         const int hh = i / PL, col = i - hh * PL;
-        float M = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, wm[ww * GM + hh]);
-        float v = M;
+        float v = ew[kWaves * GM + hh];
         if (col > 0) {
             v = 0.0f;
 #pragma unroll
-            for (int ww = 0; ww < kWaves; ++ww) {
-                const float m = wm[ww * GM + hh];
-                const float e = m == -INFINITY ? 0.0f : exp2f(m - M);
-                const float x = col == 1 ? wl[ww * GM + hh]
-                                         : (col == 2 ? wo[ww * GM + hh]
-                                                     : (col >= kPartHead && col - kPartHead < ncol
-                                                            ? wa[(ww * GM + hh) * 16 * NVB + col - kPartHead]
-                                                            : 0.0f));
-                v = fmaf(e, x, v);
-            }
+            for (int ww = 0; ww < kWaves; ++ww) v = fmaf(ew[ww * GM + hh], wx[(ww * GM + hh) * PL + col], v);
         }
         pout[i] = v;
     }
@@ -738,6 +844,13 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     DecodeArgs& a = p.args;
     a.G = G;
     a.tile_bytes = 8 * cb->total_bits;
+    {
+        const int lane_bytes = cb->total_bits / 8;  // a multiple of 8 bits: whole bytes per lane
+        a.tl.n16 = lane_bytes / 16;
+        a.tl.r4 = (lane_bytes % 16) / 4;
+        a.tl.r2 = (lane_bytes % 4) / 2;
+        a.tl.r1 = lane_bytes % 2;
+    }
     a.buf_bytes = (int)al16(a.tile_bytes);
     // the probability operand (RB KiB) overwrites the tile's key block (8 B_K bytes)
     int bk_min = 1 << 30;
@@ -745,21 +858,29 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     if (RB * 1024 > 8 * bk_min)
         return set_error(AATC_ERR_UNSUPPORTED, "%d key bits per token are too few for %d query heads", bk_min, G);
     // the epilogue reuses the ring
-    const size_t epi = ((size_t)3 * kWaves * 4 * RB + (size_t)kWaves * 4 * RB * 16 * p.v.nvb) * sizeof(float);
-    const size_t scr = scratch_bytes(RB, p.v.nqm, p.v.nvb, d);
+    const size_t epi = ((size_t)kWaves * 4 * RB * (kPartHead + 16 * p.v.nvb) + (size_t)(kWaves + 1) * 4 * RB) * sizeof(float);
+    const size_t scr = al16((size_t)scratch_bytes(RB, p.v.nqm, p.v.nvb));
     const size_t ksch = (size_t)p.v.nqm * 4 * 8 * 4;
+    const size_t group = (size_t)kWaves * a.buf_bytes;  // one ring slot of every wave
     // ring depth: the deepest that the workgroups resident per CU (set by registers) leave
-    // room for, between 2 and 4 buffers per wave
+    // room for beside the prologue's scratch, between 2 and 4 buffers per wave
     const int wgs = waves_for(p.v.rb, p.v.nqm, p.v.nvb);
     const size_t budget = (size_t)(160 * 1024) / wgs - ksch - 64;
     a.nbw = 2;
-    while (a.nbw < 4 && (size_t)kWaves * (a.nbw + 1) * a.buf_bytes <= budget) ++a.nbw;
-    const size_t ring = (size_t)kWaves * a.nbw * a.buf_bytes;
-    // the prologue's scratch goes in the last ring slot (free while the first NBW - 1 tiles
-    // stream in) when it fits there, else at the start with the tile loads issued after it
-    a.early = scr <= (size_t)kWaves * a.buf_bytes ? 1 : 0;
-    a.off_scratch = a.early ? (a.nbw - 1) * kWaves * a.buf_bytes : 0;
-    a.off_ksched = (int)al16(std::max({ring, epi, scr}));
+    while (a.nbw < 4 && (a.nbw + 1) * group + scr <= budget) ++a.nbw;
+    const size_t ring = a.nbw * group;
+    size_t top;
+    if (ring + scr <= budget) {  // the scratch beside the ring: every slot streams from the start
+        a.early = a.nbw;
+        a.off_scratch = (int)ring;
+        top = ring + scr;
+    } else {  // the scratch in the ring's last slots, streamed once the prologue is done
+        const int k = (int)std::min<size_t>(a.nbw, (scr + group - 1) / group);
+        a.early = a.nbw - k;
+        a.off_scratch = (int)(a.early * group);
+        top = std::max(ring, a.off_scratch + scr);
+    }
+    a.off_ksched = (int)al16(std::max(top, epi));
     p.lds = a.off_ksched + ksch;
     p.wgs_per_cu = std::min<int>(wgs, (int)((160 * 1024) / p.lds));
     if (p.lds > 160 * 1024 - 256)
@@ -772,7 +893,7 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
         1, std::min<int64_t>({slots / pairs, (tiles + kWaves - 1) / kWaves, (int64_t)(kMergeThreads / d) * kMergeRound}));
     a.wg_per_head = p.wg_per_head;
     a.part_ld = kPartHead + 16 * p.v.nvb;
-    p.qbuf_bytes = al256((size_t)n_seqs * cb->n_kv * (4 * RB * d + d) * sizeof(float));
+    p.qbuf_bytes = al256((size_t)n_seqs * cb->n_kv * qprep_bytes(RB, p.v.nqm));
     p.part_bytes = (size_t)n_seqs * cb->n_kv * p.wg_per_head * G * a.part_ld * sizeof(float);
     return AATC_OK;
 }
@@ -803,10 +924,10 @@ void profile_slot(hipEvent_t& a, hipEvent_t& b) {
 
 template <int RB, int NQM, int NVB, int D>
 int launch_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* blob, const uint8_t* cache,
-                  const int32_t* ids, const int64_t* lens, const uint16_t* q, float* qbuf, float* part, float* out) {
+                  const int32_t* ids, const int64_t* lens, const uint16_t* q, uint8_t* qbuf, float* part, float* out) {
     const DecodeArgs& a = p.args;
-    hipLaunchKernelGGL((qprep_kernel<RB, D>), dim3(D / 16, a.n_kv, n_seqs), dim3(64), 0, st, blob, a.layer, a.n_kv, a.G,
-                       q, qbuf);
+    hipLaunchKernelGGL((qprep_kernel<RB, NQM, D>), dim3(a.n_kv, n_seqs), dim3(D * 4), 0, st, blob, a.layer, a.n_kv,
+                       a.G, q, qbuf);
     HIP_TRY(hipGetLastError());
     if (p.lds > 64 * 1024)
         HIP_TRY(hipFuncSetAttribute((const void*)decode_kernel<RB, NQM, NVB, D>,
@@ -815,7 +936,7 @@ int launch_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* blob
     profile_slot(e0, e1);
     if (e0) HIP_TRY(hipEventRecord(e0, st));
     hipLaunchKernelGGL((decode_kernel<RB, NQM, NVB, D>), dim3(p.wg_per_head, a.n_kv, n_seqs), dim3(256), p.lds, st,
-                       blob, cache, a, ids, lens, (const float*)qbuf, part);
+                       blob, cache, a, ids, lens, (const uint8_t*)qbuf, part);
     HIP_TRY(hipGetLastError());
     if (e1) HIP_TRY(hipEventRecord(e1, st));
     hipLaunchKernelGGL((merge_kernel<D>), dim3(a.n_kv, n_seqs, a.G), dim3(kMergeThreads), 0, st, blob, a.layer, a.n_kv,
@@ -899,7 +1020,7 @@ extern "C" int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob
     if (ws_bytes < p.qbuf_bytes + p.part_bytes)
         return set_error(AATC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes,
                          p.qbuf_bytes + p.part_bytes);
-    float* qbuf = (float*)workspace;                              // [n_seqs][n_kv][4 RB * d + d] q'' and maxima
+    uint8_t* qbuf = (uint8_t*)workspace;                          // [n_seqs][n_kv] score operands and lane records
     float* part = (float*)((uint8_t*)workspace + p.qbuf_bytes);  // [n_seqs][n_kv][wg][G][part_ld] partials
     DecodeArgs& a = p.args;
     a.layer = layer;
