@@ -680,116 +680,116 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
 
 // ---------------------------------------------------------------------------------------
 // merge: one workgroup of 1024 threads per (sequence, kv-head, query head).  Softmax merge
-// of the W partials (column c of a partial is sum p x stored byte of value field c,
-// relative to the partial's reference max), then per channel j
+// of the W partials (a partial row is [reference max m, sum of p, top-field sum, 0,
+// columns]; column c = sum of p x stored byte of value field c, relative to m), then per
+// channel j
 //   A_j = sum over its fields of 2^(shift - pos) (column + [field ends at bit 7] top sum)
 // (the stored byte of a field at bit pos is field 2^pos, minus 128 at the top of a byte)
-// and o = obias + U_V (step * A / L).  Every global read is issued in one round.
+// and o = obias + U_V (step * A / L).  Every global read is issued at the start, 16 bytes
+// per lane: thread (q, s) holds float4 q of partial rows s, s + NS, ...; thread (i4, js)
+// holds float4 i4 of rows js JR .. js JR + JR - 1 of U_V^T.
 // ---------------------------------------------------------------------------------------
 static_assert(offsetof(DevHead, vch) % 16 == 0, "the merge loads a channel's field table as 16 bytes");
+static_assert(offsetof(DevHead, UVt) % 16 == 0, "the merge loads U_V^T 16 bytes per lane");
 static_assert(offsetof(DevHead, kq_slot) % 16 == 0 && offsetof(DevHead, kq_sched) % 16 == 0 &&
                   offsetof(DevHead, vb_col) % 16 == 0,
               "the decode prologue copies these tables 16 bytes per lane");
-constexpr int kMergeCols = 3;     // value columns per thread (16 kMaxVB <= 3 D for D >= 128)
-constexpr int kMergeRound = 16;   // partials per thread and column
+constexpr int kMergeRows = 8;  // partial rows per merge thread: W <= 8 (1024 / (PL / 4))
+constexpr int kMaxPL = kPartHead + 16 * aatc::kMaxVB;
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DevHead* __restrict__ blob, int layer, int n_kv,
                                                               int G, int W, int PL, const float* __restrict__ part,
                                                               float* __restrict__ out) {
-    constexpr int SL = kMergeThreads / D;  // slices (of partials, then of U_V rows) per column
-    constexpr int ROWS = D / SL;
     constexpr int NW = kMergeThreads / 64;
-    __shared__ float ew[kMergeThreads];    // per partial: reference max, then weight 2^(m - M)
-    __shared__ float wred[3][NW];          // per wave: max, sum, top sum
-    __shared__ float red[SL][D];           // slice sums
-    __shared__ float colv[16 * aatc::kMaxVB];  // merged columns
-    __shared__ float cbar[D];              // step * A / L
+    constexpr int I4 = D / 4;                 // float4 columns of U_V^T
+    constexpr int JS = kMergeThreads / I4;    // row slices of U_V^T
+    constexpr int JR = D / JS;                // rows per slice
+    __shared__ float mrow[kMergeThreads];     // per partial: reference max
+    __shared__ float wred[NW];
+    __shared__ f4 red[kMergeThreads];         // slice sums
+    __shared__ __attribute__((aligned(16))) float colv[kMaxPL];  // merged row
+    __shared__ float cbar[D];                 // step * A / L
     const int h = blockIdx.x, z = blockIdx.y, hh = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t zh = (int64_t)z * n_kv + h;
     const DevHead& H = blob[layer * n_kv + h];
     const int64_t PS = (int64_t)G * PL;              // floats between partials
     const float* P = part + (zh * W * G + hh) * PL;  // partial w at P + w * PS
-    const int ii = tid % D, sl = tid / D;
-    const int ncol = 16 * H.nvb;
-    // U_V slice, this thread's columns ii + D k of partials sl + SL r, and partial tid's
-    // (max, sum, top sum)
-    float uv[ROWS];
+    const int PL4 = PL >> 2, NS = kMergeThreads / PL4;
+    const int q = tid % PL4, s = tid / PL4;
+    // ---- every global read
+    f4 X[kMergeRows];
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) uv[r] = H.UVt[(sl * ROWS + r) * D + ii];  // UVt[j * d + i] = U_V[i][j]
-    // channel tid (tid < D): its field columns and output constants
+    for (int k = 0; k < kMergeRows; ++k) {
+        const int w = s + NS * k;
+        X[k] = s < NS && w < W ? *(const f4*)(P + w * PS + 4 * q) : f4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const int i4 = tid % I4, js = tid / I4;
+    f4 U[JR];
+#pragma unroll
+    for (int r = 0; r < JR; ++r) U[r] = *(const f4*)(H.UVt + (js * JR + r) * D + 4 * i4);  // U_V[4 i4 ..][j]
     typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
-    const int jc = tid % D;
+    const int jc = tid % D;  // channel tid (tid < D): its field columns and output constants
     const u16x8 fl = *(const u16x8*)&H.vch[jc][0];
     const float stv = H.bitsV[jc] ? H.stepV[jc] : 0.0f, obv = H.obias[jc], muv = H.muV[jc];
-    float x[kMergeCols][kMergeRound];
+    // ---- reference: the largest partial maximum
+    if (q == 0 && s < NS) {
 #pragma unroll
-    for (int k = 0; k < kMergeCols; ++k)
-#pragma unroll
-        for (int r = 0; r < kMergeRound; ++r) {
-            const int cc = ii + D * k, wgi = sl + SL * r;
-            x[k][r] = cc < ncol && wgi < W ? P[wgi * PS + kPartHead + cc] : 0.0f;
-        }
-    const bool mine = tid < W;
-    const float m_t = mine ? P[tid * PS] : -INFINITY;
-    const float l_t = mine ? P[tid * PS + 1] : 0.0f;
-    const float o_t = mine ? P[tid * PS + 2] : 0.0f;
-    float mx = wave_max(m_t);
-    if (lane == 0) wred[0][wv] = mx;
+        for (int k = 0; k < kMergeRows; ++k)
+            if (s + NS * k < W) mrow[s + NS * k] = X[k][0];
+    }
+    __syncthreads();
+    const float mx = wave_max(tid < W ? mrow[tid] : -INFINITY);
+    if (lane == 0) wred[wv] = mx;
     __syncthreads();
     float M = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < NW; ++k) M = fmaxf(M, wred[0][k]);
-    const float e_t = m_t == -INFINITY ? 0.0f : exp2f(m_t - M);
-    const float ls = wave_sum(e_t * l_t), os = wave_sum(e_t * o_t);
-    ew[tid] = e_t;
-    if (lane == 0) wred[1][wv] = ls, wred[2][wv] = os;
-    __syncthreads();
-    float L = 0.0f, O = 0.0f;
+    for (int k = 0; k < NW; ++k) M = fmaxf(M, wred[k]);
+    // ---- merged row: sum over partials of 2^(m - M) x row; slices meet in LDS
+    f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int k = 0; k < NW; ++k) L += wred[1][k], O += wred[2][k];
-    // columns: slice sums of the weighted partials, slices meet in LDS
-#pragma unroll
-    for (int k = 0; k < kMergeCols; ++k) {
-        if (D * k >= ncol) break;
-        float acc = 0.0f;
-#pragma unroll
-        for (int r = 0; r < kMergeRound; ++r) acc = fmaf(ew[min(sl + SL * r, kMergeThreads - 1)], x[k][r], acc);
-        red[sl][ii] = acc;
-        __syncthreads();
-        if (sl == 0 && ii + D * k < ncol) {
-            float v = 0.0f;
-#pragma unroll
-            for (int s2 = 0; s2 < SL; ++s2) v += red[s2][ii];
-            colv[ii + D * k] = v;
+    for (int k = 0; k < kMergeRows; ++k) {
+        const int w = s + NS * k;
+        if (s < NS && w < W) {
+            const float m = mrow[w];
+            const float e = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+            acc += e * X[k];
         }
-        __syncthreads();
     }
-    // value coefficients, dequantisation step and 1 / L
+    red[tid] = acc;
+    __syncthreads();
+    if (tid < PL4) {
+        f4 v = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int s2 = 0; s2 < NS; ++s2) v += red[s2 * PL4 + tid];
+        *(f4*)&colv[4 * tid] = v;
+    }
+    __syncthreads();
+    const float L = colv[1], O = colv[2];
+    // ---- value coefficients, dequantisation step and 1 / L
     if (tid < D) {
         float A = 0.0f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const uint32_t en = fl[k];
             if (en != 0xFFFFu) {
-                const float v = colv[en & 511] + (((en >> 13) & 1) ? O : 0.0f);
+                const float v = colv[kPartHead + (en & 511)] + (((en >> 13) & 1) ? O : 0.0f);
                 A = fmaf(__builtin_amdgcn_ldexpf(1.0f, (int)((en >> 9) & 15) - 8), v, A);
             }
         }
         cbar[tid] = L > 0.0f ? stv * A / L : 0.0f;
     }
     __syncthreads();
-    // o = obias + U_V cbar: thread (i, slice) sums its rows, slices meet in LDS
-    float y = 0.0f;
+    // ---- o = obias + U_V cbar: slices of rows of U_V^T, slices meet in LDS
+    f4 y = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) y = fmaf(uv[r], cbar[sl * ROWS + r], y);
-    red[sl][ii] = y;
+    for (int r = 0; r < JR; ++r) y += cbar[js * JR + r] * U[r];
+    red[tid] = y;
     __syncthreads();
     if (tid < D) {
         float o = 0.0f;
 #pragma unroll
-        for (int s2 = 0; s2 < SL; ++s2) o += red[s2][tid];
+        for (int s2 = 0; s2 < JS; ++s2) o += red[s2 * I4 + (tid >> 2)][tid & 3];
         out[(zh * G + hh) * D + tid] = L > 0.0f ? obv + o : muv;
     }
 }
@@ -837,9 +837,7 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     if (!found)
         return set_error(AATC_ERR_UNSUPPORTED, "no decode variant for %d query heads, %d score MFMAs and %d value blocks", G,
                          p.nqm_max, p.nvb_max);
-    if (16 * p.nvb_max > kMergeCols * d)
-        return set_error(AATC_ERR_UNSUPPORTED, "%d value fields per token exceed the merge's %d columns", 16 * p.nvb_max,
-                         kMergeCols * d);
+
     const int64_t tiles = n_tiles_of(max_len);
     DecodeArgs& a = p.args;
     a.G = G;
@@ -890,7 +888,8 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     const int64_t pairs = (int64_t)cb->n_kv * n_seqs;
     const int64_t slots = 256 * (int64_t)p.wgs_per_cu;
     p.wg_per_head = (int)std::max<int64_t>(
-        1, std::min<int64_t>({slots / pairs, (tiles + kWaves - 1) / kWaves, (int64_t)(kMergeThreads / d) * kMergeRound}));
+        1, std::min<int64_t>({slots / pairs, (tiles + kWaves - 1) / kWaves,
+                              (int64_t)kMergeRows * (kMergeThreads / ((kPartHead + 16 * p.v.nvb) / 4))}));
     a.wg_per_head = p.wg_per_head;
     a.part_ld = kPartHead + 16 * p.v.nvb;
     p.qbuf_bytes = al256((size_t)n_seqs * cb->n_kv * qprep_bytes(RB, p.v.nqm));
