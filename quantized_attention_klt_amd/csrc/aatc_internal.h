@@ -62,12 +62,18 @@ struct alignas(256) DevHead {
     float stepK[kMaxD], stepV[kMaxD];
     float invK[kMaxD], invV[kMaxD];
     int32_t bitsK[kMaxD], bitsV[kMaxD];
-    // record fields sorted by (byte, pos): chan | width << 8 | shift << 12 | pos << 16 | byte << 20;
-    // record byte q holds fields [fbyteK[q], fbyteK[q + 1]) (likewise for values)
-    uint32_t fieldK[kMaxFields];
-    uint32_t fieldV[kMaxFields];
-    int16_t fbyteK[kMaxRecordBytes + 8];
-    int16_t fbyteV[kMaxRecordBytes + 8];
+    // Encoder tables (likewise for values).  Record fields by channel: channel j's fields,
+    // lowest code bits first, are cpieceK[cfirstK[j] .. cfirstK[j + 1]), each byte | pos << 8 |
+    // width << 12 | shift << 16.  encpermK: the channel order of the encoder's MFMA columns
+    // (position 16 k + c of block k holds channel encpermK[16 k + c]): the channels of one
+    // 16-column block have first fields in record bytes distinct mod 16 where possible, so
+    // that their codes land in distinct LDS banks of the staged block.
+    uint32_t cpieceK[kMaxFields];
+    uint32_t cpieceV[kMaxFields];
+    int16_t cfirstK[kMaxD + 8];
+    int16_t cfirstV[kMaxD + 8];
+    uint8_t encpermK[kMaxD];
+    uint8_t encpermV[kMaxD];
     // ---- decode schedule -------------------------------------------------------------
     // Score MFMAs: nqm per token group.  The B operand of lane group g (lanes 16g..16g+15,
     // K-slots 16g..16g+15) in MFMA m is four dwords; dword i is key-record word w_i of the

@@ -395,6 +395,44 @@ static int build_decode_schedule(const HeadCB& H, DevHead& D) {
     return AATC_OK;
 }
 
+// Channel order of the encoder's MFMA columns (fields by channel in `fs`, sorted by channel
+// then shift): 16-column blocks whose channels' first fields sit in record bytes distinct mod
+// 16 (the encoder's staged block puts record byte q in LDS bank group q mod 16), filled
+// greedily from the largest residue classes; channels without bits fill the rest.
+static void build_encoder_order(const std::vector<Field>& fs, int d, uint8_t* perm) {
+    std::vector<int> first_byte(d, -1);
+    for (const Field& f : fs)
+        if (first_byte[f.chan] < 0) first_byte[f.chan] = f.byte;  // fs: by channel, lowest shift first
+    std::vector<std::vector<int>> cls(16);
+    std::vector<int> uncoded;
+    for (int j = 0; j < d; ++j) (first_byte[j] < 0 ? uncoded : cls[first_byte[j] % 16]).push_back(j);
+    const int nblk = d / 16;
+    std::vector<std::vector<int>> blk(nblk);
+    std::vector<uint32_t> used(nblk, 0u);
+    std::vector<int> order(16);
+    for (int r = 0; r < 16; ++r) order[r] = r;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return cls[a].size() > cls[b].size(); });
+    std::vector<int> spill;
+    for (int r : order)
+        for (int j : cls[r]) {
+            int best = -1;
+            for (int k = 0; k < nblk; ++k)
+                if (!(used[k] >> r & 1u) && blk[k].size() < 16 && (best < 0 || blk[k].size() < blk[best].size())) best = k;
+            if (best < 0) {
+                spill.push_back(j);
+                continue;
+            }
+            blk[best].push_back(j);
+            used[best] |= 1u << r;
+        }
+    for (int j : spill) uncoded.insert(uncoded.begin(), j);
+    size_t u = 0;
+    for (int k = 0; k < nblk; ++k) {
+        while (blk[k].size() < 16 && u < uncoded.size()) blk[k].push_back(uncoded[u++]);
+        for (int c = 0; c < 16; ++c) perm[16 * k + c] = (uint8_t)blk[k][c];
+    }
+}
+
 int finalize(aatc_codebook* cb) {
     const int d = cb->d;
     int total = -1;
@@ -472,18 +510,20 @@ int finalize(aatc_codebook* cb) {
             D.obias[i] = (float)o;
         }
         for (int which = 0; which < 2; ++which) {
-            const std::vector<Field>& fs = which ? H.fV : H.fK;
-            uint32_t* dst = which ? D.fieldV : D.fieldK;
-            int16_t* first = which ? D.fbyteV : D.fbyteK;
-            const int nbytes = (which ? H.BV : H.BK) / 8;
+            std::vector<Field> fs = which ? H.fV : H.fK;
+            std::stable_sort(fs.begin(), fs.end(), [](const Field& a, const Field& b) {
+                return a.chan != b.chan ? a.chan < b.chan : a.shift < b.shift;
+            });
+            uint32_t* dst = which ? D.cpieceV : D.cpieceK;
+            int16_t* first = which ? D.cfirstV : D.cfirstK;
             for (size_t i = 0; i < fs.size(); ++i)
-                dst[i] = (uint32_t)(fs[i].chan | (fs[i].width << 8) | (fs[i].shift << 12) | (fs[i].pos << 16) |
-                                    (fs[i].byte << 20));
+                dst[i] = (uint32_t)(fs[i].byte | (fs[i].pos << 8) | (fs[i].width << 12) | (fs[i].shift << 16));
             size_t f = 0;
-            for (int q = 0; q <= nbytes; ++q) {
-                while (f < fs.size() && fs[f].byte < q) ++f;
-                first[q] = (int16_t)f;
+            for (int j = 0; j <= d; ++j) {
+                while (f < fs.size() && fs[f].chan < j) ++f;
+                first[j] = (int16_t)f;
             }
+            build_encoder_order(fs, d, which ? D.encpermV : D.encpermK);
         }
         int rc = build_decode_schedule(H, D);
         if (rc != AATC_OK) return set_error(rc, "head %zu: %s", h, "decode schedule exceeds kernel limits");

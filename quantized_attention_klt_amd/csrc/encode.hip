@@ -37,70 +37,100 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // quantizer: t = c * inv (one fp32 rounding), code = clamp(floor(t) + 2^(b-1), 0, 2^b - 1)
+// (b >= 1)
 __device__ __forceinline__ uint32_t quantize(float c, float inv, int b) {
-    float t = __fmul_rn(c, inv);
-    float v = floorf(t) + (float)(1 << (b - 1));
-    v = fminf(fmaxf(v, 0.0f), (float)((1 << b) - 1));
-    return (uint32_t)v;
+    const float v = floorf(__fmul_rn(c, inv)) + (float)(1 << (b - 1));
+    return (uint32_t)__builtin_amdgcn_fmed3f(v, 0.0f, (float)((1 << b) - 1));
 }
 
-// Field tables of one record (keys or values) staged in LDS: fields sorted by (byte, pos)
-// (chan | width << 8 | shift << 12 | pos << 16 | byte << 20) and per record byte the first
-// field index.
-struct FieldTab {
-    uint32_t field[aatc::kMaxFields];
-    int16_t first[aatc::kMaxRecordBytes + 8];
+// A tile's block (keys or values) is assembled in LDS byte-major, every code's fields OR-ed
+// into place: record byte q of slots 4u .. 4u + 3 is LDS word q * kStageRow + u.  The row
+// stride of 18 words puts record byte q in bank group q mod 16, so codes of one instruction
+// whose record bytes differ mod 16 hit distinct banks.  Then the block is copied out: the
+// value block is byte-major in the tile as well; the key block is word-major (tile word
+// 64 r + s = record word r of slot s), a 4 x 4 byte transpose of four staged rows.
+constexpr int kStageRow = 18;
+constexpr int kStageWords = aatc::kMaxRecordBytes * kStageRow;
+
+// Fields of one record kind by channel, staged in LDS: channel j's fields (lowest code bits
+// first) are piece[first[j] .. first[j + 1]), each byte | pos << 8 | width << 12 | shift << 16.
+struct PieceTab {
+    uint32_t piece[aatc::kMaxFields];
+    int16_t first[aatc::kMaxD + 8];
 };
 
-__device__ void stage_fields(const DevHead& H, bool isV, FieldTab& ft, int tid, int nthreads) {
-    const uint32_t* f = isV ? H.fieldV : H.fieldK;
-    const int16_t* fb = isV ? H.fbyteV : H.fbyteK;
-    const int nf = isV ? H.nfV : H.nfK;
-    const int nb = (isV ? H.BV : H.BK) / 8;
-    for (int i = tid; i < nf; i += nthreads) ft.field[i] = f[i];
-    for (int i = tid; i <= nb; i += nthreads) ft.first[i] = fb[i];
+__device__ void stage_pieces(const DevHead& H, bool isV, PieceTab& pt, int tid, int nthreads) {
+    const uint32_t* p = isV ? H.cpieceV : H.cpieceK;
+    const int16_t* f = isV ? H.cfirstV : H.cfirstK;
+    const int np = isV ? H.nfV : H.nfK;
+    for (int i = tid; i < np; i += nthreads) pt.piece[i] = p[i];
+    for (int i = tid; i <= H.d; i += nthreads) pt.first[i] = f[i];
 }
 
-// record byte q of the slot whose codes are codes[chan * 64] (one byte per code, stride 64)
-__device__ __forceinline__ uint32_t record_byte(const FieldTab& ft, const uint8_t* codes, int q) {
-    uint32_t byte = 0u;
-    for (int f = ft.first[q]; f < ft.first[q + 1]; ++f) {
-        const uint32_t fw = ft.field[f];
-        const uint32_t chan = fw & 0xff, w = (fw >> 8) & 0xf, e = (fw >> 12) & 0xf, pos = (fw >> 16) & 0xf;
-        byte |= (((uint32_t)codes[chan * 64] >> e) & ((1u << w) - 1u)) << pos;
+// every field of channel j's code of slot s, OR-ed into the staged block
+__device__ __forceinline__ void scatter_code(uint32_t* stg, const PieceTab& pt, int j, int s, uint32_t code) {
+    for (int p = pt.first[j]; p < pt.first[j + 1]; ++p) {
+        const uint32_t pc = pt.piece[p];
+        const int q = pc & 0xff, pos = (pc >> 8) & 7, wd = (pc >> 12) & 15, e = (pc >> 16) & 15;
+        atomicOr(&stg[q * kStageRow + (s >> 2)], ((code >> e) & ((1u << wd) - 1u)) << (8 * (s & 3) + pos));
     }
-    return byte;
 }
 
-// Pack one block of a tile from its codes (LDS codes[chan][slot]) for the slots [s0, s1):
-// the key block is word-major (word 64 r + s = record word r of slot s), the value block
-// byte-major (word 16 q + u = record byte q of slots 4u .. 4u + 3).  Stored bytes carry bit
-// 7 inverted; a value word shared with slots outside [s0, s1) keeps their stored bytes.
-__device__ void pack_block(const FieldTab& ft, bool isV, int nbytes, const uint8_t* codes, uint32_t* dst, int s0,
-                           int s1, int tid, int nthreads) {
-    const int nwords = 16 * nbytes;  // 64 slots x nbytes / 4
-    for (int i = tid; i < nwords; i += nthreads) {
-        uint32_t word = 0u, keep = 0u;
+// Copy the staged block to the tile at dst for the slots [s0, s1) and clear the staging.
+// One item = 16 tile bytes: key block, record word r of slots 4u .. 4u + 3 (from staged
+// rows 4r .. 4r + 3); value block, record byte q of slots 16 v .. 16 v + 15 (staged row q).
+// Stored bytes carry bit 7 inverted; a value word shared with slots outside [s0, s1) keeps
+// their stored bytes (the staging holds codes of every slot of the tile, so the bytes of
+// those slots are masked out).
+__device__ void copy_out(uint32_t* stg, bool isV, int nbytes, uint32_t* dst, int s0, int s1, int tid, int nthreads) {
+    const int nitems = 4 * nbytes;  // 16 nbytes tile words, 4 per item
+    for (int it = tid; it < nitems; it += nthreads) {
+        uint32_t out[4];
+        int word0;  // first tile word of the item
+        uint32_t keep[4];
         if (!isV) {
-            const int r = i >> 6, s = i & 63;
-            if (s < s0 || s >= s1) continue;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) word |= record_byte(ft, codes + s, 4 * r + b) << (8 * b);
-        } else {
-            const int q = i >> 4, u = i & 15;
+            const int r = it >> 4, u = it & 15;
+            uint32_t W[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const int s = 4 * u + b;
-                if (s >= s0 && s < s1)
-                    word |= record_byte(ft, codes + s, q) << (8 * b);
-                else
-                    keep |= 0xFFu << (8 * b);
+                W[b] = stg[(4 * r + b) * kStageRow + u];
+                stg[(4 * r + b) * kStageRow + u] = 0u;
             }
-            if (keep == 0xFFFFFFFFu) continue;
+            const uint32_t t0 = __builtin_amdgcn_perm(W[1], W[0], 0x05010400u);
+            const uint32_t t1 = __builtin_amdgcn_perm(W[3], W[2], 0x05010400u);
+            const uint32_t t2 = __builtin_amdgcn_perm(W[1], W[0], 0x07030602u);
+            const uint32_t t3 = __builtin_amdgcn_perm(W[3], W[2], 0x07030602u);
+            out[0] = __builtin_amdgcn_perm(t1, t0, 0x05040100u);  // slot 4u: bytes of rows 4r .. 4r + 3
+            out[1] = __builtin_amdgcn_perm(t1, t0, 0x07060302u);
+            out[2] = __builtin_amdgcn_perm(t3, t2, 0x05040100u);
+            out[3] = __builtin_amdgcn_perm(t3, t2, 0x07060302u);
+            word0 = 64 * r + 4 * u;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) keep[k] = (4 * u + k < s0 || 4 * u + k >= s1) ? 0xFFFFFFFFu : 0u;
+        } else {
+            const int q = it >> 2, v = it & 3;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                out[k] = stg[q * kStageRow + 4 * v + k];
+                stg[q * kStageRow + 4 * v + k] = 0u;
+                keep[k] = 0u;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int s = 16 * v + 4 * k + b;
+                    if (s < s0 || s >= s1) keep[k] |= 0xFFu << (8 * b);
+                }
+            }
+            word0 = 16 * q + 4 * v;
         }
-        word ^= 0x80808080u & ~keep;
-        if (keep) word |= dst[i] & keep;
-        dst[i] = word;
+        if ((keep[0] | keep[1] | keep[2] | keep[3]) == 0u) {  // the common case: one 16-byte store
+            *(u32x4*)(dst + word0) =
+                u32x4{out[0] ^ 0x80808080u, out[1] ^ 0x80808080u, out[2] ^ 0x80808080u, out[3] ^ 0x80808080u};
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (keep[k] != 0xFFFFFFFFu)
+                    dst[word0 + k] = ((out[k] ^ 0x80808080u) & ~keep[k]) | (keep[k] ? dst[word0 + k] & keep[k] : 0u);
+        }
     }
 }
 
@@ -112,56 +142,71 @@ __device__ __forceinline__ uint8_t* tile_ptr(uint8_t* cache, int layer, int n_se
 // ------------------------------------------------------------------------------------
 // encode from bf16 K, V (MFMA): a workgroup owns one (sequence, kv-head, keys | values)
 // and the tiles bx, bx + gridDim.x, ... of the call.  c = x (U_hi + U_lo) - bias on
-// v_mfma_f32_16x16x32_bf16: rows = tokens, columns = channels; wave w keeps the B operands
-// (U^T hi / lo fragments) of its D / 4 channels in registers for all its tiles.  The 64-token
-// x tile is staged in LDS with its 16-byte chunks XOR-swizzled by token, so that the 16
-// rows an operand read touches fall in distinct banks.
+// v_mfma_f32_16x16x32_bf16: rows = tokens, columns = channels (in the encoder's channel
+// order), accumulators starting at -bias; wave w keeps the B operands (U^T hi / lo
+// fragments) of its D / 4 columns in registers for all its tiles.  The 64-token x tile is
+// staged in LDS with its 16-byte chunks XOR-swizzled by token, so that the 16 rows an
+// operand read touches fall in distinct banks.  Lane (g, c) quantizes tokens 16 tb + 4 g + e
+// of its channels and ORs each code's fields into the staged block: one shift and one LDS
+// atomic per field (the LDS word is the field's base plus an immediate offset per token).
 // ------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void encode_mfma_kernel(const DevHead* __restrict__ blob, uint8_t* __restrict__ cache,
-                                                          int layer, int n_kv, int64_t n_tiles_cap, int tile_bytes,
-                                                          SeqArgs sa, int64_t n_tokens, int64_t ntiles,
-                                                          const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                                                          int n_seqs_cache) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void encode_mfma_kernel(
+    const DevHead* __restrict__ blob, uint8_t* __restrict__ cache, int layer, int n_kv, int64_t n_tiles_cap,
+    int tile_bytes, SeqArgs sa, int64_t n_tokens, int64_t ntiles, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, int n_seqs_cache) {
     constexpr int CH = D / 8;          // 16-byte chunks per token row
     constexpr int CBW = D / 64;        // 16-channel column blocks per wave
     constexpr int KS = D / 32;         // k-steps
     constexpr int XB = 64 * D * 2;     // bytes of one x tile
     constexpr int NLD = 64 * CH / 256;  // chunk loads per thread
     __shared__ __attribute__((aligned(16))) uint8_t xs[2][XB];
-    __shared__ __attribute__((aligned(16))) uint8_t codes[D * 64];
-    __shared__ FieldTab ft;
-    const int h = blockIdx.y >> 1, kv = blockIdx.y & 1, zi = blockIdx.z;
+    __shared__ __attribute__((aligned(16))) uint32_t stg[kStageWords];
+    __shared__ PieceTab pt;
+    const int h = blockIdx.y >> 1, zi = blockIdx.z;
+    const bool isV = (blockIdx.y & 1) != 0;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
     const DevHead& H = blob[layer * n_kv + h];
-    const uint16_t* X = (kv ? V : K) + ((int64_t)zi * n_tokens * n_kv + h) * D;  // token t at X + t * n_kv * D
+    const uint16_t* X = (isV ? V : K) + ((int64_t)zi * n_tokens * n_kv + h) * D;  // token t at X + t * n_kv * D
     const int64_t xstride = (int64_t)n_kv * D;
     const int64_t start = sa.start[zi];
     const int64_t first_tile = start / kTile;
     const int seq = sa.seq[zi];
-    stage_fields(H, kv, ft, tid, 256);
-    // B operands and quantizer constants of this lane's channels j = 16 (w CBW + cbw) + c
+    stage_pieces(H, isV, pt, tid, 256);
+    for (int i = tid; i < kStageWords; i += 256) stg[i] = 0u;
+    // B operands and quantizer constants of this lane's columns 16 (w CBW + cbw) + c: channel
+    // j = encoder order of that column (an uncoded channel gets a 1-bit quantizer and no field)
     bf16x8 bh[CBW][KS], bl[CBW][KS];
-    float bias[CBW], inv[CBW];
-    int bits[CBW];
+    float nbias[CBW], inv[CBW];
+    int bits[CBW], jj[CBW];
     {
-        const uint16_t* uh = kv ? H.UVt_hi : H.UKt_hi;
-        const uint16_t* ul = kv ? H.UVt_lo : H.UKt_lo;
+        const uint16_t* uh = isV ? H.UVt_hi : H.UKt_hi;
+        const uint16_t* ul = isV ? H.UVt_lo : H.UKt_lo;
+        const uint8_t* perm = isV ? H.encpermV : H.encpermK;
 #pragma unroll
         for (int cbw = 0; cbw < CBW; ++cbw) {
-            const int j = 16 * (w * CBW + cbw) + c;
+            const int j = perm[16 * (w * CBW + cbw) + c];
+            jj[cbw] = j;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 bh[cbw][ks] = *(const bf16x8*)(uh + j * D + 32 * ks + 8 * g);
                 bl[cbw][ks] = *(const bf16x8*)(ul + j * D + 32 * ks + 8 * g);
             }
-            bias[cbw] = kv ? H.biasV[j] : H.biasK[j];
-            inv[cbw] = kv ? H.invV[j] : H.invK[j];
-            bits[cbw] = kv ? H.bitsV[j] : H.bitsK[j];
+            nbias[cbw] = -(isV ? H.biasV[j] : H.biasK[j]);
+            inv[cbw] = isV ? H.invV[j] : H.invK[j];
+            bits[cbw] = max(isV ? H.bitsV[j] : H.bitsK[j], 1);
         }
     }
-    const int nbytes = (kv ? H.BV : H.BK) / 8;
-    const int boff = kv ? 8 * H.BK : 0;  // block offset in the tile
+    const int nbytes = (isV ? H.BV : H.BK) / 8;
+    const int boff = isV ? 8 * H.BK : 0;  // block offset in the tile
+    __syncthreads();  // field table staged, staging clear
+    // this lane's channels: their fields (usually one) are pt.piece[pf[cbw] .. pl[cbw])
+    int pf[CBW], pl[CBW];
+#pragma unroll
+    for (int cbw = 0; cbw < CBW; ++cbw) {
+        pf[cbw] = pt.first[jj[cbw]];
+        pl[cbw] = pt.first[jj[cbw] + 1];
+    }
     // x tile of tile index k (chunk n of this thread: token t = ci / CH, chunk ci % CH);
     // slots outside the call's tokens read as zero
     auto load_x = [&](int64_t tile, u32x4 (&r)[NLD]) {
@@ -195,7 +240,7 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const DevHead* __restr
 #pragma unroll
         for (int cbw = 0; cbw < CBW; ++cbw)
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) acc[cbw][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int tb = 0; tb < 4; ++tb) acc[cbw][tb] = f32x4{nbias[cbw], nbias[cbw], nbias[cbw], nbias[cbw]};
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             const int t = 16 * tb + c;  // A row: token
@@ -209,19 +254,24 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const DevHead* __restr
                 }
             }
         }
-        // codes of tokens 16 tb + 4 g + e, channel 16 (w CBW + cbw) + c -> codes[j][token]
+        // codes of tokens 16 tb + 4 g + e (staged word q * kStageRow + 4 tb + g, byte e),
+        // OR-ed into the staging field by field
 #pragma unroll
         for (int cbw = 0; cbw < CBW; ++cbw) {
-            const int j = 16 * (w * CBW + cbw) + c;
+            uint32_t code[16];
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                uint32_t wv = 0u;
+            for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t code = bits[cbw] ? quantize(acc[cbw][tb][e] - bias[cbw], inv[cbw], bits[cbw]) : 0u;
-                    wv |= code << (8 * e);
-                }
-                *(uint32_t*)(&codes[j * 64 + 16 * tb + 4 * g]) = wv;
+                for (int e = 0; e < 4; ++e) code[4 * tb + e] = quantize(acc[cbw][tb][e], inv[cbw], bits[cbw]);
+            for (int p = pf[cbw]; p < pl[cbw]; ++p) {
+                const uint32_t pc = pt.piece[p];
+                const int q = pc & 0xff, pos = (pc >> 8) & 7, e0 = (pc >> 16) & 15;
+                const uint32_t mask = (1u << ((pc >> 12) & 15)) - 1u;
+                uint32_t* base = stg + q * kStageRow + g;
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) atomicOr(base + 4 * tb, ((code[4 * tb + e] >> e0) & mask) << (8 * e + pos));
             }
         }
         __syncthreads();
@@ -229,23 +279,23 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(const DevHead* __restr
         const int s0 = (int)max(start - tok0, (int64_t)0);
         const int s1 = (int)min(start + n_tokens - tok0, (int64_t)kTile);
         uint8_t* tp = tile_ptr(cache, layer, n_seqs_cache, seq, n_kv, h, n_tiles_cap, first_tile + tile, tile_bytes);
-        pack_block(ft, kv, nbytes, codes, (uint32_t*)(tp + boff), s0, s1, tid, 256);
+        copy_out(stg, isV, nbytes, (uint32_t*)(tp + boff), s0, s1, tid, 256);
         if (tile_n < ntiles) store_x(buf ^ 1, xr);
         __syncthreads();
     }
 }
 
 // ------------------------------------------------------------------------------------
-// encode given KLT coefficients: one workgroup per (tile, kv-head, sequence); codes of
-// both blocks in LDS, then both blocks packed.
+// encode given KLT coefficients: one workgroup per (tile, kv-head, sequence); the codes of
+// both blocks are OR-ed into their staging, then both blocks are copied out.
 // ------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void encode_coeffs_kernel(const DevHead* __restrict__ blob,
                                                             uint8_t* __restrict__ cache, int layer, int n_kv,
                                                             int64_t n_tiles_cap, int tile_bytes, SeqArgs sa,
                                                             int64_t n_tokens, const float* __restrict__ coeffs,
                                                             int n_seqs_cache) {
-    __shared__ __attribute__((aligned(16))) uint8_t codes[2][aatc::kMaxD * 64];
-    __shared__ FieldTab ft[2];
+    __shared__ __attribute__((aligned(16))) uint32_t stg[2][kStageWords];
+    __shared__ PieceTab pt[2];
     const int h = blockIdx.y, zi = blockIdx.z;
     const DevHead& H = blob[layer * n_kv + h];
     const int d = H.d;
@@ -254,19 +304,21 @@ __global__ __launch_bounds__(256) void encode_coeffs_kernel(const DevHead* __res
     const int64_t tok0 = tile * kTile;
     const int s0 = (int)std::max<int64_t>(start - tok0, 0);
     const int s1 = (int)std::min<int64_t>(start + n_tokens - tok0, kTile);
-    stage_fields(H, false, ft[0], threadIdx.x, blockDim.x);
-    stage_fields(H, true, ft[1], threadIdx.x, blockDim.x);
+    stage_pieces(H, false, pt[0], threadIdx.x, blockDim.x);
+    stage_pieces(H, true, pt[1], threadIdx.x, blockDim.x);
+    for (int i = threadIdx.x; i < 2 * kStageWords; i += blockDim.x) stg[i / kStageWords][i % kStageWords] = 0u;
+    __syncthreads();
     for (int i = threadIdx.x; i < (s1 - s0) * 2 * d; i += blockDim.x) {
         const int s = s0 + i / (2 * d), r = i % (2 * d), kv = r / d, j = r % d;
         const int64_t t = tok0 + s - start;  // token index in this call's input
         const float cf = coeffs[((t * n_kv + h) * 2 + kv) * d + j];
         const int b = kv ? H.bitsV[j] : H.bitsK[j];
-        codes[kv][j * 64 + s] = b ? (uint8_t)quantize(cf, kv ? H.invV[j] : H.invK[j], b) : 0;
+        if (b) scatter_code(stg[kv], pt[kv], j, s, quantize(cf, kv ? H.invV[j] : H.invK[j], b));
     }
     __syncthreads();
     uint8_t* tp = tile_ptr(cache, layer, n_seqs_cache, sa.seq[zi], n_kv, h, n_tiles_cap, tile, tile_bytes);
-    pack_block(ft[0], false, H.BK / 8, codes[0], (uint32_t*)tp, s0, s1, threadIdx.x, blockDim.x);
-    pack_block(ft[1], true, H.BV / 8, codes[1], (uint32_t*)(tp + 8 * H.BK), s0, s1, threadIdx.x, blockDim.x);
+    copy_out(stg[0], false, H.BK / 8, (uint32_t*)tp, s0, s1, threadIdx.x, blockDim.x);
+    copy_out(stg[1], true, H.BV / 8, (uint32_t*)(tp + 8 * H.BK), s0, s1, threadIdx.x, blockDim.x);
 }
 
 __global__ void flush_kernel(uint4* p, size_t n) {
