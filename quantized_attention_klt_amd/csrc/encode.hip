@@ -36,11 +36,30 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+#define LDS_AS __attribute__((address_space(3)))
+
 // quantizer: t = c * inv (one fp32 rounding), code = clamp(floor(t) + 2^(b-1), 0, 2^b - 1)
 // (b >= 1)
 __device__ __forceinline__ uint32_t quantize(float c, float inv, int b) {
     const float v = floorf(__fmul_rn(c, inv)) + (float)(1 << (b - 1));
     return (uint32_t)__builtin_amdgcn_fmed3f(v, 0.0f, (float)((1 << b) - 1));
+}
+
+// LDS-only workgroup barrier: this wave's LDS operations are complete, then s_barrier
+// (vector memory operations in flight are not waited for; their waits are explicit)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// wait until at most n of this wave's vector memory operations are outstanding (they
+// complete in issue order; n is clamped to 15, which only waits longer)
+__device__ __forceinline__ void wait_vm(int n) {
+    switch (n) {
+#define AATC_W(k) \
+    case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+        AATC_W(0) AATC_W(1) AATC_W(2) AATC_W(3) AATC_W(4) AATC_W(5) AATC_W(6) AATC_W(7)
+        AATC_W(8) AATC_W(9) AATC_W(10) AATC_W(11) AATC_W(12) AATC_W(13) AATC_W(14)
+#undef AATC_W
+        default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+    }
 }
 
 // A tile's block (keys or values) is assembled in LDS byte-major, every code's fields OR-ed
@@ -59,20 +78,31 @@ struct PieceTab {
     int16_t first[aatc::kMaxD + 8];
 };
 
-__device__ void stage_pieces(const DevHead& H, bool isV, PieceTab& pt, int tid, int nthreads) {
+__device__ void stage_pieces(const DevHead& H, bool isV, LDS_AS PieceTab* pt, int tid, int nthreads) {
     const uint32_t* p = isV ? H.cpieceV : H.cpieceK;
     const int16_t* f = isV ? H.cfirstV : H.cfirstK;
     const int np = isV ? H.nfV : H.nfK;
-    for (int i = tid; i < np; i += nthreads) pt.piece[i] = p[i];
-    for (int i = tid; i <= H.d; i += nthreads) pt.first[i] = f[i];
+    for (int i = tid; i < np; i += nthreads) pt->piece[i] = p[i];
+    for (int i = tid; i <= H.d; i += nthreads) pt->first[i] = f[i];
+}
+
+__device__ __forceinline__ void lds_or(LDS_AS uint32_t* p, uint32_t v) { (void)__atomic_fetch_or(p, v, __ATOMIC_RELAXED); }
+
+// The same LDS OR written as an instruction of its own, at p + OFF bytes.  The compiler
+// makes every LDS atomic wait for all direct-to-LDS copies in flight (vmcnt(0)), which would
+// stall the tile stream; this one it does not see.  LDS operations complete in order, so its
+// own LDS waits stay sufficient, and the workgroup barrier waits for all LDS operations.
+template <int OFF>
+__device__ __forceinline__ void lds_or_async(LDS_AS uint32_t* p, uint32_t v) {
+    asm volatile("ds_or_b32 %0, %1 offset:%2" ::"v"(p), "v"(v), "i"(OFF) : "memory");
 }
 
 // every field of channel j's code of slot s, OR-ed into the staged block
-__device__ __forceinline__ void scatter_code(uint32_t* stg, const PieceTab& pt, int j, int s, uint32_t code) {
-    for (int p = pt.first[j]; p < pt.first[j + 1]; ++p) {
-        const uint32_t pc = pt.piece[p];
+__device__ __forceinline__ void scatter_code(LDS_AS uint32_t* stg, const LDS_AS PieceTab* pt, int j, int s, uint32_t code) {
+    for (int p = pt->first[j]; p < pt->first[j + 1]; ++p) {
+        const uint32_t pc = pt->piece[p];
         const int q = pc & 0xff, pos = (pc >> 8) & 7, wd = (pc >> 12) & 15, e = (pc >> 16) & 15;
-        atomicOr(&stg[q * kStageRow + (s >> 2)], ((code >> e) & ((1u << wd) - 1u)) << (8 * (s & 3) + pos));
+        lds_or(stg + q * kStageRow + (s >> 2), ((code >> e) & ((1u << wd) - 1u)) << (8 * (s & 3) + pos));
     }
 }
 
@@ -82,7 +112,7 @@ __device__ __forceinline__ void scatter_code(uint32_t* stg, const PieceTab& pt, 
 // Stored bytes carry bit 7 inverted; a value word shared with slots outside [s0, s1) keeps
 // their stored bytes (the staging holds codes of every slot of the tile, so the bytes of
 // those slots are masked out).
-__device__ void copy_out(uint32_t* stg, bool isV, int nbytes, uint32_t* dst, int s0, int s1, int tid, int nthreads) {
+__device__ void copy_out(LDS_AS uint32_t* stg, bool isV, int nbytes, uint32_t* dst, int s0, int s1, int tid, int nthreads) {
     const int nitems = 4 * nbytes;  // 16 nbytes tile words, 4 per item
     for (int it = tid; it < nitems; it += nthreads) {
         uint32_t out[4];
@@ -151,6 +181,9 @@ __device__ __forceinline__ uint8_t* tile_ptr(uint8_t* cache, int layer, int n_se
 // atomic per field (the LDS word is the field's base plus an immediate offset per token).
 // ------------------------------------------------------------------------------------
 template <int D>
+constexpr size_t encode_lds_bytes() { return 2 * 64 * D * 2 + 4 * kStageWords + sizeof(PieceTab); }
+
+template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void encode_mfma_kernel(
     const DevHead* __restrict__ blob, uint8_t* __restrict__ cache, int layer, int n_kv, int64_t n_tiles_cap,
     int tile_bytes, SeqArgs sa, int64_t n_tokens, int64_t ntiles, const uint16_t* __restrict__ K,
@@ -160,9 +193,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
     constexpr int KS = D / 32;         // k-steps
     constexpr int XB = 64 * D * 2;     // bytes of one x tile
     constexpr int NLD = 64 * CH / 256;  // chunk loads per thread
-    __shared__ __attribute__((aligned(16))) uint8_t xs[2][XB];
-    __shared__ __attribute__((aligned(16))) uint32_t stg[kStageWords];
-    __shared__ PieceTab pt;
+    // LDS (one dynamic array): two x tiles, the staged block, the field table
+    extern __shared__ __attribute__((aligned(16))) uint8_t esm_generic[];
+    LDS_AS uint8_t* const esm = (LDS_AS uint8_t*)esm_generic;
+    LDS_AS uint8_t* const xs0 = esm;
+    LDS_AS uint8_t* const xs1 = esm + XB;
+    LDS_AS uint32_t* const stg = (LDS_AS uint32_t*)(esm + 2 * XB);
+    LDS_AS PieceTab* const pt = (LDS_AS PieceTab*)(esm + 2 * XB + 4 * kStageWords);
     const int h = blockIdx.y >> 1, zi = blockIdx.z;
     const bool isV = (blockIdx.y & 1) != 0;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
@@ -200,42 +237,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
     const int nbytes = (isV ? H.BV : H.BK) / 8;
     const int boff = isV ? 8 * H.BK : 0;  // block offset in the tile
     __syncthreads();  // field table staged, staging clear
-    // this lane's channels: their fields (usually one) are pt.piece[pf[cbw] .. pl[cbw])
+    // this lane's channels: their fields (usually one) are pt->piece[pf[cbw] .. pl[cbw])
     int pf[CBW], pl[CBW];
 #pragma unroll
     for (int cbw = 0; cbw < CBW; ++cbw) {
-        pf[cbw] = pt.first[jj[cbw]];
-        pl[cbw] = pt.first[jj[cbw] + 1];
+        pf[cbw] = pt->first[jj[cbw]];
+        pl[cbw] = pt->first[jj[cbw] + 1];
     }
-    // x tile of tile index k (chunk n of this thread: token t = ci / CH, chunk ci % CH);
-    // slots outside the call's tokens read as zero
-    auto load_x = [&](int64_t tile, u32x4 (&r)[NLD]) {
-        const int64_t tok0 = tile * kTile;
+    // x tile of tile index k into LDS by direct global->LDS copies: copy n of wave w fills
+    // the 64 chunk positions p = 64 (NLD w + n) + lane (token t = p / CH, position p % CH),
+    // and position p holds the token's chunk (p % CH) ^ (t mod CH) (the swizzle is in the
+    // source addresses).  Slots outside the call's tokens copy the call's first token (their
+    // codes are never stored).  The copies carry the non-temporal hint: inputs are read once.
+    auto copy_x = [&](int64_t tl, LDS_AS uint8_t* xd) {
+        const int64_t tok0 = tl * kTile;
 #pragma unroll
         for (int n = 0; n < NLD; ++n) {
-            const int ci = tid + 256 * n, t = ci / CH, kc = ci % CH;
-            const int64_t tt = tok0 + t - start;  // token index in this call's input
-            r[n] = (tt >= 0 && tt < n_tokens) ? *(const u32x4*)(X + tt * xstride + 8 * kc) : u32x4{0u, 0u, 0u, 0u};
+            const int p = 64 * (NLD * w + n) + lane, t = p / CH, kc = (p % CH) ^ (t & (CH - 1));
+            int64_t tt = tok0 + t - start;  // token index in this call's input
+            tt = tt < 0 || tt >= n_tokens ? 0 : tt;
+            __builtin_amdgcn_global_load_lds((const void*)(X + tt * xstride + 8 * kc),
+                                             (LDS_AS void*)(xd + 1024 * (NLD * w + n)), 16, 0, 2);
         }
     };
-    auto store_x = [&](int buf, const u32x4 (&r)[NLD]) {
-#pragma unroll
-        for (int n = 0; n < NLD; ++n) {
-            const int ci = tid + 256 * n, t = ci / CH, kc = ci % CH;
-            *(u32x4*)(&xs[buf][t * 2 * D + 16 * (kc ^ (t & (CH - 1)))]) = r[n];
-        }
-    };
+    // this wave's copy-out stores per full tile: one 16-byte store per item round it takes part in
+    const int n_items = 4 * nbytes;
+    const int st_full = max(0, (n_items - 64 * w + 255) / 256);
     int64_t tile = blockIdx.x;
-    u32x4 xr[NLD];
-    if (tile < ntiles) {
-        load_x(first_tile + tile, xr);
-        store_x(0, xr);
-    }
-    __syncthreads();
-    for (int k = 0; tile < ntiles; ++k, tile += gridDim.x) {
-        const int buf = k & 1;
+    if (tile < ntiles) copy_x(first_tile + tile, xs0);
+    int st_prev = 0;  // stores issued by the previous tile's copy-out (-1: not counted)
+    // one tile: its x in xc, the next tile's copied into xn
+    auto step = [&](const LDS_AS uint8_t* xc, LDS_AS uint8_t* xn) {
         const int64_t tile_n = tile + gridDim.x;
-        if (tile_n < ntiles) load_x(first_tile + tile_n, xr);  // next tile, in flight during the MFMAs
+        // this tile's copies have landed (the previous copy-out's stores, issued after them,
+        // may still be in flight); every wave's, and every wave is past the previous tile
+        if (st_prev < 0)
+            wait_vm(0);
+        else
+            wait_vm(st_prev);
+        lds_barrier();
+        if (tile_n < ntiles) copy_x(first_tile + tile_n, xn);  // next tile, in flight during this one
         f32x4 acc[CBW][4];
 #pragma unroll
         for (int cbw = 0; cbw < CBW; ++cbw)
@@ -246,7 +287,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
             const int t = 16 * tb + c;  // A row: token
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 av = *(const bf16x8*)(&xs[buf][t * 2 * D + 16 * ((4 * ks + g) ^ (t & (CH - 1)))]);
+                const bf16x8 av = *(const LDS_AS bf16x8*)(xc + t * 2 * D + 16 * ((4 * ks + g) ^ (t & (CH - 1))));
 #pragma unroll
                 for (int cbw = 0; cbw < CBW; ++cbw) {
                     acc[cbw][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh[cbw][ks], acc[cbw][tb], 0, 0, 0);
@@ -264,25 +305,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
 #pragma unroll
                 for (int e = 0; e < 4; ++e) code[4 * tb + e] = quantize(acc[cbw][tb][e], inv[cbw], bits[cbw]);
             for (int p = pf[cbw]; p < pl[cbw]; ++p) {
-                const uint32_t pc = pt.piece[p];
+                const uint32_t pc = pt->piece[p];
                 const int q = pc & 0xff, pos = (pc >> 8) & 7, e0 = (pc >> 16) & 15;
                 const uint32_t mask = (1u << ((pc >> 12) & 15)) - 1u;
-                uint32_t* base = stg + q * kStageRow + g;
+                LDS_AS uint32_t* base = stg + q * kStageRow + g;
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) atomicOr(base + 4 * tb, ((code[4 * tb + e] >> e0) & mask) << (8 * e + pos));
+                for (int e = 0; e < 4; ++e) {
+                    const int sh = 8 * e + pos;
+                    lds_or_async<0>(base, ((code[e] >> e0) & mask) << sh);
+                    lds_or_async<16>(base, ((code[4 + e] >> e0) & mask) << sh);
+                    lds_or_async<32>(base, ((code[8 + e] >> e0) & mask) << sh);
+                    lds_or_async<48>(base, ((code[12 + e] >> e0) & mask) << sh);
+                }
             }
         }
-        __syncthreads();
+        lds_barrier();
         const int64_t tok0 = (first_tile + tile) * kTile;
         const int s0 = (int)max(start - tok0, (int64_t)0);
         const int s1 = (int)min(start + n_tokens - tok0, (int64_t)kTile);
         uint8_t* tp = tile_ptr(cache, layer, n_seqs_cache, seq, n_kv, h, n_tiles_cap, first_tile + tile, tile_bytes);
         copy_out(stg, isV, nbytes, (uint32_t*)(tp + boff), s0, s1, tid, 256);
-        if (tile_n < ntiles) store_x(buf ^ 1, xr);
-        __syncthreads();
+        st_prev = (s0 == 0 && s1 == kTile) ? st_full : -1;
+        tile = tile_n;
+    };
+    while (tile < ntiles) {
+        step(xs0, xs1);
+        if (tile >= ntiles) break;
+        step(xs1, xs0);
     }
+    wait_vm(0);
 }
 
 // ------------------------------------------------------------------------------------
@@ -304,8 +355,11 @@ __global__ __launch_bounds__(256) void encode_coeffs_kernel(const DevHead* __res
     const int64_t tok0 = tile * kTile;
     const int s0 = (int)std::max<int64_t>(start - tok0, 0);
     const int s1 = (int)std::min<int64_t>(start + n_tokens - tok0, kTile);
-    stage_pieces(H, false, pt[0], threadIdx.x, blockDim.x);
-    stage_pieces(H, true, pt[1], threadIdx.x, blockDim.x);
+    LDS_AS PieceTab* const ptl = (LDS_AS PieceTab*)&pt[0];
+    LDS_AS uint32_t* const sg0 = (LDS_AS uint32_t*)&stg[0][0];
+    LDS_AS uint32_t* const sg1 = (LDS_AS uint32_t*)&stg[1][0];
+    stage_pieces(H, false, ptl, threadIdx.x, blockDim.x);
+    stage_pieces(H, true, ptl + 1, threadIdx.x, blockDim.x);
     for (int i = threadIdx.x; i < 2 * kStageWords; i += blockDim.x) stg[i / kStageWords][i % kStageWords] = 0u;
     __syncthreads();
     for (int i = threadIdx.x; i < (s1 - s0) * 2 * d; i += blockDim.x) {
@@ -313,12 +367,12 @@ __global__ __launch_bounds__(256) void encode_coeffs_kernel(const DevHead* __res
         const int64_t t = tok0 + s - start;  // token index in this call's input
         const float cf = coeffs[((t * n_kv + h) * 2 + kv) * d + j];
         const int b = kv ? H.bitsV[j] : H.bitsK[j];
-        if (b) scatter_code(stg[kv], pt[kv], j, s, quantize(cf, kv ? H.invV[j] : H.invK[j], b));
+        if (b) scatter_code(kv ? sg1 : sg0, ptl + kv, j, s, quantize(cf, kv ? H.invV[j] : H.invK[j], b));
     }
     __syncthreads();
     uint8_t* tp = tile_ptr(cache, layer, n_seqs_cache, sa.seq[zi], n_kv, h, n_tiles_cap, tile, tile_bytes);
-    copy_out(stg[0], false, H.BK / 8, (uint32_t*)tp, s0, s1, threadIdx.x, blockDim.x);
-    copy_out(stg[1], true, H.BV / 8, (uint32_t*)(tp + 8 * H.BK), s0, s1, threadIdx.x, blockDim.x);
+    copy_out(sg0, false, H.BK / 8, (uint32_t*)tp, s0, s1, threadIdx.x, blockDim.x);
+    copy_out(sg1, true, H.BV / 8, (uint32_t*)(tp + 8 * H.BK), s0, s1, threadIdx.x, blockDim.x);
 }
 
 __global__ void flush_kernel(uint4* p, size_t n) {
@@ -405,11 +459,11 @@ static int encode_common(const aatc_codebook* cb, const void* d_blob, const aatc
             const unsigned wx = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ntiles, kEncodeSlots / units));
             const dim3 grid(wx, (unsigned)(2 * cb->n_kv), (unsigned)used);
             if (d == 64)
-                hipLaunchKernelGGL(encode_mfma_kernel<64>, grid, dim3(256), 0, (hipStream_t)stream, blob,
+                hipLaunchKernelGGL(encode_mfma_kernel<64>, grid, dim3(256), encode_lds_bytes<64>(), (hipStream_t)stream, blob,
                                    (uint8_t*)cache->data, layer, cb->n_kv, ncap, tile_bytes, sa, n_tokens, ntiles, Kz, Vz,
                                    cache->n_seqs);
             else
-                hipLaunchKernelGGL(encode_mfma_kernel<128>, grid, dim3(256), 0, (hipStream_t)stream, blob,
+                hipLaunchKernelGGL(encode_mfma_kernel<128>, grid, dim3(256), encode_lds_bytes<128>(), (hipStream_t)stream, blob,
                                    (uint8_t*)cache->data, layer, cb->n_kv, ncap, tile_bytes, sa, n_tokens, ntiles, Kz, Vz,
                                    cache->n_seqs);
         }
