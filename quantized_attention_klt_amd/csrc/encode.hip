@@ -237,12 +237,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
     const int nbytes = (isV ? H.BV : H.BK) / 8;
     const int boff = isV ? 8 * H.BK : 0;  // block offset in the tile
     __syncthreads();  // field table staged, staging clear
-    // this lane's channels: their fields (usually one) are pt->piece[pf[cbw] .. pl[cbw])
-    int pf[CBW], pl[CBW];
+    // this lane's channels: their fields (usually one) are pt->piece[pf[cbw] .. pl[cbw]); the
+    // first (code bits from 0) as registers: staged word of its record byte for this lane's
+    // slots 4g .. 4g + 3, bit position, per-byte mask (0: no field)
+    int pf[CBW], pl[CBW], pos0[CBW];
+    LDS_AS uint32_t* base0[CBW];
+    uint32_t mask0[CBW];
 #pragma unroll
     for (int cbw = 0; cbw < CBW; ++cbw) {
         pf[cbw] = pt->first[jj[cbw]];
         pl[cbw] = pt->first[jj[cbw] + 1];
+        const uint32_t pc = pt->piece[min(pf[cbw], aatc::kMaxFields - 1)];
+        base0[cbw] = stg + (pc & 0xff) * kStageRow + g;
+        pos0[cbw] = (pc >> 8) & 7;
+        mask0[cbw] = pl[cbw] > pf[cbw] ? ((1u << ((pc >> 12) & 15)) - 1u) * 0x01010101u : 0u;
     }
     // x tile of tile index k into LDS by direct global->LDS copies: copy n of wave w fills
     // the 64 chunk positions p = 64 (NLD w + n) + lane (token t = p / CH, position p % CH),
@@ -295,28 +303,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
                 }
             }
         }
-        // codes of tokens 16 tb + 4 g + e (staged word q * kStageRow + 4 tb + g, byte e),
-        // OR-ed into the staging field by field
+        // codes of tokens 16 tb + 4 g + e: the four of one tb share staged word q * kStageRow +
+        // 4 tb + g (byte e), so they are packed into one word and OR-ed with one operation per
+        // field (the per-byte mask keeps a field's bits; later fields shift the code down)
 #pragma unroll
         for (int cbw = 0; cbw < CBW; ++cbw) {
-            uint32_t code[16];
+            uint32_t c4[4];
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
+            for (int tb = 0; tb < 4; ++tb) {
+                uint32_t v = quantize(acc[cbw][tb][0], inv[cbw], bits[cbw]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) code[4 * tb + e] = quantize(acc[cbw][tb][e], inv[cbw], bits[cbw]);
-            for (int p = pf[cbw]; p < pl[cbw]; ++p) {
+                for (int e = 1; e < 4; ++e) v |= quantize(acc[cbw][tb][e], inv[cbw], bits[cbw]) << (8 * e);
+                c4[tb] = v;
+            }
+            if (mask0[cbw]) {
+                lds_or_async<0>(base0[cbw], (c4[0] & mask0[cbw]) << pos0[cbw]);
+                lds_or_async<16>(base0[cbw], (c4[1] & mask0[cbw]) << pos0[cbw]);
+                lds_or_async<32>(base0[cbw], (c4[2] & mask0[cbw]) << pos0[cbw]);
+                lds_or_async<48>(base0[cbw], (c4[3] & mask0[cbw]) << pos0[cbw]);
+            }
+            for (int p = pf[cbw] + 1; p < pl[cbw]; ++p) {  // the rest of a split channel
                 const uint32_t pc = pt->piece[p];
-                const int q = pc & 0xff, pos = (pc >> 8) & 7, e0 = (pc >> 16) & 15;
-                const uint32_t mask = (1u << ((pc >> 12) & 15)) - 1u;
-                LDS_AS uint32_t* base = stg + q * kStageRow + g;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int sh = 8 * e + pos;
-                    lds_or_async<0>(base, ((code[e] >> e0) & mask) << sh);
-                    lds_or_async<16>(base, ((code[4 + e] >> e0) & mask) << sh);
-                    lds_or_async<32>(base, ((code[8 + e] >> e0) & mask) << sh);
-                    lds_or_async<48>(base, ((code[12 + e] >> e0) & mask) << sh);
-                }
+                LDS_AS uint32_t* base = stg + (pc & 0xff) * kStageRow + g;
+                const int pos = (pc >> 8) & 7, e0 = (pc >> 16) & 15;
+                const uint32_t mask = ((1u << ((pc >> 12) & 15)) - 1u) * 0x01010101u;
+                lds_or_async<0>(base, ((c4[0] >> e0) & mask) << pos);
+                lds_or_async<16>(base, ((c4[1] >> e0) & mask) << pos);
+                lds_or_async<32>(base, ((c4[2] >> e0) & mask) << pos);
+                lds_or_async<48>(base, ((c4[3] >> e0) & mask) << pos);
             }
         }
         lds_barrier();
