@@ -112,54 +112,68 @@ __device__ __forceinline__ void scatter_code(LDS_AS uint32_t* stg, const LDS_AS 
 // Stored bytes carry bit 7 inverted; a value word shared with slots outside [s0, s1) keeps
 // their stored bytes (the staging holds codes of every slot of the tile, so the bytes of
 // those slots are masked out).
-__device__ void copy_out(LDS_AS uint32_t* stg, bool isV, int nbytes, uint32_t* dst, int s0, int s1, int tid, int nthreads) {
-    const int nitems = 4 * nbytes;  // 16 nbytes tile words, 4 per item
-    for (int it = tid; it < nitems; it += nthreads) {
-        uint32_t out[4];
-        int word0;  // first tile word of the item
-        uint32_t keep[4];
-        if (!isV) {
-            const int r = it >> 4, u = it & 15;
-            uint32_t W[4];
+template <bool ISV>
+__device__ __forceinline__ void staged_item(LDS_AS uint32_t* stg, int it, uint32_t (&out)[4], int& word0) {
+    if (!ISV) {
+        const int r = it >> 4, u = it & 15;
+        uint32_t W[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                W[b] = stg[(4 * r + b) * kStageRow + u];
-                stg[(4 * r + b) * kStageRow + u] = 0u;
-            }
-            const uint32_t t0 = __builtin_amdgcn_perm(W[1], W[0], 0x05010400u);
-            const uint32_t t1 = __builtin_amdgcn_perm(W[3], W[2], 0x05010400u);
-            const uint32_t t2 = __builtin_amdgcn_perm(W[1], W[0], 0x07030602u);
-            const uint32_t t3 = __builtin_amdgcn_perm(W[3], W[2], 0x07030602u);
-            out[0] = __builtin_amdgcn_perm(t1, t0, 0x05040100u);  // slot 4u: bytes of rows 4r .. 4r + 3
-            out[1] = __builtin_amdgcn_perm(t1, t0, 0x07060302u);
-            out[2] = __builtin_amdgcn_perm(t3, t2, 0x05040100u);
-            out[3] = __builtin_amdgcn_perm(t3, t2, 0x07060302u);
-            word0 = 64 * r + 4 * u;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) keep[k] = (4 * u + k < s0 || 4 * u + k >= s1) ? 0xFFFFFFFFu : 0u;
-        } else {
-            const int q = it >> 2, v = it & 3;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                out[k] = stg[q * kStageRow + 4 * v + k];
-                stg[q * kStageRow + 4 * v + k] = 0u;
-                keep[k] = 0u;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int s = 16 * v + 4 * k + b;
-                    if (s < s0 || s >= s1) keep[k] |= 0xFFu << (8 * b);
-                }
-            }
-            word0 = 16 * q + 4 * v;
+        for (int b = 0; b < 4; ++b) {
+            W[b] = stg[(4 * r + b) * kStageRow + u];
+            stg[(4 * r + b) * kStageRow + u] = 0u;
         }
-        if ((keep[0] | keep[1] | keep[2] | keep[3]) == 0u) {  // the common case: one 16-byte store
+        const uint32_t t0 = __builtin_amdgcn_perm(W[1], W[0], 0x05010400u);
+        const uint32_t t1 = __builtin_amdgcn_perm(W[3], W[2], 0x05010400u);
+        const uint32_t t2 = __builtin_amdgcn_perm(W[1], W[0], 0x07030602u);
+        const uint32_t t3 = __builtin_amdgcn_perm(W[3], W[2], 0x07030602u);
+        out[0] = __builtin_amdgcn_perm(t1, t0, 0x05040100u);  // slot 4u: bytes of rows 4r .. 4r + 3
+        out[1] = __builtin_amdgcn_perm(t1, t0, 0x07060302u);
+        out[2] = __builtin_amdgcn_perm(t3, t2, 0x05040100u);
+        out[3] = __builtin_amdgcn_perm(t3, t2, 0x07060302u);
+        word0 = 64 * r + 4 * u;
+    } else {
+        const int q = it >> 2, v = it & 3;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            out[k] = stg[q * kStageRow + 4 * v + k];
+            stg[q * kStageRow + 4 * v + k] = 0u;
+        }
+        word0 = 16 * q + 4 * v;
+    }
+}
+
+template <bool ISV>
+__device__ void copy_out(LDS_AS uint32_t* stg, int nbytes, uint32_t* dst, int s0, int s1, int tid, int nthreads) {
+    const int nitems = 4 * nbytes;  // 16 nbytes tile words, 4 per item
+    if (s0 == 0 && s1 == kTile) {   // a whole tile: one 16-byte store per item
+        for (int it = tid; it < nitems; it += nthreads) {
+            uint32_t out[4];
+            int word0;
+            staged_item<ISV>(stg, it, out, word0);
             *(u32x4*)(dst + word0) =
                 u32x4{out[0] ^ 0x80808080u, out[1] ^ 0x80808080u, out[2] ^ 0x80808080u, out[3] ^ 0x80808080u};
-        } else {
+        }
+        return;
+    }
+    for (int it = tid; it < nitems; it += nthreads) {
+        uint32_t out[4];
+        int word0;
+        staged_item<ISV>(stg, it, out, word0);
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (keep[k] != 0xFFFFFFFFu)
-                    dst[word0 + k] = ((out[k] ^ 0x80808080u) & ~keep[k]) | (keep[k] ? dst[word0 + k] & keep[k] : 0u);
+        for (int k = 0; k < 4; ++k) {
+            uint32_t keep = 0u;
+            if (!ISV) {
+                const int s = 4 * (it & 15) + k;
+                if (s < s0 || s >= s1) keep = 0xFFFFFFFFu;
+            } else {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int s = 16 * (it & 3) + 4 * k + b;
+                    if (s < s0 || s >= s1) keep |= 0xFFu << (8 * b);
+                }
+            }
+            if (keep != 0xFFFFFFFFu)
+                dst[word0 + k] = ((out[k] ^ 0x80808080u) & ~keep) | (keep ? dst[word0 + k] & keep : 0u);
         }
     }
 }
@@ -183,11 +197,12 @@ __device__ __forceinline__ uint8_t* tile_ptr(uint8_t* cache, int layer, int n_se
 template <int D>
 constexpr size_t encode_lds_bytes() { return 2 * 64 * D * 2 + 4 * kStageWords + sizeof(PieceTab); }
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void encode_mfma_kernel(
-    const DevHead* __restrict__ blob, uint8_t* __restrict__ cache, int layer, int n_kv, int64_t n_tiles_cap,
-    int tile_bytes, SeqArgs sa, int64_t n_tokens, int64_t ntiles, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, int n_seqs_cache) {
+template <int D, bool isV>
+__device__ __forceinline__ void encode_mfma_body(const DevHead* __restrict__ blob, uint8_t* __restrict__ cache,
+                                                 int layer, int n_kv, int64_t n_tiles_cap, int tile_bytes,
+                                                 const SeqArgs& sa, int64_t n_tokens, int64_t ntiles,
+                                                 const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                                 int n_seqs_cache) {
     constexpr int CH = D / 8;          // 16-byte chunks per token row
     constexpr int CBW = D / 64;        // 16-channel column blocks per wave
     constexpr int KS = D / 32;         // k-steps
@@ -201,7 +216,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
     LDS_AS uint32_t* const stg = (LDS_AS uint32_t*)(esm + 2 * XB);
     LDS_AS PieceTab* const pt = (LDS_AS PieceTab*)(esm + 2 * XB + 4 * kStageWords);
     const int h = blockIdx.y >> 1, zi = blockIdx.z;
-    const bool isV = (blockIdx.y & 1) != 0;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
     const DevHead& H = blob[layer * n_kv + h];
     const uint16_t* X = (isV ? V : K) + ((int64_t)zi * n_tokens * n_kv + h) * D;  // token t at X + t * n_kv * D
@@ -236,22 +250,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
     }
     const int nbytes = (isV ? H.BV : H.BK) / 8;
     const int boff = isV ? 8 * H.BK : 0;  // block offset in the tile
-    __syncthreads();  // field table staged, staging clear
-    // this lane's channels: their fields (usually one) are pt->piece[pf[cbw] .. pl[cbw]); the
-    // first (code bits from 0) as registers: staged word of its record byte for this lane's
-    // slots 4g .. 4g + 3, bit position, per-byte mask (0: no field)
-    int pf[CBW], pl[CBW], pos0[CBW];
-    LDS_AS uint32_t* base0[CBW];
-    uint32_t mask0[CBW];
-#pragma unroll
-    for (int cbw = 0; cbw < CBW; ++cbw) {
-        pf[cbw] = pt->first[jj[cbw]];
-        pl[cbw] = pt->first[jj[cbw] + 1];
-        const uint32_t pc = pt->piece[min(pf[cbw], aatc::kMaxFields - 1)];
-        base0[cbw] = stg + (pc & 0xff) * kStageRow + g;
-        pos0[cbw] = (pc >> 8) & 7;
-        mask0[cbw] = pl[cbw] > pf[cbw] ? ((1u << ((pc >> 12) & 15)) - 1u) * 0x01010101u : 0u;
-    }
     // x tile of tile index k into LDS by direct global->LDS copies: copy n of wave w fills
     // the 64 chunk positions p = 64 (NLD w + n) + lane (token t = p / CH, position p % CH),
     // and position p holds the token's chunk (p % CH) ^ (t mod CH) (the swizzle is in the
@@ -268,11 +266,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
                                              (LDS_AS void*)(xd + 1024 * (NLD * w + n)), 16, 0, 2);
         }
     };
+    int64_t tile = blockIdx.x;
+    if (tile < ntiles) copy_x(first_tile + tile, xs0);  // the first tile streams during the set-up
+    lds_barrier();  // field table staged, staging clear
+    // this lane's channels: their fields (usually one) are pt->piece[pf[cbw] .. pl[cbw]); the
+    // first (code bits from 0) as registers: staged word of its record byte for this lane's
+    // slots 4g .. 4g + 3, bit position, per-byte mask (0: no field)
+    int pf[CBW], pl[CBW], pos0[CBW];
+    LDS_AS uint32_t* base0[CBW];
+    uint32_t mask0[CBW];
+#pragma unroll
+    for (int cbw = 0; cbw < CBW; ++cbw) {
+        pf[cbw] = pt->first[jj[cbw]];
+        pl[cbw] = pt->first[jj[cbw] + 1];
+        const uint32_t pc = pt->piece[min(pf[cbw], aatc::kMaxFields - 1)];
+        base0[cbw] = stg + (pc & 0xff) * kStageRow + g;
+        pos0[cbw] = (pc >> 8) & 7;
+        mask0[cbw] = pl[cbw] > pf[cbw] ? ((1u << ((pc >> 12) & 15)) - 1u) * 0x01010101u : 0u;
+    }
     // this wave's copy-out stores per full tile: one 16-byte store per item round it takes part in
     const int n_items = 4 * nbytes;
     const int st_full = max(0, (n_items - 64 * w + 255) / 256);
-    int64_t tile = blockIdx.x;
-    if (tile < ntiles) copy_x(first_tile + tile, xs0);
     int st_prev = 0;  // stores issued by the previous tile's copy-out (-1: not counted)
     // one tile: its x in xc, the next tile's copied into xn
     auto step = [&](const LDS_AS uint8_t* xc, LDS_AS uint8_t* xn) {
@@ -338,7 +352,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
         const int s0 = (int)max(start - tok0, (int64_t)0);
         const int s1 = (int)min(start + n_tokens - tok0, (int64_t)kTile);
         uint8_t* tp = tile_ptr(cache, layer, n_seqs_cache, seq, n_kv, h, n_tiles_cap, first_tile + tile, tile_bytes);
-        copy_out(stg, isV, nbytes, (uint32_t*)(tp + boff), s0, s1, tid, 256);
+        copy_out<isV>(stg, nbytes, (uint32_t*)(tp + boff), s0, s1, tid, 256);
         st_prev = (s0 == 0 && s1 == kTile) ? st_full : -1;
         tile = tile_n;
     };
@@ -348,6 +362,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
         step(xs1, xs0);
     }
     wait_vm(0);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void encode_mfma_kernel(
+    const DevHead* __restrict__ blob, uint8_t* __restrict__ cache, int layer, int n_kv, int64_t n_tiles_cap,
+    int tile_bytes, SeqArgs sa, int64_t n_tokens, int64_t ntiles, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, int n_seqs_cache) {
+    if (blockIdx.y & 1)
+        encode_mfma_body<D, true>(blob, cache, layer, n_kv, n_tiles_cap, tile_bytes, sa, n_tokens, ntiles, K, V,
+                                  n_seqs_cache);
+    else
+        encode_mfma_body<D, false>(blob, cache, layer, n_kv, n_tiles_cap, tile_bytes, sa, n_tokens, ntiles, K, V,
+                                   n_seqs_cache);
 }
 
 // ------------------------------------------------------------------------------------
@@ -385,8 +412,8 @@ __global__ __launch_bounds__(256) void encode_coeffs_kernel(const DevHead* __res
     }
     __syncthreads();
     uint8_t* tp = tile_ptr(cache, layer, n_seqs_cache, sa.seq[zi], n_kv, h, n_tiles_cap, tile, tile_bytes);
-    copy_out(sg0, false, H.BK / 8, (uint32_t*)tp, s0, s1, threadIdx.x, blockDim.x);
-    copy_out(sg1, true, H.BV / 8, (uint32_t*)(tp + 8 * H.BK), s0, s1, threadIdx.x, blockDim.x);
+    copy_out<false>(sg0, H.BK / 8, (uint32_t*)tp, s0, s1, threadIdx.x, blockDim.x);
+    copy_out<true>(sg1, H.BV / 8, (uint32_t*)(tp + 8 * H.BK), s0, s1, threadIdx.x, blockDim.x);
 }
 
 __global__ void flush_kernel(uint4* p, size_t n) {
