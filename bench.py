@@ -27,8 +27,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_kernel_llama128k_pmc.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "quantized_attention_klt_amd", "csrc", "decode.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "quantized_attention_klt_amd", "csrc")
+DECODE_PMC = (os.path.join(PROFILES, "decode_kernel_llama128k_pmc.txt"), os.path.join(CSRC, "decode.hip"))
+ENCODE_PMC = (os.path.join(PROFILES, "encode_kernel_llama128k_pmc.txt"), os.path.join(CSRC, "encode.hip"))
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "decode-attn effective HBM GB/s (% of peak) + encode tokens/s, 128k ctx, 2.75 b/elem"
 
@@ -64,21 +66,21 @@ def build_inputs(wname: str, ctx: int):
     return w, cb, kb, vb, qb, t2 - t0
 
 
-def source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the split-decode kernel from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or None when the
-    summary is missing or was taken from another revision of the kernel source."""
+def measured_traffic(summary: str, source: str):
+    """HBM bytes per launch of a kernel from its committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, scaled by a plain copy of known size), or None when the summary is missing
+    or was taken from another revision of the kernel source."""
     try:
-        fields = dict(l.split(":", 1) for l in open(PMC_SUMMARY) if ":" in l and not l.startswith("#"))
+        fields = dict(l.split(":", 1) for l in open(summary) if ":" in l and not l.startswith("#"))
     except OSError:
         return None
     fields = {k.strip(): v.strip() for k, v in fields.items()}
-    if fields.get("source_sha256_16") != source_hash():
+    if fields.get("source_sha256_16") != source_hash(source):
         return None
     try:
         return int(float(fields["hbm_bytes_per_launch"]))
@@ -247,14 +249,15 @@ def main():
         "wall_s_timed_region": round(wall, 3),
         "roofline": {"kernel": "decode_kernel (split decode: scores, online softmax, value sums)", "bound": "hbm",
                      "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(*DECODE_PMC),
                      "algorithmic_bytes": kern_bytes, "kernel_ms": round(kern_s * 1e3, 4),
-                     "source_sha256_16": source_hash()},
+                     "source_sha256_16": source_hash(DECODE_PMC[1])},
         "roofline_encode": {"kernel": "encode", "bound": "hbm", "achieved": round(enc_gbs, 2),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(enc_gbs / HBM_PEAK_GBS, 4),
                             "mfma_tflops": round(enc_flops / enc_s / 1e12, 2),
                             "mfma_frac": round(enc_flops / enc_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-                            "traffic": None, "algorithmic_bytes": enc_bytes},
+                            "traffic": measured_traffic(*ENCODE_PMC), "algorithmic_bytes": enc_bytes,
+                            "source_sha256_16": source_hash(ENCODE_PMC[1])},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
