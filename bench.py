@@ -67,8 +67,16 @@ def build_inputs(wname: str, ctx: int):
 
 
 def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source's code: line comments and blank lines are dropped and
+    whitespace runs collapsed, so that only a change of the code itself invalidates the
+    counters taken on it."""
+    lines = []
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            code = " ".join(line.split("//", 1)[0].split())
+            if code:
+                lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
 def measured_traffic(summary: str, source: str):

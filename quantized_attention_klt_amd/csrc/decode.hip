@@ -7,13 +7,16 @@
 // (decoding reads the whole cache every step and is bandwidth-bound).
 //
 // Three kernels on the caller's stream.
-//   qprep  - one wave per (16-channel block, sequence, kv-head) forms q' = U_K^T q for the
-//            query heads on bf16 MFMAs, scales it by the key steps (and log2 e / sqrt d) and
-//            finds per head the block's largest score slot value;
+//   qprep  - one workgroup per (sequence, kv-head) forms q' = U_K^T q for the query heads on
+//            bf16 MFMAs, scales it by the key steps (and log2 e / sqrt d), and writes the
+//            decode kernel's score operands: per key field a query weight (the field's code
+//            shift over its bit position), scaled per head so the largest is 127 and split
+//            into three int8 digits laid out as MFMA A operands, plus per head the digit
+//            scales and the score accumulator's start value;
 //   decode - W workgroups of 4 waves share the 64-token tiles of one (sequence, kv-head).
-//     prologue - the first tiles start streaming; meanwhile the workgroup splits q'' into
-//                three int8 digits laid out as the A operands of the score MFMAs (one byte
-//                per key field, weighted by the field's code shift over its bit position);
+//     prologue - the score operands, key schedule and value columns arrive by direct
+//                global->LDS copies issued ahead of the first tiles' copies and move into
+//                registers while those tiles stream;
 //     tiles    - wave w of workgroup i takes tiles 4i + w + 4Wk and streams them through a
 //                private ring of LDS buffers (direct global->LDS loads, counted waits, no
 //                workgroup barriers in the loop).  Per tile:

@@ -188,11 +188,12 @@ __device__ __forceinline__ uint8_t* tile_ptr(uint8_t* cache, int layer, int n_se
 // and the tiles bx, bx + gridDim.x, ... of the call.  c = x (U_hi + U_lo) - bias on
 // v_mfma_f32_16x16x32_bf16: rows = tokens, columns = channels (in the encoder's channel
 // order), accumulators starting at -bias; wave w keeps the B operands (U^T hi / lo
-// fragments) of its D / 4 columns in registers for all its tiles.  The 64-token x tile is
-// staged in LDS with its 16-byte chunks XOR-swizzled by token, so that the 16 rows an
+// fragments) of its D / 4 columns in registers for all its tiles.  The 64-token x tiles
+// arrive by direct global->LDS copies into two buffers (the next tile streams while this
+// one is computed), their 16-byte chunks XOR-swizzled by token so that the 16 rows an
 // operand read touches fall in distinct banks.  Lane (g, c) quantizes tokens 16 tb + 4 g + e
-// of its channels and ORs each code's fields into the staged block: one shift and one LDS
-// atomic per field (the LDS word is the field's base plus an immediate offset per token).
+// of its channel, packs the four codes of one tb into a word (they share a staged word) and
+// ORs each field into the staged block with one LDS operation per field and four tokens.
 // ------------------------------------------------------------------------------------
 template <int D>
 constexpr size_t encode_lds_bytes() { return 2 * 64 * D * 2 + 4 * kStageWords + sizeof(PieceTab); }
