@@ -222,9 +222,9 @@ int aatc_decode_workspace_bytes(const aatc_codebook* cb, int32_t n_seqs, int64_t
  * arrays (1 <= seq_lens[s] <= max_len <= max_tokens); max_len (host) sizes the grid.
  * q: device bf16 [n_seqs][H_q][d]; out: device float32 [n_seqs][H_q][d]; workspace:
  * device scratch of aatc_decode_workspace_bytes() bytes (256-byte aligned, no
- * initialisation needed) for the transformed queries and the split partials.  Calls that
- * share a workspace must not overlap in time (same stream, or ordered).  Three kernels run
- * on `stream`: query transform, split decode over the packed tiles, merge + inverse
+ * initialisation needed) for the split partials.  Calls that share a workspace must not
+ * overlap in time (same stream, or ordered).  Two kernels run on `stream`: split decode
+ * over the packed tiles (each workgroup transforms the queries itself), merge + inverse
  * transform ("KV Cache Compression Through the Lens of Transform Coding", Methodology;
  * "Attention-Aware Transform Coding Guide", KLT section: q.k = (U_K^T q).(U_K^T k)).
  * At most 65535 sequences per call (CAPACITY beyond).

@@ -6,17 +6,15 @@
 // inverse-transformed once per query head); "Spend Bits Where Queries Look" abstract
 // (decoding reads the whole cache every step and is bandwidth-bound).
 //
-// Three kernels on the caller's stream.
-//   qprep  - one workgroup per (sequence, kv-head) forms q' = U_K^T q for the query heads on
-//            bf16 MFMAs, scales it by the key steps (and log2 e / sqrt d), and writes the
-//            decode kernel's score operands: per key field a query weight (the field's code
-//            shift over its bit position), scaled per head so the largest is 127 and split
-//            into three int8 digits laid out as MFMA A operands, plus per head the digit
-//            scales and the score accumulator's start value;
+// Two kernels on the caller's stream.
 //   decode - W workgroups of 4 waves share the 64-token tiles of one (sequence, kv-head).
-//     prologue - the score operands, key schedule and value columns arrive by direct
-//                global->LDS copies issued ahead of the first tiles' copies and move into
-//                registers while those tiles stream;
+//     prologue - every workgroup forms q' = U_K^T q for the kv-head's query heads on bf16
+//                MFMAs (U_K^T is read from the device cache), scales it by the key steps
+//                (and log2 e / sqrt d) and builds the score operands: per key field a query
+//                weight (the field's code shift over its bit position), scaled per head so
+//                the largest is 127 and split into three int8 digits laid out as MFMA A
+//                operands, plus per head the digit scales and the accumulator's start value;
+//                the first tiles stream meanwhile;
 //     tiles    - wave w of workgroup i takes tiles 4i + w + 4Wk and streams them through a
 //                private ring of LDS buffers (direct global->LDS loads, counted waits, no
 //                workgroup barriers in the loop).  Per tile:
@@ -61,7 +59,6 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kWaves = 4;            // waves per decode workgroup
 constexpr int kMergeThreads = 1024;  // threads per merge workgroup
 constexpr float kHeadroom = 2.0f;    // log2 headroom added to the reference max at a rescale
 constexpr float kLog2e = 1.4426950408889634f;
@@ -90,6 +87,13 @@ struct DecodeArgs {
 // LDS-only workgroup barrier: this wave's LDS operations are complete, then s_barrier.
 // (Global->LDS tile loads in flight are not waited for; their waits are explicit.)
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// LDS add written as an instruction of its own: the compiler makes every LDS atomic wait for
+// all direct-to-LDS copies in flight (vmcnt(0)), which would stall the tile stream.  LDS
+// operations complete in order; the LDS-only barrier waits for them.
+__device__ __forceinline__ void lds_add_async(LDS_AS int* p, int v) {
+    asm volatile("ds_add_u32 %0, %1" ::"v"(p), "v"(v) : "memory");
+}
 
 // wait until at most n of this wave's vector memory operations are outstanding (n is
 // clamped to 15, which only waits longer)
@@ -196,170 +200,38 @@ __device__ __forceinline__ void split256(float x, int& a0, int& a1, int& a2) {
     a2 = (int)rintf((r1 - d1) * 256.0f);
 }
 
-// Registers per lane grow with the row blocks and value column blocks; the waves per SIMD
-// the allocation is sized for (the LDS plan matches it).
+// Registers per lane grow with the row blocks and value column blocks.  One row block with
+// at most 3 score operand blocks and 8 value column blocks fits 168 VGPRs (three waves per
+// SIMD) without spills; the rest take two waves (256 VGPRs).  A spill reloaded in the tile
+// loop would wait for every tile load in flight.  The LDS plan matches the wave count.
 // The key schedule (per score MFMA: four record-word offsets and four masks of this lane's
 // group) stays in registers when it is small.
-constexpr bool ksched_in_regs(int nqm) { return nqm <= 3; }
-constexpr int vgpr_estimate(int rb, int nqm, int nvb) {
-    return rb * nvb * 4 + nqm * rb * 4 + 2 * nvb + rb * 20 + 56 + (ksched_in_regs(nqm) ? 8 * nqm : 0);
-}
-constexpr int waves_for(int rb, int nqm, int nvb) { return vgpr_estimate(rb, nqm, nvb) <= 168 ? 3 : 2; }
+constexpr bool ksched_in_regs(int nqm) { return nqm <= 2; }
+constexpr int waves_for(int rb, int nqm, int nvb) { return rb == 1 && nqm <= 3 && nvb <= 8 ? 3 : 2; }
+// A decode workgroup fills one CU at that occupancy: 4 SIMDs x waves_for waves.
+constexpr int wg_waves(int rb, int nqm, int nvb) { return 4 * waves_for(rb, nqm, nvb); }
 
-// bytes of the query preparation's output per (sequence, kv-head): the score A operands
-// [NQM][RB][64 lanes] (16 bytes each), then per (row block, head) a 32-byte lane record
-// (three float digit scales, three int score start values, two zero words)
-constexpr int qprep_bytes(int rb, int nqm) { return nqm * rb * 1024 + rb * 4 * 32; }
-// bytes of the decode prologue's LDS scratch: that output, then the value columns [NVB][16]
-constexpr int scratch_bytes(int rb, int nqm, int nvb) { return qprep_bytes(rb, nqm) + nvb * 64; }
-
-// ---------------------------------------------------------------------------------------
-// query preparation, one workgroup of D / 16 waves per (kv-head, sequence).  Wave b forms
-// q' = U_K^T q for channels 16 b .. 16 b + 15 and the kv-head's query heads on bf16 MFMAs
-// (q is bf16; U_K = hi + lo, channel-major; rows = channels, columns = heads),
-// q'' = q' * step_K * log2(e) / sqrt(d), and per head the block's largest slot value
-// |q''[j]| max over the fields of j of 2^(shift - pos).  Then the workgroup writes the
-// decode kernel's score operands: key field (chan, shift, pos) of score slot k gets
-// q''[chan] * 2^shift / 2^pos, scaled per head so that the largest slot is 127, split into
-// three int8 digits (rows 4 head + digit of the A operand); and per (row block, head) the
-// digit scales and 128 x the digit sums of slots whose field ends at bit 7 (the score
-// accumulator's start value, which undoes the -128 those fields read as).  It also streams
-// U_V^T (the merge's) and the decode tables through the device cache.
-// ---------------------------------------------------------------------------------------
-template <int RB, int NQM, int D>
-__global__ __launch_bounds__(D * 4) void qprep_kernel(const DevHead* __restrict__ blob, int layer, int n_kv, int G,
-                                                      const uint16_t* __restrict__ q, uint8_t* __restrict__ qbuf) {
-    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    constexpr int GM = 4 * RB;
-    constexpr int KS = D / 32;  // k-steps over the input dimension
-    constexpr int NB = D / 16;  // 16-channel blocks, one per wave
-    constexpr int NT = NB * 64;
-    __shared__ __attribute__((aligned(16))) float qf[GM][D];  // q''
-    __shared__ float bmax[NB][16];                            // per block and head: largest slot value
-    __shared__ int corr[RB * 16];                             // per row: digit sums of bit-7 slots
-    const int h = blockIdx.x, z = blockIdx.y;
-    const int tid = threadIdx.x, cb = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
-    const DevHead& H = blob[layer * n_kv + h];
-    const int64_t zh = (int64_t)z * n_kv + h;
-    uint8_t* out = qbuf + zh * qprep_bytes(RB, NQM);
-    // the slot descriptors of this thread's first operand item (see below)
-    typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
-    u16x4 slots0 = u16x4{0xFFFF, 0xFFFF, 0xFFFF, 0xFFFF};
-    if (tid < NQM * RB * 64) {
-        const int iw = (tid >> 2) & 3, gg = (tid >> 4) & 3, m = (tid >> 6) / RB;
-        slots0 = *(const u16x4*)&H.kq_slot[m][gg][4 * iw];
-    }
-    bf16x8 ah[KS], al[KS], bq[KS];
-    const int j = 16 * cb + c;  // A row: channel
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        ah[ks] = *(const bf16x8*)(H.UKt_hi + j * D + 32 * ks + 8 * g);
-        al[ks] = *(const bf16x8*)(H.UKt_lo + j * D + 32 * ks + 8 * g);
-        bq[ks] = *(const bf16x8*)(q + (zh * G + min(c, G - 1)) * D + 32 * ks + 8 * g);  // B column: head c
-    }
-    const int j0 = 16 * cb + 4 * g;  // output rows of this lane
-    const f4 stv = *(const f4*)(H.stepK + j0), fmv = *(const f4*)(H.kq_fmax + j0);
-    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 b = c < G ? bq[ks] : bf16x8{};  // heads past G: zero columns
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], b, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], b, acc, 0, 0, 0);
-    }
-    // U_V^T (the merge's) and the decode tables pass through the device cache: loads into
-    // registers that are only waited for at the end (issued once this thread's operand
-    // loads are used, so that they delay nothing)
-    constexpr int NWV = 16 * D * 4 / 1024, KSB = NQM * 128, VCB = (int)sizeof(H.vb_col);
-    constexpr int NWT = (KSB + 1023) / 1024 + (VCB + 1023) / 1024;
-    u32x4 wv[NWV + NWT];
-    {
-        const uint8_t* uv = (const uint8_t*)(H.UVt + 16 * cb * D);
-#pragma unroll
-        for (int k = 0; k < NWV; ++k) wv[k] = *(const u32x4*)(uv + 1024 * k + 16 * lane);
-        const uint8_t* ks = (const uint8_t*)&H.kq_sched[0][0][0];
-        const uint8_t* vc = (const uint8_t*)&H.vb_col[0][0];
-        int k = NWV;
-#pragma unroll
-        for (int off = 0; off < KSB; off += 1024, ++k) wv[k] = *(const u32x4*)(ks + min(off + 16 * lane, KSB - 16));
-#pragma unroll
-        for (int off = 0; off < VCB; off += 1024, ++k) wv[k] = *(const u32x4*)(vc + min(off + 16 * lane, VCB - 16));
-    }
-    const float qscale = kLog2e / sqrtf((float)D);
-    f4 v;
-    float mag = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        v[e] = acc[e] * stv[e] * qscale;  // step_K is 0 for uncoded channels
-        mag = fmaxf(mag, fabsf(v[e]) * fmv[e]);
-    }
-    if (c < GM) *(f4*)&qf[c][j0] = v;
-    mag = fmaxf(mag, __shfl_xor(mag, 16));
-    mag = fmaxf(mag, __shfl_xor(mag, 32));
-    if (g == 0) bmax[cb][c] = mag;
-    if (tid < RB * 16) corr[tid] = 0;
-    lds_barrier();  // (LDS only: the cache-warming loads stay in flight)
-    // operands: thread (m, rb, lane group gg, dword iw, head hh4) forms the three digit words
-    // of its four slots (rows 4 hh4 + 0..2; row 3 stays zero)
-    for (int i = tid; i < NQM * RB * 64; i += NT) {
-        const int hh4 = i & 3, iw = (i >> 2) & 3, gg = (i >> 4) & 3, rb = (i >> 6) % RB, m = (i >> 6) / RB;
-        const int hh = 4 * rb + hh4;
-        float mx = 0.0f;
-#pragma unroll
-        for (int bk = 0; bk < NB; ++bk) mx = fmaxf(mx, bmax[bk][hh]);
-        const float sc = hh < G && mx > 0.0f ? 127.0f / mx : 0.0f;
-        uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
-        int f0 = 0, f1 = 0, f2 = 0;
-        const u16x4 sls = i == tid ? slots0 : *(const u16x4*)&H.kq_slot[m][gg][4 * iw];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t sl = sls[e];
-            if (sl != 0xFFFFu) {
-                const int sh = (int)((sl >> 8) & 7) - (int)((sl >> 11) & 7);
-                float d0, d1, d2;
-                digits254(qf[hh][sl & 255] * __builtin_amdgcn_ldexpf(sc, sh), d0, d1, d2);
-                w0 |= ((uint32_t)(int)d0 & 0xFFu) << (8 * e);
-                w1 |= ((uint32_t)(int)d1 & 0xFFu) << (8 * e);
-                w2 |= ((uint32_t)(int)d2 & 0xFFu) << (8 * e);
-                if (sl & 0x4000u) f0 += (int)d0, f1 += (int)d1, f2 += (int)d2;
-            }
-        }
-        // dword iw of lane (gg, row) in operand [m][rb], rows 4 hh4 + digit
-        uint32_t* dst = (uint32_t*)(out + ((m * RB + rb) * 64 + 16 * gg + 4 * hh4) * 16) + iw;
-        dst[0] = w0;
-        dst[4] = w1;
-        dst[8] = w2;
-        dst[12] = 0u;
-        if (f0 | f1 | f2) {
-            atomicAdd(&corr[rb * 16 + 4 * hh4], f0);
-            atomicAdd(&corr[rb * 16 + 4 * hh4 + 1], f1);
-            atomicAdd(&corr[rb * 16 + 4 * hh4 + 2], f2);
-        }
-    }
-    lds_barrier();
-    if (tid < RB * 4) {  // lane record of (row block, head)
-        const int rb = tid >> 2, g4 = tid & 3, hh = 4 * rb + g4;
-        float mx = 0.0f;
-#pragma unroll
-        for (int bk = 0; bk < NB; ++bk) mx = fmaxf(mx, bmax[bk][hh]);
-        mx *= 1.0f / 127.0f;
-        const int* cr = &corr[16 * rb + 4 * g4];
-        u32x4* rec = (u32x4*)(out + NQM * RB * 1024 + 32 * tid);
-        rec[0] = u32x4{__builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, mx * kQ1),
-                       __builtin_bit_cast(uint32_t, mx * kQ2), (uint32_t)(128 * cr[0])};
-        rec[1] = u32x4{(uint32_t)(128 * cr[1]), (uint32_t)(128 * cr[2]), 0u, 0u};
-    }
-#pragma unroll
-    for (int k = 0; k < NWV + NWT; ++k) asm volatile("" ::"v"(wv[k]));
+// bytes of the score operands in LDS: the A operands [NQM][RB][64 lanes] (16 bytes each),
+// then per (row block, head) a 32-byte lane record (three float digit scales, three int
+// score start values, two zero words)
+constexpr int operand_bytes(int rb, int nqm) { return nqm * rb * 1024 + rb * 4 * 32; }
+// bytes of the decode prologue's LDS scratch: the operands, the value columns [NVB][16],
+// the slot descriptors [NQM][4][16], q'' [4 RB][D], block maxima [D / 16][16], bit-7 digit
+// sums [RB][16]
+constexpr int scratch_bytes(int rb, int nqm, int nvb, int d) {
+    return operand_bytes(rb, nqm) + nvb * 64 + nqm * 128 + 16 * rb * d + 4 * d + 64 * rb;
 }
 
 template <int RB, int NQM, int NVB, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel(
+__global__ __launch_bounds__(64 * wg_waves(RB, NQM, NVB))
+__attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel(
     const DevHead* __restrict__ blob, const uint8_t* __restrict__ cache, DecodeArgs a,
-    const int32_t* __restrict__ seq_ids, const int64_t* __restrict__ seq_lens, const uint8_t* __restrict__ qbuf,
+    const int32_t* __restrict__ seq_ids, const int64_t* __restrict__ seq_lens, const uint16_t* __restrict__ q,
     float* __restrict__ part) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
     constexpr int PST = 64;          // bytes per row of the probability operand (64 tokens)
     constexpr int GM = 4 * RB;       // query heads the operands have room for
+    constexpr int NW = wg_waves(RB, NQM, NVB);  // waves per workgroup
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     LDS_AS uint8_t* sm = (LDS_AS uint8_t*)smem_generic;
     const int wgi = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
@@ -379,39 +251,138 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
     if (seq < 0 || seq >= a.n_seqs_cache) len = 0;
     const int64_t n_tiles = (len + kTile - 1) / kTile;
     const uint8_t* tiles = cache + (((int64_t)a.layer * a.n_seqs_cache + seq) * a.n_kv + h) * a.n_tiles_cap * TB;
-    // wave w of workgroup wgi takes tiles 4 wgi + w + k (4 W): every wave of the (sequence,
+    // wave w of workgroup wgi takes tiles NW wgi + w + k (NW W): every wave of the (sequence,
     // kv-head) gets the same number of tiles to within one, and neighbouring waves stream
     // neighbouring tiles.  Ring slot k of this wave: ring + k * RS.
-    const int64_t stride = (int64_t)kWaves * a.wg_per_head;
+    const int64_t stride = (int64_t)NW * a.wg_per_head;
     const int NBW = a.nbw;
     const TileLoads tl = a.tl;
     const int nl = tl.n16 + tl.r4 + tl.r2 + tl.r1;  // load instructions per tile
     LDS_AS uint8_t* ring = sm + w * BB;
-    const int RS = kWaves * BB;  // bytes between a wave's ring slots
-    int64_t t = (int64_t)wgi * kWaves + w;
-    // ---- prologue: the loop's register operands - the score A operands and lane records of
-    // the query preparation, this lane group's key schedule, this lane's value columns -
-    // arrive by direct global->LDS copies issued before the first tiles' copies, so waiting
-    // for them leaves the tiles in flight.  The scratch has room of its own beside the ring
-    // when it fits (every ring slot streams from the start), else it takes the ring's last
-    // slots, whose tiles are issued once the operands are in registers.
-    constexpr int QB = qprep_bytes(RB, NQM);
-    LDS_AS uint8_t* scr = sm + a.off_scratch;                   // [QB] operands and records
-    LDS_AS uint32_t* vcol = (LDS_AS uint32_t*)(scr + QB);       // [NVB][16] value columns
-    LDS_AS u32x4* ksched = (LDS_AS u32x4*)(sm + a.off_ksched);  // [NQM][4][2]: offsets, masks
-    {
-        const uint8_t* qz = qbuf + zh * QB;
-        for (int off = 1024 * w; off < QB; off += 1024 * kWaves)
-            if (off + 16 * lane < QB)
-                __builtin_amdgcn_global_load_lds((const void*)(qz + off + 16 * lane), (LDS_AS void*)(scr + off), 16, 0, 0);
-        if (w == kWaves - 1) load_tile((const uint8_t*)&H.vb_col[0][0], (LDS_AS uint8_t*)vcol, NVB * 64, lane, 0);
-        if (w == kWaves - 2) load_tile((const uint8_t*)&H.kq_sched[0][0][0], (LDS_AS uint8_t*)ksched, NQM * 128, lane, 0);
+    const int RS = NW * BB;  // bytes between a wave's ring slots
+    int64_t t = (int64_t)wgi * NW + w;
+    // ---- prologue.  Waves 0 .. D/16 - 1 each form one 16-channel block of q' = U_K^T q:
+    // (1) register loads of the block's U_K^T rows (hi, lo), the query heads, the key steps
+    // and slot weights; (2) direct global->LDS copies of the slot descriptors, the key
+    // schedule and the value columns (waves 0..2, one table each); (3) the block on bf16
+    // MFMAs, q'' and per head the block's largest slot value into LDS; (4) only then this
+    // wave's tile copies: the compiler cannot count copies of run-time size, so a register
+    // load consumed after them would wait for all of them.  The other waves issue their tile
+    // copies at once.  (5) while the tiles stream, the workgroup builds the score operands
+    // in LDS (three int8 digits per key field, laid out as MFMA A operands) and per head the
+    // lane record (digit scales and the accumulator's start value), and moves them into
+    // registers.
+    constexpr int NB = D / 16;         // 16-channel blocks of q'
+    constexpr int KS = D / 32;         // k-steps over the input dimension
+    static_assert(NB <= NW && NB >= 3, "one wave per channel block; the first three copy the tables");
+    constexpr int QB = operand_bytes(RB, NQM);
+    LDS_AS uint8_t* scr = sm + a.off_scratch;                             // [QB] operands and records
+    LDS_AS uint32_t* vcol = (LDS_AS uint32_t*)(scr + QB);                 // [NVB][16] value columns
+    LDS_AS uint16_t* kslot = (LDS_AS uint16_t*)(scr + QB + NVB * 64);     // [NQM][4][16] slot descriptors
+    LDS_AS float* qf = (LDS_AS float*)(scr + QB + NVB * 64 + NQM * 128);  // [GM][D] q''
+    LDS_AS float* bmax = qf + GM * D;                                     // [NB][16] block maxima per head
+    LDS_AS int* corr = (LDS_AS int*)(bmax + NB * 16);                     // [RB][16] digit sums of bit-7 slots
+    LDS_AS u32x4* ksched = (LDS_AS u32x4*)(sm + a.off_ksched);            // [NQM][4][2]: offsets, masks
+    const bool qwave = w < NB;  // this wave forms channel block w
+    bf16x8 ah[KS], al[KS], bq[KS];
+    f4 stv, fmv;
+    if (qwave) {
+        const int j = 16 * w + c;  // A row: channel j
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            ah[ks] = *(const bf16x8*)(H.UKt_hi + j * D + 32 * ks + 8 * g);
+            al[ks] = *(const bf16x8*)(H.UKt_lo + j * D + 32 * ks + 8 * g);
+        }
+        stv = *(const f4*)(H.stepK + 16 * w + 4 * g);
+        fmv = *(const f4*)(H.kq_fmax + 16 * w + 4 * g);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)  // B column: query head c of the group (clamped; zeroed below)
+            bq[ks] = *(const bf16x8*)(q + ((int64_t)zh * G + min(c, G - 1)) * D + 32 * ks + 8 * g);
     }
+    // (the channel-block waves copy the tables: they wait for their own loads before the
+    // MFMAs anyway, and the other waves start their tiles with nothing else in flight)
+    if (w == 0) load_tile((const uint8_t*)&H.vb_col[0][0], (LDS_AS uint8_t*)vcol, NVB * 64, lane, 0);
+    if (w == 1) load_tile((const uint8_t*)&H.kq_sched[0][0][0], (LDS_AS uint8_t*)ksched, NQM * 128, lane, 0);
+    if (w == 2) load_tile((const uint8_t*)&H.kq_slot[0][0][0], (LDS_AS uint8_t*)kslot, NQM * 128, lane, 0);
+    if (qwave) {
+        const float qscale = kLog2e / sqrtf((float)D);
+        f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 bv = c < G ? bq[ks] : bf16x8{};  // heads past G: zero columns
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bv, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], bv, acc, 0, 0, 0);
+        }
+        // lane (g, c): channels 16 w + 4 g + e of head c
+        f4 v;
+        float mag = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[e] = acc[e] * stv[e] * qscale;  // step_K is 0 for uncoded channels
+            mag = fmaxf(mag, fabsf(v[e]) * fmv[e]);
+        }
+        if (c < GM) *(LDS_AS f4*)&qf[c * D + 16 * w + 4 * g] = v;
+        mag = fmaxf(mag, __shfl_xor(mag, 16));
+        mag = fmaxf(mag, __shfl_xor(mag, 32));
+        if (g == 0) bmax[w * 16 + c] = mag;
+    }
+    if (tid < RB * 16) corr[tid] = 0;
     int issued = 0;  // tiles of this wave whose loads have been issued; tile number k uses ring slot k % NBW
     for (; issued < a.early && t + stride * issued < n_tiles; ++issued)
         stream_tile(tiles + (t + stride * issued) * TB, ring + issued * RS, tl, lane);
-    wait_vm(nl * issued);  // this wave's copies have landed
-    lds_barrier();         // ... and every wave's
+    wait_vm(nl * issued);  // the table copies (issued before the tiles) have landed
+    lds_barrier();         // ... in every wave, and q'' and the block maxima are in LDS
+    // score operands: item (m, rb, lane group gg, dword iw, head hh4) forms the three digit
+    // words of its four slots (rows 4 hh4 + 0..2 of operand [m][rb]; row 4 hh4 + 3 is zero)
+    for (int i = tid; i < NQM * RB * 64; i += NW * 64) {
+        const int hh4 = i & 3, iw = (i >> 2) & 3, gg = (i >> 4) & 3, rb = (i >> 6) % RB, m = (i >> 6) / RB;
+        const int hh = 4 * rb + hh4;
+        float mx = 0.0f;
+#pragma unroll
+        for (int bk = 0; bk < NB; ++bk) mx = fmaxf(mx, bmax[bk * 16 + hh]);
+        const float sc = hh < G && mx > 0.0f ? 127.0f / mx : 0.0f;
+        typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+        const u16x4 sls = *(const LDS_AS u16x4*)&kslot[(m * 4 + gg) * 16 + 4 * iw];
+        uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
+        int f0 = 0, f1 = 0, f2 = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t sl = sls[e];
+            if (sl != 0xFFFFu) {  // slot = chan | shift << 8 | pos << 11 | ends-at-bit-7 << 14
+                const int sh = (int)((sl >> 8) & 7) - (int)((sl >> 11) & 7);
+                float d0, d1, d2;
+                digits254(qf[hh * D + (sl & 255)] * __builtin_amdgcn_ldexpf(sc, sh), d0, d1, d2);
+                w0 |= ((uint32_t)(int)d0 & 0xFFu) << (8 * e);
+                w1 |= ((uint32_t)(int)d1 & 0xFFu) << (8 * e);
+                w2 |= ((uint32_t)(int)d2 & 0xFFu) << (8 * e);
+                if (sl & 0x4000u) f0 += (int)d0, f1 += (int)d1, f2 += (int)d2;
+            }
+        }
+        LDS_AS uint32_t* dst = (LDS_AS uint32_t*)(scr + ((m * RB + rb) * 64 + 16 * gg + 4 * hh4) * 16) + iw;
+        dst[0] = w0;
+        dst[4] = w1;
+        dst[8] = w2;
+        dst[12] = 0u;
+        if (f0 | f1 | f2) {
+            lds_add_async(&corr[rb * 16 + 4 * hh4], f0);
+            lds_add_async(&corr[rb * 16 + 4 * hh4 + 1], f1);
+            lds_add_async(&corr[rb * 16 + 4 * hh4 + 2], f2);
+        }
+    }
+    lds_barrier();
+    if (tid < RB * 4) {  // lane record of (row block, head): digit scales, 128 x bit-7 digit sums
+        const int rb = tid >> 2, g4 = tid & 3, hh = 4 * rb + g4;
+        float mx = 0.0f;
+#pragma unroll
+        for (int bk = 0; bk < NB; ++bk) mx = fmaxf(mx, bmax[bk * 16 + hh]);
+        mx *= 1.0f / 127.0f;
+        const LDS_AS int* cr = &corr[16 * rb + 4 * g4];
+        LDS_AS u32x4* rec = (LDS_AS u32x4*)(scr + NQM * RB * 1024 + 32 * tid);
+        rec[0] = u32x4{__float_as_uint(mx), __float_as_uint(mx * kQ1), __float_as_uint(mx * kQ2),
+                       (uint32_t)(128 * cr[0])};
+        rec[1] = u32x4{(uint32_t)(128 * cr[1]), (uint32_t)(128 * cr[2]), 0u, 0u};
+    }
+    lds_barrier();
     uint32_t voff[NVB], vmask[NVB];  // value columns of this lane: tile offset of its plane slice, mask
 #pragma unroll
     for (int cb = 0; cb < NVB; ++cb) {
@@ -631,15 +602,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
         slot = slot + 1 == NBW ? 0 : slot + 1;
     }
 
-    // ---------------- epilogue: the four waves' results meet in LDS (ring reused), laid out
+    // ---------------- epilogue: the waves' results meet in LDS (ring reused), laid out
     // like the partial: per wave and head [reference max, sum, 128 x probability digit sum
     // / 127, 0, columns: accumulator / 127 = sum of p x stored byte].  Per head the
     // workgroup's reference is the largest of the waves', each wave weighted by 2^(m - M).
     constexpr int PL = kPartHead + 16 * NVB;  // floats per partial and head
     wait_all();
     lds_barrier();
-    LDS_AS float* wx = (LDS_AS float*)sm;   // [4 waves][GM][PL]
-    LDS_AS float* ew = wx + kWaves * GM * PL;  // [4 waves][GM] weights, then [GM] maxima
+    LDS_AS float* wx = (LDS_AS float*)sm;  // [NW waves][GM][PL]
+    LDS_AS float* ew = wx + NW * GM * PL;  // [NW waves][GM] weights, then [GM] maxima
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         LDS_AS float* o = wx + (w * GM + 4 * rb + g) * PL;
@@ -659,23 +630,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_for(R
     if (tid < GM) {
         float M = -INFINITY;
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, wx[(ww * GM + tid) * PL]);
+        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wx[(ww * GM + tid) * PL]);
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
+        for (int ww = 0; ww < NW; ++ww) {
             const float m = wx[(ww * GM + tid) * PL];
             ew[ww * GM + tid] = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
         }
-        ew[kWaves * GM + tid] = M;
+        ew[NW * GM + tid] = M;
     }
     lds_barrier();
     float* pout = part + (zh * a.wg_per_head + wgi) * G * PL;
-    for (int i = tid; i < G * PL; i += 256) {
+    for (int i = tid; i < G * PL; i += NW * 64) {
         const int hh = i / PL, col = i - hh * PL;
-        float v = ew[kWaves * GM + hh];
+        float v = ew[NW * GM + hh];
         if (col > 0) {
             v = 0.0f;
 #pragma unroll
-            for (int ww = 0; ww < kWaves; ++ww) v = fmaf(ew[ww * GM + hh], wx[(ww * GM + hh) * PL + col], v);
+            for (int ww = 0; ww < NW; ++ww) v = fmaf(ew[ww * GM + hh], wx[(ww * GM + hh) * PL + col], v);
         }
         pout[i] = v;
     }
@@ -811,8 +782,8 @@ constexpr Variant kVariants[] = {{1, 2, 4},  {1, 2, 8},  {1, 3, 8},  {1, 3, 10},
 
 struct Plan {
     Variant v;
-    int nqm_max, nvb_max, wg_per_head, wgs_per_cu;
-    size_t qbuf_bytes, part_bytes;
+    int nqm_max, nvb_max, wg_per_head, wgs_per_cu, nw;
+    size_t part_bytes;
     DecodeArgs args;
     size_t lds;
 };
@@ -858,15 +829,16 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     for (int h = 0; h < cb->n_kv; ++h) bk_min = std::min(bk_min, cb->blob[(size_t)layer * cb->n_kv + h].BK);
     if (RB * 1024 > 8 * bk_min)
         return set_error(AATC_ERR_UNSUPPORTED, "%d key bits per token are too few for %d query heads", bk_min, G);
-    // the epilogue reuses the ring
-    const size_t epi = ((size_t)kWaves * 4 * RB * (kPartHead + 16 * p.v.nvb) + (size_t)(kWaves + 1) * 4 * RB) * sizeof(float);
-    const size_t scr = al16((size_t)scratch_bytes(RB, p.v.nqm, p.v.nvb));
+    // one workgroup of NW waves per CU; the epilogue reuses the ring
+    const int NW = wg_waves(p.v.rb, p.v.nqm, p.v.nvb);
+    p.nw = NW;
+    const size_t epi = ((size_t)NW * 4 * RB * (kPartHead + 16 * p.v.nvb) + (size_t)(NW + 1) * 4 * RB) * sizeof(float);
+    const size_t scr = al16((size_t)scratch_bytes(RB, p.v.nqm, p.v.nvb, d));
     const size_t ksch = (size_t)p.v.nqm * 4 * 8 * 4;
-    const size_t group = (size_t)kWaves * a.buf_bytes;  // one ring slot of every wave
-    // ring depth: the deepest that the workgroups resident per CU (set by registers) leave
-    // room for beside the prologue's scratch, between 2 and 4 buffers per wave
-    const int wgs = waves_for(p.v.rb, p.v.nqm, p.v.nvb);
-    const size_t budget = (size_t)(160 * 1024) / wgs - ksch - 64;
+    const size_t group = (size_t)NW * a.buf_bytes;  // one ring slot of every wave
+    // ring depth: the deepest that the CU's LDS leaves room for beside the prologue's
+    // scratch, between 2 and 4 buffers per wave
+    const size_t budget = (size_t)(160 * 1024) - ksch - 256;
     a.nbw = 2;
     while (a.nbw < 4 && (a.nbw + 1) * group + scr <= budget) ++a.nbw;
     const size_t ring = a.nbw * group;
@@ -883,7 +855,7 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     }
     a.off_ksched = (int)al16(std::max(top, epi));
     p.lds = a.off_ksched + ksch;
-    p.wgs_per_cu = std::min<int>(wgs, (int)((160 * 1024) / p.lds));
+    p.wgs_per_cu = 1;
     if (p.lds > 160 * 1024 - 256)
         return set_error(AATC_ERR_UNSUPPORTED, "decode needs %zu bytes of LDS per workgroup", p.lds);
     // workgroups per (sequence, kv-head): every resident workgroup slot of the chip busy,
@@ -891,11 +863,10 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     const int64_t pairs = (int64_t)cb->n_kv * n_seqs;
     const int64_t slots = 256 * (int64_t)p.wgs_per_cu;
     p.wg_per_head = (int)std::max<int64_t>(
-        1, std::min<int64_t>({slots / pairs, (tiles + kWaves - 1) / kWaves,
+        1, std::min<int64_t>({slots / pairs, (tiles + NW - 1) / NW,
                               (int64_t)kMergeRows * (kMergeThreads / ((kPartHead + 16 * p.v.nvb) / 4))}));
     a.wg_per_head = p.wg_per_head;
     a.part_ld = kPartHead + 16 * p.v.nvb;
-    p.qbuf_bytes = al256((size_t)n_seqs * cb->n_kv * qprep_bytes(RB, p.v.nqm));
     p.part_bytes = (size_t)n_seqs * cb->n_kv * p.wg_per_head * G * a.part_ld * sizeof(float);
     return AATC_OK;
 }
@@ -926,19 +897,17 @@ void profile_slot(hipEvent_t& a, hipEvent_t& b) {
 
 template <int RB, int NQM, int NVB, int D>
 int launch_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* blob, const uint8_t* cache,
-                  const int32_t* ids, const int64_t* lens, const uint16_t* q, uint8_t* qbuf, float* part, float* out) {
+                  const int32_t* ids, const int64_t* lens, const uint16_t* q, float* part, float* out) {
     const DecodeArgs& a = p.args;
-    hipLaunchKernelGGL((qprep_kernel<RB, NQM, D>), dim3(a.n_kv, n_seqs), dim3(D * 4), 0, st, blob, a.layer, a.n_kv,
-                       a.G, q, qbuf);
-    HIP_TRY(hipGetLastError());
     if (p.lds > 64 * 1024)
         HIP_TRY(hipFuncSetAttribute((const void*)decode_kernel<RB, NQM, NVB, D>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds));
     hipEvent_t e0, e1;
     profile_slot(e0, e1);
     if (e0) HIP_TRY(hipEventRecord(e0, st));
-    hipLaunchKernelGGL((decode_kernel<RB, NQM, NVB, D>), dim3(p.wg_per_head, a.n_kv, n_seqs), dim3(256), p.lds, st,
-                       blob, cache, a, ids, lens, (const uint8_t*)qbuf, part);
+    if (p.nw != wg_waves(RB, NQM, NVB)) return set_error(AATC_ERR_UNSUPPORTED, "decode plan and variant disagree");
+    hipLaunchKernelGGL((decode_kernel<RB, NQM, NVB, D>), dim3(p.wg_per_head, a.n_kv, n_seqs), dim3(64 * p.nw), p.lds, st,
+                       blob, cache, a, ids, lens, q, part);
     HIP_TRY(hipGetLastError());
     if (e1) HIP_TRY(hipEventRecord(e1, st));
     hipLaunchKernelGGL((merge_kernel<D>), dim3(a.n_kv, n_seqs, a.G), dim3(kMergeThreads), 0, st, blob, a.layer, a.n_kv,
@@ -996,7 +965,7 @@ extern "C" int aatc_decode_workspace_bytes(const aatc_codebook* cb, int32_t n_se
         Plan p;
         int rc = make_plan(cb, layer, n_seqs, max_len, p);
         if (rc) return rc;
-        worst = std::max(worst, p.qbuf_bytes + p.part_bytes);
+        worst = std::max(worst, p.part_bytes);
     }
     *bytes = worst;
     return AATC_OK;
@@ -1019,11 +988,9 @@ extern "C" int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob
     Plan p;
     rc = make_plan(cb, layer, n_seqs, max_len, p);
     if (rc) return rc;
-    if (ws_bytes < p.qbuf_bytes + p.part_bytes)
-        return set_error(AATC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes,
-                         p.qbuf_bytes + p.part_bytes);
-    uint8_t* qbuf = (uint8_t*)workspace;                          // [n_seqs][n_kv] score operands and lane records
-    float* part = (float*)((uint8_t*)workspace + p.qbuf_bytes);  // [n_seqs][n_kv][wg][G][part_ld] partials
+    if (ws_bytes < p.part_bytes)
+        return set_error(AATC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, p.part_bytes);
+    float* part = (float*)workspace;  // [n_seqs][n_kv][wg][G][part_ld] partials
     DecodeArgs& a = p.args;
     a.layer = layer;
     a.n_kv = cb->n_kv;
@@ -1036,8 +1003,8 @@ extern "C" int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob
 #define AATC_DECODE_CASE(rb_, nqm_, nvb_)                                                                    \
     if (p.v.rb == rb_ && p.v.nqm == nqm_ && p.v.nvb == nvb_)                                                 \
         return cb->d == 64                                                                                   \
-                   ? launch_decode<rb_, nqm_, nvb_, 64>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, qbuf, part, out) \
-                   : launch_decode<rb_, nqm_, nvb_, 128>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, qbuf, part, out);
+                   ? launch_decode<rb_, nqm_, nvb_, 64>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, part, out) \
+                   : launch_decode<rb_, nqm_, nvb_, 128>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, part, out);
     AATC_DECODE_CASE(1, 2, 4)
     AATC_DECODE_CASE(1, 2, 8)
     AATC_DECODE_CASE(1, 3, 8)
