@@ -160,21 +160,23 @@ __device__ __forceinline__ void load_tile(const uint8_t* src, LDS_AS uint8_t* ld
 
 // Stream one cache tile (64 token slots of B bits: 64 x B / 8 bytes, so every lane's share is
 // whole bytes) with all lanes active: n16 loads of 16 bytes per lane (1 KiB each), then the
-// lane share's remainder in 4-, 2- and 1-byte loads (r4, r2, r1 of them).  No per-lane
-// conditions: the issue path is a few scalar instructions per load.
-__device__ __forceinline__ void stream_tile(const uint8_t* src, LDS_AS uint8_t* lds, const TileLoads& tl, int lane) {
-    for (int k = 0; k < tl.n16; ++k)
-        __builtin_amdgcn_global_load_lds((const void*)(src + 1024 * k + 16 * lane), (LDS_AS void*)(lds + 1024 * k), 16, 0,
-                                         kStreamPolicy);
-    int off = 1024 * tl.n16;
-    for (int k = 0; k < tl.r4; ++k, off += 256)
-        __builtin_amdgcn_global_load_lds((const void*)(src + off + 4 * lane), (LDS_AS void*)(lds + off), 4, 0, kStreamPolicy);
+// lane share's remainder in 4-, 2- and 1-byte loads (r4, r2, r1 of them).  Buffer loads
+// over the (sequence, kv-head)'s tile range: the tile's offset is a scalar, the lane's a
+// fixed register, so a load costs no vector instruction (and a read past the range returns
+// zeros instead of faulting).
+__device__ __forceinline__ void stream_tile(__amdgpu_buffer_rsrc_t rs, uint32_t off, LDS_AS uint8_t* lds,
+                                            const TileLoads& tl, int lane) {
+    for (int k = 0; k < tl.n16; ++k, off += 1024)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(lds + 1024 * k), 16, 16 * lane, off, 0, kStreamPolicy);
+    LDS_AS uint8_t* l = lds + 1024 * tl.n16;
+    for (int k = 0; k < tl.r4; ++k, off += 256, l += 256)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)l, 4, 4 * lane, off, 0, kStreamPolicy);
     if (tl.r2) {
-        __builtin_amdgcn_global_load_lds((const void*)(src + off + 2 * lane), (LDS_AS void*)(lds + off), 2, 0, kStreamPolicy);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)l, 2, 2 * lane, off, 0, kStreamPolicy);
         off += 128;
+        l += 128;
     }
-    if (tl.r1)
-        __builtin_amdgcn_global_load_lds((const void*)(src + off + lane), (LDS_AS void*)(lds + off), 1, 0, kStreamPolicy);
+    if (tl.r1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)l, 1, lane, off, 0, kStreamPolicy);
 }
 
 // three base-254 digits of x: x = d0 + d1 / 254 + d2 / 254^2 (+ rounding); each fits int8
@@ -251,16 +253,23 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
     if (seq < 0 || seq >= a.n_seqs_cache) len = 0;
     const int64_t n_tiles = (len + kTile - 1) / kTile;
     const uint8_t* tiles = cache + (((int64_t)a.layer * a.n_seqs_cache + seq) * a.n_kv + h) * a.n_tiles_cap * TB;
-    // wave w of workgroup wgi takes tiles NW wgi + w + k (NW W): every wave of the (sequence,
-    // kv-head) gets the same number of tiles to within one, and neighbouring waves stream
-    // neighbouring tiles.  Ring slot k of this wave: ring + k * RS.
-    const int64_t stride = (int64_t)NW * a.wg_per_head;
+    // buffer resource over this (sequence, kv-head)'s tiles (the host keeps the range below 2^31 bytes)
+    const __amdgpu_buffer_rsrc_t trs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)tiles, (short)0, (int)(a.n_tiles_cap * TB), 0x00020000);
+    // workgroup wgi takes the tiles [t_end(wgi - 1), t_end(wgi)) of an even split (every
+    // workgroup within one tile of the others), and its wave w the tiles t_begin + s + NW k
+    // with s = (w + 4) mod NW: the waves of a workgroup differ by at most one tile, and the
+    // waves with one more are waves NW - 4 .. NW - 1 (s < 4) - four consecutive waves, one
+    // per SIMD when waves are placed on the SIMDs in turn, and not the waves that form q'
+    // when there are 12.  Ring slot k of this wave: ring + k * RS.
+    const int64_t t_end = n_tiles * (wgi + 1) / a.wg_per_head;
+    const int64_t stride = NW;
     const int NBW = a.nbw;
     const TileLoads tl = a.tl;
     const int nl = tl.n16 + tl.r4 + tl.r2 + tl.r1;  // load instructions per tile
     LDS_AS uint8_t* ring = sm + w * BB;
     const int RS = NW * BB;  // bytes between a wave's ring slots
-    int64_t t = (int64_t)wgi * NW + w;
+    int64_t t = n_tiles * wgi / a.wg_per_head + (w + 4) % NW;
     // ---- prologue.  Waves 0 .. D/16 - 1 each form one 16-channel block of q' = U_K^T q:
     // (1) register loads of the block's U_K^T rows (hi, lo), the query heads, the key steps
     // and slot weights; (2) direct global->LDS copies of the slot descriptors, the key
@@ -327,9 +336,13 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
         if (g == 0) bmax[w * 16 + c] = mag;
     }
     if (tid < RB * 16) corr[tid] = 0;
+    // One tile per wave streams while the workgroup builds the score operands; the rest of
+    // the ring is issued after that work: the issue of a copy stalls while the memory
+    // system's queues are full, and with every wave's ring issued at once the waves would
+    // sit in those stalls instead of preparing the operands.
     int issued = 0;  // tiles of this wave whose loads have been issued; tile number k uses ring slot k % NBW
-    for (; issued < a.early && t + stride * issued < n_tiles; ++issued)
-        stream_tile(tiles + (t + stride * issued) * TB, ring + issued * RS, tl, lane);
+    for (; issued < min(a.early, 1) && t + stride * issued < t_end; ++issued)
+        stream_tile(trs, (uint32_t)((t + stride * issued) * TB), ring + issued * RS, tl, lane);
     wait_vm(nl * issued);  // the table copies (issued before the tiles) have landed
     lds_barrier();         // ... in every wave, and q'' and the block maxima are in LDS
     // score operands: item (m, rb, lane group gg, dword iw, head hh4) forms the three digit
@@ -434,10 +447,12 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
 #pragma unroll
         for (int m = 0; m < NQM; ++m) asm volatile("" ::"v"(koffr[m]), "v"(kmaskr[m]));
     }
+    for (; issued < a.early && t + stride * issued < t_end; ++issued)  // the rest of the first slots
+        stream_tile(trs, (uint32_t)((t + stride * issued) * TB), ring + issued * RS, tl, lane);
     if (a.early < NBW) {  // the scratch was in the ring's last slots: stream them now
         lds_barrier();
-        for (; issued < NBW && t + stride * issued < n_tiles; ++issued)
-            stream_tile(tiles + (t + stride * issued) * TB, ring + issued * RS, tl, lane);
+        for (; issued < NBW && t + stride * issued < t_end; ++issued)
+            stream_tile(trs, (uint32_t)((t + stride * issued) * TB), ring + issued * RS, tl, lane);
     }
 
     // int32 sums of P digits x value bytes, relative to the reference max mref, and the
@@ -459,7 +474,7 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
     // ---- this wave's tiles: the ring keeps up to NBW - 1 of them in flight; the wave
     // waits on its own load count
     int slot = 0;
-    for (int done = 0; t < n_tiles; t += stride, ++done) {
+    for (int done = 0; t < t_end; t += stride, ++done) {
         // tile t (this wave's tile number done) has landed once only the later tiles' loads
         // are outstanding
         wait_vm(nl * (issued - done - 1));
@@ -594,9 +609,9 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
         }
         // the slot streams the tile NBW ahead once this wave's reads of it are done
         const int64_t tn = t + stride * NBW;
-        if (tn < n_tiles) {
+        if (tn < t_end) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            stream_tile(tiles + tn * TB, curb, tl, lane);
+            stream_tile(trs, (uint32_t)(tn * TB), curb, tl, lane);
             ++issued;
         }
         slot = slot + 1 == NBW ? 0 : slot + 1;
@@ -996,6 +1011,9 @@ extern "C" int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob
     a.n_kv = cb->n_kv;
     a.n_seqs_cache = cache->n_seqs;
     a.n_tiles_cap = n_tiles_of(cache->max_tokens);
+    if (a.n_tiles_cap * (int64_t)a.tile_bytes >= ((int64_t)1 << 31))
+        return set_error(AATC_ERR_CAPACITY, "a (sequence, kv-head) cache range of %lld bytes (at most 2^31 - 1)",
+                         (long long)(a.n_tiles_cap * a.tile_bytes));
     a.max_len = max_len;
     const DevHead* blob = (const DevHead*)d_blob;
     hipStream_t st = (hipStream_t)stream;
