@@ -59,7 +59,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kMergeThreads = 1024;  // threads per merge workgroup
+constexpr int kMergeThreads = 256;  // threads per merge workgroup
 constexpr float kHeadroom = 2.0f;    // log2 headroom added to the reference max at a rescale
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kQ1 = 1.0f / 254.0f, kQ2 = 1.0f / 64516.0f;  // query digit weights (base 254)
@@ -336,12 +336,12 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
         if (g == 0) bmax[w * 16 + c] = mag;
     }
     if (tid < RB * 16) corr[tid] = 0;
-    // One tile per wave streams while the workgroup builds the score operands; the rest of
-    // the ring is issued after that work: the issue of a copy stalls while the memory
-    // system's queues are full, and with every wave's ring issued at once the waves would
-    // sit in those stalls instead of preparing the operands.
+    // The waves that do not form q' issue their whole first ring at once; the others one
+    // tile, and the rest once the score operands are built: the issue of a copy stalls while
+    // the memory system's queues are full, and the q' waves would sit in those stalls instead
+    // of preparing the operands.
     int issued = 0;  // tiles of this wave whose loads have been issued; tile number k uses ring slot k % NBW
-    for (; issued < min(a.early, 1) && t + stride * issued < t_end; ++issued)
+    for (; issued < (qwave ? min(a.early, 1) : a.early) && t + stride * issued < t_end; ++issued)
         stream_tile(trs, (uint32_t)((t + stride * issued) * TB), ring + issued * RS, tl, lane);
     wait_vm(nl * issued);  // the table copies (issued before the tiles) have landed
     lds_barrier();         // ... in every wave, and q'' and the block maxima are in LDS
@@ -668,46 +668,52 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
 }
 
 // ---------------------------------------------------------------------------------------
-// merge: one workgroup of 1024 threads per (sequence, kv-head, query head).  Softmax merge
-// of the W partials (a partial row is [reference max m, sum of p, top-field sum, 0,
-// columns]; column c = sum of p x stored byte of value field c, relative to m), then per
-// channel j
+// merge: one workgroup of 256 threads per (sequence, kv-head, query head, slice of 32 output
+// channels).  Softmax merge of the W partials (a partial row is [reference max m, sum of p,
+// top-field sum, 0, columns]; column c = sum of p x stored byte of value field c, relative
+// to m), then per channel j
 //   A_j = sum over its fields of 2^(shift - pos) (column + [field ends at bit 7] top sum)
 // (the stored byte of a field at bit pos is field 2^pos, minus 128 at the top of a byte)
-// and o = obias + U_V (step * A / L).  Every global read is issued at the start, 16 bytes
-// per lane: thread (q, s) holds float4 q of partial rows s, s + NS, ...; thread (i4, js)
-// holds float4 i4 of rows js JR .. js JR + JR - 1 of U_V^T.
+// and the slice of o = obias + U_V (step * A / L).  The reads - the partial maxima, the
+// partial rows (thread (q, s) holds float4 q of rows s, s + NS, ...), the slice's columns
+// of U_V^T (thread (i4, js) holds float4 i4 of rows js JR .. js JR + JR - 1) and the
+// channel tables - are issued together at the start, 16 bytes per lane where they can be.
 // ---------------------------------------------------------------------------------------
 static_assert(offsetof(DevHead, vch) % 16 == 0, "the merge loads a channel's field table as 16 bytes");
 static_assert(offsetof(DevHead, UVt) % 16 == 0, "the merge loads U_V^T 16 bytes per lane");
 static_assert(offsetof(DevHead, kq_slot) % 16 == 0 && offsetof(DevHead, kq_sched) % 16 == 0 &&
                   offsetof(DevHead, vb_col) % 16 == 0,
               "the decode prologue copies these tables 16 bytes per lane");
-constexpr int kMergeRows = 8;  // partial rows per merge thread: W <= 8 (1024 / (PL / 4))
+constexpr int kMergeSlice = 32;  // output channels per merge workgroup
+constexpr int kMergeRows = 8;    // partial rows per thread and round
+constexpr int kMaxWG = 256;      // workgroups per (sequence, kv-head) at most (one per CU)
 constexpr int kMaxPL = kPartHead + 16 * aatc::kMaxVB;
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DevHead* __restrict__ blob, int layer, int n_kv,
                                                               int G, int W, int PL, const float* __restrict__ part,
                                                               float* __restrict__ out) {
-    constexpr int NW = kMergeThreads / 64;
-    constexpr int I4 = D / 4;                 // float4 columns of U_V^T
-    constexpr int JS = kMergeThreads / I4;    // row slices of U_V^T
-    constexpr int JR = D / JS;                // rows per slice
-    __shared__ float mrow[kMergeThreads];     // per partial: reference max
-    __shared__ float wred[NW];
-    __shared__ f4 red[kMergeThreads];         // slice sums
+    constexpr int NT = kMergeThreads, NWV = NT / 64;
+    constexpr int NSL = D / kMergeSlice;  // slices
+    constexpr int I4 = kMergeSlice / 4;   // float4 columns of the slice
+    constexpr int JS = NT / I4;           // row slices of U_V^T
+    constexpr int JR = D / JS;            // rows per row slice
+    static_assert(D <= NT && JR * JS == D, "merge thread layout");
+    __shared__ float pm[kMaxWG];                              // partial maxima
+    __shared__ float wred[NWV];
+    __shared__ f4 red[NT];                                    // slice sums
     __shared__ __attribute__((aligned(16))) float colv[kMaxPL];  // merged row
-    __shared__ float cbar[D];                 // step * A / L
-    const int h = blockIdx.x, z = blockIdx.y, hh = blockIdx.z;
+    __shared__ float cbar[D];                                 // step * A / L
+    const int h = blockIdx.x / NSL, sl = blockIdx.x - h * NSL, z = blockIdx.y, hh = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t zh = (int64_t)z * n_kv + h;
     const DevHead& H = blob[layer * n_kv + h];
     const int64_t PS = (int64_t)G * PL;              // floats between partials
     const float* P = part + (zh * W * G + hh) * PL;  // partial w at P + w * PS
-    const int PL4 = PL >> 2, NS = kMergeThreads / PL4;
+    const int PL4 = PL >> 2, NS = NT / PL4;
     const int q = tid % PL4, s = tid / PL4;
-    // ---- every global read
+    // ---- every global read of the first round
+    for (int w = tid; w < W; w += NT) pm[w] = P[w * PS];
     f4 X[kMergeRows];
 #pragma unroll
     for (int k = 0; k < kMergeRows; ++k) {
@@ -717,33 +723,38 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DevHead* __r
     const int i4 = tid % I4, js = tid / I4;
     f4 U[JR];
 #pragma unroll
-    for (int r = 0; r < JR; ++r) U[r] = *(const f4*)(H.UVt + (js * JR + r) * D + 4 * i4);  // U_V[4 i4 ..][j]
+    for (int r = 0; r < JR; ++r) U[r] = *(const f4*)(H.UVt + (js * JR + r) * D + kMergeSlice * sl + 4 * i4);
     typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
-    const int jc = tid % D;  // channel tid (tid < D): its field columns and output constants
+    const int jc = tid % D;  // channel tid (tid < D): its field columns
     const u16x8 fl = *(const u16x8*)&H.vch[jc][0];
-    const float stv = H.bitsV[jc] ? H.stepV[jc] : 0.0f, obv = H.obias[jc], muv = H.muV[jc];
-    // ---- reference: the largest partial maximum
-    if (q == 0 && s < NS) {
-#pragma unroll
-        for (int k = 0; k < kMergeRows; ++k)
-            if (s + NS * k < W) mrow[s + NS * k] = X[k][0];
-    }
+    const float stv = H.bitsV[jc] ? H.stepV[jc] : 0.0f;
     __syncthreads();
-    const float mx = wave_max(tid < W ? mrow[tid] : -INFINITY);
+    // ---- reference: the largest partial maximum
+    float mx = -INFINITY;
+    for (int w = tid; w < W; w += NT) mx = fmaxf(mx, pm[w]);
+    mx = wave_max(mx);
     if (lane == 0) wred[wv] = mx;
     __syncthreads();
     float M = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < NW; ++k) M = fmaxf(M, wred[k]);
-    // ---- merged row: sum over partials of 2^(m - M) x row; slices meet in LDS
+    for (int k = 0; k < NWV; ++k) M = fmaxf(M, wred[k]);
+    // ---- merged row: sum over partials of 2^(m - M) x row, kMergeRows rows per thread a round
     f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int w0 = 0;; w0 += NS * kMergeRows) {
 #pragma unroll
-    for (int k = 0; k < kMergeRows; ++k) {
-        const int w = s + NS * k;
-        if (s < NS && w < W) {
-            const float m = mrow[w];
-            const float e = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-            acc += e * X[k];
+        for (int k = 0; k < kMergeRows; ++k) {
+            const int w = w0 + s + NS * k;
+            if (s < NS && w < W) {
+                const float m = pm[w];
+                const float e = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+                acc += e * X[k];
+            }
+        }
+        if (w0 + NS * kMergeRows >= W) break;
+#pragma unroll
+        for (int k = 0; k < kMergeRows; ++k) {  // the next round (partials beyond 8 NS)
+            const int w = w0 + NS * kMergeRows + s + NS * k;
+            X[k] = s < NS && w < W ? *(const f4*)(P + w * PS + 4 * q) : f4{0.0f, 0.0f, 0.0f, 0.0f};
         }
     }
     red[tid] = acc;
@@ -755,7 +766,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DevHead* __r
     }
     __syncthreads();
     const float L = colv[1], O = colv[2];
-    // ---- value coefficients, dequantisation step and 1 / L
+    // ---- value coefficients, dequantisation step and 1 / L (every channel)
     if (tid < D) {
         float A = 0.0f;
 #pragma unroll
@@ -769,17 +780,17 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DevHead* __r
         cbar[tid] = L > 0.0f ? stv * A / L : 0.0f;
     }
     __syncthreads();
-    // ---- o = obias + U_V cbar: slices of rows of U_V^T, slices meet in LDS
+    // ---- this slice of o = obias + U_V cbar: row slices meet in LDS
     f4 y = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int r = 0; r < JR; ++r) y += cbar[js * JR + r] * U[r];
     red[tid] = y;
     __syncthreads();
-    if (tid < D) {
+    if (tid < kMergeSlice) {
         float o = 0.0f;
-#pragma unroll
         for (int s2 = 0; s2 < JS; ++s2) o += red[s2 * I4 + (tid >> 2)][tid & 3];
-        out[(zh * G + hh) * D + tid] = L > 0.0f ? obv + o : muv;
+        const int i = kMergeSlice * sl + tid;
+        out[(zh * G + hh) * D + i] = L > 0.0f ? H.obias[i] + o : H.muV[i];
     }
 }
 
@@ -877,9 +888,7 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     // at least one tile per wave, at most what one merge round reads
     const int64_t pairs = (int64_t)cb->n_kv * n_seqs;
     const int64_t slots = 256 * (int64_t)p.wgs_per_cu;
-    p.wg_per_head = (int)std::max<int64_t>(
-        1, std::min<int64_t>({slots / pairs, (tiles + NW - 1) / NW,
-                              (int64_t)kMergeRows * (kMergeThreads / ((kPartHead + 16 * p.v.nvb) / 4))}));
+    p.wg_per_head = (int)std::max<int64_t>(1, std::min<int64_t>({slots / pairs, (tiles + NW - 1) / NW, kMaxWG}));
     a.wg_per_head = p.wg_per_head;
     a.part_ld = kPartHead + 16 * p.v.nvb;
     p.part_bytes = (size_t)n_seqs * cb->n_kv * p.wg_per_head * G * a.part_ld * sizeof(float);
@@ -925,7 +934,8 @@ int launch_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* blob
                        blob, cache, a, ids, lens, q, part);
     HIP_TRY(hipGetLastError());
     if (e1) HIP_TRY(hipEventRecord(e1, st));
-    hipLaunchKernelGGL((merge_kernel<D>), dim3(a.n_kv, n_seqs, a.G), dim3(kMergeThreads), 0, st, blob, a.layer, a.n_kv,
+    hipLaunchKernelGGL((merge_kernel<D>), dim3(a.n_kv * (D / kMergeSlice), n_seqs, a.G), dim3(kMergeThreads), 0, st,
+                       blob, a.layer, a.n_kv,
                        a.G, p.wg_per_head, a.part_ld, (const float*)part, out);
     HIP_TRY(hipGetLastError());
     return AATC_OK;
