@@ -77,13 +77,18 @@ typedef struct {
  * reverse water-filling section, sum_j R_j = d * avg_bits per tensor); max_bits: per
  * channel cap (1..8); joint: 1 = keys and values share one budget of 2*d*avg_bits bits
  * per token (one water level for the sum D_K + D_V of the theorem), 0 = d*avg_bits each;
- * max_sweeps: Jacobi sweep limit of the eigensolver (0 = default 60). */
+ * max_sweeps: Jacobi sweep limit of the eigensolver (0 = default 60);
+ * key_transform: 0 = KLT of the key covariance (orthogonal U_K), 1 = attention-optimal
+ * non-orthogonal transform T_K = M_Q^{1/2} R, R the eigenvectors of
+ * M_Q^{1/2} Sigma_K M_Q^{1/2}, under which the attention-aware key distortion is the MSE of
+ * the coefficients ("Spend Bits Where Queries Look", abstract; M_Q gets a ridge of 1e-6 of
+ * its mean eigenvalue).  Values always use the KLT. */
 typedef struct {
     double avg_bits;
     int32_t max_bits;
     int32_t joint;
     int32_t max_sweeps;
-    int32_t reserved;
+    int32_t key_transform;
 } aatc_calib_params;
 
 /* Device-side cache descriptor.  data: caller-allocated device memory of
@@ -137,7 +142,10 @@ int aatc_calibrate(int32_t d, int32_t n_layers, int32_t n_kv, int32_t group,
                    aatc_codebook** out);
 
 /* Build a codebook from explicit per-head arrays (e.g. produced by another calibration
- * tool): U_k, U_v [n_heads][d][d] float64; mu_k, mu_v [n_heads][d] float64; bits_k,
+ * tool): U_k, U_v [n_heads][d][d] float64 - coefficients are c = (x - mu) U, so U_v must be
+ * orthogonal (the value reconstruction uses U_v^T) while U_k may be any invertible key
+ * transform (queries are transformed by U_k^{-1}, computed here in fp64; INVALID_ARG when
+ * singular); mu_k, mu_v [n_heads][d] float64; bits_k,
  * bits_v [n_heads][d] int32 in [0,8]; step_k, step_v [n_heads][d] float32 (> 0 where
  * bits > 0).  Every head must have the same total bits per token (a multiple of 8), with
  * key bits a multiple of 32.

@@ -17,7 +17,8 @@ function cites the passage of the AATC pages it follows:
   "Optimal Bit Allocation via Reverse Water-Filling", and its code listing
   (taken as a description only).
 * p3 = "Spend Bits Where Queries Look" (NOVA-KV) abstract: fixed per-token
-  bit count, bandwidth-bound decoding.
+  bit count, bandwidth-bound decoding, and a non-orthogonal key transform under which
+  attention distortion becomes transform-domain MSE (nova_key_transform).
 
 Readings taken where the pages are silent, garbled or contradict each other
 are stated in the docstring of the function that takes them.  Parity status:
@@ -28,6 +29,7 @@ and is pinned by an independent bit-by-bit implementation in the tests.
 from .calib import (  # noqa: F401
     head_stats, klt, channel_weights, waterfill_theta, allocate_bits,
     uniform_quantizer_mse, optimal_step, build_head_codebook, HeadCodebook,
+    nova_key_transform, key_weights_general,
 )
 from .codec import (  # noqa: F401
     fields, quantize, transform_coeffs, pack_cache, unpack_cache, dequantize,

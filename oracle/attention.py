@@ -28,7 +28,7 @@ def decode_attention(cache: np.ndarray, cb, q_heads: np.ndarray, n_tokens: int) 
     packed cache: unpack, dequantize, inverse transform, then plain attention (every
     cached token is attended; no mask).  q_heads [G, d] -> out [G, d] float64."""
     cK, cV = unpack_cache(cache, cb.bK, cb.bV, n_tokens)
-    Khat = reconstruct(dequantize(cK, cb.bK, cb.stepK), cb.muK, cb.UK)
+    Khat = cb.muK[None, :] + dequantize(cK, cb.bK, cb.stepK) @ cb.UKinv  # c = (k - mu) T  =>  k = mu + c T^{-1}
     Vhat = reconstruct(dequantize(cV, cb.bV, cb.stepV), cb.muV, cb.UV)
     return attention(q_heads, Khat, Vhat)
 

@@ -80,8 +80,49 @@ def klt(Sigma: np.ndarray):
 
 
 # ----------------------------------------------------------------------------------------
+# attention-optimal (non-orthogonal) key transform
+# ----------------------------------------------------------------------------------------
+NOVA_RIDGE = 1e-6  # M_Q + ridge * (tr M_Q / d) I: the transform needs an invertible M_Q
+
+
+def nova_key_transform(SigK: np.ndarray, MQ: np.ndarray, ridge: float = NOVA_RIDGE):
+    """Key transform under which the attention-aware key distortion is plain MSE of the
+    coefficients ("Spend Bits Where Queries Look", abstract: a non-orthogonal optimal
+    transform from calibration statistics; a generalized Parseval relation turns
+    attention distortion into transform-domain MSE).
+
+    Reading (the pages give no formula): a key error e costs (first order, p2 "Theorem")
+    e^T M_Q e.  With coefficients c = (k - mu) T, an error eps in c is e = eps T^{-1}, and
+    e^T M_Q e = eps (T^{-1} M_Q T^{-T}) eps^T, which is |eps|^2 for every T = M_Q^{1/2} R with
+    R orthogonal.  Among those, R = the eigenvectors of M_Q^{1/2} Sigma_K M_Q^{1/2} also
+    decorrelates the coefficients (variances mu = its eigenvalues), which is what the
+    per-channel quantizer and the water-filling assume.  M_Q gets a small ridge so that
+    it is invertible (queries need not span every direction).
+
+    Returns (mu descending, T, T^{-1}); R follows the KLT's order and sign rule."""
+    MQ = np.asarray(MQ, np.float64)
+    d = MQ.shape[0]
+    Mr = 0.5 * (MQ + MQ.T) + ridge * (np.trace(MQ) / d) * np.eye(d)
+    w, V = np.linalg.eigh(Mr)
+    if not np.all(w > 0):
+        raise ValueError("M_Q is not positive definite after the ridge")
+    Mh = (V * np.sqrt(w)[None, :]) @ V.T
+    Mih = (V / np.sqrt(w)[None, :]) @ V.T
+    mu, R = klt(Mh @ np.asarray(SigK, np.float64) @ Mh)
+    return mu, Mh @ R, R.T @ Mih
+
+
+# ----------------------------------------------------------------------------------------
 # attention-aware channel weights
 # ----------------------------------------------------------------------------------------
+def key_weights_general(MQ: np.ndarray, var: np.ndarray, Tinv: np.ndarray) -> np.ndarray:
+    """x_j = var_j (T^{-1} M_Q T^{-T})_jj / d for a general key transform T (coefficient
+    errors eps map to key errors eps T^{-1}); the KLT's weights are the case T = U_K."""
+    d = MQ.shape[0]
+    w = np.einsum("ji,ik,jk->j", Tinv, np.asarray(MQ, np.float64), Tinv) / d
+    return np.maximum(np.asarray(var, np.float64) * w, 0.0)
+
+
 def channel_weights(stats: dict, UK: np.ndarray, lamK: np.ndarray, UV: np.ndarray,
                     lamV: np.ndarray):
     """Per-channel distortion scale x_j = w_j * lambda_j in the KLT domain.
@@ -289,6 +330,11 @@ class HeadCodebook:
     stepK: np.ndarray   # float32 [d] (0 where b = 0)
     stepV: np.ndarray
     theta: float
+    UKinv: np.ndarray = None  # float64 [d, d]: key reconstruction (k_hat = mu + c_hat UKinv); U_K^T for the KLT
+
+    def __post_init__(self):
+        if self.UKinv is None:
+            self.UKinv = self.UK.T.copy()
 
     @property
     def UK32(self):
@@ -320,23 +366,32 @@ KEY_ALIGN = 32  # key bits per token are kept a multiple of one 32-bit word
 
 
 def build_head_codebook(stats: dict, avg_bits: float, max_bits: int = 8,
-                        joint: bool = True) -> HeadCodebook:
-    """Calibrate one head: KLT of both covariances, weights, exact-budget integer bits
-    with total 2 d avg_bits (a multiple of 8; key bits a multiple of 32), and fp32 steps
-    step_b * sqrt(lambda_j)."""
+                        joint: bool = True, key_transform: str = "klt") -> HeadCodebook:
+    """Calibrate one head: KLT of both covariances (or, for the keys, the attention-optimal
+    transform of nova_key_transform), weights, exact-budget integer bits with total
+    2 d avg_bits (a multiple of 8; key bits a multiple of 32), and fp32 steps
+    step_b * sqrt(coefficient variance)."""
     d = stats["d"]
     total = 2.0 * d * avg_bits
     B = int(round(total))
     if abs(total - B) > 1e-9 or B % 8:
         raise ValueError("2*d*avg_bits must be a whole number of bytes (the packed records "
                          "are byte strings)")
-    lamK, UK = klt(stats["SigK"])
     lamV, UV = klt(stats["SigV"])
-    xK, xV = channel_weights(stats, UK, lamK, UV, lamV)
+    if key_transform == "klt":
+        lamK, UK = klt(stats["SigK"])
+        UKinv = UK.T.copy()
+        xK, xV = channel_weights(stats, UK, lamK, UV, lamV)
+    elif key_transform == "nova":
+        lamK, UK, UKinv = nova_key_transform(stats["SigK"], stats["MQ"])
+        xK = key_weights_general(stats["MQ"], lamK, UKinv)
+        xV = np.maximum(lamV * stats["gammaV"], 0.0)
+    else:
+        raise ValueError(f"unknown key transform {key_transform!r}")
     theta, _ = waterfill_theta(np.concatenate([xK, xV]), B, max_bits)
     bK, bV = allocate_bits(xK, xV, B, max_bits, joint, key_align=KEY_ALIGN)
     st = step_table(max_bits)
     stepK = np.where(bK > 0, st[bK] * np.sqrt(lamK), 0.0).astype(np.float32)
     stepV = np.where(bV > 0, st[bV] * np.sqrt(lamV), 0.0).astype(np.float32)
     return HeadCodebook(d, UK, UV, lamK, lamV, stats["muK"].copy(), stats["muV"].copy(),
-                        xK, xV, bK, bV, stepK, stepV, theta)
+                        xK, xV, bK, bV, stepK, stepV, theta, UKinv)

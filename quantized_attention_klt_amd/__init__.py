@@ -37,7 +37,7 @@ class HeadStats(C.Structure):
 
 class CalibParams(C.Structure):
     _fields_ = [("avg_bits", C.c_double), ("max_bits", C.c_int32), ("joint", C.c_int32),
-                ("max_sweeps", C.c_int32), ("reserved", C.c_int32)]
+                ("max_sweeps", C.c_int32), ("key_transform", C.c_int32)]
 
 
 class Cache(C.Structure):
@@ -234,8 +234,12 @@ class Codebook:
 
 
 def calibrate(stats: Sequence[dict], d: int, n_layers: int, n_kv: int, group: int, avg_bits: float,
-              max_bits: int = 8, joint: bool = True, max_sweeps: int = 0) -> Codebook:
-    """aatc_calibrate over per-head statistics dicts (muK, muV, SigK, SigV, MQ, gammaV)."""
+              max_bits: int = 8, joint: bool = True, max_sweeps: int = 0, key_transform: str = "klt") -> Codebook:
+    """aatc_calibrate over per-head statistics dicts (muK, muV, SigK, SigV, MQ, gammaV);
+    key_transform "klt" (orthogonal) or "nova" (attention-optimal, non-orthogonal)."""
+    kt = {"klt": 0, "nova": 1}.get(key_transform)
+    if kt is None:
+        raise ValueError(f"unknown key transform {key_transform!r}")
     keep = []
     arr = (HeadStats * len(stats))()
     for i, s in enumerate(stats):
@@ -243,7 +247,7 @@ def calibrate(stats: Sequence[dict], d: int, n_layers: int, n_kv: int, group: in
         keep.append(a)
         pd = C.POINTER(C.c_double)
         arr[i] = HeadStats(*(x.ctypes.data_as(pd) for x in a), float(s["gammaV"]))
-    p = CalibParams(avg_bits, max_bits, 1 if joint else 0, max_sweeps, 0)
+    p = CalibParams(avg_bits, max_bits, 1 if joint else 0, max_sweeps, kt)
     out = C.c_void_p()
     _check(load().aatc_calibrate(d, n_layers, n_kv, group, arr, C.byref(p), C.byref(out)))
     return Codebook(out.value)

@@ -55,6 +55,10 @@ struct alignas(256) DevHead {
     uint16_t UKt_lo[kMaxD * kMaxD];
     uint16_t UVt_hi[kMaxD * kMaxD];
     uint16_t UVt_lo[kMaxD * kMaxD];
+    // query transform q' = T_K^{-1} q (T_K the key basis; T_K^{-1} = U_K^T for the KLT),
+    // bf16 split in the same layout: QKt_hi[j*d + i] + QKt_lo[j*d + i] = (T_K^{-1})[j][i]
+    uint16_t QKt_hi[kMaxD * kMaxD];
+    uint16_t QKt_lo[kMaxD * kMaxD];
     float muV[kMaxD];
     float obias[kMaxD];           // mu_V - U_V (step_V * (2^(b-1) - 1/2)): output of all-zero codes
     float biasK[kMaxD];           // mu_K (U_hi + U_lo), fp64 sum rounded once

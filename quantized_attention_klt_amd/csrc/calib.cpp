@@ -433,6 +433,46 @@ static void build_encoder_order(const std::vector<Field>& fs, int d, uint8_t* pe
     }
 }
 
+// Inverse of a d x d matrix (row-major) by Gauss-Jordan elimination with partial pivoting,
+// in fp64.  Returns false for a (numerically) singular matrix.
+static bool invert(int d, const std::vector<double>& A, std::vector<double>& inv) {
+    std::vector<double> M(A);
+    inv.assign((size_t)d * d, 0.0);
+    for (int i = 0; i < d; ++i) inv[(size_t)i * d + i] = 1.0;
+    double scale = 0.0;
+    for (double v : A) scale = std::max(scale, std::fabs(v));
+    if (!(scale > 0.0) || !std::isfinite(scale)) return false;
+    for (int c = 0; c < d; ++c) {
+        int piv = c;
+        for (int r = c + 1; r < d; ++r)
+            if (std::fabs(M[(size_t)r * d + c]) > std::fabs(M[(size_t)piv * d + c])) piv = r;
+        const double pv = M[(size_t)piv * d + c];
+        if (!(std::fabs(pv) > 1e-13 * scale)) return false;
+        if (piv != c)
+            for (int k = 0; k < d; ++k) {
+                std::swap(M[(size_t)piv * d + k], M[(size_t)c * d + k]);
+                std::swap(inv[(size_t)piv * d + k], inv[(size_t)c * d + k]);
+            }
+        const double ip = 1.0 / pv;
+        for (int k = 0; k < d; ++k) {
+            M[(size_t)c * d + k] *= ip;
+            inv[(size_t)c * d + k] *= ip;
+        }
+        for (int r = 0; r < d; ++r) {
+            if (r == c) continue;
+            const double f = M[(size_t)r * d + c];
+            if (f == 0.0) continue;
+            for (int k = 0; k < d; ++k) {
+                M[(size_t)r * d + k] -= f * M[(size_t)c * d + k];
+                inv[(size_t)r * d + k] -= f * inv[(size_t)c * d + k];
+            }
+        }
+    }
+    for (double v : inv)
+        if (!std::isfinite(v)) return false;
+    return true;
+}
+
 int finalize(aatc_codebook* cb) {
     const int d = cb->d;
     int total = -1;
@@ -492,6 +532,15 @@ int finalize(aatc_codebook* cb) {
         }
         for (int i = 0; i < d; ++i)
             for (int j = 0; j < d; ++j) D.UVt[j * d + i] = D.UV[i * d + j];
+        // query transform: coefficients c = (k - mu) T, so q.k = (T^{-1} q).c + q.mu
+        std::vector<double> Tinv;
+        if (!invert(d, H.UK, Tinv)) return set_error(AATC_ERR_INVALID_ARG, "head %zu: the key basis is not invertible", h);
+        for (int j = 0; j < d; ++j)
+            for (int i = 0; i < d; ++i) {
+                const float u = (float)Tinv[(size_t)j * d + i];
+                D.QKt_hi[j * d + i] = f32_to_bf16(u);
+                D.QKt_lo[j * d + i] = f32_to_bf16(u - bf16_to_f32(D.QKt_hi[j * d + i]));
+            }
         for (int j = 0; j < d; ++j) {
             D.muV[j] = (float)H.muV[j];
             D.bitsK[j] = H.bK[j];
@@ -544,6 +593,75 @@ using namespace aatc;
 // ======================================================================================
 // C ABI: version / errors
 // ======================================================================================
+// Attention-optimal key transform ("Spend Bits Where Queries Look", abstract: a
+// non-orthogonal transform under which the attention-aware key distortion is the MSE of
+// the coefficients).  A key error e costs e^T M_Q e; with c = (k - mu) T an error eps in c
+// is e = eps T^{-1}, so T = M_Q^{1/2} R makes the cost |eps|^2 for any orthogonal R, and
+// R = the eigenvectors of M_Q^{1/2} Sigma_K M_Q^{1/2} decorrelates the coefficients
+// (variances lam = its eigenvalues).  M_Q gets a ridge of 1e-6 of its mean eigenvalue so
+// that it is invertible.  Outputs T (row-major, [i][j] = T_ij) and T^{-1}.
+static int nova_key_transform(int d, const double* sigma_k, const double* m_q, int sweeps, std::vector<double>& lam,
+                              std::vector<double>& T, std::vector<double>& Tinv) {
+    const size_t dd = (size_t)d * d;
+    std::vector<double> M(dd);
+    double tr = 0.0;
+    for (int i = 0; i < d; ++i) tr += m_q[(size_t)i * d + i];
+    for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) M[(size_t)i * d + j] = 0.5 * (m_q[(size_t)i * d + j] + m_q[(size_t)j * d + i]);
+    for (int i = 0; i < d; ++i) M[(size_t)i * d + i] += 1e-6 * tr / d;
+    std::vector<double> w, V;
+    int rc = jacobi_eigen(d, M.data(), sweeps, w, V);
+    if (rc != AATC_OK) return rc;
+    for (int k = 0; k < d; ++k)
+        if (!(w[k] > 0.0)) return set_error(AATC_ERR_STATS, "M_Q is not positive definite");
+    std::vector<double> Mh(dd, 0.0), Mih(dd, 0.0);
+    for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) {
+            double a = 0.0, b = 0.0;
+            for (int k = 0; k < d; ++k) {
+                const double vv = V[(size_t)i * d + k] * V[(size_t)j * d + k];
+                a += vv * std::sqrt(w[k]);
+                b += vv / std::sqrt(w[k]);
+            }
+            Mh[(size_t)i * d + j] = a;
+            Mih[(size_t)i * d + j] = b;
+        }
+    std::vector<double> A(dd, 0.0), tmp(dd, 0.0);  // A = Mh Sigma_K Mh
+    for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) {
+            double a = 0.0;
+            for (int k = 0; k < d; ++k) a += Mh[(size_t)i * d + k] * sigma_k[(size_t)k * d + j];
+            tmp[(size_t)i * d + j] = a;
+        }
+    for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) {
+            double a = 0.0;
+            for (int k = 0; k < d; ++k) a += tmp[(size_t)i * d + k] * Mh[(size_t)k * d + j];
+            A[(size_t)i * d + j] = a;
+        }
+    for (int i = 0; i < d; ++i)  // exact symmetry for the eigensolver
+        for (int j = i + 1; j < d; ++j) {
+            const double s = 0.5 * (A[(size_t)i * d + j] + A[(size_t)j * d + i]);
+            A[(size_t)i * d + j] = A[(size_t)j * d + i] = s;
+        }
+    std::vector<double> R;
+    rc = jacobi_eigen(d, A.data(), sweeps, lam, R);
+    if (rc != AATC_OK) return rc;
+    T.assign(dd, 0.0);
+    Tinv.assign(dd, 0.0);
+    for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) {
+            double a = 0.0, b = 0.0;
+            for (int k = 0; k < d; ++k) {
+                a += Mh[(size_t)i * d + k] * R[(size_t)k * d + j];   // T = Mh R
+                b += R[(size_t)k * d + i] * Mih[(size_t)k * d + j];  // T^{-1} = R^T Mih
+            }
+            T[(size_t)i * d + j] = a;
+            Tinv[(size_t)i * d + j] = b;
+        }
+    return AATC_OK;
+}
+
 extern "C" int aatc_version(void) { return AATC_VERSION; }
 extern "C" int aatc_layout_version(void) { return AATC_LAYOUT_VERSION; }
 
@@ -677,6 +795,8 @@ extern "C" int aatc_calibrate(int32_t d, int32_t n_layers, int32_t n_kv, int32_t
         return set_error(AATC_ERR_BUDGET, "separate key/value budgets need d*avg_bits (%d) to be a multiple of %d",
                          total / 2, kKeyAlign);
     const int sweeps = p->max_sweeps > 0 ? p->max_sweeps : 60;
+    if (p->key_transform != 0 && p->key_transform != 1)
+        return set_error(AATC_ERR_INVALID_ARG, "key_transform must be 0 (KLT) or 1 (attention-optimal)");
     const int n_heads = n_layers * n_kv;
 
     auto* cb = new aatc_codebook();
@@ -707,7 +827,13 @@ extern "C" int aatc_calibrate(int32_t d, int32_t n_layers, int32_t n_kv, int32_t
             msg[h] = "non-finite statistics";
             return;
         }
-        int rc = jacobi_eigen(d, S.sigma_k, sweeps, H.lamK, H.UK);
+        int rc = AATC_OK;
+        std::vector<double> Tinv;  // attention-optimal transform only: T^{-1}
+        if (p->key_transform == 1) {
+            rc = nova_key_transform(d, S.sigma_k, S.m_q, sweeps, H.lamK, H.UK, Tinv);
+        } else {
+            rc = jacobi_eigen(d, S.sigma_k, sweeps, H.lamK, H.UK);
+        }
         if (rc == AATC_OK) rc = jacobi_eigen(d, S.sigma_v, sweeps, H.lamV, H.UV);
         if (rc != AATC_OK) {
             status[h] = rc;
@@ -720,12 +846,15 @@ extern "C" int aatc_calibrate(int32_t d, int32_t n_layers, int32_t n_kv, int32_t
         H.xK.assign(d, 0.0);
         H.xV.assign(d, 0.0);
         for (int j = 0; j < d; ++j) {
+            // key weight: coefficient variance x (T^{-1} M_Q T^{-T})_jj / d, with T^{-1} = U_K^T
+            // for the KLT (row j of T^{-1} = column j of U_K)
             double w = 0.0;
             for (int a = 0; a < d; ++a) {
-                double ua = H.UK[(size_t)a * d + j];
+                double ua = Tinv.empty() ? H.UK[(size_t)a * d + j] : Tinv[(size_t)j * d + a];
                 if (ua == 0.0) continue;
                 double r = 0.0;
-                for (int b = 0; b < d; ++b) r += S.m_q[(size_t)a * d + b] * H.UK[(size_t)b * d + j];
+                for (int b = 0; b < d; ++b)
+                    r += S.m_q[(size_t)a * d + b] * (Tinv.empty() ? H.UK[(size_t)b * d + j] : Tinv[(size_t)j * d + b]);
                 w += ua * r;
             }
             H.xK[j] = std::max(0.0, H.lamK[j] * w / d);

@@ -1,23 +1,26 @@
 // Split-context decode attention over the packed cache (gfx950).
 //
 // Pages: "Attention-Aware Transform Coding Guide" ("Formal Attention Distortion Model":
-// o = softmax(q K^T / sqrt(d)) V; KLT section K' = K U_K, so q.k = (U_K^T q).(U_K^T k) and
-// keys are scored in the transform domain and never reconstructed; values are
-// inverse-transformed once per query head); "Spend Bits Where Queries Look" abstract
-// (decoding reads the whole cache every step and is bandwidth-bound).
+// o = softmax(q K^T / sqrt(d)) V; KLT section K' = K U_K); "Spend Bits Where Queries Look"
+// abstract (decoding reads the whole cache every step and is bandwidth-bound; a
+// non-orthogonal key transform).  Key coefficients are c = (k - mu) T_K (T_K = U_K for the
+// KLT), so q.k = (T_K^{-1} q).c + q.mu: keys are scored in the transform domain and never
+// reconstructed (the q.mu term is the same for every token); values are inverse-transformed
+// once per query head.
 //
 // Two kernels on the caller's stream.
-//   decode - W workgroups of 4 waves share the 64-token tiles of one (sequence, kv-head).
-//     prologue - every workgroup forms q' = U_K^T q for the kv-head's query heads on bf16
-//                MFMAs (U_K^T is read from the device cache), scales it by the key steps
-//                (and log2 e / sqrt d) and builds the score operands: per key field a query
-//                weight (the field's code shift over its bit position), scaled per head so
-//                the largest is 127 and split into three int8 digits laid out as MFMA A
-//                operands, plus per head the digit scales and the accumulator's start value;
-//                the first tiles stream meanwhile;
-//     tiles    - wave w of workgroup i takes tiles 4i + w + 4Wk and streams them through a
-//                private ring of LDS buffers (direct global->LDS loads, counted waits, no
-//                workgroup barriers in the loop).  Per tile:
+//   decode - W workgroups (one per CU, 8 or 12 waves) share the 64-token tiles of one
+//            (sequence, kv-head).
+//     prologue - every workgroup forms q' = T_K^{-1} q for the kv-head's query heads on bf16
+//                MFMAs (the matrix is read from the device cache), scales it by the key
+//                steps (and log2 e / sqrt d) and builds the score operands: per key field a
+//                query weight (the field's code shift over its bit position), scaled per
+//                head so the largest is 127 and split into three int8 digits laid out as
+//                MFMA A operands, plus per head the digit scales and the accumulator's start
+//                value; the first tiles stream meanwhile;
+//     tiles    - workgroup i takes an even share of the tiles, its waves every NW-th of
+//                those, streamed through private rings of LDS buffers (direct buffer loads
+//                into LDS, counted waits, no workgroup barriers in the loop).  Per tile:
 //       scores  - v_mfma_i32_16x16x64_i8 with rows 4*head + digit and one column per token:
 //                 a B dword is a key-record word ANDed with a mask that keeps one field per
 //                 byte; with bit 7 of stored bytes inverted such a byte reads as
@@ -29,12 +32,13 @@
 //       values  - the same MFMA with one column per value field: the B operand of a column
 //                 is 16 bytes of its record byte's plane (16 tokens) ANDed with the field
 //                 mask;
-//     epilogue - the four waves meet in LDS; the workgroup writes one partial per query
-//                head: reference max, sum of p, sum of p x (128 for fields ending at bit 7),
-//                and per value column sum of p x stored byte.
-//   merge  - one workgroup per (sequence, kv-head, query head) combines the W partials,
-//            turns columns into value coefficients (weight 2^(shift - pos), plus the 128
-//            for fields ending at bit 7), and writes o = obias + U_V (step * A) / L.
+//     epilogue - the waves meet in LDS; the workgroup writes one partial per query head:
+//                reference max, sum of p, sum of p x (128 for fields ending at bit 7), and
+//                per value column sum of p x stored byte.
+//   merge  - one workgroup per (sequence, kv-head, query head, 32 output channels) combines
+//            the W partials, turns columns into value coefficients (weight 2^(shift - pos),
+//            plus the 128 for fields ending at bit 7), and writes its slice of
+//            o = obias + U_V (step * A) / L.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -270,8 +274,8 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
     LDS_AS uint8_t* ring = sm + w * BB;
     const int RS = NW * BB;  // bytes between a wave's ring slots
     int64_t t = n_tiles * wgi / a.wg_per_head + (w + 4) % NW;
-    // ---- prologue.  Waves 0 .. D/16 - 1 each form one 16-channel block of q' = U_K^T q:
-    // (1) register loads of the block's U_K^T rows (hi, lo), the query heads, the key steps
+    // ---- prologue.  Waves 0 .. D/16 - 1 each form one 16-channel block of q' = T_K^{-1} q
+    // (T_K the key basis; U_K^T for the KLT): (1) register loads of the block's rows (hi, lo), the query heads, the key steps
     // and slot weights; (2) direct global->LDS copies of the slot descriptors, the key
     // schedule and the value columns (waves 0..2, one table each); (3) the block on bf16
     // MFMAs, q'' and per head the block's largest slot value into LDS; (4) only then this
@@ -299,8 +303,8 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
         const int j = 16 * w + c;  // A row: channel j
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            ah[ks] = *(const bf16x8*)(H.UKt_hi + j * D + 32 * ks + 8 * g);
-            al[ks] = *(const bf16x8*)(H.UKt_lo + j * D + 32 * ks + 8 * g);
+            ah[ks] = *(const bf16x8*)(H.QKt_hi + j * D + 32 * ks + 8 * g);
+            al[ks] = *(const bf16x8*)(H.QKt_lo + j * D + 32 * ks + 8 * g);
         }
         stv = *(const f4*)(H.stepK + 16 * w + 4 * g);
         fmv = *(const f4*)(H.kq_fmax + 16 * w + 4 * g);

@@ -230,3 +230,44 @@ def test_decode_argument_errors(lib, torch):
     with pytest.raises(lib.AatcError) as e:
         lib.encode(cb, blob, cache, 0, [0], [120], 10, K, K)
     assert e.value.status == -6
+
+
+# ---- attention-optimal (non-orthogonal) key transform: the encoder projects keys with T,
+# the decode transforms queries with T^{-1} (computed by the library); same bars.
+@pytest.mark.parametrize("wname,ctx", [("tiny", 512), ("llama_32k", 3000)])
+def test_decode_parity_attention_optimal_keys(lib, torch, wname, ctx):
+    _log(f"decode (attention-optimal keys) {wname} ctx={ctx}")
+    case = Case(wname, ctx, n_calib_q=64, key_transform="nova")
+    cache_host, _ = case.oracle_cache()
+    got = _decode(lib, torch, case, cache_host, case.lens, ctx)
+    err = normwise_rel_err(got, case.oracle_decode(cache_host))
+    _log(f"  rel err {err:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= ATTN_BAR
+
+
+@pytest.mark.parametrize("wname,ctx", [("tiny", 512), ("llama_32k", 1000)])
+def test_encode_flips_attention_optimal_keys(lib, torch, wname, ctx):
+    _log(f"encode (attention-optimal keys) {wname} ctx={ctx}")
+    case = Case(wname, ctx, n_calib_q=64, key_transform="nova")
+    cb, blob = _device_codebook(lib, torch, case)
+    ct, cache = _new_cache(lib, torch, cb, 1, ctx)
+    K = torch.from_numpy(case.k_bits.view(np.int16)).cuda()
+    V = torch.from_numpy(case.v_bits.view(np.int16)).cuda()
+    lib.encode(cb, blob, cache, 0, [0], [0], ctx, K, V)
+    torch.cuda.synchronize()
+    got = ct.cpu().numpy().reshape(case.n_kv, -1)
+    _, codes = case.oracle_cache()
+    flips, total, worst = 0, 0, 0
+    for h, c in enumerate(case.cbs):
+        gK, gV = oracle.unpack_cache(got[h], c.bK, c.bV, ctx)
+        rK, rV = codes[(0, h)]
+        for g, r, b in ((gK, rK, c.bK), (gV, rV, c.bV)):
+            m = np.broadcast_to(b > 0, g.shape)
+            dlt = np.abs(g - r)[m]
+            flips += int((dlt > 0).sum())
+            total += int(m.sum())
+            worst = max(worst, int(dlt.max()))
+    _log(f"  flips {flips}/{total}")
+    assert worst <= 1
+    assert flips <= FLIP_BAR * total

@@ -53,6 +53,34 @@ def test_calibrate_matches_oracle(wname, joint):
     assert cb.total_bits == int(2 * w.d * w.avg_bits) and cb.tile_bytes == 8 * cb.total_bits
 
 
+@pytest.mark.parametrize("wname", ["tiny", "llama_32k"])
+def test_calibrate_attention_optimal_keys_matches_oracle(wname):
+    """key_transform = attention-optimal: the library's non-orthogonal key basis,
+    coefficient variances, weights, bits and steps against the oracle's."""
+    w, K, V, Q = _samples(wname)
+    st = oracle.head_stats(K.astype(np.float64), V.astype(np.float64), Q.astype(np.float64))
+    cb = q.calibrate([st], w.d, 1, 1, w.group, w.avg_bits, key_transform="nova")
+    ref = oracle.build_head_codebook(st, w.avg_bits, key_transform="nova")
+    h = cb.head(0)
+    assert np.abs(h["lamK"] - ref.lamK).max() <= 1e-10 * ref.lamK.max()
+    gap = np.minimum(np.r_[np.inf, -np.diff(ref.lamK)], np.r_[-np.diff(ref.lamK), np.inf])
+    sep = gap > 1e-6 * ref.lamK.max()
+    assert np.abs(h["UK"][:, sep] - ref.UK[:, sep]).max() < 1e-7 * np.abs(ref.UK).max()
+    assert np.abs(h["UK"].T @ h["UK"] - np.eye(w.d)).max() > 1e-3  # not orthogonal
+    assert np.array_equal(h["bK"], ref.bK) and np.array_equal(h["bV"], ref.bV)
+    assert np.allclose(h["stepK"], ref.stepK, rtol=1e-6) and np.allclose(h["stepV"], ref.stepV, rtol=1e-6)
+    assert np.allclose(h["xK"], ref.xK, rtol=1e-9) and np.allclose(h["xV"], ref.xV, rtol=1e-9)
+
+
+def test_codebook_rejects_singular_key_basis():
+    w, ref = _oracle_codebook()
+    T = ref.UK.copy()
+    T[:, 1] = T[:, 0]
+    with pytest.raises(q.AatcError):
+        q.codebook_create(ref.d, 1, 1, 4, T[None], ref.UV[None], ref.muK[None], ref.muV[None], ref.bK[None],
+                          ref.bV[None], ref.stepK[None], ref.stepV[None])
+
+
 def w_name_has_heads(wname):
     return synth.WORKLOADS[wname].n_kv > 1
 

@@ -11,7 +11,7 @@ class Case:
     """Oracle codebooks and synthetic K/V/Q for n_kv heads of one layer of workload w."""
 
     def __init__(self, wname: str, ctx: int, n_seqs: int = 1, n_kv: int | None = None, layer: int = 0,
-                 n_calib_q: int | None = None, lens=None, step: int = 0):
+                 n_calib_q: int | None = None, lens=None, step: int = 0, key_transform: str = "klt"):
         w = synth.WORKLOADS[wname]
         self.w = w
         self.d = w.d
@@ -28,7 +28,8 @@ class Case:
             K, V, Q = synth.calibration_samples(w, hm, layer, h)
             if n_calib_q is not None:
                 Q = Q.reshape(w.group, -1, w.d)[:, :n_calib_q].reshape(-1, w.d)
-            self.cbs.append(oracle.build_head_codebook(oracle.head_stats(K, V, Q), w.avg_bits))
+            self.cbs.append(oracle.build_head_codebook(oracle.head_stats(K, V, Q), w.avg_bits,
+                                                       key_transform=key_transform))
         # cached K/V: bf16 bits [n_seqs, ctx, n_kv, d] and their float64 values
         self.k_bits = np.zeros((n_seqs, ctx, self.n_kv, w.d), np.uint16)
         self.v_bits = np.zeros_like(self.k_bits)
