@@ -242,6 +242,23 @@ int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob, const aat
                           const int64_t* seq_lens, int64_t max_len, const uint16_t* q,
                           float* out, void* workspace, size_t ws_bytes, void* stream);
 
+/* One generation step of one layer: append one token per sequence, then decode over the
+ * grown cache, in the same launch.  k_new, v_new: device bf16 [n_seqs][n_kv][d] (16-byte
+ * aligned); the token of sequence s is written at slot seq_lens[s] (device array: the
+ * tokens cached before the call) with the codes aatc_encode would write for it, and the
+ * attention runs over seq_lens[s] + 1 tokens (each limited to max_len and max_tokens; a
+ * slot past that limit is neither written nor attended).  The caller advances seq_lens
+ * afterwards.  Other arguments, workspace and errors as aatc_decode_attention.  The
+ * workgroup that owns the token's tile codes it (the encoder's MFMA projection and
+ * quantizer) and places its records in its copy of the tile, so the step needs no ordering
+ * between the write and the tile's stream ("Spend Bits Where Queries Look", abstract:
+ * decoding reads the whole cache at every step). */
+int aatc_decode_attention_append(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
+                                 int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                                 const int64_t* seq_lens, int64_t max_len, const uint16_t* k_new,
+                                 const uint16_t* v_new, const uint16_t* q, float* out, void* workspace,
+                                 size_t ws_bytes, void* stream);
+
 /* ---- measurement helpers ----------------------------------------------------------- */
 
 /* Overwrite `bytes` of caller-allocated device memory with a streaming write (used to

@@ -51,7 +51,7 @@ EXPORTS = [
     "aatc_codebook_head", "aatc_codebook_fields", "aatc_codebook_save", "aatc_codebook_load", "aatc_codebook_free",
     "aatc_codebook_device_bytes", "aatc_codebook_upload", "aatc_cache_bytes", "aatc_encode",
     "aatc_encode_coeffs", "aatc_decode_workspace_bytes", "aatc_decode_attention",
-    "aatc_flush_write", "aatc_profile_begin", "aatc_profile_end",
+    "aatc_decode_attention_append", "aatc_flush_write", "aatc_profile_begin", "aatc_profile_end",
 ]
 
 _lib = None
@@ -95,6 +95,8 @@ def load() -> C.CDLL:
         "aatc_decode_workspace_bytes": ([P, i32, i64, C.POINTER(C.c_size_t)], C.c_int),
         "aatc_decode_attention": ([P, P, C.POINTER(Cache), i32, i32, P, P, i64, P, P, P, C.c_size_t, P],
                                   C.c_int),
+        "aatc_decode_attention_append": ([P, P, C.POINTER(Cache), i32, i32, P, P, i64, P, P, P, P, P, C.c_size_t, P],
+                                         C.c_int),
         "aatc_flush_write": ([P, C.c_size_t, P], C.c_int),
         "aatc_profile_begin": ([i32], C.c_int),
         "aatc_profile_end": ([C.POINTER(C.c_float), C.POINTER(i32)], C.c_int),
@@ -300,6 +302,17 @@ def decode_attention(cb: Codebook, d_blob, cache: Cache, layer: int, seq_ids, se
                                         _dev(seq_ids), _dev(seq_lens), max_len, _dev(q), _dev(out),
                                         _dev(workspace), workspace.numel() * workspace.element_size(),
                                         _stream(stream)))
+
+
+def decode_attention_append(cb: Codebook, d_blob, cache: Cache, layer: int, seq_ids, seq_lens, max_len: int, k_new,
+                            v_new, q, out, workspace, stream=None):
+    """aatc_decode_attention_append: k_new, v_new bf16 device [n_seqs, n_kv, d] are written
+    at slot seq_lens[s] (the tokens cached before the call) and attended to together with
+    the cached tokens; the caller advances seq_lens afterwards."""
+    _check(load().aatc_decode_attention_append(cb.handle, _dev(d_blob), C.byref(cache), layer, seq_ids.numel(),
+                                               _dev(seq_ids), _dev(seq_lens), max_len, _dev(k_new), _dev(v_new),
+                                               _dev(q), _dev(out), _dev(workspace),
+                                               workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def flush_write(buf, stream=None):

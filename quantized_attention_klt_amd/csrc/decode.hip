@@ -53,6 +53,7 @@ using aatc::check_cache;
 using aatc::DevHead;
 using aatc::kTile;
 using aatc::n_tiles_of;
+using aatc::quantize;
 using aatc::set_error;
 
 namespace {
@@ -81,11 +82,15 @@ struct DecodeArgs {
     int64_t n_tiles_cap;
     int64_t max_len;
     int tile_bytes, wg_per_head, part_ld;
+    // append mode: one new token per (sequence, kv-head) - keys, values [n_seqs][n_kv][d]
+    // bf16 - is written at slot seq_lens[s] and attended to (null: plain decode)
+    const uint16_t* k_new;
+    const uint16_t* v_new;
     TileLoads tl;  // the load instructions of one tile
     // LDS carve-up (bytes): slot k of wave w's ring at (k * 4 + w) * buf_bytes; the
     // prologue's scratch at off_scratch, beside the ring (early = nbw: every slot streams
     // from the start) or in its last nbw - early slots
-    int nbw, buf_bytes, early, off_scratch, off_ksched;
+    int nbw, buf_bytes, early, off_scratch, off_ksched, off_rec;
 };
 
 // LDS-only workgroup barrier: this wave's LDS operations are complete, then s_barrier.
@@ -97,6 +102,11 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // operations complete in order; the LDS-only barrier waits for them.
 __device__ __forceinline__ void lds_add_async(LDS_AS int* p, int v) {
     asm volatile("ds_add_u32 %0, %1" ::"v"(p), "v"(v) : "memory");
+}
+
+// LDS OR as an instruction of its own (see lds_add_async)
+__device__ __forceinline__ void lds_or_async(LDS_AS uint32_t* p, uint32_t v) {
+    asm volatile("ds_or_b32 %0, %1" ::"v"(p), "v"(v) : "memory");
 }
 
 // wait until at most n of this wave's vector memory operations are outstanding (n is
@@ -224,14 +234,63 @@ constexpr int operand_bytes(int rb, int nqm) { return nqm * rb * 1024 + rb * 4 *
 // bytes of the decode prologue's LDS scratch: the operands, the value columns [NVB][16],
 // the slot descriptors [NQM][4][16], q'' [4 RB][D], block maxima [D / 16][16], bit-7 digit
 // sums [RB][16]
+constexpr int kMaxRecord = 2 * aatc::kMaxD;  // bytes of a token's two records at 8 bits per element
 constexpr int scratch_bytes(int rb, int nqm, int nvb, int d) {
     return operand_bytes(rb, nqm) + nvb * 64 + nqm * 128 + 16 * rb * d + 4 * d + 64 * rb;
+}
+
+// Append mode: the codes of one token for column block cb of 2 D / 16 (key blocks, then
+// value blocks), OR-ed into its records staged in LDS (key record bytes, then value record
+// bytes).  The projection runs on the encoder's MFMAs with the same operands, start value
+// and order (hi then lo per k-step), and the same quantizer, so the codes equal those the
+// encoder writes for the token.  Lane (0, c) holds the token's coefficient of channel
+// 16 (cb mod D / 16) + c (MFMA row 0; the other rows are zero).
+template <int D>
+__device__ __forceinline__ void append_block(const DevHead& H, const uint16_t* xk, const uint16_t* xv, int cb,
+                                             LDS_AS uint32_t* rec, int g, int c) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    constexpr int NB = D / 16, KS = D / 32;
+    const bool isV = cb >= NB;
+    const int j = 16 * (isV ? cb - NB : cb) + c;
+    const uint16_t* uh = isV ? H.UVt_hi : H.UKt_hi;
+    const uint16_t* ul = isV ? H.UVt_lo : H.UKt_lo;
+    const uint16_t* x = isV ? xv : xk;
+    bf16x8 bh[KS], bl[KS], av[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        bh[ks] = *(const bf16x8*)(uh + j * D + 32 * ks + 8 * g);
+        bl[ks] = *(const bf16x8*)(ul + j * D + 32 * ks + 8 * g);
+        const bf16x8 xa = *(const bf16x8*)(x + 32 * ks + 8 * g);
+        av[ks] = c == 0 ? xa : bf16x8{};
+    }
+    const float nb = -(isV ? H.biasV[j] : H.biasK[j]);
+    const float inv = isV ? H.invV[j] : H.invK[j];
+    const int bits = isV ? H.bitsV[j] : H.bitsK[j];
+    const uint32_t* pc = isV ? H.cpieceV : H.cpieceK;
+    const int16_t* cf = isV ? H.cfirstV : H.cfirstK;
+    const int p0 = cf[j], p1 = cf[j + 1];
+    const int base = isV ? H.BK / 8 : 0;  // record byte of the value record's byte 0
+    f4 acc = f4{nb, nb, nb, nb};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks], bh[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks], bl[ks], acc, 0, 0, 0);
+    }
+    if (g == 0 && bits > 0) {
+        const uint32_t code = quantize(acc[0], inv, bits);
+        for (int p = p0; p < p1; ++p) {  // piece = byte | pos << 8 | width << 12 | shift << 16
+            const uint32_t pcv = pc[p];
+            const int rb = base + (int)(pcv & 0xff), pos = (pcv >> 8) & 7, wd = (pcv >> 12) & 15, sh = (pcv >> 16) & 15;
+            const uint32_t v = ((code >> sh) & ((1u << wd) - 1u)) << pos;
+            lds_or_async(rec + (rb >> 2), v << (8 * (rb & 3)));
+        }
+    }
 }
 
 template <int RB, int NQM, int NVB, int D>
 __global__ __launch_bounds__(64 * wg_waves(RB, NQM, NVB))
 __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel(
-    const DevHead* __restrict__ blob, const uint8_t* __restrict__ cache, DecodeArgs a,
+    const DevHead* __restrict__ blob, uint8_t* __restrict__ cache, DecodeArgs a,
     const int32_t* __restrict__ seq_ids, const int64_t* __restrict__ seq_lens, const uint16_t* __restrict__ q,
     float* __restrict__ part) {
     typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -250,13 +309,19 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
     // the value block's offset in a tile, read (as a scalar load) before any copy is issued:
     // a vector load after them would make the compiler wait for every copy in flight
     const uint32_t vblock = 8u * (uint32_t)H.BK;
-    asm volatile("" ::"s"(vblock));
+    const int nkw = H.BK / 32, nvr = H.BV / 8;  // a token's key record words, value record bytes
+    asm volatile("" ::"s"(vblock), "s"(nkw), "s"(nvr));
     // ---- sequence geometry (device arguments clamped: no read outside the cache)
     const int seq = seq_ids[z];
-    int64_t len = min(min(seq_lens[z], a.max_len), a.n_tiles_cap * kTile);
+    const int64_t len0 = seq_lens[z];  // tokens cached before this call
+    int64_t len = min(min(len0 + (a.k_new ? 1 : 0), a.max_len), a.n_tiles_cap * kTile);
     if (seq < 0 || seq >= a.n_seqs_cache) len = 0;
     const int64_t n_tiles = (len + kTile - 1) / kTile;
-    const uint8_t* tiles = cache + (((int64_t)a.layer * a.n_seqs_cache + seq) * a.n_kv + h) * a.n_tiles_cap * TB;
+    uint8_t* tiles = cache + (((int64_t)a.layer * a.n_seqs_cache + seq) * a.n_kv + h) * a.n_tiles_cap * TB;
+    // append mode: the new token's slot, when it lies within the attended range
+    const bool app = a.k_new && len0 >= 0 && len0 < len;
+    const int64_t t_app = app ? len0 / kTile : -1;
+    const int s_app = (int)(len0 & (kTile - 1));
     // buffer resource over this (sequence, kv-head)'s tiles (the host keeps the range below 2^31 bytes)
     const __amdgpu_buffer_rsrc_t trs =
         __builtin_amdgcn_make_buffer_rsrc((void*)tiles, (short)0, (int)(a.n_tiles_cap * TB), 0x00020000);
@@ -274,6 +339,7 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
     LDS_AS uint8_t* ring = sm + w * BB;
     const int RS = NW * BB;  // bytes between a wave's ring slots
     int64_t t = n_tiles * wgi / a.wg_per_head + (w + 4) % NW;
+    const bool owner = t_app >= n_tiles * wgi / a.wg_per_head && t_app < t_end;  // this workgroup codes the new token
     // ---- prologue.  Waves 0 .. D/16 - 1 each form one 16-channel block of q' = T_K^{-1} q
     // (T_K the key basis; U_K^T for the KLT): (1) register loads of the block's rows (hi, lo), the query heads, the key steps
     // and slot weights; (2) direct global->LDS copies of the slot descriptors, the key
@@ -295,6 +361,7 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
     LDS_AS float* qf = (LDS_AS float*)(scr + QB + NVB * 64 + NQM * 128);  // [GM][D] q''
     LDS_AS float* bmax = qf + GM * D;                                     // [NB][16] block maxima per head
     LDS_AS int* corr = (LDS_AS int*)(bmax + NB * 16);                     // [RB][16] digit sums of bit-7 slots
+    LDS_AS uint32_t* rec = (LDS_AS uint32_t*)(sm + a.off_rec);            // [kMaxRecord] appended token's records
     LDS_AS u32x4* ksched = (LDS_AS u32x4*)(sm + a.off_ksched);            // [NQM][4][2]: offsets, masks
     const bool qwave = w < NB;  // this wave forms channel block w
     bf16x8 ah[KS], al[KS], bq[KS];
@@ -340,6 +407,12 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
         if (g == 0) bmax[w * 16 + c] = mag;
     }
     if (tid < RB * 16) corr[tid] = 0;
+    if (owner) {  // (workgroup-uniform) the new token's codes, before this workgroup's tiles stream
+        if (tid < kMaxRecord / 4) rec[tid] = 0u;
+        lds_barrier();
+        const int64_t row = ((int64_t)z * a.n_kv + h) * D;
+        for (int cb = w; cb < 2 * NB; cb += NW) append_block<D>(H, a.k_new + row, a.v_new + row, cb, rec, g, c);
+    }
     // The waves that do not form q' issue their whole first ring at once; the others one
     // tile, and the rest once the score operands are built: the issue of a copy stalls while
     // the memory system's queues are full, and the q' waves would sit in those stalls instead
@@ -349,6 +422,7 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
         stream_tile(trs, (uint32_t)((t + stride * issued) * TB), ring + issued * RS, tl, lane);
     wait_vm(nl * issued);  // the table copies (issued before the tiles) have landed
     lds_barrier();         // ... in every wave, and q'' and the block maxima are in LDS
+
     // score operands: item (m, rb, lane group gg, dword iw, head hh4) forms the three digit
     // words of its four slots (rows 4 hh4 + 0..2 of operand [m][rb]; row 4 hh4 + 3 is zero)
     for (int i = tid; i < NQM * RB * 64; i += NW * 64) {
@@ -483,6 +557,12 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
         // are outstanding
         wait_vm(nl * (issued - done - 1));
         LDS_AS uint8_t* curb = ring + slot * RS;
+        if (owner && t == t_app) {  // the appended token's slot, whatever the copy read for it
+            for (int r = lane; r < nkw; r += 64) ((LDS_AS uint32_t*)curb)[64 * r + s_app] = rec[r] ^ 0x80808080u;
+            for (int q = lane; q < nvr; q += 64)
+                curb[vblock + 64 * q + s_app] = (uint8_t)(((const LDS_AS uint8_t*)rec)[4 * nkw + q] ^ 0x80u);
+            asm volatile("" ::: "memory");
+        }
         const int valid = (int)min((int64_t)kTile, len - t * kTile);
 
         // ---------------- scores: token group tg, lane (g, c) -> token 4c + tg.  One 16-byte
@@ -627,6 +707,12 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
     // workgroup's reference is the largest of the waves', each wave weighted by 2^(m - M).
     constexpr int PL = kPartHead + 16 * NVB;  // floats per partial and head
     wait_all();
+    if (owner && w == NW - 1) {  // the new token's records into the cache (stored bytes: bit 7 inverted)
+        uint8_t* tp = tiles + t_app * TB;
+        for (int r = lane; r < nkw; r += 64) ((uint32_t*)tp)[64 * r + s_app] = rec[r] ^ 0x80808080u;
+        for (int q = lane; q < nvr; q += 64)
+            tp[vblock + 64 * q + s_app] = (uint8_t)(((const LDS_AS uint8_t*)rec)[4 * nkw + q] ^ 0x80u);
+    }
     lds_barrier();
     LDS_AS float* wx = (LDS_AS float*)sm;  // [NW waves][GM][PL]
     LDS_AS float* ew = wx + NW * GM * PL;  // [NW waves][GM] weights, then [GM] maxima
@@ -884,7 +970,8 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
         top = std::max(ring, a.off_scratch + scr);
     }
     a.off_ksched = (int)al16(std::max(top, epi));
-    p.lds = a.off_ksched + ksch;
+    a.off_rec = (int)al16(a.off_ksched + ksch);  // the appended token's records (outside ring and scratch)
+    p.lds = a.off_rec + kMaxRecord;
     p.wgs_per_cu = 1;
     if (p.lds > 160 * 1024 - 256)
         return set_error(AATC_ERR_UNSUPPORTED, "decode needs %zu bytes of LDS per workgroup", p.lds);
@@ -924,7 +1011,7 @@ void profile_slot(hipEvent_t& a, hipEvent_t& b) {
 }
 
 template <int RB, int NQM, int NVB, int D>
-int launch_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* blob, const uint8_t* cache,
+int launch_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* blob, uint8_t* cache,
                   const int32_t* ids, const int64_t* lens, const uint16_t* q, float* part, float* out) {
     const DecodeArgs& a = p.args;
     if (p.lds > 64 * 1024)
@@ -1000,10 +1087,10 @@ extern "C" int aatc_decode_workspace_bytes(const aatc_codebook* cb, int32_t n_se
     return AATC_OK;
 }
 
-extern "C" int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
-                                     int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const int64_t* seq_lens,
-                                     int64_t max_len, const uint16_t* q, float* out, void* workspace,
-                                     size_t ws_bytes, void* stream) {
+static int decode_impl(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache, int32_t layer,
+                       int32_t n_seqs, const int32_t* seq_ids, const int64_t* seq_lens, int64_t max_len,
+                       const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q, float* out, void* workspace,
+                       size_t ws_bytes, void* stream) {
     if (!cb || !d_blob) return set_error(AATC_ERR_INVALID_ARG, "null codebook or blob");
     int rc = check_cache(cb, cache, layer);
     if (rc) return rc;
@@ -1031,7 +1118,9 @@ extern "C" int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob
     a.max_len = max_len;
     const DevHead* blob = (const DevHead*)d_blob;
     hipStream_t st = (hipStream_t)stream;
-    const uint8_t* c = (const uint8_t*)cache->data;
+    uint8_t* c = (uint8_t*)cache->data;
+    a.k_new = k_new;
+    a.v_new = v_new;
 #define AATC_DECODE_CASE(rb_, nqm_, nvb_)                                                                    \
     if (p.v.rb == rb_ && p.v.nqm == nqm_ && p.v.nvb == nvb_)                                                 \
         return cb->d == 64                                                                                   \
@@ -1056,4 +1145,24 @@ extern "C" int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob
     AATC_DECODE_CASE(4, 16, 24)
 #undef AATC_DECODE_CASE
     return set_error(AATC_ERR_UNSUPPORTED, "decode variant missing");
+}
+
+extern "C" int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
+                                     int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const int64_t* seq_lens,
+                                     int64_t max_len, const uint16_t* q, float* out, void* workspace,
+                                     size_t ws_bytes, void* stream) {
+    return decode_impl(cb, d_blob, cache, layer, n_seqs, seq_ids, seq_lens, max_len, nullptr, nullptr, q, out,
+                       workspace, ws_bytes, stream);
+}
+
+extern "C" int aatc_decode_attention_append(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
+                                            int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                                            const int64_t* seq_lens, int64_t max_len, const uint16_t* k_new,
+                                            const uint16_t* v_new, const uint16_t* q, float* out, void* workspace,
+                                            size_t ws_bytes, void* stream) {
+    if (!k_new || !v_new) return set_error(AATC_ERR_INVALID_ARG, "null new key or value");
+    if ((((uintptr_t)k_new) | ((uintptr_t)v_new)) & 15)
+        return set_error(AATC_ERR_INVALID_ARG, "new key and value rows must be 16-byte aligned");
+    return decode_impl(cb, d_blob, cache, layer, n_seqs, seq_ids, seq_lens, max_len, k_new, v_new, q, out,
+                       workspace, ws_bytes, stream);
 }

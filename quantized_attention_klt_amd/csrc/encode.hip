@@ -19,6 +19,7 @@ using aatc::check_cache;
 using aatc::DevHead;
 using aatc::kTile;
 using aatc::n_tiles_of;
+using aatc::quantize;
 using aatc::set_error;
 
 namespace {
@@ -38,12 +39,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
-// quantizer: t = c * inv (one fp32 rounding), code = clamp(floor(t) + 2^(b-1), 0, 2^b - 1)
-// (b >= 1)
-__device__ __forceinline__ uint32_t quantize(float c, float inv, int b) {
-    const float v = floorf(__fmul_rn(c, inv)) + (float)(1 << (b - 1));
-    return (uint32_t)__builtin_amdgcn_fmed3f(v, 0.0f, (float)((1 << b) - 1));
-}
 
 // LDS-only workgroup barrier: this wave's LDS operations are complete, then s_barrier
 // (vector memory operations in flight are not waited for; their waits are explicit)

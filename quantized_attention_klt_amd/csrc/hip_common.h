@@ -29,4 +29,11 @@ inline int check_cache(const aatc_codebook* cb, const aatc_cache* cache, int lay
 
 __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// The scalar quantizer of every encode path: t = c * inv (one fp32 rounding),
+// code = clamp(floor(t) + 2^(b-1), 0, 2^b - 1) (b >= 1).
+__device__ __forceinline__ uint32_t quantize(float c, float inv, int b) {
+    const float v = floorf(__fmul_rn(c, inv)) + (float)(1 << (b - 1));
+    return (uint32_t)__builtin_amdgcn_fmed3f(v, 0.0f, (float)((1 << b) - 1));
+}
+
 }  // namespace aatc

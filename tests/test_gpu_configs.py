@@ -172,3 +172,52 @@ def test_decode_wide_batch(lib, torch):
     _log(f"  rel err {err:.3e}")
     assert np.all(np.isfinite(got))
     assert err <= ATTN_BAR
+
+
+@pytest.mark.parametrize("wname,n_seqs,l0,steps", [("tiny", 2, (126, 63), 4), ("llama_loop", 1, (3000,), 4)])
+def test_fused_append_decode_loop(lib, torch, wname, n_seqs, l0, steps):
+    """Generation loop through aatc_decode_attention_append: per step one new token per
+    (sequence, kv-head) is coded and attended in the same launch.  The cache bytes equal
+    those of aatc_encode appending the same tokens (bit-exact), and every step's output
+    is within the decode bar of the oracle on the GPU's own bytes (tile boundaries and
+    ragged sequences included)."""
+    ctx = max(l0) + steps
+    case = Case(wname, ctx, n_seqs=n_seqs, n_calib_q=64)
+    _log(f"{wname}: fused append+decode, {n_seqs} sequences from {l0}, {steps} steps")
+    cb, blob = _device_codebook(lib, torch, case)
+    ct, cache = _new_cache(lib, torch, cb, n_seqs, ctx)
+    rt, rcache = _new_cache(lib, torch, cb, n_seqs, ctx)
+    K = torch.from_numpy(case.k_bits.view(np.int16)).cuda()
+    V = torch.from_numpy(case.v_bits.view(np.int16)).cuda()
+    for s in range(n_seqs):  # prefill both caches with the encoder
+        for c in (cache, rcache):
+            lib.encode(cb, blob, c, 0, [s], [0], l0[s], K[s:s + 1, :l0[s]].contiguous(), V[s:s + 1, :l0[s]].contiguous())
+    ids = torch.arange(n_seqs, dtype=torch.int32, device="cuda")
+    lens = torch.tensor(l0, dtype=torch.int64, device="cuda")
+    ws = torch.zeros((cb.decode_workspace_bytes(n_seqs, ctx),), dtype=torch.uint8, device="cuda")
+    G = case.group
+    for st in range(steps):
+        pos = [l + st for l in l0]
+        kn = torch.stack([K[s, pos[s]] for s in range(n_seqs)]).contiguous()  # [n_seqs, n_kv, d]
+        vn = torch.stack([V[s, pos[s]] for s in range(n_seqs)]).contiguous()
+        q_bits = np.stack([synth.to_bf16_bits(synth.decode_queries(case.w, case.hms, case.layer, s, step=st + 1))
+                           for s in range(n_seqs)])
+        qd = torch.from_numpy(q_bits.view(np.int16)).cuda()
+        out = torch.full((n_seqs, case.n_q, case.d), float("nan"), dtype=torch.float32, device="cuda")
+        lib.decode_attention_append(cb, blob, cache, 0, ids, lens, ctx, kn, vn, qd, out, ws)
+        for s in range(n_seqs):
+            lib.encode(cb, blob, rcache, 0, [s], [pos[s]], 1, K[s:s + 1, pos[s]:pos[s] + 1].contiguous(),
+                       V[s:s + 1, pos[s]:pos[s] + 1].contiguous())
+        lens += 1
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        bytes_ = ct.cpu().numpy().reshape(n_seqs, case.n_kv, -1)
+        assert np.array_equal(bytes_, rt.cpu().numpy().reshape(n_seqs, case.n_kv, -1)), f"step {st}: cache bytes"
+        qf = synth.bf16_bits_to_f64(q_bits)
+        ref = np.stack([np.stack([oracle.decode_attention(bytes_[s, h], case.cbs[h], qf[s, h * G:(h + 1) * G],
+                                                          pos[s] + 1) for h in range(case.n_kv)]).reshape(case.n_q, case.d)
+                        for s in range(n_seqs)])
+        err = normwise_rel_err(got, ref)
+        _log(f"  step {st}: lengths {[p + 1 for p in pos]}, rel err {err:.3e}")
+        assert np.all(np.isfinite(got))
+        assert err <= ATTN_BAR
