@@ -91,6 +91,7 @@ struct DecodeArgs {
     // prologue's scratch at off_scratch, beside the ring (early = nbw: every slot streams
     // from the start) or in its last nbw - early slots
     int nbw, buf_bytes, early, off_scratch, off_ksched, off_rec;
+    int off_pbuf;  // per-wave probability operands [NW][RB KiB] when the key block is smaller, else -1
 };
 
 // LDS-only workgroup barrier: this wave's LDS operations are complete, then s_barrier.
@@ -226,6 +227,8 @@ constexpr bool ksched_in_regs(int nqm) { return nqm <= 2; }
 constexpr int waves_for(int rb, int nqm, int nvb) { return rb == 1 && nqm <= 3 && nvb <= 8 ? 3 : 2; }
 // A decode workgroup fills one CU at that occupancy: 4 SIMDs x waves_for waves.
 constexpr int wg_waves(int rb, int nqm, int nvb) { return 4 * waves_for(rb, nqm, nvb); }
+// the epilogue combines the waves' results for at most two row blocks at a time
+constexpr int epilogue_row_blocks(int rb) { return rb < 2 ? rb : 2; }
 
 // bytes of the score operands in LDS: the A operands [NQM][RB][64 lanes] (16 bytes each),
 // then per (row block, head) a 32-byte lane record (three float digit scales, three int
@@ -297,6 +300,8 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
     constexpr int PST = 64;          // bytes per row of the probability operand (64 tokens)
     constexpr int GM = 4 * RB;       // query heads the operands have room for
     constexpr int NW = wg_waves(RB, NQM, NVB);  // waves per workgroup
+    constexpr int RBP = epilogue_row_blocks(RB);  // row blocks per epilogue pass
+    constexpr int GP = 4 * RBP;                   // query heads per epilogue pass
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     LDS_AS uint8_t* sm = (LDS_AS uint8_t*)smem_generic;
     const int wgi = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
@@ -645,8 +650,9 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
         // probabilities: N = round(p * 127 * 2^16) < 2^23; the bytes of N + 0x8080 with
         // bit 7 of the two low bytes inverted are its base-256 digits (top digit 0..127, the
         // others -128..127).  P[16 rb + 4 head + digit][token] over the tile's key block
-        // (wave-private; the key words of this tile were all read above).
-        LDS_AS uint8_t* P = curb;
+        // (wave-private; the key words of this tile were all read above), or in a buffer of
+        // the wave's own when the key block is smaller than the operand.
+        LDS_AS uint8_t* P = a.off_pbuf < 0 ? curb : sm + a.off_pbuf + w * (RB * 1024);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             uint32_t Mv[4];
@@ -713,47 +719,52 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
         for (int q = lane; q < nvr; q += 64)
             tp[vblock + 64 * q + s_app] = (uint8_t)(((const LDS_AS uint8_t*)rec)[4 * nkw + q] ^ 0x80u);
     }
-    lds_barrier();
-    LDS_AS float* wx = (LDS_AS float*)sm;  // [NW waves][GM][PL]
-    LDS_AS float* ew = wx + NW * GM * PL;  // [NW waves][GM] weights, then [GM] maxima
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        LDS_AS float* o = wx + (w * GM + 4 * rb + g) * PL;
-        const float ls = row16_sum(lsum[rb]);
-        const float os = row16_sum(combine256(ones[rb][0], ones[rb][1], ones[rb][2]));
-        if (c == 0) {
-            o[0] = mref[rb];
-            o[1] = ls;
-            o[2] = os * (128.0f / 127.0f);
-            o[3] = 0.0f;
-        }
-#pragma unroll
-        for (int cb = 0; cb < NVB; ++cb)
-            o[kPartHead + 16 * cb + c] = combine256(acc_i[rb][cb][0], acc_i[rb][cb][1], acc_i[rb][cb][2]) * (1.0f / 127.0f);
-    }
-    lds_barrier();
-    if (tid < GM) {
-        float M = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wx[(ww * GM + tid) * PL]);
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-            const float m = wx[(ww * GM + tid) * PL];
-            ew[ww * GM + tid] = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-        }
-        ew[NW * GM + tid] = M;
-    }
-    lds_barrier();
+    // (in passes of at most two row blocks - 8 query heads - to bound the LDS it takes)
     float* pout = part + (zh * a.wg_per_head + wgi) * G * PL;
-    for (int i = tid; i < G * PL; i += NW * 64) {
-        const int hh = i / PL, col = i - hh * PL;
-        float v = ew[NW * GM + hh];
-        if (col > 0) {
-            v = 0.0f;
+    LDS_AS float* wx = (LDS_AS float*)sm;   // [NW waves][GP][PL]
+    LDS_AS float* ew = wx + NW * GP * PL;   // [NW waves][GP] weights, then [GP] maxima
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) v = fmaf(ew[ww * GM + hh], wx[(ww * GM + hh) * PL + col], v);
+    for (int r0 = 0; r0 < RB; r0 += RBP) {
+        lds_barrier();  // (the previous pass's reads are done)
+#pragma unroll
+        for (int rb = r0; rb < r0 + RBP && rb < RB; ++rb) {
+            LDS_AS float* o = wx + (w * GP + 4 * (rb - r0) + g) * PL;
+            const float ls = row16_sum(lsum[rb]);
+            const float os = row16_sum(combine256(ones[rb][0], ones[rb][1], ones[rb][2]));
+            if (c == 0) {
+                o[0] = mref[rb];
+                o[1] = ls;
+                o[2] = os * (128.0f / 127.0f);
+                o[3] = 0.0f;
+            }
+#pragma unroll
+            for (int cb = 0; cb < NVB; ++cb)
+                o[kPartHead + 16 * cb + c] = combine256(acc_i[rb][cb][0], acc_i[rb][cb][1], acc_i[rb][cb][2]) * (1.0f / 127.0f);
         }
-        pout[i] = v;
+        lds_barrier();
+        if (tid < GP) {
+            float M = -INFINITY;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wx[(ww * GP + tid) * PL]);
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                const float m = wx[(ww * GP + tid) * PL];
+                ew[ww * GP + tid] = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+            }
+            ew[NW * GP + tid] = M;
+        }
+        lds_barrier();
+        const int h0 = 4 * r0, nh = min(GP, G - h0);  // this pass's query heads
+        for (int i = tid; i < nh * PL; i += NW * 64) {
+            const int hl = i / PL, col = i - hl * PL;
+            float v = ew[NW * GP + hl];
+            if (col > 0) {
+                v = 0.0f;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) v = fmaf(ew[ww * GP + hl], wx[(ww * GP + hl) * PL + col], v);
+            }
+            pout[h0 * PL + i] = v;
+        }
     }
 }
 
@@ -943,20 +954,22 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     // the probability operand (RB KiB) overwrites the tile's key block (8 B_K bytes)
     int bk_min = 1 << 30;
     for (int h = 0; h < cb->n_kv; ++h) bk_min = std::min(bk_min, cb->blob[(size_t)layer * cb->n_kv + h].BK);
-    if (RB * 1024 > 8 * bk_min)
-        return set_error(AATC_ERR_UNSUPPORTED, "%d key bits per token are too few for %d query heads", bk_min, G);
+    const bool own_p = RB * 1024 > 8 * bk_min;  // the probability operand does not fit the key block
     // one workgroup of NW waves per CU; the epilogue reuses the ring
     const int NW = wg_waves(p.v.rb, p.v.nqm, p.v.nvb);
     p.nw = NW;
-    const size_t epi = ((size_t)NW * 4 * RB * (kPartHead + 16 * p.v.nvb) + (size_t)(NW + 1) * 4 * RB) * sizeof(float);
+    const int GP = 4 * epilogue_row_blocks(RB);
+    const size_t epi = ((size_t)NW * GP * (kPartHead + 16 * p.v.nvb) + (size_t)(NW + 1) * GP) * sizeof(float);
     const size_t scr = al16((size_t)scratch_bytes(RB, p.v.nqm, p.v.nvb, d));
     const size_t ksch = (size_t)p.v.nqm * 4 * 8 * 4;
     const size_t group = (size_t)NW * a.buf_bytes;  // one ring slot of every wave
     // ring depth: the deepest that the CU's LDS leaves room for beside the prologue's
-    // scratch, between 2 and 4 buffers per wave
-    const size_t budget = (size_t)(160 * 1024) - ksch - 256;
+    // scratch, between 2 and 4 buffers per wave (1 when two do not fit: the waves then
+    // overlap each other's streams rather than their own)
+    const size_t budget = (size_t)(160 * 1024) - ksch - 256 - kMaxRecord - 32 - (own_p ? (size_t)NW * RB * 1024 : 0);
     a.nbw = 2;
     while (a.nbw < 4 && (a.nbw + 1) * group + scr <= budget) ++a.nbw;
+    if (2 * group > budget) a.nbw = 1;  // large tiles: one buffer per wave
     const size_t ring = a.nbw * group;
     size_t top;
     if (ring + scr <= budget) {  // the scratch beside the ring: every slot streams from the start
@@ -972,6 +985,11 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     a.off_ksched = (int)al16(std::max(top, epi));
     a.off_rec = (int)al16(a.off_ksched + ksch);  // the appended token's records (outside ring and scratch)
     p.lds = a.off_rec + kMaxRecord;
+    a.off_pbuf = -1;
+    if (own_p) {
+        a.off_pbuf = (int)al16(p.lds);
+        p.lds = a.off_pbuf + (size_t)NW * RB * 1024;
+    }
     p.wgs_per_cu = 1;
     if (p.lds > 160 * 1024 - 256)
         return set_error(AATC_ERR_UNSUPPORTED, "decode needs %zu bytes of LDS per workgroup", p.lds);

@@ -112,6 +112,10 @@ WORKLOADS: Dict[str, Workload] = {
     "llama_batch": Workload("llama_batch", 4, 128, 8, 32, 32, 32, 8192, 2.75, 8192, 256, "bf16"),
     # Llama geometry, one layer, 64k cached tokens, append loop at 2.0 bits/element
     "llama_loop": Workload("llama_loop", 5, 128, 8, 32, 1, 1, 65536, 2.0, 8192, 256, "bf16"),
+    # limits of the decode path (the Llama recipe, own seeds): the largest query group
+    # (16 heads per kv-head) at d = 64 and 3.0 bits/element, and at d = 128 and 6.0
+    "edge_g16": Workload("edge_g16", 6, 64, 2, 32, 1, 1, 1024, 3.0, 2048, 64, "bf16"),
+    "edge_rate": Workload("edge_rate", 7, 128, 1, 16, 1, 1, 1024, 6.0, 4096, 32, "bf16"),
 }
 
 

@@ -221,3 +221,33 @@ def test_fused_append_decode_loop(lib, torch, wname, n_seqs, l0, steps):
         _log(f"  step {st}: lengths {[p + 1 for p in pos]}, rel err {err:.3e}")
         assert np.all(np.isfinite(got))
         assert err <= ATTN_BAR
+
+
+@pytest.mark.parametrize("wname,ctx,lens", [("edge_g16", 700, [700, 65]), ("edge_rate", 300, [300])])
+def test_decode_and_encode_at_the_limits(lib, torch, wname, ctx, lens):
+    """16 query heads per kv-head (the probability operands in buffers of their own when the
+    key block is smaller, d = 64 at 3.0 b/e) and a high rate (d = 128 at 6.0 b/e: the widest
+    score and value schedules): decode within the bar of the oracle on the same bytes,
+    end-to-end codes within the flip bar."""
+    case = Case(wname, ctx, n_seqs=len(lens), n_calib_q=32, lens=lens)
+    _log(f"{wname}: G={case.group}, d={case.d}, lengths {lens}")
+    cache_host, _ = case.oracle_cache()
+    got = _decode(lib, torch, case, cache_host, lens, ctx)
+    err = normwise_rel_err(got, case.oracle_decode(cache_host, lens))
+    _log(f"  decode rel err {err:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= ATTN_BAR
+    cb, blob = _device_codebook(lib, torch, case)
+    ct, cache = _new_cache(lib, torch, cb, 1, ctx)
+    K = torch.from_numpy(case.k_bits[:1].view(np.int16)).cuda()
+    V = torch.from_numpy(case.v_bits[:1].view(np.int16)).cuda()
+    lib.encode(cb, blob, cache, 0, [0], [0], ctx, K, V)
+    torch.cuda.synchronize()
+    got_b = ct.cpu().numpy().reshape(case.n_kv, -1)
+    flips = total = worst = 0
+    for h in range(case.n_kv):
+        f, t, wst = _flips(got_b[h], case, h, ctx, case.kf(0, h), case.vf(0, h))
+        flips, total, worst = flips + f, total + t, max(worst, wst)
+    _log(f"  codes: {flips} flips of {total}")
+    assert worst <= 1
+    assert flips <= FLIP_BAR * total
