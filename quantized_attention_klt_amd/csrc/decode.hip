@@ -904,7 +904,7 @@ struct Variant {
 // compile-time (row blocks, score operand blocks, value column blocks) bounds available;
 // (the operand blocks of a head must fit the bounds; unused blocks multiply zero)
 constexpr Variant kVariants[] = {{1, 2, 4},  {1, 2, 8},  {1, 3, 8},  {1, 3, 10}, {1, 4, 12}, {1, 6, 16},
-                                 {1, 8, 24}, {1, 16, 24}, {2, 2, 8},  {2, 3, 10}, {2, 4, 12}, {2, 8, 24},
+                                 {1, 8, 24}, {1, 16, 24}, {2, 2, 8},  {2, 3, 8},  {2, 3, 10}, {2, 4, 12}, {2, 8, 24},
                                  {2, 16, 24}, {3, 4, 12}, {3, 16, 24}, {4, 4, 12}, {4, 16, 24}};
 
 struct Plan {
@@ -1153,6 +1153,7 @@ static int decode_impl(const aatc_codebook* cb, const void* d_blob, const aatc_c
     AATC_DECODE_CASE(1, 8, 24)
     AATC_DECODE_CASE(1, 16, 24)
     AATC_DECODE_CASE(2, 2, 8)
+    AATC_DECODE_CASE(2, 3, 8)
     AATC_DECODE_CASE(2, 3, 10)
     AATC_DECODE_CASE(2, 4, 12)
     AATC_DECODE_CASE(2, 8, 24)
