@@ -82,13 +82,29 @@ typedef struct {
  * non-orthogonal transform T_K = M_Q^{1/2} R, R the eigenvectors of
  * M_Q^{1/2} Sigma_K M_Q^{1/2}, under which the attention-aware key distortion is the MSE of
  * the coefficients ("Spend Bits Where Queries Look", abstract; M_Q gets a ridge of 1e-6 of
- * its mean eigenvalue).  Values always use the KLT. */
+ * its mean eigenvalue).  Values always use the KLT.
+ * key_quantizer: 0 = scalar (per-channel widths from the water-filling), 1 = vector
+ * quantization ("Spend Bits Where Queries Look", abstract): the d*avg_bits key bits of a
+ * token become d*avg_bits/8 one-byte indices, one per group of 4 coefficients, into a
+ * 256-word codebook per group.  Needs joint = 0, avg_bits <= 2 and d*avg_bits a multiple
+ * of 32.  The 4 n_g coefficients of largest weight x_j are coded (the rest reconstruct to
+ * the mean), grouped greedily toward equal volume prod x_j (largest weight first, into the
+ * unfilled group of smallest sum of log(x_j / x_min)); each codebook is vq_iters (0 = 20)
+ * rounds of Lloyd's algorithm (initial words: the first 256 points) on the points
+ * vq_normals[n] * sqrt(x_j), n < vq_n_train, in the weighted domain u_j = sqrt(w_j) c_j
+ * (w_j = x_j / lambda_j), where the attention-aware key distortion is plain MSE.
+ * vq_normals: vq_n_train >= 256 rows of 4 standard normal draws (host, caller-owned),
+ * ignored for scalar keys. */
 typedef struct {
     double avg_bits;
     int32_t max_bits;
     int32_t joint;
     int32_t max_sweeps;
     int32_t key_transform;
+    int32_t key_quantizer;
+    int32_t vq_iters;
+    const double* vq_normals;
+    int64_t vq_n_train;
 } aatc_calib_params;
 
 /* Device-side cache descriptor.  data: caller-allocated device memory of
@@ -154,6 +170,27 @@ int aatc_codebook_create(int32_t d, int32_t n_layers, int32_t n_kv, int32_t grou
                          const double* U_k, const double* U_v, const double* mu_k,
                          const double* mu_v, const int32_t* bits_k, const int32_t* bits_v,
                          const float* step_k, const float* step_v, aatc_codebook** out);
+
+/* Build a codebook with vector-quantized keys from explicit arrays.  Arguments as for
+ * aatc_codebook_create, except for the keys: n_groups (a multiple of 4, 4*n_groups <= d)
+ * groups; vq_chan [n_heads][n_groups][4] int32 key channels (distinct within a head);
+ * vq_scale [n_heads][d] float32 s_j > 0 for coded channels; vq_cent
+ * [n_heads][n_groups][256][4] float32 codewords in the weighted domain u = s c.
+ * Encoding: index = argmin over words z of (t0 t0 + t1 t1) + (t2 t2 + t3 t3), t_k =
+ * fp32(c_k s_k) - z_k, every operation rounded to fp32, lowest index on ties; decoding
+ * c_j = z_k / s_j.  A token's key record is n_groups bytes (byte g = index of group g).
+ * Errors: INVALID_ARG, BUDGET. */
+int aatc_codebook_create_vq(int32_t d, int32_t n_layers, int32_t n_kv, int32_t group,
+                            const double* U_k, const double* U_v, const double* mu_k,
+                            const double* mu_v, int32_t n_groups, const int32_t* vq_chan,
+                            const float* vq_scale, const float* vq_cent, const int32_t* bits_v,
+                            const float* step_v, aatc_codebook** out);
+
+/* Vector-quantized keys of one head: *n_groups (0 for scalar keys) and, where the
+ * pointers are non-NULL and the head has them, vq_chan [n_groups*4], vq_scale [d],
+ * vq_cent [n_groups*256*4] in the layout of aatc_codebook_create_vq. */
+int aatc_codebook_vq(const aatc_codebook* cb, int32_t head, int32_t* n_groups, int32_t* vq_chan,
+                     float* vq_scale, float* vq_cent);
 
 /* Geometry of a codebook; any output pointer may be NULL.  total_bits = bits per token
  * and kv-head (keys and values); tile_bytes = 8 * total_bits. */

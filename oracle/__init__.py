@@ -18,7 +18,9 @@ function cites the passage of the AATC pages it follows:
   (taken as a description only).
 * p3 = "Spend Bits Where Queries Look" (NOVA-KV) abstract: fixed per-token
   bit count, bandwidth-bound decoding, and a non-orthogonal key transform under which
-  attention distortion becomes transform-domain MSE (nova_key_transform).
+  attention distortion becomes transform-domain MSE (nova_key_transform); vector
+  quantization of the key coefficients with equal-volume groups and equal-size
+  codebooks (oracle.vq).
 
 Readings taken where the pages are silent, garbled or contradict each other
 are stated in the docstring of the function that takes them.  Parity status:
@@ -33,7 +35,11 @@ from .calib import (  # noqa: F401
 )
 from .codec import (  # noqa: F401
     fields, quantize, transform_coeffs, pack_cache, unpack_cache, dequantize,
-    reconstruct, tile_bytes, record_bits, encode_cache,
+    reconstruct, tile_bytes, record_bits, encode_cache, key_record_bits,
+)
+from .vq import (  # noqa: F401
+    VQ_DIM, VQ_SIZE, coded_key_channels, equal_volume_groups, group_log_volumes, lloyd,
+    group_codebooks, vq_scales, vq_encode, vq_dequantize,
 )
 from .attention import (  # noqa: F401
     attention, decode_attention, predicted_distortion, monte_carlo_distortion,

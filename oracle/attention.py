@@ -7,7 +7,8 @@ import math
 
 import numpy as np
 
-from .codec import dequantize, reconstruct, unpack_cache
+from .codec import dequantize, key_record_bits, reconstruct, unpack_cache
+from .vq import vq_dequantize
 
 
 def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
@@ -27,8 +28,12 @@ def decode_attention(cache: np.ndarray, cb, q_heads: np.ndarray, n_tokens: int) 
     """Attention of the query heads of one kv-head group over the first n_tokens of a
     packed cache: unpack, dequantize, inverse transform, then plain attention (every
     cached token is attended; no mask).  q_heads [G, d] -> out [G, d] float64."""
-    cK, cV = unpack_cache(cache, cb.bK, cb.bV, n_tokens)
-    Khat = cb.muK[None, :] + dequantize(cK, cb.bK, cb.stepK) @ cb.UKinv  # c = (k - mu) T  =>  k = mu + c T^{-1}
+    cK, cV = unpack_cache(cache, key_record_bits(cb), cb.bV, n_tokens)
+    if cb.vq is not None:
+        chatK = vq_dequantize(cK, cb.vq.groups, cb.vq.scale32, cb.vq.cent32, cb.d)
+    else:
+        chatK = dequantize(cK, cb.bK, cb.stepK)
+    Khat = cb.muK[None, :] + chatK @ cb.UKinv  # c = (k - mu) T  =>  k = mu + c T^{-1}
     Vhat = reconstruct(dequantize(cV, cb.bV, cb.stepV), cb.muV, cb.UV)
     return attention(q_heads, Khat, Vhat)
 

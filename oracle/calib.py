@@ -315,6 +315,22 @@ def optimal_step(bits: int) -> float:
 # codebook of one head
 # ----------------------------------------------------------------------------------------
 @dataclass
+class VQKeys:
+    groups: np.ndarray   # int [n_groups, 4] key channels per group
+    scale32: np.ndarray  # float32 [d]: s_j = sqrt(w_j)
+    cent: np.ndarray     # float64 [n_groups, 256, 4] Lloyd codebooks (weighted domain)
+
+    @property
+    def cent32(self):
+        return self.cent.astype(np.float32)
+
+    @property
+    def record_bits(self):
+        """Pseudo-channel widths of the key record: one byte per group."""
+        return np.full(len(self.groups), 8, np.int64)
+
+
+@dataclass
 class HeadCodebook:
     d: int
     UK: np.ndarray      # float64 [d, d], columns = KLT basis (descending eigenvalues)
@@ -331,6 +347,7 @@ class HeadCodebook:
     stepV: np.ndarray
     theta: float
     UKinv: np.ndarray = None  # float64 [d, d]: key reconstruction (k_hat = mu + c_hat UKinv); U_K^T for the KLT
+    vq: "VQKeys" = None       # vector-quantized keys (bK all zero then), else None
 
     def __post_init__(self):
         if self.UKinv is None:
@@ -366,11 +383,18 @@ KEY_ALIGN = 32  # key bits per token are kept a multiple of one 32-bit word
 
 
 def build_head_codebook(stats: dict, avg_bits: float, max_bits: int = 8,
-                        joint: bool = True, key_transform: str = "klt") -> HeadCodebook:
+                        joint: bool = True, key_transform: str = "klt",
+                        key_quantizer: str = "scalar", vq_normals: np.ndarray | None = None,
+                        vq_iters: int = 20) -> HeadCodebook:
     """Calibrate one head: KLT of both covariances (or, for the keys, the attention-optimal
     transform of nova_key_transform), weights, exact-budget integer bits with total
     2 d avg_bits (a multiple of 8; key bits a multiple of 32), and fp32 steps
-    step_b * sqrt(coefficient variance)."""
+    step_b * sqrt(coefficient variance).
+
+    key_quantizer "vq" (NOVA-KV abstract; readings in oracle.vq): separate budgets of
+    d avg_bits bits for keys and values; the key bits go to d avg_bits / 8 groups of four
+    coefficients with one 256-word Lloyd codebook each (so avg_bits <= 2 and d avg_bits a
+    multiple of 32), trained on vq_normals; the values keep the scalar quantizer."""
     d = stats["d"]
     total = 2.0 * d * avg_bits
     B = int(round(total))
@@ -389,9 +413,26 @@ def build_head_codebook(stats: dict, avg_bits: float, max_bits: int = 8,
     else:
         raise ValueError(f"unknown key transform {key_transform!r}")
     theta, _ = waterfill_theta(np.concatenate([xK, xV]), B, max_bits)
-    bK, bV = allocate_bits(xK, xV, B, max_bits, joint, key_align=KEY_ALIGN)
+    vq = None
+    if key_quantizer == "vq":
+        if joint:
+            raise ValueError("vector-quantized keys take separate key and value budgets")
+        BK = B // 2
+        if BK % KEY_ALIGN or 4 * (BK // 8) > d:
+            raise ValueError("vector-quantized keys need d*avg_bits a multiple of 32 and "
+                             "avg_bits <= 2")
+        from .vq import equal_volume_groups, group_codebooks, vq_scales
+        _, bV = allocate_bits(xK, xV, B, max_bits, False, key_align=KEY_ALIGN)
+        bK = np.zeros(d, np.int64)
+        groups = equal_volume_groups(xK, BK // 8)
+        w = np.where(lamK > 0, xK / np.where(lamK > 0, lamK, 1.0), 0.0)
+        vq = VQKeys(groups, vq_scales(w), group_codebooks(xK, groups, vq_normals, vq_iters))
+    elif key_quantizer == "scalar":
+        bK, bV = allocate_bits(xK, xV, B, max_bits, joint, key_align=KEY_ALIGN)
+    else:
+        raise ValueError(f"unknown key quantizer {key_quantizer!r}")
     st = step_table(max_bits)
     stepK = np.where(bK > 0, st[bK] * np.sqrt(lamK), 0.0).astype(np.float32)
     stepV = np.where(bV > 0, st[bV] * np.sqrt(lamV), 0.0).astype(np.float32)
     return HeadCodebook(d, UK, UV, lamK, lamV, stats["muK"].copy(), stats["muV"].copy(),
-                        xK, xV, bK, bV, stepK, stepV, theta, UKinv)
+                        xK, xV, bK, bV, stepK, stepV, theta, UKinv, vq)

@@ -169,11 +169,22 @@ def unpack_cache(cache: np.ndarray, bK: np.ndarray, bV: np.ndarray, n: int):
     return out[0], out[1]
 
 
+def key_record_bits(cb) -> np.ndarray:
+    """Field widths of the key record: the channel bits, or one 8-bit pseudo-channel per
+    group for vector-quantized keys (byte g = index of group g)."""
+    return cb.vq.record_bits if cb.vq is not None else cb.bK
+
+
 def encode_cache(K: np.ndarray, V: np.ndarray, cb, n_tiles: int | None = None):
     """Whole encoder for one (layer, seq, head): transform, quantize, pack.
-    Returns (cache bytes, codesK, codesV)."""
+    Returns (cache bytes, codesK, codesV); codesK holds the group indices [n, n_groups]
+    for vector-quantized keys."""
     cKf = transform_coeffs(K, cb.muK, cb.UK)
     cVf = transform_coeffs(V, cb.muV, cb.UV)
-    codesK = quantize(cKf, cb.inv_step("K"), cb.bK)
+    if cb.vq is not None:
+        from .vq import vq_encode
+        codesK = vq_encode(cKf, cb.vq.groups, cb.vq.scale32, cb.vq.cent32)
+    else:
+        codesK = quantize(cKf, cb.inv_step("K"), cb.bK)
     codesV = quantize(cVf, cb.inv_step("V"), cb.bV)
-    return pack_cache(codesK, codesV, cb.bK, cb.bV, n_tiles), codesK, codesV
+    return pack_cache(codesK, codesV, key_record_bits(cb), cb.bV, n_tiles), codesK, codesV

@@ -37,7 +37,8 @@ class HeadStats(C.Structure):
 
 class CalibParams(C.Structure):
     _fields_ = [("avg_bits", C.c_double), ("max_bits", C.c_int32), ("joint", C.c_int32),
-                ("max_sweeps", C.c_int32), ("key_transform", C.c_int32)]
+                ("max_sweeps", C.c_int32), ("key_transform", C.c_int32), ("key_quantizer", C.c_int32),
+                ("vq_iters", C.c_int32), ("vq_normals", C.c_void_p), ("vq_n_train", C.c_int64)]
 
 
 class Cache(C.Structure):
@@ -47,7 +48,8 @@ class Cache(C.Structure):
 
 EXPORTS = [
     "aatc_version", "aatc_layout_version", "aatc_status_string", "aatc_last_error",
-    "aatc_stats_from_samples", "aatc_calibrate", "aatc_codebook_create", "aatc_codebook_info",
+    "aatc_stats_from_samples", "aatc_calibrate", "aatc_codebook_create", "aatc_codebook_create_vq",
+    "aatc_codebook_vq", "aatc_codebook_info",
     "aatc_codebook_head", "aatc_codebook_fields", "aatc_codebook_save", "aatc_codebook_load", "aatc_codebook_free",
     "aatc_codebook_device_bytes", "aatc_codebook_upload", "aatc_cache_bytes", "aatc_encode",
     "aatc_encode_coeffs", "aatc_decode_workspace_bytes", "aatc_decode_attention",
@@ -81,6 +83,8 @@ def load() -> C.CDLL:
         "aatc_calibrate": ([i32, i32, i32, i32, C.POINTER(HeadStats), C.POINTER(CalibParams),
                             C.POINTER(P)], C.c_int),
         "aatc_codebook_create": ([i32, i32, i32, i32, P, P, P, P, P, P, P, P, C.POINTER(P)], C.c_int),
+        "aatc_codebook_create_vq": ([i32, i32, i32, i32, P, P, P, P, i32, P, P, P, P, P, C.POINTER(P)], C.c_int),
+        "aatc_codebook_vq": ([P, i32, P, P, P, P], C.c_int),
         "aatc_codebook_info": ([P, P, P, P, P, P, P], C.c_int),
         "aatc_codebook_head": ([P, i32] + [P] * 13, C.c_int),
         "aatc_codebook_fields": ([P, i32, i32, P, P], C.c_int),
@@ -204,6 +208,19 @@ class Codebook:
         r["theta"] = float(th[0])
         return r
 
+    def vq(self, h: int):
+        """Vector-quantized keys of head h: None for scalar keys, else dict(groups [n_g, 4],
+        scale32 [d], cent32 [n_g, 256, 4])."""
+        n = C.c_int32()
+        _check(load().aatc_codebook_vq(self.handle, h, C.byref(n), None, None, None))
+        if n.value == 0:
+            return None
+        ch = np.zeros((n.value, 4), np.int32)
+        sc = np.zeros(self.d, np.float32)
+        ce = np.zeros((n.value, 256, 4), np.float32)
+        _check(load().aatc_codebook_vq(self.handle, h, C.byref(n), _ptr(ch), _ptr(sc), _ptr(ce)))
+        return dict(groups=ch.astype(np.int64), scale32=sc, cent32=ce)
+
     def fields(self, h: int, which: int) -> list:
         """Record fields of head h (which: 0 keys, 1 values) as (chan, width, shift, byte, pos)."""
         n = C.c_int32(0)
@@ -236,12 +253,18 @@ class Codebook:
 
 
 def calibrate(stats: Sequence[dict], d: int, n_layers: int, n_kv: int, group: int, avg_bits: float,
-              max_bits: int = 8, joint: bool = True, max_sweeps: int = 0, key_transform: str = "klt") -> Codebook:
+              max_bits: int = 8, joint: bool = True, max_sweeps: int = 0, key_transform: str = "klt",
+              key_quantizer: str = "scalar", vq_normals=None, vq_iters: int = 0) -> Codebook:
     """aatc_calibrate over per-head statistics dicts (muK, muV, SigK, SigV, MQ, gammaV);
-    key_transform "klt" (orthogonal) or "nova" (attention-optimal, non-orthogonal)."""
+    key_transform "klt" (orthogonal) or "nova" (attention-optimal, non-orthogonal);
+    key_quantizer "scalar" or "vq" (vq_normals: [n, 4] standard normal training draws)."""
     kt = {"klt": 0, "nova": 1}.get(key_transform)
     if kt is None:
         raise ValueError(f"unknown key transform {key_transform!r}")
+    kq = {"scalar": 0, "vq": 1}.get(key_quantizer)
+    if kq is None:
+        raise ValueError(f"unknown key quantizer {key_quantizer!r}")
+    normals = None if vq_normals is None else np.ascontiguousarray(vq_normals, np.float64).reshape(-1, 4)
     keep = []
     arr = (HeadStats * len(stats))()
     for i, s in enumerate(stats):
@@ -249,7 +272,8 @@ def calibrate(stats: Sequence[dict], d: int, n_layers: int, n_kv: int, group: in
         keep.append(a)
         pd = C.POINTER(C.c_double)
         arr[i] = HeadStats(*(x.ctypes.data_as(pd) for x in a), float(s["gammaV"]))
-    p = CalibParams(avg_bits, max_bits, 1 if joint else 0, max_sweeps, kt)
+    p = CalibParams(avg_bits, max_bits, 1 if joint else 0, max_sweeps, kt, kq, vq_iters,
+                    None if normals is None else normals.ctypes.data, 0 if normals is None else normals.shape[0])
     out = C.c_void_p()
     _check(load().aatc_calibrate(d, n_layers, n_kv, group, arr, C.byref(p), C.byref(out)))
     return Codebook(out.value)
@@ -264,6 +288,22 @@ def codebook_create(d: int, n_layers: int, n_kv: int, group: int, UK, UV, muK, m
     out = C.c_void_p()
     _check(load().aatc_codebook_create(d, n_layers, n_kv, group, *(_ptr(x) for x in a), *(_ptr(x) for x in b),
                                        *(_ptr(x) for x in s), C.byref(out)))
+    return Codebook(out.value)
+
+
+def codebook_create_vq(d: int, n_layers: int, n_kv: int, group: int, UK, UV, muK, muV, vq_chan,
+                       vq_scale, vq_cent, bV, stepV) -> Codebook:
+    """aatc_codebook_create_vq from per-head arrays stacked along the first axis:
+    vq_chan [heads, n_groups, 4], vq_scale [heads, d], vq_cent [heads, n_groups, 256, 4]."""
+    a = [np.ascontiguousarray(x, np.float64) for x in (UK, UV, muK, muV)]
+    ch = np.ascontiguousarray(vq_chan, np.int32)
+    sc = np.ascontiguousarray(vq_scale, np.float32)
+    ce = np.ascontiguousarray(vq_cent, np.float32)
+    bv = np.ascontiguousarray(bV, np.int32)
+    sv = np.ascontiguousarray(stepV, np.float32)
+    out = C.c_void_p()
+    _check(load().aatc_codebook_create_vq(d, n_layers, n_kv, group, *(_ptr(x) for x in a), ch.shape[-2],
+                                          _ptr(ch), _ptr(sc), _ptr(ce), _ptr(bv), _ptr(sv), C.byref(out)))
     return Codebook(out.value)
 
 

@@ -17,6 +17,9 @@ constexpr int kMaxQM = 16;       // score MFMAs per token group (<= 32 words x 8
 constexpr int kMaxVB = 24;       // value column blocks of 16 fields per head
 constexpr int kKeyAlign = 32;    // key bits per token are a multiple of one 32-bit word
 constexpr int kMaxRecordBytes = kMaxD;  // bytes of one record (at most 8 bits per channel)
+constexpr int kVqDim = 4;        // key coefficients per vector-quantized group
+constexpr int kVqSize = 256;     // codewords per group (one index byte)
+constexpr int kMaxVqGroups = kMaxD / kVqDim;
 
 // One byte-aligned field of a token record: code bits [shift, shift + width) of channel
 // chan at bits [pos, pos + width) of record byte `byte` (never crossing a byte).
@@ -36,6 +39,11 @@ struct HeadCB {
     std::vector<int32_t> bK, bV;
     std::vector<float> stepK, stepV;
     double theta = 0.0;
+    // vector-quantized keys (vq_groups > 0; bK all zero then): channels [g*4 + k],
+    // weighted-domain scales s_j [d], codewords [g][256][4]
+    int vq_groups = 0;
+    std::vector<int32_t> vq_chan;
+    std::vector<float> vq_scale, vq_cent;
     // derived: record fields sorted by (byte, pos)
     std::vector<Field> fK, fV;
     int BK = 0, BV = 0;
@@ -45,7 +53,8 @@ struct HeadCB {
 // actual d (e.g. UK[i*d + j]).
 struct alignas(256) DevHead {
     int32_t d, BK, BV, nfK, nfV;
-    int32_t pad0[59];
+    int32_t vq_groups;  // > 0: vector-quantized keys (the vq_* arrays below)
+    int32_t pad0[58];
     float UK[kMaxD * kMaxD];      // fp32 basis (query transform)
     float UV[kMaxD * kMaxD];      // fp32 basis (inverse transform of values)
     float UVt[kMaxD * kMaxD];     // its transpose, UVt[j*d + i] = UV[i*d + j]
@@ -101,6 +110,14 @@ struct alignas(256) DevHead {
     // Value channel j: the columns of its fields (at most 8: a field has at least one bit),
     // each col | (shift - pos + 8) << 9 | flip << 13, unused entries 0xFFFF.
     uint16_t vch[kMaxD][8];
+    // ---- vector-quantized keys ---------------------------------------------------------
+    // group g codes channels vq_chan[g][0..3]; its index is key-record byte g; coefficient
+    // u = fp32(c * vq_scale[j]) is matched against vq_cent[g][i][0..3]; the reconstructed
+    // coefficient is codeword * vq_rscale[j] (fp32 of 1 / scale).
+    uint8_t vq_chan[kMaxVqGroups][kVqDim];
+    float vq_scale[kMaxD];
+    float vq_rscale[kMaxD];
+    float vq_cent[kMaxVqGroups][kVqSize][kVqDim];
 };
 
 }  // namespace aatc

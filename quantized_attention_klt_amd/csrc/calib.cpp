@@ -473,6 +473,71 @@ static bool invert(int d, const std::vector<double>& A, std::vector<double>& inv
     return true;
 }
 
+// ------------------------------------------------------------------------------------
+// Vector-quantized keys ("Spend Bits Where Queries Look", abstract: equal-volume groups,
+// equal-size codebooks).  Groups of kVqDim coefficients: the kVqDim * n_g of largest
+// weight (ties: lower channel), formed greedily toward equal volume prod x_j - largest
+// weight first, each into the unfilled group with the smallest sum of log(x_j / x_min)
+// (ties: lower group).  Output: channels of group g at chan[g * kVqDim ..], ascending.
+// ------------------------------------------------------------------------------------
+static bool vq_groups(const std::vector<double>& x, int n_g, std::vector<int32_t>& chan) {
+    const int d = (int)x.size(), n = kVqDim * n_g;
+    std::vector<int> order(d);
+    for (int j = 0; j < d; ++j) order[j] = j;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return x[a] > x[b]; });
+    order.resize(n);  // coded channels, by decreasing weight (ties: lower index)
+    double xmin = x[order[n - 1]];
+    if (!(xmin > 0)) return false;
+    std::vector<double> load(n_g, 0.0);
+    std::vector<std::vector<int32_t>> mem(n_g);
+    for (int j : order) {
+        int best = -1;
+        for (int g = 0; g < n_g; ++g)
+            if ((int)mem[g].size() < kVqDim && (best < 0 || load[g] < load[best])) best = g;
+        mem[best].push_back(j);
+        load[best] += std::log(x[j] / xmin);
+    }
+    chan.clear();
+    for (auto& m : mem) {
+        std::sort(m.begin(), m.end());
+        chan.insert(chan.end(), m.begin(), m.end());
+    }
+    return true;
+}
+
+// Lloyd's algorithm in fp64 on points y [n][kVqDim]: iters rounds of nearest-word
+// assignment (squared distance summed in coordinate order, lowest index on ties) and
+// cell means (an empty cell keeps its word); initial words: the first kVqSize points.
+static void lloyd(const std::vector<double>& y, int64_t n, int iters, std::vector<double>& code) {
+    code.assign(y.begin(), y.begin() + (size_t)kVqSize * kVqDim);
+    std::vector<int32_t> a(n);
+    std::vector<double> sum((size_t)kVqSize * kVqDim);
+    std::vector<int64_t> cnt(kVqSize);
+    for (int it = 0; it < iters; ++it) {
+        for (int64_t i = 0; i < n; ++i) {
+            const double* p = &y[(size_t)i * kVqDim];
+            double best = 0.0;
+            int bi = 0;
+            for (int c = 0; c < kVqSize; ++c) {
+                const double* z = &code[(size_t)c * kVqDim];
+                double e = 0.0;
+                for (int k = 0; k < kVqDim; ++k) e += (p[k] - z[k]) * (p[k] - z[k]);
+                if (c == 0 || e < best) best = e, bi = c;
+            }
+            a[i] = bi;
+        }
+        std::fill(sum.begin(), sum.end(), 0.0);
+        std::fill(cnt.begin(), cnt.end(), 0);
+        for (int64_t i = 0; i < n; ++i) {
+            ++cnt[a[i]];
+            for (int k = 0; k < kVqDim; ++k) sum[(size_t)a[i] * kVqDim + k] += y[(size_t)i * kVqDim + k];
+        }
+        for (int c = 0; c < kVqSize; ++c)
+            if (cnt[c])
+                for (int k = 0; k < kVqDim; ++k) code[(size_t)c * kVqDim + k] = sum[(size_t)c * kVqDim + k] / (double)cnt[c];
+    }
+}
+
 int finalize(aatc_codebook* cb) {
     const int d = cb->d;
     int total = -1;
@@ -485,7 +550,26 @@ int finalize(aatc_codebook* cb) {
                 (H.bV[j] > 0 && !(H.stepV[j] > 0 && std::isfinite(H.stepV[j]))))
                 return set_error(AATC_ERR_STATS, "head %zu channel %d: coded channel needs a positive step", h, j);
         }
-        if (!make_fields(H.bK, H.fK, H.BK) || !make_fields(H.bV, H.fV, H.BV))
+        if (H.vq_groups) {
+            const int n_g = H.vq_groups;
+            if (n_g % 4 || kVqDim * n_g > d || (int)H.vq_chan.size() != kVqDim * n_g ||
+                (int)H.vq_scale.size() != d || H.vq_cent.size() != (size_t)n_g * kVqSize * kVqDim)
+                return set_error(AATC_ERR_BUDGET, "head %zu: vector-quantized keys need a multiple of 4 groups "
+                                 "of 4 channels (at most d / 4 groups)", h);
+            std::vector<int> seen(d, 0);
+            for (int32_t j : H.vq_chan) {
+                if (j < 0 || j >= d || seen[j]++)
+                    return set_error(AATC_ERR_INVALID_ARG, "head %zu: group channels must be distinct and in [0, d)", h);
+                if (!(H.vq_scale[j] > 0 && std::isfinite(H.vq_scale[j])))
+                    return set_error(AATC_ERR_INVALID_ARG, "head %zu channel %d: coded channel needs a positive scale", h, j);
+            }
+            for (float z : H.vq_cent)
+                if (!std::isfinite(z)) return set_error(AATC_ERR_INVALID_ARG, "head %zu: non-finite codeword", h);
+            for (int j = 0; j < d; ++j)
+                if (H.bK[j]) return set_error(AATC_ERR_INVALID_ARG, "head %zu: scalar key bits with vector-quantized keys", h);
+        }
+        const std::vector<int32_t> keybits = H.vq_groups ? std::vector<int32_t>(H.vq_groups, 8) : H.bK;
+        if (!make_fields(keybits, H.fK, H.BK) || !make_fields(H.bV, H.fV, H.BV))
             return set_error(AATC_ERR_BUDGET, "head %zu: key and value bits per token must be whole bytes", h);
         if ((int)H.fK.size() > kMaxFields || (int)H.fV.size() > kMaxFields)
             return set_error(AATC_ERR_UNSUPPORTED, "head %zu: more than %d fields in a record", h, kMaxFields);
@@ -576,6 +660,16 @@ int finalize(aatc_codebook* cb) {
         }
         int rc = build_decode_schedule(H, D);
         if (rc != AATC_OK) return set_error(rc, "head %zu: %s", h, "decode schedule exceeds kernel limits");
+        D.vq_groups = H.vq_groups;
+        for (int g = 0; g < H.vq_groups; ++g)
+            for (int k = 0; k < kVqDim; ++k) {
+                const int j = H.vq_chan[g * kVqDim + k];
+                D.vq_chan[g][k] = (uint8_t)j;
+                D.vq_scale[j] = H.vq_scale[j];
+                D.vq_rscale[j] = (float)(1.0 / (double)H.vq_scale[j]);
+                for (int i = 0; i < kVqSize; ++i)
+                    D.vq_cent[g][i][k] = H.vq_cent[((size_t)g * kVqSize + i) * kVqDim + k];
+            }
     }
     return AATC_OK;
 }
@@ -797,6 +891,21 @@ extern "C" int aatc_calibrate(int32_t d, int32_t n_layers, int32_t n_kv, int32_t
     const int sweeps = p->max_sweeps > 0 ? p->max_sweeps : 60;
     if (p->key_transform != 0 && p->key_transform != 1)
         return set_error(AATC_ERR_INVALID_ARG, "key_transform must be 0 (KLT) or 1 (attention-optimal)");
+    if (p->key_quantizer != 0 && p->key_quantizer != 1)
+        return set_error(AATC_ERR_INVALID_ARG, "key_quantizer must be 0 (scalar) or 1 (vector)");
+    const int vq_n_g = p->key_quantizer ? total / 2 / 8 : 0;
+    if (p->key_quantizer) {
+        if (p->joint) return set_error(AATC_ERR_BUDGET, "vector-quantized keys take separate budgets (joint = 0)");
+        if (kVqDim * vq_n_g > d)
+            return set_error(AATC_ERR_BUDGET, "vector-quantized keys code at most 2 bits per element (avg_bits %g)",
+                             p->avg_bits);
+        if (!p->vq_normals || p->vq_n_train < kVqSize)
+            return set_error(AATC_ERR_INVALID_ARG, "vector-quantized keys need at least %d training draws", kVqSize);
+        if (!finite_all(p->vq_normals, (size_t)p->vq_n_train * kVqDim))
+            return set_error(AATC_ERR_INVALID_ARG, "non-finite training draw");
+        if (p->vq_iters < 0) return set_error(AATC_ERR_INVALID_ARG, "vq_iters must be >= 0");
+    }
+    const int vq_iters = p->vq_iters > 0 ? p->vq_iters : 20;
     const int n_heads = n_layers * n_kv;
 
     auto* cb = new aatc_codebook();
@@ -863,7 +972,30 @@ extern "C" int aatc_calibrate(int32_t d, int32_t n_layers, int32_t n_kv, int32_t
         std::vector<double> xall(H.xK);
         xall.insert(xall.end(), H.xV.begin(), H.xV.end());
         H.theta = waterfill_theta(xall, total, max_bits);
-        if (cb->joint) {
+        if (vq_n_g) {
+            H.bK.assign(d, 0);
+            H.bV = greedy_bits(H.xV, total / 2, max_bits);
+            if (!vq_groups(H.xK, vq_n_g, H.vq_chan)) {
+                status[h] = AATC_ERR_STATS;
+                msg[h] = "a coded key coefficient has zero weight";
+                return;
+            }
+            H.vq_groups = vq_n_g;
+            H.vq_scale.assign(d, 0.0f);
+            for (int j = 0; j < d; ++j)
+                if (H.lamK[j] > 0) H.vq_scale[j] = (float)std::sqrt(std::max(0.0, H.xK[j] / H.lamK[j]));
+            H.vq_cent.assign((size_t)vq_n_g * kVqSize * kVqDim, 0.0f);
+            const int64_t n = p->vq_n_train;
+            std::vector<double> y((size_t)n * kVqDim), code;
+            for (int g = 0; g < vq_n_g; ++g) {
+                for (int64_t i = 0; i < n; ++i)
+                    for (int k = 0; k < kVqDim; ++k)
+                        y[(size_t)i * kVqDim + k] =
+                            p->vq_normals[(size_t)i * kVqDim + k] * std::sqrt(H.xK[H.vq_chan[g * kVqDim + k]]);
+                lloyd(y, n, vq_iters, code);
+                for (size_t i = 0; i < code.size(); ++i) H.vq_cent[(size_t)g * kVqSize * kVqDim + i] = (float)code[i];
+            }
+        } else if (cb->joint) {
             allocate_joint(H.xK, H.xV, total, max_bits, kKeyAlign, H.bK, H.bV);
         } else {
             H.bK = greedy_bits(H.xK, total / 2, max_bits);
@@ -935,6 +1067,81 @@ extern "C" int aatc_codebook_create(int32_t d, int32_t n_layers, int32_t n_kv, i
     return AATC_OK;
 }
 
+template <class T, class S>
+static void copy_out(T* dst, const std::vector<S>& src) {
+    if (dst)
+        for (size_t i = 0; i < src.size(); ++i) dst[i] = (T)src[i];
+}
+
+extern "C" int aatc_codebook_create_vq(int32_t d, int32_t n_layers, int32_t n_kv, int32_t group,
+                                       const double* U_k, const double* U_v, const double* mu_k,
+                                       const double* mu_v, int32_t n_groups, const int32_t* vq_chan,
+                                       const float* vq_scale, const float* vq_cent, const int32_t* bits_v,
+                                       const float* step_v, aatc_codebook** out) {
+    if (!out) return set_error(AATC_ERR_INVALID_ARG, "null pointer");
+    *out = nullptr;
+    if (d != 64 && d != 128) return set_error(AATC_ERR_INVALID_ARG, "d must be 64 or 128 (got %d)", d);
+    if (n_layers < 1 || n_kv < 1 || group < 1 || group > 16)
+        return set_error(AATC_ERR_INVALID_ARG, "need n_layers >= 1, n_kv >= 1, 1 <= group <= 16");
+    if (!U_k || !U_v || !mu_k || !mu_v || !vq_chan || !vq_scale || !vq_cent || !bits_v || !step_v)
+        return set_error(AATC_ERR_INVALID_ARG, "null pointer");
+    if (n_groups < 4 || n_groups % 4 || kVqDim * n_groups > d)
+        return set_error(AATC_ERR_BUDGET, "n_groups must be a positive multiple of 4 with 4*n_groups <= d");
+    const int n_heads = n_layers * n_kv;
+    auto* cb = new aatc_codebook();
+    cb->d = d;
+    cb->n_layers = n_layers;
+    cb->n_kv = n_kv;
+    cb->group = group;
+    cb->joint = 0;
+    cb->heads.resize(n_heads);
+    const size_t dd = (size_t)d * d, nc = (size_t)n_groups * kVqSize * kVqDim;
+    for (int h = 0; h < n_heads; ++h) {
+        HeadCB& H = cb->heads[h];
+        H.UK.assign(U_k + h * dd, U_k + (h + 1) * dd);
+        H.UV.assign(U_v + h * dd, U_v + (h + 1) * dd);
+        H.muK.assign(mu_k + (size_t)h * d, mu_k + (size_t)(h + 1) * d);
+        H.muV.assign(mu_v + (size_t)h * d, mu_v + (size_t)(h + 1) * d);
+        H.bK.assign(d, 0);
+        H.stepK.assign(d, 0.0f);
+        H.bV.assign(bits_v + (size_t)h * d, bits_v + (size_t)(h + 1) * d);
+        H.stepV.assign(step_v + (size_t)h * d, step_v + (size_t)(h + 1) * d);
+        H.vq_groups = n_groups;
+        H.vq_chan.assign(vq_chan + (size_t)h * kVqDim * n_groups, vq_chan + (size_t)(h + 1) * kVqDim * n_groups);
+        H.vq_scale.assign(d, 0.0f);
+        for (int32_t j : H.vq_chan)
+            if (j >= 0 && j < d) H.vq_scale[j] = vq_scale[(size_t)h * d + j];
+        H.vq_cent.assign(vq_cent + h * nc, vq_cent + (h + 1) * nc);
+        if (!finite_all(H.UK.data(), dd) || !finite_all(H.UV.data(), dd) || !finite_all(H.muK.data(), d) ||
+            !finite_all(H.muV.data(), d)) {
+            delete cb;
+            return set_error(AATC_ERR_INVALID_ARG, "head %d: non-finite basis or mean", h);
+        }
+    }
+    int rc = finalize(cb);
+    if (rc != AATC_OK) {
+        delete cb;
+        return rc;
+    }
+    cb->avg_bits = cb->total_bits / (2.0 * d);
+    *out = cb;
+    return AATC_OK;
+}
+
+extern "C" int aatc_codebook_vq(const aatc_codebook* cb, int32_t head, int32_t* n_groups, int32_t* vq_chan,
+                                float* vq_scale, float* vq_cent) {
+    if (!cb || !n_groups) return set_error(AATC_ERR_INVALID_ARG, "null pointer");
+    if (head < 0 || head >= (int)cb->heads.size()) return set_error(AATC_ERR_INVALID_ARG, "head %d out of range", head);
+    const HeadCB& H = cb->heads[head];
+    *n_groups = H.vq_groups;
+    if (H.vq_groups) {
+        copy_out(vq_chan, H.vq_chan);
+        copy_out(vq_scale, H.vq_scale);
+        copy_out(vq_cent, H.vq_cent);
+    }
+    return AATC_OK;
+}
+
 extern "C" int aatc_codebook_info(const aatc_codebook* cb, int32_t* d, int32_t* n_layers, int32_t* n_kv,
                                   int32_t* group, int32_t* total_bits, int32_t* tile_bytes) {
     if (!cb) return set_error(AATC_ERR_INVALID_ARG, "null codebook");
@@ -945,12 +1152,6 @@ extern "C" int aatc_codebook_info(const aatc_codebook* cb, int32_t* d, int32_t* 
     if (total_bits) *total_bits = cb->total_bits;
     if (tile_bytes) *tile_bytes = 8 * cb->total_bits;
     return AATC_OK;
-}
-
-template <class T, class S>
-static void copy_out(T* dst, const std::vector<S>& src) {
-    if (dst)
-        for (size_t i = 0; i < src.size(); ++i) dst[i] = (T)src[i];
 }
 
 extern "C" int aatc_codebook_head(const aatc_codebook* cb, int32_t head, double* U_k, double* U_v,
@@ -1041,6 +1242,8 @@ const char kMagic[8] = {'A', 'A', 'T', 'C', 'C', 'B', 0, 1};
 
 extern "C" int aatc_codebook_save(const aatc_codebook* cb, const char* path) {
     if (!cb || !path) return set_error(AATC_ERR_INVALID_ARG, "null pointer");
+    for (const HeadCB& H : cb->heads)
+        if (H.vq_groups) return set_error(AATC_ERR_UNSUPPORTED, "codebooks with vector-quantized keys are not persisted");
     Writer w;
     for (char c : kMagic) w.put(c);
     w.put<int32_t>(AATC_VERSION);

@@ -35,6 +35,7 @@ ST_CACHE_KV = 6
 ST_CALIB_Q = 7
 ST_DECODE_Q = 8
 ST_STEP = 9
+ST_VQ_TRAIN = 10  # standard normal training draws of the key codebooks
 ST_Q_BASIS = 16  # + query head index
 
 
@@ -116,6 +117,10 @@ WORKLOADS: Dict[str, Workload] = {
     # (16 heads per kv-head) at d = 64 and 3.0 bits/element, and at d = 128 and 6.0
     "edge_g16": Workload("edge_g16", 6, 64, 2, 32, 1, 1, 1024, 3.0, 2048, 64, "bf16"),
     "edge_rate": Workload("edge_rate", 7, 128, 1, 16, 1, 1, 1024, 6.0, 4096, 32, "bf16"),
+    # vector-quantized keys at 2.0 bits/element (one byte per group of 4 coefficients):
+    # a small head, and the Llama layer at 128k context
+    "vq_tiny": Workload("vq_tiny", 8, 64, 1, 4, 1, 1, 512, 2.0, 2048, 256, "bf16"),
+    "llama_vq_128k": Workload("llama_vq_128k", 9, 128, 8, 32, 1, 1, 131072, 2.0, 8192, 256, "bf16"),
 }
 
 
@@ -188,6 +193,11 @@ def draw_kv(hm: HeadModel, n: int, rng: np.random.Generator):
 def draw_q(hm: HeadModel, g: int, n: int, rng: np.random.Generator) -> np.ndarray:
     """n queries (float64) for query head g of the group."""
     return _draw(hm.UQ[g], hm.lamQ[g], np.zeros(hm.d), np.zeros(0, dtype=np.int64), n, rng)
+
+
+def vq_normals(w: Workload, layer: int, n: int) -> np.ndarray:
+    """[n, 4] standard normal draws that train the key codebooks of one layer."""
+    return rng_for(w.cfg, layer, 0, 0, ST_VQ_TRAIN).standard_normal((n, 4))
 
 
 def calibration_samples(w: Workload, hm: HeadModel, layer: int, head: int):

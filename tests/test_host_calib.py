@@ -182,3 +182,55 @@ def test_record_fields_match_the_oracle_placement():
                             ref.bK[None].astype(np.int32), ref.bV[None].astype(np.int32), ref.stepK[None],
                             ref.stepV[None])
     assert cbl.fields(0, 0) == oracle.fields(ref.bK) and cbl.fields(0, 1) == oracle.fields(ref.bV)
+
+
+@pytest.mark.parametrize("key_transform", ["klt", "nova"])
+def test_calibrate_vector_quantized_keys_matches_oracle(key_transform):
+    """key_quantizer = vq: the library's groups, weighted-domain scales, Lloyd codebooks and
+    value bits against the oracle's (same statistics, same training draws)."""
+    w, K, V, Q = _samples("vq_tiny")
+    st = oracle.head_stats(K.astype(np.float64), V.astype(np.float64), Q.astype(np.float64))
+    normals = synth.vq_normals(w, 0, 1024)
+    cb = q.calibrate([st], w.d, 1, 1, w.group, w.avg_bits, joint=False, key_transform=key_transform,
+                     key_quantizer="vq", vq_normals=normals, vq_iters=6)
+    ref = oracle.build_head_codebook(st, w.avg_bits, joint=False, key_transform=key_transform,
+                                     key_quantizer="vq", vq_normals=normals, vq_iters=6)
+    got = cb.vq(0)
+    assert got is not None and got["groups"].shape == (w.d * w.avg_bits // 8, 4)
+    np.testing.assert_array_equal(got["groups"], ref.vq.groups)
+    np.testing.assert_allclose(got["scale32"], ref.vq.scale32, rtol=2e-7)
+    np.testing.assert_allclose(got["cent32"], ref.vq.cent32, rtol=1e-5, atol=1e-6 * np.abs(ref.vq.cent).max())
+    h = cb.head(0)
+    assert not h["bK"].any() and np.array_equal(h["bV"], ref.bV)
+    assert cb.total_bits == 2 * int(w.d * w.avg_bits)
+    with pytest.raises(q.AatcError):
+        cb.save("/dev/null")
+
+
+def test_vector_quantized_keys_error_paths():
+    w, K, V, Q = _samples("vq_tiny")
+    st = oracle.head_stats(K.astype(np.float64), V.astype(np.float64), Q.astype(np.float64))
+    normals = synth.vq_normals(w, 0, 512)
+    for kw in (dict(joint=True, vq_normals=normals), dict(joint=False, vq_normals=None),
+               dict(joint=False, vq_normals=normals[:100])):
+        with pytest.raises(q.AatcError):
+            q.calibrate([st], w.d, 1, 1, w.group, w.avg_bits, key_quantizer="vq", **kw)
+    with pytest.raises(q.AatcError):  # more than 2 bits per key element
+        q.calibrate([st], w.d, 1, 1, w.group, 3.0, joint=False, key_quantizer="vq", vq_normals=normals)
+    ref = oracle.build_head_codebook(st, w.avg_bits, joint=False, key_quantizer="vq", vq_normals=normals,
+                                     vq_iters=2)
+    args = (w.d, 1, 1, w.group, ref.UK[None], ref.UV[None], ref.muK[None], ref.muV[None])
+    good = (ref.vq.groups[None], ref.vq.scale32[None], ref.vq.cent32[None], ref.bV[None], ref.stepV[None])
+    cb = q.codebook_create_vq(*args, *good)
+    np.testing.assert_array_equal(cb.vq(0)["groups"], ref.vq.groups)
+    np.testing.assert_array_equal(cb.vq(0)["cent32"], ref.vq.cent32)
+    dup = ref.vq.groups.copy()
+    dup[1, 0] = dup[0, 0]
+    bad_scale = ref.vq.scale32.copy()
+    bad_scale[ref.vq.groups[0, 0]] = 0.0
+    bad_cent = ref.vq.cent32.copy()
+    bad_cent[0, 0, 0] = np.nan
+    for g, sc, ce in ((dup, good[1][0], good[2][0]), (good[0][0], bad_scale, good[2][0]),
+                      (good[0][0], good[1][0], bad_cent), (good[0][0][:3], good[1][0], good[2][0][:3])):
+        with pytest.raises(q.AatcError):
+            q.codebook_create_vq(*args, g[None], sc[None], ce[None], ref.bV[None], ref.stepV[None])
