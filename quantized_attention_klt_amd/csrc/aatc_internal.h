@@ -69,6 +69,7 @@ struct alignas(256) DevHead {
     uint16_t QKt_hi[kMaxD * kMaxD];
     uint16_t QKt_lo[kMaxD * kMaxD];
     float muV[kMaxD];
+    float muK[kMaxD];
     float obias[kMaxD];           // mu_V - U_V (step_V * (2^(b-1) - 1/2)): output of all-zero codes
     float biasK[kMaxD];           // mu_K (U_hi + U_lo), fp64 sum rounded once
     float biasV[kMaxD];

@@ -576,6 +576,8 @@ int finalize(aatc_codebook* cb) {
         if (H.BK % kKeyAlign)
             return set_error(AATC_ERR_BUDGET, "head %zu: key bits per token (%d) must be a multiple of %d", h, H.BK,
                              kKeyAlign);
+        if (H.vq_groups != cb->heads[0].vq_groups)
+            return set_error(AATC_ERR_INVALID_ARG, "head %zu: every head of a codebook has the same key quantizer", h);
         int B = H.BK + H.BV;
         if (total < 0) total = B;
         if (B != total) return set_error(AATC_ERR_BUDGET, "head %zu has %d bits per token, head 0 has %d", h, B, total);
@@ -627,6 +629,7 @@ int finalize(aatc_codebook* cb) {
             }
         for (int j = 0; j < d; ++j) {
             D.muV[j] = (float)H.muV[j];
+            D.muK[j] = (float)H.muK[j];
             D.bitsK[j] = H.bK[j];
             D.bitsV[j] = H.bV[j];
             D.stepK[j] = H.bK[j] ? H.stepK[j] : 0.0f;

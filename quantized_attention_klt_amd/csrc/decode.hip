@@ -52,6 +52,8 @@
 using aatc::check_cache;
 using aatc::DevHead;
 using aatc::kTile;
+using aatc::kVqSize;
+using aatc::bf16f;
 using aatc::n_tiles_of;
 using aatc::quantize;
 using aatc::set_error;
@@ -906,12 +908,195 @@ constexpr Variant kVariants[] = {{1, 2, 4},  {1, 2, 8},  {1, 3, 8},  {1, 3, 10},
                                  {1, 8, 24}, {1, 16, 24}, {2, 2, 8},  {2, 3, 8},  {2, 3, 10}, {2, 4, 12}, {2, 8, 24},
                                  {2, 16, 24}, {3, 4, 12}, {3, 16, 24}, {4, 4, 12}, {4, 16, 24}};
 
+// ------------------------------------------------------------------------------------
+// Split decode over vector-quantized keys ("Spend Bits Where Queries Look", abstract).
+// Grid (workgroups per head x chunks of 4 query heads, kv-heads, sequences), 256 threads.
+// Prologue: q'' = (T_K^{-1} q) / s * log2(e) / sqrt(d) for the chunk's heads, then one
+// score table per (head, group): lut[m][g][i] = sum_k q''[chan(g, k)] z_gik over the
+// group's 256 codewords, so that a token's score is the sum over groups of
+// lut[m][g][index_g] (the dropped term q . mu_K is the same for every token).  Tiles of the
+// workgroup's contiguous share stream into two LDS buffers by direct global->LDS copies
+// (the next while this one is computed).  Per tile: wave m < 4 scores head m with one token
+// per lane (the record's index bytes, one table read per group), keeps that head's running
+// max and sum (base 2) and writes p to LDS; then every wave runs value blocks of 16 fields
+// on v_mfma_f32_16x16x4_f32 (A = p of the 4 heads over 4 token rows, B = the fields'
+// masked stored bytes as signed values), the accumulators rescaled by the heads' max
+// updates.  The partials have the split-decode layout, so merge_kernel finishes the call.
+// ------------------------------------------------------------------------------------
+struct VqLds {
+    int lut, tb0, tb1, pb, qv, alpha, total;
+};
+
+__host__ __device__ inline VqLds vq_lds(int n_g, int tile_bytes, int d) {
+    VqLds L;
+    const int tba = (tile_bytes + 15) & ~15;
+    L.lut = 0;
+    L.tb0 = 4 * n_g * kVqSize * 4;
+    L.tb1 = L.tb0 + tba;
+    L.pb = L.tb1 + tba;        // [4][64] float
+    L.qv = L.pb + 4 * 64 * 4;  // [4][d] float
+    L.alpha = L.qv + 4 * d * 4;
+    L.total = L.alpha + 16;
+    return L;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void vq_decode_kernel(const DevHead* __restrict__ blob, const uint8_t* __restrict__ cache,
+                                                        DecodeArgs a, const int32_t* __restrict__ seq_ids,
+                                                        const int64_t* __restrict__ seq_lens, const uint16_t* __restrict__ q,
+                                                        float* __restrict__ part) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t vsm_generic[];
+    LDS_AS uint8_t* const sm = (LDS_AS uint8_t*)vsm_generic;
+    const int n_chunks = (a.G + 3) / 4;
+    const int wgi = blockIdx.x / n_chunks, chunk = blockIdx.x - wgi * n_chunks;
+    const int h = blockIdx.y, z = blockIdx.z;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const DevHead& H = blob[a.layer * a.n_kv + h];
+    const int n_g = H.vq_groups, nvb = H.nvb, BK = H.BK;
+    const int hh0 = 4 * chunk, GC = min(4, a.G - hh0);
+    const int tbytes = a.tile_bytes, n16 = tbytes / 16;
+    const VqLds L = vq_lds(n_g, tbytes, D);
+    LDS_AS float* const lut = (LDS_AS float*)(sm + L.lut);
+    LDS_AS float* const pb = (LDS_AS float*)(sm + L.pb);
+    LDS_AS float* const qv = (LDS_AS float*)(sm + L.qv);
+    LDS_AS float* const alpha = (LDS_AS float*)(sm + L.alpha);
+    const int seq = seq_ids[z];
+    const int64_t len = max<int64_t>(0, min<int64_t>(seq_lens[z], a.max_len));
+    const int64_t n_tiles = (len + kTile - 1) / kTile;
+    const int64_t t_begin = n_tiles * wgi / a.wg_per_head, t_end = n_tiles * (wgi + 1) / a.wg_per_head;
+    const uint8_t* const base =
+        cache + (((int64_t)a.layer * a.n_seqs_cache + seq) * a.n_kv + h) * a.n_tiles_cap * (int64_t)tbytes;
+    // tile copies: instruction k of wave w moves chunks 256 k + 64 w + lane (16 bytes each)
+    int nlw = 0;
+    for (int k = 0; 256 * k + 64 * w < n16; ++k) ++nlw;
+    auto issue = [&](int64_t t, int buf) {
+        LDS_AS uint8_t* dst = sm + (buf ? L.tb1 : L.tb0);
+        for (int k = 0; k < nlw; ++k) {
+            const int c = 256 * k + 64 * w + lane;
+            if (c < n16)
+                __builtin_amdgcn_global_load_lds((const void*)(base + t * tbytes + 16 * c),
+                                                 (LDS_AS void*)(dst + 16 * (256 * k + 64 * w)), 16, 0, 2);
+        }
+    };
+    if (t_begin < t_end) issue(t_begin, 0);
+    // ---- prologue: q'' of the chunk's heads, the score tables, zero probability rows
+    for (int i = tid; i < 4 * D; i += 256) {
+        const int m = i / D, j = i - m * D;
+        float acc = 0.0f;
+        if (m < GC) {
+            const uint16_t* qr = q + (((int64_t)z * a.n_kv + h) * a.G + hh0 + m) * D;
+            for (int k = 0; k < D; ++k)
+                acc = fmaf(bf16f(H.QKt_hi[j * D + k]) + bf16f(H.QKt_lo[j * D + k]), bf16f(qr[k]), acc);
+            acc *= H.vq_rscale[j] * (kLog2e / sqrtf((float)D));
+        }
+        qv[i] = acc;
+    }
+    pb[tid] = 0.0f;
+    if (tid < 4) alpha[tid] = 1.0f;
+    lds_barrier();
+    for (int pi = tid; pi < n_g * kVqSize; pi += 256) {
+        const int g = pi / kVqSize, i = pi - g * kVqSize;
+        const float4 zc = *(const float4*)H.vq_cent[g][i];
+        const uint32_t chw = *(const uint32_t*)H.vq_chan[g];
+        const int c0 = chw & 255, c1 = (chw >> 8) & 255, c2 = (chw >> 16) & 255, c3 = chw >> 24;
+        for (int m = 0; m < GC; ++m) {
+            const LDS_AS float* qm = qv + m * D;
+            lut[(m * n_g + g) * kVqSize + i] = fmaf(qm[c3], zc.w, fmaf(qm[c2], zc.z, fmaf(qm[c1], zc.y, qm[c0] * zc.x)));
+        }
+    }
+    // value columns of this wave's blocks cb = w, w + 4, ... (at most 6)
+    constexpr int kMaxBW = (aatc::kMaxVB + 3) / 4;
+    uint32_t vcol[kMaxBW];
+#pragma unroll
+    for (int r = 0; r < kMaxBW; ++r) vcol[r] = w + 4 * r < nvb ? H.vb_col[w + 4 * r][lane & 15] : 0u;
+    f4 acc[kMaxBW];
+#pragma unroll
+    for (int r = 0; r < kMaxBW; ++r) acc[r] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY, l_run = 0.0f;  // wave m < GC: head m's running max and sum
+    lds_barrier();
+    // ---- the tiles
+    for (int64_t t = t_begin; t < t_end; ++t) {
+        const int cur = (int)((t - t_begin) & 1);
+        if (t + 1 < t_end) {
+            issue(t + 1, cur ^ 1);
+            wait_vm(nlw);
+        } else {
+            wait_vm(0);
+        }
+        lds_barrier();
+        const LDS_AS uint8_t* tb = sm + (cur ? L.tb1 : L.tb0);
+        if (w < GC) {
+            const int64_t tok = t * kTile + lane;
+            float s = 0.0f;
+            const LDS_AS float* lm = lut + w * n_g * kVqSize;
+            for (int r = 0; r < n_g / 4; ++r) {
+                const uint32_t wd = ((const LDS_AS uint32_t*)tb)[64 * r + lane] ^ 0x80808080u;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) s += lm[(4 * r + b) * kVqSize + ((wd >> (8 * b)) & 255u)];
+            }
+            const bool valid = tok < len;
+            const float mt = wave_max(valid ? s : -INFINITY);
+            const float m_new = fmaxf(m_run, mt);
+            const float al = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+            const float p = valid ? __builtin_amdgcn_exp2f(s - m_new) : 0.0f;
+            l_run = l_run * al + wave_sum(p);
+            m_run = m_new;
+            pb[w * 64 + lane] = p;
+            if (lane == 0) alpha[w] = al;
+        }
+        lds_barrier();
+        const int mrow = lane & 15, kk = lane >> 4;
+        float A[16];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const f4 x = mrow < 4 ? *(const LDS_AS f4*)&pb[mrow * 64 + 16 * kk + 4 * v] : f4{0.0f, 0.0f, 0.0f, 0.0f};
+            A[4 * v] = x[0];
+            A[4 * v + 1] = x[1];
+            A[4 * v + 2] = x[2];
+            A[4 * v + 3] = x[3];
+        }
+        const f4 al4 = kk == 0 ? *(const LDS_AS f4*)alpha : f4{1.0f, 1.0f, 1.0f, 1.0f};
+#pragma unroll
+        for (int r = 0; r < kMaxBW; ++r) {
+            if (w + 4 * r >= nvb) break;
+            acc[r] *= al4;
+            const uint32_t off = vcol[r] & 0xFFFFu, msk = (vcol[r] >> 16) * 0x01010101u;
+            const u32x4 by = *(const LDS_AS u32x4*)(tb + 8 * BK + off + 16 * kk);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int bv = (int)(int8_t)(((by[i >> 2] & msk) >> (8 * (i & 3))) & 255u);
+                acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[i], (float)bv, acc[r], 0, 0, 0);
+            }
+        }
+        lds_barrier();
+    }
+    wait_vm(0);
+    // ---- partials: [max, sum, 128 sum, 0, columns]
+    const int64_t zh = (int64_t)z * a.n_kv + h;
+    float* const P = part + ((zh * a.wg_per_head + wgi) * a.G + hh0) * a.part_ld;
+    if (w < GC && lane == 0) {
+        float* o = P + w * a.part_ld;
+        o[0] = m_run;
+        o[1] = l_run;
+        o[2] = 128.0f * l_run;
+        o[3] = 0.0f;
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int r = 0; r < kMaxBW; ++r) {
+            if (w + 4 * r >= nvb) break;
+            for (int m = 0; m < GC; ++m) P[m * a.part_ld + kPartHead + 16 * (w + 4 * r) + lane] = acc[r][m];
+        }
+    }
+}
+
 struct Plan {
     Variant v;
     int nqm_max, nvb_max, wg_per_head, wgs_per_cu, nw;
     size_t part_bytes;
     DecodeArgs args;
     size_t lds;
+    bool vq = false;  // vector-quantized keys: vq_decode_kernel
 };
 
 size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
@@ -926,6 +1111,24 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
         const DevHead& D = cb->blob[(size_t)layer * cb->n_kv + h];
         p.nqm_max = std::max(p.nqm_max, D.nqm);
         p.nvb_max = std::max(p.nvb_max, D.nvb);
+    }
+    if (cb->heads[0].vq_groups) {  // vector-quantized keys
+        DecodeArgs& a = p.args;
+        p.vq = true;
+        a.G = G;
+        a.tile_bytes = 8 * cb->total_bits;
+        const VqLds L = vq_lds(cb->heads[0].vq_groups, a.tile_bytes, d);
+        p.lds = (size_t)L.total;
+        if (p.lds > 160 * 1024) return set_error(AATC_ERR_UNSUPPORTED, "decode needs %zu bytes of LDS", p.lds);
+        p.wgs_per_cu = (int)std::max<size_t>(1, (160 * 1024) / p.lds);
+        p.nw = 4;
+        const int64_t units = (int64_t)cb->n_kv * n_seqs * ((G + 3) / 4);
+        const int64_t slots = 256 * (int64_t)p.wgs_per_cu;
+        p.wg_per_head = (int)std::max<int64_t>(1, std::min<int64_t>({slots / units, n_tiles_of(max_len), kMaxWG}));
+        a.wg_per_head = p.wg_per_head;
+        a.part_ld = kPartHead + 16 * p.nvb_max;
+        p.part_bytes = (size_t)n_seqs * cb->n_kv * p.wg_per_head * G * a.part_ld * sizeof(float);
+        return AATC_OK;
     }
     bool found = false;
     for (const Variant& v : kVariants)
@@ -1090,6 +1293,26 @@ extern "C" int aatc_profile_end(float* ms, int32_t* n_out) {
     return rc;
 }
 
+template <int D>
+int launch_vq_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* blob, uint8_t* cache,
+                     const int32_t* ids, const int64_t* lens, const uint16_t* q, float* part, float* out) {
+    const DecodeArgs& a = p.args;
+    if (p.lds > 64 * 1024)
+        HIP_TRY(hipFuncSetAttribute((const void*)vq_decode_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)p.lds));
+    hipEvent_t e0, e1;
+    profile_slot(e0, e1);
+    if (e0) HIP_TRY(hipEventRecord(e0, st));
+    hipLaunchKernelGGL((vq_decode_kernel<D>), dim3(p.wg_per_head * ((a.G + 3) / 4), a.n_kv, n_seqs), dim3(256), p.lds,
+                       st, blob, cache, a, ids, lens, q, part);
+    HIP_TRY(hipGetLastError());
+    if (e1) HIP_TRY(hipEventRecord(e1, st));
+    hipLaunchKernelGGL((merge_kernel<D>), dim3(a.n_kv * (D / kMergeSlice), n_seqs, a.G), dim3(kMergeThreads), 0, st,
+                       blob, a.layer, a.n_kv, a.G, p.wg_per_head, a.part_ld, (const float*)part, out);
+    HIP_TRY(hipGetLastError());
+    return AATC_OK;
+}
+
 extern "C" int aatc_decode_workspace_bytes(const aatc_codebook* cb, int32_t n_seqs, int64_t max_len, size_t* bytes) {
     if (!cb || !bytes) return set_error(AATC_ERR_INVALID_ARG, "null pointer");
     if (n_seqs < 1 || max_len < 1) return set_error(AATC_ERR_INVALID_ARG, "need n_seqs >= 1 and max_len >= 1");
@@ -1138,6 +1361,11 @@ static int decode_impl(const aatc_codebook* cb, const void* d_blob, const aatc_c
     uint8_t* c = (uint8_t*)cache->data;
     a.k_new = k_new;
     a.v_new = v_new;
+    if (p.vq) {
+        if (k_new) return set_error(AATC_ERR_UNSUPPORTED, "fused append with vector-quantized keys");
+        return cb->d == 64 ? launch_vq_decode<64>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, part, out)
+                           : launch_vq_decode<128>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, part, out);
+    }
 #define AATC_DECODE_CASE(rb_, nqm_, nvb_)                                                                    \
     if (p.v.rb == rb_ && p.v.nqm == nqm_ && p.v.nvb == nvb_)                                                 \
         return cb->d == 64                                                                                   \

@@ -364,7 +364,8 @@ template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void encode_mfma_kernel(
     const DevHead* __restrict__ blob, uint8_t* __restrict__ cache, int layer, int n_kv, int64_t n_tiles_cap,
     int tile_bytes, SeqArgs sa, int64_t n_tokens, int64_t ntiles, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, int n_seqs_cache) {
+    const uint16_t* __restrict__ V, int n_seqs_cache, int values_only) {
+    if (values_only && !(blockIdx.y & 1)) return;  // keys are vector-quantized by vq_keys_kernel
     if (blockIdx.y & 1)
         encode_mfma_body<D, true>(blob, cache, layer, n_kv, n_tiles_cap, tile_bytes, sa, n_tokens, ntiles, K, V,
                                   n_seqs_cache);
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(256) void encode_coeffs_kernel(const DevHead* __res
     __shared__ PieceTab pt[2];
     const int h = blockIdx.y, zi = blockIdx.z;
     const DevHead& H = blob[layer * n_kv + h];
-    const int d = H.d;
+    const int d = H.d, n_g = H.vq_groups;
     const int64_t start = sa.start[zi];
     const int64_t tile = start / kTile + blockIdx.x;
     const int64_t tok0 = tile * kTile;
@@ -406,10 +407,96 @@ __global__ __launch_bounds__(256) void encode_coeffs_kernel(const DevHead* __res
         const int b = kv ? H.bitsV[j] : H.bitsK[j];
         if (b) scatter_code(kv ? sg1 : sg0, ptl + kv, j, s, quantize(cf, kv ? H.invV[j] : H.invK[j], b));
     }
+    // vector-quantized keys: one index per (slot, group), record byte g
+    for (int i = threadIdx.x; i < (s1 - s0) * n_g; i += blockDim.x) {
+        const int s = s0 + i / n_g, g = i % n_g;
+        const float* cf = coeffs + ((tok0 + s - start) * n_kv + h) * 2 * d;
+        float u[aatc::kVqDim];
+#pragma unroll
+        for (int k = 0; k < aatc::kVqDim; ++k) {
+            const int j = H.vq_chan[g][k];
+            u[k] = __fmul_rn(cf[j], H.vq_scale[j]);
+        }
+        scatter_code(sg0, ptl, g, s, aatc::vq_nearest(H.vq_cent[g], u[0], u[1], u[2], u[3]));
+    }
     __syncthreads();
     uint8_t* tp = tile_ptr(cache, layer, n_seqs_cache, sa.seq[zi], n_kv, h, n_tiles_cap, tile, tile_bytes);
     copy_out<false>(sg0, H.BK / 8, (uint32_t*)tp, s0, s1, threadIdx.x, blockDim.x);
     copy_out<true>(sg1, H.BV / 8, (uint32_t*)(tp + 8 * H.BK), s0, s1, threadIdx.x, blockDim.x);
+}
+
+// ------------------------------------------------------------------------------------
+// vector-quantized keys from bf16 K ("Spend Bits Where Queries Look", abstract): one
+// workgroup per (tile, kv-head, sequence).  The tile's centred rows x - mu_K go to LDS in
+// fp32; coefficients c_j = sum_i (x - mu)_i U_K[i][j] by fp32 multiply-adds in i order
+// (thread: channel j, every 256/D-th token), written back over the rows; then wave w takes
+// the groups w, w + 4, ... with one token per lane: u_k = fp32(c_k s_k), the nearest of the
+// group's 256 codewords (the host-side definition, bit for bit), OR-ed into the staged key
+// block as record byte g.  The values of these tokens are coded by the MFMA encoder.
+// ------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void vq_keys_kernel(const DevHead* __restrict__ blob, uint8_t* __restrict__ cache,
+                                                      int layer, int n_kv, int64_t n_tiles_cap, int tile_bytes,
+                                                      SeqArgs sa, int64_t n_tokens, const uint16_t* __restrict__ K,
+                                                      int n_seqs_cache) {
+    constexpr int XS = D + 4;        // LDS row stride (floats)
+    constexpr int TPH = 256 / D;     // token phases
+    constexpr int NT = kTile / TPH;  // tokens per thread
+    __shared__ __attribute__((aligned(16))) float xs[kTile * XS];
+    __shared__ __attribute__((aligned(16))) uint32_t stg[kStageWords];
+    __shared__ PieceTab pt;
+    const int h = blockIdx.y, zi = blockIdx.z, tid = threadIdx.x;
+    const DevHead& H = blob[layer * n_kv + h];
+    const int n_g = H.vq_groups;
+    const int64_t start = sa.start[zi];
+    const int64_t tile = start / kTile + blockIdx.x;
+    const int64_t tok0 = tile * kTile;
+    const int s0 = (int)std::max<int64_t>(start - tok0, 0);
+    const int s1 = (int)std::min<int64_t>(start + n_tokens - tok0, kTile);
+    LDS_AS PieceTab* const ptl = (LDS_AS PieceTab*)&pt;
+    LDS_AS uint32_t* const sg = (LDS_AS uint32_t*)&stg[0];
+    stage_pieces(H, false, ptl, tid, 256);
+    for (int i = tid; i < kStageWords; i += 256) stg[i] = 0u;
+    const uint16_t* X = K + ((int64_t)zi * n_tokens * n_kv + h) * D;  // token t at X + t * n_kv * D
+    for (int i = tid; i < kTile * D; i += 256) {
+        const int s = i / D, c = i % D;
+        xs[s * XS + c] = s >= s0 && s < s1 ? bf16f(X[(tok0 + s - start) * n_kv * D + c]) - H.muK[c] : 0.0f;
+    }
+    __syncthreads();
+    const int j = tid % D, ph = tid / D;
+    float acc[NT];
+#pragma unroll
+    for (int k = 0; k < NT; ++k) acc[k] = 0.0f;
+    for (int i = 0; i < D; i += 4) {
+        const float u0 = H.UK[(i + 0) * D + j], u1 = H.UK[(i + 1) * D + j];
+        const float u2 = H.UK[(i + 2) * D + j], u3 = H.UK[(i + 3) * D + j];
+#pragma unroll
+        for (int k = 0; k < NT; ++k) {
+            const float4 x = *(const float4*)&xs[(ph + TPH * k) * XS + i];
+            acc[k] = fmaf(x.x, u0, acc[k]);
+            acc[k] = fmaf(x.y, u1, acc[k]);
+            acc[k] = fmaf(x.z, u2, acc[k]);
+            acc[k] = fmaf(x.w, u3, acc[k]);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NT; ++k) xs[(ph + TPH * k) * XS + j] = acc[k];
+    __syncthreads();
+    const int w = tid >> 6, s = tid & 63;
+    for (int g = w; g < n_g; g += 4) {
+        float u[aatc::kVqDim];
+#pragma unroll
+        for (int k = 0; k < aatc::kVqDim; ++k) {
+            const int c = H.vq_chan[g][k];
+            u[k] = __fmul_rn(xs[s * XS + c], H.vq_scale[c]);
+        }
+        const uint32_t idx = aatc::vq_nearest(H.vq_cent[g], u[0], u[1], u[2], u[3]);
+        if (s >= s0 && s < s1) scatter_code(sg, ptl, g, s, idx);
+    }
+    __syncthreads();
+    uint8_t* tp = tile_ptr(cache, layer, n_seqs_cache, sa.seq[zi], n_kv, h, n_tiles_cap, tile, tile_bytes);
+    copy_out<false>(sg, H.BK / 8, (uint32_t*)tp, s0, s1, tid, 256);
 }
 
 __global__ void flush_kernel(uint4* p, size_t n) {
@@ -495,14 +582,25 @@ static int encode_common(const aatc_codebook* cb, const void* d_blob, const aatc
             const int64_t units = (int64_t)used * cb->n_kv * 2;
             const unsigned wx = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ntiles, kEncodeSlots / units));
             const dim3 grid(wx, (unsigned)(2 * cb->n_kv), (unsigned)used);
-            if (d == 64)
+            const int vq = cb->heads[0].vq_groups > 0;
+            const dim3 kgrid((unsigned)ntiles, (unsigned)cb->n_kv, (unsigned)used);
+            if (d == 64) {
                 hipLaunchKernelGGL(encode_mfma_kernel<64>, grid, dim3(256), encode_lds_bytes<64>(), (hipStream_t)stream, blob,
                                    (uint8_t*)cache->data, layer, cb->n_kv, ncap, tile_bytes, sa, n_tokens, ntiles, Kz, Vz,
-                                   cache->n_seqs);
-            else
+                                   cache->n_seqs, vq);
+                if (vq)
+                    hipLaunchKernelGGL(vq_keys_kernel<64>, kgrid, dim3(256), 0, (hipStream_t)stream, blob,
+                                       (uint8_t*)cache->data, layer, cb->n_kv, ncap, tile_bytes, sa, n_tokens, Kz,
+                                       cache->n_seqs);
+            } else {
                 hipLaunchKernelGGL(encode_mfma_kernel<128>, grid, dim3(256), encode_lds_bytes<128>(), (hipStream_t)stream, blob,
                                    (uint8_t*)cache->data, layer, cb->n_kv, ncap, tile_bytes, sa, n_tokens, ntiles, Kz, Vz,
-                                   cache->n_seqs);
+                                   cache->n_seqs, vq);
+                if (vq)
+                    hipLaunchKernelGGL(vq_keys_kernel<128>, kgrid, dim3(256), 0, (hipStream_t)stream, blob,
+                                       (uint8_t*)cache->data, layer, cb->n_kv, ncap, tile_bytes, sa, n_tokens, Kz,
+                                       cache->n_seqs);
+            }
         }
         HIP_TRY(hipGetLastError());
         s0 += used;

@@ -36,4 +36,24 @@ __device__ __forceinline__ uint32_t quantize(float c, float inv, int b) {
     return (uint32_t)__builtin_amdgcn_fmed3f(v, 0.0f, (float)((1 << b) - 1));
 }
 
+// Nearest codeword of the weighted key coefficients (u0, u1, u2, u3) among cent[0..255]
+// (one group of vector-quantized keys): t_k = u_k - z_k, distance (t0 t0 + t1 t1) +
+// (t2 t2 + t3 t3), each operation rounded to fp32 (contraction off), lowest index on ties.
+__device__ __forceinline__ uint32_t vq_nearest(const float (*__restrict__ cent)[kVqDim], float u0, float u1, float u2,
+                                               float u3) {
+#pragma clang fp contract(off)
+    float best = __builtin_inff();
+    uint32_t bi = 0;
+    for (int i = 0; i < kVqSize; ++i) {
+        const float4 z = *(const float4*)cent[i];
+        const float t0 = u0 - z.x, t1 = u1 - z.y, t2 = u2 - z.z, t3 = u3 - z.w;
+        const float e = (t0 * t0 + t1 * t1) + (t2 * t2 + t3 * t3);
+        if (e < best) {
+            best = e;
+            bi = (uint32_t)i;
+        }
+    }
+    return bi;
+}
+
 }  // namespace aatc

@@ -32,8 +32,13 @@ def torch():
 
 def _device_codebook(q, torch, case):
     a = case.codebook_arrays()
-    cb = q.codebook_create(case.d, 1, case.n_kv, case.group, a["UK"], a["UV"], a["muK"], a["muV"], a["bK"],
-                           a["bV"], a["stepK"], a["stepV"])
+    if a["vq"] is not None:
+        v = a["vq"]
+        cb = q.codebook_create_vq(case.d, 1, case.n_kv, case.group, a["UK"], a["UV"], a["muK"], a["muV"],
+                                  v["groups"], v["scale32"], v["cent32"], a["bV"], a["stepV"])
+    else:
+        cb = q.codebook_create(case.d, 1, case.n_kv, case.group, a["UK"], a["UV"], a["muK"], a["muV"], a["bK"],
+                               a["bV"], a["stepK"], a["stepV"])
     blob = torch.empty(cb.device_bytes(), dtype=torch.uint8, device="cuda")
     cb.upload(blob)
     return cb, blob

@@ -11,7 +11,8 @@ class Case:
     """Oracle codebooks and synthetic K/V/Q for n_kv heads of one layer of workload w."""
 
     def __init__(self, wname: str, ctx: int, n_seqs: int = 1, n_kv: int | None = None, layer: int = 0,
-                 n_calib_q: int | None = None, lens=None, step: int = 0, key_transform: str = "klt"):
+                 n_calib_q: int | None = None, lens=None, step: int = 0, key_transform: str = "klt",
+                 key_quantizer: str = "scalar", vq_train: int = 1024, vq_iters: int = 8):
         w = synth.WORKLOADS[wname]
         self.w = w
         self.d = w.d
@@ -28,8 +29,13 @@ class Case:
             K, V, Q = synth.calibration_samples(w, hm, layer, h)
             if n_calib_q is not None:
                 Q = Q.reshape(w.group, -1, w.d)[:, :n_calib_q].reshape(-1, w.d)
-            self.cbs.append(oracle.build_head_codebook(oracle.head_stats(K, V, Q), w.avg_bits,
-                                                       key_transform=key_transform))
+            if key_quantizer == "vq":
+                self.cbs.append(oracle.build_head_codebook(
+                    oracle.head_stats(K, V, Q), w.avg_bits, joint=False, key_transform=key_transform,
+                    key_quantizer="vq", vq_normals=synth.vq_normals(w, layer, vq_train), vq_iters=vq_iters))
+            else:
+                self.cbs.append(oracle.build_head_codebook(oracle.head_stats(K, V, Q), w.avg_bits,
+                                                           key_transform=key_transform))
         # cached K/V: bf16 bits [n_seqs, ctx, n_kv, d] and their float64 values
         self.k_bits = np.zeros((n_seqs, ctx, self.n_kv, w.d), np.uint16)
         self.v_bits = np.zeros_like(self.k_bits)
@@ -53,7 +59,7 @@ class Case:
 
     @property
     def tile_bytes(self):
-        return oracle.tile_bytes(self.cbs[0].bK, self.cbs[0].bV)
+        return oracle.tile_bytes(oracle.key_record_bits(self.cbs[0]), self.cbs[0].bV)
 
     def n_tiles(self, max_tokens=None):
         return ((max_tokens or self.ctx) + 63) // 64
@@ -86,7 +92,11 @@ class Case:
         return dict(UK=np.stack([c.UK for c in cbs]), UV=np.stack([c.UV for c in cbs]),
                     muK=np.stack([c.muK for c in cbs]), muV=np.stack([c.muV for c in cbs]),
                     bK=np.stack([c.bK for c in cbs]), bV=np.stack([c.bV for c in cbs]),
-                    stepK=np.stack([c.stepK for c in cbs]), stepV=np.stack([c.stepV for c in cbs]))
+                    stepK=np.stack([c.stepK for c in cbs]), stepV=np.stack([c.stepV for c in cbs]),
+                    vq=None if cbs[0].vq is None else dict(
+                        groups=np.stack([c.vq.groups for c in cbs]),
+                        scale32=np.stack([c.vq.scale32 for c in cbs]),
+                        cent32=np.stack([c.vq.cent32 for c in cbs])))
 
     def coeffs(self, s):
         """Oracle fp32 KLT coefficients [ctx, n_kv, 2, d] of sequence s."""
