@@ -39,6 +39,14 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+VQ_TRAIN, VQ_ITERS = 8192, 20  # key codebook training draws and Lloyd rounds
+
+
+def vq_keys(w) -> bool:
+    """Workloads whose keys are vector-quantized (one byte per group of 4 coefficients)."""
+    return "vq" in w.name
+
+
 def build_inputs(wname: str, ctx: int):
     import synth
     import quantized_attention_klt_amd as q
@@ -52,7 +60,11 @@ def build_inputs(wname: str, ctx: int):
         K, V, Q = synth.calibration_samples(w, hm, 0, h)
         stats.append(q.stats_from_samples(K, V, Q))
     t1 = time.perf_counter()
-    cb = q.calibrate(stats, w.d, 1, w.n_kv, w.group, w.avg_bits)
+    if vq_keys(w):
+        cb = q.calibrate(stats, w.d, 1, w.n_kv, w.group, w.avg_bits, joint=False, key_quantizer="vq",
+                         vq_normals=synth.vq_normals(w, 0, VQ_TRAIN), vq_iters=VQ_ITERS)
+    else:
+        cb = q.calibrate(stats, w.d, 1, w.n_kv, w.group, w.avg_bits)
     t2 = time.perf_counter()
     log(f"calibration: stats {t1 - t0:.2f}s, calibrate {t2 - t1:.2f}s")
     kb = np.zeros((1, ctx, w.n_kv, w.d), np.uint16)
@@ -103,7 +115,12 @@ def cpu_baseline(wname: str, n_tokens: int = 16384):
     w = synth.WORKLOADS[wname]
     hm = synth.head_model(w, 0, 0)
     K, V, Q = synth.calibration_samples(w, hm, 0, 0)
-    cb = oracle.build_head_codebook(oracle.head_stats(K, V, Q), w.avg_bits)
+    if vq_keys(w):
+        cb = oracle.build_head_codebook(oracle.head_stats(K, V, Q), w.avg_bits, joint=False,
+                                        key_quantizer="vq", vq_normals=synth.vq_normals(w, 0, VQ_TRAIN),
+                                        vq_iters=VQ_ITERS)
+    else:
+        cb = oracle.build_head_codebook(oracle.head_stats(K, V, Q), w.avg_bits)
     Kc, Vc = synth.cache_kv(w, hm, 0, 0, 0, n_tokens)
     kf = synth.bf16_bits_to_f64(synth.to_bf16_bits(Kc))
     vf = synth.bf16_bits_to_f64(synth.to_bf16_bits(Vc))
@@ -118,7 +135,7 @@ def cpu_baseline(wname: str, n_tokens: int = 16384):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    tb = oracle.tile_bytes(cb.bK, cb.bV)
+    tb = oracle.tile_bytes(oracle.key_record_bits(cb), cb.bV)
     dec_bytes = n_tokens * tb / 64
     return {
         "value": dec_bytes / (t2 - t1) / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
@@ -217,10 +234,13 @@ def main():
     tb = cb.tile_bytes
     n_tiles = (ctx + 63) // 64
     cache_bytes = w.n_kv * n_tiles * tb
-    side = 2 * w.n_kv * w.d * w.d * 4 + w.n_q * w.d * 2 + w.n_q * w.d * 4
-    dec_bytes = cache_bytes + side
-    # the split-decode kernel alone: the packed cache, U_K and the bf16 queries
-    kern_bytes = cache_bytes + w.n_kv * w.d * w.d * 4 + w.n_q * w.d * 2
+    vq = vq_keys(w)
+    # vector-quantized keys: the codebooks (n_g x 256 words of 4 fp32) are side information too
+    books = w.n_kv * (w.d * w.avg_bits // 8) * 256 * 4 * 4 if vq else 0
+    side = 2 * w.n_kv * w.d * w.d * 4 + w.n_q * w.d * 2 + w.n_q * w.d * 4 + books
+    dec_bytes = int(cache_bytes + side)
+    # the split-decode kernel alone: the packed cache, U_K (or T_K^-1), the codebooks, the bf16 queries
+    kern_bytes = int(cache_bytes + w.n_kv * w.d * w.d * 4 + w.n_q * w.d * 2 + books)
     kern_s = float(kern_ms.mean()) / 1e3
     kern_gbs = kern_bytes / kern_s / 1e9
     enc_bytes = 2 * ctx * w.n_kv * w.d * 2 + cache_bytes
@@ -242,7 +262,8 @@ def main():
         "vs_baseline": None,
         "dtype": "i8+f32",
         "data": "synthetic",
-        "config": {"workload": "llama3.1-8b-attention-layer", "kv_heads": w.n_kv, "q_heads": w.n_q,
+        "config": {"workload": "llama3.1-8b-attention-layer" + ("-vq-keys" if vq else ""),
+                   "kv_heads": w.n_kv, "q_heads": w.n_q,
                    "head_dim": w.d, "ctx": ctx, "batch": 1, "bits_per_element": w.avg_bits,
                    "step": "prefill-encode of ctx tokens + one decode-attention step"},
         "decode_ms": round(float(dec_ms.mean()), 4),
@@ -255,16 +276,20 @@ def main():
         "compression_ratio": round(16.0 / w.avg_bits, 4),
         "calibration_s": round(calib_s, 3),
         "wall_s_timed_region": round(wall, 3),
-        "roofline": {"kernel": "decode_kernel (split decode: scores, online softmax, value sums)", "bound": "hbm",
+        "roofline": {"kernel": ("vq_decode_kernel (split decode over vector-quantized keys)" if vq else
+                                "decode_kernel (split decode: scores, online softmax, value sums)"),
+                     "bound": "hbm",
                      "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(*DECODE_PMC),
+                     "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if vq else measured_traffic(*DECODE_PMC),
                      "algorithmic_bytes": kern_bytes, "kernel_ms": round(kern_s * 1e3, 4),
                      "source_sha256_16": source_hash(DECODE_PMC[1])},
         "roofline_encode": {"kernel": "encode", "bound": "hbm", "achieved": round(enc_gbs, 2),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(enc_gbs / HBM_PEAK_GBS, 4),
                             "mfma_tflops": round(enc_flops / enc_s / 1e12, 2),
                             "mfma_frac": round(enc_flops / enc_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-                            "traffic": measured_traffic(*ENCODE_PMC), "algorithmic_bytes": enc_bytes,
+                            "traffic": None if vq else measured_traffic(*ENCODE_PMC),
+                            "algorithmic_bytes": enc_bytes,
                             "source_sha256_16": source_hash(ENCODE_PMC[1])},
     }
     if not args.no_cpu_baseline:

@@ -915,32 +915,37 @@ constexpr Variant kVariants[] = {{1, 2, 4},  {1, 2, 8},  {1, 3, 8},  {1, 3, 10},
 // score table per (head, group): lut[m][g][i] = sum_k q''[chan(g, k)] z_gik over the
 // group's 256 codewords, so that a token's score is the sum over groups of
 // lut[m][g][index_g] (the dropped term q . mu_K is the same for every token).  Tiles of the
-// workgroup's contiguous share stream into two LDS buffers by direct global->LDS copies
-// (the next while this one is computed).  Per tile: wave m < 4 scores head m with one token
+// workgroup's contiguous share stream through a ring of LDS buffers (as many as the LDS
+// beside the tables holds, at most 8) by direct global->LDS copies, all but one of them in
+// flight while a tile is computed: with one workgroup per CU, the bytes in flight set the
+// rate (one tile ahead streamed at about 0.5 TB/s).  Per tile: wave m < 4 scores head m with one token
 // per lane (the record's index bytes, one table read per group), keeps that head's running
-// max and sum (base 2) and writes p to LDS; then every wave runs value blocks of 16 fields
-// on v_mfma_f32_16x16x4_f32 (A = p of the 4 heads over 4 token rows, B = the fields'
-// masked stored bytes as signed values), the accumulators rescaled by the heads' max
-// updates.  The partials have the split-decode layout, so merge_kernel finishes the call.
+// max and sum (base 2) of p rounded to fp16 and writes p to LDS; then every wave runs value
+// blocks of 16 fields on v_mfma_f32_16x16x16_f16 (A = p of the 4 heads over 16 tokens, B =
+// the fields' masked stored bytes as signed values, exact in fp16), the accumulators
+// rescaled by the heads' max updates.  The partials have the split-decode layout, so merge_kernel finishes the call.
 // ------------------------------------------------------------------------------------
 struct VqLds {
-    int lut, tb0, tb1, pb, qv, alpha, total;
+    int lut, pb, qv, alpha, ring, tba, nbuf, total;
 };
 
 __host__ __device__ inline VqLds vq_lds(int n_g, int tile_bytes, int d) {
     VqLds L;
-    const int tba = (tile_bytes + 15) & ~15;
+    L.tba = (tile_bytes + 15) & ~15;
     L.lut = 0;
-    L.tb0 = 4 * n_g * kVqSize * 4;
-    L.tb1 = L.tb0 + tba;
-    L.pb = L.tb1 + tba;        // [4][64] float
-    L.qv = L.pb + 4 * 64 * 4;  // [4][d] float
+    L.pb = 4 * n_g * kVqSize * 4;  // [4][64] float
+    L.qv = L.pb + 4 * 64 * 4;      // [4][d] float
     L.alpha = L.qv + 4 * d * 4;
-    L.total = L.alpha + 16;
+    L.ring = L.alpha + 16;
+    const int room = (160 * 1024 - L.ring) / L.tba;
+    L.nbuf = room < 2 ? 2 : (room > 8 ? 8 : room);
+    L.total = L.ring + L.nbuf * L.tba;
     return L;
 }
 
-template <int D>
+// NG: the number of groups when fixed at compile time (every index word and table read of a
+// tile issued back to back), 0 for any multiple of 4 at run time.
+template <int D, int NG>
 __global__ __launch_bounds__(256) void vq_decode_kernel(const DevHead* __restrict__ blob, const uint8_t* __restrict__ cache,
                                                         DecodeArgs a, const int32_t* __restrict__ seq_ids,
                                                         const int64_t* __restrict__ seq_lens, const uint16_t* __restrict__ q,
@@ -950,9 +955,10 @@ __global__ __launch_bounds__(256) void vq_decode_kernel(const DevHead* __restric
     const int n_chunks = (a.G + 3) / 4;
     const int wgi = blockIdx.x / n_chunks, chunk = blockIdx.x - wgi * n_chunks;
     const int h = blockIdx.y, z = blockIdx.z;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    // the wave index as a scalar: the copy counts and waits below are uniform branches
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const DevHead& H = blob[a.layer * a.n_kv + h];
-    const int n_g = H.vq_groups, nvb = H.nvb, BK = H.BK;
+    const int n_g = NG ? NG : H.vq_groups, nvb = H.nvb, BK = H.BK;
     const int hh0 = 4 * chunk, GC = min(4, a.G - hh0);
     const int tbytes = a.tile_bytes, n16 = tbytes / 16;
     const VqLds L = vq_lds(n_g, tbytes, D);
@@ -970,7 +976,7 @@ __global__ __launch_bounds__(256) void vq_decode_kernel(const DevHead* __restric
     int nlw = 0;
     for (int k = 0; 256 * k + 64 * w < n16; ++k) ++nlw;
     auto issue = [&](int64_t t, int buf) {
-        LDS_AS uint8_t* dst = sm + (buf ? L.tb1 : L.tb0);
+        LDS_AS uint8_t* dst = sm + L.ring + buf * L.tba;
         for (int k = 0; k < nlw; ++k) {
             const int c = 256 * k + 64 * w + lane;
             if (c < n16)
@@ -978,15 +984,22 @@ __global__ __launch_bounds__(256) void vq_decode_kernel(const DevHead* __restric
                                                  (LDS_AS void*)(dst + 16 * (256 * k + 64 * w)), 16, 0, 2);
         }
     };
-    if (t_begin < t_end) issue(t_begin, 0);
+    const int NB = L.nbuf;
+    for (int k = 0; k < NB - 1 && t_begin + k < t_end; ++k) issue(t_begin + k, k);
     // ---- prologue: q'' of the chunk's heads, the score tables, zero probability rows
+    typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
     for (int i = tid; i < 4 * D; i += 256) {
         const int m = i / D, j = i - m * D;
         float acc = 0.0f;
         if (m < GC) {
             const uint16_t* qr = q + (((int64_t)z * a.n_kv + h) * a.G + hh0 + m) * D;
-            for (int k = 0; k < D; ++k)
-                acc = fmaf(bf16f(H.QKt_hi[j * D + k]) + bf16f(H.QKt_lo[j * D + k]), bf16f(qr[k]), acc);
+#pragma unroll 4
+            for (int k = 0; k < D; k += 8) {
+                const u16x8 hi = *(const u16x8*)&H.QKt_hi[j * D + k], lo = *(const u16x8*)&H.QKt_lo[j * D + k];
+                const u16x8 qq = *(const u16x8*)&qr[k];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = fmaf(bf16f(hi[e]) + bf16f(lo[e]), bf16f(qq[e]), acc);
+            }
             acc *= H.vq_rscale[j] * (kLog2e / sqrtf((float)D));
         }
         qv[i] = acc;
@@ -994,14 +1007,23 @@ __global__ __launch_bounds__(256) void vq_decode_kernel(const DevHead* __restric
     pb[tid] = 0.0f;
     if (tid < 4) alpha[tid] = 1.0f;
     lds_barrier();
-    for (int pi = tid; pi < n_g * kVqSize; pi += 256) {
-        const int g = pi / kVqSize, i = pi - g * kVqSize;
-        const float4 zc = *(const float4*)H.vq_cent[g][i];
-        const uint32_t chw = *(const uint32_t*)H.vq_chan[g];
-        const int c0 = chw & 255, c1 = (chw >> 8) & 255, c2 = (chw >> 16) & 255, c3 = chw >> 24;
-        for (int m = 0; m < GC; ++m) {
-            const LDS_AS float* qm = qv + m * D;
-            lut[(m * n_g + g) * kVqSize + i] = fmaf(qm[c3], zc.w, fmaf(qm[c2], zc.z, fmaf(qm[c1], zc.y, qm[c0] * zc.x)));
+    // thread tid: codeword tid of every group, four groups' loads in flight at a time
+    for (int g0 = 0; g0 < n_g; g0 += 4) {
+        float4 zc[4];
+        uint32_t chw[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            zc[u] = *(const float4*)H.vq_cent[g0 + u][tid];
+            chw[u] = *(const uint32_t*)H.vq_chan[g0 + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c0 = chw[u] & 255, c1 = (chw[u] >> 8) & 255, c2 = (chw[u] >> 16) & 255, c3 = chw[u] >> 24;
+            for (int m = 0; m < GC; ++m) {
+                const LDS_AS float* qm = qv + m * D;
+                lut[(m * n_g + g0 + u) * kVqSize + tid] =
+                    fmaf(qm[c3], zc[u].w, fmaf(qm[c2], zc[u].z, fmaf(qm[c1], zc[u].y, qm[c0] * zc[u].x)));
+            }
         }
     }
     // value columns of this wave's blocks cb = w, w + 4, ... (at most 6)
@@ -1016,44 +1038,52 @@ __global__ __launch_bounds__(256) void vq_decode_kernel(const DevHead* __restric
     lds_barrier();
     // ---- the tiles
     for (int64_t t = t_begin; t < t_end; ++t) {
-        const int cur = (int)((t - t_begin) & 1);
-        if (t + 1 < t_end) {
-            issue(t + 1, cur ^ 1);
-            wait_vm(nlw);
-        } else {
-            wait_vm(0);
-        }
+        const int cur = (int)((t - t_begin) % NB);
+        // refill the buffer of the previous tile (every wave is past it), then wait for this
+        // tile's copies: the ones issued after them may stay in flight
+        if (t + NB - 1 < t_end) issue(t + NB - 1, (cur + NB - 1) % NB);
+        wait_vm(nlw * (int)min<int64_t>(NB - 1, t_end - 1 - t));
         lds_barrier();
-        const LDS_AS uint8_t* tb = sm + (cur ? L.tb1 : L.tb0);
+        const LDS_AS uint8_t* tb = sm + L.ring + cur * L.tba;
         if (w < GC) {
             const int64_t tok = t * kTile + lane;
             float s = 0.0f;
             const LDS_AS float* lm = lut + w * n_g * kVqSize;
-            for (int r = 0; r < n_g / 4; ++r) {
-                const uint32_t wd = ((const LDS_AS uint32_t*)tb)[64 * r + lane] ^ 0x80808080u;
+            if constexpr (NG > 0) {
+                uint32_t wd[NG / 4];
 #pragma unroll
-                for (int b = 0; b < 4; ++b) s += lm[(4 * r + b) * kVqSize + ((wd >> (8 * b)) & 255u)];
+                for (int r = 0; r < NG / 4; ++r) wd[r] = ((const LDS_AS uint32_t*)tb)[64 * r + lane] ^ 0x80808080u;
+                float e[NG];
+#pragma unroll
+                for (int g = 0; g < NG; ++g) e[g] = lm[g * kVqSize + ((wd[g >> 2] >> (8 * (g & 3))) & 255u)];
+#pragma unroll
+                for (int g = 0; g < NG; ++g) s += e[g];
+            } else {
+                for (int r = 0; r < n_g / 4; ++r) {
+                    const uint32_t wd = ((const LDS_AS uint32_t*)tb)[64 * r + lane] ^ 0x80808080u;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) s += lm[(4 * r + b) * kVqSize + ((wd >> (8 * b)) & 255u)];
+                }
             }
             const bool valid = tok < len;
             const float mt = wave_max(valid ? s : -INFINITY);
             const float m_new = fmaxf(m_run, mt);
             const float al = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-            const float p = valid ? __builtin_amdgcn_exp2f(s - m_new) : 0.0f;
+            const float p = valid ? (float)(_Float16)__builtin_amdgcn_exp2f(s - m_new) : 0.0f;
             l_run = l_run * al + wave_sum(p);
             m_run = m_new;
             pb[w * 64 + lane] = p;
             if (lane == 0) alpha[w] = al;
         }
         lds_barrier();
+        // MFMA i, lane group kk, k-slot e: token 16 kk + 4 i + e
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
         const int mrow = lane & 15, kk = lane >> 4;
-        float A[16];
+        h4 A[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const f4 x = mrow < 4 ? *(const LDS_AS f4*)&pb[mrow * 64 + 16 * kk + 4 * v] : f4{0.0f, 0.0f, 0.0f, 0.0f};
-            A[4 * v] = x[0];
-            A[4 * v + 1] = x[1];
-            A[4 * v + 2] = x[2];
-            A[4 * v + 3] = x[3];
+            A[v] = h4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
         }
         const f4 al4 = kk == 0 ? *(const LDS_AS f4*)alpha : f4{1.0f, 1.0f, 1.0f, 1.0f};
 #pragma unroll
@@ -1063,9 +1093,11 @@ __global__ __launch_bounds__(256) void vq_decode_kernel(const DevHead* __restric
             const uint32_t off = vcol[r] & 0xFFFFu, msk = (vcol[r] >> 16) * 0x01010101u;
             const u32x4 by = *(const LDS_AS u32x4*)(tb + 8 * BK + off + 16 * kk);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int bv = (int)(int8_t)(((by[i >> 2] & msk) >> (8 * (i & 3))) & 255u);
-                acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[i], (float)bv, acc[r], 0, 0, 0);
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t x = by[i] & msk;
+                const h4 B = h4{(_Float16)(int8_t)(x & 255u), (_Float16)(int8_t)((x >> 8) & 255u),
+                                (_Float16)(int8_t)((x >> 16) & 255u), (_Float16)(int8_t)(x >> 24)};
+                acc[r] = __builtin_amdgcn_mfma_f32_16x16x16f16(A[i], B, acc[r], 0, 0, 0);
             }
         }
         lds_barrier();
@@ -1293,17 +1325,17 @@ extern "C" int aatc_profile_end(float* ms, int32_t* n_out) {
     return rc;
 }
 
-template <int D>
+template <int D, int NG>
 int launch_vq_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* blob, uint8_t* cache,
                      const int32_t* ids, const int64_t* lens, const uint16_t* q, float* part, float* out) {
     const DecodeArgs& a = p.args;
     if (p.lds > 64 * 1024)
-        HIP_TRY(hipFuncSetAttribute((const void*)vq_decode_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        HIP_TRY(hipFuncSetAttribute((const void*)vq_decode_kernel<D, NG>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                     (int)p.lds));
     hipEvent_t e0, e1;
     profile_slot(e0, e1);
     if (e0) HIP_TRY(hipEventRecord(e0, st));
-    hipLaunchKernelGGL((vq_decode_kernel<D>), dim3(p.wg_per_head * ((a.G + 3) / 4), a.n_kv, n_seqs), dim3(256), p.lds,
+    hipLaunchKernelGGL((vq_decode_kernel<D, NG>), dim3(p.wg_per_head * ((a.G + 3) / 4), a.n_kv, n_seqs), dim3(256), p.lds,
                        st, blob, cache, a, ids, lens, q, part);
     HIP_TRY(hipGetLastError());
     if (e1) HIP_TRY(hipEventRecord(e1, st));
@@ -1363,8 +1395,13 @@ static int decode_impl(const aatc_codebook* cb, const void* d_blob, const aatc_c
     a.v_new = v_new;
     if (p.vq) {
         if (k_new) return set_error(AATC_ERR_UNSUPPORTED, "fused append with vector-quantized keys");
-        return cb->d == 64 ? launch_vq_decode<64>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, part, out)
-                           : launch_vq_decode<128>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, part, out);
+        const int ng = cb->heads[0].vq_groups;
+        if (cb->d == 64)
+            return ng == 16 ? launch_vq_decode<64, 16>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, part, out)
+                            : launch_vq_decode<64, 0>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, part, out);
+        return ng == 32 ? launch_vq_decode<128, 32>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, part, out)
+               : ng == 16 ? launch_vq_decode<128, 16>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, part, out)
+                          : launch_vq_decode<128, 0>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, part, out);
     }
 #define AATC_DECODE_CASE(rb_, nqm_, nvb_)                                                                    \
     if (p.v.rb == rb_ && p.v.nqm == nqm_ && p.v.nvb == nvb_)                                                 \

@@ -120,6 +120,8 @@ WORKLOADS: Dict[str, Workload] = {
     # vector-quantized keys at 2.0 bits/element (one byte per group of 4 coefficients):
     # a small head, and the Llama layer at 128k context
     "vq_tiny": Workload("vq_tiny", 8, 64, 1, 4, 1, 1, 512, 2.0, 2048, 256, "bf16"),
+    # ... at 1.0 bit/element: 8 groups code the 32 coefficients of largest weight
+    "vq_low": Workload("vq_low", 10, 64, 1, 4, 1, 1, 512, 1.0, 2048, 256, "bf16"),
     "llama_vq_128k": Workload("llama_vq_128k", 9, 128, 8, 32, 1, 1, 131072, 2.0, 8192, 256, "bf16"),
 }
 

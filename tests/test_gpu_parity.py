@@ -32,7 +32,7 @@ def torch():
 
 def _device_codebook(q, torch, case):
     a = case.codebook_arrays()
-    if a["vq"] is not None:
+    if "vq" in a:
         v = a["vq"]
         cb = q.codebook_create_vq(case.d, 1, case.n_kv, case.group, a["UK"], a["UV"], a["muK"], a["muV"],
                                   v["groups"], v["scale32"], v["cent32"], a["bV"], a["stepV"])

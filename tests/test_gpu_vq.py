@@ -40,6 +40,7 @@ def _encode_bf16(lib, torch, case, chunks=None):
 @pytest.mark.parametrize("wname,ctx,n_kv,chunks", [
     ("vq_tiny", 512, None, [512]),
     ("vq_tiny", 512, None, [1, 63, 200, 248]),
+    ("vq_low", 300, None, [300]),
     ("llama_vq_128k", 333, 2, [1, 127, 205]),
 ])
 def test_vq_encode_coeffs_bit_exact(lib, torch, wname, ctx, n_kv, chunks):
@@ -98,6 +99,7 @@ def test_vq_encode_end_to_end(lib, torch, wname, ctx, n_kv, chunks):
     ("vq_tiny", 512, None, 1, [1]),
     ("vq_tiny", 512, None, 1, [65]),
     ("vq_tiny", 512, None, 3, [512, 1, 300]),
+    ("vq_low", 512, None, 3, [512, 77, 300]),
     ("llama_vq_128k", 1000, 2, 1, [1000]),
     ("llama_vq_128k", 4096, 2, 2, [4096, 2049]),
 ])

@@ -89,14 +89,15 @@ class Case:
 
     def codebook_arrays(self):
         cbs = self.cbs
-        return dict(UK=np.stack([c.UK for c in cbs]), UV=np.stack([c.UV for c in cbs]),
-                    muK=np.stack([c.muK for c in cbs]), muV=np.stack([c.muV for c in cbs]),
-                    bK=np.stack([c.bK for c in cbs]), bV=np.stack([c.bV for c in cbs]),
-                    stepK=np.stack([c.stepK for c in cbs]), stepV=np.stack([c.stepV for c in cbs]),
-                    vq=None if cbs[0].vq is None else dict(
-                        groups=np.stack([c.vq.groups for c in cbs]),
-                        scale32=np.stack([c.vq.scale32 for c in cbs]),
-                        cent32=np.stack([c.vq.cent32 for c in cbs])))
+        out = dict(UK=np.stack([c.UK for c in cbs]), UV=np.stack([c.UV for c in cbs]),
+                   muK=np.stack([c.muK for c in cbs]), muV=np.stack([c.muV for c in cbs]),
+                   bK=np.stack([c.bK for c in cbs]), bV=np.stack([c.bV for c in cbs]),
+                   stepK=np.stack([c.stepK for c in cbs]), stepV=np.stack([c.stepV for c in cbs]))
+        if cbs[0].vq is not None:  # vector-quantized keys
+            out["vq"] = dict(groups=np.stack([c.vq.groups for c in cbs]),
+                             scale32=np.stack([c.vq.scale32 for c in cbs]),
+                             cent32=np.stack([c.vq.cent32 for c in cbs]))
+        return out
 
     def coeffs(self, s):
         """Oracle fp32 KLT coefficients [ctx, n_kv, 2, d] of sequence s."""
