@@ -273,6 +273,9 @@ int aatc_decode_workspace_bytes(const aatc_codebook* cb, int32_t n_seqs, int64_t
  * transform ("KV Cache Compression Through the Lens of Transform Coding", Methodology;
  * "Attention-Aware Transform Coding Guide", KLT section: q.k = (U_K^T q).(U_K^T k)).
  * At most 65535 sequences per call (CAPACITY beyond).
+ * With vector-quantized keys (aatc_codebook_create_vq, key_quantizer = 1) the scores come
+ * from per-(query head, group) tables over the codebooks (a token's score is the sum of
+ * its groups' entries); the workspace and merge are the same.
  * Errors: INVALID_ARG, CAPACITY, WORKSPACE, HIP. */
 int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
                           int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
@@ -289,7 +292,8 @@ int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob, const aat
  * workgroup that owns the token's tile codes it (the encoder's MFMA projection and
  * quantizer) and places its records in its copy of the tile, so the step needs no ordering
  * between the write and the tile's stream ("Spend Bits Where Queries Look", abstract:
- * decoding reads the whole cache at every step). */
+ * decoding reads the whole cache at every step).  UNSUPPORTED for codebooks with
+ * vector-quantized keys (append with aatc_encode, then decode). */
 int aatc_decode_attention_append(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
                                  int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                                  const int64_t* seq_lens, int64_t max_len, const uint16_t* k_new,
