@@ -120,7 +120,8 @@ def cpu_baseline(wname: str, n_tokens: int = 16384):
                                         key_quantizer="vq", vq_normals=synth.vq_normals(w, 0, VQ_TRAIN),
                                         vq_iters=VQ_ITERS)
     else:
-        cb = oracle.build_head_codebook(oracle.head_stats(K, V, Q), w.avg_bits)
+        # the oracle encodes the library's packed layout: key records in whole 32-bit words
+        cb = oracle.build_head_codebook(oracle.head_stats(K, V, Q), w.avg_bits, key_align=32)
     Kc, Vc = synth.cache_kv(w, hm, 0, 0, 0, n_tokens)
     kf = synth.bf16_bits_to_f64(synth.to_bf16_bits(Kc))
     vf = synth.bf16_bits_to_f64(synth.to_bf16_bits(Vc))

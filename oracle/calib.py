@@ -207,17 +207,20 @@ def allocate_bits(xK: np.ndarray, xV: np.ndarray, total_bits: int, max_bits: int
     gives the exact-budget optimum of the separable convex problem (ties: keys before
     values, then lower channel index, then lower k).
 
-    key_align: the keys' total bits must be a multiple of key_align (the packed layout
-    keeps each token's key record in whole 32-bit words, key_align = 32).  The result is
-    the optimum over such splits: for every admissible key budget B_K the key and value
-    sub-problems are solved exactly, and the split of least total cost is taken (ties:
-    the smaller B_K).  joint=False gives keys and values total_bits/2 each.
+    key_align = 1 (the default) is the method itself: one budget over all channels.
+    key_align > 1 is a storage constraint named by the caller (a layout holding key
+    records in whole words of key_align bits): the keys' total must be a multiple of it,
+    and the result is the optimum over such splits - for every admissible key budget B_K
+    the key and value sub-problems are solved exactly and the split of least total cost
+    is taken (ties: the smaller B_K).  joint=False gives keys and values total_bits/2
+    each.
     """
     xK = np.asarray(xK, np.float64)
     xV = np.asarray(xV, np.float64)
     d = xK.size
     if not joint:
-        assert total_bits % 2 == 0 and (total_bits // 2) % key_align == 0
+        if total_bits % 2 or (total_bits // 2) % key_align:
+            raise ValueError("separate budgets need total_bits/2 a multiple of key_align")
         return (_greedy([(0, xK)], total_bits // 2, max_bits)[0],
                 _greedy([(1, xV)], total_bits // 2, max_bits)[1])
     assert 0 <= total_bits <= 2 * d * max_bits
@@ -379,22 +382,26 @@ def step_table(max_bits: int = 8) -> np.ndarray:
     return _STEP_CACHE[max_bits]
 
 
-KEY_ALIGN = 32  # key bits per token are kept a multiple of one 32-bit word
-
-
 def build_head_codebook(stats: dict, avg_bits: float, max_bits: int = 8,
                         joint: bool = True, key_transform: str = "klt",
                         key_quantizer: str = "scalar", vq_normals: np.ndarray | None = None,
-                        vq_iters: int = 20) -> HeadCodebook:
+                        vq_iters: int = 20, key_align: int = 1) -> HeadCodebook:
     """Calibrate one head: KLT of both covariances (or, for the keys, the attention-optimal
     transform of nova_key_transform), weights, exact-budget integer bits with total
-    2 d avg_bits (a multiple of 8; key bits a multiple of 32), and fp32 steps
-    step_b * sqrt(coefficient variance).
+    2 d avg_bits (a multiple of 8), and fp32 steps step_b * sqrt(coefficient variance).
+
+    The bits are the exact-budget optimum of p2's water-filling over all 2d channels
+    (key_align = 1).  key_align > 1 is a storage constraint that the caller names: a
+    packed layout that keeps each token's key record in whole words of key_align bits
+    can only hold key totals that are multiples of it, and allocate_bits then returns
+    the best allocation among those (its cost over the unconstrained optimum is pinned by
+    the tests).
 
     key_quantizer "vq" (NOVA-KV abstract; readings in oracle.vq): separate budgets of
     d avg_bits bits for keys and values; the key bits go to d avg_bits / 8 groups of four
     coefficients with one 256-word Lloyd codebook each (so avg_bits <= 2 and d avg_bits a
-    multiple of 32), trained on vq_normals; the values keep the scalar quantizer."""
+    multiple of 32: whole groups of four one-byte indices), trained on vq_normals; the
+    values keep the scalar quantizer."""
     d = stats["d"]
     total = 2.0 * d * avg_bits
     B = int(round(total))
@@ -418,17 +425,17 @@ def build_head_codebook(stats: dict, avg_bits: float, max_bits: int = 8,
         if joint:
             raise ValueError("vector-quantized keys take separate key and value budgets")
         BK = B // 2
-        if BK % KEY_ALIGN or 4 * (BK // 8) > d:
+        if BK % 32 or 4 * (BK // 8) > d:
             raise ValueError("vector-quantized keys need d*avg_bits a multiple of 32 and "
                              "avg_bits <= 2")
         from .vq import equal_volume_groups, group_codebooks, vq_scales
-        _, bV = allocate_bits(xK, xV, B, max_bits, False, key_align=KEY_ALIGN)
+        _, bV = allocate_bits(xK, xV, B, max_bits, False)
         bK = np.zeros(d, np.int64)
         groups = equal_volume_groups(xK, BK // 8)
         w = np.where(lamK > 0, xK / np.where(lamK > 0, lamK, 1.0), 0.0)
         vq = VQKeys(groups, vq_scales(w), group_codebooks(xK, groups, vq_normals, vq_iters))
     elif key_quantizer == "scalar":
-        bK, bV = allocate_bits(xK, xV, B, max_bits, joint, key_align=KEY_ALIGN)
+        bK, bV = allocate_bits(xK, xV, B, max_bits, joint, key_align=key_align)
     else:
         raise ValueError(f"unknown key quantizer {key_quantizer!r}")
     st = step_table(max_bits)

@@ -7,6 +7,7 @@ import pytest
 import oracle
 import quantized_attention_klt_amd as q
 import synth
+from util import LAYOUT_KEY_ALIGN
 
 
 def _samples(wname, head=0, layer=0):
@@ -34,7 +35,7 @@ def test_calibrate_matches_oracle(wname, joint):
     w, K, V, Q = _samples(wname, head=1 if w_name_has_heads(wname) else 0)
     st = oracle.head_stats(K.astype(np.float64), V.astype(np.float64), Q.astype(np.float64))
     cb = q.calibrate([st], w.d, 1, 1, w.group, w.avg_bits, joint=joint)
-    ref = oracle.build_head_codebook(st, w.avg_bits, joint=joint)
+    ref = oracle.build_head_codebook(st, w.avg_bits, joint=joint, key_align=LAYOUT_KEY_ALIGN)
     h = cb.head(0)
     lm = ref.lamK.max()
     assert np.abs(h["lamK"] - ref.lamK).max() <= 1e-10 * lm
@@ -60,7 +61,7 @@ def test_calibrate_attention_optimal_keys_matches_oracle(wname):
     w, K, V, Q = _samples(wname)
     st = oracle.head_stats(K.astype(np.float64), V.astype(np.float64), Q.astype(np.float64))
     cb = q.calibrate([st], w.d, 1, 1, w.group, w.avg_bits, key_transform="nova")
-    ref = oracle.build_head_codebook(st, w.avg_bits, key_transform="nova")
+    ref = oracle.build_head_codebook(st, w.avg_bits, key_transform="nova", key_align=LAYOUT_KEY_ALIGN)
     h = cb.head(0)
     assert np.abs(h["lamK"] - ref.lamK).max() <= 1e-10 * ref.lamK.max()
     gap = np.minimum(np.r_[np.inf, -np.diff(ref.lamK)], np.r_[-np.diff(ref.lamK), np.inf])
@@ -88,7 +89,7 @@ def w_name_has_heads(wname):
 def _oracle_codebook(wname="tiny"):
     w, K, V, Q = _samples(wname)
     st = oracle.head_stats(K.astype(np.float64), V.astype(np.float64), Q.astype(np.float64))
-    return w, oracle.build_head_codebook(st, w.avg_bits)
+    return w, oracle.build_head_codebook(st, w.avg_bits, key_align=LAYOUT_KEY_ALIGN)
 
 
 def test_codebook_create_and_persist(tmp_path):

@@ -189,25 +189,100 @@ def test_key_aligned_allocation_brute_force(seed):
 
 
 def test_integer_allocation_properties():
+    """The method's allocation (one water level over all 2d channels, exact budget):
+    every channel within one bit of the joint continuous water-filling, monotone in the
+    weights within keys and within values."""
     w = synth.WORKLOADS["llama_32k"]
     hm = synth.head_model(w, 0, 3)
     K, V, Q = synth.calibration_samples(w, hm, 0, 3)
     st = oracle.head_stats(K, V, Q)
     cb = oracle.build_head_codebook(st, 2.75)
     assert cb.bK.sum() + cb.bV.sum() == 704
-    assert cb.bK.sum() % 32 == 0
     assert cb.bK.min() >= 0 and cb.bK.max() <= 8 and cb.bV.max() <= 8
-    # monotone in x within keys and within values
     for x, b in ((cb.xK, cb.bK), (cb.xV, cb.bV)):
         o = np.argsort(-x, kind="stable")
         assert np.all(np.diff(b[o]) <= 0)
-        # within one bit of the continuous water-filling of the same sub-budget
-        theta, R = oracle.waterfill_theta(x, int(b.sum()))
-        act = (R > 0) & (R < 8)
-        assert np.all(np.abs(b[act] - R[act]) <= 1.0 + 1e-9)
-    # the key/value split moves at most 16 bits against the unaligned optimum
-    bK0, bV0 = oracle.allocate_bits(cb.xK, cb.xV, 704)
-    assert abs(int(cb.bK.sum()) - int(bK0.sum())) <= 16
+    theta, R = oracle.waterfill_theta(np.concatenate([cb.xK, cb.xV]), 704)
+    b = np.concatenate([cb.bK, cb.bV])
+    assert abs(R.sum() - 704) < 1e-6
+    assert np.all(np.abs(b - R) <= 1.0 + 1e-9), np.abs(b - R).max()
+    assert abs(theta / cb.theta - 1) < 1e-12
+
+
+def _alloc_cost(xK, xV, bK, bV):
+    return float(np.sum(xK * 4.0 ** -bK.astype(np.float64)) + np.sum(xV * 4.0 ** -bV.astype(np.float64)))
+
+
+def _shift_bound(xK, xV, bK, bV, align, max_bits=8):
+    """Cost of the best of the two aligned allocations reached from (bK, bV) by moving the
+    key total's remainder mod `align` to the values or the missing bits from the values to
+    the keys, one marginal bit at a time (the aligned optimum can only be cheaper)."""
+    def moved(bK, bV, n, to_keys):
+        bK, bV = bK.copy(), bV.copy()
+        for _ in range(n):
+            src, dst, xs, xd = (bV, bK, xV, xK) if to_keys else (bK, bV, xK, xV)
+            give = np.where(src > 0, xs * 4.0 ** -(src - 1.0), np.inf)  # gain lost by removing a bit
+            take = np.where(dst < max_bits, xd * 4.0 ** -dst.astype(np.float64), -np.inf)  # gain of adding one
+            src[int(np.argmin(give))] -= 1
+            dst[int(np.argmax(take))] += 1
+        return _alloc_cost(xK, xV, bK, bV)
+    r = int(bK.sum()) % align
+    if r == 0:
+        return _alloc_cost(xK, xV, bK, bV)
+    return min(moved(bK, bV, r, False), moved(bK, bV, align - r, True))
+
+
+def _workload_heads():
+    """(workload, layer, head) of every scalar-key head the workloads calibrate."""
+    out = []
+    for name in ("tiny", "llama_32k", "llama_loop", "qwen_128k", "llama_batch", "edge_g16", "edge_rate"):
+        w = synth.WORKLOADS[name]
+        out += [(name, layer, h) for layer in range(w.n_layers) for h in range(w.n_kv)]
+    return out
+
+
+def _one_blas_thread():
+    from threadpoolctl import threadpool_limits
+    global _LIMITS
+    _LIMITS = threadpool_limits(1)
+
+
+def _aligned_cost_of_head(args):
+    name, layer, h = args
+    w = synth.WORKLOADS[name]
+    hm = synth.head_model(w, layer, h)
+    st = oracle.head_stats(*synth.calibration_samples(w, hm, layer, h))
+    lamK, UK = oracle.klt(st["SigK"])
+    lamV, UV = oracle.klt(st["SigV"])
+    xK, xV = oracle.channel_weights(st, UK, lamK, UV, lamV)
+    B = int(round(2 * w.d * w.avg_bits))
+    bK, bV = oracle.allocate_bits(xK, xV, B)
+    aK, aV = oracle.allocate_bits(xK, xV, B, key_align=32)
+    free, aligned = _alloc_cost(xK, xV, bK, bV), _alloc_cost(xK, xV, aK, aV)
+    return name, int(aK.sum()), int(aK.sum() + aV.sum()) - B, free, aligned, _shift_bound(xK, xV, bK, bV, 32)
+
+
+def test_layout_aligned_allocation_cost_on_every_workload_head():
+    """The library's layout stores key records in whole 32-bit words, so its codebooks use
+    the best allocation whose key total is a multiple of 32 (a storage constraint, not part
+    of the method).  On every head of every scalar-key workload (calibrated with the
+    workload's own recipe): the budget stays exact, the constrained optimum is no worse
+    than the two nearest single-bit shifts of the method's allocation, and its modelled
+    distortion sum_j x_j 4^-b_j exceeds the method's optimum by at most 3 %, and by at most
+    2 % on the 128-dimensional heads (measured over 388 heads: worst 2.58 % on the tiny
+    64-dimensional head, 1.63 % on a Qwen-shaped head; medians 0.4-0.7 %)."""
+    import multiprocessing as mp
+    heads = _workload_heads()
+    with mp.get_context("fork").Pool(min(8, os.cpu_count() or 1), initializer=_one_blas_thread) as pool:
+        res = pool.map(_aligned_cost_of_head, heads, chunksize=8)
+    worst = {}
+    for name, bk, dB, free, aligned, bound in res:
+        assert bk % 32 == 0 and dB == 0
+        assert free <= aligned * (1 + 1e-12)
+        assert aligned <= bound * (1 + 1e-12)
+        worst[name] = max(worst.get(name, 0.0), aligned / free - 1)
+    assert max(worst.values()) <= 0.03, worst
+    assert max(v for k, v in worst.items() if synth.WORKLOADS[k].d == 128) <= 0.02, worst
 
 
 def test_uniform_weights_give_uniform_bits():

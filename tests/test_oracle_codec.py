@@ -6,6 +6,7 @@ import pytest
 
 import oracle
 import synth
+from util import LAYOUT_KEY_ALIGN
 
 
 # ---------------------------------------------------------------- quantizer
@@ -258,7 +259,7 @@ def test_decode_attention_equals_dequantized_attention():
     w = synth.WORKLOADS["tiny"]
     hm = synth.head_model(w, 0, 0)
     st = oracle.head_stats(*synth.calibration_samples(w, hm, 0, 0))
-    cb = oracle.build_head_codebook(st, w.avg_bits)
+    cb = oracle.build_head_codebook(st, w.avg_bits, key_align=LAYOUT_KEY_ALIGN)
     K, V = synth.cache_kv(w, hm, 0, 0, 0, 100)
     cache, cK, cV = oracle.encode_cache(K, V, cb)
     q = synth.decode_queries(w, [hm], 0, 0)
@@ -283,7 +284,7 @@ def test_reconstruction_error_within_half_step():
     w = synth.WORKLOADS["tiny"]
     hm = synth.head_model(w, 0, 0)
     st = oracle.head_stats(*synth.calibration_samples(w, hm, 0, 0))
-    cb = oracle.build_head_codebook(st, w.avg_bits)
+    cb = oracle.build_head_codebook(st, w.avg_bits, key_align=LAYOUT_KEY_ALIGN)
     K, V = synth.cache_kv(w, hm, 0, 0, 0, 256)
     c = oracle.transform_coeffs(K, cb.muK, cb.UK)
     codes = oracle.quantize(c, cb.inv_step("K"), cb.bK)

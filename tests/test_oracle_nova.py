@@ -15,6 +15,7 @@ import pytest
 
 import oracle
 import synth
+from util import LAYOUT_KEY_ALIGN
 
 
 def _tiny_stats(head=0):
@@ -72,7 +73,7 @@ def test_general_key_transform_reconstruction():
     """decode_attention over a packed cache = attention over keys rebuilt as
     mu + c_hat T^{-1}, with T^{-1} from a general matrix inverse."""
     w, hm, K, st = _tiny_stats()
-    cb = oracle.build_head_codebook(st, w.avg_bits, key_transform="nova")
+    cb = oracle.build_head_codebook(st, w.avg_bits, key_transform="nova", key_align=LAYOUT_KEY_ALIGN)
     L = 200
     Kc, Vc = synth.cache_kv(w, hm, 0, 0, 0, L)
     kf = synth.bf16_bits_to_f64(synth.to_bf16_bits(Kc))
@@ -100,7 +101,7 @@ def test_smaller_attention_error_than_the_klt(head):
     exact = oracle.attention(qs, kf, vf)
     err = {}
     for kt in ("klt", "nova"):
-        cb = oracle.build_head_codebook(st, w.avg_bits, key_transform=kt)
+        cb = oracle.build_head_codebook(st, w.avg_bits, key_transform=kt, key_align=LAYOUT_KEY_ALIGN)
         cache, _, _ = oracle.encode_cache(kf, vf, cb)
         err[kt] = ((oracle.decode_attention(cache, cb, qs, L) - exact) ** 2).sum(1).mean()
     assert err["nova"] < 0.9 * err["klt"], err

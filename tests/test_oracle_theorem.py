@@ -88,3 +88,65 @@ def test_theorem_in_klt_domain_with_quantizer_noise():
     # the off-diagonal native-domain covariance is not captured by natK; the KLT-domain
     # expression is the exact first-order one and is what the allocation uses
     assert DK_klt > 0 and DK_nat > 0
+
+
+def _calibration_head(nq=64):
+    """Tiny workload, head 0: calibration keys/values and 64 calibration queries per query
+    head, their statistics, both KLTs and the channel weights from channel_weights."""
+    w = synth.WORKLOADS["tiny"]
+    hm = synth.head_model(w, 0, 0)
+    K, V, Q = synth.calibration_samples(w, hm, 0, 0)
+    Q = Q.reshape(w.group, -1, w.d)[:, :nq].reshape(-1, w.d)
+    st = oracle.head_stats(K, V, Q)
+    lamK, UK = oracle.klt(st["SigK"])
+    lamV, UV = oracle.klt(st["SigV"])
+    xK, xV = oracle.channel_weights(st, UK, lamK, UV, lamV)
+    return K, V, Q, st, lamK, UK, lamV, UV, xK, xV
+
+
+def _mean_distortion(Q, K, V, eK, eV, trials, rng):
+    """Monte Carlo over independent draws: per trial, the mean over the calibration queries
+    of ||o - o_hat||^2 with KLT-domain errors eK(rng), eV(rng) added to every token."""
+    o0 = oracle.attention(Q, K, V)
+    D = np.array([((oracle.attention(Q, K + eK(rng), V + eV(rng)) - o0) ** 2).sum(1).mean()
+                  for _ in range(trials)])
+    return D.mean(), D.std(ddof=1) / np.sqrt(trials)
+
+
+def test_channel_weights_predict_mean_distortion_over_calibration_queries():
+    """p2 "Theorem: Additive Error Decomposition" averaged over the calibration queries:
+    with KLT-domain errors of variance s_j^2 on every token, the mean over those queries of
+    E||o - o_hat||^2 is sum_j s_j^2 x_j / lambda_j with the weights of channel_weights -
+    to first order for keys, exactly for values.  The key weights must be the query average
+    of the product g(q) q q^T: the same check with M_Q = mean(g) mean(q q^T) misses by many
+    standard errors, so this pin tells the two readings apart."""
+    K, V, Q, st, lamK, UK, lamV, UV, xK, xV = _calibration_head()
+    n, d = K.shape
+    eps = 0.01
+    zero = lambda rng: 0.0
+    rng = np.random.default_rng(11)
+    # keys: every channel at eps^2 lambda_j, and a random subset of channels at one variance
+    sub = rng.choice(d, 6, replace=False)
+    for var in (eps ** 2 * lamK, np.where(np.isin(np.arange(d), sub), 0.05 * eps ** 2 * lamK[0], 0.0)):
+        sd = np.sqrt(var)
+        m, se = _mean_distortion(Q, K, V, lambda r: (r.standard_normal((n, d)) * sd) @ UK.T, zero, 100, rng)
+        pred = float((var * xK / lamK).sum())
+        assert abs(m - pred) < 4 * se + 0.01 * pred, (m, se, pred)
+    # the product of expectations would predict a different distortion
+    o, A = None, None
+    s = Q @ K.T / np.sqrt(d)
+    A = np.exp(s - s.max(1, keepdims=True))
+    A /= A.sum(1, keepdims=True)
+    o = A @ V
+    g = np.einsum("qi,qi->q", A * A, ((V[None, :, :] - o[:, None, :]) ** 2).sum(2))
+    mut = dict(st, MQ=g.mean() * (Q.T @ Q) / Q.shape[0])
+    xKm, _ = oracle.channel_weights(mut, UK, lamK, UV, lamV)
+    var = eps ** 2 * lamK
+    m, se = _mean_distortion(Q, K, V, lambda r: (r.standard_normal((n, d)) * np.sqrt(var)) @ UK.T, zero, 100,
+                             np.random.default_rng(12))
+    assert abs(m - float((var * xKm / lamK).sum())) > 8 * se
+    # values: the value term is quadratic in the errors, so the prediction is exact
+    varV = eps ** 2 * lamV
+    m, se = _mean_distortion(Q, K, V, zero, lambda r: (r.standard_normal((n, d)) * np.sqrt(varV)) @ UV.T, 100,
+                             np.random.default_rng(13))
+    assert abs(m - float((varV * xV / lamV).sum())) < 4 * se

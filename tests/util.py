@@ -6,6 +6,10 @@ import numpy as np
 import oracle
 import synth
 
+# The library's packed layout keeps a token's key record in whole 32-bit words, so every
+# codebook the GPU path is fed is calibrated with that storage constraint named.
+LAYOUT_KEY_ALIGN = 32
+
 
 class Case:
     """Oracle codebooks and synthetic K/V/Q for n_kv heads of one layer of workload w."""
@@ -35,7 +39,8 @@ class Case:
                     key_quantizer="vq", vq_normals=synth.vq_normals(w, layer, vq_train), vq_iters=vq_iters))
             else:
                 self.cbs.append(oracle.build_head_codebook(oracle.head_stats(K, V, Q), w.avg_bits,
-                                                           key_transform=key_transform))
+                                                           key_transform=key_transform,
+                                                           key_align=LAYOUT_KEY_ALIGN))
         # cached K/V: bf16 bits [n_seqs, ctx, n_kv, d] and their float64 values
         self.k_bits = np.zeros((n_seqs, ctx, self.n_kv, w.d), np.uint16)
         self.v_bits = np.zeros_like(self.k_bits)
