@@ -257,7 +257,8 @@ int aatc_encode_coeffs(const aatc_codebook* cb, const void* d_blob, const aatc_c
                        int32_t layer, int32_t seq, int64_t start_pos, int64_t n_tokens,
                        const float* coeffs, void* stream);
 
-/* Workspace bytes for aatc_decode_attention with n_seqs sequences of length <= max_len. */
+/* Workspace bytes for aatc_decode_attention with n_seqs sequences of length <= max_len: a
+ * 1 KiB block of arrival counters followed by the split partials. */
 int aatc_decode_workspace_bytes(const aatc_codebook* cb, int32_t n_seqs, int64_t max_len,
                                 size_t* bytes);
 
@@ -266,11 +267,15 @@ int aatc_decode_workspace_bytes(const aatc_codebook* cb, int32_t n_seqs, int64_t
  * kv-head floor(h / G).  seq_ids [n_seqs] int32 and seq_lens [n_seqs] int64 are DEVICE
  * arrays (1 <= seq_lens[s] <= max_len <= max_tokens); max_len (host) sizes the grid.
  * q: device bf16 [n_seqs][H_q][d]; out: device float32 [n_seqs][H_q][d]; workspace:
- * device scratch of aatc_decode_workspace_bytes() bytes (256-byte aligned, no
- * initialisation needed) for the split partials.  Calls that share a workspace must not
- * overlap in time (same stream, or ordered).  Two kernels run on `stream`: split decode
- * over the packed tiles (each workgroup transforms the queries itself), merge + inverse
- * transform ("KV Cache Compression Through the Lens of Transform Coding", Methodology;
+ * device scratch of aatc_decode_workspace_bytes() bytes (256-byte aligned) for the split
+ * partials and their arrival counters.  It must be zero-filled once before its first use
+ * (e.g. at allocation); every call leaves the counters at zero again.  Calls that share a
+ * workspace must not overlap in time (same stream, or ordered).  The split decode over the
+ * packed tiles runs as one kernel on `stream` (each workgroup transforms the queries
+ * itself; the last workgroup of each (sequence, kv-head) to finish merges the partials and
+ * applies the inverse transform), or, when a call has more than 256 (sequence, kv-head)
+ * pairs or more than 64 workgroups per pair, as that kernel followed by a merge kernel
+ * ("KV Cache Compression Through the Lens of Transform Coding", Methodology;
  * "Attention-Aware Transform Coding Guide", KLT section: q.k = (U_K^T q).(U_K^T k)).
  * At most 65535 sequences per call (CAPACITY beyond).
  * With vector-quantized keys (aatc_codebook_create_vq, key_quantizer = 1) the scores come

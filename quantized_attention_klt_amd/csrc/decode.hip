@@ -92,8 +92,9 @@ struct DecodeArgs {
     // LDS carve-up (bytes): slot k of wave w's ring at (k * 4 + w) * buf_bytes; the
     // prologue's scratch at off_scratch, beside the ring (early = nbw: every slot streams
     // from the start) or in its last nbw - early slots
-    int nbw, buf_bytes, early, off_scratch, off_ksched, off_rec;
+    int nbw, buf_bytes, early, off_scratch, off_ksched, off_rec, off_sync;
     int off_pbuf;  // per-wave probability operands [NW][RB KiB] when the key block is smaller, else -1
+    int fused;  // the last workgroup of each (sequence, kv-head) merges (no merge launch)
 };
 
 // LDS-only workgroup barrier: this wave's LDS operations are complete, then s_barrier.
@@ -110,6 +111,41 @@ __device__ __forceinline__ void lds_add_async(LDS_AS int* p, int v) {
 // LDS OR as an instruction of its own (see lds_add_async)
 __device__ __forceinline__ void lds_or_async(LDS_AS uint32_t* p, uint32_t v) {
     asm volatile("ds_or_b32 %0, %1" ::"v"(p), "v"(v) : "memory");
+}
+
+// LDS-counter meeting of a subset of the workgroup's waves (the others carry on): this wave's
+// LDS operations complete, lane 0 adds one arrival, then the wave waits until `target`
+// arrivals have been counted.  LDS operations complete in order, so data written before an
+// arrival is visible to every wave that has seen the count.
+__device__ __forceinline__ void q_wait(LDS_AS int* ctr, int target) {
+    while (*(volatile LDS_AS int*)ctr < target) __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void q_sync(LDS_AS int* ctr, int target, int lane) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) lds_add_async(ctr, 1);
+    while (*(volatile LDS_AS int*)ctr < target) __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
+}
+
+// Scalar loads of a head's record sizes (DevHead::BK, BV at byte offset 4), a sequence id and a
+// sequence length, waited for inside the same statement on the scalar counter only.
+__device__ __forceinline__ void load_head_and_sequence(const DevHead* hp, const int32_t* idp, const int64_t* lenp,
+                                                       int& BK, int& BV, int& seq, int64_t& len) {
+    static_assert(offsetof(DevHead, BK) == 4 && offsetof(DevHead, BV) == 8, "record sizes at bytes 4..11");
+    uint64_t kv, ln;
+    uint32_t sq;
+    asm volatile(
+        "s_load_dwordx2 %0, %3, 0x4\n\t"
+        "s_load_dword %1, %4, 0x0\n\t"
+        "s_load_dwordx2 %2, %5, 0x0\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&s"(kv), "=&s"(sq), "=&s"(ln)
+        : "s"(hp), "s"(idp), "s"(lenp));
+    BK = (int)(uint32_t)kv;
+    BV = (int)(uint32_t)(kv >> 32);
+    seq = (int)sq;
+    len = (int64_t)ln;
 }
 
 // wait until at most n of this wave's vector memory operations are outstanding (n is
@@ -292,12 +328,146 @@ __device__ __forceinline__ void append_block(const DevHead& H, const uint16_t* x
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// The merge done by the last workgroup of a (sequence, kv-head) to finish the split decode
+// (one launch for the whole call).  Its arithmetic is merge_kernel's (softmax merge of the W
+// partials, value coefficients from the columns, o = obias + U_V (step * A) / L) for the G
+// query heads of the kv-head at once.  Every global read is issued in one round: the partial
+// maxima, the partial rows (thread (c4, s) holds float4 c4 of partials s, s + S, ...), the
+// columns of U_V^T that thread (i, js) multiplies (rows js JR .. js JR + JR - 1 of column i)
+// and the channel tables; then reductions in LDS.
+// ---------------------------------------------------------------------------------------
+constexpr int kFuseMaxW = 64;       // partials per (sequence, kv-head) the last workgroup merges
+constexpr int kFuseMaxPairs = 256;  // (sequence, kv-head) pairs per fused call: one counter each
+constexpr int kFuseRows = 8;        // partial rows per thread and round
+constexpr size_t kCounterBytes = 4 * kFuseMaxPairs;  // the workspace's first bytes: arrival counters
+
+// LDS bytes of merge_last (beside nothing else: the ring is free by then)
+__host__ __device__ constexpr int merge_lds_bytes(int G, int PL, int D, int NT) {
+    return 4 * kFuseMaxW * 16 + 16 * NT + 4 * G * PL + 4 * G * D + 4 * (D / 8) * G * D;
+}
+constexpr int kCoherentLoad = 16;  // buffer-load cache policy sc1: coherent across the device's caches
+
+template <int D, int NVB, int NT>
+__device__ __forceinline__ void merge_last(const DevHead& H, const float* __restrict__ P, int W, int G, float* __restrict__ out,
+                           LDS_AS uint8_t* sm, int tid) {
+    constexpr int PL = kPartHead + 16 * NVB;
+    constexpr int JR = 8, JS = D / JR;  // row slices of U_V^T in the product (JS x D/4 threads)
+    static_assert(NT % D == 0 && JS * (D / 4) <= NT, "merge thread layout");
+    const int PW = G * PL;  // floats per partial
+    const int C4 = PW / 4, S = NT / C4;
+    const int c4 = tid % C4, sl = tid / C4;
+    const bool rowt = sl < S;
+    LDS_AS float* ew = (LDS_AS float*)sm;                     // [W][G] weights 2^(m - M)
+    LDS_AS f4* red = (LDS_AS f4*)(ew + kFuseMaxW * 16);       // [S][C4] slice sums
+    LDS_AS float* colv = (LDS_AS float*)(red + NT);           // [G][PL] merged rows
+    LDS_AS float* cbar = colv + G * PL;                       // [G][D] step * A / L
+    LDS_AS float* red2 = cbar + G * D;                        // [JS][G][D] product slices (16-byte aligned)
+    // ---- every global read of the merge.  The partials were written by other workgroups,
+    // possibly on other XCDs, with device-coherent stores; they are read with device-coherent
+    // loads (cache policy sc1), which need no cache invalidation.
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)P, (short)0, W * PW * 4, 0x00020000);
+    f4 X[kFuseRows];
+#pragma unroll
+    for (int k = 0; k < kFuseRows; ++k) {
+        const int w = sl + S * k;
+        X[k] = rowt && w < W ? __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          prs, 4 * (w * PW + 4 * c4), 0, kCoherentLoad))
+                             : f4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const int i = tid % D;                             // channel i (value coefficient, output)
+    const int i4 = tid % (D / 4), js = tid / (D / 4);  // product: outputs 4 i4 .. 4 i4 + 3 of row slice js
+    f4 U[JR];
+    if (js < JS) {
+#pragma unroll
+        for (int r = 0; r < JR; ++r) U[r] = *(const f4*)&H.UVt[(js * JR + r) * D + 4 * i4];
+    }
+    typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+    const u16x8 fl = *(const u16x8*)&H.vch[i][0];  // channel i's field columns
+    // (both loaded and selected after the first barrier: a branch on bitsV here would wait
+    // for every load issued before it)
+    const int bv = H.bitsV[i];
+    const float sv = H.stepV[i];
+    const float ob = H.obias[i], mu = H.muV[i];
+    // per head (one wave each) the partial maxima, the largest one and each partial's weight
+    const int wv = tid >> 6, ln = tid & 63;
+    for (int hh = wv; hh < G; hh += NT / 64) {
+        const float m = ln < W ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                               prs, 4 * (ln * PW + hh * PL), 0, kCoherentLoad))
+                               : -INFINITY;
+        const float M = wave_max(m);
+        if (ln < W) ew[ln * G + hh] = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+    }
+    __syncthreads();
+    // ---- merged rows: sum over partials of weight x row
+    if (rowt) {
+        const int hh = (4 * c4) / PL;
+        f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int w0 = 0;; w0 += S * kFuseRows) {
+#pragma unroll
+            for (int k = 0; k < kFuseRows; ++k) {
+                const int w = w0 + sl + S * k;
+                if (w < W) acc += ew[w * G + hh] * X[k];
+            }
+            if (w0 + S * kFuseRows >= W) break;
+#pragma unroll
+            for (int k = 0; k < kFuseRows; ++k) {  // the next round (partials beyond 8 S)
+                const int w = w0 + S * kFuseRows + sl + S * k;
+                X[k] = w < W ? *(const f4*)(P + (int64_t)w * PW + 4 * c4) : f4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        }
+        red[sl * C4 + c4] = acc;
+    }
+    __syncthreads();
+    for (int k = tid; k < C4; k += NT) {
+        f4 v = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int s2 = 0; s2 < S; ++s2) v += red[s2 * C4 + k];
+        ((LDS_AS f4*)colv)[k] = v;
+    }
+    __syncthreads();
+    // ---- value coefficients, dequantisation step and 1 / L (thread: channel i of heads hh)
+    for (int k = tid; k < G * D; k += NT) {
+        const int hh = k / D;
+        const LDS_AS float* cv = colv + hh * PL;
+        const float L = cv[1], O = cv[2];
+        float A = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t en = fl[e];
+            if (en != 0xFFFFu) {
+                const float v = cv[kPartHead + (en & 511)] + (((en >> 13) & 1) ? O : 0.0f);
+                A = fmaf(__builtin_amdgcn_ldexpf(1.0f, (int)((en >> 9) & 15) - 8), v, A);
+            }
+        }
+        cbar[hh * D + i] = L > 0.0f && bv ? sv * A / L : 0.0f;
+    }
+    __syncthreads();
+    // ---- o = obias + U_V cbar: row slices meet in LDS
+    if (js < JS) {
+        for (int hh = 0; hh < G; ++hh) {
+            f4 y = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int r = 0; r < JR; ++r) y += cbar[hh * D + js * JR + r] * U[r];
+            *(LDS_AS f4*)&red2[(js * G + hh) * D + 4 * i4] = y;
+        }
+    }
+    __syncthreads();
+    for (int k = tid; k < G * D; k += NT) {
+        const int hh = k / D;
+        float y = 0.0f;
+#pragma unroll
+        for (int s2 = 0; s2 < JS; ++s2) y += red2[(s2 * G + hh) * D + i];
+        out[k] = colv[hh * PL + 1] > 0.0f ? ob + y : mu;
+    }
+}
+
 template <int RB, int NQM, int NVB, int D>
 __global__ __launch_bounds__(64 * wg_waves(RB, NQM, NVB))
 __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel(
     const DevHead* __restrict__ blob, uint8_t* __restrict__ cache, DecodeArgs a,
     const int32_t* __restrict__ seq_ids, const int64_t* __restrict__ seq_lens, const uint16_t* __restrict__ q,
-    float* __restrict__ part) {
+    float* __restrict__ part, int* __restrict__ ctrs, float* __restrict__ out) {
     typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
     constexpr int PST = 64;          // bytes per row of the probability operand (64 tokens)
     constexpr int GM = 4 * RB;       // query heads the operands have room for
@@ -312,18 +482,52 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
     const DevHead& H = blob[a.layer * a.n_kv + h];
     const int G = a.G, TB = a.tile_bytes, BB = a.buf_bytes;
     const int64_t zh = (int64_t)z * a.n_kv + h;
+    // every pointer argument in scalar registers at once: the argument loads then form one
+    // batch instead of a second round trip inside a branch
+    asm volatile("" ::"s"(blob), "s"(cache), "s"(seq_ids), "s"(seq_lens), "s"(q), "s"(part), "s"(ctrs), "s"(out));
+    constexpr int NB = D / 16;         // 16-channel blocks of q'
+    constexpr int KS = D / 32;         // k-steps over the input dimension
+    constexpr int QW = 4;              // q-waves (see the prologue below)
+    constexpr int BPW = NB / QW;       // channel blocks per q-wave
+    static_assert(NB % QW == 0 && QW >= 3 && QW < NW, "whole blocks per q-wave; the first three copy the tables");
+    const bool qwave = w < QW;
+    // The q-waves request their matrix rows, query heads, key steps and slot weights first:
+    // the addresses come from the arguments alone, so these requests are in flight while the
+    // scalar loads below (codebook fields, sequence ids and lengths) make their round trip.
+    bf16x8 ah[BPW][KS], al[BPW][KS], bq[KS];
+    f4 stv[BPW], fmv[BPW];
+    if (qwave) {
+#pragma unroll
+        for (int b = 0; b < BPW; ++b) {
+            const int j = 16 * (w * BPW + b) + c;  // A row: channel j
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                ah[b][ks] = *(const bf16x8*)(H.QKt_hi + j * D + 32 * ks + 8 * g);
+                al[b][ks] = *(const bf16x8*)(H.QKt_lo + j * D + 32 * ks + 8 * g);
+            }
+            stv[b] = *(const f4*)(H.stepK + 16 * (w * BPW + b) + 4 * g);
+            fmv[b] = *(const f4*)(H.kq_fmax + 16 * (w * BPW + b) + 4 * g);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)  // B column: query head c of the group (clamped; zeroed below)
+            bq[ks] = *(const bf16x8*)(q + ((int64_t)zh * G + min(c, G - 1)) * D + 32 * ks + 8 * g);
+    }
 
-    // the value block's offset in a tile, read (as a scalar load) before any copy is issued:
-    // a vector load after them would make the compiler wait for every copy in flight
-    const uint32_t vblock = 8u * (uint32_t)H.BK;
-    const int nkw = H.BK / 32, nvr = H.BV / 8;  // a token's key record words, value record bytes
+    // The record sizes of the head and this sequence's id and length, as scalar loads issued
+    // after the q-waves' requests and waited for on the scalar counter only (those requests
+    // stay in flight); the compiler would make them vector loads here, whose wait would also
+    // wait for the matrix rows.  They are read before any copy is issued: a vector load after
+    // the copies would make the compiler wait for every copy in flight.
+    int hBK, hBV, seq;
+    int64_t len0;  // tokens cached before this call
+    load_head_and_sequence(&H, seq_ids + z, seq_lens + z, hBK, hBV, seq, len0);
+    const uint32_t vblock = 8u * (uint32_t)hBK;
+    const int nkw = hBK / 32, nvr = hBV / 8;  // a token's key record words, value record bytes
     asm volatile("" ::"s"(vblock), "s"(nkw), "s"(nvr));
     // ---- sequence geometry (device arguments clamped: no read outside the cache)
-    const int seq = seq_ids[z];
-    const int64_t len0 = seq_lens[z];  // tokens cached before this call
     int64_t len = min(min(len0 + (a.k_new ? 1 : 0), a.max_len), a.n_tiles_cap * kTile);
     if (seq < 0 || seq >= a.n_seqs_cache) len = 0;
-    const int64_t n_tiles = (len + kTile - 1) / kTile;
+    const int n_tiles = (int)((len + kTile - 1) / kTile);  // < 2^31 / 64: the host bounds the range
     uint8_t* tiles = cache + (((int64_t)a.layer * a.n_seqs_cache + seq) * a.n_kv + h) * a.n_tiles_cap * TB;
     // append mode: the new token's slot, when it lies within the attended range
     const bool app = a.k_new && len0 >= 0 && len0 < len;
@@ -332,34 +536,40 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
     // buffer resource over this (sequence, kv-head)'s tiles (the host keeps the range below 2^31 bytes)
     const __amdgpu_buffer_rsrc_t trs =
         __builtin_amdgcn_make_buffer_rsrc((void*)tiles, (short)0, (int)(a.n_tiles_cap * TB), 0x00020000);
-    // workgroup wgi takes the tiles [t_end(wgi - 1), t_end(wgi)) of an even split (every
-    // workgroup within one tile of the others), and its wave w the tiles t_begin + w + NW k:
+    // workgroup wgi takes the tiles [t_begin, t_end) of an even split (the first n_tiles mod W
+    // workgroups one more; 32-bit arithmetic), and its wave w the tiles t_begin + w + NW k:
     // the waves of a workgroup differ by at most one tile, and the waves with one more are
     // the first ones, which the SIMDs' oldest-first issue favours (measured: 0.5-1 us less
-    // than giving the extra tiles to the last waves).  Ring slot k of this wave: ring + k * RS.
-    const int64_t t_end = n_tiles * (wgi + 1) / a.wg_per_head;
+    // than giving the extra tiles to the last waves).  The assignment is static, so every
+    // call sums in the same order and gives the same bits (a wave claiming tiles from an LDS
+    // counter balanced the waves but not the workgroup's end, which its CU's share of the
+    // bandwidth sets).  Ring slot k of this wave: ring + k * RS.
+    const int tq = n_tiles / a.wg_per_head, tr = n_tiles - tq * a.wg_per_head;
+    const int64_t t_begin = (int64_t)tq * wgi + min(wgi, tr);
+    const int64_t t_end = t_begin + tq + (wgi < tr ? 1 : 0);
     const int64_t stride = NW;
     const int NBW = a.nbw;
     const TileLoads tl = a.tl;
     const int nl = tl.n16 + tl.r4 + tl.r2 + tl.r1;  // load instructions per tile
     LDS_AS uint8_t* ring = sm + w * BB;
     const int RS = NW * BB;  // bytes between a wave's ring slots
-    int64_t t = n_tiles * wgi / a.wg_per_head + w;
-    const bool owner = t_app >= n_tiles * wgi / a.wg_per_head && t_app < t_end;  // this workgroup codes the new token
-    // ---- prologue.  Waves 0 .. D/16 - 1 each form one 16-channel block of q' = T_K^{-1} q
-    // (T_K the key basis; U_K^T for the KLT): (1) register loads of the block's rows (hi, lo), the query heads, the key steps
-    // and slot weights; (2) direct global->LDS copies of the slot descriptors, the key
-    // schedule and the value columns (waves 0..2, one table each); (3) the block on bf16
-    // MFMAs, q'' and per head the block's largest slot value into LDS; (4) only then this
-    // wave's tile copies: the compiler cannot count copies of run-time size, so a register
-    // load consumed after them would wait for all of them.  The other waves issue their tile
-    // copies at once.  (5) while the tiles stream, the workgroup builds the score operands
-    // in LDS (three int8 digits per key field, laid out as MFMA A operands) and per head the
-    // lane record (digit scales and the accumulator's start value), and moves them into
-    // registers.
-    constexpr int NB = D / 16;         // 16-channel blocks of q'
-    constexpr int KS = D / 32;         // k-steps over the input dimension
-    static_assert(NB <= NW && NB >= 3, "one wave per channel block; the first three copy the tables");
+    int64_t t = t_begin + w;
+    const bool owner = t_app >= t_begin && t_app < t_end;  // this workgroup codes the new token
+    // ---- prologue.  The first QW waves (the "q-waves") form q' = T_K^{-1} q (T_K the key
+    // basis; U_K^T for the KLT), BPW 16-channel blocks each: (1) register loads of their
+    // blocks' rows (hi, lo), the query heads, the key steps and slot weights (at the top of
+    // the kernel), and direct global->LDS copies of the slot descriptors, the key schedule
+    // and the value columns (waves 0..2, one table each); (2) a workgroup barrier, so that these requests precede
+    // every tile request of the workgroup and are not queued behind the tile stream;
+    // (3) the blocks on bf16 MFMAs, q'' and per head each block's largest slot value into
+    // LDS; (4) the score operands (three int8 digits per key field, laid out as MFMA A
+    // operands) and per head the lane record (digit scales and the accumulator's start
+    // value) - the q-waves meet each other through an LDS counter between these steps.  The
+    // other waves (the "stream waves") issue their tile copies right after the barrier and
+    // meet the q-waves only at the final barrier: a copy issue stalls while the memory
+    // queues are full, and a stalled wave must not hold up the operands.  The q-waves issue
+    // their own tiles after the prologue (the compiler cannot count copies of run-time size,
+    // so a register load consumed after them would wait for all of them).
     constexpr int QB = operand_bytes(RB, NQM);
     LDS_AS uint8_t* scr = sm + a.off_scratch;                             // [QB] operands and records
     LDS_AS uint32_t* vcol = (LDS_AS uint32_t*)(scr + QB);                 // [NVB][16] value columns
@@ -369,117 +579,103 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
     LDS_AS int* corr = (LDS_AS int*)(bmax + NB * 16);                     // [RB][16] digit sums of bit-7 slots
     LDS_AS uint32_t* rec = (LDS_AS uint32_t*)(sm + a.off_rec);            // [kMaxRecord] appended token's records
     LDS_AS u32x4* ksched = (LDS_AS u32x4*)(sm + a.off_ksched);            // [NQM][4][2]: offsets, masks
-    const bool qwave = w < NB;  // this wave forms channel block w
-    bf16x8 ah[KS], al[KS], bq[KS];
-    f4 stv, fmv;
-    if (qwave) {
-        const int j = 16 * w + c;  // A row: channel j
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            ah[ks] = *(const bf16x8*)(H.QKt_hi + j * D + 32 * ks + 8 * g);
-            al[ks] = *(const bf16x8*)(H.QKt_lo + j * D + 32 * ks + 8 * g);
-        }
-        stv = *(const f4*)(H.stepK + 16 * w + 4 * g);
-        fmv = *(const f4*)(H.kq_fmax + 16 * w + 4 * g);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)  // B column: query head c of the group (clamped; zeroed below)
-            bq[ks] = *(const bf16x8*)(q + ((int64_t)zh * G + min(c, G - 1)) * D + 32 * ks + 8 * g);
-    }
-    // (the channel-block waves copy the tables: they wait for their own loads before the
-    // MFMAs anyway, and the other waves start their tiles with nothing else in flight)
+    LDS_AS int* qctr = (LDS_AS int*)(sm + a.off_sync);                    // arrivals of the q-waves
+
     if (w == 0) load_tile((const uint8_t*)&H.vb_col[0][0], (LDS_AS uint8_t*)vcol, NVB * 64, lane, 0);
     if (w == 1) load_tile((const uint8_t*)&H.kq_sched[0][0][0], (LDS_AS uint8_t*)ksched, NQM * 128, lane, 0);
     if (w == 2) load_tile((const uint8_t*)&H.kq_slot[0][0][0], (LDS_AS uint8_t*)kslot, NQM * 128, lane, 0);
-    if (qwave) {
-        const float qscale = kLog2e / sqrtf((float)D);
-        f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 bv = c < G ? bq[ks] : bf16x8{};  // heads past G: zero columns
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bv, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], bv, acc, 0, 0, 0);
-        }
-        // lane (g, c): channels 16 w + 4 g + e of head c
-        f4 v;
-        float mag = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            v[e] = acc[e] * stv[e] * qscale;  // step_K is 0 for uncoded channels
-            mag = fmaxf(mag, fabsf(v[e]) * fmv[e]);
-        }
-        if (c < GM) *(LDS_AS f4*)&qf[c * D + 16 * w + 4 * g] = v;
-        mag = fmaxf(mag, __shfl_xor(mag, 16));
-        mag = fmaxf(mag, __shfl_xor(mag, 32));
-        if (g == 0) bmax[w * 16 + c] = mag;
-    }
-    if (tid < RB * 16) corr[tid] = 0;
-    if (owner) {  // (workgroup-uniform) the new token's codes, before this workgroup's tiles stream
-        if (tid < kMaxRecord / 4) rec[tid] = 0u;
-        lds_barrier();
-        const int64_t row = ((int64_t)z * a.n_kv + h) * D;
-        for (int cb = w; cb < 2 * NB; cb += NW) append_block<D>(H, a.k_new + row, a.v_new + row, cb, rec, g, c);
-    }
-    // The waves that do not form q' issue their whole first ring at once; the others one
-    // tile, and the rest once the score operands are built: the issue of a copy stalls while
-    // the memory system's queues are full, and the q' waves would sit in those stalls instead
-    // of preparing the operands.
+    if (tid == 0) *qctr = 0;
+    lds_barrier();  // the q-waves' requests are issued; the counter is zero
     int issued = 0;  // tiles of this wave whose loads have been issued; tile number k uses ring slot k % NBW
-    for (; issued < (qwave ? min(a.early, 1) : a.early) && t + stride * issued < t_end; ++issued)
-        stream_tile(trs, (uint32_t)((t + stride * issued) * TB), ring + issued * RS, tl, lane);
-    wait_vm(nl * issued);  // the table copies (issued before the tiles) have landed
-    lds_barrier();         // ... in every wave, and q'' and the block maxima are in LDS
-
-    // score operands: item (m, rb, lane group gg, dword iw, head hh4) forms the three digit
-    // words of its four slots (rows 4 hh4 + 0..2 of operand [m][rb]; row 4 hh4 + 3 is zero)
-    for (int i = tid; i < NQM * RB * 64; i += NW * 64) {
-        const int hh4 = i & 3, iw = (i >> 2) & 3, gg = (i >> 4) & 3, rb = (i >> 6) % RB, m = (i >> 6) / RB;
-        const int hh = 4 * rb + hh4;
-        float mx = 0.0f;
+    if (!qwave)
+        for (; issued < a.early && t + stride * issued < t_end; ++issued)
+            stream_tile(trs, (uint32_t)((t + stride * issued) * TB), ring + issued * RS, tl, lane);
+    if (qwave) {
+        if (tid < RB * 16) corr[tid] = 0;
+        if (owner && tid < kMaxRecord / 4) rec[tid] = 0u;
+        const float qscale = kLog2e / sqrtf((float)D);
 #pragma unroll
-        for (int bk = 0; bk < NB; ++bk) mx = fmaxf(mx, bmax[bk * 16 + hh]);
-        const float sc = hh < G && mx > 0.0f ? 127.0f / mx : 0.0f;
-        typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
-        const u16x4 sls = *(const LDS_AS u16x4*)&kslot[(m * 4 + gg) * 16 + 4 * iw];
-        uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
-        int f0 = 0, f1 = 0, f2 = 0;
+        for (int b = 0; b < BPW; ++b) {
+            const int blk = w * BPW + b;
+            f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t sl = sls[e];
-            if (sl != 0xFFFFu) {  // slot = chan | shift << 8 | pos << 11 | ends-at-bit-7 << 14
-                const int sh = (int)((sl >> 8) & 7) - (int)((sl >> 11) & 7);
-                float d0, d1, d2;
-                digits254(qf[hh * D + (sl & 255)] * __builtin_amdgcn_ldexpf(sc, sh), d0, d1, d2);
-                w0 |= ((uint32_t)(int)d0 & 0xFFu) << (8 * e);
-                w1 |= ((uint32_t)(int)d1 & 0xFFu) << (8 * e);
-                w2 |= ((uint32_t)(int)d2 & 0xFFu) << (8 * e);
-                if (sl & 0x4000u) f0 += (int)d0, f1 += (int)d1, f2 += (int)d2;
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 bv = c < G ? bq[ks] : bf16x8{};  // heads past G: zero columns
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[b][ks], bv, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[b][ks], bv, acc, 0, 0, 0);
+            }
+            // lane (g, c): channels 16 blk + 4 g + e of head c
+            f4 v;
+            float mag = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = acc[e] * stv[b][e] * qscale;  // step_K is 0 for uncoded channels
+                mag = fmaxf(mag, fabsf(v[e]) * fmv[b][e]);
+            }
+            if (c < GM) *(LDS_AS f4*)&qf[c * D + 16 * blk + 4 * g] = v;
+            mag = fmaxf(mag, __shfl_xor(mag, 16));
+            mag = fmaxf(mag, __shfl_xor(mag, 32));
+            if (g == 0) bmax[blk * 16 + c] = mag;
+        }
+        wait_vm(0);  // the table copies have landed (these waves have no tile in flight yet)
+        q_sync(qctr, QW, lane);
+        if (owner) {  // (workgroup-uniform) the new token's codes
+            const int64_t row = ((int64_t)z * a.n_kv + h) * D;
+            for (int cb = w; cb < 2 * NB; cb += QW) append_block<D>(H, a.k_new + row, a.v_new + row, cb, rec, g, c);
+        }
+        // score operands: item (m, rb, lane group gg, dword iw, head hh4) forms the three digit
+        // words of its four slots (rows 4 hh4 + 0..2 of operand [m][rb]; row 4 hh4 + 3 is zero)
+        for (int i = tid; i < NQM * RB * 64; i += QW * 64) {
+            const int hh4 = i & 3, iw = (i >> 2) & 3, gg = (i >> 4) & 3, rb = (i >> 6) % RB, m = (i >> 6) / RB;
+            const int hh = 4 * rb + hh4;
+            float mx = 0.0f;
+#pragma unroll
+            for (int bk = 0; bk < NB; ++bk) mx = fmaxf(mx, bmax[bk * 16 + hh]);
+            const float sc = hh < G && mx > 0.0f ? 127.0f / mx : 0.0f;
+            typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+            const u16x4 sls = *(const LDS_AS u16x4*)&kslot[(m * 4 + gg) * 16 + 4 * iw];
+            uint32_t w0 = 0u, w1 = 0u, w2 = 0u;
+            int f0 = 0, f1 = 0, f2 = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t sl = sls[e];
+                if (sl != 0xFFFFu) {  // slot = chan | shift << 8 | pos << 11 | ends-at-bit-7 << 14
+                    const int sh = (int)((sl >> 8) & 7) - (int)((sl >> 11) & 7);
+                    float d0, d1, d2;
+                    digits254(qf[hh * D + (sl & 255)] * __builtin_amdgcn_ldexpf(sc, sh), d0, d1, d2);
+                    w0 |= ((uint32_t)(int)d0 & 0xFFu) << (8 * e);
+                    w1 |= ((uint32_t)(int)d1 & 0xFFu) << (8 * e);
+                    w2 |= ((uint32_t)(int)d2 & 0xFFu) << (8 * e);
+                    if (sl & 0x4000u) f0 += (int)d0, f1 += (int)d1, f2 += (int)d2;
+                }
+            }
+            LDS_AS uint32_t* dst = (LDS_AS uint32_t*)(scr + ((m * RB + rb) * 64 + 16 * gg + 4 * hh4) * 16) + iw;
+            dst[0] = w0;
+            dst[4] = w1;
+            dst[8] = w2;
+            dst[12] = 0u;
+            if (f0 | f1 | f2) {
+                lds_add_async(&corr[rb * 16 + 4 * hh4], f0);
+                lds_add_async(&corr[rb * 16 + 4 * hh4 + 1], f1);
+                lds_add_async(&corr[rb * 16 + 4 * hh4 + 2], f2);
             }
         }
-        LDS_AS uint32_t* dst = (LDS_AS uint32_t*)(scr + ((m * RB + rb) * 64 + 16 * gg + 4 * hh4) * 16) + iw;
-        dst[0] = w0;
-        dst[4] = w1;
-        dst[8] = w2;
-        dst[12] = 0u;
-        if (f0 | f1 | f2) {
-            lds_add_async(&corr[rb * 16 + 4 * hh4], f0);
-            lds_add_async(&corr[rb * 16 + 4 * hh4 + 1], f1);
-            lds_add_async(&corr[rb * 16 + 4 * hh4 + 2], f2);
-        }
-    }
-    lds_barrier();
-    if (tid < RB * 4) {  // lane record of (row block, head): digit scales, 128 x bit-7 digit sums
-        const int rb = tid >> 2, g4 = tid & 3, hh = 4 * rb + g4;
-        float mx = 0.0f;
+        q_sync(qctr, 2 * QW, lane);
+        if (tid < RB * 4) {  // lane record of (row block, head): digit scales, 128 x bit-7 digit sums
+            const int rb = tid >> 2, g4 = tid & 3, hh = 4 * rb + g4;
+            float mx = 0.0f;
 #pragma unroll
-        for (int bk = 0; bk < NB; ++bk) mx = fmaxf(mx, bmax[bk * 16 + hh]);
-        mx *= 1.0f / 127.0f;
-        const LDS_AS int* cr = &corr[16 * rb + 4 * g4];
-        LDS_AS u32x4* rec = (LDS_AS u32x4*)(scr + NQM * RB * 1024 + 32 * tid);
-        rec[0] = u32x4{__float_as_uint(mx), __float_as_uint(mx * kQ1), __float_as_uint(mx * kQ2),
-                       (uint32_t)(128 * cr[0])};
-        rec[1] = u32x4{(uint32_t)(128 * cr[1]), (uint32_t)(128 * cr[2]), 0u, 0u};
+            for (int bk = 0; bk < NB; ++bk) mx = fmaxf(mx, bmax[bk * 16 + hh]);
+            mx *= 1.0f / 127.0f;
+            const LDS_AS int* cr = &corr[16 * rb + 4 * g4];
+            LDS_AS u32x4* lr = (LDS_AS u32x4*)(scr + NQM * RB * 1024 + 32 * tid);
+            lr[0] = u32x4{__float_as_uint(mx), __float_as_uint(mx * kQ1), __float_as_uint(mx * kQ2),
+                          (uint32_t)(128 * cr[0])};
+            lr[1] = u32x4{(uint32_t)(128 * cr[1]), (uint32_t)(128 * cr[2]), 0u, 0u};
+        }
+        q_sync(qctr, 3 * QW, lane);
     }
-    lds_barrier();
+    if (!qwave) q_wait(qctr, 3 * QW);  // the operands, records, tables and the appended token's records are in LDS
     uint32_t voff[NVB], vmask[NVB];  // value columns of this lane: tile offset of its plane slice, mask
 #pragma unroll
     for (int cb = 0; cb < NVB; ++cb) {
@@ -508,8 +704,8 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
     v4i sinit[RB];    // score accumulator start: 128 x the digits multiplying bit-7 fields
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        const LDS_AS u32x4* rec = (const LDS_AS u32x4*)(scr + NQM * RB * 1024 + 32 * (4 * rb + g));
-        const u32x4 r0 = rec[0], r1 = rec[1];
+        const LDS_AS u32x4* lr = (const LDS_AS u32x4*)(scr + NQM * RB * 1024 + 32 * (4 * rb + g));
+        const u32x4 r0 = lr[0], r1 = lr[1];
         // (through scalars: a bit cast of a vector element reads element 0 with this compiler)
         const uint32_t q0 = r0[0], q1 = r0[1], q2 = r0[2];
         qs[rb][0] = __uint_as_float(q0);
@@ -531,7 +727,7 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
 #pragma unroll
         for (int m = 0; m < NQM; ++m) asm volatile("" ::"v"(koffr[m]), "v"(kmaskr[m]));
     }
-    for (; issued < a.early && t + stride * issued < t_end; ++issued)  // the rest of the first slots
+    for (; issued < a.early && t + stride * issued < t_end; ++issued)  // the q-waves' first slots
         stream_tile(trs, (uint32_t)((t + stride * issued) * TB), ring + issued * RS, tl, lane);
     if (a.early < NBW) {  // the scratch was in the ring's last slots: stream them now
         lds_barrier();
@@ -764,7 +960,29 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww) v = fmaf(ew[ww * GP + hl], wx[(ww * GP + hl) * PL + col], v);
             }
-            pout[h0 * PL + i] = v;
+            if (a.fused)  // read by the last workgroup, possibly on another XCD
+                __hip_atomic_store(pout + h0 * PL + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                pout[h0 * PL + i] = v;
+        }
+    }
+    if (a.fused) {
+        // publish this workgroup's partial and count it; the last of the W workgroups of this
+        // (sequence, kv-head) merges them and writes the output, then resets the counter
+        LDS_AS int* lastf = qctr + 1;
+        // every thread's coherent partial stores have completed before the count
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) {
+            const int old = __hip_atomic_fetch_add(ctrs + zh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int last = old == a.wg_per_head - 1;
+            if (last) __hip_atomic_store(ctrs + zh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *lastf = last;
+        }
+        __syncthreads();
+        if (*lastf) {
+            merge_last<D, NVB, NW * 64>(H, part + zh * a.wg_per_head * G * PL, a.wg_per_head, G, out + zh * G * D,
+                                        sm, tid);
         }
     }
 }
@@ -966,12 +1184,18 @@ __global__ __launch_bounds__(256) void vq_decode_kernel(const DevHead* __restric
     LDS_AS float* const pb = (LDS_AS float*)(sm + L.pb);
     LDS_AS float* const qv = (LDS_AS float*)(sm + L.qv);
     LDS_AS float* const alpha = (LDS_AS float*)(sm + L.alpha);
+    // sequence geometry (device arguments clamped: no read outside the cache)
     const int seq = seq_ids[z];
-    const int64_t len = max<int64_t>(0, min<int64_t>(seq_lens[z], a.max_len));
+    int64_t len = max<int64_t>(0, min<int64_t>(min<int64_t>(seq_lens[z], a.max_len), a.n_tiles_cap * kTile));
+    if (seq < 0 || seq >= a.n_seqs_cache) len = 0;
     const int64_t n_tiles = (len + kTile - 1) / kTile;
     const int64_t t_begin = n_tiles * wgi / a.wg_per_head, t_end = n_tiles * (wgi + 1) / a.wg_per_head;
     const uint8_t* const base =
-        cache + (((int64_t)a.layer * a.n_seqs_cache + seq) * a.n_kv + h) * a.n_tiles_cap * (int64_t)tbytes;
+        cache + (((int64_t)a.layer * a.n_seqs_cache + max(seq, 0)) * a.n_kv + h) * a.n_tiles_cap * (int64_t)tbytes;
+    // buffer resource over this (sequence, kv-head)'s tiles (the host keeps the range below 2^31
+    // bytes): a read past the range returns zeros instead of faulting
+    const __amdgpu_buffer_rsrc_t trs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(a.n_tiles_cap * tbytes), 0x00020000);
     // tile copies: instruction k of wave w moves chunks 256 k + 64 w + lane (16 bytes each)
     int nlw = 0;
     for (int k = 0; 256 * k + 64 * w < n16; ++k) ++nlw;
@@ -980,8 +1204,8 @@ __global__ __launch_bounds__(256) void vq_decode_kernel(const DevHead* __restric
         for (int k = 0; k < nlw; ++k) {
             const int c = 256 * k + 64 * w + lane;
             if (c < n16)
-                __builtin_amdgcn_global_load_lds((const void*)(base + t * tbytes + 16 * c),
-                                                 (LDS_AS void*)(dst + 16 * (256 * k + 64 * w)), 16, 0, 2);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(trs, (LDS_AS void*)(dst + 16 * (256 * k + 64 * w)), 16, 16 * c,
+                                                         (int)(t * tbytes), 0, 2);
         }
     };
     const int NB = L.nbuf;
@@ -1159,7 +1383,8 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
         p.wg_per_head = (int)std::max<int64_t>(1, std::min<int64_t>({slots / units, n_tiles_of(max_len), kMaxWG}));
         a.wg_per_head = p.wg_per_head;
         a.part_ld = kPartHead + 16 * p.nvb_max;
-        p.part_bytes = (size_t)n_seqs * cb->n_kv * p.wg_per_head * G * a.part_ld * sizeof(float);
+        a.fused = 0;
+        p.part_bytes = kCounterBytes + (size_t)n_seqs * cb->n_kv * p.wg_per_head * G * a.part_ld * sizeof(float);
         return AATC_OK;
     }
     bool found = false;
@@ -1200,7 +1425,8 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     // ring depth: the deepest that the CU's LDS leaves room for beside the prologue's
     // scratch, between 2 and 4 buffers per wave (1 when two do not fit: the waves then
     // overlap each other's streams rather than their own)
-    const size_t budget = (size_t)(160 * 1024) - ksch - 256 - kMaxRecord - 32 - (own_p ? (size_t)NW * RB * 1024 : 0);
+    const size_t budget =
+        (size_t)(160 * 1024) - ksch - 256 - kMaxRecord - 16 - 32 - (own_p ? (size_t)NW * RB * 1024 : 0);
     a.nbw = 2;
     while (a.nbw < 4 && (a.nbw + 1) * group + scr <= budget) ++a.nbw;
     if (2 * group > budget) a.nbw = 1;  // large tiles: one buffer per wave
@@ -1218,7 +1444,8 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     }
     a.off_ksched = (int)al16(std::max(top, epi));
     a.off_rec = (int)al16(a.off_ksched + ksch);  // the appended token's records (outside ring and scratch)
-    p.lds = a.off_rec + kMaxRecord;
+    a.off_sync = a.off_rec + kMaxRecord;         // the q-waves' arrival counter
+    p.lds = a.off_sync + 16;
     a.off_pbuf = -1;
     if (own_p) {
         a.off_pbuf = (int)al16(p.lds);
@@ -1234,7 +1461,13 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     p.wg_per_head = (int)std::max<int64_t>(1, std::min<int64_t>({slots / pairs, (tiles + NW - 1) / NW, kMaxWG}));
     a.wg_per_head = p.wg_per_head;
     a.part_ld = kPartHead + 16 * p.v.nvb;
-    p.part_bytes = (size_t)n_seqs * cb->n_kv * p.wg_per_head * G * a.part_ld * sizeof(float);
+    // the workspace: kCounterBytes of arrival counters (zero between calls), then the partials
+    p.part_bytes = kCounterBytes + (size_t)n_seqs * cb->n_kv * p.wg_per_head * G * a.part_ld * sizeof(float);
+    // one launch when the last workgroup of a (sequence, kv-head) can merge: few enough
+    // partials, one counter per pair, a partial row within one workgroup's threads, and the
+    // merge's LDS below the arrival words
+    a.fused = pairs <= kFuseMaxPairs && p.wg_per_head <= kFuseMaxW && G * a.part_ld / 4 <= 64 * NW &&
+              merge_lds_bytes(G, a.part_ld, d, 64 * NW) <= a.off_sync;
     return AATC_OK;
 }
 
@@ -1264,7 +1497,7 @@ void profile_slot(hipEvent_t& a, hipEvent_t& b) {
 
 template <int RB, int NQM, int NVB, int D>
 int launch_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* blob, uint8_t* cache,
-                  const int32_t* ids, const int64_t* lens, const uint16_t* q, float* part, float* out) {
+                  const int32_t* ids, const int64_t* lens, const uint16_t* q, int* ctrs, float* part, float* out) {
     const DecodeArgs& a = p.args;
     if (p.lds > 64 * 1024)
         HIP_TRY(hipFuncSetAttribute((const void*)decode_kernel<RB, NQM, NVB, D>,
@@ -1274,13 +1507,14 @@ int launch_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* blob
     if (e0) HIP_TRY(hipEventRecord(e0, st));
     if (p.nw != wg_waves(RB, NQM, NVB)) return set_error(AATC_ERR_UNSUPPORTED, "decode plan and variant disagree");
     hipLaunchKernelGGL((decode_kernel<RB, NQM, NVB, D>), dim3(p.wg_per_head, a.n_kv, n_seqs), dim3(64 * p.nw), p.lds, st,
-                       blob, cache, a, ids, lens, q, part);
+                       blob, cache, a, ids, lens, q, part, ctrs, out);
     HIP_TRY(hipGetLastError());
     if (e1) HIP_TRY(hipEventRecord(e1, st));
-    hipLaunchKernelGGL((merge_kernel<D>), dim3(a.n_kv * (D / kMergeSlice), n_seqs, a.G), dim3(kMergeThreads), 0, st,
-                       blob, a.layer, a.n_kv,
-                       a.G, p.wg_per_head, a.part_ld, (const float*)part, out);
-    HIP_TRY(hipGetLastError());
+    if (!a.fused) {
+        hipLaunchKernelGGL((merge_kernel<D>), dim3(a.n_kv * (D / kMergeSlice), n_seqs, a.G), dim3(kMergeThreads), 0, st,
+                           blob, a.layer, a.n_kv, a.G, p.wg_per_head, a.part_ld, (const float*)part, out);
+        HIP_TRY(hipGetLastError());
+    }
     return AATC_OK;
 }
 
@@ -1378,7 +1612,8 @@ static int decode_impl(const aatc_codebook* cb, const void* d_blob, const aatc_c
     if (rc) return rc;
     if (ws_bytes < p.part_bytes)
         return set_error(AATC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, p.part_bytes);
-    float* part = (float*)workspace;  // [n_seqs][n_kv][wg][G][part_ld] partials
+    int* ctrs = (int*)workspace;                                           // arrival counters
+    float* part = (float*)((uint8_t*)workspace + kCounterBytes);           // [n_seqs][n_kv][wg][G][part_ld]
     DecodeArgs& a = p.args;
     a.layer = layer;
     a.n_kv = cb->n_kv;
@@ -1406,8 +1641,8 @@ static int decode_impl(const aatc_codebook* cb, const void* d_blob, const aatc_c
 #define AATC_DECODE_CASE(rb_, nqm_, nvb_)                                                                    \
     if (p.v.rb == rb_ && p.v.nqm == nqm_ && p.v.nvb == nvb_)                                                 \
         return cb->d == 64                                                                                   \
-                   ? launch_decode<rb_, nqm_, nvb_, 64>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, part, out) \
-                   : launch_decode<rb_, nqm_, nvb_, 128>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, part, out);
+                   ? launch_decode<rb_, nqm_, nvb_, 64>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, ctrs, part, out) \
+                   : launch_decode<rb_, nqm_, nvb_, 128>(p, n_seqs, st, blob, c, seq_ids, seq_lens, q, ctrs, part, out);
     AATC_DECODE_CASE(1, 2, 4)
     AATC_DECODE_CASE(1, 2, 8)
     AATC_DECODE_CASE(1, 3, 8)
