@@ -1,16 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark of the transform-coded KV cache hot path on one MI355X.
 
-One step = prefill-encode of the whole context of a Llama-3.1-8B-shaped attention layer
-(8 KV heads, 32 query heads, head_dim 128, 131072 tokens, bf16 K/V, 2.75 bits/element)
-followed by one decode-attention step over the packed cache.  Inputs are seeded synthetic
-tensors (synth/) resident in HBM before timing starts; the codebook comes from the
-library's own host calibration on synthetic calibration data.
+Default workload (the headline): a Llama-3.1-8B-shaped attention layer (8 KV heads, 32
+query heads, head_dim 128) at 131072 cached tokens and 2.75 bits/element.  One step =
+prefill-encode of the whole context + one decode-attention step over the packed cache.
+The codebook comes from the library's own host calibration on seeded synthetic
+calibration data.
 
-Prints one JSON line.  `value` is the decode-attention effective HBM bandwidth
-(algorithmic bytes / time); encode tokens/s, both kernels' roofline figures and the CPU
-oracle baseline ride along.  The device's 256 MB last-level cache is flushed (512 MB
-streaming write, untimed) before every timed encode and decode.
+Other workloads (--workload):
+  llama_32k      the same layer at 32768 tokens;
+  qwen_128k      a Qwen-2.5-7B-shaped model, all 28 layers (4 KV / 28 query heads) at
+                 131072 tokens: one decode step across the layers (28 calls in a HIP graph);
+  llama_batch    Llama geometry, 32 layers x 32 sequences x 8192 tokens: one batched decode
+                 step (32 calls in a HIP graph);
+  llama_loop     one Llama layer, 65536 cached tokens, 1024 generation steps at 2.0 b/e, each
+                 appending one token per kv-head and attending over the grown cache
+                 (aatc_decode_attention_append);
+  llama_vq_128k  the headline layer with vector-quantized keys at 2.0 b/e.
+
+Inputs are resident in HBM before timing starts.  The device's 256 MB last-level cache
+is flushed (512 MB streaming write, untimed) before every timed encode and decode.
+Prints one JSON line: `value` is the decode-attention effective HBM bandwidth
+(algorithmic bytes / time of the decode call(s)); the decode kernel's roofline (with the
+read rate of the library's streaming probe on the same bytes), the encoder's, and the CPU
+oracle baseline ride along.
 """
 from __future__ import annotations
 
@@ -33,6 +46,16 @@ DECODE_PMC = (os.path.join(PROFILES, "decode_kernel_llama128k_pmc.txt"), os.path
 ENCODE_PMC = (os.path.join(PROFILES, "encode_kernel_llama128k_pmc.txt"), os.path.join(CSRC, "encode.hip"))
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "decode-attn effective HBM GB/s (% of peak) + encode tokens/s, 128k ctx, 2.75 b/elem"
+FLUSH_BYTES = 512 << 20
+
+WORKLOAD_LABELS = {
+    "llama_128k": "llama3.1-8b-shaped attention layer, 131072 tokens, 2.75 b/e",
+    "llama_32k": "llama3.1-8b-shaped attention layer, 32768 tokens, 2.75 b/e",
+    "qwen_128k": "qwen2.5-7b-shaped model, 28 layers, 131072 tokens, 2.75 b/e",
+    "llama_batch": "llama3.1-8b geometry, 32 layers x 32 sequences x 8192 tokens, 2.75 b/e",
+    "llama_loop": "llama3.1-8b-shaped layer, 65536 -> 66560 tokens, 1024 append+decode steps, 2.0 b/e",
+    "llama_vq_128k": "llama3.1-8b-shaped attention layer, 131072 tokens, vector-quantized keys, 2.0 b/e",
+}
 
 
 def log(msg):
@@ -47,35 +70,66 @@ def vq_keys(w) -> bool:
     return "vq" in w.name
 
 
-def build_inputs(wname: str, ctx: int):
+def path_dtype(w) -> str:
+    """The arithmetic the decode path computes in: int8 MFMA digit products with fp32
+    combination for scalar keys; fp32 score tables and fp16 value MFMAs for VQ keys."""
+    return "f32+f16" if vq_keys(w) else "i8+f32"
+
+
+def calibrate(w, q, n_layers: int):
+    """Library host calibration of every (layer, kv-head) of the workload."""
     import synth
-    import quantized_attention_klt_amd as q
-    w = synth.WORKLOADS[wname]
     t0 = time.perf_counter()
-    stats = []
-    hms = []
-    for h in range(w.n_kv):
-        hm = synth.head_model(w, 0, h)
-        hms.append(hm)
-        K, V, Q = synth.calibration_samples(w, hm, 0, h)
-        stats.append(q.stats_from_samples(K, V, Q))
+    stats, hms = [], []
+    for layer in range(n_layers):
+        for h in range(w.n_kv):
+            hm = synth.head_model(w, layer, h)
+            hms.append(hm)
+            K, V, Q = synth.calibration_samples(w, hm, layer, h)
+            stats.append(q.stats_from_samples(K, V, Q))
     t1 = time.perf_counter()
     if vq_keys(w):
-        cb = q.calibrate(stats, w.d, 1, w.n_kv, w.group, w.avg_bits, joint=False, key_quantizer="vq",
+        cb = q.calibrate(stats, w.d, n_layers, w.n_kv, w.group, w.avg_bits, joint=False, key_quantizer="vq",
                          vq_normals=synth.vq_normals(w, 0, VQ_TRAIN), vq_iters=VQ_ITERS)
     else:
-        cb = q.calibrate(stats, w.d, 1, w.n_kv, w.group, w.avg_bits)
+        cb = q.calibrate(stats, w.d, n_layers, w.n_kv, w.group, w.avg_bits)
     t2 = time.perf_counter()
-    log(f"calibration: stats {t1 - t0:.2f}s, calibrate {t2 - t1:.2f}s")
-    kb = np.zeros((1, ctx, w.n_kv, w.d), np.uint16)
-    vb = np.zeros_like(kb)
-    for h, hm in enumerate(hms):
-        K, V = synth.cache_kv(w, hm, 0, 0, h, ctx)
-        kb[0, :, h] = synth.to_bf16_bits(K)
-        vb[0, :, h] = synth.to_bf16_bits(V)
-    qb = synth.to_bf16_bits(synth.decode_queries(w, hms, 0, 0))[None]
-    log(f"inputs generated ({time.perf_counter() - t2:.1f}s)")
-    return w, cb, kb, vb, qb, t2 - t0
+    log(f"calibration of {len(stats)} heads: stats {t1 - t0:.2f}s, calibrate {t2 - t1:.2f}s")
+    return cb, hms, t2 - t0
+
+
+def gpu_draws(torch, hm, n: int, seed: int, dev):
+    """n seeded K and V rows of one (layer, kv-head) on the GPU, bf16 [n, d]: the head
+    model's recipe x = mu + U diag(sqrt(lambda)) z (outlier channels x10), with z from
+    torch's device generator (the same distribution as synth.cache_kv, another stream)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    out = []
+    for U, lam, mu, ch in ((hm.UK, hm.lamK, hm.muK, hm.outK), (hm.UV, hm.lamV, hm.muV, hm.outV)):
+        z = torch.randn((n, hm.d), generator=gen, device=dev, dtype=torch.float32)
+        A = torch.from_numpy((U * np.sqrt(lam)[None, :]).T.astype(np.float32)).to(dev)
+        x = z @ A + torch.from_numpy(mu.astype(np.float32)).to(dev)
+        if ch.size:
+            x[:, torch.from_numpy(ch).to(dev)] *= 10.0
+        out.append(x.to(torch.bfloat16).view(torch.int16))
+    return out
+
+
+def gpu_queries(torch, hm, w, seed: int, dev):
+    """One decode step's queries of the G query heads of a kv-head, bf16 [G, d]."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    qs = []
+    for g in range(w.group):
+        z = torch.randn((hm.d,), generator=gen, device=dev, dtype=torch.float32)
+        A = torch.from_numpy((hm.UQ[g] * np.sqrt(hm.lamQ[g])[None, :]).T.astype(np.float32)).to(dev)
+        qs.append(z @ A)
+    return torch.stack(qs).to(torch.bfloat16).view(torch.int16)
+
+
+def seed_of(*parts) -> int:
+    import synth
+    return int(np.random.SeedSequence([synth.S0, *parts]).generate_state(1, np.uint64)[0] >> 1)
 
 
 def source_hash(path: str) -> str:
@@ -108,8 +162,19 @@ def measured_traffic(summary: str, source: str):
         return None
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wname: str, n_tokens: int = 16384):
-    """Oracle (numpy, float64) on one kv-head and n_tokens tokens: encode and decode rates."""
+    """Oracle (numpy, float64) on a bounded sample: one kv-head of the workload's first
+    layer, n_tokens tokens - oracle encode then oracle decode of its query-head group."""
     import oracle
     import synth
     w = synth.WORKLOADS[wname]
@@ -138,12 +203,376 @@ def cpu_baseline(wname: str, n_tokens: int = 16384):
         cores = len(os.sched_getaffinity(0))
     tb = oracle.tile_bytes(oracle.key_record_bits(cb), cb.bV)
     dec_bytes = n_tokens * tb / 64
+    rate = dec_bytes / (t2 - t1) / 1e9
+    full = w.n_layers * w.n_seqs * w.n_kv * w.ctx * tb / 64
     return {
-        "value": dec_bytes / (t2 - t1) / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-        "sample": f"one kv-head of the workload, {n_tokens} tokens: oracle encode then oracle decode of one "
-                  f"4-query-head group; decode rate = packed bytes / decode time",
+        "value": rate, "unit": "GB/s", "cores": int(cores), "cpu_model": cpu_model(), "kind": "oracle",
+        "sample": f"one kv-head of the first layer, {n_tokens} tokens: oracle encode, then oracle decode of its "
+                  f"{w.group}-query-head group; decode rate = packed bytes / decode time",
+        "scale_up": f"the rate is per byte and the same for every (layer, sequence, kv-head); at it the whole "
+                    f"workload's {full / 1e6:.0f} MB of packed cache would take {full / rate / 1e9:.1f} s per decode step",
         "encode_tokens_per_s": n_tokens / (t1 - t0),
         "encode_s": t1 - t0, "decode_s": t2 - t1,
+    }
+
+
+class Timer:
+    """Device events on torch's current stream around a region."""
+
+    def __init__(self, torch, n):
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+
+    def start(self, i):
+        self.ev[i][0].record()
+
+    def stop(self, i):
+        self.ev[i][1].record()
+
+    def ms(self):
+        return np.array([a.elapsed_time(b) for a, b in self.ev])
+
+
+def probe_rates(torch, q, dev, nbytes: int, tile_bytes: int, cache_t, flush, reps: int):
+    """Read rate (GB/s, median over reps, LLC flushed before each) of the library's
+    streaming probe: plain loads of nbytes, and the decode kernel's tile stream over the
+    cache buffer."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    sink = torch.zeros(16, dtype=torch.uint8, device=dev)
+    res = {}
+    for name, mode, buf, n in (("plain", 0, src, nbytes), ("tiles", 1, cache_t, cache_t.numel())):
+        tm = Timer(torch, reps)
+        for i in range(reps + 2):
+            q.flush_write(flush)
+            if i >= 2:
+                tm.start(i - 2)
+            q.read_probe(buf, mode, sink, tile_bytes=tile_bytes, nbytes=n)
+            if i >= 2:
+                tm.stop(i - 2)
+        torch.cuda.synchronize()
+        ms = float(np.median(tm.ms()))
+        nb = n if mode == 0 else (n // tile_bytes) * tile_bytes
+        res[name] = {"ms": ms, "gbs": nb / (ms * 1e6), "bytes": nb}
+    del src
+    return res
+
+
+# ---------------------------------------------------------------------------- one layer
+def run_layer(args, w, ctx, torch, q, dev):
+    import synth
+    cb, hms, calib_s = calibrate(w, q, 1)
+    blob = torch.empty(cb.device_bytes(), dtype=torch.uint8, device=dev)
+    cb.upload(blob)
+    cache_t = torch.zeros(cb.cache_bytes(1, 1, ctx), dtype=torch.uint8, device=dev)
+    cache = q.make_cache(cache_t, 1, 1, ctx)
+    kb = np.zeros((1, ctx, w.n_kv, w.d), np.uint16)
+    vb = np.zeros_like(kb)
+    for h, hm in enumerate(hms):
+        K, V = synth.cache_kv(w, hm, 0, 0, h, ctx)
+        kb[0, :, h] = synth.to_bf16_bits(K)
+        vb[0, :, h] = synth.to_bf16_bits(V)
+    qb = synth.to_bf16_bits(synth.decode_queries(w, hms, 0, 0))[None]
+    K = torch.from_numpy(kb.view(np.int16)).to(dev)
+    V = torch.from_numpy(vb.view(np.int16)).to(dev)
+    Qd = torch.from_numpy(qb.view(np.int16)).to(dev)
+    del kb, vb
+    out = torch.empty((1, w.n_q, w.d), dtype=torch.float32, device=dev)
+    ws = torch.zeros(cb.decode_workspace_bytes(1, ctx), dtype=torch.uint8, device=dev)
+    ids = torch.zeros(1, dtype=torch.int32, device=dev)
+    lens = torch.full((1,), ctx, dtype=torch.int64, device=dev)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
+    def encode():
+        q.encode(cb, blob, cache, 0, [0], [0], ctx, K, V)
+
+    def decode():
+        q.decode_attention(cb, blob, cache, 0, ids, lens, ctx, Qd, out, ws)
+
+    for _ in range(args.warmup):
+        q.flush_write(flush)
+        encode()
+        q.flush_write(flush)
+        decode()
+    torch.cuda.synchronize()
+    te, td = Timer(torch, args.steps), Timer(torch, args.steps)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        q.flush_write(flush)
+        te.start(i)
+        encode()
+        te.stop(i)
+        q.flush_write(flush)
+        td.start(i)
+        decode()
+        td.stop(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    enc_ms, dec_ms = te.ms(), td.ms()
+    # second pass, same steps: library events around the split-decode kernel alone
+    q.profile_begin(args.steps)
+    for i in range(args.steps):
+        q.flush_write(flush)
+        decode()
+    torch.cuda.synchronize()
+    kern_ms = q.profile_end(args.steps)
+
+    tb = cb.tile_bytes
+    cache_bytes = w.n_kv * ((ctx + 63) // 64) * tb
+    vq = vq_keys(w)
+    books = w.n_kv * (w.d * w.avg_bits // 8) * 256 * 4 * 4 if vq else 0  # VQ codebooks: side information
+    side = 2 * w.n_kv * w.d * w.d * 4 + w.n_q * w.d * 2 + w.n_q * w.d * 4 + books
+    dec_bytes = int(cache_bytes + side)
+    # the split-decode kernel alone (the merge kernel that follows it reads U_V and writes
+    # out): the packed cache, U_K (or T_K^-1), the VQ codebooks, the bf16 queries
+    kern_bytes = int(cache_bytes + w.n_kv * w.d * w.d * 4 + w.n_q * w.d * 2 + books)
+    probe = probe_rates(torch, q, dev, kern_bytes, tb, cache_t, flush, max(5, args.steps // 2)) if not vq else None
+    if args.copy_probe_mb:
+        a = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_probe_mb} MiB read + written")
+    kern_s = float(kern_ms.mean()) / 1e3
+    kern_gbs = kern_bytes / kern_s / 1e9
+    enc_bytes = 2 * ctx * w.n_kv * w.d * 2 + cache_bytes
+    dec_s = dec_ms.mean() / 1e3
+    enc_s = enc_ms.mean() / 1e3
+    dec_gbs = dec_bytes / dec_s / 1e9
+    enc_gbs = enc_bytes / enc_s / 1e9
+    enc_flops = 2 * 2 * ctx * w.n_kv * w.d * w.d  # K and V projections, algorithmic
+    roof = {"kernel": ("vq_decode_kernel (split decode over vector-quantized keys)" if vq else
+                       "decode_kernel (split decode: query transform, scores, online softmax, value sums)"),
+            "bound": "hbm", "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None if vq else measured_traffic(*DECODE_PMC),
+            "algorithmic_bytes": kern_bytes, "kernel_ms": round(kern_s * 1e3, 4),
+            "source_sha256_16": source_hash(DECODE_PMC[1])}
+    if probe:
+        roof.update({"probe_gbs": round(probe["plain"]["gbs"], 2), "frac_of_probe": round(kern_gbs / probe["plain"]["gbs"], 4),
+                     "probe_tile_stream_gbs": round(probe["tiles"]["gbs"], 2),
+                     "probe": "library read probe (aatc_read_probe) by the same events, LLC flushed: mode 0 = plain "
+                              "16-byte loads of the kernel's algorithmic bytes, mode 1 = this cache's tiles streamed "
+                              "into LDS like the decode kernel"})
+    return {
+        "value": round(dec_gbs, 2),
+        "steps": args.steps,
+        "ms_per_step": round(float((enc_ms + dec_ms).mean()), 4),
+        "config": {"workload": WORKLOAD_LABELS.get(w.name, w.name), "kv_heads": w.n_kv, "q_heads": w.n_q,
+                   "head_dim": w.d, "ctx": ctx, "batch": 1, "layers": 1, "bits_per_element": w.avg_bits,
+                   "step": "prefill-encode of ctx tokens + one decode-attention step"},
+        "decode_ms": round(float(dec_ms.mean()), 4),
+        "decode_bytes": dec_bytes,
+        "decode_ms_min": round(float(dec_ms.min()), 4),
+        "decode_frac_of_peak": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "encode_ms": round(float(enc_ms.mean()), 4),
+        "encode_tokens_per_s": round(ctx / enc_s, 1),
+        "encode_gbs": round(enc_gbs, 2),
+        "compression_ratio": round(16.0 / w.avg_bits, 4),
+        "calibration_s": round(calib_s, 3),
+        "wall_s_timed_region": round(wall, 3),
+        "roofline": roof,
+        "roofline_encode": {"kernel": "encode", "bound": "hbm", "achieved": round(enc_gbs, 2),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(enc_gbs / HBM_PEAK_GBS, 4),
+                            "mfma_tflops": round(enc_flops / enc_s / 1e12, 2),
+                            "mfma_frac": round(enc_flops / enc_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                            "traffic": None if vq else measured_traffic(*ENCODE_PMC),
+                            "algorithmic_bytes": enc_bytes,
+                            "source_sha256_16": source_hash(ENCODE_PMC[1])},
+    }
+
+
+# ------------------------------------------------------------------- several layers
+def run_layers(args, w, torch, q, dev):
+    """A decode step across every layer of the workload (one call per layer, captured in a
+    HIP graph), over caches prefilled by aatc_encode from seeded device draws."""
+    L, S, ctx = w.n_layers, w.n_seqs, w.ctx
+    cb, hms, calib_s = calibrate(w, q, L)
+    blob = torch.empty(cb.device_bytes(), dtype=torch.uint8, device=dev)
+    cb.upload(blob)
+    cache_t = torch.zeros(cb.cache_bytes(L, S, ctx), dtype=torch.uint8, device=dev)
+    cache = q.make_cache(cache_t, L, S, ctx)
+    t0 = time.perf_counter()
+    enc_ms = []
+    for layer in range(L):
+        K = torch.empty((S, ctx, w.n_kv, w.d), dtype=torch.int16, device=dev)
+        V = torch.empty_like(K)
+        for s in range(S):
+            for h in range(w.n_kv):
+                k, v = gpu_draws(torch, hms[layer * w.n_kv + h], ctx, seed_of(w.cfg, layer, s, h, 6), dev)
+                K[s, :, h] = k
+                V[s, :, h] = v
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        q.encode(cb, blob, cache, layer, list(range(S)), [0] * S, ctx, K, V)
+        e1.record()
+        torch.cuda.synchronize()
+        enc_ms.append(e0.elapsed_time(e1))
+        del K, V
+    log(f"prefill of {L} layers x {S} sequences x {ctx} tokens ({time.perf_counter() - t0:.1f}s)")
+    Qd = torch.stack([torch.stack([torch.cat([gpu_queries(torch, hms[layer * w.n_kv + h], w,
+                                                          seed_of(w.cfg, layer, s, h, 8), dev)
+                                              for h in range(w.n_kv)]) for s in range(S)]) for layer in range(L)])
+    out = torch.empty((L, S, w.n_q, w.d), dtype=torch.float32, device=dev)
+    ws = torch.zeros(cb.decode_workspace_bytes(S, ctx), dtype=torch.uint8, device=dev)
+    ids = torch.arange(S, dtype=torch.int32, device=dev)
+    lens = torch.full((S,), ctx, dtype=torch.int64, device=dev)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
+    def step():
+        for layer in range(L):
+            q.decode_attention(cb, blob, cache, layer, ids, lens, ctx, Qd[layer], out[layer], ws)
+
+    side_stream = torch.cuda.Stream()
+    side_stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side_stream):
+        step()
+    torch.cuda.current_stream().wait_stream(side_stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(args.warmup):
+        q.flush_write(flush)
+        g.replay()
+    torch.cuda.synchronize()
+    tg, te = Timer(torch, args.steps), Timer(torch, args.steps)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        q.flush_write(flush)
+        tg.start(i)
+        g.replay()
+        tg.stop(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for i in range(args.steps):  # the same step launched eagerly
+        q.flush_write(flush)
+        te.start(i)
+        step()
+        te.stop(i)
+    torch.cuda.synchronize()
+    gms, ems = tg.ms(), te.ms()
+    tb = cb.tile_bytes
+    cache_bytes = L * S * w.n_kv * ((ctx + 63) // 64) * tb
+    side = L * (2 * w.n_kv * w.d * w.d * 4 + S * (w.n_q * w.d * 2 + w.n_q * w.d * 4))
+    dec_bytes = int(cache_bytes + side)
+    gbs = dec_bytes / (gms.mean() / 1e3) / 1e9
+    return {
+        "value": round(gbs, 2),
+        "steps": args.steps,
+        "ms_per_step": round(float(gms.mean()), 4),
+        "config": {"workload": WORKLOAD_LABELS.get(w.name, w.name), "kv_heads": w.n_kv, "q_heads": w.n_q,
+                   "head_dim": w.d, "ctx": ctx, "batch": S, "layers": L, "bits_per_element": w.avg_bits,
+                   "step": f"one decode step across {L} layers ({L} calls replayed as a HIP graph)"},
+        "decode_ms": round(float(gms.mean()), 4),
+        "decode_ms_p50": round(float(np.median(gms)), 4),
+        "decode_ms_min": round(float(gms.min()), 4),
+        "decode_ms_eager": round(float(ems.mean()), 4),
+        "decode_bytes": dec_bytes,
+        "decode_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "encode_ms_per_layer": round(float(np.mean(enc_ms)), 4),
+        "encode_tokens_per_s": round(S * ctx / (np.mean(enc_ms) / 1e3), 1),
+        "compression_ratio": round(16.0 / w.avg_bits, 4),
+        "calibration_s": round(calib_s, 3),
+        "wall_s_timed_region": round(wall, 3),
+        "roofline": {"kernel": "decode_kernel per layer (one launch each)", "bound": "hbm",
+                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": dec_bytes,
+                     "kernel_ms": round(float(gms.mean()), 4), "source_sha256_16": source_hash(DECODE_PMC[1])},
+    }
+
+
+# ------------------------------------------------------------------- generation loop
+def run_loop(args, w, torch, q, dev):
+    """Prefill, then n generation steps: each appends one new K/V token per kv-head and
+    decodes over the grown cache in one launch (aatc_decode_attention_append)."""
+    l0, n = w.ctx, args.loop_steps
+    cb, hms, calib_s = calibrate(w, q, 1)
+    blob = torch.empty(cb.device_bytes(), dtype=torch.uint8, device=dev)
+    cb.upload(blob)
+    cap = l0 + n
+    cache_t = torch.zeros(cb.cache_bytes(1, 1, cap), dtype=torch.uint8, device=dev)
+    cache = q.make_cache(cache_t, 1, 1, cap)
+    K = torch.empty((1, l0, w.n_kv, w.d), dtype=torch.int16, device=dev)
+    V = torch.empty_like(K)
+    for h in range(w.n_kv):
+        k, v = gpu_draws(torch, hms[h], l0, seed_of(w.cfg, 0, 0, h, 6), dev)
+        K[0, :, h] = k
+        V[0, :, h] = v
+    q.encode(cb, blob, cache, 0, [0], [0], l0, K, V)
+    del K, V
+    # per-step draws: one K/V token per kv-head and the queries (stream 9 of the recipe)
+    kn = torch.empty((n, 1, w.n_kv, w.d), dtype=torch.int16, device=dev)
+    vn = torch.empty_like(kn)
+    qn = torch.empty((n, 1, w.n_q, w.d), dtype=torch.int16, device=dev)
+    for h in range(w.n_kv):
+        k, v = gpu_draws(torch, hms[h], n, seed_of(w.cfg, 0, 0, h, 9), dev)
+        kn[:, 0, h] = k
+        vn[:, 0, h] = v
+        for i in range(n):
+            qn[i, 0, h * w.group:(h + 1) * w.group] = gpu_queries(torch, hms[h], w, seed_of(w.cfg, 0, 0, h, 9, i), dev)
+    lens_all = torch.arange(l0, l0 + n, dtype=torch.int64, device=dev)  # tokens cached before step i
+    out = torch.empty((n, 1, w.n_q, w.d), dtype=torch.float32, device=dev)
+    ws = torch.zeros(cb.decode_workspace_bytes(1, cap), dtype=torch.uint8, device=dev)
+    ids = torch.zeros(1, dtype=torch.int32, device=dev)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    pristine = cache_t.clone()
+
+    def step(i):
+        q.decode_attention_append(cb, blob, cache, 0, ids, lens_all[i:i + 1], cap, kn[i], vn[i], qn[i], out[i], ws)
+
+    # (a) every step eagerly, the LLC flushed before each (as in a model whose other layers
+    # evict this layer's cache between steps): per-step latency distribution
+    tm = Timer(torch, n)
+    for i in range(n):
+        q.flush_write(flush)
+        tm.start(i)
+        step(i)
+        tm.stop(i)
+    torch.cuda.synchronize()
+    ms = tm.ms()
+    # (b) the whole loop back to back as one HIP graph (the single layer's cache stays in
+    # the LLC between steps)
+    cache_t.copy_(pristine)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            step(i)
+    cache_t.copy_(pristine)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    graph_ms = e0.elapsed_time(e1)
+    tb = cb.tile_bytes
+    mean_len = l0 + (n + 1) / 2.0
+    step_bytes = int(w.n_kv * mean_len / 64 * tb + 2 * w.n_kv * w.d * w.d * 4 + w.n_q * w.d * 6)
+    gbs = step_bytes / (ms.mean() / 1e3) / 1e9
+    return {
+        "value": round(gbs, 2),
+        "steps": n,
+        "ms_per_step": round(float(ms.mean()), 4),
+        "config": {"workload": WORKLOAD_LABELS.get(w.name, w.name), "kv_heads": w.n_kv, "q_heads": w.n_q,
+                   "head_dim": w.d, "ctx": l0, "batch": 1, "layers": 1, "bits_per_element": w.avg_bits,
+                   "step": "append one K/V token per kv-head + decode over the grown cache (one launch)"},
+        "step_ms_mean": round(float(ms.mean()), 5),
+        "step_ms_p50": round(float(np.percentile(ms, 50)), 5),
+        "step_ms_p99": round(float(np.percentile(ms, 99)), 5),
+        "step_ms_graph_back_to_back": round(graph_ms / n, 5),
+        "loop_ms_graph": round(graph_ms, 3),
+        "step_bytes_mean": step_bytes,
+        "decode_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "compression_ratio": round(16.0 / w.avg_bits, 4),
+        "calibration_s": round(calib_s, 3),
+        "wall_s_timed_region": round(wall, 3),
+        "roofline": {"kernel": "decode_kernel, append mode (one launch per step)", "bound": "hbm",
+                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": step_bytes,
+                     "kernel_ms": round(float(ms.mean()), 5), "source_sha256_16": source_hash(DECODE_PMC[1])},
     }
 
 
@@ -153,7 +582,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama_128k")
-    ap.add_argument("--ctx", type=int, default=0, help="override context length")
+    ap.add_argument("--ctx", type=int, default=0, help="override context length (one-layer workloads)")
+    ap.add_argument("--loop-steps", type=int, default=1024, help="generation steps of llama_loop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
@@ -171,132 +601,23 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     import synth
-    w0 = synth.WORKLOADS[args.workload]
-    ctx = args.ctx or w0.ctx
-    w, cb, kb, vb, qb, calib_s = build_inputs(args.workload, ctx)
+    w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    blob = torch.empty(cb.device_bytes(), dtype=torch.uint8, device=dev)
-    cb.upload(blob)
-    cache_t = torch.zeros(cb.cache_bytes(1, 1, ctx), dtype=torch.uint8, device=dev)
-    cache = q.make_cache(cache_t, 1, 1, ctx)
-    K = torch.from_numpy(kb.view(np.int16)).to(dev)
-    V = torch.from_numpy(vb.view(np.int16)).to(dev)
-    Qd = torch.from_numpy(qb.view(np.int16)).to(dev)
-    out = torch.empty((1, w.n_q, w.d), dtype=torch.float32, device=dev)
-    ws = torch.zeros(cb.decode_workspace_bytes(1, ctx), dtype=torch.uint8, device=dev)
-    ids = torch.zeros(1, dtype=torch.int32, device=dev)
-    lens = torch.full((1,), ctx, dtype=torch.int64, device=dev)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    del kb, vb
-
-    def encode():
-        q.encode(cb, blob, cache, 0, [0], [0], ctx, K, V)
-
-    def decode():
-        q.decode_attention(cb, blob, cache, 0, ids, lens, ctx, Qd, out, ws)
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for _ in range(args.warmup):
-        q.flush_write(flush)
-        encode()
-        q.flush_write(flush)
-        decode()
-    torch.cuda.synchronize()
-    # timed region: the whole step, events around the encode and the decode call
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        q.flush_write(flush)
-        ev[i][0].record()
-        encode()
-        ev[i][1].record()
-        q.flush_write(flush)
-        ev[i][2].record()
-        decode()
-        ev[i][3].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    enc_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    dec_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
-    # second timed region, same steps: device events around the split-decode kernel alone
-    # (kept out of the first region: markers between kernels stretch the call they sit in)
-    q.profile_begin(args.steps)
-    for i in range(args.steps):
-        q.flush_write(flush)
-        decode()
-    torch.cuda.synchronize()
-    kern_ms = q.profile_end(args.steps)
-    if args.copy_probe_mb:
-        a = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        log(f"copy probe: {args.copy_probe_mb} MiB read + written")
-
-    tb = cb.tile_bytes
-    n_tiles = (ctx + 63) // 64
-    cache_bytes = w.n_kv * n_tiles * tb
-    vq = vq_keys(w)
-    # vector-quantized keys: the codebooks (n_g x 256 words of 4 fp32) are side information too
-    books = w.n_kv * (w.d * w.avg_bits // 8) * 256 * 4 * 4 if vq else 0
-    side = 2 * w.n_kv * w.d * w.d * 4 + w.n_q * w.d * 2 + w.n_q * w.d * 4 + books
-    dec_bytes = int(cache_bytes + side)
-    # the split-decode kernel alone: the packed cache, U_K (or T_K^-1), the codebooks, the bf16 queries
-    kern_bytes = int(cache_bytes + w.n_kv * w.d * w.d * 4 + w.n_q * w.d * 2 + books)
-    kern_s = float(kern_ms.mean()) / 1e3
-    kern_gbs = kern_bytes / kern_s / 1e9
-    enc_bytes = 2 * ctx * w.n_kv * w.d * 2 + cache_bytes
-    dec_s = dec_ms.mean() / 1e3
-    enc_s = enc_ms.mean() / 1e3
-    dec_gbs = dec_bytes / dec_s / 1e9
-    enc_gbs = enc_bytes / enc_s / 1e9
-    enc_flops = 2 * 2 * ctx * w.n_kv * w.d * w.d  # K and V projections, algorithmic
-    res = {
-        "metric": METRIC,
-        "value": round(dec_gbs, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(float((enc_ms + dec_ms).mean()), 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "i8+f32",
-        "data": "synthetic",
-        "config": {"workload": "llama3.1-8b-attention-layer" + ("-vq-keys" if vq else ""),
-                   "kv_heads": w.n_kv, "q_heads": w.n_q,
-                   "head_dim": w.d, "ctx": ctx, "batch": 1, "bits_per_element": w.avg_bits,
-                   "step": "prefill-encode of ctx tokens + one decode-attention step"},
-        "decode_ms": round(float(dec_ms.mean()), 4),
-        "decode_bytes": dec_bytes,
-        "decode_ms_min": round(float(dec_ms.min()), 4),
-        "decode_frac_of_peak": round(dec_gbs / HBM_PEAK_GBS, 4),
-        "encode_ms": round(float(enc_ms.mean()), 4),
-        "encode_tokens_per_s": round(ctx / enc_s, 1),
-        "encode_gbs": round(enc_gbs, 2),
-        "compression_ratio": round(16.0 / w.avg_bits, 4),
-        "calibration_s": round(calib_s, 3),
-        "wall_s_timed_region": round(wall, 3),
-        "roofline": {"kernel": ("vq_decode_kernel (split decode over vector-quantized keys)" if vq else
-                                "decode_kernel (split decode: scores, online softmax, value sums)"),
-                     "bound": "hbm",
-                     "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None if vq else measured_traffic(*DECODE_PMC),
-                     "algorithmic_bytes": kern_bytes, "kernel_ms": round(kern_s * 1e3, 4),
-                     "source_sha256_16": source_hash(DECODE_PMC[1])},
-        "roofline_encode": {"kernel": "encode", "bound": "hbm", "achieved": round(enc_gbs, 2),
-                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(enc_gbs / HBM_PEAK_GBS, 4),
-                            "mfma_tflops": round(enc_flops / enc_s / 1e12, 2),
-                            "mfma_frac": round(enc_flops / enc_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-                            "traffic": None if vq else measured_traffic(*ENCODE_PMC),
-                            "algorithmic_bytes": enc_bytes,
-                            "source_sha256_16": source_hash(ENCODE_PMC[1])},
-    }
+    if w.name == "llama_loop":
+        res = run_loop(args, w, torch, q, dev)
+    elif w.n_layers > 1 or w.n_seqs > 1:
+        res = run_layers(args, w, torch, q, dev)
+    else:
+        res = run_layer(args, w, args.ctx or w.ctx, torch, q, dev)
+    line = {"metric": METRIC, "value": res.pop("value"), "unit": "GB/s", "n_gpus": 1, "steps": res.pop("steps"),
+            "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": path_dtype(w), "data": "synthetic",
+            "config": res.pop("config")}
+    line.update(res)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
-        res["cpu_baseline"] = cpu_baseline(args.workload)
-    print(json.dumps(res), flush=True)
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

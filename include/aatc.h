@@ -311,6 +311,19 @@ int aatc_decode_attention_append(const aatc_codebook* cb, const void* d_blob, co
  * evict the device's last-level cache between timed repetitions).  Errors: HIP. */
 int aatc_flush_write(void* d_buf, size_t bytes, void* stream);
 
+/* Streaming-read probe: one launch on `stream` reads `bytes` of caller-allocated device
+ * memory d_src the way a decode step reads its cache, to measure the HBM read rate the
+ * decode kernel can be held to ("Spend Bits Where Queries Look", abstract: decoding is
+ * bandwidth-bound).  mode 0: plain 16-byte register loads over the whole buffer; mode 1:
+ * tiles of tile_bytes bytes (a multiple of 256, at most 6656) streamed into LDS like the
+ * decode kernel's ring (one 768-thread workgroup per CU, even share, two slots per wave),
+ * over the first floor(bytes / tile_bytes) tiles (at most 2^31 - 1 bytes).  d_sink: 16
+ * bytes of device memory the probe may write (it never does for real data: the loaded
+ * words only feed a checksum).  Both pointers 16-byte aligned.
+ * Errors: INVALID_ARG, CAPACITY, HIP. */
+int aatc_read_probe(const void* d_src, size_t bytes, int32_t mode, int32_t tile_bytes, void* d_sink,
+                    void* stream);
+
 /* Kernel timing for measurement: after aatc_profile_begin(n) the next n calls of
  * aatc_decode_attention (any thread, current device) record a pair of device events
  * around their split-decode kernel on the call's stream (the query-preparation kernel

@@ -53,7 +53,7 @@ EXPORTS = [
     "aatc_codebook_head", "aatc_codebook_fields", "aatc_codebook_save", "aatc_codebook_load", "aatc_codebook_free",
     "aatc_codebook_device_bytes", "aatc_codebook_upload", "aatc_cache_bytes", "aatc_encode",
     "aatc_encode_coeffs", "aatc_decode_workspace_bytes", "aatc_decode_attention",
-    "aatc_decode_attention_append", "aatc_flush_write", "aatc_profile_begin", "aatc_profile_end",
+    "aatc_decode_attention_append", "aatc_flush_write", "aatc_read_probe", "aatc_profile_begin", "aatc_profile_end",
 ]
 
 _lib = None
@@ -102,6 +102,7 @@ def load() -> C.CDLL:
         "aatc_decode_attention_append": ([P, P, C.POINTER(Cache), i32, i32, P, P, i64, P, P, P, P, P, C.c_size_t, P],
                                          C.c_int),
         "aatc_flush_write": ([P, C.c_size_t, P], C.c_int),
+        "aatc_read_probe": ([P, C.c_size_t, i32, i32, P, P], C.c_int),
         "aatc_profile_begin": ([i32], C.c_int),
         "aatc_profile_end": ([C.POINTER(C.c_float), C.POINTER(i32)], C.c_int),
     }
@@ -357,6 +358,13 @@ def decode_attention_append(cb: Codebook, d_blob, cache: Cache, layer: int, seq_
 
 def flush_write(buf, stream=None):
     _check(load().aatc_flush_write(_dev(buf), buf.numel() * buf.element_size(), _stream(stream)))
+
+
+def read_probe(src, mode: int, sink, tile_bytes: int = 0, nbytes: int | None = None, stream=None):
+    """aatc_read_probe: stream `nbytes` (default: all) of device tensor src; mode 0 register
+    loads, mode 1 tiles of tile_bytes into LDS like the decode kernel."""
+    n = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(load().aatc_read_probe(_dev(src), n, mode, tile_bytes, _dev(sink), _stream(stream)))
 
 
 def profile_begin(n: int):

@@ -338,6 +338,11 @@ __device__ __forceinline__ void append_block(const DevHead& H, const uint16_t* x
 // and the channel tables; then reductions in LDS.
 // ---------------------------------------------------------------------------------------
 constexpr int kFuseMaxW = 64;       // partials per (sequence, kv-head) the last workgroup merges
+// ... and their bytes: one CU reads them all, so a large merge (the 128k Llama layer: 32
+// partials x 4 heads, 68 KB; the Qwen layer: 64 x 7, 236 KB) is faster as the separate
+// merge kernel spread over many CUs, despite its launch (measured: 5.3 vs 5.2 us and 10 vs
+// 5 us); small merges (one workgroup per sequence in a batch) are fused
+constexpr int kFuseMaxBytes = 32 * 1024;
 constexpr int kFuseMaxPairs = 256;  // (sequence, kv-head) pairs per fused call: one counter each
 constexpr int kFuseRows = 8;        // partial rows per thread and round
 constexpr size_t kCounterBytes = 4 * kFuseMaxPairs;  // the workspace's first bytes: arrival counters
@@ -1005,7 +1010,7 @@ static_assert(offsetof(DevHead, kq_slot) % 16 == 0 && offsetof(DevHead, kq_sched
                   offsetof(DevHead, vb_col) % 16 == 0,
               "the decode prologue copies these tables 16 bytes per lane");
 constexpr int kMergeSlice = 32;  // output channels per merge workgroup
-constexpr int kMergeRows = 8;    // partial rows per thread and round
+constexpr int kMergeRows = 12;   // partial rows per thread and round (84 partials in one round)
 constexpr int kMaxWG = 256;      // workgroups per (sequence, kv-head) at most (one per CU)
 constexpr int kMaxPL = kPartHead + 16 * aatc::kMaxVB;
 
@@ -1467,6 +1472,7 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     // partials, one counter per pair, a partial row within one workgroup's threads, and the
     // merge's LDS below the arrival words
     a.fused = pairs <= kFuseMaxPairs && p.wg_per_head <= kFuseMaxW && G * a.part_ld / 4 <= 64 * NW &&
+              (size_t)p.wg_per_head * G * a.part_ld * sizeof(float) <= kFuseMaxBytes &&
               merge_lds_bytes(G, a.part_ld, d, 64 * NW) <= a.off_sync;
     return AATC_OK;
 }
