@@ -287,6 +287,20 @@ int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob, const aat
                           const int64_t* seq_lens, int64_t max_len, const uint16_t* q,
                           float* out, void* workspace, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving
+ * loops that forbid allocation): aatc_decode_attention with its partials and arrival
+ * counters in an 8 MiB device array of the library's own (one per GPU, held until the
+ * process ends) instead of a caller workspace; nothing is allocated.  The counters are zero
+ * when the library is loaded and every call leaves them at zero.  All calls on one GPU
+ * share the array: calls that overlap in time on the same GPU race (issue them on one
+ * stream, or order them).  Other arguments as aatc_decode_attention.
+ * Errors: CAPACITY when the call needs more than 8 MiB of partials
+ * (aatc_decode_workspace_bytes > 8 MiB), otherwise as aatc_decode_attention. */
+int aatc_decode_attention_static(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
+                                 int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                                 const int64_t* seq_lens, int64_t max_len, const uint16_t* q, float* out,
+                                 void* stream);
+
 /* One generation step of one layer: append one token per sequence, then decode over the
  * grown cache, in the same launch.  k_new, v_new: device bf16 [n_seqs][n_kv][d] (16-byte
  * aligned); the token of sequence s is written at slot seq_lens[s] (device array: the

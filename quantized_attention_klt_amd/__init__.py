@@ -53,7 +53,8 @@ EXPORTS = [
     "aatc_codebook_head", "aatc_codebook_fields", "aatc_codebook_save", "aatc_codebook_load", "aatc_codebook_free",
     "aatc_codebook_device_bytes", "aatc_codebook_upload", "aatc_cache_bytes", "aatc_encode",
     "aatc_encode_coeffs", "aatc_decode_workspace_bytes", "aatc_decode_attention",
-    "aatc_decode_attention_append", "aatc_flush_write", "aatc_read_probe", "aatc_profile_begin", "aatc_profile_end",
+    "aatc_decode_attention_append", "aatc_decode_attention_static", "aatc_flush_write", "aatc_read_probe",
+    "aatc_profile_begin", "aatc_profile_end",
 ]
 
 _lib = None
@@ -101,6 +102,7 @@ def load() -> C.CDLL:
                                   C.c_int),
         "aatc_decode_attention_append": ([P, P, C.POINTER(Cache), i32, i32, P, P, i64, P, P, P, P, P, C.c_size_t, P],
                                          C.c_int),
+        "aatc_decode_attention_static": ([P, P, C.POINTER(Cache), i32, i32, P, P, i64, P, P, P], C.c_int),
         "aatc_flush_write": ([P, C.c_size_t, P], C.c_int),
         "aatc_read_probe": ([P, C.c_size_t, i32, i32, P, P], C.c_int),
         "aatc_profile_begin": ([i32], C.c_int),
@@ -354,6 +356,15 @@ def decode_attention_append(cb: Codebook, d_blob, cache: Cache, layer: int, seq_
                                                _dev(seq_ids), _dev(seq_lens), max_len, _dev(k_new), _dev(v_new),
                                                _dev(q), _dev(out), _dev(workspace),
                                                workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def decode_attention_static(cb: Codebook, d_blob, cache: Cache, layer: int, seq_ids, seq_lens, max_len: int, q,
+                            out, stream=None):
+    """aatc_decode_attention_static: as decode_attention, with the partials in the library's
+    own device array instead of a caller workspace (no allocation anywhere in the call)."""
+    _check(load().aatc_decode_attention_static(cb.handle, _dev(d_blob), C.byref(cache), layer, seq_ids.numel(),
+                                               _dev(seq_ids), _dev(seq_lens), max_len, _dev(q), _dev(out),
+                                               _stream(stream)))
 
 
 def flush_write(buf, stream=None):

@@ -1679,6 +1679,58 @@ extern "C" int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob
                        workspace, ws_bytes, stream);
 }
 
+// ---------------------------------------------------------------------------------------
+// Decode without a caller-provided workspace: the partials and arrival counters live in a
+// file-scope device array, one copy per GPU, for callers that cannot allocate device memory
+// (code under graph capture, serving loops that forbid allocation).  Host code uses the
+// array only through the address hipGetSymbolAddress returns for the current device (the
+// array's name on the host is a stand-in, not a device address).  The arrival counters
+// (the first bytes) are zero when the code object is loaded and every call leaves them at
+// zero; the partials are overwritten by each call before they are read.  Calls that overlap
+// in time on one GPU share the array and race.
+// ---------------------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];  // per device: the device address of `scratch`, once looked up
+
+// the current device's copy of the scratch array (looked up once per device)
+static int static_scratch(void** out) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return set_error(AATC_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+        if (!ptr) return set_error(AATC_ERR_HIP, "hipGetSymbolAddress returned a null address");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return AATC_OK;
+}
+
+extern "C" int aatc_decode_attention_static(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
+                                            int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                                            const int64_t* seq_lens, int64_t max_len, const uint16_t* q, float* out,
+                                            void* stream) {
+    if (!cb) return set_error(AATC_ERR_INVALID_ARG, "null codebook");
+    if (n_seqs < 1 || max_len < 1) return set_error(AATC_ERR_INVALID_ARG, "need n_seqs >= 1 and max_len >= 1");
+    size_t need = 0;
+    int rc = aatc_decode_workspace_bytes(cb, n_seqs, max_len, &need);
+    if (rc) return rc;
+    if (need > kStaticScratchBytes)
+        return set_error(AATC_ERR_CAPACITY, "the call needs %zu bytes of partials, the static scratch holds %zu", need,
+                         kStaticScratchBytes);
+    void* ws = nullptr;
+    rc = static_scratch(&ws);
+    if (rc) return rc;
+    return decode_impl(cb, d_blob, cache, layer, n_seqs, seq_ids, seq_lens, max_len, nullptr, nullptr, q, out, ws,
+                       kStaticScratchBytes, stream);
+}
+
 extern "C" int aatc_decode_attention_append(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
                                             int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                                             const int64_t* seq_lens, int64_t max_len, const uint16_t* k_new,
