@@ -36,6 +36,8 @@ import time
 
 import numpy as np
 
+import synth
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -78,7 +80,6 @@ def path_dtype(w) -> str:
 
 def calibrate(w, q, n_layers: int):
     """Library host calibration of every (layer, kv-head) of the workload."""
-    import synth
     t0 = time.perf_counter()
     stats, hms = [], []
     for layer in range(n_layers):
@@ -96,40 +97,6 @@ def calibrate(w, q, n_layers: int):
     t2 = time.perf_counter()
     log(f"calibration of {len(stats)} heads: stats {t1 - t0:.2f}s, calibrate {t2 - t1:.2f}s")
     return cb, hms, t2 - t0
-
-
-def gpu_draws(torch, hm, n: int, seed: int, dev):
-    """n seeded K and V rows of one (layer, kv-head) on the GPU, bf16 [n, d]: the head
-    model's recipe x = mu + U diag(sqrt(lambda)) z (outlier channels x10), with z from
-    torch's device generator (the same distribution as synth.cache_kv, another stream)."""
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(seed)
-    out = []
-    for U, lam, mu, ch in ((hm.UK, hm.lamK, hm.muK, hm.outK), (hm.UV, hm.lamV, hm.muV, hm.outV)):
-        z = torch.randn((n, hm.d), generator=gen, device=dev, dtype=torch.float32)
-        A = torch.from_numpy((U * np.sqrt(lam)[None, :]).T.astype(np.float32)).to(dev)
-        x = z @ A + torch.from_numpy(mu.astype(np.float32)).to(dev)
-        if ch.size:
-            x[:, torch.from_numpy(ch).to(dev)] *= 10.0
-        out.append(x.to(torch.bfloat16).view(torch.int16))
-    return out
-
-
-def gpu_queries(torch, hm, w, seed: int, dev):
-    """One decode step's queries of the G query heads of a kv-head, bf16 [G, d]."""
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(seed)
-    qs = []
-    for g in range(w.group):
-        z = torch.randn((hm.d,), generator=gen, device=dev, dtype=torch.float32)
-        A = torch.from_numpy((hm.UQ[g] * np.sqrt(hm.lamQ[g])[None, :]).T.astype(np.float32)).to(dev)
-        qs.append(z @ A)
-    return torch.stack(qs).to(torch.bfloat16).view(torch.int16)
-
-
-def seed_of(*parts) -> int:
-    import synth
-    return int(np.random.SeedSequence([synth.S0, *parts]).generate_state(1, np.uint64)[0] >> 1)
 
 
 def source_hash(path: str) -> str:
@@ -176,7 +143,6 @@ def cpu_baseline(wname: str, n_tokens: int = 16384):
     """Oracle (numpy, float64) on a bounded sample: one kv-head of the workload's first
     layer, n_tokens tokens - oracle encode then oracle decode of its query-head group."""
     import oracle
-    import synth
     w = synth.WORKLOADS[wname]
     hm = synth.head_model(w, 0, 0)
     K, V, Q = synth.calibration_samples(w, hm, 0, 0)
@@ -259,7 +225,6 @@ def probe_rates(torch, q, dev, nbytes: int, tile_bytes: int, cache_t, flush, rep
 
 # ---------------------------------------------------------------------------- one layer
 def run_layer(args, w, ctx, torch, q, dev):
-    import synth
     cb, hms, calib_s = calibrate(w, q, 1)
     blob = torch.empty(cb.device_bytes(), dtype=torch.uint8, device=dev)
     cb.upload(blob)
@@ -398,7 +363,8 @@ def run_layers(args, w, torch, q, dev):
         V = torch.empty_like(K)
         for s in range(S):
             for h in range(w.n_kv):
-                k, v = gpu_draws(torch, hms[layer * w.n_kv + h], ctx, seed_of(w.cfg, layer, s, h, 6), dev)
+                k, v = synth.device_kv(torch, hms[layer * w.n_kv + h], ctx,
+                                       synth.seed_of(w.cfg, layer, s, h, synth.ST_CACHE_KV), dev)
                 K[s, :, h] = k
                 V[s, :, h] = v
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -409,8 +375,9 @@ def run_layers(args, w, torch, q, dev):
         enc_ms.append(e0.elapsed_time(e1))
         del K, V
     log(f"prefill of {L} layers x {S} sequences x {ctx} tokens ({time.perf_counter() - t0:.1f}s)")
-    Qd = torch.stack([torch.stack([torch.cat([gpu_queries(torch, hms[layer * w.n_kv + h], w,
-                                                          seed_of(w.cfg, layer, s, h, 8), dev)
+    Qd = torch.stack([torch.stack([torch.cat([synth.device_queries(torch, hms[layer * w.n_kv + h], w.group,
+                                                                   synth.seed_of(w.cfg, layer, s, h, synth.ST_DECODE_Q),
+                                                                   dev)[0]
                                               for h in range(w.n_kv)]) for s in range(S)]) for layer in range(L)])
     out = torch.empty((L, S, w.n_q, w.d), dtype=torch.float32, device=dev)
     ws = torch.zeros(cb.decode_workspace_bytes(S, ctx), dtype=torch.uint8, device=dev)
@@ -495,7 +462,7 @@ def run_loop(args, w, torch, q, dev):
     K = torch.empty((1, l0, w.n_kv, w.d), dtype=torch.int16, device=dev)
     V = torch.empty_like(K)
     for h in range(w.n_kv):
-        k, v = gpu_draws(torch, hms[h], l0, seed_of(w.cfg, 0, 0, h, 6), dev)
+        k, v = synth.device_kv(torch, hms[h], l0, synth.seed_of(w.cfg, 0, 0, h, synth.ST_CACHE_KV), dev)
         K[0, :, h] = k
         V[0, :, h] = v
     q.encode(cb, blob, cache, 0, [0], [0], l0, K, V)
@@ -505,11 +472,11 @@ def run_loop(args, w, torch, q, dev):
     vn = torch.empty_like(kn)
     qn = torch.empty((n, 1, w.n_q, w.d), dtype=torch.int16, device=dev)
     for h in range(w.n_kv):
-        k, v = gpu_draws(torch, hms[h], n, seed_of(w.cfg, 0, 0, h, 9), dev)
+        k, v = synth.device_kv(torch, hms[h], n, synth.seed_of(w.cfg, 0, 0, h, synth.ST_STEP), dev)
         kn[:, 0, h] = k
         vn[:, 0, h] = v
-        for i in range(n):
-            qn[i, 0, h * w.group:(h + 1) * w.group] = gpu_queries(torch, hms[h], w, seed_of(w.cfg, 0, 0, h, 9, i), dev)
+        qn[:, 0, h * w.group:(h + 1) * w.group] = synth.device_queries(
+            torch, hms[h], w.group, synth.seed_of(w.cfg, 0, 0, h, synth.ST_DECODE_Q), dev, n)
     lens_all = torch.arange(l0, l0 + n, dtype=torch.int64, device=dev)  # tokens cached before step i
     out = torch.empty((n, 1, w.n_q, w.d), dtype=torch.float32, device=dev)
     ws = torch.zeros(cb.decode_workspace_bytes(1, cap), dtype=torch.uint8, device=dev)
@@ -600,7 +567,6 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
-    import synth
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     if w.name == "llama_loop":

@@ -144,7 +144,13 @@ int aatc_stats_from_samples(int32_t d, const float* K, const float* V, int64_t n
                             const float* Q, int64_t nq, double* mu_k, double* mu_v,
                             double* sigma_k, double* sigma_v, double* m_q, double* gamma_v);
 
-/* Calibrate n_layers * n_kv heads (stats indexed layer*n_kv + head): eigendecomposition of
+/* Calibration ("Attention-Aware Transform Coding Guide": "Decorrelation via the
+ * Karhunen-Loeve Transform" for the bases, "Optimal Bit Allocation via Reverse
+ * Water-Filling" for the weights, the water level and the integer bits; "KV Cache
+ * Compression Through the Lens of Transform Coding", Methodology, for the
+ * attention-aware key and value weights; "Spend Bits Where Queries Look", abstract, for
+ * the fixed bit count per token that the exact integer total keeps).
+ * Calibrate n_layers * n_kv heads (stats indexed layer*n_kv + head): eigendecomposition of
  * both covariances (eigenvalues descending; each eigenvector's largest-magnitude entry
  * positive), channel weights x_K = lambda_K (U_K^T M_Q U_K)_jj / d and
  * x_V = lambda_V gamma_V, integer bits in [0, max_bits] with an exact total per token
@@ -235,7 +241,12 @@ int aatc_codebook_upload(const aatc_codebook* cb, void* d_blob, size_t bytes, vo
 int aatc_cache_bytes(const aatc_codebook* cb, int32_t n_layers, int32_t n_seqs,
                      int64_t max_tokens, size_t* bytes);
 
-/* Append n_tokens tokens to each of n_seqs sequences of one layer.
+/* Encoder ("Attention-Aware Transform Coding Guide", "Decorrelation via the
+ * Karhunen-Loeve Transform": coefficients c = (x - mu) U; its code listing, read as a
+ * per-channel uniform scalar quantizer at the allotted width; "Spend Bits Where Queries
+ * Look", abstract: a fixed number of bits per token, which the 64-token tiles of
+ * 8 * B bytes keep).
+ * Append n_tokens tokens to each of n_seqs sequences of one layer.
  * seq_ids [n_seqs], start_pos [n_seqs]: host arrays; sequence s writes token slots
  * start_pos[s] .. start_pos[s]+n_tokens-1.  K, V: device bf16 [n_seqs][n_tokens][n_kv][d]
  * (contiguous).  The slots being written are rebuilt; the other slots of a partially
@@ -248,7 +259,10 @@ int aatc_encode(const aatc_codebook* cb, const void* d_blob, const aatc_cache* c
                 const int64_t* start_pos, int64_t n_tokens, const uint16_t* K,
                 const uint16_t* V, void* stream);
 
-/* Encode given KLT coefficients (skips the projection): coeffs device float32
+/* Quantize and pack given KLT coefficients ("Attention-Aware Transform Coding Guide",
+ * code listing, read as a midrise uniform quantizer per channel; the 2^b-level step that
+ * minimizes the mean squared error of a unit Gaussian, scaled by sqrt(lambda_j), is this
+ * library's reading of the same section's quantizer).  Skips the projection: coeffs device float32
  * [n_tokens][n_kv][2][d] (keys then values, KLT channel order) for one (layer, seq)
  * starting at slot start_pos.  Code of channel j with b > 0 bits:
  * t = fp32(c * fp32(1/step_j)) (one rounding), code = clamp(floor(t) + 2^(b-1), 0, 2^b-1).

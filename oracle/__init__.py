@@ -42,5 +42,5 @@ from .vq import (  # noqa: F401
     group_codebooks, vq_scales, vq_encode, vq_dequantize,
 )
 from .attention import (  # noqa: F401
-    attention, decode_attention, predicted_distortion, monte_carlo_distortion,
+    attention, decoded_kv, decode_attention, predicted_distortion, monte_carlo_distortion,
 )

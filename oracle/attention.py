@@ -24,10 +24,9 @@ def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
     return p @ V
 
 
-def decode_attention(cache: np.ndarray, cb, q_heads: np.ndarray, n_tokens: int) -> np.ndarray:
-    """Attention of the query heads of one kv-head group over the first n_tokens of a
-    packed cache: unpack, dequantize, inverse transform, then plain attention (every
-    cached token is attended; no mask).  q_heads [G, d] -> out [G, d] float64."""
+def decoded_kv(cache: np.ndarray, cb, n_tokens: int):
+    """The keys and values a packed cache stands for, first n_tokens tokens: unpack,
+    dequantize, inverse transform.  -> (K_hat, V_hat) [n_tokens, d] float64."""
     cK, cV = unpack_cache(cache, key_record_bits(cb), cb.bV, n_tokens)
     if cb.vq is not None:
         chatK = vq_dequantize(cK, cb.vq.groups, cb.vq.scale32, cb.vq.cent32, cb.d)
@@ -35,6 +34,14 @@ def decode_attention(cache: np.ndarray, cb, q_heads: np.ndarray, n_tokens: int) 
         chatK = dequantize(cK, cb.bK, cb.stepK)
     Khat = cb.muK[None, :] + chatK @ cb.UKinv  # c = (k - mu) T  =>  k = mu + c T^{-1}
     Vhat = reconstruct(dequantize(cV, cb.bV, cb.stepV), cb.muV, cb.UV)
+    return Khat, Vhat
+
+
+def decode_attention(cache: np.ndarray, cb, q_heads: np.ndarray, n_tokens: int) -> np.ndarray:
+    """Attention of the query heads of one kv-head group over the first n_tokens of a
+    packed cache: the decoded keys and values, then plain attention (every cached token
+    is attended; no mask).  q_heads [G, d] -> out [G, d] float64."""
+    Khat, Vhat = decoded_kv(cache, cb, n_tokens)
     return attention(q_heads, Khat, Vhat)
 
 

@@ -123,6 +123,10 @@ WORKLOADS: Dict[str, Workload] = {
     # ... at 1.0 bit/element: 8 groups code the 32 coefficients of largest weight
     "vq_low": Workload("vq_low", 10, 64, 1, 4, 1, 1, 512, 1.0, 2048, 256, "bf16"),
     "llama_vq_128k": Workload("llama_vq_128k", 9, 128, 8, 32, 1, 1, 131072, 2.0, 8192, 256, "bf16"),
+    # vector-quantized keys with 7 query heads per kv-head (the Qwen group, d = 128) and
+    # with 2 (d = 64): group sizes the other vector-quantized workloads do not reach
+    "vq_g7": Workload("vq_g7", 11, 128, 2, 14, 1, 1, 4096, 2.0, 4096, 64, "bf16"),
+    "vq_g2": Workload("vq_g2", 12, 64, 2, 4, 1, 1, 4096, 2.0, 2048, 64, "bf16"),
 }
 
 
@@ -244,3 +248,43 @@ def as_cache_dtype(w: Workload, x: np.ndarray):
     """Values as stored at the cache boundary: (bf16 bits, float64 values of those bits)."""
     bits = to_bf16_bits(x)
     return bits, bf16_bits_to_f64(bits)
+
+
+# ------------------------------------------------------------------ device-side draws
+# Large workloads are drawn on the GPU with torch's device generator: the same recipe
+# as draw_kv / draw_q (x = mu + U diag(sqrt(lambda)) z, outlier channels x10), another
+# random stream.  Seeds come from seed_of, so any (layer, seq, head, stream) slice can be
+# drawn again on its own.
+
+def seed_of(*parts) -> int:
+    """63-bit torch generator seed for the slice named by parts (cfg, layer, seq, head, stream, ...)."""
+    return int(np.random.SeedSequence([S0, *parts]).generate_state(1, np.uint64)[0] >> 1)
+
+
+def device_kv(torch, hm: HeadModel, n: int, seed: int, dev):
+    """n seeded K and V rows of one (layer, kv-head) on device dev: bf16 bit patterns as
+    int16 tensors [n, d] (the z draws are fp32; the product rounds once to bf16)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    out = []
+    for U, lam, mu, ch in ((hm.UK, hm.lamK, hm.muK, hm.outK), (hm.UV, hm.lamV, hm.muV, hm.outV)):
+        z = torch.randn((n, hm.d), generator=gen, device=dev, dtype=torch.float32)
+        A = torch.from_numpy((U * np.sqrt(lam)[None, :]).T.astype(np.float32)).to(dev)
+        x = z @ A + torch.from_numpy(mu.astype(np.float32)).to(dev)
+        if ch.size:
+            x[:, torch.from_numpy(ch).to(dev)] *= 10.0
+        out.append(x.to(torch.bfloat16).view(torch.int16))
+    return out
+
+
+def device_queries(torch, hm: HeadModel, group: int, seed: int, dev, n: int = 1):
+    """n decode steps' queries of the group's query heads on device dev: bf16 bit patterns
+    as int16 [n, group, d]."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    qs = []
+    for g in range(group):
+        z = torch.randn((n, hm.d), generator=gen, device=dev, dtype=torch.float32)
+        A = torch.from_numpy((hm.UQ[g] * np.sqrt(hm.lamQ[g])[None, :]).T.astype(np.float32)).to(dev)
+        qs.append(z @ A)
+    return torch.stack(qs, dim=1).to(torch.bfloat16).view(torch.int16)

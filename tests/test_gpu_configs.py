@@ -10,7 +10,7 @@
 
 Bars as in the other parity tests: attention within 2e-3 normwise relative error of the
 oracle on the same bytes; end-to-end codes differ on at most 1e-4 of coded pairs, by one
-level.
+level, each within the fp32 rounding window of a cell edge.
 """
 import numpy as np
 import pytest
@@ -18,7 +18,7 @@ import pytest
 import oracle
 import synth
 from test_gpu_parity import _decode, _device_codebook, _new_cache
-from util import Case, normwise_rel_err
+from util import Case, code_flips, normwise_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -39,18 +39,10 @@ def _log(msg):
 
 
 def _flips(got_bytes, case, h, n_tokens, K64, V64):
-    """(flips, coded pairs, worst level difference) of kv-head h's codes against the oracle's."""
-    c = case.cbs[h]
-    gK, gV = oracle.unpack_cache(got_bytes, c.bK, c.bV, n_tokens)
-    rK = oracle.quantize(oracle.transform_coeffs(K64, c.muK, c.UK), c.inv_step("K"), c.bK)
-    rV = oracle.quantize(oracle.transform_coeffs(V64, c.muV, c.UV), c.inv_step("V"), c.bV)
-    flips = total = worst = 0
-    for g, r, b in ((gK, rK, c.bK), (gV, rV, c.bV)):
-        m = np.broadcast_to(b > 0, g.shape)
-        dlt = np.abs(g.astype(np.int64) - r.astype(np.int64))[m]
-        flips += int((dlt > 0).sum())
-        total += int(m.sum())
-        worst = max(worst, int(dlt.max()))
+    """(flips, coded pairs, worst level difference) of kv-head h's codes against the
+    oracle's; every flipped code must lie in the fp32 rounding window of a cell edge."""
+    flips, total, worst, edge = code_flips(got_bytes, case.cbs[h], n_tokens, K64, V64)
+    assert edge <= 1.0, f"kv-head {h}: a flipped code lies {edge:.3g} windows from a cell edge"
     return flips, total, worst
 
 

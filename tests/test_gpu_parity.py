@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
-from util import Case, normwise_rel_err
+from util import Case, code_flips, normwise_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -93,19 +93,14 @@ def test_encode_end_to_end_flips(lib, torch, wname, ctx, chunks):
         pos += n
     torch.cuda.synchronize()
     got = ct.cpu().numpy().reshape(case.n_kv, -1)
-    ref, codes = case.oracle_cache()
-    flips, total, worst = 0, 0, 0
+    flips = total = worst = 0
+    edge = 0.0
     for h, c in enumerate(case.cbs):
-        gK, gV = oracle.unpack_cache(got[h], c.bK, c.bV, ctx)
-        rK, rV = codes[(0, h)]
-        for g, r, b in ((gK, rK, c.bK), (gV, rV, c.bV)):
-            m = np.broadcast_to(b > 0, g.shape)
-            dlt = np.abs(g - r)[m]
-            flips += int((dlt > 0).sum())
-            total += int(m.sum())
-            worst = max(worst, int(dlt.max()))
-    _log(f"  flips {flips}/{total}")
+        f, t, wst, e = code_flips(got[h], c, ctx, case.kf(0, h), case.vf(0, h))
+        flips, total, worst, edge = flips + f, total + t, max(worst, wst), max(edge, e)
+    _log(f"  flips {flips}/{total}, worst edge ratio {edge:.3g}")
     assert worst <= 1
+    assert edge <= 1.0  # every flipped code sits within the fp32 rounding window of a cell edge
     assert flips <= FLIP_BAR * total
 
 

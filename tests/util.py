@@ -118,3 +118,64 @@ def normwise_rel_err(o, ref):
     o = np.asarray(o, np.float64).reshape(-1, o.shape[-1])
     ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
     return float((np.abs(o - ref).max(axis=1) / np.abs(ref).max(axis=1)).max())
+
+
+# ------------------------------------------------------------ end-to-end code flips
+# The GPU encoder computes a coefficient c = (x - mu) U in fp32 from bf16 x, with U held
+# as two bf16 parts (hi + lo, which leaves |U - hi - lo| <= 2^-18 |U|) or in fp32, and the
+# mean folded into a bias or subtracted first.  Its quantizer input t = c / step then
+# differs from the exact one by at most
+#     E = (2^-17 + (d + 4) 2^-24) S / step + 4 2^-24 |t|,   S = sum_i (|x_i| + |mu_i|) |U_ij|
+# (split error of U, fp32 accumulation over d terms, bias and product roundings, with
+# margin), and the oracle's fp32 t (c rounded once, then the product) by at most
+# 2 2^-24 |t|.  Codes are floor(t) + 2^(b-1), so the two codes can differ only where
+# the exact t lies within E of an integer: every flipped code is checked for that.
+_U24 = 2.0 ** -24
+
+
+def edge_ratio(x64, mu, U, inv32, idx):
+    """max over (token, channel) pairs idx [n, 2] of (distance of the exact t from the
+    nearest integer) / E; a flip outside the rounding window gives a ratio above 1."""
+    if len(idx) == 0:
+        return 0.0
+    rows, ch = idx[:, 0], idx[:, 1]
+    X = np.asarray(x64, np.float64)[rows] - mu[None, :]
+    Uc = np.asarray(U, np.float64)[:, ch].T  # [n, d]
+    inv = inv32[ch].astype(np.float64)
+    t = (X * Uc).sum(axis=1) * inv
+    S = ((np.abs(np.asarray(x64, np.float64)[rows]) + np.abs(mu)[None, :]) * np.abs(Uc)).sum(axis=1)
+    d = Uc.shape[1]
+    bound = (2.0 ** -17 + (d + 4) * _U24) * S * inv + 4 * _U24 * np.abs(t)
+    return float((np.abs(t - np.round(t)) / bound).max())
+
+
+def code_flips(got_bytes, cb, n_tokens, K64, V64, first=0):
+    """Codes of the GPU's packed bytes for tokens [first, n_tokens) against the oracle's
+    codes of the same bf16 rows (K64, V64 hold exactly those rows).  Scalar-coded
+    channels only (vector-quantized keys are compared by their own near-tie test).
+    Returns (flips, coded pairs, worst level difference, worst edge ratio)."""
+    gK, gV = oracle.unpack_cache(got_bytes, oracle.key_record_bits(cb), cb.bV, n_tokens)
+    flips = total = worst = 0
+    edge = 0.0
+    for which, g, x64, U, mu, bits in (("K", gK, K64, cb.UK, cb.muK, cb.bK), ("V", gV, V64, cb.UV, cb.muV, cb.bV)):
+        if which == "K" and cb.vq is not None:
+            continue
+        g = g[first:]
+        r = oracle.quantize(oracle.transform_coeffs(x64, mu, U), cb.inv_step(which), bits)
+        m = np.broadcast_to(bits > 0, g.shape)
+        dlt = np.abs(g.astype(np.int64) - r.astype(np.int64))
+        bad = (dlt > 0) & m
+        flips += int(bad.sum())
+        total += int(m.sum())
+        worst = max(worst, int(dlt[m].max(initial=0)))
+        edge = max(edge, edge_ratio(x64, mu, U, cb.inv_step(which), np.argwhere(bad)))
+    return flips, total, worst, edge
+
+
+def library_head_codebook(cb, i: int):
+    """The library's calibrated codebook of head i (layer-major) as an oracle codebook, so
+    that the oracle decodes the bytes the library's parameters produced."""
+    h = cb.head(i)
+    return oracle.HeadCodebook(d=cb.d, UK=h["UK"], UV=h["UV"], lamK=h["lamK"], lamV=h["lamV"], muK=h["muK"],
+                               muV=h["muV"], xK=h["xK"], xV=h["xV"], bK=h["bK"], bV=h["bV"], stepK=h["stepK"],
+                               stepV=h["stepV"], theta=h["theta"])
