@@ -251,8 +251,12 @@ int aatc_cache_bytes(const aatc_codebook* cb, int32_t n_layers, int32_t n_seqs,
  * start_pos[s] .. start_pos[s]+n_tokens-1.  K, V: device bf16 [n_seqs][n_tokens][n_kv][d]
  * (contiguous).  The slots being written are rebuilt; the other slots of a partially
  * filled tile are kept (the tile is read, merged and written back).
- * Coefficients: c = x (U_hi + U_lo) - mu (U_hi + U_lo) with U_hi/U_lo the bf16 split of
- * U (bf16 MFMA, fp32 accumulation); codes as the quantizer of aatc_encode_coeffs.
+ * Arithmetic: u = x (W_hi + W_lo) + (2^(b-1) - 1/2 - mu (W_hi + W_lo)) with W = U scaled
+ * per channel by the fp32 reciprocal step and W_hi/W_lo its bf16 split (bf16 MFMA, fp32
+ * accumulation, the start value rounded once from fp64); code = u clamped to
+ * [0, 2^b - 1] and rounded to nearest, ties to even.  That is the quantizer of
+ * aatc_encode_coeffs, floor(c/step) + 2^(b-1), wherever c/step is not within the fp32
+ * rounding of this arithmetic of a cell edge.
  * Errors: INVALID_ARG, CAPACITY (start_pos + n_tokens > max_tokens), HIP. */
 int aatc_encode(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
                 int32_t layer, int32_t n_seqs, const int32_t* seq_ids,

@@ -58,12 +58,14 @@ struct alignas(256) DevHead {
     float UK[kMaxD * kMaxD];      // fp32 basis (query transform)
     float UV[kMaxD * kMaxD];      // fp32 basis (inverse transform of values)
     float UVt[kMaxD * kMaxD];     // its transpose, UVt[j*d + i] = UV[i*d + j]
-    // bf16 split of the bases, channel-major: UKt_hi[j*d + i] + UKt_lo[j*d + i] = U_K[i][j]
-    // (+ rounding), the MFMA operand order (16 consecutive bytes along i)
-    uint16_t UKt_hi[kMaxD * kMaxD];
-    uint16_t UKt_lo[kMaxD * kMaxD];
-    uint16_t UVt_hi[kMaxD * kMaxD];
-    uint16_t UVt_lo[kMaxD * kMaxD];
+    // Encoder bases W = U diag(1/step) (the quantizer's scale folded into the projection;
+    // zero columns for uncoded channels), bf16 split, channel-major: EKt_hi[j*d + i] +
+    // EKt_lo[j*d + i] = fp32(U_K[i][j] * invK[j]) (+ rounding), the MFMA operand order (16
+    // consecutive bytes along i)
+    uint16_t EKt_hi[kMaxD * kMaxD];
+    uint16_t EKt_lo[kMaxD * kMaxD];
+    uint16_t EVt_hi[kMaxD * kMaxD];
+    uint16_t EVt_lo[kMaxD * kMaxD];
     // query transform q' = T_K^{-1} q (T_K the key basis; T_K^{-1} = U_K^T for the KLT),
     // bf16 split in the same layout: QKt_hi[j*d + i] + QKt_lo[j*d + i] = (T_K^{-1})[j][i]
     uint16_t QKt_hi[kMaxD * kMaxD];
@@ -71,8 +73,10 @@ struct alignas(256) DevHead {
     float muV[kMaxD];
     float muK[kMaxD];
     float obias[kMaxD];           // mu_V - U_V (step_V * (2^(b-1) - 1/2)): output of all-zero codes
-    float biasK[kMaxD];           // mu_K (U_hi + U_lo), fp64 sum rounded once
-    float biasV[kMaxD];
+    // encoder accumulator start: 2^(b-1) - 1/2 - mu_K (W_hi + W_lo), fp64 sum rounded once
+    // (0 for uncoded channels), so that the projection yields t + 2^(b-1) - 1/2
+    float estartK[kMaxD];
+    float estartV[kMaxD];
     float stepK[kMaxD], stepV[kMaxD];
     float invK[kMaxD], invV[kMaxD];
     int32_t bitsK[kMaxD], bitsV[kMaxD];

@@ -598,22 +598,24 @@ int finalize(aatc_codebook* cb) {
         for (int which = 0; which < 2; ++which) {
             const std::vector<double>& U = which ? H.UV : H.UK;
             const std::vector<double>& mu = which ? H.muV : H.muK;
+            const std::vector<int32_t>& bits = which ? H.bV : H.bK;
+            const std::vector<float>& step = which ? H.stepV : H.stepK;
             float* U32 = which ? D.UV : D.UK;
-            uint16_t* hi = which ? D.UVt_hi : D.UKt_hi;  // [j * d + i]
-            uint16_t* lo = which ? D.UVt_lo : D.UKt_lo;
-            float* bias = which ? D.biasV : D.biasK;
-            for (int i = 0; i < d; ++i)
-                for (int j = 0; j < d; ++j) {
-                    const float u = (float)U[(size_t)i * d + j];
-                    U32[i * d + j] = u;
-                    hi[j * d + i] = f32_to_bf16(u);
-                    lo[j * d + i] = f32_to_bf16(u - bf16_to_f32(hi[j * d + i]));
-                }
+            uint16_t* hi = which ? D.EVt_hi : D.EKt_hi;  // [j * d + i]
+            uint16_t* lo = which ? D.EVt_lo : D.EKt_lo;
+            float* start = which ? D.estartV : D.estartK;
             for (int j = 0; j < d; ++j) {
+                // the fp32 reciprocal step of the quantizer (0: uncoded channel)
+                const double inv = bits[j] ? (double)(float)(1.0 / (double)step[j]) : 0.0;
                 double s = 0.0;
-                for (int i = 0; i < d; ++i)
+                for (int i = 0; i < d; ++i) {
+                    U32[i * d + j] = (float)U[(size_t)i * d + j];
+                    const float w = (float)(U[(size_t)i * d + j] * inv);
+                    hi[j * d + i] = f32_to_bf16(w);
+                    lo[j * d + i] = f32_to_bf16(w - bf16_to_f32(hi[j * d + i]));
                     s += mu[i] * ((double)bf16_to_f32(hi[j * d + i]) + (double)bf16_to_f32(lo[j * d + i]));
-                bias[j] = (float)s;
+                }
+                start[j] = bits[j] ? (float)((double)(1 << (bits[j] - 1)) - 0.5 - s) : 0.0f;
             }
         }
         for (int i = 0; i < d; ++i)

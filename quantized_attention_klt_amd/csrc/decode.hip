@@ -55,7 +55,7 @@ using aatc::kTile;
 using aatc::kVqSize;
 using aatc::bf16f;
 using aatc::n_tiles_of;
-using aatc::quantize;
+using aatc::code_byte;
 using aatc::set_error;
 
 namespace {
@@ -293,8 +293,8 @@ __device__ __forceinline__ void append_block(const DevHead& H, const uint16_t* x
     constexpr int NB = D / 16, KS = D / 32;
     const bool isV = cb >= NB;
     const int j = 16 * (isV ? cb - NB : cb) + c;
-    const uint16_t* uh = isV ? H.UVt_hi : H.UKt_hi;
-    const uint16_t* ul = isV ? H.UVt_lo : H.UKt_lo;
+    const uint16_t* uh = isV ? H.EVt_hi : H.EKt_hi;
+    const uint16_t* ul = isV ? H.EVt_lo : H.EKt_lo;
     const uint16_t* x = isV ? xv : xk;
     bf16x8 bh[KS], bl[KS], av[KS];
 #pragma unroll
@@ -304,21 +304,20 @@ __device__ __forceinline__ void append_block(const DevHead& H, const uint16_t* x
         const bf16x8 xa = *(const bf16x8*)(x + 32 * ks + 8 * g);
         av[ks] = c == 0 ? xa : bf16x8{};
     }
-    const float nb = -(isV ? H.biasV[j] : H.biasK[j]);
-    const float inv = isV ? H.invV[j] : H.invK[j];
+    const float st = isV ? H.estartV[j] : H.estartK[j];
     const int bits = isV ? H.bitsV[j] : H.bitsK[j];
     const uint32_t* pc = isV ? H.cpieceV : H.cpieceK;
     const int16_t* cf = isV ? H.cfirstV : H.cfirstK;
     const int p0 = cf[j], p1 = cf[j + 1];
     const int base = isV ? H.BK / 8 : 0;  // record byte of the value record's byte 0
-    f4 acc = f4{nb, nb, nb, nb};
+    f4 acc = f4{st, st, st, st};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks], bh[ks], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks], bl[ks], acc, 0, 0, 0);
     }
     if (g == 0 && bits > 0) {
-        const uint32_t code = quantize(acc[0], inv, bits);
+        const uint32_t code = code_byte(acc[0], (float)((1 << bits) - 1), 0, 0u);
         for (int p = p0; p < p1; ++p) {  // piece = byte | pos << 8 | width << 12 | shift << 16
             const uint32_t pcv = pc[p];
             const int rb = base + (int)(pcv & 0xff), pos = (pcv >> 8) & 7, wd = (pcv >> 12) & 15, sh = (pcv >> 16) & 15;

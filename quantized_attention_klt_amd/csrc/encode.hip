@@ -19,13 +19,15 @@ using aatc::check_cache;
 using aatc::DevHead;
 using aatc::kTile;
 using aatc::n_tiles_of;
+using aatc::code_byte;
 using aatc::quantize;
 using aatc::set_error;
 
 namespace {
 
 constexpr int kMaxSeqPerLaunch = 64;
-constexpr int kEncodeSlots = 768;  // resident encode workgroups the launch aims for
+constexpr int kCUs = 256;               // compute units of an MI355X
+constexpr size_t kLdsPerCU = 160 * 1024;  // LDS bytes per compute unit (gfx950)
 
 struct SeqArgs {
     int32_t n;
@@ -180,9 +182,11 @@ __device__ __forceinline__ uint8_t* tile_ptr(uint8_t* cache, int layer, int n_se
 
 // ------------------------------------------------------------------------------------
 // encode from bf16 K, V (MFMA): a workgroup owns one (sequence, kv-head, keys | values)
-// and the tiles bx, bx + gridDim.x, ... of the call.  c = x (U_hi + U_lo) - bias on
-// v_mfma_f32_16x16x32_bf16: rows = tokens, columns = channels (in the encoder's channel
-// order), accumulators starting at -bias; wave w keeps the B operands (U^T hi / lo
+// and the tiles bx, bx + gridDim.x, ... of the call.  u = x (W_hi + W_lo) + start (W = U
+// scaled by 1/step per channel, start = 2^(b-1) - 1/2 - mu W, so u = c/step + 2^(b-1) - 1/2)
+// on v_mfma_f32_16x16x32_bf16: rows = tokens, columns = channels (in the encoder's channel
+// order), accumulators starting at start; the code is u clamped and rounded (code_byte).
+// Wave w keeps the B operands (W^T hi / lo
 // fragments) of its D / 4 columns in registers for all its tiles.  The 64-token x tiles
 // arrive by direct global->LDS copies into two buffers (the next tile streams while this
 // one is computed), their 16-byte chunks XOR-swizzled by token so that the 16 rows an
@@ -190,8 +194,14 @@ __device__ __forceinline__ uint8_t* tile_ptr(uint8_t* cache, int layer, int n_se
 // of its channel, packs the four codes of one tb into a word (they share a staged word) and
 // ORs each field into the staged block with one LDS operation per field and four tokens.
 // ------------------------------------------------------------------------------------
+// x tiles per workgroup in LDS (all but one in flight).  Two: a third buffer lowers the
+// residency to two workgroups per CU, and the kernel is bound by its MFMA and VALU work, not
+// by the bytes in flight (the 128k Llama layer: 164 us with two buffers, 197 us with three,
+// before the quantizer was folded into the projection).
+constexpr int kEncodeRing = 2;
+
 template <int D>
-constexpr size_t encode_lds_bytes() { return 2 * 64 * D * 2 + 4 * kStageWords + sizeof(PieceTab); }
+constexpr size_t encode_lds_bytes() { return kEncodeRing * 64 * D * 2 + 4 * kStageWords + sizeof(PieceTab); }
 
 template <int D, bool isV>
 __device__ __forceinline__ void encode_mfma_body(const DevHead* __restrict__ blob, uint8_t* __restrict__ cache,
@@ -204,13 +214,12 @@ __device__ __forceinline__ void encode_mfma_body(const DevHead* __restrict__ blo
     constexpr int KS = D / 32;         // k-steps
     constexpr int XB = 64 * D * 2;     // bytes of one x tile
     constexpr int NLD = 64 * CH / 256;  // chunk loads per thread
-    // LDS (one dynamic array): two x tiles, the staged block, the field table
+    constexpr int NB = kEncodeRing;
+    // LDS (one dynamic array): NB x tiles, the staged block, the field table
     extern __shared__ __attribute__((aligned(16))) uint8_t esm_generic[];
     LDS_AS uint8_t* const esm = (LDS_AS uint8_t*)esm_generic;
-    LDS_AS uint8_t* const xs0 = esm;
-    LDS_AS uint8_t* const xs1 = esm + XB;
-    LDS_AS uint32_t* const stg = (LDS_AS uint32_t*)(esm + 2 * XB);
-    LDS_AS PieceTab* const pt = (LDS_AS PieceTab*)(esm + 2 * XB + 4 * kStageWords);
+    LDS_AS uint32_t* const stg = (LDS_AS uint32_t*)(esm + NB * XB);
+    LDS_AS PieceTab* const pt = (LDS_AS PieceTab*)(esm + NB * XB + 4 * kStageWords);
     const int h = blockIdx.y >> 1, zi = blockIdx.z;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
     const DevHead& H = blob[layer * n_kv + h];
@@ -222,13 +231,13 @@ __device__ __forceinline__ void encode_mfma_body(const DevHead* __restrict__ blo
     stage_pieces(H, isV, pt, tid, 256);
     for (int i = tid; i < kStageWords; i += 256) stg[i] = 0u;
     // B operands and quantizer constants of this lane's columns 16 (w CBW + cbw) + c: channel
-    // j = encoder order of that column (an uncoded channel gets a 1-bit quantizer and no field)
+    // j = encoder order of that column (an uncoded channel has a zero column and no field)
     bf16x8 bh[CBW][KS], bl[CBW][KS];
-    float nbias[CBW], inv[CBW];
-    int bits[CBW], jj[CBW];
+    float ustart[CBW], cmax[CBW];
+    int jj[CBW];
     {
-        const uint16_t* uh = isV ? H.UVt_hi : H.UKt_hi;
-        const uint16_t* ul = isV ? H.UVt_lo : H.UKt_lo;
+        const uint16_t* uh = isV ? H.EVt_hi : H.EKt_hi;
+        const uint16_t* ul = isV ? H.EVt_lo : H.EKt_lo;
         const uint8_t* perm = isV ? H.encpermV : H.encpermK;
 #pragma unroll
         for (int cbw = 0; cbw < CBW; ++cbw) {
@@ -239,9 +248,8 @@ __device__ __forceinline__ void encode_mfma_body(const DevHead* __restrict__ blo
                 bh[cbw][ks] = *(const bf16x8*)(uh + j * D + 32 * ks + 8 * g);
                 bl[cbw][ks] = *(const bf16x8*)(ul + j * D + 32 * ks + 8 * g);
             }
-            nbias[cbw] = -(isV ? H.biasV[j] : H.biasK[j]);
-            inv[cbw] = isV ? H.invV[j] : H.invK[j];
-            bits[cbw] = max(isV ? H.bitsV[j] : H.bitsK[j], 1);
+            ustart[cbw] = isV ? H.estartV[j] : H.estartK[j];
+            cmax[cbw] = (float)((1 << (isV ? H.bitsV[j] : H.bitsK[j])) - 1);
         }
     }
     const int nbytes = (isV ? H.BV : H.BK) / 8;
@@ -263,7 +271,10 @@ __device__ __forceinline__ void encode_mfma_body(const DevHead* __restrict__ blo
         }
     };
     int64_t tile = blockIdx.x;
-    if (tile < ntiles) copy_x(first_tile + tile, xs0);  // the first tile streams during the set-up
+    // the first NB - 1 tiles stream during the set-up
+#pragma unroll
+    for (int m = 0; m < NB - 1; ++m)
+        if (tile + (int64_t)m * gridDim.x < ntiles) copy_x(first_tile + tile + (int64_t)m * gridDim.x, esm + m * XB);
     lds_barrier();  // field table staged, staging clear
     // this lane's channels: their fields (usually one) are pt->piece[pf[cbw] .. pl[cbw]); the
     // first (code bits from 0) as registers: staged word of its record byte for this lane's
@@ -283,35 +294,62 @@ __device__ __forceinline__ void encode_mfma_body(const DevHead* __restrict__ blo
     // this wave's copy-out stores per full tile: one 16-byte store per item round it takes part in
     const int n_items = 4 * nbytes;
     const int st_full = max(0, (n_items - 64 * w + 255) / 256);
-    int st_prev = 0;  // stores issued by the previous tile's copy-out (-1: not counted)
-    // one tile: its x in xc, the next tile's copied into xn
-    auto step = [&](const LDS_AS uint8_t* xc, LDS_AS uint8_t* xn) {
-        const int64_t tile_n = tile + gridDim.x;
-        // this tile's copies have landed (the previous copy-out's stores, issued after them,
-        // may still be in flight); every wave's, and every wave is past the previous tile
-        if (st_prev < 0)
-            wait_vm(0);
-        else
-            wait_vm(st_prev);
+    // stores issued by the copy-outs of the previous NB - 1 tiles, latest first (-1: not
+    // counted; a partial tile's copy-out is a read-modify-write of run-time length)
+    int st_prev[NB - 1];
+#pragma unroll
+    for (int m = 0; m < NB - 1; ++m) st_prev[m] = 0;
+    // one tile: its x in ring slot `slot`; tile + (NB - 1) strides is copied into the slot
+    // the previous tile used
+    auto step = [&](int slot) {
+        const LDS_AS uint8_t* xc = esm + slot * XB;
+        // this tile's copies have landed: issued after them are the copies of the next
+        // NB - 2 tiles (those that exist) and the copy-outs of the previous NB - 1 tiles;
+        // then every wave's have, and every wave is past the previous tile
+        int after = 0;
+        bool counted = true;
+#pragma unroll
+        for (int m = 0; m < NB - 1; ++m) {
+            counted = counted && st_prev[m] >= 0;
+            after += st_prev[m];
+        }
+#pragma unroll
+        for (int m = 1; m < NB - 1; ++m)
+            if (tile + (int64_t)m * gridDim.x < ntiles) after += NLD;
+        wait_vm(counted ? after : 0);
         lds_barrier();
-        if (tile_n < ntiles) copy_x(first_tile + tile_n, xn);  // next tile, in flight during this one
+        const int64_t tile_f = tile + (int64_t)(NB - 1) * gridDim.x;
+        if (tile_f < ntiles)  // in flight during this tile and the next NB - 2
+            copy_x(first_tile + tile_f, esm + (slot == 0 ? NB - 1 : slot - 1) * XB);
         f32x4 acc[CBW][4];
 #pragma unroll
         for (int cbw = 0; cbw < CBW; ++cbw)
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) acc[cbw][tb] = f32x4{nbias[cbw], nbias[cbw], nbias[cbw], nbias[cbw]};
+            for (int tb = 0; tb < 4; ++tb) acc[cbw][tb] = f32x4{ustart[cbw], ustart[cbw], ustart[cbw], ustart[cbw]};
+        // two token blocks at a time, per k-step: the hi products of their 2 CBW accumulators,
+        // then the lo products, so that consecutive MFMAs are independent (each accumulator
+        // still adds hi then lo per k-step; four blocks at once spill registers)
+        constexpr int TBG = 2;
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            const int t = 16 * tb + c;  // A row: token
+        for (int tg = 0; tg < 4; tg += TBG)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 av = *(const LDS_AS bf16x8*)(xc + t * 2 * D + 16 * ((4 * ks + g) ^ (t & (CH - 1))));
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 av[TBG];
 #pragma unroll
-                for (int cbw = 0; cbw < CBW; ++cbw) {
-                    acc[cbw][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh[cbw][ks], acc[cbw][tb], 0, 0, 0);
-                    acc[cbw][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl[cbw][ks], acc[cbw][tb], 0, 0, 0);
-                }
+            for (int u = 0; u < TBG; ++u) {
+                const int t = 16 * (tg + u) + c;  // A row: token
+                av[u] = *(const LDS_AS bf16x8*)(xc + t * 2 * D + 16 * ((4 * ks + g) ^ (t & (CH - 1))));
             }
+#pragma unroll
+            for (int u = 0; u < TBG; ++u)
+#pragma unroll
+                for (int cbw = 0; cbw < CBW; ++cbw)
+                    acc[cbw][tg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bh[cbw][ks], acc[cbw][tg + u], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < TBG; ++u)
+#pragma unroll
+                for (int cbw = 0; cbw < CBW; ++cbw)
+                    acc[cbw][tg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bl[cbw][ks], acc[cbw][tg + u], 0, 0, 0);
         }
         // codes of tokens 16 tb + 4 g + e: the four of one tb share staged word q * kStageRow +
         // 4 tb + g (byte e), so they are packed into one word and OR-ed with one operation per
@@ -321,10 +359,10 @@ __device__ __forceinline__ void encode_mfma_body(const DevHead* __restrict__ blo
             uint32_t c4[4];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                uint32_t v = quantize(acc[cbw][tb][0], inv[cbw], bits[cbw]);
-#pragma unroll
-                for (int e = 1; e < 4; ++e) v |= quantize(acc[cbw][tb][e], inv[cbw], bits[cbw]) << (8 * e);
-                c4[tb] = v;
+                uint32_t v = code_byte(acc[cbw][tb][0], cmax[cbw], 0, 0u);
+                v = code_byte(acc[cbw][tb][1], cmax[cbw], 1, v);
+                v = code_byte(acc[cbw][tb][2], cmax[cbw], 2, v);
+                c4[tb] = code_byte(acc[cbw][tb][3], cmax[cbw], 3, v);
             }
             if (mask0[cbw]) {
                 lds_or_async<0>(base0[cbw], (c4[0] & mask0[cbw]) << pos0[cbw]);
@@ -349,14 +387,12 @@ __device__ __forceinline__ void encode_mfma_body(const DevHead* __restrict__ blo
         const int s1 = (int)min(start + n_tokens - tok0, (int64_t)kTile);
         uint8_t* tp = tile_ptr(cache, layer, n_seqs_cache, seq, n_kv, h, n_tiles_cap, first_tile + tile, tile_bytes);
         copy_out<isV>(stg, nbytes, (uint32_t*)(tp + boff), s0, s1, tid, 256);
-        st_prev = (s0 == 0 && s1 == kTile) ? st_full : -1;
-        tile = tile_n;
+#pragma unroll
+        for (int m = NB - 2; m > 0; --m) st_prev[m] = st_prev[m - 1];
+        st_prev[0] = (s0 == 0 && s1 == kTile) ? st_full : -1;
+        tile += gridDim.x;
     };
-    while (tile < ntiles) {
-        step(xs0, xs1);
-        if (tile >= ntiles) break;
-        step(xs1, xs0);
-    }
+    for (int slot = 0; tile < ntiles; slot = slot + 1 == NB ? 0 : slot + 1) step(slot);
     wait_vm(0);
 }
 
@@ -580,10 +616,15 @@ static int encode_common(const aatc_codebook* cb, const void* d_blob, const aatc
         } else {
             // workgroups per (sequence, kv-head, keys | values): fill the resident slots
             const int64_t units = (int64_t)used * cb->n_kv * 2;
-            const unsigned wx = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ntiles, kEncodeSlots / units));
+            const size_t lds = d == 64 ? encode_lds_bytes<64>() : encode_lds_bytes<128>();
+            const int64_t slots = (int64_t)kCUs * std::min<size_t>(3, kLdsPerCU / lds);  // 3: waves_per_eu
+            const unsigned wx = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ntiles, slots / units));
             const dim3 grid(wx, (unsigned)(2 * cb->n_kv), (unsigned)used);
             const int vq = cb->heads[0].vq_groups > 0;
             const dim3 kgrid((unsigned)ntiles, (unsigned)cb->n_kv, (unsigned)used);
+            if (lds > 64 * 1024)
+                HIP_TRY(hipFuncSetAttribute(d == 64 ? (const void*)encode_mfma_kernel<64> : (const void*)encode_mfma_kernel<128>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
             if (d == 64) {
                 hipLaunchKernelGGL(encode_mfma_kernel<64>, grid, dim3(256), encode_lds_bytes<64>(), (hipStream_t)stream, blob,
                                    (uint8_t*)cache->data, layer, cb->n_kv, ncap, tile_bytes, sa, n_tokens, ntiles, Kz, Vz,

@@ -36,6 +36,16 @@ __device__ __forceinline__ uint32_t quantize(float c, float inv, int b) {
     return (uint32_t)__builtin_amdgcn_fmed3f(v, 0.0f, (float)((1 << b) - 1));
 }
 
+// The quantizer of the bf16 encode paths, on the projection u = t + 2^(b-1) - 1/2 (the
+// encoder bases carry the factor 1/step and the start value the offset): u clamped to
+// [0, cmax = 2^b - 1], rounded to the nearest integer (ties to even) and written into byte
+// `byte` of acc (v_cvt_pk_u8_f32).  Equal to clamp(floor(t) + 2^(b-1), 0, 2^b - 1) except
+// where t + 2^(b-1) is an odd integer: on a cell edge, where the fp32 projection's own
+// rounding decides the code anyway.
+__device__ __forceinline__ uint32_t code_byte(float u, float cmax, uint32_t byte, uint32_t acc) {
+    return __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(u, 0.0f, cmax), byte, acc);
+}
+
 // Nearest codeword of the weighted key coefficients (u0, u1, u2, u3) among cent[0..255]
 // (one group of vector-quantized keys): t_k = u_k - z_k, distance (t0 t0 + t1 t1) +
 // (t2 t2 + t3 t3), each operation rounded to fp32 (contraction off), lowest index on ties.

@@ -121,19 +121,21 @@ def normwise_rel_err(o, ref):
 
 
 # ------------------------------------------------------------ end-to-end code flips
-# The GPU encoder computes a coefficient c = (x - mu) U in fp32 from bf16 x, with U held
-# as two bf16 parts (hi + lo, which leaves |U - hi - lo| <= 2^-18 |U|) or in fp32, and the
-# mean folded into a bias or subtracted first.  Its quantizer input t = c / step then
-# differs from the exact one by at most
-#     E = (2^-17 + (d + 4) 2^-24) S / step + 4 2^-24 |t|,   S = sum_i (|x_i| + |mu_i|) |U_ij|
-# (split error of U, fp32 accumulation over d terms, bias and product roundings, with
-# margin), and the oracle's fp32 t (c rounded once, then the product) by at most
-# 2 2^-24 |t|.  Codes are floor(t) + 2^(b-1), so the two codes can differ only where
-# the exact t lies within E of an integer: every flipped code is checked for that.
+# The GPU encoder computes u = t + 2^(b-1) - 1/2 in fp32 from bf16 x: the bases scaled by the
+# fp32 reciprocal step, W = fp32(U / step), held as two bf16 parts (hi + lo, which leaves
+# |W - hi - lo| <= 2^-18 |W|) or in fp32, and the accumulators starting at
+# 2^(b-1) - 1/2 - mu W.  Its t then differs from the exact t = c * inv32 by at most
+#     E = (2^-17 + (d + 4) 2^-24) S inv32 + (d + 4) 2^-24 (2^(b-1) + 1) + 4 2^-24 |t|,
+#     S = sum_i (|x_i| + |mu_i|) |U_ij|
+# (split and scaling roundings of W, fp32 accumulation over d terms and the start value,
+# with margin), and the oracle's fp32 t (c rounded once, then the product) by at most
+# 2 2^-24 |t|.  Codes are floor(t) + 2^(b-1) (the GPU rounds u to nearest, which is the same
+# away from integers t), so the two codes can differ only where the exact t lies within E
+# of an integer: every flipped code is checked for that.
 _U24 = 2.0 ** -24
 
 
-def edge_ratio(x64, mu, U, inv32, idx):
+def edge_ratio(x64, mu, U, inv32, bits, idx):
     """max over (token, channel) pairs idx [n, 2] of (distance of the exact t from the
     nearest integer) / E; a flip outside the rounding window gives a ratio above 1."""
     if len(idx) == 0:
@@ -145,7 +147,8 @@ def edge_ratio(x64, mu, U, inv32, idx):
     t = (X * Uc).sum(axis=1) * inv
     S = ((np.abs(np.asarray(x64, np.float64)[rows]) + np.abs(mu)[None, :]) * np.abs(Uc)).sum(axis=1)
     d = Uc.shape[1]
-    bound = (2.0 ** -17 + (d + 4) * _U24) * S * inv + 4 * _U24 * np.abs(t)
+    half = 2.0 ** (np.asarray(bits)[ch] - 1)
+    bound = (2.0 ** -17 + (d + 4) * _U24) * S * inv + (d + 4) * _U24 * (half + 1) + 4 * _U24 * np.abs(t)
     return float((np.abs(t - np.round(t)) / bound).max())
 
 
@@ -168,7 +171,7 @@ def code_flips(got_bytes, cb, n_tokens, K64, V64, first=0):
         flips += int(bad.sum())
         total += int(m.sum())
         worst = max(worst, int(dlt[m].max(initial=0)))
-        edge = max(edge, edge_ratio(x64, mu, U, cb.inv_step(which), np.argwhere(bad)))
+        edge = max(edge, edge_ratio(x64, mu, U, cb.inv_step(which), bits, np.argwhere(bad)))
     return flips, total, worst, edge
 
 
