@@ -1132,62 +1132,79 @@ constexpr Variant kVariants[] = {{1, 2, 4},  {1, 2, 8},  {1, 3, 8},  {1, 3, 10},
 
 // ------------------------------------------------------------------------------------
 // Split decode over vector-quantized keys ("Spend Bits Where Queries Look", abstract).
-// Grid (workgroups per head x chunks of 4 query heads, kv-heads, sequences), 256 threads.
-// Prologue: q'' = (T_K^{-1} q) / s * log2(e) / sqrt(d) for the chunk's heads, then one
-// score table per (head, group): lut[m][g][i] = sum_k q''[chan(g, k)] z_gik over the
-// group's 256 codewords, so that a token's score is the sum over groups of
-// lut[m][g][index_g] (the dropped term q . mu_K is the same for every token).  Tiles of the
-// workgroup's contiguous share stream through a ring of LDS buffers (as many as the LDS
-// beside the tables holds, at most 8) by direct global->LDS copies, all but one of them in
-// flight while a tile is computed: with one workgroup per CU, the bytes in flight set the
-// rate (one tile ahead streamed at about 0.5 TB/s).  Per tile: wave m < 4 scores head m with one token
-// per lane (the record's index bytes, one table read per group), keeps that head's running
-// max and sum (base 2) of p rounded to fp16 and writes p to LDS; then every wave runs value
-// blocks of 16 fields on v_mfma_f32_16x16x16_f16 (A = p of the 4 heads over 16 tokens, B =
-// the fields' masked stored bytes as signed values, exact in fp16), the accumulators
-// rescaled by the heads' max updates.  The partials have the split-decode layout, so merge_kernel finishes the call.
+// Grid (workgroups per head x chunks of 4 query heads, kv-heads, sequences), one workgroup
+// of kVqWaves waves per CU.  Prologue: q'' = (T_K^{-1} q) / s * log2(e) / sqrt(d) for the
+// chunk's heads, then one score table per (head, group) in LDS: lut[m][g][i] =
+// sum_k q''[chan(g, k)] z_gik over the group's 256 codewords, so that a token's score is
+// the sum over groups of lut[m][g][index_g] (the dropped term q . mu_K is the same for every
+// token).  Every wave owns whole tiles of the workgroup's share (t_begin + w, + kVqWaves,
+// ...), read straight into registers (buffer loads over the (sequence, kv-head)'s range; the
+// next tile's loads are in flight while one is computed): lane = token, its key record
+// words, and per value block the 16 bytes (tokens 16 kk .. 16 kk + 15 of one field's byte
+// plane) that its MFMA B operand needs.  Per tile a wave scores the chunk's heads (one table
+// read per (head, group)), keeps per head the running max and sum (base 2) of p rounded to
+// fp16, writes p to its own LDS rows, and accumulates the value columns on
+// v_mfma_f32_16x16x16_f16: A = p of the heads over 16 tokens, B = the field's masked byte,
+// as the fp16 number 1024 + byte (its bits 0x64 | byte, one v_perm per two values; a top
+// field's byte with bit 7 restored).  The waves' results are combined in LDS into one
+// partial per head in the split-decode layout [max, sum, 128 sum, 0, columns], the column
+// of a field being sum p * (its stored bits as a signed byte): the offsets 1024 (and 128
+// for top fields) times the sum are taken off.  merge_kernel finishes the call.
 // ------------------------------------------------------------------------------------
+constexpr int kVqWaves = 8;  // waves per workgroup (one workgroup per CU)
+// value blocks per launch (all read ahead into registers): d / 16, the blocks of a record
+// with one field per channel; a record with more takes one launch per d / 16 blocks
+constexpr int vq_blocks(int d) { return d / 16; }
+
 struct VqLds {
-    int lut, pb, qv, alpha, ring, tba, nbuf, total;
+    int lut, pbuf, epi, total;
 };
 
-__host__ __device__ inline VqLds vq_lds(int n_g, int tile_bytes, int d) {
+// LDS: the score tables [4][n_g][256] float, then per wave p [4][64] fp16 (the prologue's
+// q'' [4][d] float in the same place); the epilogue reuses the start: per wave and head the
+// max and sum, then the columns [kVqWaves][4][16 nvb] float
+__host__ __device__ inline VqLds vq_lds(int n_g, int d, int nvb) {
     VqLds L;
-    L.tba = (tile_bytes + 15) & ~15;
     L.lut = 0;
-    L.pb = 4 * n_g * kVqSize * 4;  // [4][64] float
-    L.qv = L.pb + 4 * 64 * 4;      // [4][d] float
-    L.alpha = L.qv + 4 * d * 4;
-    L.ring = L.alpha + 16;
-    const int room = (160 * 1024 - L.ring) / L.tba;
-    L.nbuf = room < 2 ? 2 : (room > 8 ? 8 : room);
-    L.total = L.ring + L.nbuf * L.tba;
+    L.pbuf = 4 * n_g * kVqSize * 4;
+    const int pb = kVqWaves * 4 * 64 * 2, qv = 4 * d * 4;
+    L.epi = 2 * kVqWaves * 4 * 4;
+    const int epi_end = L.epi + kVqWaves * 4 * 16 * nvb * 4;
+    L.total = L.pbuf + (pb > qv ? pb : qv);
+    if (epi_end > L.total) L.total = epi_end;
     return L;
 }
 
-// NG: the number of groups when fixed at compile time (every index word and table read of a
-// tile issued back to back), 0 for any multiple of 4 at run time.
+// NG: the number of groups when fixed at compile time, 0 for any multiple of 4 at run time.
+// vb0: the first value block of this launch (its columns and the maxima and sums go to the
+// partials; launches for later blocks of the same call write the same maxima and sums).
 template <int D, int NG>
-__global__ __launch_bounds__(256) void vq_decode_kernel(const DevHead* __restrict__ blob, const uint8_t* __restrict__ cache,
-                                                        DecodeArgs a, const int32_t* __restrict__ seq_ids,
-                                                        const int64_t* __restrict__ seq_lens, const uint16_t* __restrict__ q,
-                                                        float* __restrict__ part) {
+__global__ __launch_bounds__(64 * kVqWaves) void vq_decode_kernel(const DevHead* __restrict__ blob,
+                                                                  const uint8_t* __restrict__ cache, DecodeArgs a,
+                                                                  const int32_t* __restrict__ seq_ids,
+                                                                  const int64_t* __restrict__ seq_lens,
+                                                                  const uint16_t* __restrict__ q,
+                                                                  float* __restrict__ part, int vb0) {
+    constexpr int NGW = (NG ? NG : aatc::kMaxVqGroups) / 4;  // key record words per token (at most)
+    constexpr int NVB = vq_blocks(D);
+    constexpr int NT = 64 * kVqWaves;
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
     extern __shared__ __attribute__((aligned(16))) uint8_t vsm_generic[];
     LDS_AS uint8_t* const sm = (LDS_AS uint8_t*)vsm_generic;
     const int n_chunks = (a.G + 3) / 4;
     const int wgi = blockIdx.x / n_chunks, chunk = blockIdx.x - wgi * n_chunks;
     const int h = blockIdx.y, z = blockIdx.z;
-    // the wave index as a scalar: the copy counts and waits below are uniform branches
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int col = lane & 15, kk = lane >> 4;
     const DevHead& H = blob[a.layer * a.n_kv + h];
-    const int n_g = NG ? NG : H.vq_groups, nvb = H.nvb, BK = H.BK;
+    const int n_g = NG ? NG : H.vq_groups, nvb = max(0, min(NVB, H.nvb - vb0)), BK = H.BK;
     const int hh0 = 4 * chunk, GC = min(4, a.G - hh0);
-    const int tbytes = a.tile_bytes, n16 = tbytes / 16;
-    const VqLds L = vq_lds(n_g, tbytes, D);
+    const int tbytes = a.tile_bytes;
+    const VqLds L = vq_lds(n_g, D, nvb);
     LDS_AS float* const lut = (LDS_AS float*)(sm + L.lut);
-    LDS_AS float* const pb = (LDS_AS float*)(sm + L.pb);
-    LDS_AS float* const qv = (LDS_AS float*)(sm + L.qv);
-    LDS_AS float* const alpha = (LDS_AS float*)(sm + L.alpha);
+    LDS_AS float* const qv = (LDS_AS float*)(sm + L.pbuf);
+    LDS_AS _Float16* const pw = (LDS_AS _Float16*)(sm + L.pbuf) + w * 256;  // this wave's p [4][64]
     // sequence geometry (device arguments clamped: no read outside the cache)
     const int seq = seq_ids[z];
     int64_t len = max<int64_t>(0, min<int64_t>(min<int64_t>(seq_lens[z], a.max_len), a.n_tiles_cap * kTile));
@@ -1196,156 +1213,233 @@ __global__ __launch_bounds__(256) void vq_decode_kernel(const DevHead* __restric
     const int64_t t_begin = n_tiles * wgi / a.wg_per_head, t_end = n_tiles * (wgi + 1) / a.wg_per_head;
     const uint8_t* const base =
         cache + (((int64_t)a.layer * a.n_seqs_cache + max(seq, 0)) * a.n_kv + h) * a.n_tiles_cap * (int64_t)tbytes;
-    // buffer resource over this (sequence, kv-head)'s tiles (the host keeps the range below 2^31
-    // bytes): a read past the range returns zeros instead of faulting
+    // buffer resource over this (sequence, kv-head)'s tiles (the host keeps the range below
+    // 2^31 bytes); the offsets are per lane, so a read past the range returns zeros
     const __amdgpu_buffer_rsrc_t trs =
         __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(a.n_tiles_cap * tbytes), 0x00020000);
-    // tile copies: instruction k of wave w moves chunks 256 k + 64 w + lane (16 bytes each)
-    int nlw = 0;
-    for (int k = 0; 256 * k + 64 * w < n16; ++k) ++nlw;
-    auto issue = [&](int64_t t, int buf) {
-        LDS_AS uint8_t* dst = sm + L.ring + buf * L.tba;
-        for (int k = 0; k < nlw; ++k) {
-            const int c = 256 * k + 64 * w + lane;
-            if (c < n16)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(trs, (LDS_AS void*)(dst + 16 * (256 * k + 64 * w)), 16, 16 * c,
-                                                         (int)(t * tbytes), 0, 2);
-        }
+    // this lane's value operand bytes of block vb0 + r: tile offset, byte mask, top-field flag
+    uint32_t voff[NVB], vmsk[NVB], vflp[NVB];
+#pragma unroll
+    for (int r = 0; r < NVB; ++r) {
+        const uint32_t vc = r < nvb ? H.vb_col[vb0 + r][col] : 0u;
+        const uint32_t m8 = (vc >> 16) & 0xFFu;
+        voff[r] = 8 * BK + (vc & 0xFFFFu) + 16 * kk;
+        vmsk[r] = m8 * 0x01010101u;
+        vflp[r] = (m8 & 0x80u) ? 0x80808080u : 0u;
+    }
+    struct Tile {
+        uint32_t kw[NGW];
+        u32x4 vv[NVB];
     };
-    const int NB = L.nbuf;
-    for (int k = 0; k < NB - 1 && t_begin + k < t_end; ++k) issue(t_begin + k, k);
-    // ---- prologue: q'' of the chunk's heads, the score tables, zero probability rows
-    typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
-    for (int i = tid; i < 4 * D; i += 256) {
-        const int m = i / D, j = i - m * D;
-        float acc = 0.0f;
-        if (m < GC) {
-            const uint16_t* qr = q + (((int64_t)z * a.n_kv + h) * a.G + hh0 + m) * D;
-#pragma unroll 4
-            for (int k = 0; k < D; k += 8) {
-                const u16x8 hi = *(const u16x8*)&H.QKt_hi[j * D + k], lo = *(const u16x8*)&H.QKt_lo[j * D + k];
-                const u16x8 qq = *(const u16x8*)&qr[k];
+    // a tile's registers; tiles past the workgroup's share are read too (in range or zeros)
+    // so that every tile issues the same loads
+    auto load = [&](int64_t t, Tile& T) {
+        const uint32_t tb = (uint32_t)(t * tbytes);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc = fmaf(bf16f(hi[e]) + bf16f(lo[e]), bf16f(qq[e]), acc);
-            }
-            acc *= H.vq_rscale[j] * (kLog2e / sqrtf((float)D));
+        for (int r = 0; r < NGW; ++r)
+            if (NG || 4 * r < n_g)
+                T.kw[r] = __builtin_amdgcn_raw_buffer_load_b32(trs, tb + 4 * (64 * r + lane), 0, 2);
+#pragma unroll
+        for (int r = 0; r < NVB; ++r)  // blocks past the record's read too (their offsets stay in the tile)
+            T.vv[r] = __builtin_amdgcn_raw_buffer_load_b128(trs, tb + voff[r], 0, 2);
+    };
+    // ---- prologue: q' = T_K^{-1} q of the chunk's heads on bf16 MFMAs (wave w < D / 16: rows
+    // 16 w .. 16 w + 15 of T_K^{-1} = hi + lo as A, the heads' q as the B columns), then
+    // q'' = q' / s * log2(e) / sqrt(d) into LDS
+    if (w < D / 16) {
+        typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+        const int j0 = 16 * w;
+        const uint16_t* qr = q + (((int64_t)z * a.n_kv + h) * a.G + hh0 + min(col, GC - 1)) * D;
+        f4 qa = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const bf16x8 ah = *(const bf16x8*)&H.QKt_hi[(j0 + col) * D + 32 * ks + 8 * kk];
+            const bf16x8 al = *(const bf16x8*)&H.QKt_lo[(j0 + col) * D + 32 * ks + 8 * kk];
+            const bf16x8 bq = col < GC ? *(const bf16x8*)&qr[32 * ks + 8 * kk] : bf16x8{};
+            qa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bq, qa, 0, 0, 0);
+            qa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bq, qa, 0, 0, 0);
         }
-        qv[i] = acc;
-    }
-    pb[tid] = 0.0f;
-    if (tid < 4) alpha[tid] = 1.0f;
-    lds_barrier();
-    // thread tid: codeword tid of every group, four groups' loads in flight at a time
-    for (int g0 = 0; g0 < n_g; g0 += 4) {
-        float4 zc[4];
-        uint32_t chw[4];
+        if (col < 4) {  // lane (kk, head col): rows j0 + 4 kk + e
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            zc[u] = *(const float4*)H.vq_cent[g0 + u][tid];
-            chw[u] = *(const uint32_t*)H.vq_chan[g0 + u];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int c0 = chw[u] & 255, c1 = (chw[u] >> 8) & 255, c2 = (chw[u] >> 16) & 255, c3 = chw[u] >> 24;
-            for (int m = 0; m < GC; ++m) {
-                const LDS_AS float* qm = qv + m * D;
-                lut[(m * n_g + g0 + u) * kVqSize + tid] =
-                    fmaf(qm[c3], zc[u].w, fmaf(qm[c2], zc[u].z, fmaf(qm[c1], zc[u].y, qm[c0] * zc[u].x)));
+            for (int e = 0; e < 4; ++e) {
+                const int j = j0 + 4 * kk + e;
+                qv[col * D + j] = col < GC ? qa[e] * (H.vq_rscale[j] * (kLog2e / sqrtf((float)D))) : 0.0f;
             }
         }
     }
-    // value columns of this wave's blocks cb = w, w + 4, ... (at most 6)
-    constexpr int kMaxBW = (aatc::kMaxVB + 3) / 4;
-    uint32_t vcol[kMaxBW];
-#pragma unroll
-    for (int r = 0; r < kMaxBW; ++r) vcol[r] = w + 4 * r < nvb ? H.vb_col[w + 4 * r][lane & 15] : 0u;
-    f4 acc[kMaxBW];
-#pragma unroll
-    for (int r = 0; r < kMaxBW; ++r) acc[r] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY, l_run = 0.0f;  // wave m < GC: head m's running max and sum
     lds_barrier();
-    // ---- the tiles
-    for (int64_t t = t_begin; t < t_end; ++t) {
-        const int cur = (int)((t - t_begin) % NB);
-        // refill the buffer of the previous tile (every wave is past it), then wait for this
-        // tile's copies: the ones issued after them may stay in flight
-        if (t + NB - 1 < t_end) issue(t + NB - 1, (cur + NB - 1) % NB);
-        wait_vm(nlw * (int)min<int64_t>(NB - 1, t_end - 1 - t));
-        lds_barrier();
-        const LDS_AS uint8_t* tb = sm + L.ring + cur * L.tba;
-        if (w < GC) {
-            const int64_t tok = t * kTile + lane;
-            float s = 0.0f;
-            const LDS_AS float* lm = lut + w * n_g * kVqSize;
-            if constexpr (NG > 0) {
-                uint32_t wd[NG / 4];
+    // tables, the four heads' entries of one (group, codeword) side by side (one 16-byte read
+    // per group and token in the tile loop; entries of absent heads are zero).  Codeword
+    // i = tid mod 256 of groups tid / 256, + NT / 256, ...: every load first
+    LDS_AS f4* const lut4 = (LDS_AS f4*)lut;
+    constexpr int GPT = (NG ? NG : aatc::kMaxVqGroups) / (NT / 256);  // groups per thread (at most)
+    constexpr int GB = GPT > 8 ? GPT / 2 : GPT;                             // ... per batch of loads
+    {
+        const int i = tid & 255, g0 = tid >> 8;
+        Tile T0;
 #pragma unroll
-                for (int r = 0; r < NG / 4; ++r) wd[r] = ((const LDS_AS uint32_t*)tb)[64 * r + lane] ^ 0x80808080u;
-                float e[NG];
+        for (int u0 = 0; u0 < GPT; u0 += GB) {
+            float4 zc[GB];
+            uint32_t chw[GB];
 #pragma unroll
-                for (int g = 0; g < NG; ++g) e[g] = lm[g * kVqSize + ((wd[g >> 2] >> (8 * (g & 3))) & 255u)];
-#pragma unroll
-                for (int g = 0; g < NG; ++g) s += e[g];
-            } else {
-                for (int r = 0; r < n_g / 4; ++r) {
-                    const uint32_t wd = ((const LDS_AS uint32_t*)tb)[64 * r + lane] ^ 0x80808080u;
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) s += lm[(4 * r + b) * kVqSize + ((wd >> (8 * b)) & 255u)];
+            for (int u = 0; u < GB; ++u) {
+                const int g = g0 + (u0 + u) * (NT / 256);
+                if (NG || g < n_g) {
+                    zc[u] = *(const float4*)H.vq_cent[g][i];
+                    chw[u] = *(const uint32_t*)H.vq_chan[g];
                 }
             }
-            const bool valid = tok < len;
-            const float mt = wave_max(valid ? s : -INFINITY);
-            const float m_new = fmaxf(m_run, mt);
-            const float al = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-            const float p = valid ? (float)(_Float16)__builtin_amdgcn_exp2f(s - m_new) : 0.0f;
-            l_run = l_run * al + wave_sum(p);
-            m_run = m_new;
-            pb[w * 64 + lane] = p;
-            if (lane == 0) alpha[w] = al;
-        }
-        lds_barrier();
-        // MFMA i, lane group kk, k-slot e: token 16 kk + 4 i + e
-        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-        const int mrow = lane & 15, kk = lane >> 4;
-        h4 A[4];
+            // the first tile's loads follow the first batch: in flight while the tables are built
+            if (u0 == 0 && t_begin + w < t_end) load(t_begin + w, T0);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const f4 x = mrow < 4 ? *(const LDS_AS f4*)&pb[mrow * 64 + 16 * kk + 4 * v] : f4{0.0f, 0.0f, 0.0f, 0.0f};
-            A[v] = h4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
-        }
-        const f4 al4 = kk == 0 ? *(const LDS_AS f4*)alpha : f4{1.0f, 1.0f, 1.0f, 1.0f};
+            for (int u = 0; u < GB; ++u) {
+                const int g = g0 + (u0 + u) * (NT / 256);
+                if (NG || g < n_g) {
+                    const int c0 = chw[u] & 255, c1 = (chw[u] >> 8) & 255, c2 = (chw[u] >> 16) & 255,
+                              c3 = chw[u] >> 24;
+                    f4 e4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int r = 0; r < kMaxBW; ++r) {
-            if (w + 4 * r >= nvb) break;
-            acc[r] *= al4;
-            const uint32_t off = vcol[r] & 0xFFFFu, msk = (vcol[r] >> 16) * 0x01010101u;
-            const u32x4 by = *(const LDS_AS u32x4*)(tb + 8 * BK + off + 16 * kk);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t x = by[i] & msk;
-                const h4 B = h4{(_Float16)(int8_t)(x & 255u), (_Float16)(int8_t)((x >> 8) & 255u),
-                                (_Float16)(int8_t)((x >> 16) & 255u), (_Float16)(int8_t)(x >> 24)};
-                acc[r] = __builtin_amdgcn_mfma_f32_16x16x16f16(A[i], B, acc[r], 0, 0, 0);
+                    for (int m = 0; m < 4; ++m) {
+                        const LDS_AS float* qm = qv + m * D;
+                        e4[m] = fmaf(qm[c3], zc[u].w, fmaf(qm[c2], zc[u].z, fmaf(qm[c1], zc[u].y, qm[c0] * zc[u].x)));
+                    }
+                    lut4[g * kVqSize + i] = e4;
+                }
             }
         }
-        lds_barrier();
+        lds_barrier();  // tables complete, q'' no longer read (the p rows take its place)
+        // ---- this wave's tiles
+        f4 acc[NVB];
+#pragma unroll
+        for (int r = 0; r < NVB; ++r) acc[r] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        // per head: the reference max (uniform; raised only when a score exceeds it) and this
+        // lane's sum of p
+        float m_run[4], l_lane[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            m_run[m] = -INFINITY;
+            l_lane[m] = 0.0f;
+            if (m >= GC) pw[m * 64 + lane] = (_Float16)0.0f;  // rows of absent heads stay zero
+        }
+        auto process = [&](const Tile& T, int64_t t) {
+            const bool valid = t * kTile + lane < len;
+            // scores of the chunk's heads
+            float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            // the table base as a value the sums so far feed (a move in asm): reads of at most
+            // two record words (8 groups) are in flight before their sums are formed, where
+            // the compiler would otherwise hold all of them in registers
+            uint32_t lb = (uint32_t)(uintptr_t)lut4;
+#pragma unroll
+            for (int r = 0; r < NGW; ++r) {
+                if (!NG && 4 * r >= n_g) break;
+                const uint32_t wd = T.kw[r] ^ 0x80808080u;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const uint32_t ad = lb + 16u * ((4 * r + b) * kVqSize + ((wd >> (8 * b)) & 255u));
+                    const f4 e4 = *(const LDS_AS f4*)(uintptr_t)ad;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) s[m] += e4[m];
+                }
+                if (r & 1)
+                    asm volatile("v_mov_b32 %0, %1" : "=v"(lb) : "v"(lb), "v"(s[0]), "v"(s[1]), "v"(s[2]), "v"(s[3]));
+            }
+            // online softmax per head (base 2): the reference max rises only when a score of
+            // the tile exceeds it, rescaling the sums and the accumulators; p (fp16) into this
+            // wave's rows
+            f4 al4 = f4{1.0f, 1.0f, 1.0f, 1.0f};
+            bool rescale = false;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if (m < GC) {
+                    const float sv = valid ? s[m] : -INFINITY;
+                    if (__builtin_amdgcn_ballot_w64(sv > m_run[m])) {
+                        const float mn = wave_max(sv);
+                        const float al = __builtin_amdgcn_exp2f(m_run[m] - mn);  // 0 while nothing is summed
+                        l_lane[m] *= al;
+                        al4[m] = al;
+                        rescale = true;
+                        m_run[m] = mn;
+                    }
+                    const float p = valid ? (float)(_Float16)__builtin_amdgcn_exp2f(sv - m_run[m]) : 0.0f;
+                    l_lane[m] += p;
+                    pw[m * 64 + lane] = (_Float16)p;
+                }
+            }
+            // A operands: row = head (rows 4.. zero), k-slot e of MFMA i = token 16 kk + 4 i + e
+            h4 A[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                A[i] = col < GC ? *(const LDS_AS h4*)&pw[col * 64 + 16 * kk + 4 * i] : h4{};
+#pragma unroll
+            for (int r = 0; r < NVB; ++r) {
+                if (r >= nvb) break;
+                if (rescale) acc[r] *= al4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t y = (T.vv[r][i] & vmsk[r]) ^ vflp[r];
+                    // fp16 1024 + byte: high byte 0x64 over each data byte
+                    const uint32_t lo2 = __builtin_amdgcn_perm(0x64646464u, y, 0x07010600u);
+                    const uint32_t hi2 = __builtin_amdgcn_perm(0x64646464u, y, 0x07030602u);
+                    const h4 B = __builtin_bit_cast(h4, (uint64_t)lo2 | ((uint64_t)hi2 << 32));
+                    acc[r] = __builtin_amdgcn_mfma_f32_16x16x16f16(A[i], B, acc[r], 0, 0, 0);
+                }
+            }
+        };
+        // two register sets: the next tile's loads in flight while one is computed
+        Tile T1;
+        for (int64_t t = t_begin + w; t < t_end; t += 2 * kVqWaves) {
+            load(t + kVqWaves, T1);
+            process(T0, t);
+            if (t + kVqWaves >= t_end) break;
+            load(t + 2 * kVqWaves, T0);
+            process(T1, t + kVqWaves);
+        }
+        float l_run[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) l_run[m] = m < GC ? wave_sum(l_lane[m]) : 0.0f;
+        // ---- combine the waves: maxima and sums, then the columns
+        lds_barrier();  // every wave is past its tiles (the tables are free)
+        LDS_AS float* const em = (LDS_AS float*)(sm + L.epi) - 2 * kVqWaves * 4;  // [2][kVqWaves][4]
+        LDS_AS float* const ec = (LDS_AS float*)(sm + L.epi);                      // [kVqWaves][4][16 nvb]
+        if (lane < 4) {
+            em[w * 4 + lane] = lane < GC ? m_run[lane] : -INFINITY;
+            em[(kVqWaves + w) * 4 + lane] = lane < GC ? l_run[lane] : 0.0f;
+        }
+        if (kk == 0) {
+#pragma unroll
+            for (int r = 0; r < NVB; ++r) {
+                if (r >= nvb) break;
+                const float off = vflp[r] ? 1152.0f : 1024.0f;
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    if (m < GC) ec[(w * 4 + m) * 16 * nvb + 16 * r + col] = acc[r][m] - off * l_run[m];
+            }
+        }
     }
-    wait_vm(0);
-    // ---- partials: [max, sum, 128 sum, 0, columns]
+    lds_barrier();
+    LDS_AS float* const em = (LDS_AS float*)(sm + L.epi) - 2 * kVqWaves * 4;
+    LDS_AS float* const ec = (LDS_AS float*)(sm + L.epi);
     const int64_t zh = (int64_t)z * a.n_kv + h;
     float* const P = part + ((zh * a.wg_per_head + wgi) * a.G + hh0) * a.part_ld;
-    if (w < GC && lane == 0) {
-        float* o = P + w * a.part_ld;
-        o[0] = m_run;
-        o[1] = l_run;
-        o[2] = 128.0f * l_run;
-        o[3] = 0.0f;
-    }
-    if (lane < 16) {
+    for (int i = tid; i < GC * (16 * nvb + 1); i += NT) {
+        const int m = i / (16 * nvb + 1), c = i - m * (16 * nvb + 1);
+        float M = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < kMaxBW; ++r) {
-            if (w + 4 * r >= nvb) break;
-            for (int m = 0; m < GC; ++m) P[m * a.part_ld + kPartHead + 16 * (w + 4 * r) + lane] = acc[r][m];
+        for (int v = 0; v < kVqWaves; ++v) M = fmaxf(M, em[v * 4 + m]);
+        float sum = 0.0f;
+#pragma unroll
+        for (int v = 0; v < kVqWaves; ++v) {
+            const float mv = em[v * 4 + m];
+            const float wt = mv == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
+            sum += wt * (c == 16 * nvb ? em[(kVqWaves + v) * 4 + m] : ec[(v * 4 + m) * 16 * nvb + c]);
+        }
+        if (c == 16 * nvb) {
+            P[m * a.part_ld + 0] = M;
+            P[m * a.part_ld + 1] = sum;
+            P[m * a.part_ld + 2] = 128.0f * sum;
+            P[m * a.part_ld + 3] = 0.0f;
+        } else {
+            P[m * a.part_ld + kPartHead + 16 * vb0 + c] = sum;
         }
     }
 }
@@ -1377,11 +1471,11 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
         p.vq = true;
         a.G = G;
         a.tile_bytes = 8 * cb->total_bits;
-        const VqLds L = vq_lds(cb->heads[0].vq_groups, a.tile_bytes, d);
+        const VqLds L = vq_lds(cb->heads[0].vq_groups, d, std::min(p.nvb_max, vq_blocks(d)));
         p.lds = (size_t)L.total;
         if (p.lds > 160 * 1024) return set_error(AATC_ERR_UNSUPPORTED, "decode needs %zu bytes of LDS", p.lds);
-        p.wgs_per_cu = (int)std::max<size_t>(1, (160 * 1024) / p.lds);
-        p.nw = 4;
+        p.wgs_per_cu = 1;
+        p.nw = kVqWaves;
         const int64_t units = (int64_t)cb->n_kv * n_seqs * ((G + 3) / 4);
         const int64_t slots = 256 * (int64_t)p.wgs_per_cu;
         p.wg_per_head = (int)std::max<int64_t>(1, std::min<int64_t>({slots / units, n_tiles_of(max_len), kMaxWG}));
@@ -1574,9 +1668,11 @@ int launch_vq_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* b
     hipEvent_t e0, e1;
     profile_slot(e0, e1);
     if (e0) HIP_TRY(hipEventRecord(e0, st));
-    hipLaunchKernelGGL((vq_decode_kernel<D, NG>), dim3(p.wg_per_head * ((a.G + 3) / 4), a.n_kv, n_seqs), dim3(256), p.lds,
-                       st, blob, cache, a, ids, lens, q, part);
-    HIP_TRY(hipGetLastError());
+    for (int vb0 = 0; vb0 < p.nvb_max; vb0 += vq_blocks(D)) {
+        hipLaunchKernelGGL((vq_decode_kernel<D, NG>), dim3(p.wg_per_head * ((a.G + 3) / 4), a.n_kv, n_seqs),
+                           dim3(64 * kVqWaves), p.lds, st, blob, cache, a, ids, lens, q, part, vb0);
+        HIP_TRY(hipGetLastError());
+    }
     if (e1) HIP_TRY(hipEventRecord(e1, st));
     hipLaunchKernelGGL((merge_kernel<D>), dim3(a.n_kv * (D / kMergeSlice), n_seqs, a.G), dim3(kMergeThreads), 0, st,
                        blob, a.layer, a.n_kv, a.G, p.wg_per_head, a.part_ld, (const float*)part, out);
