@@ -46,6 +46,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "quantized_attention_klt_amd", "csrc")
 DECODE_PMC = (os.path.join(PROFILES, "decode_kernel_llama128k_pmc.txt"), os.path.join(CSRC, "decode.hip"))
 ENCODE_PMC = (os.path.join(PROFILES, "encode_kernel_llama128k_pmc.txt"), os.path.join(CSRC, "encode.hip"))
+VQ_DECODE_PMC = (os.path.join(PROFILES, "vq_decode_kernel_llama128k_pmc.txt"), os.path.join(CSRC, "decode.hip"))
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "decode-attn effective HBM GB/s (% of peak) + encode tokens/s, 128k ctx, 2.75 b/elem"
 FLUSH_BYTES = 512 << 20
@@ -127,6 +128,18 @@ def measured_traffic(summary: str, source: str):
         return int(float(fields["hbm_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def profiled_us(summary: str, kernel: str):
+    """Average duration (us) of the kernel whose name starts with `kernel` in a committed
+    rocprofv3 --stats summary (profiles/*_kstats.txt), or None."""
+    try:
+        for line in open(summary):
+            if not line.startswith("#") and kernel in line.split("(")[0]:
+                return float(line.split()[-3])
+    except (OSError, ValueError, IndexError):
+        pass
+    return None
 
 
 def cpu_model() -> str:
@@ -309,9 +322,16 @@ def run_layer(args, w, ctx, torch, q, dev):
                        "decode_kernel (split decode: query transform, scores, online softmax, value sums)"),
             "bound": "hbm", "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None if vq else measured_traffic(*DECODE_PMC),
+            "traffic": measured_traffic(*(VQ_DECODE_PMC if vq else DECODE_PMC)),
             "algorithmic_bytes": kern_bytes, "kernel_ms": round(kern_s * 1e3, 4),
             "source_sha256_16": source_hash(DECODE_PMC[1])}
+    ks = os.path.join(PROFILES, "vq_path_kernels_llama128k_kstats.txt" if vq else "path_kernels_llama128k_kstats.txt")
+    if w.name in ("llama_128k", "llama_vq_128k") and ctx == w.ctx:
+        k_us = profiled_us(ks, "void vq_decode_kernel<" if vq else "void decode_kernel<")
+        m_us = profiled_us(ks, "void merge_kernel<")
+        if k_us:
+            roof.update({"rocprof_summary": os.path.relpath(ks, ROOT), "rocprof_kernel_us": k_us,
+                         "rocprof_merge_us": m_us, "rocprof_frac": round(kern_bytes / (k_us * 1e3) / HBM_PEAK_GBS, 4)})
     if probe:
         roof.update({"probe_gbs": round(probe["plain"]["gbs"], 2), "frac_of_probe": round(kern_gbs / probe["plain"]["gbs"], 4),
                      "probe_tile_stream_gbs": round(probe["tiles"]["gbs"], 2),

@@ -1231,10 +1231,10 @@ __global__ __launch_bounds__(64 * kVqWaves) void vq_decode_kernel(const DevHead*
         uint32_t kw[NGW];
         u32x4 vv[NVB];
     };
-    // a tile's registers; tiles past the workgroup's share are read too (in range or zeros)
-    // so that every tile issues the same loads
+    // a tile's registers; every tile issues the same loads, and those of a tile past the
+    // workgroup's share take an offset past the range (zeros, no memory traffic)
     auto load = [&](int64_t t, Tile& T) {
-        const uint32_t tb = (uint32_t)(t * tbytes);
+        const uint32_t tb = t < t_end ? (uint32_t)(t * tbytes) : 0x80000000u;
 #pragma unroll
         for (int r = 0; r < NGW; ++r)
             if (NG || 4 * r < n_g)
