@@ -507,6 +507,12 @@ def run_loop(args, w, torch, q, dev):
     def step(i):
         q.decode_attention_append(cb, blob, cache, 0, ids, lens_all[i:i + 1], cap, kn[i], vn[i], qn[i], out[i], ws)
 
+    # warm-up steps (first-call costs), then the cache back to its prefilled state
+    for i in range(min(args.warmup, n)):
+        q.flush_write(flush)
+        step(i)
+    cache_t.copy_(pristine)
+    torch.cuda.synchronize()
     # (a) every step eagerly, the LLC flushed before each (as in a model whose other layers
     # evict this layer's cache between steps): per-step latency distribution
     tm = Timer(torch, n)
