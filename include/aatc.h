@@ -253,7 +253,9 @@ int aatc_cache_bytes(const aatc_codebook* cb, int32_t n_layers, int32_t n_seqs,
  * filled tile are kept (the tile is read, merged and written back).
  * Arithmetic: u = x (W_hi + W_lo) + (2^(b-1) - 1/2 - mu (W_hi + W_lo)) with W = U scaled
  * per channel by the fp32 reciprocal step and W_hi/W_lo its bf16 split (bf16 MFMA, fp32
- * accumulation, the start value rounded once from fp64); code = u clamped to
+ * accumulation, the start value rounded once from fp64; above 6.5 bits/element a third
+ * bf16 term W_mid = W - W_hi - W_lo joins, for codebooks whose narrow cells the two-term
+ * rounding would flip more than 1e-4 of the codes of); code = u clamped to
  * [0, 2^b - 1] and rounded to nearest, ties to even.  That is the quantizer of
  * aatc_encode_coeffs, floor(c/step) + 2^(b-1), wherever c/step is not within the fp32
  * rounding of this arithmetic of a cell edge.
@@ -292,14 +294,17 @@ int aatc_decode_workspace_bytes(const aatc_codebook* cb, int32_t n_seqs, int64_t
  * packed tiles runs as one kernel on `stream` (each workgroup transforms the queries
  * itself; the last workgroup of each (sequence, kv-head) to finish merges the partials and
  * applies the inverse transform), or, when a call has more than 256 (sequence, kv-head)
- * pairs or more than 64 workgroups per pair, as that kernel followed by a merge kernel
+ * pairs, more than 64 workgroups per pair or more than 32 KiB of partials per pair (a large
+ * merge is faster spread over many CUs), as that kernel followed by a merge kernel
  * ("KV Cache Compression Through the Lens of Transform Coding", Methodology;
  * "Attention-Aware Transform Coding Guide", KLT section: q.k = (U_K^T q).(U_K^T k)).
  * At most 65535 sequences per call (CAPACITY beyond).
  * With vector-quantized keys (aatc_codebook_create_vq, key_quantizer = 1) the scores come
  * from per-(query head, group) tables over the codebooks (a token's score is the sum of
- * its groups' entries); the workspace and merge are the same.
- * Errors: INVALID_ARG, CAPACITY, WORKSPACE, HIP. */
+ * its groups' entries); the workspace is the same and the merge kernel always follows.
+ * Errors: INVALID_ARG, CAPACITY, WORKSPACE, HIP; UNSUPPORTED (before anything is enqueued,
+ * also from aatc_decode_workspace_bytes) when a head's tiles and operand scratch need more
+ * LDS than a CU holds: at d = 128 above 7.5 bits/element. */
 int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
                           int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                           const int64_t* seq_lens, int64_t max_len, const uint16_t* q,

@@ -54,7 +54,11 @@ struct HeadCB {
 struct alignas(256) DevHead {
     int32_t d, BK, BV, nfK, nfV;
     int32_t vq_groups;  // > 0: vector-quantized keys (the vq_* arrays below)
-    int32_t pad0[58];
+    // encoder basis terms: 2 (W = hi + lo) or 3 (+ mid, for rates above 6.5 bits/element,
+    // where the channels' cells are narrow enough that the hi + lo rounding would flip more
+    // than 1e-4 of the codes)
+    int32_t enc_terms;
+    int32_t pad0[57];
     float UK[kMaxD * kMaxD];      // fp32 basis (query transform)
     float UV[kMaxD * kMaxD];      // fp32 basis (inverse transform of values)
     float UVt[kMaxD * kMaxD];     // its transpose, UVt[j*d + i] = UV[i*d + j]
@@ -66,6 +70,8 @@ struct alignas(256) DevHead {
     uint16_t EKt_lo[kMaxD * kMaxD];
     uint16_t EVt_hi[kMaxD * kMaxD];
     uint16_t EVt_lo[kMaxD * kMaxD];
+    uint16_t EKt_mid[kMaxD * kMaxD];  // third terms: bf16(W - hi - lo) (zero when enc_terms = 2)
+    uint16_t EVt_mid[kMaxD * kMaxD];
     // query transform q' = T_K^{-1} q (T_K the key basis; T_K^{-1} = U_K^T for the KLT),
     // bf16 split in the same layout: QKt_hi[j*d + i] + QKt_lo[j*d + i] = (T_K^{-1})[j][i]
     uint16_t QKt_hi[kMaxD * kMaxD];
@@ -125,6 +131,12 @@ struct alignas(256) DevHead {
     float vq_cent[kMaxVqGroups][kVqSize][kVqDim];
 };
 
+}  // namespace aatc
+
+namespace aatc {
+// encoder basis terms for a codebook of total_bits per token and kv-head at head_dim d:
+// three above 6.5 bits/element
+inline int enc_terms_for(int total_bits, int d) { return total_bits > 13 * d ? 3 : 2; }
 }  // namespace aatc
 
 struct aatc_codebook {

@@ -595,6 +595,7 @@ int finalize(aatc_codebook* cb) {
         D.BV = H.BV;
         D.nfK = (int)H.fK.size();
         D.nfV = (int)H.fV.size();
+        D.enc_terms = enc_terms_for(cb->total_bits, d);
         for (int which = 0; which < 2; ++which) {
             const std::vector<double>& U = which ? H.UV : H.UK;
             const std::vector<double>& mu = which ? H.muV : H.muK;
@@ -603,6 +604,7 @@ int finalize(aatc_codebook* cb) {
             float* U32 = which ? D.UV : D.UK;
             uint16_t* hi = which ? D.EVt_hi : D.EKt_hi;  // [j * d + i]
             uint16_t* lo = which ? D.EVt_lo : D.EKt_lo;
+            uint16_t* mid = which ? D.EVt_mid : D.EKt_mid;
             float* start = which ? D.estartV : D.estartK;
             for (int j = 0; j < d; ++j) {
                 // the fp32 reciprocal step of the quantizer (0: uncoded channel)
@@ -613,7 +615,11 @@ int finalize(aatc_codebook* cb) {
                     const float w = (float)(U[(size_t)i * d + j] * inv);
                     hi[j * d + i] = f32_to_bf16(w);
                     lo[j * d + i] = f32_to_bf16(w - bf16_to_f32(hi[j * d + i]));
-                    s += mu[i] * ((double)bf16_to_f32(hi[j * d + i]) + (double)bf16_to_f32(lo[j * d + i]));
+                    mid[j * d + i] = D.enc_terms == 3
+                                         ? f32_to_bf16(w - bf16_to_f32(hi[j * d + i]) - bf16_to_f32(lo[j * d + i]))
+                                         : (uint16_t)0;
+                    s += mu[i] * ((double)bf16_to_f32(hi[j * d + i]) + (double)bf16_to_f32(lo[j * d + i]) +
+                                  (double)bf16_to_f32(mid[j * d + i]));
                 }
                 start[j] = bits[j] ? (float)((double)(1 << (bits[j] - 1)) - 0.5 - s) : 0.0f;
             }

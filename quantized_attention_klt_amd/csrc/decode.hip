@@ -283,8 +283,8 @@ constexpr int scratch_bytes(int rb, int nqm, int nvb, int d) {
 // Append mode: the codes of one token for column block cb of 2 D / 16 (key blocks, then
 // value blocks), OR-ed into its records staged in LDS (key record bytes, then value record
 // bytes).  The projection runs on the encoder's MFMAs with the same operands, start value
-// and order (hi then lo per k-step), and the same quantizer, so the codes equal those the
-// encoder writes for the token.  Lane (0, c) holds the token's coefficient of channel
+// and order (hi, lo and, for three-term bases, mid per k-step), and the same quantizer, so
+// the codes equal those the encoder writes for the token.  Lane (0, c) holds the token's coefficient of channel
 // 16 (cb mod D / 16) + c (MFMA row 0; the other rows are zero).
 template <int D>
 __device__ __forceinline__ void append_block(const DevHead& H, const uint16_t* xk, const uint16_t* xv, int cb,
@@ -295,12 +295,15 @@ __device__ __forceinline__ void append_block(const DevHead& H, const uint16_t* x
     const int j = 16 * (isV ? cb - NB : cb) + c;
     const uint16_t* uh = isV ? H.EVt_hi : H.EKt_hi;
     const uint16_t* ul = isV ? H.EVt_lo : H.EKt_lo;
+    const uint16_t* um = isV ? H.EVt_mid : H.EKt_mid;
+    const bool t3 = H.enc_terms == 3;
     const uint16_t* x = isV ? xv : xk;
-    bf16x8 bh[KS], bl[KS], av[KS];
+    bf16x8 bh[KS], bl[KS], bm[KS], av[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         bh[ks] = *(const bf16x8*)(uh + j * D + 32 * ks + 8 * g);
         bl[ks] = *(const bf16x8*)(ul + j * D + 32 * ks + 8 * g);
+        bm[ks] = *(const bf16x8*)(um + j * D + 32 * ks + 8 * g);
         const bf16x8 xa = *(const bf16x8*)(x + 32 * ks + 8 * g);
         av[ks] = c == 0 ? xa : bf16x8{};
     }
@@ -315,6 +318,7 @@ __device__ __forceinline__ void append_block(const DevHead& H, const uint16_t* x
     for (int ks = 0; ks < KS; ++ks) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks], bh[ks], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks], bl[ks], acc, 0, 0, 0);
+        if (t3) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks], bm[ks], acc, 0, 0, 0);
     }
     if (g == 0 && bits > 0) {
         const uint32_t code = code_byte(acc[0], (float)((1 << bits) - 1), 0, 0u);

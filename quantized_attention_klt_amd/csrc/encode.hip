@@ -203,7 +203,7 @@ constexpr int kEncodeRing = 2;
 template <int D>
 constexpr size_t encode_lds_bytes() { return kEncodeRing * 64 * D * 2 + 4 * kStageWords + sizeof(PieceTab); }
 
-template <int D, bool isV>
+template <int D, bool isV, int NT3>
 __device__ __forceinline__ void encode_mfma_body(const DevHead* __restrict__ blob, uint8_t* __restrict__ cache,
                                                  int layer, int n_kv, int64_t n_tiles_cap, int tile_bytes,
                                                  const SeqArgs& sa, int64_t n_tokens, int64_t ntiles,
@@ -233,6 +233,7 @@ __device__ __forceinline__ void encode_mfma_body(const DevHead* __restrict__ blo
     // B operands and quantizer constants of this lane's columns 16 (w CBW + cbw) + c: channel
     // j = encoder order of that column (an uncoded channel has a zero column and no field)
     bf16x8 bh[CBW][KS], bl[CBW][KS];
+    bf16x8 bm[NT3 == 3 ? CBW : 1][KS];  // third terms (three-term bases only)
     float ustart[CBW], cmax[CBW];
     int jj[CBW];
     {
@@ -247,6 +248,7 @@ __device__ __forceinline__ void encode_mfma_body(const DevHead* __restrict__ blo
             for (int ks = 0; ks < KS; ++ks) {
                 bh[cbw][ks] = *(const bf16x8*)(uh + j * D + 32 * ks + 8 * g);
                 bl[cbw][ks] = *(const bf16x8*)(ul + j * D + 32 * ks + 8 * g);
+                if constexpr (NT3 == 3) bm[cbw][ks] = *(const bf16x8*)((isV ? H.EVt_mid : H.EKt_mid) + j * D + 32 * ks + 8 * g);
             }
             ustart[cbw] = isV ? H.estartV[j] : H.estartK[j];
             cmax[cbw] = (float)((1 << (isV ? H.bitsV[j] : H.bitsK[j])) - 1);
@@ -350,6 +352,14 @@ __device__ __forceinline__ void encode_mfma_body(const DevHead* __restrict__ blo
 #pragma unroll
                 for (int cbw = 0; cbw < CBW; ++cbw)
                     acc[cbw][tg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bl[cbw][ks], acc[cbw][tg + u], 0, 0, 0);
+            if constexpr (NT3 == 3) {
+#pragma unroll
+                for (int u = 0; u < TBG; ++u)
+#pragma unroll
+                    for (int cbw = 0; cbw < CBW; ++cbw)
+                        acc[cbw][tg + u] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bm[cbw][ks], acc[cbw][tg + u], 0, 0, 0);
+            }
         }
         // codes of tokens 16 tb + 4 g + e: the four of one tb share staged word q * kStageRow +
         // 4 tb + g (byte e), so they are packed into one word and OR-ed with one operation per
@@ -396,18 +406,20 @@ __device__ __forceinline__ void encode_mfma_body(const DevHead* __restrict__ blo
     wait_vm(0);
 }
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void encode_mfma_kernel(
+// NT3: basis terms (2, or 3 for rates above 6.5 bits/element, whose third operands take the
+// registers of a third wave per SIMD)
+template <int D, int NT3>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT3 == 3 ? 2 : 3))) void encode_mfma_kernel(
     const DevHead* __restrict__ blob, uint8_t* __restrict__ cache, int layer, int n_kv, int64_t n_tiles_cap,
     int tile_bytes, SeqArgs sa, int64_t n_tokens, int64_t ntiles, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, int n_seqs_cache, int values_only) {
     if (values_only && !(blockIdx.y & 1)) return;  // keys are vector-quantized by vq_keys_kernel
     if (blockIdx.y & 1)
-        encode_mfma_body<D, true>(blob, cache, layer, n_kv, n_tiles_cap, tile_bytes, sa, n_tokens, ntiles, K, V,
-                                  n_seqs_cache);
+        encode_mfma_body<D, true, NT3>(blob, cache, layer, n_kv, n_tiles_cap, tile_bytes, sa, n_tokens, ntiles, K, V,
+                                       n_seqs_cache);
     else
-        encode_mfma_body<D, false>(blob, cache, layer, n_kv, n_tiles_cap, tile_bytes, sa, n_tokens, ntiles, K, V,
-                                   n_seqs_cache);
+        encode_mfma_body<D, false, NT3>(blob, cache, layer, n_kv, n_tiles_cap, tile_bytes, sa, n_tokens, ntiles, K, V,
+                                        n_seqs_cache);
 }
 
 // ------------------------------------------------------------------------------------
@@ -615,32 +627,41 @@ static int encode_common(const aatc_codebook* cb, const void* d_blob, const aatc
                                n_tokens, coeffs, cache->n_seqs);
         } else {
             // workgroups per (sequence, kv-head, keys | values): fill the resident slots
+            const int nt3 = aatc::enc_terms_for(cb->total_bits, d);
             const int64_t units = (int64_t)used * cb->n_kv * 2;
             const size_t lds = d == 64 ? encode_lds_bytes<64>() : encode_lds_bytes<128>();
-            const int64_t slots = (int64_t)kCUs * std::min<size_t>(3, kLdsPerCU / lds);  // 3: waves_per_eu
+            const int64_t slots = (int64_t)kCUs * std::min<size_t>(nt3 == 3 ? 2 : 3, kLdsPerCU / lds);  // waves_per_eu
             const unsigned wx = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ntiles, slots / units));
             const dim3 grid(wx, (unsigned)(2 * cb->n_kv), (unsigned)used);
             const int vq = cb->heads[0].vq_groups > 0;
             const dim3 kgrid((unsigned)ntiles, (unsigned)cb->n_kv, (unsigned)used);
+            const void* kern = d == 64 ? (nt3 == 3 ? (const void*)encode_mfma_kernel<64, 3> : (const void*)encode_mfma_kernel<64, 2>)
+                                       : (nt3 == 3 ? (const void*)encode_mfma_kernel<128, 3> : (const void*)encode_mfma_kernel<128, 2>);
             if (lds > 64 * 1024)
-                HIP_TRY(hipFuncSetAttribute(d == 64 ? (const void*)encode_mfma_kernel<64> : (const void*)encode_mfma_kernel<128>,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+                HIP_TRY(hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+            uint8_t* cdata = (uint8_t*)cache->data;
+#define AATC_ENCODE_LAUNCH(D_, T_)                                                                                 \
+    hipLaunchKernelGGL((encode_mfma_kernel<D_, T_>), grid, dim3(256), lds, (hipStream_t)stream, blob, cdata, layer, \
+                       cb->n_kv, ncap, tile_bytes, sa, n_tokens, ntiles, Kz, Vz, cache->n_seqs, vq)
             if (d == 64) {
-                hipLaunchKernelGGL(encode_mfma_kernel<64>, grid, dim3(256), encode_lds_bytes<64>(), (hipStream_t)stream, blob,
-                                   (uint8_t*)cache->data, layer, cb->n_kv, ncap, tile_bytes, sa, n_tokens, ntiles, Kz, Vz,
-                                   cache->n_seqs, vq);
-                if (vq)
-                    hipLaunchKernelGGL(vq_keys_kernel<64>, kgrid, dim3(256), 0, (hipStream_t)stream, blob,
-                                       (uint8_t*)cache->data, layer, cb->n_kv, ncap, tile_bytes, sa, n_tokens, Kz,
-                                       cache->n_seqs);
+                if (nt3 == 3)
+                    AATC_ENCODE_LAUNCH(64, 3);
+                else
+                    AATC_ENCODE_LAUNCH(64, 2);
             } else {
-                hipLaunchKernelGGL(encode_mfma_kernel<128>, grid, dim3(256), encode_lds_bytes<128>(), (hipStream_t)stream, blob,
-                                   (uint8_t*)cache->data, layer, cb->n_kv, ncap, tile_bytes, sa, n_tokens, ntiles, Kz, Vz,
-                                   cache->n_seqs, vq);
-                if (vq)
-                    hipLaunchKernelGGL(vq_keys_kernel<128>, kgrid, dim3(256), 0, (hipStream_t)stream, blob,
-                                       (uint8_t*)cache->data, layer, cb->n_kv, ncap, tile_bytes, sa, n_tokens, Kz,
-                                       cache->n_seqs);
+                if (nt3 == 3)
+                    AATC_ENCODE_LAUNCH(128, 3);
+                else
+                    AATC_ENCODE_LAUNCH(128, 2);
+            }
+#undef AATC_ENCODE_LAUNCH
+            if (vq) {
+                if (d == 64)
+                    hipLaunchKernelGGL(vq_keys_kernel<64>, kgrid, dim3(256), 0, (hipStream_t)stream, blob, cdata, layer,
+                                       cb->n_kv, ncap, tile_bytes, sa, n_tokens, Kz, cache->n_seqs);
+                else
+                    hipLaunchKernelGGL(vq_keys_kernel<128>, kgrid, dim3(256), 0, (hipStream_t)stream, blob, cdata, layer,
+                                       cb->n_kv, ncap, tile_bytes, sa, n_tokens, Kz, cache->n_seqs);
             }
         }
         HIP_TRY(hipGetLastError());

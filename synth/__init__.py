@@ -117,6 +117,8 @@ WORKLOADS: Dict[str, Workload] = {
     # (16 heads per kv-head) at d = 64 and 3.0 bits/element, and at d = 128 and 6.0
     "edge_g16": Workload("edge_g16", 6, 64, 2, 32, 1, 1, 1024, 3.0, 2048, 64, "bf16"),
     "edge_rate": Workload("edge_rate", 7, 128, 1, 16, 1, 1, 1024, 6.0, 4096, 32, "bf16"),
+    # the largest rate: 8 bits on every channel (d = 64, 8 KiB tiles)
+    "edge_max": Workload("edge_max", 13, 64, 1, 4, 1, 1, 512, 8.0, 2048, 32, "bf16"),
     # vector-quantized keys at 2.0 bits/element (one byte per group of 4 coefficients):
     # a small head, and the Llama layer at 128k context
     "vq_tiny": Workload("vq_tiny", 8, 64, 1, 4, 1, 1, 512, 2.0, 2048, 256, "bf16"),

@@ -166,13 +166,14 @@ def test_decode_wide_batch(lib, torch):
     assert err <= ATTN_BAR
 
 
-@pytest.mark.parametrize("wname,n_seqs,l0,steps", [("tiny", 2, (126, 63), 4), ("llama_loop", 1, (3000,), 4)])
+@pytest.mark.parametrize("wname,n_seqs,l0,steps", [("tiny", 2, (126, 63), 4), ("llama_loop", 1, (3000,), 4),
+                                                    ("edge_max", 1, (127,), 3)])
 def test_fused_append_decode_loop(lib, torch, wname, n_seqs, l0, steps):
     """Generation loop through aatc_decode_attention_append: per step one new token per
     (sequence, kv-head) is coded and attended in the same launch.  The cache bytes equal
     those of aatc_encode appending the same tokens (bit-exact), and every step's output
     is within the decode bar of the oracle on the GPU's own bytes (tile boundaries and
-    ragged sequences included)."""
+    ragged sequences included; 8 bits on every channel takes the three-term encoder basis)."""
     ctx = max(l0) + steps
     case = Case(wname, ctx, n_seqs=n_seqs, n_calib_q=64)
     _log(f"{wname}: fused append+decode, {n_seqs} sequences from {l0}, {steps} steps")
@@ -215,11 +216,13 @@ def test_fused_append_decode_loop(lib, torch, wname, n_seqs, l0, steps):
         assert err <= ATTN_BAR
 
 
-@pytest.mark.parametrize("wname,ctx,lens", [("edge_g16", 700, [700, 65]), ("edge_rate", 300, [300])])
+@pytest.mark.parametrize("wname,ctx,lens", [("edge_g16", 700, [700, 65]), ("edge_rate", 300, [300]),
+                                            ("edge_max", 300, [300, 1])])
 def test_decode_and_encode_at_the_limits(lib, torch, wname, ctx, lens):
     """16 query heads per kv-head (the probability operands in buffers of their own when the
-    key block is smaller, d = 64 at 3.0 b/e) and a high rate (d = 128 at 6.0 b/e: the widest
-    score and value schedules): decode within the bar of the oracle on the same bytes,
+    key block is smaller, d = 64 at 3.0 b/e), a high rate (d = 128 at 6.0 b/e: the widest
+    score and value schedules) and the largest (8 bits on every channel at d = 64, a 1-token
+    sequence beside a 300-token one): decode within the bar of the oracle on the same bytes,
     end-to-end codes within the flip bar."""
     case = Case(wname, ctx, n_seqs=len(lens), n_calib_q=32, lens=lens)
     _log(f"{wname}: G={case.group}, d={case.d}, lengths {lens}")

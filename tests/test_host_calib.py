@@ -235,3 +235,23 @@ def test_vector_quantized_keys_error_paths():
                       (good[0][0], good[1][0], bad_cent), (good[0][0][:3], good[1][0], good[2][0][:3])):
         with pytest.raises(q.AatcError):
             q.codebook_create_vq(*args, g[None], sc[None], ce[None], ref.bV[None], ref.stepV[None])
+
+
+def test_decode_rate_limit_is_reported_before_launch():
+    """At d = 128 the decode supports up to 7.5 bits/element: 8 bits on every channel makes
+    16 KiB tiles whose ring and operand scratch need more LDS than a CU holds, and the plan
+    (computed on the host, before anything is enqueued) says so with UNSUPPORTED.  At d = 64
+    the same rate is supported."""
+    for d, rate, ok in ((128, 7.5, True), (128, 8.0, False), (64, 8.0, True)):
+        w = synth.Workload("limit", 13, d, 1, 4, 1, 1, 512, rate, 2048, 16, "bf16")
+        hm = synth.head_model(w, 0, 0)
+        K, V, Q = synth.calibration_samples(w, hm, 0, 0)
+        ref = oracle.build_head_codebook(oracle.head_stats(K, V, Q), rate, key_align=LAYOUT_KEY_ALIGN)
+        cb = q.codebook_create(d, 1, 1, 4, ref.UK[None], ref.UV[None], ref.muK[None], ref.muV[None], ref.bK[None],
+                               ref.bV[None], ref.stepK[None], ref.stepV[None])
+        if ok:
+            assert cb.decode_workspace_bytes(1, 512) > 0
+        else:
+            with pytest.raises(q.AatcError) as e:
+                cb.decode_workspace_bytes(1, 512)
+            assert e.value.status == -2  # AATC_ERR_UNSUPPORTED

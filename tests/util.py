@@ -123,7 +123,8 @@ def normwise_rel_err(o, ref):
 # ------------------------------------------------------------ end-to-end code flips
 # The GPU encoder computes u = t + 2^(b-1) - 1/2 in fp32 from bf16 x: the bases scaled by the
 # fp32 reciprocal step, W = fp32(U / step), held as two bf16 parts (hi + lo, which leaves
-# |W - hi - lo| <= 2^-18 |W|) or in fp32, and the accumulators starting at
+# |W - hi - lo| <= 2^-18 |W|), three (above 6.5 bits/element) or in fp32, and the
+# accumulators starting at
 # 2^(b-1) - 1/2 - mu W.  Its t then differs from the exact t = c * inv32 by at most
 #     E = (2^-17 + (d + 4) 2^-24) S inv32 + (d + 4) 2^-24 (2^(b-1) + 1) + 4 2^-24 |t|,
 #     S = sum_i (|x_i| + |mu_i|) |U_ij|
