@@ -180,6 +180,43 @@ __device__ __forceinline__ uint8_t* tile_ptr(uint8_t* cache, int layer, int n_se
     return cache + ((((int64_t)layer * n_seqs_cache + seq) * n_kv + h) * n_tiles_cap + tile) * (int64_t)tile_bytes;
 }
 
+// The 64 token rows (D bf16 each) of tile index tl into LDS at xd by direct global->LDS
+// copies: copy n of wave w fills the 64 chunk positions p = 64 (NLD w + n) + lane (token
+// t = p / CH, position p % CH), and position p holds the token's chunk (p % CH) ^ (t mod CH)
+// (the swizzle is in the source addresses), so that the 16 rows an MFMA operand read touches
+// fall in distinct banks.  Slots outside the call's tokens copy the call's first token
+// (their codes are never stored).  The copies carry the non-temporal hint: inputs are read
+// once.  A tile whose 64 tokens all lie in the call is read by buffer loads: one resource per
+// tile (scalar, based at its first token).  Copy n's token is t0 + n (64 / CH) and its chunk
+// kc0 ^ ((n 64 / CH) mod CH) (t0 mod CH has no bits in common with n 64 / CH), so the lane's
+// byte offset is xa + (xb ^ 16 K_n) plus a scalar n (64 / CH) token rows.
+template <int D>
+__device__ __forceinline__ void copy_x_rows(const uint16_t* __restrict__ X, int64_t xstride, int64_t start,
+                                            int64_t n_tokens, int64_t tl, LDS_AS uint8_t* xd, int w, int lane) {
+    constexpr int CH = D / 8, NLD = 64 * CH / 256;
+    const int64_t tok0 = tl * kTile;
+    if (tok0 >= start && tok0 + kTile <= start + n_tokens) {
+        const int t0 = (64 * NLD * w + lane) / CH;
+        const uint32_t xa = (uint32_t)(2 * t0 * xstride), xb = 16u * (uint32_t)((lane % CH) ^ (t0 & (CH - 1)));
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(X + (tok0 - start) * xstride), (short)0, (int)(2 * kTile * xstride), 0x00020000);
+#pragma unroll
+        for (int n = 0; n < NLD; ++n)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(xd + 1024 * (NLD * w + n)), 16,
+                                                     xa + (xb ^ (16u * ((n * 64 / CH) & (CH - 1)))),
+                                                     (int)(2 * n * (64 / CH) * xstride), 0, 2);
+        return;
+    }
+#pragma unroll
+    for (int n = 0; n < NLD; ++n) {
+        const int p = 64 * (NLD * w + n) + lane, t = p / CH, kc = (p % CH) ^ (t & (CH - 1));
+        int64_t tt = tok0 + t - start;  // token index in this call's input
+        tt = tt < 0 || tt >= n_tokens ? 0 : tt;
+        __builtin_amdgcn_global_load_lds((const void*)(X + tt * xstride + 8 * kc),
+                                         (LDS_AS void*)(xd + 1024 * (NLD * w + n)), 16, 0, 2);
+    }
+}
+
 // ------------------------------------------------------------------------------------
 // encode from bf16 K, V (MFMA): a workgroup owns one (sequence, kv-head, keys | values)
 // and the tiles bx, bx + gridDim.x, ... of the call.  u = x (W_hi + W_lo) + start (W = U
@@ -221,7 +258,7 @@ __device__ __forceinline__ void encode_mfma_body(const DevHead* __restrict__ blo
     LDS_AS uint32_t* const stg = (LDS_AS uint32_t*)(esm + NB * XB);
     LDS_AS PieceTab* const pt = (LDS_AS PieceTab*)(esm + NB * XB + 4 * kStageWords);
     const int h = blockIdx.y >> 1, zi = blockIdx.z;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, c = lane & 15;
     const DevHead& H = blob[layer * n_kv + h];
     const uint16_t* X = (isV ? V : K) + ((int64_t)zi * n_tokens * n_kv + h) * D;  // token t at X + t * n_kv * D
     const int64_t xstride = (int64_t)n_kv * D;
@@ -256,22 +293,7 @@ __device__ __forceinline__ void encode_mfma_body(const DevHead* __restrict__ blo
     }
     const int nbytes = (isV ? H.BV : H.BK) / 8;
     const int boff = isV ? 8 * H.BK : 0;  // block offset in the tile
-    // x tile of tile index k into LDS by direct global->LDS copies: copy n of wave w fills
-    // the 64 chunk positions p = 64 (NLD w + n) + lane (token t = p / CH, position p % CH),
-    // and position p holds the token's chunk (p % CH) ^ (t mod CH) (the swizzle is in the
-    // source addresses).  Slots outside the call's tokens copy the call's first token (their
-    // codes are never stored).  The copies carry the non-temporal hint: inputs are read once.
-    auto copy_x = [&](int64_t tl, LDS_AS uint8_t* xd) {
-        const int64_t tok0 = tl * kTile;
-#pragma unroll
-        for (int n = 0; n < NLD; ++n) {
-            const int p = 64 * (NLD * w + n) + lane, t = p / CH, kc = (p % CH) ^ (t & (CH - 1));
-            int64_t tt = tok0 + t - start;  // token index in this call's input
-            tt = tt < 0 || tt >= n_tokens ? 0 : tt;
-            __builtin_amdgcn_global_load_lds((const void*)(X + tt * xstride + 8 * kc),
-                                             (LDS_AS void*)(xd + 1024 * (NLD * w + n)), 16, 0, 2);
-        }
-    };
+    auto copy_x = [&](int64_t tl, LDS_AS uint8_t* xd) { copy_x_rows<D>(X, xstride, start, n_tokens, tl, xd, w, lane); };
     int64_t tile = blockIdx.x;
     // the first NB - 1 tiles stream during the set-up
 #pragma unroll
