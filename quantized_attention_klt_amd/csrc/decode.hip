@@ -927,7 +927,6 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
     // (in passes of at most two row blocks - 8 query heads - to bound the LDS it takes)
     float* pout = part + (zh * a.wg_per_head + wgi) * G * PL;
     LDS_AS float* wx = (LDS_AS float*)sm;   // [NW waves][GP][PL]
-    LDS_AS float* ew = wx + NW * GP * PL;   // [NW waves][GP] weights, then [GP] maxima
 #pragma unroll
     for (int r0 = 0; r0 < RB; r0 += RBP) {
         lds_barrier();  // (the previous pass's reads are done)
@@ -947,26 +946,24 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
                 o[kPartHead + 16 * cb + c] = combine256(acc_i[rb][cb][0], acc_i[rb][cb][1], acc_i[rb][cb][2]) * (1.0f / 127.0f);
         }
         lds_barrier();
-        if (tid < GP) {
-            float M = -INFINITY;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wx[(ww * GP + tid) * PL]);
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-                const float m = wx[(ww * GP + tid) * PL];
-                ew[ww * GP + tid] = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-            }
-            ew[NW * GP + tid] = M;
-        }
-        lds_barrier();
+        // every entry of the workgroup's partial: each thread forms its head's reference (the
+        // waves' largest maximum) and the waves' weights itself (no serial pass, no barrier)
         const int h0 = 4 * r0, nh = min(GP, G - h0);  // this pass's query heads
         for (int i = tid; i < nh * PL; i += NW * 64) {
             const int hl = i / PL, col = i - hl * PL;
-            float v = ew[NW * GP + hl];
+            float mw[NW], M = -INFINITY;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                mw[ww] = wx[(ww * GP + hl) * PL];
+                M = fmaxf(M, mw[ww]);
+            }
+            float v = M;
             if (col > 0) {
                 v = 0.0f;
 #pragma unroll
-                for (int ww = 0; ww < NW; ++ww) v = fmaf(ew[ww * GP + hl], wx[(ww * GP + hl) * PL + col], v);
+                for (int ww = 0; ww < NW; ++ww)
+                    v = fmaf(mw[ww] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw[ww] - M),
+                             wx[(ww * GP + hl) * PL + col], v);
             }
             if (a.fused)  // read by the last workgroup, possibly on another XCD
                 __hip_atomic_store(pout + h0 * PL + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1056,6 +1053,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DevHead* __r
     const int jc = tid % D;  // channel tid (tid < D): its field columns
     const u16x8 fl = *(const u16x8*)&H.vch[jc][0];
     const float stv = H.bitsV[jc] ? H.stepV[jc] : 0.0f;
+    const int io = kMergeSlice * sl + (tid & (kMergeSlice - 1));  // output channel (tid < kMergeSlice)
+    const float ob = H.obias[io], mu = H.muV[io];
     __syncthreads();
     // ---- reference: the largest partial maximum
     float mx = -INFINITY;
@@ -1117,8 +1116,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DevHead* __r
     if (tid < kMergeSlice) {
         float o = 0.0f;
         for (int s2 = 0; s2 < JS; ++s2) o += red[s2 * I4 + (tid >> 2)][tid & 3];
-        const int i = kMergeSlice * sl + tid;
-        out[(zh * G + hh) * D + i] = L > 0.0f ? H.obias[i] + o : H.muV[i];
+        out[(zh * G + hh) * D + io] = L > 0.0f ? ob + o : mu;
     }
 }
 
@@ -1520,7 +1518,7 @@ int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, P
     const int NW = wg_waves(p.v.rb, p.v.nqm, p.v.nvb);
     p.nw = NW;
     const int GP = 4 * epilogue_row_blocks(RB);
-    const size_t epi = ((size_t)NW * GP * (kPartHead + 16 * p.v.nvb) + (size_t)(NW + 1) * GP) * sizeof(float);
+    const size_t epi = (size_t)NW * GP * (kPartHead + 16 * p.v.nvb) * sizeof(float);
     const size_t scr = al16((size_t)scratch_bytes(RB, p.v.nqm, p.v.nvb, d));
     const size_t ksch = (size_t)p.v.nqm * 4 * 8 * 4;
     const size_t group = (size_t)NW * a.buf_bytes;  // one ring slot of every wave
