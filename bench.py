@@ -437,7 +437,25 @@ def run_layers(args, w, torch, q, dev):
         step()
         te.stop(i)
     torch.cuda.synchronize()
-    gms, ems = tg.ms(), te.ms()
+    # the same layers' queries decoded by one batched-layers call (one launch per run of
+    # layers that share a decode variant), for callers that hold every layer's queries
+    wsl = torch.zeros(cb.decode_layers_workspace_bytes(0, L, S, ctx), dtype=torch.uint8, device=dev)
+    outl = torch.empty_like(out)
+
+    def step_layers():
+        q.decode_attention_layers(cb, blob, cache, 0, L, ids, lens, ctx, Qd, outl, wsl)
+
+    for _ in range(args.warmup):
+        q.flush_write(flush)
+        step_layers()
+    tl = Timer(torch, args.steps)
+    for i in range(args.steps):
+        q.flush_write(flush)
+        tl.start(i)
+        step_layers()
+        tl.stop(i)
+    torch.cuda.synchronize()
+    gms, ems, lms = tg.ms(), te.ms(), tl.ms()
     tb = cb.tile_bytes
     cache_bytes = L * S * w.n_kv * ((ctx + 63) // 64) * tb
     side = L * (2 * w.n_kv * w.d * w.d * 4 + S * (w.n_q * w.d * 2 + w.n_q * w.d * 4))
@@ -454,6 +472,11 @@ def run_layers(args, w, torch, q, dev):
         "decode_ms_p50": round(float(np.median(gms)), 4),
         "decode_ms_min": round(float(gms.min()), 4),
         "decode_ms_eager": round(float(ems.mean()), 4),
+        "decode_ms_batched_layers": round(float(lms.mean()), 4),
+        "decode_gbs_batched_layers": round(dec_bytes / (lms.mean() / 1e3) / 1e9, 2),
+        "batched_layers": (f"the {L} layers' queries decoded by one aatc_decode_attention_layers call (a launch per "
+                           "run of layers sharing a decode variant); a model's step runs its layers one after "
+                           "another, which value and decode_ms measure"),
         "decode_bytes": dec_bytes,
         "decode_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
         "encode_ms_per_layer": round(float(np.mean(enc_ms)), 4),

@@ -310,6 +310,35 @@ int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob, const aat
                           const int64_t* seq_lens, int64_t max_len, const uint16_t* q,
                           float* out, void* workspace, size_t ws_bytes, void* stream);
 
+/* Workspace bytes for aatc_decode_attention_layers over layers [layer0, layer0 + n_layers)
+ * with n_seqs sequences of length <= max_len (the largest any of its launches needs).
+ * Errors: INVALID_ARG, UNSUPPORTED (vector-quantized keys; a variant as for
+ * aatc_decode_attention_layers). */
+int aatc_decode_layers_workspace_bytes(const aatc_codebook* cb, int32_t layer0, int32_t n_layers,
+                                       int32_t n_seqs, int64_t max_len, size_t* bytes);
+
+/* aatc_decode_attention for the same sequences in n_layers consecutive layers
+ * [layer0, layer0 + n_layers) at once, for callers that hold every layer's queries (the
+ * attention of each layer is the one defined for aatc_decode_attention: "Attention-Aware
+ * Transform Coding Guide", Formal Attention Distortion Model and KLT section).  q and out
+ * are [n_layers][n_seqs][H_q][d] (layer-major); seq_ids / seq_lens as for one layer and
+ * shared by all layers.  The layers run as few launches: one per run of consecutive layers
+ * whose heads take the same decode variant, each run's (layer, sequence, kv-head) triples
+ * splitting the CUs between them, so the fixed cost of a launch is paid once per run
+ * rather than once per layer.  Results are those of one aatc_decode_attention call per
+ * layer.  In a model the layers of one step follow each other (a layer's queries depend on
+ * the previous layer's output); per-layer calls are the path for that.  Workspace:
+ * aatc_decode_layers_workspace_bytes() bytes, rules as for aatc_decode_attention (the runs
+ * use it one after another on `stream`).  At most 65535 (layer, sequence) slots.
+ * Errors: INVALID_ARG (also layers outside the codebook), CAPACITY, WORKSPACE, HIP;
+ * UNSUPPORTED with vector-quantized keys.  Every argument and run is checked before the
+ * first launch. */
+int aatc_decode_attention_layers(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
+                                 int32_t layer0, int32_t n_layers, int32_t n_seqs,
+                                 const int32_t* seq_ids, const int64_t* seq_lens, int64_t max_len,
+                                 const uint16_t* q, float* out, void* workspace, size_t ws_bytes,
+                                 void* stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph capture, serving
  * loops that forbid allocation): aatc_decode_attention with its partials and arrival
  * counters in an 8 MiB device array of the library's own (one per GPU, held until the

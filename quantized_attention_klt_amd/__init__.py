@@ -53,6 +53,7 @@ EXPORTS = [
     "aatc_codebook_head", "aatc_codebook_fields", "aatc_codebook_save", "aatc_codebook_load", "aatc_codebook_free",
     "aatc_codebook_device_bytes", "aatc_codebook_upload", "aatc_cache_bytes", "aatc_encode",
     "aatc_encode_coeffs", "aatc_decode_workspace_bytes", "aatc_decode_attention",
+    "aatc_decode_layers_workspace_bytes", "aatc_decode_attention_layers",
     "aatc_decode_attention_append", "aatc_decode_attention_static", "aatc_flush_write", "aatc_read_probe",
     "aatc_profile_begin", "aatc_profile_end",
 ]
@@ -98,6 +99,9 @@ def load() -> C.CDLL:
         "aatc_encode": ([P, P, C.POINTER(Cache), i32, i32, P, P, i64, P, P, P], C.c_int),
         "aatc_encode_coeffs": ([P, P, C.POINTER(Cache), i32, i32, i64, i64, P, P], C.c_int),
         "aatc_decode_workspace_bytes": ([P, i32, i64, C.POINTER(C.c_size_t)], C.c_int),
+        "aatc_decode_layers_workspace_bytes": ([P, i32, i32, i32, i64, C.POINTER(C.c_size_t)], C.c_int),
+        "aatc_decode_attention_layers": ([P, P, C.POINTER(Cache), i32, i32, i32, P, P, i64, P, P, P, C.c_size_t, P],
+                                         C.c_int),
         "aatc_decode_attention": ([P, P, C.POINTER(Cache), i32, i32, P, P, i64, P, P, P, C.c_size_t, P],
                                   C.c_int),
         "aatc_decode_attention_append": ([P, P, C.POINTER(Cache), i32, i32, P, P, i64, P, P, P, P, P, C.c_size_t, P],
@@ -249,6 +253,11 @@ class Codebook:
         _check(load().aatc_cache_bytes(self.handle, n_layers, n_seqs, max_tokens, C.byref(n)))
         return n.value
 
+    def decode_layers_workspace_bytes(self, layer0: int, n_layers: int, n_seqs: int, max_len: int) -> int:
+        n = C.c_size_t()
+        _check(load().aatc_decode_layers_workspace_bytes(self.handle, layer0, n_layers, n_seqs, max_len, C.byref(n)))
+        return n.value
+
     def decode_workspace_bytes(self, n_seqs: int, max_len: int) -> int:
         n = C.c_size_t()
         _check(load().aatc_decode_workspace_bytes(self.handle, n_seqs, max_len, C.byref(n)))
@@ -345,6 +354,16 @@ def decode_attention(cb: Codebook, d_blob, cache: Cache, layer: int, seq_ids, se
                                         _dev(seq_ids), _dev(seq_lens), max_len, _dev(q), _dev(out),
                                         _dev(workspace), workspace.numel() * workspace.element_size(),
                                         _stream(stream)))
+
+
+def decode_attention_layers(cb: Codebook, d_blob, cache: Cache, layer0: int, n_layers: int, seq_ids, seq_lens,
+                            max_len: int, q, out, workspace, stream=None):
+    """aatc_decode_attention_layers: layers [layer0, layer0 + n_layers) at once; q bf16 device
+    [n_layers, n_seqs, H_q, d], out float32 device of the same shape."""
+    _check(load().aatc_decode_attention_layers(cb.handle, _dev(d_blob), C.byref(cache), layer0, n_layers,
+                                               seq_ids.numel(), _dev(seq_ids), _dev(seq_lens), max_len, _dev(q),
+                                               _dev(out), _dev(workspace), workspace.numel() * workspace.element_size(),
+                                               _stream(stream)))
 
 
 def decode_attention_append(cb: Codebook, d_blob, cache: Cache, layer: int, seq_ids, seq_lens, max_len: int, k_new,

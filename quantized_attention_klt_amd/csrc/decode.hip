@@ -95,6 +95,9 @@ struct DecodeArgs {
     int nbw, buf_bytes, early, off_scratch, off_ksched, off_rec, off_sync;
     int off_pbuf;  // per-wave probability operands [NW][RB KiB] when the key block is smaller, else -1
     int fused;  // the last workgroup of each (sequence, kv-head) merges (no merge launch)
+    // sequences per layer: grid index z covers layer a.layer + z / n_seqs_call, sequence slot
+    // z mod n_seqs_call (one layer per launch unless layers are batched)
+    int n_seqs_call;
 };
 
 // LDS-only workgroup barrier: this wave's LDS operations are complete, then s_barrier.
@@ -487,7 +490,9 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
     const int wgi = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, c = lane & 15;
-    const DevHead& H = blob[a.layer * a.n_kv + h];
+    const int zl = z / a.n_seqs_call, zs = z - zl * a.n_seqs_call;  // layer offset, sequence slot
+    const int layer = a.layer + zl;
+    const DevHead& H = blob[layer * a.n_kv + h];
     const int G = a.G, TB = a.tile_bytes, BB = a.buf_bytes;
     const int64_t zh = (int64_t)z * a.n_kv + h;
     // every pointer argument in scalar registers at once: the argument loads then form one
@@ -528,7 +533,7 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
     // the copies would make the compiler wait for every copy in flight.
     int hBK, hBV, seq;
     int64_t len0;  // tokens cached before this call
-    load_head_and_sequence(&H, seq_ids + z, seq_lens + z, hBK, hBV, seq, len0);
+    load_head_and_sequence(&H, seq_ids + zs, seq_lens + zs, hBK, hBV, seq, len0);
     const uint32_t vblock = 8u * (uint32_t)hBK;
     const int nkw = hBK / 32, nvr = hBV / 8;  // a token's key record words, value record bytes
     asm volatile("" ::"s"(vblock), "s"(nkw), "s"(nvr));
@@ -536,7 +541,7 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
     int64_t len = min(min(len0 + (a.k_new ? 1 : 0), a.max_len), a.n_tiles_cap * kTile);
     if (seq < 0 || seq >= a.n_seqs_cache) len = 0;
     const int n_tiles = (int)((len + kTile - 1) / kTile);  // < 2^31 / 64: the host bounds the range
-    uint8_t* tiles = cache + (((int64_t)a.layer * a.n_seqs_cache + seq) * a.n_kv + h) * a.n_tiles_cap * TB;
+    uint8_t* tiles = cache + (((int64_t)layer * a.n_seqs_cache + seq) * a.n_kv + h) * a.n_tiles_cap * TB;
     // append mode: the new token's slot, when it lies within the attended range
     const bool app = a.k_new && len0 >= 0 && len0 < len;
     const int64_t t_app = app ? len0 / kTile : -1;
@@ -1017,7 +1022,7 @@ constexpr int kMaxPL = kPartHead + 16 * aatc::kMaxVB;
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DevHead* __restrict__ blob, int layer, int n_kv,
                                                               int G, int W, int PL, const float* __restrict__ part,
-                                                              float* __restrict__ out) {
+                                                              float* __restrict__ out, int n_seqs_call) {
     constexpr int NT = kMergeThreads, NWV = NT / 64;
     constexpr int NSL = D / kMergeSlice;  // slices
     constexpr int I4 = kMergeSlice / 4;   // float4 columns of the slice
@@ -1032,7 +1037,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DevHead* __r
     const int h = blockIdx.x / NSL, sl = blockIdx.x - h * NSL, z = blockIdx.y, hh = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t zh = (int64_t)z * n_kv + h;
-    const DevHead& H = blob[layer * n_kv + h];
+    const DevHead& H = blob[(layer + z / n_seqs_call) * n_kv + h];  // (z: layer offset and sequence slot)
     const int64_t PS = (int64_t)G * PL;              // floats between partials
     const float* P = part + (zh * W * G + hh) * PL;  // partial w at P + w * PS
     const int PL4 = PL >> 2, NS = NT / PL4;
@@ -1458,16 +1463,20 @@ struct Plan {
 size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, Plan& p) {
+// n_seqs: the launch's (layer, sequence) slots - n_layers consecutive layers from `layer`,
+// n_seqs / n_layers sequences each
+int make_plan(const aatc_codebook* cb, int layer, int n_seqs, int64_t max_len, Plan& p, int n_layers = 1) {
     const int G = cb->group, d = cb->d;
     const int RB = (G + 3) / 4;
     p.nqm_max = 0;
     p.nvb_max = 0;
-    for (int h = 0; h < cb->n_kv; ++h) {
-        const DevHead& D = cb->blob[(size_t)layer * cb->n_kv + h];
-        p.nqm_max = std::max(p.nqm_max, D.nqm);
-        p.nvb_max = std::max(p.nvb_max, D.nvb);
-    }
+    for (int l = layer; l < layer + n_layers; ++l)
+        for (int h = 0; h < cb->n_kv; ++h) {
+            const DevHead& D = cb->blob[(size_t)l * cb->n_kv + h];
+            p.nqm_max = std::max(p.nqm_max, D.nqm);
+            p.nvb_max = std::max(p.nvb_max, D.nvb);
+        }
+    p.args.n_seqs_call = n_seqs / n_layers;
     if (cb->heads[0].vq_groups) {  // vector-quantized keys
         DecodeArgs& a = p.args;
         p.vq = true;
@@ -1613,7 +1622,7 @@ int launch_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* blob
     if (e1) HIP_TRY(hipEventRecord(e1, st));
     if (!a.fused) {
         hipLaunchKernelGGL((merge_kernel<D>), dim3(a.n_kv * (D / kMergeSlice), n_seqs, a.G), dim3(kMergeThreads), 0, st,
-                           blob, a.layer, a.n_kv, a.G, p.wg_per_head, a.part_ld, (const float*)part, out);
+                           blob, a.layer, a.n_kv, a.G, p.wg_per_head, a.part_ld, (const float*)part, out, a.n_seqs_call);
         HIP_TRY(hipGetLastError());
     }
     return AATC_OK;
@@ -1677,7 +1686,7 @@ int launch_vq_decode(const Plan& p, int n_seqs, hipStream_t st, const DevHead* b
     }
     if (e1) HIP_TRY(hipEventRecord(e1, st));
     hipLaunchKernelGGL((merge_kernel<D>), dim3(a.n_kv * (D / kMergeSlice), n_seqs, a.G), dim3(kMergeThreads), 0, st,
-                       blob, a.layer, a.n_kv, a.G, p.wg_per_head, a.part_ld, (const float*)part, out);
+                       blob, a.layer, a.n_kv, a.G, p.wg_per_head, a.part_ld, (const float*)part, out, a.n_seqs_call);
     HIP_TRY(hipGetLastError());
     return AATC_OK;
 }
@@ -1696,27 +1705,14 @@ extern "C" int aatc_decode_workspace_bytes(const aatc_codebook* cb, int32_t n_se
     return AATC_OK;
 }
 
-static int decode_impl(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache, int32_t layer,
-                       int32_t n_seqs, const int32_t* seq_ids, const int64_t* seq_lens, int64_t max_len,
+// Fill a plan's call arguments and launch it: n_slots (layer, sequence) slots of the plan's
+// layers (p.args.n_seqs_call sequences per layer), partials and counters in workspace.
+static int launch_plan(const aatc_codebook* cb, Plan& p, const aatc_cache* cache, int32_t layer, int n_slots,
+                       int64_t max_len, const DevHead* blob, const int32_t* seq_ids, const int64_t* seq_lens,
                        const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q, float* out, void* workspace,
-                       size_t ws_bytes, void* stream) {
-    if (!cb || !d_blob) return set_error(AATC_ERR_INVALID_ARG, "null codebook or blob");
-    int rc = check_cache(cb, cache, layer);
-    if (rc) return rc;
-    if (n_seqs < 1 || n_seqs > cache->n_seqs || !seq_ids || !seq_lens || !q || !out || !workspace)
-        return set_error(AATC_ERR_INVALID_ARG, "bad decode arguments");
-    if (n_seqs > 65535) return set_error(AATC_ERR_CAPACITY, "at most 65535 sequences per call");
-    if (max_len < 1 || max_len > cache->max_tokens)
-        return set_error(AATC_ERR_CAPACITY, "max_len %lld outside [1, %lld]", (long long)max_len,
-                         (long long)cache->max_tokens);
-    if (((uintptr_t)workspace) & 255) return set_error(AATC_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    Plan p;
-    rc = make_plan(cb, layer, n_seqs, max_len, p);
-    if (rc) return rc;
-    if (ws_bytes < p.part_bytes)
-        return set_error(AATC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, p.part_bytes);
-    int* ctrs = (int*)workspace;                                           // arrival counters
-    float* part = (float*)((uint8_t*)workspace + kCounterBytes);           // [n_seqs][n_kv][wg][G][part_ld]
+                       hipStream_t st) {
+    int* ctrs = (int*)workspace;                                  // arrival counters
+    float* part = (float*)((uint8_t*)workspace + kCounterBytes);  // [slots][n_kv][wg][G][part_ld]
     DecodeArgs& a = p.args;
     a.layer = layer;
     a.n_kv = cb->n_kv;
@@ -1726,11 +1722,10 @@ static int decode_impl(const aatc_codebook* cb, const void* d_blob, const aatc_c
         return set_error(AATC_ERR_CAPACITY, "a (sequence, kv-head) cache range of %lld bytes (at most 2^31 - 1)",
                          (long long)(a.n_tiles_cap * a.tile_bytes));
     a.max_len = max_len;
-    const DevHead* blob = (const DevHead*)d_blob;
-    hipStream_t st = (hipStream_t)stream;
     uint8_t* c = (uint8_t*)cache->data;
     a.k_new = k_new;
     a.v_new = v_new;
+    const int n_seqs = n_slots;
     if (p.vq) {
         if (k_new) return set_error(AATC_ERR_UNSUPPORTED, "fused append with vector-quantized keys");
         const int ng = cb->heads[0].vq_groups;
@@ -1768,12 +1763,114 @@ static int decode_impl(const aatc_codebook* cb, const void* d_blob, const aatc_c
     return set_error(AATC_ERR_UNSUPPORTED, "decode variant missing");
 }
 
+static int check_decode_args(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache, int32_t layer,
+                             int32_t n_seqs, const int32_t* seq_ids, const int64_t* seq_lens, int64_t max_len,
+                             const uint16_t* q, float* out, void* workspace) {
+    if (!cb || !d_blob) return set_error(AATC_ERR_INVALID_ARG, "null codebook or blob");
+    int rc = check_cache(cb, cache, layer);
+    if (rc) return rc;
+    if (n_seqs < 1 || n_seqs > cache->n_seqs || !seq_ids || !seq_lens || !q || !out || !workspace)
+        return set_error(AATC_ERR_INVALID_ARG, "bad decode arguments");
+    if (n_seqs > 65535) return set_error(AATC_ERR_CAPACITY, "at most 65535 sequences per call");
+    if (max_len < 1 || max_len > cache->max_tokens)
+        return set_error(AATC_ERR_CAPACITY, "max_len %lld outside [1, %lld]", (long long)max_len,
+                         (long long)cache->max_tokens);
+    if (((uintptr_t)workspace) & 255) return set_error(AATC_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    return AATC_OK;
+}
+
+static int decode_impl(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache, int32_t layer,
+                       int32_t n_seqs, const int32_t* seq_ids, const int64_t* seq_lens, int64_t max_len,
+                       const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q, float* out, void* workspace,
+                       size_t ws_bytes, void* stream) {
+    int rc = check_decode_args(cb, d_blob, cache, layer, n_seqs, seq_ids, seq_lens, max_len, q, out, workspace);
+    if (rc) return rc;
+    Plan p;
+    rc = make_plan(cb, layer, n_seqs, max_len, p);
+    if (rc) return rc;
+    if (ws_bytes < p.part_bytes)
+        return set_error(AATC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, p.part_bytes);
+    return launch_plan(cb, p, cache, layer, n_seqs, max_len, (const DevHead*)d_blob, seq_ids, seq_lens, k_new, v_new, q,
+                       out, workspace, (hipStream_t)stream);
+}
+
+// Layers [layer0, layer0 + n_layers) in runs of consecutive layers that take the same decode
+// variant (one launch per run, merge included): run r covers layers [first[r], first[r + 1]).
+static int layer_runs(const aatc_codebook* cb, int layer0, int n_layers, int n_seqs, int64_t max_len,
+                      std::vector<int>& first) {
+    first.clear();
+    Variant prev{0, 0, 0};
+    for (int l = layer0; l < layer0 + n_layers; ++l) {
+        Plan p;
+        const int rc = make_plan(cb, l, n_seqs, max_len, p);
+        if (rc) return rc;
+        if (p.vq) return set_error(AATC_ERR_UNSUPPORTED, "batched layers with vector-quantized keys");
+        if (l == layer0 || p.v.rb != prev.rb || p.v.nqm != prev.nqm || p.v.nvb != prev.nvb) first.push_back(l);
+        prev = p.v;
+    }
+    first.push_back(layer0 + n_layers);
+    return AATC_OK;
+}
+
 extern "C" int aatc_decode_attention(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
                                      int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const int64_t* seq_lens,
                                      int64_t max_len, const uint16_t* q, float* out, void* workspace,
                                      size_t ws_bytes, void* stream) {
     return decode_impl(cb, d_blob, cache, layer, n_seqs, seq_ids, seq_lens, max_len, nullptr, nullptr, q, out,
                        workspace, ws_bytes, stream);
+}
+
+extern "C" int aatc_decode_layers_workspace_bytes(const aatc_codebook* cb, int32_t layer0, int32_t n_layers,
+                                                  int32_t n_seqs, int64_t max_len, size_t* bytes) {
+    if (!cb || !bytes) return set_error(AATC_ERR_INVALID_ARG, "null pointer");
+    if (n_seqs < 1 || max_len < 1 || n_layers < 1 || layer0 < 0 || layer0 + n_layers > cb->n_layers)
+        return set_error(AATC_ERR_INVALID_ARG, "need n_seqs, max_len, n_layers >= 1 and layers within the codebook");
+    std::vector<int> first;
+    int rc = layer_runs(cb, layer0, n_layers, n_seqs, max_len, first);
+    if (rc) return rc;
+    size_t worst = 0;
+    for (size_t r = 0; r + 1 < first.size(); ++r) {
+        const int nl = first[r + 1] - first[r];
+        Plan p;
+        rc = make_plan(cb, first[r], nl * n_seqs, max_len, p, nl);
+        if (rc) return rc;
+        worst = std::max(worst, p.part_bytes);
+    }
+    *bytes = worst;
+    return AATC_OK;
+}
+
+extern "C" int aatc_decode_attention_layers(const aatc_codebook* cb, const void* d_blob, const aatc_cache* cache,
+                                            int32_t layer0, int32_t n_layers, int32_t n_seqs, const int32_t* seq_ids,
+                                            const int64_t* seq_lens, int64_t max_len, const uint16_t* q, float* out,
+                                            void* workspace, size_t ws_bytes, void* stream) {
+    if (n_layers < 1 || layer0 < 0 || !cb || layer0 + n_layers > cb->n_layers)
+        return set_error(AATC_ERR_INVALID_ARG, "layers [%d, %d) outside the codebook", layer0, layer0 + n_layers);
+    for (int l = layer0; l < layer0 + n_layers; ++l) {
+        const int rc = check_decode_args(cb, d_blob, cache, l, n_seqs, seq_ids, seq_lens, max_len, q, out, workspace);
+        if (rc) return rc;
+    }
+    if ((int64_t)n_layers * n_seqs > 65535) return set_error(AATC_ERR_CAPACITY, "at most 65535 (layer, sequence) slots");
+    std::vector<int> first;
+    int rc = layer_runs(cb, layer0, n_layers, n_seqs, max_len, first);
+    if (rc) return rc;
+    std::vector<Plan> plans(first.size() - 1);
+    for (size_t r = 0; r + 1 < first.size(); ++r) {  // every run checked before the first launch
+        const int nl = first[r + 1] - first[r];
+        rc = make_plan(cb, first[r], nl * n_seqs, max_len, plans[r], nl);
+        if (rc) return rc;
+        if (ws_bytes < plans[r].part_bytes)
+            return set_error(AATC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, plans[r].part_bytes);
+    }
+    const size_t row = (size_t)cb->n_kv * cb->group * cb->d;  // q / out elements per (layer, sequence)
+    for (size_t r = 0; r + 1 < first.size(); ++r) {
+        const int nl = first[r + 1] - first[r];
+        const size_t off = (size_t)(first[r] - layer0) * n_seqs * row;
+        rc = launch_plan(cb, plans[r], cache, first[r], nl * n_seqs, max_len, (const DevHead*)d_blob, seq_ids, seq_lens,
+                         nullptr, nullptr, q + off, out + off, workspace, (hipStream_t)stream);
+        if (rc) return rc;
+    }
+    return AATC_OK;
 }
 
 // ---------------------------------------------------------------------------------------

@@ -29,6 +29,14 @@ pytestmark = pytest.mark.gpu
 
 ATTN_BAR = 2e-3
 FLIP_BAR = 1e-4
+# batched-layers call against one call per layer: the same arithmetic per (layer, sequence,
+# kv-head) with the tiles split among another number of workgroups.  The probabilities are
+# fixed-point integers relative to each wave's reference maximum, so another split rounds
+# them differently; over diffuse attention on zero-mean values that noise reaches a few
+# 1e-4 of the output (observed 5e-4 on the Qwen-shaped model), within the oracle bar that
+# both outputs are held to.  The whole outputs are compared at that bar, and both are
+# checked against the oracle on the (layer, sequence, kv-head) where they differ most.
+BATCH_BAR = ATTN_BAR
 DEV = "cuda"
 
 
@@ -98,7 +106,8 @@ def _bits_of(t):
 
 def _layers_step(torch, q, w, n_layers, n_seqs, ctx):
     """Calibrate, prefill every layer, then one decode step over all layers as a HIP graph
-    and eagerly; returns what the slice checks need."""
+    and eagerly, and once more as one batched-layers call; returns what the slice checks
+    need (the per-layer and the batched outputs)."""
     t0 = time.perf_counter()
     cb, hms = _library_codebook(q, w, n_layers)
     _log(f"  library calibration of {len(hms)} heads: {time.perf_counter() - t0:.1f}s")
@@ -137,7 +146,23 @@ def _layers_step(torch, q, w, n_layers, n_seqs, ctx):
         torch.cuda.synchronize()
         assert torch.equal(out, eager), "graph replay differs from the eager calls"
     _log(f"  decode step over {n_layers} layers: graph replays bit-identical to the eager calls")
-    return cb, hms, cache_t, out.cpu().numpy()
+    # all layers in one batched call (one launch per run of layers sharing a decode variant):
+    # another split of the tiles, so the same attention up to the rounding of the merge
+    wsl = torch.zeros(cb.decode_layers_workspace_bytes(0, n_layers, n_seqs, ctx), dtype=torch.uint8, device=DEV)
+    outl = torch.full_like(out, float("nan"))
+    q.decode_attention_layers(cb, blob, cache, 0, n_layers, ids, lens, ctx, Qd, outl, wsl)
+    torch.cuda.synchronize()
+    a, b = outl.double(), eager.double()
+    assert bool(torch.isfinite(a).all()), "batched-layers call left non-finite outputs"
+    G = w.group
+    rel = ((a - b).reshape(n_layers, n_seqs, w.n_kv, G * w.d).norm(dim=-1) /
+           b.reshape(n_layers, n_seqs, w.n_kv, G * w.d).norm(dim=-1))
+    diff = rel.max().item()
+    worst = np.unravel_index(int(rel.argmax().item()), tuple(rel.shape))
+    _log(f"  batched-layers call: largest normwise difference to the per-layer calls {diff:.2e} "
+         f"at (layer, seq, kv-head) {tuple(int(x) for x in worst)}")
+    assert diff <= BATCH_BAR
+    return cb, hms, cache_t, (out.cpu().numpy(), outl.cpu().numpy()), tuple(int(x) for x in worst)
 
 
 def _check_slice(torch, cb, w, hms, cache_t, out, n_seqs, ctx, layer, s, h):
@@ -153,11 +178,13 @@ def _check_slice(torch, cb, w, hms, cache_t, out, n_seqs, ctx, layer, s, h):
     qf = synth.bf16_bits_to_f64(_bits_of(_queries(torch, w, hms, layer, s)))
     G = w.group
     ref = oracle.decode_attention(got_bytes, ocb, qf[h * G:(h + 1) * G], ctx)
-    err = normwise_rel_err(out[layer, s, h * G:(h + 1) * G], ref)
+    err = 0.0
+    for o in out:  # the per-layer calls' output and the batched call's
+        assert np.all(np.isfinite(o[layer, s, h * G:(h + 1) * G]))
+        err = max(err, normwise_rel_err(o[layer, s, h * G:(h + 1) * G], ref))
     flips, total, worst, edge = code_flips(got_bytes, ocb, ctx, K64, V64)
     _log(f"  (layer {layer}, seq {s}, kv-head {h}): rel err {err:.3e}, {flips} flips of {total}, "
          f"edge ratio {edge:.3g}")
-    assert np.all(np.isfinite(out[layer, s, h * G:(h + 1) * G]))
     assert err <= ATTN_BAR
     assert worst <= 1 and edge <= 1.0
     assert flips <= FLIP_BAR * total
@@ -167,19 +194,19 @@ def test_qwen_28_layers_131072_tokens(lib, torch):
     w = synth.WORKLOADS["qwen_128k"]
     L, S, ctx = w.n_layers, 1, w.ctx
     _log(f"qwen_128k: {L} layers x {ctx} tokens, {w.n_kv} kv-heads, G={w.group}")
-    cb, hms, cache_t, out = _layers_step(torch, lib, w, L, S, ctx)
+    cb, hms, cache_t, out, worst = _layers_step(torch, lib, w, L, S, ctx)
     _check_calibration(cb, w, hms, [(0, 0), (13, 2), (27, 3)])
-    for layer, h in ((0, 0), (13, 2), (27, 3)):
-        _check_slice(torch, cb, w, hms, cache_t, out, S, ctx, layer, 0, h)
+    for layer, s, h in ((0, 0, 0), (13, 0, 2), (27, 0, 3), worst):
+        _check_slice(torch, cb, w, hms, cache_t, out, S, ctx, layer, s, h)
 
 
 def test_llama_batch_32_layers_32_sequences_8192_tokens(lib, torch):
     w = synth.WORKLOADS["llama_batch"]
     L, S, ctx = w.n_layers, w.n_seqs, w.ctx
     _log(f"llama_batch: {L} layers x {S} sequences x {ctx} tokens")
-    cb, hms, cache_t, out = _layers_step(torch, lib, w, L, S, ctx)
+    cb, hms, cache_t, out, worst = _layers_step(torch, lib, w, L, S, ctx)
     _check_calibration(cb, w, hms, [(0, 0), (31, 7)])
-    for layer, s, h in ((0, 0, 0), (9, 31, 5), (22, 4, 2), (31, 17, 7)):
+    for layer, s, h in ((0, 0, 0), (9, 31, 5), (22, 4, 2), (31, 17, 7), worst):
         _check_slice(torch, cb, w, hms, cache_t, out, S, ctx, layer, s, h)
 
 

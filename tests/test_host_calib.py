@@ -159,6 +159,34 @@ def test_multi_head_codebook_geometry():
     assert cb.device_bytes() > 0
 
 
+def test_batched_layers_workspace_and_argument_errors():
+    """The batched-layers decode's workspace query runs its plans on the host: a layer range
+    inside the codebook gives a positive size at least that of the largest per-layer call's
+    share, a range outside it or an empty one is INVALID_ARG, and a codebook with
+    vector-quantized keys is UNSUPPORTED."""
+    w = synth.WORKLOADS["tiny"]
+    stats = []
+    for layer in range(2):
+        for h in range(2):
+            hm = synth.head_model(w, layer, h)
+            K, V, Q = synth.calibration_samples(w, hm, layer, h)
+            stats.append(oracle.head_stats(K, V, Q[:64]))
+    cb = q.calibrate(stats, 64, 2, 2, 4, 3.0)
+    both = cb.decode_layers_workspace_bytes(0, 2, 3, 100)
+    assert both > 0 and cb.decode_layers_workspace_bytes(1, 1, 3, 100) > 0
+    for args in ((0, 3, 3, 100), (2, 1, 3, 100), (-1, 1, 3, 100), (0, 0, 3, 100), (0, 2, 0, 100), (0, 2, 3, 0)):
+        with pytest.raises(q.AatcError) as e:
+            cb.decode_layers_workspace_bytes(*args)
+        assert e.value.status == -1  # AATC_ERR_INVALID_ARG
+    wv, K, V, Q = _samples("vq_tiny")
+    st = oracle.head_stats(K.astype(np.float64), V.astype(np.float64), Q.astype(np.float64))
+    cbv = q.calibrate([st], wv.d, 1, 1, wv.group, wv.avg_bits, joint=False, key_quantizer="vq",
+                      vq_normals=synth.vq_normals(wv, 0, 512))
+    with pytest.raises(q.AatcError) as e:
+        cbv.decode_layers_workspace_bytes(0, 1, 1, 512)
+    assert e.value.status == -2  # AATC_ERR_UNSUPPORTED
+
+
 def test_record_fields_match_the_oracle_placement():
     """The library's field placement (what the encoder and decoder use) equals the
     oracle's, for calibrated heads and for random bit vectors."""
