@@ -230,6 +230,32 @@ def test_decode_argument_errors(lib, torch):
     with pytest.raises(lib.AatcError) as e:
         lib.encode(cb, blob, cache, 0, [0], [120], 10, K, K)
     assert e.value.status == -6
+    # the batched-layers call: layers outside the codebook, max_len beyond the cache and a
+    # short workspace are refused before anything is launched (out keeps its contents)
+    out.fill_(7.0)
+    wsl = torch.zeros((cb.decode_layers_workspace_bytes(0, 1, 1, 128),), dtype=torch.uint8, device="cuda")
+    for l0, nl, status in ((0, 2, -1), (1, 1, -1), (-1, 1, -1), (0, 0, -1)):
+        with pytest.raises(lib.AatcError) as e:
+            lib.decode_attention_layers(cb, blob, cache, l0, nl, ids, ln, 128, qd, out, wsl)
+        assert e.value.status == status
+    with pytest.raises(lib.AatcError) as e:
+        lib.decode_attention_layers(cb, blob, cache, 0, 1, ids, ln, 129, qd, out, wsl)
+    assert e.value.status == -6
+    with pytest.raises(lib.AatcError) as e:
+        lib.decode_attention_layers(cb, blob, cache, 0, 1, ids, ln, 128, qd, out, small)
+    assert e.value.status == -7
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    # and a valid one-layer batch equals aatc_decode_attention (same plan, same bits)
+    ws.zero_()
+    wsl.zero_()
+    g = torch.Generator(device="cuda").manual_seed(11)
+    qd.copy_(torch.randn(qd.shape, generator=g, device="cuda").to(torch.bfloat16).view(torch.int16))
+    ref = torch.empty_like(out)
+    lib.decode_attention(cb, blob, cache, 0, ids, ln, 128, qd, ref, ws)
+    lib.decode_attention_layers(cb, blob, cache, 0, 1, ids, ln, 128, qd, out, wsl)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
 
 
 # ---- attention-optimal (non-orthogonal) key transform: the encoder projects keys with T,
