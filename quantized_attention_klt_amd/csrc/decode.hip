@@ -334,6 +334,107 @@ __device__ __forceinline__ void append_block(const DevHead& H, const uint16_t* x
     }
 }
 
+// The new token's codes of the column blocks cb = w0, w0 + STEP, ... (NBW of them) of one
+// wave, with append_block's arithmetic and order, but the memory accesses of all the blocks
+// batched into two rounds instead of two per block: (1) every block's channel start value,
+// bits and piece range, the token's key and value rows and the first half of the blocks'
+// operands, (2) every block's first field pieces (a channel has at most kPrePieces; more are
+// read one by one) and the second half's operands.  Under the tile stream of the other
+// workgroups a round trip to memory takes over a microsecond, so the owner workgroup's
+// prologue would otherwise be the last to finish.
+constexpr int kPrePieces = 3;
+template <int D, int NBW, int STEP>
+__device__ __forceinline__ void append_blocks(const DevHead& H, const uint16_t* xk, const uint16_t* xv, int w0,
+                                              LDS_AS uint32_t* rec, int g, int c) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    constexpr int NB = D / 16, KS = D / 32, HALF = (NBW + 1) / 2;
+    const bool t3 = H.enc_terms == 3;
+    int jb[NBW], bits[NBW], p0[NBW], p1[NBW];
+    float st[NBW];
+    bool isv[NBW];
+#pragma unroll
+    for (int k = 0; k < NBW; ++k) {
+        const int cb = w0 + STEP * k;
+        isv[k] = cb >= NB;
+        const int j = 16 * (isv[k] ? cb - NB : cb) + c;
+        jb[k] = j;
+        st[k] = isv[k] ? H.estartV[j] : H.estartK[j];
+        bits[k] = isv[k] ? H.bitsV[j] : H.bitsK[j];
+        const int16_t* cf = isv[k] ? H.cfirstV : H.cfirstK;
+        p0[k] = cf[j];
+        p1[k] = cf[j + 1];
+    }
+    bf16x8 xr[2][KS];  // the token's key and value rows (MFMA row 0; the other rows are zero)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 xa = *(const bf16x8*)(xk + 32 * ks + 8 * g);
+        const bf16x8 xb = *(const bf16x8*)(xv + 32 * ks + 8 * g);
+        xr[0][ks] = c == 0 ? xa : bf16x8{};
+        xr[1][ks] = c == 0 ? xb : bf16x8{};
+    }
+    auto operands = [&](int k, bf16x8 (&bh)[KS], bf16x8 (&bl)[KS], bf16x8 (&bm)[KS]) {
+        const uint16_t* uh = isv[k] ? H.EVt_hi : H.EKt_hi;
+        const uint16_t* ul = isv[k] ? H.EVt_lo : H.EKt_lo;
+        const uint16_t* um = isv[k] ? H.EVt_mid : H.EKt_mid;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bh[ks] = *(const bf16x8*)(uh + jb[k] * D + 32 * ks + 8 * g);
+            bl[ks] = *(const bf16x8*)(ul + jb[k] * D + 32 * ks + 8 * g);
+            bm[ks] = t3 ? *(const bf16x8*)(um + jb[k] * D + 32 * ks + 8 * g) : bf16x8{};
+        }
+    };
+    auto project = [&](int k, const bf16x8 (&bh)[KS], const bf16x8 (&bl)[KS], const bf16x8 (&bm)[KS]) {
+        f4 acc = f4{st[k], st[k], st[k], st[k]};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xr[isv[k]][ks], bh[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xr[isv[k]][ks], bl[ks], acc, 0, 0, 0);
+            if (t3) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xr[isv[k]][ks], bm[ks], acc, 0, 0, 0);
+        }
+        return acc[0];
+    };
+    float u[NBW];
+    {
+        bf16x8 bh[HALF][KS], bl[HALF][KS], bm[HALF][KS];
+#pragma unroll
+        for (int k = 0; k < HALF; ++k) operands(k, bh[k], bl[k], bm[k]);
+#pragma unroll
+        for (int k = 0; k < HALF; ++k) u[k] = project(k, bh[k], bl[k], bm[k]);
+    }
+    uint32_t pcs[NBW][kPrePieces];
+#pragma unroll
+    for (int k = 0; k < NBW; ++k) {
+        const uint32_t* pc = isv[k] ? H.cpieceV : H.cpieceK;
+#pragma unroll
+        for (int e = 0; e < kPrePieces; ++e) pcs[k][e] = p0[k] + e < p1[k] ? pc[p0[k] + e] : 0u;
+    }
+    if constexpr (NBW > HALF) {
+        bf16x8 bh[NBW - HALF][KS], bl[NBW - HALF][KS], bm[NBW - HALF][KS];
+#pragma unroll
+        for (int k = HALF; k < NBW; ++k) operands(k, bh[k - HALF], bl[k - HALF], bm[k - HALF]);
+#pragma unroll
+        for (int k = HALF; k < NBW; ++k) u[k] = project(k, bh[k - HALF], bl[k - HALF], bm[k - HALF]);
+    }
+#pragma unroll
+    for (int k = 0; k < NBW; ++k) {
+        if (g == 0 && bits[k] > 0) {
+            const uint32_t code = code_byte(u[k], (float)((1 << bits[k]) - 1), 0, 0u);
+            const uint32_t* pc = isv[k] ? H.cpieceV : H.cpieceK;
+            const int base = isv[k] ? H.BK / 8 : 0;  // record byte of the value record's byte 0
+            for (int p = p0[k]; p < p1[k]; ++p) {  // piece = byte | pos << 8 | width << 12 | shift << 16
+                uint32_t pcv = 0u;
+#pragma unroll
+                for (int e = 0; e < kPrePieces; ++e)
+                    if (p == p0[k] + e) pcv = pcs[k][e];
+                if (p >= p0[k] + kPrePieces) pcv = pc[p];
+                const int rb = base + (int)(pcv & 0xff), pos = (pcv >> 8) & 7, wd = (pcv >> 12) & 15, sh = (pcv >> 16) & 15;
+                const uint32_t v = ((code >> sh) & ((1u << wd) - 1u)) << pos;
+                lds_or_async(rec + (rb >> 2), v << (8 * (rb & 3)));
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------------------
 // The merge done by the last workgroup of a (sequence, kv-head) to finish the split decode
 // (one launch for the whole call).  Its arithmetic is merge_kernel's (softmax merge of the W
@@ -634,7 +735,7 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
         q_sync(qctr, QW, lane);
         if (owner) {  // (workgroup-uniform) the new token's codes
             const int64_t row = ((int64_t)z * a.n_kv + h) * D;
-            for (int cb = w; cb < 2 * NB; cb += QW) append_block<D>(H, a.k_new + row, a.v_new + row, cb, rec, g, c);
+            append_blocks<D, 2 * NB / QW, QW>(H, a.k_new + row, a.v_new + row, w, rec, g, c);
         }
         // score operands: item (m, rb, lane group gg, dword iw, head hh4) forms the three digit
         // words of its four slots (rows 4 hh4 + 0..2 of operand [m][rb]; row 4 hh4 + 3 is zero)
