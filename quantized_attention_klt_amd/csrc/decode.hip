@@ -698,15 +698,15 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
     if (w == 0) load_tile((const uint8_t*)&H.vb_col[0][0], (LDS_AS uint8_t*)vcol, NVB * 64, lane, 0);
     if (w == 1) load_tile((const uint8_t*)&H.kq_sched[0][0][0], (LDS_AS uint8_t*)ksched, NQM * 128, lane, 0);
     if (w == 2) load_tile((const uint8_t*)&H.kq_slot[0][0][0], (LDS_AS uint8_t*)kslot, NQM * 128, lane, 0);
-    if (tid == 0) *qctr = 0;
-    lds_barrier();  // the q-waves' requests are issued; the counter is zero
+    if (tid == 0) qctr[0] = qctr[2] = 0;
+    if (owner && tid < kMaxRecord / 4) rec[tid] = 0u;
+    lds_barrier();  // the q-waves' requests are issued; the counters and records are zero
     int issued = 0;  // tiles of this wave whose loads have been issued; tile number k uses ring slot k % NBW
-    if (!qwave)
+    if (!qwave && !owner)
         for (; issued < a.early && t + stride * issued < t_end; ++issued)
             stream_tile(trs, (uint32_t)((t + stride * issued) * TB), ring + issued * RS, tl, lane);
     if (qwave) {
         if (tid < RB * 16) corr[tid] = 0;
-        if (owner && tid < kMaxRecord / 4) rec[tid] = 0u;
         const float qscale = kLog2e / sqrtf((float)D);
 #pragma unroll
         for (int b = 0; b < BPW; ++b) {
@@ -733,10 +733,6 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
         }
         wait_vm(0);  // the table copies have landed (these waves have no tile in flight yet)
         q_sync(qctr, QW, lane);
-        if (owner) {  // (workgroup-uniform) the new token's codes
-            const int64_t row = ((int64_t)z * a.n_kv + h) * D;
-            append_blocks<D, 2 * NB / QW, QW>(H, a.k_new + row, a.v_new + row, w, rec, g, c);
-        }
         // score operands: item (m, rb, lane group gg, dword iw, head hh4) forms the three digit
         // words of its four slots (rows 4 hh4 + 0..2 of operand [m][rb]; row 4 hh4 + 3 is zero)
         for (int i = tid; i < NQM * RB * 64; i += QW * 64) {
@@ -788,6 +784,23 @@ __attribute__((amdgpu_waves_per_eu(waves_for(RB, NQM, NVB)))) void decode_kernel
             lr[1] = u32x4{(uint32_t)(128 * cr[1]), (uint32_t)(128 * cr[2]), 0u, 0u};
         }
         q_sync(qctr, 3 * QW, lane);
+    }
+    constexpr int NSW = NW - QW;  // stream waves
+    if (owner) {
+        // (workgroup-uniform) the new token's codes, by the stream waves before they request
+        // any tile: their loads then meet nearly empty memory queues (a coding block's two
+        // dependent round trips take several microseconds each once every CU's ring is in
+        // flight); every wave meets the complete records before its tile loop
+        static_assert((2 * NB) % NSW == 0, "whole coding blocks per stream wave");
+        if (!qwave) {
+            const int64_t row = ((int64_t)z * a.n_kv + h) * D;
+            append_blocks<D, 2 * NB / NSW, NSW>(H, a.k_new + row, a.v_new + row, w - QW, rec, g, c);
+            q_sync(qctr + 2, NSW, lane);
+            for (; issued < a.early && t + stride * issued < t_end; ++issued)
+                stream_tile(trs, (uint32_t)((t + stride * issued) * TB), ring + issued * RS, tl, lane);
+        } else {
+            q_wait(qctr + 2, NSW);
+        }
     }
     if (!qwave) q_wait(qctr, 3 * QW);  // the operands, records, tables and the appended token's records are in LDS
     uint32_t voff[NVB], vmask[NVB];  // value columns of this lane: tile offset of its plane slice, mask
